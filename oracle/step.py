@@ -1,0 +1,105 @@
+"""One batched decode step in plain fp64 (oracle; test infrastructure only).
+
+P1 "The weight read is the only term that does not scale" and P2 "The two
+halves of a decode-step memory bill" describe the step: the weights are
+streamed once and multiplied against every sequence's hidden state; each
+sequence reads its own whole KV cache; norms and SwiGLU process one row per
+sequence; the LM head matmul and the (greedy) sampling are per sequence.
+
+Model: a pre-norm decoder.  Per layer
+    h  = f16(RMSNorm(x))             ; [q;k;v] = h W_qkv^T
+    q, k = RoPE(q, k, pos)           ; append f16(k), f16(v) (or Q8_0) at pos
+    O  = Attention(f16(q), cache[0..pos])  ; x += f16(O) W_o^T
+    h2 = f16(RMSNorm(x))             ; x += f16(silu(h2 W_g^T) * (h2 W_u^T)) W_d^T
+then hf = f16(RMSNorm_final(x)), logits = hf W_lm^T, token = argmax (lowest
+index on ties).  f16(.) is round-to-nearest-even to fp16; everything else is
+fp64.  The model object needs attributes dims, embed, lm_head, norm_final and
+layers[i].{w_qkv, w_o, w_gate_up, w_down, norm_attn, norm_ffn}; caches are per
+layer with k, v (fp16) or kq, ks, vq, vs (Q8_0) arrays of logical shape
+[n_slots, n_kv, capacity, head_dim] (scales [.., head_dim/32]).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import q8_0_dequant, q8_0_quantize, round_f16
+from .ops import argmax_lowest, attention, dense_gemm, q4k_gemm, rmsnorm, rope, swiglu
+
+
+def kv_append(cache, kind: str, slot: int, pos: int, k: np.ndarray, v: np.ndarray) -> None:
+    """Store one token's keys and values ([n_kv, D], fp64) at index pos of slot.
+
+    fp16 cache: round to nearest-even fp16.  Q8_0 cache (P3 "Why Q8 is close to
+    free and where the sharp edges are"): per 32 values of one token and head,
+    see formats.q8_0_quantize.
+    """
+    if kind == "f16":
+        cache.k[slot, :, pos] = np.asarray(k, dtype=np.float64).astype(np.float16)
+        cache.v[slot, :, pos] = np.asarray(v, dtype=np.float64).astype(np.float16)
+    elif kind == "q8_0":
+        cache.kq[slot, :, pos], cache.ks[slot, :, pos] = q8_0_quantize(k)
+        cache.vq[slot, :, pos], cache.vs[slot, :, pos] = q8_0_quantize(v)
+    else:
+        raise ValueError(kind)
+
+
+def kv_read(cache, kind: str, slot: int, n: int):
+    """Keys and values of the first n positions of slot as fp64 [n_kv, n, D].
+
+    P3 (FAQ "Is KV cache quantization a kernel change or a storage change?"):
+    the attention reads the quantized values dequantized, d*q.
+    """
+    if kind == "f16":
+        return (cache.k[slot, :, :n].astype(np.float64), cache.v[slot, :, :n].astype(np.float64))
+    if kind == "q8_0":
+        return (q8_0_dequant(cache.kq[slot, :, :n], cache.ks[slot, :, :n]),
+                q8_0_dequant(cache.vq[slot, :, :n], cache.vs[slot, :, :n]))
+    raise ValueError(kind)
+
+
+def attention_batch(q: np.ndarray, cache, kind: str, slots, n_ctx, scale: float) -> np.ndarray:
+    """Standalone decode attention: q [B, Hq, D] against n_ctx[b] cached tokens of slot[b]."""
+    out = np.empty(q.shape, dtype=np.float64)
+    for b in range(q.shape[0]):
+        kd, vd = kv_read(cache, kind, int(slots[b]), int(n_ctx[b]))
+        out[b] = attention(q[b], kd, vd, scale)
+    return out
+
+
+def decode_step(model, caches, kind: str, slots, pos, tok, n_layers=None):
+    """Advance every sequence by one token.
+
+    Appends this step's keys/values to ``caches`` (mutated) at pos[b] and
+    attends over pos[b]+1 tokens.  Returns (logits fp64 [B, vocab], next token
+    int64 [B]); the caller advances pos by one.
+    """
+    dm = model.dims
+    hq, hkv, hd = dm.n_q_heads, dm.n_kv_heads, dm.head_dim
+    f = dm.ffn
+    qrows, krows = hq * hd, hkv * hd
+    tok = np.asarray(tok, dtype=np.int64)
+    bsz = tok.shape[0]
+    scale = 1.0 / np.sqrt(hd)
+    x = model.embed[tok].astype(np.float64)
+    layers = model.layers if n_layers is None else model.layers[:n_layers]
+    for li, ly in enumerate(layers):
+        cache = caches[li]
+        h = round_f16(rmsnorm(x, ly.norm_attn, dm.rms_eps))
+        qkv = q4k_gemm(ly.w_qkv, qrows + 2 * krows, dm.hidden, h)
+        o = np.empty((bsz, qrows), dtype=np.float64)
+        for b in range(bsz):
+            p = int(pos[b])
+            q = rope(qkv[b, :qrows].reshape(hq, hd), p, dm.rope_base)
+            k = rope(qkv[b, qrows:qrows + krows].reshape(hkv, hd), p, dm.rope_base)
+            v = qkv[b, qrows + krows:].reshape(hkv, hd)
+            kv_append(cache, kind, int(slots[b]), p, k, v)
+            kd, vd = kv_read(cache, kind, int(slots[b]), p + 1)
+            o[b] = attention(round_f16(q), kd, vd, scale).reshape(-1)
+        x = x + q4k_gemm(ly.w_o, dm.hidden, qrows, round_f16(o))
+        h2 = round_f16(rmsnorm(x, ly.norm_ffn, dm.rms_eps))
+        gu = q4k_gemm(ly.w_gate_up, 2 * f, dm.hidden, h2)
+        a = round_f16(swiglu(gu[:, :f], gu[:, f:]))
+        x = x + q4k_gemm(ly.w_down, dm.hidden, f, a)
+    hf = round_f16(rmsnorm(x, model.norm_final, dm.rms_eps))
+    logits = dense_gemm(model.lm_head, hf)
+    return logits, argmax_lowest(logits)

@@ -1,0 +1,239 @@
+"""Pins for the oracle's decode step (CPU only).
+
+* batch invariance, bitwise: a batched step equals B single-sequence steps;
+* an identity network (zero output projections) reduces the step to
+  embedding -> final RMSNorm -> LM head -> argmax, checked directly;
+* a pure-Python brute force of a micro model built from Q4_K *fields* (not
+  bytes), fp16 rounding via ``struct``'s half format, Q8_0 via exact rationals.
+"""
+import copy
+import math
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import step as S
+from tests.test_oracle_formats import pack_q4k
+
+
+def f16(x: float) -> float:
+    return struct.unpack("<e", struct.pack("<e", x))[0]
+
+
+def _toy(seed=1000, kind="f16", n_layers=None, batch=2, length=128):
+    dims = synth.TOY
+    model = synth.make_model(dims, seed, n_layers=n_layers)
+    st = synth.Streams(seed + 7)
+    cap = length + 8
+    filled = [length] * batch
+    caches = []
+    for _ in model.layers:
+        if kind == "f16":
+            caches.append(synth.kv_cache_f16(st.next(), st.next(), batch, dims.n_kv_heads, cap,
+                                             dims.head_dim, filled))
+        else:
+            caches.append(synth.kv_cache_q8(st.next(), st.next(), batch, dims.n_kv_heads, cap,
+                                            dims.head_dim, filled))
+    tok = synth.tokens(st.next(), batch, dims.vocab)
+    return model, caches, tok
+
+
+@pytest.mark.parametrize("kind", ["f16", "q8_0"])
+def test_batch_invariance_bitwise(kind):
+    model, caches, tok = _toy(kind=kind)
+    slots = np.array([0, 1])
+    pos = np.array([128, 128])
+    c_batch = copy.deepcopy(caches)
+    lg, nt = S.decode_step(model, c_batch, kind, slots, pos, tok)
+    for b in range(2):
+        c_one = copy.deepcopy(caches)
+        lg1, nt1 = S.decode_step(model, c_one, kind, slots[b:b + 1], pos[b:b + 1], tok[b:b + 1])
+        assert np.array_equal(lg1[0], lg[b])
+        assert nt1[0] == nt[b]
+        for ca, cb in zip(c_one, c_batch):
+            for name in vars(ca):
+                assert np.array_equal(getattr(ca, name)[b], getattr(cb, name)[b])
+
+
+def test_identity_network_reduces_to_lm_head():
+    model, caches, tok = _toy()
+    for ly in model.layers:
+        ly.w_o = np.zeros_like(ly.w_o)
+        ly.w_down = np.zeros_like(ly.w_down)
+    lg, nt = S.decode_step(model, caches, "f16", np.array([0, 1]), np.array([128, 128]), tok)
+    dims = model.dims
+    for b in range(2):
+        x = model.embed[tok[b]].astype(np.float64)
+        ms = math.fsum(float(v) * float(v) for v in x) / dims.hidden
+        hf = [f16(float(model.norm_final[i]) * float(x[i]) / math.sqrt(ms + dims.rms_eps))
+              for i in range(dims.hidden)]
+        want = np.array([math.fsum(hf[i] * float(model.lm_head[v, i]) for i in range(dims.hidden))
+                         for v in range(0, dims.vocab, 97)])
+        assert np.allclose(lg[b, ::97], want, rtol=1e-12, atol=1e-12)
+        assert nt[b] == int(np.argmax(lg[b]))
+
+
+# ---------------------------------------------------------------- micro-model brute force
+MICRO = synth.ModelDims(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                        ffn=256, vocab=64)
+
+
+class FieldMatrix:
+    """A Q4_K matrix kept as fields, plus its packed row-tiled bytes for the oracle."""
+
+    def __init__(self, rng, n, k):
+        self.n, self.k = n, k
+        kb = k // 256
+        self.d = rng.integers(0, 0x1C00, (n, kb))       # fp16 bit patterns, positive, small
+        self.dmin = rng.integers(0, 0x1C00, (n, kb))
+        self.sc = rng.integers(0, 64, (n, kb, 8))
+        self.m = rng.integers(0, 64, (n, kb, 8))
+        self.q = rng.integers(0, 16, (n, kb, 256))
+        rows = np.zeros((n, kb, 144), np.uint8)
+        for r in range(n):
+            for c in range(kb):
+                rows[r, c] = np.frombuffer(pack_q4k(int(self.d[r, c]), int(self.dmin[r, c]), self.sc[r, c],
+                                                    self.m[r, c], self.q[r, c]), np.uint8)
+        self.bytes = np.ascontiguousarray(rows.reshape(n // 16, 16, kb, 144).transpose(0, 2, 1, 3))
+        hb = lambda b: struct.unpack("<e", struct.pack("<H", int(b)))[0]
+        self.w = [[hb(self.d[r, c // 256]) * int(self.sc[r, c // 256, (c % 256) // 32]) * int(self.q[r, c // 256, c % 256])
+                   - hb(self.dmin[r, c // 256]) * int(self.m[r, c // 256, (c % 256) // 32])
+                   for c in range(k)] for r in range(n)]
+
+    def matvec(self, x):
+        return [math.fsum(wi * xi for wi, xi in zip(row, x)) for row in self.w]
+
+
+def _q8_brute(vals):
+    amax = max(abs(v) for v in vals)
+    d = f16(amax / 127.0)
+    if d == 0.0:
+        return [0] * len(vals), 0.0
+    out = []
+    for v in vals:
+        y = Fraction(v / d)
+        r = math.floor(abs(y) + Fraction(1, 2))
+        out.append(int(math.copysign(min(r, 127), v)) if r else 0)
+    return out, d
+
+
+def _brute_step(mdl, cache, kind, slots, pos, tok):
+    dm = MICRO
+    hq, hkv, hd, f = dm.n_q_heads, dm.n_kv_heads, dm.head_dim, dm.ffn
+    logits, toks = [], []
+    for b in range(len(tok)):
+        x = [float(v) for v in mdl["embed"][tok[b]]]
+        p = int(pos[b])
+        slot = int(slots[b])
+        for li, ly in enumerate(mdl["layers"]):
+            def norm(vec, g):
+                ms = math.fsum(v * v for v in vec) / len(vec)
+                return [f16(float(g[i]) * vec[i] / math.sqrt(ms + dm.rms_eps)) for i in range(len(vec))]
+            h = norm(x, ly["norm_attn"])
+            qkv = ly["w_qkv"].matvec(h)
+
+            def rot(vec):
+                out = list(vec)
+                for i in range(hd // 2):
+                    a = p * dm.rope_base ** (-2.0 * i / hd)
+                    c, s = math.cos(a), math.sin(a)
+                    out[i] = vec[i] * c - vec[i + hd // 2] * s
+                    out[i + hd // 2] = vec[i + hd // 2] * c + vec[i] * s
+                return out
+            qs = [rot(qkv[hh * hd:(hh + 1) * hd]) for hh in range(hq)]
+            ks = [rot(qkv[(hq + g) * hd:(hq + g + 1) * hd]) for g in range(hkv)]
+            vs = [qkv[(hq + hkv + g) * hd:(hq + hkv + g + 1) * hd] for g in range(hkv)]
+            for g in range(hkv):   # append, then read back as the attention sees it
+                if kind == "f16":
+                    cache[li]["k"][slot][g][p] = [f16(v) for v in ks[g]]
+                    cache[li]["v"][slot][g][p] = [f16(v) for v in vs[g]]
+                else:
+                    for name, src in (("k", ks[g]), ("v", vs[g])):
+                        row = []
+                        for blk in range(hd // 32):
+                            qv, dd = _q8_brute(src[32 * blk:32 * blk + 32])
+                            row += [dd * qq for qq in qv]
+                        cache[li][name][slot][g][p] = row
+            o = []
+            for hh in range(hq):
+                g = hh // (hq // hkv)
+                qv = [f16(v) for v in qs[hh]]
+                sc = [math.fsum(qv[i] * cache[li]["k"][slot][g][t][i] for i in range(hd)) / math.sqrt(hd)
+                      for t in range(p + 1)]
+                mx = max(sc)
+                e = [math.exp(s - mx) for s in sc]
+                tot = math.fsum(e)
+                o += [f16(math.fsum(e[t] * cache[li]["v"][slot][g][t][i] for t in range(p + 1)) / tot)
+                      for i in range(hd)]
+            x = [a + c for a, c in zip(x, ly["w_o"].matvec(o))]
+            h2 = norm(x, ly["norm_ffn"])
+            gu = ly["w_gate_up"].matvec(h2)
+            act = []
+            for i in range(f):
+                z = gu[i]
+                sil = z / (1.0 + math.exp(-z)) if z >= 0 else z * math.exp(z) / (1.0 + math.exp(z))
+                act.append(f16(sil * gu[f + i]))
+            x = [a + c for a, c in zip(x, ly["w_down"].matvec(act))]
+        ms = math.fsum(v * v for v in x) / len(x)
+        hf = [f16(float(mdl["norm_final"][i]) * x[i] / math.sqrt(ms + dm.rms_eps)) for i in range(len(x))]
+        lg = [math.fsum(hf[i] * float(mdl["lm_head"][v, i]) for i in range(len(x))) for v in range(dm.vocab)]
+        logits.append(lg)
+        toks.append(max(range(dm.vocab), key=lambda v: (lg[v], -v)))
+    return np.array(logits), np.array(toks)
+
+
+@pytest.mark.parametrize("kind", ["f16", "q8_0"])
+def test_micro_model_brute_force(kind):
+    rng = np.random.default_rng(77)
+    dm = MICRO
+    hq, hkv, hd = dm.n_q_heads, dm.n_kv_heads, dm.head_dim
+    mdl = {"embed": rng.standard_normal((dm.vocab, dm.hidden)).astype(np.float16),
+           "lm_head": (rng.standard_normal((dm.vocab, dm.hidden)) / 16).astype(np.float16),
+           "norm_final": (1 + 0.1 * rng.standard_normal(dm.hidden)).astype(np.float32), "layers": []}
+    for _ in range(dm.n_layers):
+        mdl["layers"].append({
+            "w_qkv": FieldMatrix(rng, (hq + 2 * hkv) * hd, dm.hidden),
+            "w_o": FieldMatrix(rng, dm.hidden, hq * hd),
+            "w_gate_up": FieldMatrix(rng, 2 * dm.ffn, dm.hidden),
+            "w_down": FieldMatrix(rng, dm.hidden, dm.ffn),
+            "norm_attn": (1 + 0.1 * rng.standard_normal(dm.hidden)).astype(np.float32),
+            "norm_ffn": (1 + 0.1 * rng.standard_normal(dm.hidden)).astype(np.float32)})
+    model = synth.ModelWeights(dims=dm, embed=mdl["embed"], lm_head=mdl["lm_head"], norm_final=mdl["norm_final"],
+                               layers=[synth.LayerWeights(w_qkv=ly["w_qkv"].bytes, w_o=ly["w_o"].bytes,
+                                                          w_gate_up=ly["w_gate_up"].bytes, w_down=ly["w_down"].bytes,
+                                                          norm_attn=ly["norm_attn"], norm_ffn=ly["norm_ffn"])
+                                       for ly in mdl["layers"]])
+    n_slots, cap, length = 3, 8, 3
+    st = synth.Streams(5)
+    caches, bf_cache = [], []
+    for _ in range(dm.n_layers):
+        if kind == "f16":
+            c = synth.kv_cache_f16(st.next(), st.next(), n_slots, hkv, cap, hd, [length] * n_slots)
+            kk, vv = c.k.astype(np.float64), c.v.astype(np.float64)
+        else:
+            c = synth.kv_cache_q8(st.next(), st.next(), n_slots, hkv, cap, hd, [length] * n_slots)
+            kk = c.kq.astype(np.float64) * np.repeat(c.ks.astype(np.float64), 32, axis=-1)
+            vv = c.vq.astype(np.float64) * np.repeat(c.vs.astype(np.float64), 32, axis=-1)
+        caches.append(c)
+        bf_cache.append({"k": kk.tolist(), "v": vv.tolist()})
+    slots, pos = np.array([2, 0]), np.array([3, 3])
+    tok = np.array([5, 17])
+    for stepno in range(2):
+        lg, nt = S.decode_step(model, caches, kind, slots, pos, tok)
+        lb, tb = _brute_step(mdl, bf_cache, kind, slots, pos, tok)
+        assert np.allclose(lg, lb, rtol=1e-9, atol=1e-9), np.abs(lg - lb).max()
+        assert (nt == tb).all()
+        for li in range(dm.n_layers):   # the appended entries agree exactly
+            for b, s in enumerate(slots):
+                p = int(pos[b])
+                if kind == "f16":
+                    got_k = caches[li].k[s, :, p].astype(np.float64)
+                else:
+                    got_k = caches[li].kq[s, :, p].astype(np.float64) * np.repeat(
+                        caches[li].ks[s, :, p].astype(np.float64), 32, axis=-1)
+                assert np.array_equal(got_k, np.array(bf_cache[li]["k"][s])[:, p])
+        pos = pos + 1
+        tok = nt
