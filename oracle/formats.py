@@ -50,6 +50,32 @@ def round_f16(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
 
 
+def round_f16_blocked(x, block: int = 256) -> np.ndarray:
+    """fp16 rounding with one power-of-two exponent offset per block of values.
+
+    Along the last axis, each run of `block` consecutive values gets the
+    smallest integer s >= 0 with max|x| * 2^-s <= 65504, and each value
+    becomes 2^s * RN_fp16(x * 2^-s).  A block already inside fp16's range has
+    s = 0, so this equals round_f16 wherever plain fp16 does not overflow.
+    Used for the SwiGLU activation handed to the down projection, whose
+    magnitude the pages leave open and which exceeds fp16's range on the
+    synthetic weights (their mean is about 0.16, not 0).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-1]
+    assert n % block == 0
+    xb = x.reshape(x.shape[:-1] + (n // block, block))
+    amax = np.max(np.abs(xb), axis=-1, keepdims=True)
+    s = np.zeros_like(amax)
+    while True:
+        over = amax * np.exp2(-s) > 65504.0
+        if not over.any():
+            break
+        s = s + over
+    scale = np.exp2(s)
+    return (round_f16(xb / scale) * scale).reshape(x.shape)
+
+
 def q4k_fields(blocks: np.ndarray):
     """Decode the fields of Q4_K blocks.
 

@@ -10,10 +10,12 @@ Model: a pre-norm decoder.  Per layer
     h  = f16(RMSNorm(x))             ; [q;k;v] = h W_qkv^T
     q, k = RoPE(q, k, pos)           ; append f16(k), f16(v) (or Q8_0) at pos
     O  = Attention(f16(q), cache[0..pos])  ; x += f16(O) W_o^T
-    h2 = f16(RMSNorm(x))             ; x += f16(silu(h2 W_g^T) * (h2 W_u^T)) W_d^T
+    h2 = f16(RMSNorm(x))             ; x += f16b(silu(h2 W_g^T) * (h2 W_u^T)) W_d^T
 then hf = f16(RMSNorm_final(x)), logits = hf W_lm^T, token = argmax (lowest
-index on ties).  f16(.) is round-to-nearest-even to fp16; everything else is
-fp64.  The model object needs attributes dims, embed, lm_head, norm_final and
+index on ties).  f16(.) is round-to-nearest-even to fp16; f16b(.) is the same
+with one power-of-two exponent offset per 256 values (formats.round_f16_blocked)
+so that the SwiGLU activation cannot overflow; everything else is fp64.
+The model object needs attributes dims, embed, lm_head, norm_final and
 layers[i].{w_qkv, w_o, w_gate_up, w_down, norm_attn, norm_ffn}; caches are per
 layer with k, v (fp16) or kq, ks, vq, vs (Q8_0) arrays of logical shape
 [n_slots, n_kv, capacity, head_dim] (scales [.., head_dim/32]).
@@ -22,7 +24,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import q8_0_dequant, q8_0_quantize, round_f16
+from .formats import q8_0_dequant, q8_0_quantize, round_f16, round_f16_blocked
 from .ops import argmax_lowest, attention, dense_gemm, q4k_gemm, rmsnorm, rope, swiglu
 
 
@@ -98,7 +100,7 @@ def decode_step(model, caches, kind: str, slots, pos, tok, n_layers=None):
         x = x + q4k_gemm(ly.w_o, dm.hidden, qrows, round_f16(o))
         h2 = round_f16(rmsnorm(x, ly.norm_ffn, dm.rms_eps))
         gu = q4k_gemm(ly.w_gate_up, 2 * f, dm.hidden, h2)
-        a = round_f16(swiglu(gu[:, :f], gu[:, f:]))
+        a = round_f16_blocked(swiglu(gu[:, :f], gu[:, f:]))
         x = x + q4k_gemm(ly.w_down, dm.hidden, f, a)
     hf = round_f16(rmsnorm(x, model.norm_final, dm.rms_eps))
     logits = dense_gemm(model.lm_head, hf)

@@ -262,3 +262,42 @@ def test_q8_0_shapes(shape):
     q, d = F.q8_0_quantize(x)
     assert q.shape == shape and d.shape == shape[:-1] + (shape[-1] // 32,)
     assert q.dtype == np.int8 and d.dtype == np.float16
+
+
+# ---------------------------------------------------------------- blocked fp16 rounding
+def test_blocked_f16_equals_plain_f16_in_range():
+    x = np.random.default_rng(3).standard_normal((3, 512)) * 1000
+    assert np.array_equal(F.round_f16_blocked(x), F.round_f16(x))
+
+
+def test_blocked_f16_exponent_offsets():
+    x = np.zeros((1, 768))
+    x[0, 5] = 1e6          # block 0: 1e6 / 16 = 62500 <= 65504, 1e6 / 8 > 65504 -> s = 4
+    x[0, 6] = 3.0          # small value in the same block keeps 11 bits at 2^4 granularity
+    x[0, 256] = 65504.0    # block 1: exactly at the limit -> s = 0
+    x[0, 512] = 65505.0    # block 2: just above -> s = 1
+    x[0, 513] = -1e-3
+    y = F.round_f16_blocked(x)
+    assert y[0, 5] == 16 * float(np.float16(1e6 / 16))
+    assert y[0, 6] == 3.0
+    assert y[0, 256] == 65504.0
+    assert y[0, 512] == 2 * float(np.float16(65505.0 / 2))
+    assert y[0, 513] == 2 * float(np.float16(-1e-3 / 2))
+    # every result is an fp16 value times its block's power of two
+    for blk, s in ((0, 4), (1, 0), (2, 1)):
+        part = y[0, 256 * blk:256 * (blk + 1)] / 2.0 ** s
+        assert np.array_equal(part, part.astype(np.float16).astype(np.float64))
+    assert np.isfinite(F.round_f16_blocked(np.full((1, 256), 1e30))).all()
+    with pytest.raises(AssertionError):
+        F.round_f16_blocked(np.zeros(100))
+
+
+def test_blocked_f16_relative_precision():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((4, 1024)) * 10.0 ** rng.integers(3, 9, (4, 1))
+    y = F.round_f16_blocked(x)
+    amax = np.abs(x).reshape(4, 4, 256).max(-1, keepdims=True)
+    err = np.abs(y - x).reshape(4, 4, 256)
+    # normal-range values keep fp16's half-ulp relative error
+    big = np.abs(x).reshape(4, 4, 256) > amax * 2.0 ** -10
+    assert (err[big] <= np.abs(x.reshape(4, 4, 256))[big] * 2.0 ** -11).all()
