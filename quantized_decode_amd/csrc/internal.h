@@ -1,0 +1,59 @@
+// Host-side launchers shared between the translation units of libqkdec.
+// Every launcher assumes its arguments were validated by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/qkdec.h"
+
+namespace qk {
+
+// ---- Q4_K GEMM (gemm_q4k.hip); force_tw / force_kc = 0 pick the tiling by shape.
+// ws: device workspace of gemm_workspace_bytes(); its counters must be zero
+// before the first launch (every launch leaves them zero again).
+size_t gemm_workspace_bytes(int64_t n_rows, int64_t K, int B, bool swiglu);
+hipError_t launch_gemm_q4k(const void* W, int64_t N, int64_t K, const uint16_t* X, int64_t ldx, int B,
+                           float* Y, int64_t ldy, const float* residual, int64_t ldr, void* ws, hipStream_t st,
+                           int force_tw = 0, int force_kc = 0);
+hipError_t launch_gemm_q4k_xf32(const void* W, int64_t N, int64_t K, const float* X, int64_t ldx, int B,
+                                float* Y, int64_t ldy, const float* residual, int64_t ldr, void* ws, hipStream_t st,
+                                int force_tw = 0, int force_kc = 0);
+hipError_t launch_gemm_q4k_swiglu(const void* W, int64_t F, int64_t K, const uint16_t* X, int64_t ldx, int B,
+                                  float* A, int64_t lda, void* ws, hipStream_t st, int force_tw = 0,
+                                  int force_kc = 0);
+hipError_t launch_dequant_q4k(const void* W, int64_t n_blocks, float* out, hipStream_t st);
+
+// ---- attention (attn_decode.hip)
+// tokens per split work item
+constexpr int kAttnChunk = 128;
+inline int attn_n_splits(int capacity) { return (capacity + kAttnChunk - 1) / kAttnChunk; }
+// partial results per (b, q head, split): m, l, then head_dim values of o
+inline size_t attn_partials_bytes(int B, int n_q_heads, int head_dim, int capacity) {
+  return (size_t)B * n_q_heads * attn_n_splits(capacity) * (size_t)(head_dim + 2) * sizeof(float);
+}
+hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, const int32_t* n_ctx, int B,
+                              const uint16_t* Q, int n_q_heads, float scale, float* O, uint16_t* O16,
+                              float* partials, int n_ctx_add, hipStream_t st);
+
+// ---- KV append and RoPE (kv_append.hip)
+hipError_t launch_kv_append(const qkdec_kv_layer& kv, const int32_t* slot, const int32_t* pos, const float* k,
+                            const float* v, int B, int32_t* err, hipStream_t st);
+// rotate q, k of a [B][(Hq + 2 Hkv) * D] QKV row at pos[b], write q as fp16 and
+// append k, v to the cache
+hipError_t launch_rope_append(const qkdec_kv_layer& kv, const int32_t* slot, const int32_t* pos, const float* qkv,
+                              int B, int n_q_heads, float rope_base, uint16_t* q16, int32_t* err, hipStream_t st);
+
+// ---- small kernels (small.hip)
+hipError_t launch_embed(const uint16_t* E, int hidden, int vocab, const int32_t* tok, int B, float* x, hipStream_t st);
+hipError_t launch_rmsnorm_f16(const float* x, const float* gamma, int hidden, int B, float eps, uint16_t* h,
+                              hipStream_t st);
+size_t lm_head_partials_bytes(int64_t V, int B);
+// bytes of LDS the LM head kernel needs for B sequences of width H
+inline size_t lm_head_lds_bytes(int64_t H, int B) { return (size_t)B * (size_t)(H + 8) * 2; }
+hipError_t launch_lm_head_argmax(const uint16_t* Wlm, int64_t V, int64_t H, const uint16_t* X, int B,
+                                 float* logits, int32_t* tok, void* partials, int32_t* pos_inc, hipStream_t st);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+
+}  // namespace qk

@@ -1,0 +1,417 @@
+// The extern "C" entry points of libqkdec: argument validation, workspace
+// carving, the kernel chain of one decode step, and HIP-graph plans.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <new>
+
+#include "internal.h"
+
+namespace {
+
+using namespace qk;
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline qkdec_status hip_status(hipError_t e) { return e == hipSuccess ? QKDEC_OK : QKDEC_E_HIP; }
+// HIP's last-error state is sticky per thread: clear whatever an earlier call
+// (of this library or of the caller) left there, so that the check after our
+// own launches reports only our launches.
+inline void clear_stale_error() { (void)hipGetLastError(); }
+
+// LDS a work-group may use on the current device (queried per call: cheap,
+// and keeps the library free of mutable global state)
+qkdec_status check_lds(size_t bytes) {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return QKDEC_E_HIP;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) return QKDEC_E_HIP;
+  return bytes <= (size_t)v ? QKDEC_OK : QKDEC_E_UNSUPPORTED;
+}
+
+qkdec_status check_gemm(const void* W, int64_t N, int64_t K, const uint16_t* X, int64_t ldx, int32_t B) {
+  if (!W || !X) return QKDEC_E_ARG;
+  if (B < 1 || B > 16) return QKDEC_E_SHAPE;
+  if (N <= 0 || K <= 0 || N % 16 != 0 || K % 256 != 0) return QKDEC_E_SHAPE;
+  if (N / 16 > (int64_t)1 << 30 || K / 256 > (int64_t)1 << 20) return QKDEC_E_SHAPE;
+  if (ldx < K) return QKDEC_E_SHAPE;
+  if (!aligned(W, 16) || !aligned(X, 16) || ldx % 8 != 0) return QKDEC_E_ALIGN;
+  return QKDEC_OK;
+}
+
+qkdec_status check_kv(const qkdec_kv_layer* kv) {
+  if (!kv) return QKDEC_E_ARG;
+  if (kv->type != QKDEC_KV_F16 && kv->type != QKDEC_KV_Q8_0) return QKDEC_E_ARG;
+  if (!kv->k || !kv->v) return QKDEC_E_ARG;
+  if (kv->head_dim != 64 && kv->head_dim != 128) return QKDEC_E_SHAPE;
+  if (kv->n_kv_heads < 1 || kv->n_slots < 1 || kv->capacity < 32 || kv->capacity % 32 != 0) return QKDEC_E_SHAPE;
+  if (!aligned(kv->k, 16) || !aligned(kv->v, 16)) return QKDEC_E_ALIGN;
+  if (kv->type == QKDEC_KV_Q8_0) {
+    if (!kv->k_scale || !kv->v_scale) return QKDEC_E_ARG;
+    if (!aligned(kv->k_scale, 16) || !aligned(kv->v_scale, 16)) return QKDEC_E_ALIGN;
+  }
+  return QKDEC_OK;
+}
+
+bool same_kv_shape(const qkdec_kv_layer& a, const qkdec_kv_layer& b) {
+  return a.type == b.type && a.n_kv_heads == b.n_kv_heads && a.head_dim == b.head_dim &&
+         a.capacity == b.capacity && a.n_slots == b.n_slots;
+}
+
+qkdec_status check_model(const qkdec_model* m, const qkdec_kv_layer* kv) {
+  if (!m || !kv) return QKDEC_E_ARG;
+  if (m->n_layers < 1 || !m->layers || !m->embed || !m->lm_head || !m->norm_final) return QKDEC_E_ARG;
+  if (m->hidden <= 0 || m->hidden % 256 != 0 || m->ffn <= 0 || m->ffn % 256 != 0 || m->vocab <= 0 ||
+      m->vocab % 16 != 0)
+    return QKDEC_E_SHAPE;
+  if (m->n_q_heads < 1 || m->n_kv_heads < 1 || m->n_q_heads % m->n_kv_heads != 0 ||
+      m->n_q_heads / m->n_kv_heads > 16)
+    return QKDEC_E_SHAPE;
+  if (m->head_dim != 64 && m->head_dim != 128) return QKDEC_E_SHAPE;
+  if (((int64_t)m->n_q_heads * m->head_dim) % 256 != 0) return QKDEC_E_SHAPE;
+  if (!(m->rms_eps >= 0.f) || !(m->rope_base > 0.f)) return QKDEC_E_ARG;
+  if (!aligned(m->embed, 16) || !aligned(m->lm_head, 16)) return QKDEC_E_ALIGN;
+  for (int l = 0; l < m->n_layers; ++l) {
+    const qkdec_layer& ly = m->layers[l];
+    if (!ly.w_qkv || !ly.w_o || !ly.w_gate_up || !ly.w_down || !ly.norm_attn || !ly.norm_ffn) return QKDEC_E_ARG;
+    if (!aligned(ly.w_qkv, 16) || !aligned(ly.w_o, 16) || !aligned(ly.w_gate_up, 16) || !aligned(ly.w_down, 16))
+      return QKDEC_E_ALIGN;
+    const qkdec_status s = check_kv(&kv[l]);
+    if (s != QKDEC_OK) return s;
+    if (!same_kv_shape(kv[l], kv[0])) return QKDEC_E_SHAPE;
+  }
+  if (kv[0].n_kv_heads != m->n_kv_heads || kv[0].head_dim != m->head_dim) return QKDEC_E_SHAPE;
+  return QKDEC_OK;
+}
+
+// ---- step workspace layout (every region 256-byte aligned)
+struct StepWs {
+  int32_t* err;
+  float* x;
+  uint16_t* h;
+  float* qkv;
+  uint16_t* q16;
+  uint16_t* o16;
+  float* a;
+  float* attn_part;
+  void* lm_part;
+  void* gemm_ws;
+  size_t bytes;
+};
+
+StepWs step_layout(const qkdec_model* m, int B, const qkdec_kv_layer* kv, char* base) {
+  StepWs w{};
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    char* p = base ? base + off : nullptr;
+    off += round_up(n, 256);
+    return p;
+  };
+  const int64_t hq = (int64_t)m->n_q_heads * m->head_dim;
+  const int64_t nqkv = (int64_t)(m->n_q_heads + 2 * m->n_kv_heads) * m->head_dim;
+  w.err = reinterpret_cast<int32_t*>(take(256));
+  w.x = reinterpret_cast<float*>(take((size_t)B * m->hidden * 4));
+  w.h = reinterpret_cast<uint16_t*>(take((size_t)B * m->hidden * 2));
+  w.qkv = reinterpret_cast<float*>(take((size_t)B * nqkv * 4));
+  w.q16 = reinterpret_cast<uint16_t*>(take((size_t)B * hq * 2));
+  w.o16 = reinterpret_cast<uint16_t*>(take((size_t)B * hq * 2));
+  w.a = reinterpret_cast<float*>(take((size_t)B * m->ffn * 4));
+  w.attn_part = reinterpret_cast<float*>(take(attn_partials_bytes(B, m->n_q_heads, m->head_dim, kv[0].capacity)));
+  w.lm_part = take(lm_head_partials_bytes(m->vocab, B));
+  size_t g = gemm_workspace_bytes(nqkv, m->hidden, B, false);
+  g = std::max(g, gemm_workspace_bytes(m->hidden, hq, B, false));
+  g = std::max(g, gemm_workspace_bytes(2 * (int64_t)m->ffn, m->hidden, B, true));
+  g = std::max(g, gemm_workspace_bytes(m->hidden, m->ffn, B, false));
+  w.gemm_ws = take(g);
+  w.bytes = off;
+  return w;
+}
+
+qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int32_t* slot, int32_t* pos,
+                      int32_t* tok, int B, float* logits, void* workspace, hipStream_t st) {
+  const StepWs w = step_layout(m, B, kv, reinterpret_cast<char*>(workspace));
+  const int H = m->hidden, F = m->ffn, D = m->head_dim, Hq = m->n_q_heads;
+  const int64_t hq = (int64_t)Hq * D;
+  const int64_t nqkv = (int64_t)(Hq + 2 * m->n_kv_heads) * D;
+  const float scale = 1.0f / sqrtf((float)D);
+#define QK_TRY(expr)                                 \
+  do {                                               \
+    const hipError_t e_ = (expr);                    \
+    if (e_ != hipSuccess) return QKDEC_E_HIP;        \
+  } while (0)
+  QK_TRY(launch_embed(m->embed, H, m->vocab, tok, B, w.x, st));
+  for (int l = 0; l < m->n_layers; ++l) {
+    const qkdec_layer& ly = m->layers[l];
+    QK_TRY(launch_rmsnorm_f16(w.x, ly.norm_attn, H, B, m->rms_eps, w.h, st));
+    QK_TRY(launch_gemm_q4k(ly.w_qkv, nqkv, H, w.h, H, B, w.qkv, nqkv, nullptr, 0, w.gemm_ws, st));
+    QK_TRY(launch_rope_append(kv[l], slot, pos, w.qkv, B, Hq, m->rope_base, w.q16, w.err, st));
+    QK_TRY(launch_attn_decode(kv[l], slot, pos, B, w.q16, Hq, scale, nullptr, w.o16, w.attn_part, 1, st));
+    QK_TRY(launch_gemm_q4k(ly.w_o, H, hq, w.o16, hq, B, w.x, H, w.x, H, w.gemm_ws, st));
+    QK_TRY(launch_rmsnorm_f16(w.x, ly.norm_ffn, H, B, m->rms_eps, w.h, st));
+    QK_TRY(launch_gemm_q4k_swiglu(ly.w_gate_up, F, H, w.h, H, B, w.a, F, w.gemm_ws, st));
+    QK_TRY(launch_gemm_q4k_xf32(ly.w_down, H, F, w.a, F, B, w.x, H, w.x, H, w.gemm_ws, st));
+  }
+  QK_TRY(launch_rmsnorm_f16(w.x, m->norm_final, H, B, m->rms_eps, w.h, st));
+  QK_TRY(launch_lm_head_argmax(m->lm_head, m->vocab, H, w.h, B, logits, tok, w.lm_part, pos, st));
+#undef QK_TRY
+  return QKDEC_OK;
+}
+
+}  // namespace
+
+struct qkdec_plan {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+extern "C" {
+
+const char* qkdec_status_str(qkdec_status s) {
+  switch (s) {
+    case QKDEC_OK: return "QKDEC_OK";
+    case QKDEC_E_ARG: return "QKDEC_E_ARG: invalid argument";
+    case QKDEC_E_SHAPE: return "QKDEC_E_SHAPE: unsupported or inconsistent shape";
+    case QKDEC_E_ALIGN: return "QKDEC_E_ALIGN: misaligned pointer or leading dimension";
+    case QKDEC_E_WORKSPACE: return "QKDEC_E_WORKSPACE: workspace missing or too small";
+    case QKDEC_E_CAPACITY: return "QKDEC_E_CAPACITY: position reached the cache capacity";
+    case QKDEC_E_UNSUPPORTED: return "QKDEC_E_UNSUPPORTED: not supported by this build";
+    case QKDEC_E_HIP: return "QKDEC_E_HIP: HIP runtime error";
+    default: return "QKDEC: unknown status";
+  }
+}
+
+int32_t qkdec_abi_version(void) { return QKDEC_ABI_VERSION; }
+
+size_t qkdec_gemm_q4k_workspace_size(int64_t N, int64_t K, int32_t B) {
+  if (N <= 0 || K <= 0 || N % 16 || K % 256 || B < 1 || B > 16) return 0;
+  return gemm_workspace_bytes(N, K, B, false);
+}
+
+qkdec_status qkdec_gemm_q4k(const void* W, int64_t N, int64_t K, const uint16_t* X, int64_t ldx, int32_t B,
+                            float* Y, int64_t ldy, const float* residual, int64_t ldr, void* workspace,
+                            size_t ws_bytes, void* stream) {
+  qkdec_status s = check_gemm(W, N, K, X, ldx, B);
+  if (s != QKDEC_OK) return s;
+  if (!Y) return QKDEC_E_ARG;
+  if (ldy < N || (residual && ldr < N)) return QKDEC_E_SHAPE;
+  if (!workspace || ws_bytes < gemm_workspace_bytes(N, K, B, false)) return QKDEC_E_WORKSPACE;
+  if (!aligned(workspace, 256)) return QKDEC_E_ALIGN;
+  clear_stale_error();
+  return hip_status(launch_gemm_q4k(W, N, K, X, ldx, B, Y, ldy, residual, ldr, workspace, as_stream(stream)));
+}
+
+qkdec_status qkdec_gemm_q4k_xf32(const void* W, int64_t N, int64_t K, const float* X, int64_t ldx, int32_t B,
+                                 float* Y, int64_t ldy, const float* residual, int64_t ldr, void* workspace,
+                                 size_t ws_bytes, void* stream) {
+  if (!W || !X) return QKDEC_E_ARG;
+  if (B < 1 || B > 16) return QKDEC_E_SHAPE;
+  if (N <= 0 || K <= 0 || N % 16 != 0 || K % 256 != 0) return QKDEC_E_SHAPE;
+  if (N / 16 > (int64_t)1 << 30 || K / 256 > (int64_t)1 << 20) return QKDEC_E_SHAPE;
+  if (ldx < K) return QKDEC_E_SHAPE;
+  if (!aligned(W, 16) || !aligned(X, 16) || ldx % 4 != 0) return QKDEC_E_ALIGN;
+  if (!Y) return QKDEC_E_ARG;
+  if (ldy < N || (residual && ldr < N)) return QKDEC_E_SHAPE;
+  if (!workspace || ws_bytes < gemm_workspace_bytes(N, K, B, false)) return QKDEC_E_WORKSPACE;
+  if (!aligned(workspace, 256)) return QKDEC_E_ALIGN;
+  clear_stale_error();
+  return hip_status(
+      launch_gemm_q4k_xf32(W, N, K, X, ldx, B, Y, ldy, residual, ldr, workspace, as_stream(stream)));
+}
+
+size_t qkdec_gemm_q4k_swiglu_workspace_size(int64_t F, int64_t K, int32_t B) {
+  if (F <= 0 || K <= 0 || F % 16 || K % 256 || B < 1 || B > 16) return 0;
+  return gemm_workspace_bytes(2 * F, K, B, true);
+}
+
+qkdec_status qkdec_gemm_q4k_swiglu(const void* W, int64_t F, int64_t K, const uint16_t* X, int64_t ldx, int32_t B,
+                                   float* A, int64_t lda, void* workspace, size_t ws_bytes, void* stream) {
+  if (F <= 0 || F % 16 != 0) return QKDEC_E_SHAPE;
+  qkdec_status s = check_gemm(W, 2 * F, K, X, ldx, B);
+  if (s != QKDEC_OK) return s;
+  if (!A) return QKDEC_E_ARG;
+  if (lda < F) return QKDEC_E_SHAPE;
+  if (!workspace || ws_bytes < gemm_workspace_bytes(2 * F, K, B, true)) return QKDEC_E_WORKSPACE;
+  if (!aligned(workspace, 256)) return QKDEC_E_ALIGN;
+  clear_stale_error();
+  return hip_status(launch_gemm_q4k_swiglu(W, F, K, X, ldx, B, A, lda, workspace, as_stream(stream)));
+}
+
+qkdec_status qkdec_dequant_q4k(const void* W, int64_t n_blocks, float* out, void* stream) {
+  if (!W || !out) return QKDEC_E_ARG;
+  if (n_blocks <= 0 || n_blocks > ((int64_t)1 << 31) - 1) return QKDEC_E_SHAPE;
+  if (!aligned(W, 4)) return QKDEC_E_ALIGN;
+  clear_stale_error();
+  return hip_status(launch_dequant_q4k(W, n_blocks, out, as_stream(stream)));
+}
+
+static qkdec_status kv_append_common(const qkdec_kv_layer* kv, int type, const int32_t* slot, const int32_t* pos,
+                                     const float* k, const float* v, int32_t B, int32_t* err, void* stream) {
+  qkdec_status s = check_kv(kv);
+  if (s != QKDEC_OK) return s;
+  if (kv->type != type) return QKDEC_E_ARG;
+  if (!slot || !pos || !k || !v) return QKDEC_E_ARG;
+  if (B < 1 || B > 16) return QKDEC_E_SHAPE;
+  clear_stale_error();
+  return hip_status(launch_kv_append(*kv, slot, pos, k, v, B, err, as_stream(stream)));
+}
+
+qkdec_status qkdec_kv_append_f16(const qkdec_kv_layer* kv, const int32_t* slot, const int32_t* pos, const float* k,
+                                 const float* v, int32_t B, int32_t* err, void* stream) {
+  return kv_append_common(kv, QKDEC_KV_F16, slot, pos, k, v, B, err, stream);
+}
+
+qkdec_status qkdec_kv_append_q8_0(const qkdec_kv_layer* kv, const int32_t* slot, const int32_t* pos, const float* k,
+                                  const float* v, int32_t B, int32_t* err, void* stream) {
+  return kv_append_common(kv, QKDEC_KV_Q8_0, slot, pos, k, v, B, err, stream);
+}
+
+size_t qkdec_attn_workspace_size(int32_t B, int32_t n_q_heads, const qkdec_kv_layer* kv) {
+  if (!kv || B < 1 || n_q_heads < 1 || kv->capacity < 1 || kv->head_dim < 1) return 0;
+  return attn_partials_bytes(B, n_q_heads, kv->head_dim, kv->capacity);
+}
+
+qkdec_status qkdec_attn_decode(const qkdec_kv_layer* kv, const int32_t* slot, const int32_t* n_ctx, int32_t B,
+                               const uint16_t* Q, int32_t n_q_heads, float scale, float* O, uint16_t* O16,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  qkdec_status s = check_kv(kv);
+  if (s != QKDEC_OK) return s;
+  if (!slot || !n_ctx || !Q || (!O && !O16)) return QKDEC_E_ARG;
+  if (B < 1 || B > 16) return QKDEC_E_SHAPE;
+  if (n_q_heads < 1 || n_q_heads % kv->n_kv_heads != 0 || n_q_heads / kv->n_kv_heads > 16) return QKDEC_E_SHAPE;
+  if (!(scale == scale)) return QKDEC_E_ARG;
+  if (!aligned(Q, 16) || (O && !aligned(O, 16))) return QKDEC_E_ALIGN;
+  const size_t need = attn_partials_bytes(B, n_q_heads, kv->head_dim, kv->capacity);
+  if (!workspace || ws_bytes < need) return QKDEC_E_WORKSPACE;
+  if (!aligned(workspace, 16)) return QKDEC_E_ALIGN;
+  clear_stale_error();
+  return hip_status(launch_attn_decode(*kv, slot, n_ctx, B, Q, n_q_heads, scale, O, O16,
+                                       reinterpret_cast<float*>(workspace), 0, as_stream(stream)));
+}
+
+size_t qkdec_lm_head_workspace_size(int64_t V, int32_t B) {
+  if (V < 1 || B < 1) return 0;
+  return lm_head_partials_bytes(V, B);
+}
+
+qkdec_status qkdec_lm_head_argmax(const uint16_t* Wlm, int64_t V, int64_t H, const uint16_t* X, int32_t B,
+                                  float* logits, int32_t* tok, void* workspace, size_t ws_bytes, void* stream) {
+  if (!Wlm || !X || !tok) return QKDEC_E_ARG;
+  if (B < 1 || B > 16 || V < 16 || V % 16 != 0 || V > ((int64_t)1 << 30) || H < 256 || H % 256 != 0 ||
+      H > ((int64_t)1 << 20))
+    return QKDEC_E_SHAPE;
+  if (!aligned(Wlm, 16) || !aligned(X, 16)) return QKDEC_E_ALIGN;
+  if (!workspace || ws_bytes < lm_head_partials_bytes(V, B)) return QKDEC_E_WORKSPACE;
+  qkdec_status s = check_lds(lm_head_lds_bytes(H, B));
+  if (s != QKDEC_OK) return s;
+  clear_stale_error();
+  return hip_status(launch_lm_head_argmax(Wlm, V, H, X, B, logits, tok, workspace, nullptr, as_stream(stream)));
+}
+
+size_t qkdec_step_workspace_size(const qkdec_model* m, int32_t B, const qkdec_kv_layer* kv) {
+  if (check_model(m, kv) != QKDEC_OK || B < 1 || B > 16) return 0;
+  return step_layout(m, B, kv, nullptr).bytes;
+}
+
+qkdec_status qkdec_step_workspace_views(const qkdec_model* m, int32_t B, const qkdec_kv_layer* kv,
+                                        qkdec_step_views* out) {
+  if (!out) return QKDEC_E_ARG;
+  const qkdec_status s = check_model(m, kv);
+  if (s != QKDEC_OK) return s;
+  if (B < 1 || B > 16) return QKDEC_E_SHAPE;
+  char* const base = reinterpret_cast<char*>(256);  // any non-null base; offsets are relative to it
+  const StepWs w = step_layout(m, B, kv, base);
+  auto off = [&](const void* p) { return (size_t)(reinterpret_cast<const char*>(p) - base); };
+  out->x = off(w.x);
+  out->h = off(w.h);
+  out->qkv = off(w.qkv);
+  out->q16 = off(w.q16);
+  out->o16 = off(w.o16);
+  out->a = off(w.a);
+  return QKDEC_OK;
+}
+
+qkdec_status qkdec_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
+  if (!workspace || ws_bytes == 0) return QKDEC_E_ARG;
+  if (!aligned(workspace, 4)) return QKDEC_E_ALIGN;
+  clear_stale_error();
+  return hip_status(launch_fill_zero(workspace, ws_bytes, as_stream(stream)));
+}
+
+qkdec_status qkdec_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int32_t* slot, int32_t* pos,
+                        int32_t* tok, int32_t B, float* logits, void* workspace, size_t ws_bytes, void* stream) {
+  qkdec_status s = check_model(m, kv);
+  if (s != QKDEC_OK) return s;
+  if (!slot || !pos || !tok) return QKDEC_E_ARG;
+  if (B < 1 || B > 16) return QKDEC_E_SHAPE;
+  if (!workspace || ws_bytes < step_layout(m, B, kv, nullptr).bytes) return QKDEC_E_WORKSPACE;
+  if (!aligned(workspace, 256)) return QKDEC_E_ALIGN;
+  s = check_lds(lm_head_lds_bytes(m->hidden, B));
+  if (s != QKDEC_OK) return s;
+  clear_stale_error();
+  return run_step(m, kv, slot, pos, tok, B, logits, workspace, as_stream(stream));
+}
+
+qkdec_status qkdec_step_status(void* workspace, void* stream) {
+  if (!workspace) return QKDEC_E_ARG;
+  int32_t flag = 0;
+  hipStream_t st = as_stream(stream);
+  if (hipMemcpyAsync(&flag, workspace, sizeof(flag), hipMemcpyDeviceToHost, st) != hipSuccess) return QKDEC_E_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return QKDEC_E_HIP;
+  if (flag == 0) return QKDEC_OK;
+  const int32_t zero = 0;
+  if (hipMemcpyAsync(workspace, &zero, sizeof(zero), hipMemcpyHostToDevice, st) != hipSuccess) return QKDEC_E_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return QKDEC_E_HIP;
+  return QKDEC_E_CAPACITY;
+}
+
+qkdec_status qkdec_plan_create(qkdec_plan** plan, const qkdec_model* m, const qkdec_kv_layer* kv,
+                               const int32_t* slot, int32_t* pos, int32_t* tok, int32_t B, float* logits,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  if (!plan || !stream) return QKDEC_E_ARG;
+  *plan = nullptr;
+  qkdec_status s = check_model(m, kv);
+  if (s != QKDEC_OK) return s;
+  if (!slot || !pos || !tok) return QKDEC_E_ARG;
+  if (B < 1 || B > 16) return QKDEC_E_SHAPE;
+  if (!workspace || ws_bytes < step_layout(m, B, kv, nullptr).bytes) return QKDEC_E_WORKSPACE;
+  if (!aligned(workspace, 256)) return QKDEC_E_ALIGN;
+  s = check_lds(lm_head_lds_bytes(m->hidden, B));
+  if (s != QKDEC_OK) return s;
+  hipStream_t st = as_stream(stream);
+  clear_stale_error();
+  if (hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal) != hipSuccess) return QKDEC_E_HIP;
+  const qkdec_status rs = run_step(m, kv, slot, pos, tok, B, logits, workspace, st);
+  hipGraph_t graph = nullptr;
+  const hipError_t ec = hipStreamEndCapture(st, &graph);
+  if (rs != QKDEC_OK || ec != hipSuccess || !graph) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return rs != QKDEC_OK ? rs : QKDEC_E_HIP;
+  }
+  hipGraphExec_t exec = nullptr;
+  if (hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) != hipSuccess) {
+    (void)hipGraphDestroy(graph);
+    return QKDEC_E_HIP;
+  }
+  qkdec_plan* p = new (std::nothrow) qkdec_plan{graph, exec};
+  if (!p) {
+    (void)hipGraphExecDestroy(exec);
+    (void)hipGraphDestroy(graph);
+    return QKDEC_E_ARG;
+  }
+  *plan = p;
+  return QKDEC_OK;
+}
+
+qkdec_status qkdec_plan_launch(qkdec_plan* plan, void* stream) {
+  if (!plan) return QKDEC_E_ARG;
+  return hip_status(hipGraphLaunch(plan->exec, as_stream(stream)));
+}
+
+void qkdec_plan_destroy(qkdec_plan* plan) {
+  if (!plan) return;
+  (void)hipGraphExecDestroy(plan->exec);
+  (void)hipGraphDestroy(plan->graph);
+  delete plan;
+}
+
+}  // extern "C"

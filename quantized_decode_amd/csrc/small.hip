@@ -1,0 +1,197 @@
+// Embedding gather, RMSNorm -> fp16, and the fp16 LM head with fused argmax.
+//
+// P1 "The weight read is the only term that does not scale": the norms run
+// over one row per sequence; reading the output embedding is shared by the
+// batch while the matmul against it and the sampling are per sequence.
+#include "common.h"
+#include "internal.h"
+
+namespace qk {
+
+// x[b] = E[tok[b]] in fp32; a token outside [0, vocab) reads row 0.
+__global__ void embed_kernel(const half_t* __restrict__ E, int hidden, int vocab, const int32_t* tok, float* x) {
+  const int b = blockIdx.y;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= hidden) return;
+  int t = tok[b];
+  if (t < 0 || t >= vocab) t = 0;
+  x[(size_t)b * hidden + i] = (float)E[(size_t)t * hidden + i];
+}
+
+// h = f16(gamma * x / sqrt(mean(x^2) + eps)), one block per sequence.
+__global__ void __launch_bounds__(256) rmsnorm_f16_kernel(const float* __restrict__ x, const float* __restrict__ gamma,
+                                                          int hidden, float eps, half_t* __restrict__ h) {
+  const int b = blockIdx.x;
+  const float* xr = x + (size_t)b * hidden;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < hidden; i += 256) ss = __builtin_fmaf(xr[i], xr[i], ss);
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+  __shared__ float part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+  const float r = 1.0f / sqrtf(tot / (float)hidden + eps);
+  half_t* hr = h + (size_t)b * hidden;
+  for (int i = threadIdx.x; i < hidden; i += 256) hr[i] = (half_t)(gamma[i] * xr[i] * r);
+}
+
+// ------------------------------------------------------------------ LM head
+// Tiles of 16 vocabulary rows; v_mfma_f32_16x16x32_f16 with A = hidden states
+// (sequence rows, staged once per work-group in LDS) and B = W_lm^T.  Lane
+// (g, r) reads row r of the tile, 8 values at 32j + 8g of each 256-wide chunk.
+// Every wave keeps a running (max, lowest index) per sequence; the work-group
+// result goes to a partials buffer that lm_argmax_reduce_kernel folds.
+constexpr int kLmWaves = 4;
+constexpr int kLmGroups = 512;   // work-groups of the LM head launch (grid-stride over tiles)
+
+__device__ __forceinline__ void better(float& v, int& ix, float v2, int ix2) {
+  if (v2 > v || (v2 == v && ix2 < ix)) { v = v2; ix = ix2; }
+}
+
+__global__ void __launch_bounds__(256) lm_head_kernel(const half_t* __restrict__ W, int n_tiles, int H,
+                                                      const half_t* __restrict__ X, int B, float* logits, int64_t V,
+                                                      float* part_v, int32_t* part_i) {
+  extern __shared__ half_t xs[];                 // [B][H + 8]
+  const int ldsx = H + 8;
+  for (int idx = threadIdx.x; idx < B * (H / 8); idx += 256) {
+    const int b = idx / (H / 8), c = idx % (H / 8);
+    *reinterpret_cast<half8_t*>(xs + b * ldsx + 8 * c) = *reinterpret_cast<const half8_t*>(X + (size_t)b * H + 8 * c);
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, r = lane & 15;
+  const bool act = r < B;
+  float bestv[4];
+  int besti[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { bestv[i] = -__builtin_inff(); besti[i] = 0x7fffffff; }
+
+  const int nchunks = H / 256;
+  for (int tile = blockIdx.x * kLmWaves + wave; tile < n_tiles; tile += gridDim.x * kLmWaves) {
+    const half_t* wrow = W + ((size_t)tile * 16 + r) * H + 8 * g;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    half8_t wb[2][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wb[0][j] = *reinterpret_cast<const half8_t*>(wrow + 32 * j);
+    for (int c0 = 0; c0 < nchunks; c0 += 2) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int c = c0 + p;
+        if (c < nchunks) {
+          const int nx = (c + 1 < nchunks) ? c + 1 : c;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) wb[p ^ 1][j] = *reinterpret_cast<const half8_t*>(wrow + 256 * nx + 32 * j);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            half8_t a = act ? *reinterpret_cast<const half8_t*>(xs + r * ldsx + 256 * c + 32 * j + 8 * g)
+                            : half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+            acc = mfma16x16x32(a, wb[p][j], acc);
+          }
+        }
+      }
+    }
+    const int v = tile * 16 + r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = 4 * g + i;
+      if (b < B) {
+        if (logits) logits[(size_t)b * V + v] = acc[i];
+        better(bestv[i], besti[i], acc[i], v);
+      }
+    }
+  }
+  // reduce over the 16 rows (lanes r) of each lane group
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    for (int o = 8; o >= 1; o >>= 1) {
+      const float v2 = __shfl_xor(bestv[i], o, 16);
+      const int i2 = __shfl_xor(besti[i], o, 16);
+      better(bestv[i], besti[i], v2, i2);
+    }
+  }
+  __shared__ float sv[kLmWaves][16];
+  __shared__ int si[kLmWaves][16];
+  if (r == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { sv[wave][4 * g + i] = bestv[i]; si[wave][4 * g + i] = besti[i]; }
+  }
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    const int b = threadIdx.x;
+    float v = sv[0][b];
+    int ix = si[0][b];
+    for (int w = 1; w < kLmWaves; ++w) better(v, ix, sv[w][b], si[w][b]);
+    part_v[blockIdx.x * 16 + b] = v;
+    part_i[blockIdx.x * 16 + b] = ix;
+  }
+}
+
+// tok[b] = index of the best partial; pos[b] += 1 when pos is given.
+__global__ void lm_argmax_reduce_kernel(const float* part_v, const int32_t* part_i, int n_parts, int B,
+                                        int32_t* tok, int32_t* pos_inc) {
+  const int b = blockIdx.x;
+  float v = -__builtin_inff();
+  int ix = 0x7fffffff;
+  for (int j = threadIdx.x; j < n_parts; j += 64) better(v, ix, part_v[j * 16 + b], part_i[j * 16 + b]);
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float v2 = __shfl_xor(v, o);
+    const int i2 = __shfl_xor(ix, o);
+    better(v, ix, v2, i2);
+  }
+  if (threadIdx.x == 0) {
+    tok[b] = (ix == 0x7fffffff) ? 0 : ix;
+    if (pos_inc) pos_inc[b] += 1;
+  }
+}
+
+__global__ void fill_zero_kernel(uint32_t* p, size_t n_words) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n_words; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+hipError_t launch_embed(const uint16_t* E, int hidden, int vocab, const int32_t* tok, int B, float* x,
+                        hipStream_t st) {
+  hipLaunchKernelGGL(embed_kernel, dim3((hidden + 255) / 256, B), dim3(256), 0, st, reinterpret_cast<const half_t*>(E),
+                     hidden, vocab, tok, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_f16(const float* x, const float* gamma, int hidden, int B, float eps, uint16_t* h,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3(B), dim3(256), 0, st, x, gamma, hidden, eps,
+                     reinterpret_cast<half_t*>(h));
+  return hipGetLastError();
+}
+
+size_t lm_head_partials_bytes(int64_t V, int B) {
+  (void)V;
+  (void)B;
+  return (size_t)kLmGroups * 16 * (sizeof(float) + sizeof(int32_t));
+}
+
+hipError_t launch_lm_head_argmax(const uint16_t* Wlm, int64_t V, int64_t H, const uint16_t* X, int B, float* logits,
+                                 int32_t* tok, void* partials, int32_t* pos_inc, hipStream_t st) {
+  const int n_tiles = (int)(V / 16);
+  int groups = (n_tiles + kLmWaves - 1) / kLmWaves;
+  if (groups > kLmGroups) groups = kLmGroups;
+  float* pv = reinterpret_cast<float*>(partials);
+  int32_t* pi = reinterpret_cast<int32_t*>(pv + (size_t)kLmGroups * 16);
+  const size_t lds = (size_t)B * (H + 8) * sizeof(half_t);
+  hipLaunchKernelGGL(lm_head_kernel, dim3(groups), dim3(256), lds, st, reinterpret_cast<const half_t*>(Wlm), n_tiles,
+                     (int)H, reinterpret_cast<const half_t*>(X), B, logits, V, pv, pi);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(lm_argmax_reduce_kernel, dim3(B), dim3(64), 0, st, pv, pi, groups, B, tok, pos_inc);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
+  const size_t words = bytes / 4;
+  if (words == 0) return hipSuccess;
+  size_t blocks = (words + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, reinterpret_cast<uint32_t*>(p), words);
+  return hipGetLastError();
+}
+
+}  // namespace qk

@@ -1,0 +1,86 @@
+"""Device-memory helpers: lay host arrays out in the library's storage formats.
+
+These only move and reorder bytes (torch is used for device memory); the one
+layout change is the value cache, which the library keeps transposed per head
+([slot][kv head][head_dim][capacity]).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+from . import KV_F16, KV_Q8_0, KVLayer, kv_layer
+
+
+def dev(a: np.ndarray):
+    """numpy -> contiguous CUDA tensor with the same bytes and dtype."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to("cuda")
+
+
+def empty(shape, dtype):
+    import torch
+    return torch.empty(shape, dtype=dtype, device="cuda")
+
+
+@dataclass
+class DeviceKV:
+    """One layer of device KV cache plus its ctypes descriptor."""
+    kind: int
+    k: object
+    v: object                 # transposed: [slots][kv][D][cap]
+    k_scale: Optional[object]
+    v_scale: Optional[object]
+    desc: KVLayer
+
+    def logical_f16(self):
+        """(k, v) as numpy fp16 [slots, kv, cap, D] (v transposed back)."""
+        k = self.k.cpu().numpy()
+        v = self.v.cpu().numpy().transpose(0, 1, 3, 2)
+        return k, np.ascontiguousarray(v)
+
+    def logical_q8(self):
+        kq = self.k.cpu().numpy()
+        vq = np.ascontiguousarray(self.v.cpu().numpy().transpose(0, 1, 3, 2))
+        return kq, self.k_scale.cpu().numpy(), vq, self.v_scale.cpu().numpy()
+
+
+def _f16_t(a):
+    import torch
+    return dev(np.ascontiguousarray(a).view(np.uint16)).view(torch.float16)
+
+
+def upload_kv_f16(k: np.ndarray, v: np.ndarray) -> DeviceKV:
+    """k, v: fp16 [slots, kv, cap, D] (logical)."""
+    slots, nkv, cap, d = k.shape
+    kd = _f16_t(k)
+    vd = _f16_t(np.ascontiguousarray(v.transpose(0, 1, 3, 2)))
+    return DeviceKV(KV_F16, kd, vd, None, None, kv_layer(KV_F16, nkv, d, cap, slots, kd, vd))
+
+
+def upload_kv_q8(kq: np.ndarray, ks: np.ndarray, vq: np.ndarray, vs: np.ndarray) -> DeviceKV:
+    """kq, vq: int8 [slots, kv, cap, D]; ks, vs: fp16 [slots, kv, cap, D/32] (logical)."""
+    slots, nkv, cap, d = kq.shape
+    kd = dev(kq)
+    vd = dev(np.ascontiguousarray(vq.transpose(0, 1, 3, 2)))
+    ksd, vsd = _f16_t(ks), _f16_t(vs)
+    return DeviceKV(KV_Q8_0, kd, vd, ksd, vsd, kv_layer(KV_Q8_0, nkv, d, cap, slots, kd, vd, ksd, vsd))
+
+
+def upload_cache(c) -> DeviceKV:
+    """A logical cache object with k, v (fp16) or kq, ks, vq, vs (Q8_0)."""
+    if hasattr(c, "kq"):
+        return upload_kv_q8(c.kq, c.ks, c.vq, c.vs)
+    return upload_kv_f16(c.k, c.v)
+
+
+def upload_model(model):
+    """Device tensors of a synthetic model: (embed, lm_head, norm_final, [layer dicts])."""
+    import torch
+    layers = [dict(w_qkv=dev(l.w_qkv.reshape(-1)), w_o=dev(l.w_o.reshape(-1)),
+                   w_gate_up=dev(l.w_gate_up.reshape(-1)), w_down=dev(l.w_down.reshape(-1)),
+                   norm_attn=dev(l.norm_attn), norm_ffn=dev(l.norm_ffn)) for l in model.layers]
+    return (_f16_t(model.embed), _f16_t(model.lm_head), dev(model.norm_final), layers)

@@ -1,0 +1,78 @@
+"""Seeded synthetic inputs drawn directly on the GPU (torch Philox), for the
+multi-gigabyte workloads.  Same distributions as the numpy generators in
+synth/__init__.py; like them, this module computes nothing the decode step
+computes.  The oracle reads D2H copies of whatever it needs.
+"""
+from __future__ import annotations
+
+import torch
+
+Q4K_BLOCK_BYTES = 144
+
+
+def generator(seed: int) -> torch.Generator:
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return g
+
+
+def q4k_matrix(g: torch.Generator, n_rows: int, n_cols: int) -> torch.Tensor:
+    """Random Q4_K matrix bytes (row-tiled order), uint8 tensor of n_rows*n_cols/256*144 bytes."""
+    n_blocks = n_rows * (n_cols // 256)
+    b = torch.randint(0, 256, (n_blocks, Q4K_BLOCK_BYTES), dtype=torch.uint8, device="cuda", generator=g)
+    d = (torch.randn((n_blocks, 2), device="cuda", generator=g).abs() * 1e-3).to(torch.float16)
+    b[:, 0:4] = d.view(torch.uint8).view(n_blocks, 4)
+    return b.view(-1)
+
+
+def f16_normal(g: torch.Generator, shape, scale: float = 1.0) -> torch.Tensor:
+    x = torch.randn(shape, device="cuda", generator=g)
+    if scale != 1.0:
+        x = x * scale
+    return x.to(torch.float16)
+
+
+def gains(g: torch.Generator, n: int) -> torch.Tensor:
+    return 1.0 + 0.1 * torch.randn(n, device="cuda", generator=g)
+
+
+def model(dims, seed: int, n_layers=None):
+    """(embed, lm_head, norm_final, [layer dicts]) on the GPU for the step ABI."""
+    g = generator(seed)
+    embed = f16_normal(g, (dims.vocab, dims.hidden))
+    lm_head = f16_normal(g, (dims.vocab, dims.hidden), scale=dims.hidden ** -0.5)
+    norm_final = gains(g, dims.hidden)
+    hq = dims.n_q_heads * dims.head_dim
+    layers = []
+    for _ in range(dims.n_layers if n_layers is None else n_layers):
+        layers.append(dict(w_qkv=q4k_matrix(g, dims.qkv_rows, dims.hidden),
+                           w_o=q4k_matrix(g, dims.hidden, hq),
+                           w_gate_up=q4k_matrix(g, 2 * dims.ffn, dims.hidden),
+                           w_down=q4k_matrix(g, dims.hidden, dims.ffn),
+                           norm_attn=gains(g, dims.hidden), norm_ffn=gains(g, dims.hidden)))
+    return embed, lm_head, norm_final, layers
+
+
+def kv_cache(g: torch.Generator, kind: str, n_slots: int, n_kv: int, capacity: int, head_dim: int, filled: int):
+    """One layer of device cache in the library's layout (values transposed),
+    N(0,1) fp16 or Q8_0 (int8 uniform in -127..127, scale |N|*0.02) for
+    positions < filled and zeros beyond.  Returns (k, v, k_scale, v_scale)."""
+    if kind == "f16":
+        k = torch.zeros((n_slots, n_kv, capacity, head_dim), dtype=torch.float16, device="cuda")
+        v = torch.zeros((n_slots, n_kv, head_dim, capacity), dtype=torch.float16, device="cuda")
+        k[:, :, :filled] = f16_normal(g, (n_slots, n_kv, filled, head_dim))
+        v[:, :, :, :filled] = f16_normal(g, (n_slots, n_kv, head_dim, filled))
+        return k, v, None, None
+    k = torch.zeros((n_slots, n_kv, capacity, head_dim), dtype=torch.int8, device="cuda")
+    v = torch.zeros((n_slots, n_kv, head_dim, capacity), dtype=torch.int8, device="cuda")
+    ks = torch.zeros((n_slots, n_kv, capacity, head_dim // 32), dtype=torch.float16, device="cuda")
+    vs = torch.zeros_like(ks)
+    k[:, :, :filled] = torch.randint(-127, 128, (n_slots, n_kv, filled, head_dim), dtype=torch.int8, device="cuda",
+                                     generator=g)
+    v[:, :, :, :filled] = torch.randint(-127, 128, (n_slots, n_kv, head_dim, filled), dtype=torch.int8, device="cuda",
+                                        generator=g)
+    ks[:, :, :filled] = (torch.randn((n_slots, n_kv, filled, head_dim // 32), device="cuda", generator=g).abs()
+                         * 0.02).to(torch.float16)
+    vs[:, :, :filled] = (torch.randn((n_slots, n_kv, filled, head_dim // 32), device="cuda", generator=g).abs()
+                         * 0.02).to(torch.float16)
+    return k, v, ks, vs

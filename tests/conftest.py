@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests run on the GPU machine only; skip them cleanly where no GPU is visible.
+    # GPU tests need a visible GPU; skip them cleanly where there is none.
     try:
         import torch
         have_gpu = torch.cuda.is_available()

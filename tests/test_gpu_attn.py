@@ -1,0 +1,131 @@
+"""Split-K flash-decode attention (fp16 and Q8_0 caches) on the GPU against the oracle."""
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import step as OS
+from tests.gpu_util import assert_rel, sync, ws
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def qd():
+    import quantized_decode_amd as m
+    m.load_library()
+    return m
+
+
+def _make(kind, seed, n_slots, n_kv, cap, d, filled):
+    st = synth.Streams(seed)
+    if kind == "f16":
+        c = synth.kv_cache_f16(st.next(), st.next(), n_slots, n_kv, cap, d, filled)
+    else:
+        c = synth.kv_cache_q8(st.next(), st.next(), n_slots, n_kv, cap, d, filled)
+    return c, st
+
+
+def _run(qd, cache, kind, q, slots, n_ctx, scale, poison=False):
+    import torch
+    from quantized_decode_amd.tensors import dev, upload_cache
+    dkv = upload_cache(cache)
+    if poison:   # positions past n_ctx hold NaN / garbage: they must never reach the output
+        if kind == "f16":
+            for s in range(cache.k.shape[0]):
+                used = max(int(n) for b, n in enumerate(n_ctx) if slots[b] == s) if s in list(slots) else 0
+                dkv.k[s, :, used:] = float("nan")
+                dkv.v[s, :, :, used:] = float("nan")
+        else:
+            for s in range(cache.kq.shape[0]):
+                used = max(int(n) for b, n in enumerate(n_ctx) if slots[b] == s) if s in list(slots) else 0
+                dkv.k[s, :, used:] = 127
+                dkv.v[s, :, :, used:] = -127
+                dkv.k_scale[s, :, used:] = float("nan")
+                dkv.v_scale[s, :, used:] = float("inf")
+    b, hq, d = q.shape
+    qd_t = dev(q.view(np.uint16)).view(torch.float16)
+    o = torch.empty((b, hq, d), dtype=torch.float32, device="cuda")
+    o16 = torch.empty((b, hq, d), dtype=torch.float16, device="cuda")
+    w = ws(qd.qkdec_attn_workspace_size(b, hq, dkv.desc))
+    qd.qkdec_attn_decode(dkv.desc, dev(np.asarray(slots, np.int32)), dev(np.asarray(n_ctx, np.int32)), b, qd_t, hq,
+                         scale, o=o, o16=o16, workspace=w)
+    sync()
+    return o.cpu().numpy(), o16.cpu().numpy()
+
+
+CASES = [
+    # (kind, hq, hkv, d, cap, n_ctx per sequence)
+    ("f16", 8, 2, 64, 256, [1, 31]),
+    ("f16", 8, 2, 64, 256, [32, 33]),
+    ("f16", 8, 2, 64, 256, [127, 128]),
+    ("f16", 8, 2, 64, 256, [129, 256]),
+    ("f16", 32, 8, 128, 512, [1, 100, 128, 129, 300, 512]),
+    ("f16", 16, 1, 128, 384, [383, 257, 5]),
+    ("f16", 16, 16, 64, 160, [160, 65]),
+    ("f16", 32, 4, 128, 288, [200, 288]),
+    ("q8_0", 8, 2, 64, 256, [1, 31]),
+    ("q8_0", 8, 2, 64, 256, [129, 256]),
+    ("q8_0", 32, 8, 128, 512, [1, 100, 128, 129, 300, 512]),
+    ("q8_0", 16, 1, 128, 384, [383, 257, 5]),
+    ("q8_0", 32, 4, 128, 288, [200, 288]),
+]
+
+
+@pytest.mark.parametrize("kind,hq,hkv,d,cap,n_ctx", CASES)
+def test_attention_small(qd, kind, hq, hkv, d, cap, n_ctx):
+    bsz = len(n_ctx)
+    n_slots = bsz + 1
+    slots = list(np.random.default_rng(cap + bsz).permutation(n_slots)[:bsz])
+    filled = [0] * n_slots
+    for s, n in zip(slots, n_ctx):
+        filled[s] = n
+    cache, st = _make(kind, 50 + cap + d + hq, n_slots, hkv, cap, d, filled)
+    q = synth.f16_normal(st.next(), (bsz, hq, d))
+    scale = 1.0 / math.sqrt(d)
+    o, o16 = _run(qd, cache, kind, q, slots, n_ctx, scale, poison=True)
+    ref = OS.attention_batch(q.astype(np.float64), cache, kind, slots, n_ctx, scale)
+    assert_rel(o, ref, what=f"{kind} hq={hq} hkv={hkv} d={d} n={n_ctx}")
+    assert np.array_equal(o16, o.astype(np.float16))
+
+
+@pytest.mark.parametrize("kind", ["f16", "q8_0"])
+def test_attention_full_config(qd, kind):
+    # 32 query heads on 8 KV heads of 128, B = 8 sequences of 2400 tokens, one layer
+    bsz, hq, hkv, d, L = 8, 32, 8, 128, 2400
+    cap = 2432
+    cache, st = _make(kind, 2024, bsz, hkv, cap, d, [L] * bsz)
+    q = synth.f16_normal(st.next(), (bsz, hq, d))
+    slots = list(range(bsz))
+    o, _ = _run(qd, cache, kind, q, slots, [L] * bsz, 1 / math.sqrt(d))
+    ref = OS.attention_batch(q.astype(np.float64), cache, kind, slots, [L] * bsz, 1 / math.sqrt(d))
+    assert_rel(o, ref, what=f"{kind} full")
+
+
+def test_attention_ragged_lengths(qd):
+    bsz, hq, hkv, d = 8, 32, 8, 128
+    lens = synth.ragged_lengths(np.random.default_rng(4242), bsz)
+    cap = 8192
+    cache, st = _make("f16", 4243, bsz, hkv, cap, d, list(lens))
+    q = synth.f16_normal(st.next(), (bsz, hq, d))
+    o, _ = _run(qd, cache, "f16", q, list(range(bsz)), list(lens), 1 / math.sqrt(d))
+    ref = OS.attention_batch(q.astype(np.float64), cache, "f16", list(range(bsz)), list(lens), 1 / math.sqrt(d))
+    assert_rel(o, ref, what=f"ragged {list(lens)}")
+
+
+def test_attention_empty_sequence_gives_zero(qd):
+    cache, st = _make("f16", 77, 2, 2, 64, 64, [10, 64])
+    q = synth.f16_normal(st.next(), (2, 8, 64))
+    o, _ = _run(qd, cache, "f16", q, [0, 1], [0, 64], 0.125)
+    assert not o[0].any()
+    ref = OS.attention_batch(q[1:].astype(np.float64), cache, "f16", [1], [64], 0.125)
+    assert_rel(o[1:], ref)
+
+
+def test_attention_deterministic(qd):
+    cache, st = _make("q8_0", 78, 4, 8, 1024, 128, [1000, 17, 1024, 640])
+    q = synth.f16_normal(st.next(), (4, 32, 128))
+    o1, _ = _run(qd, cache, "q8_0", q, [0, 1, 2, 3], [1000, 17, 1024, 640], 0.088)
+    o2, _ = _run(qd, cache, "q8_0", q, [0, 1, 2, 3], [1000, 17, 1024, 640], 0.088)
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
