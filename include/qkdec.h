@@ -87,11 +87,13 @@ int32_t qkdec_abi_version(void);
  *
  * W: Q4_K matrix (format above).  X: fp16 [B][ldx] (ldx >= K, ldx % 8 == 0,
  * 16-byte aligned).  Y: fp32 [B][ldy] (ldy >= N).  residual: fp32 [B][ldr] or
- * NULL (then Y = product); it may alias Y.  1 <= B <= 16.
+ * NULL (then Y = product); it may alias Y.  1 <= B <= 16, N <= 2^20.
  * workspace: device memory of at least qkdec_gemm_q4k_workspace_size(N, K, B)
- * bytes, zeroed once with qkdec_workspace_init before its first use (holds
- * split-K partial sums and arrival counters; every call leaves the counters
- * zero again).  Calls that share a workspace must not overlap.
+ * bytes, zeroed once with qkdec_workspace_init before its first use (holds a
+ * fixed 64 KiB area of split-K arrival counters, then the partial sums; every
+ * call leaves the counters zero again, so one workspace serves calls of any
+ * shapes it is large enough for).  Calls that share a workspace must not
+ * overlap.
  * The K-chunk partial sums are added in a fixed order: results are
  * deterministic and independent of scheduling.
  */
@@ -261,8 +263,8 @@ qkdec_status qkdec_step_status(void* workspace, void* stream);
  * [B][hidden] (final RMSNorm output fed to the LM head), qkv fp32
  * [B][(n_q_heads + 2 n_kv_heads) head_dim] (projection before RoPE), q16 fp16
  * [B][n_q_heads head_dim] (rotated queries), o16 fp16 [B][n_q_heads head_dim]
- * (attention output), a fp32 [B][ffn] (SwiGLU activation, already rounded
- * by f16b).  Returns QKDEC_E_ARG/E_SHAPE on a model the step rejects. */
+ * (attention output), a fp32 [B][ffn] (SwiGLU activation before the f16b
+ * rounding, which the down projection applies as it reads it).  Returns QKDEC_E_ARG/E_SHAPE on a model the step rejects. */
 typedef struct {
   size_t x, h, qkv, q16, o16, a;
 } qkdec_step_views;

@@ -94,6 +94,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m quantized_decode_amd.build`")
+    # torch ships its own libamdhip64.so.7.  Loading it first makes the library's
+    # dependency of the same soname resolve to that copy; loaded the other way
+    # round, the process holds two HIP runtimes and launches on torch's memory fail.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     for name, (res, args) in _SIGNATURES.items():
         fn = getattr(lib, name)

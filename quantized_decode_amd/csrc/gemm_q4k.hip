@@ -13,7 +13,9 @@
 // accumulates in fp32.  The min term sum_s m_s * (sum of x over sub-block s)
 // is one v_mfma_f32_16x16x16_f16 per super-block whose A operand holds the
 // eight sub-block sums of x, each split into an fp16 hi + lo pair (about 22
-// significant bits), and whose B operand holds the integer mins.  Per
+// significant bits; a super-block whose sums exceed fp16's range has them
+// divided by 32 and dmin multiplied by 32), and whose B operand holds the
+// integer mins.  Per
 // super-block and weight row the two results are scaled by d and dmin in fp32.
 // No weight is ever rounded.
 //
@@ -160,7 +162,9 @@ __global__ void __launch_bounds__(256) gemm_q4k_kernel(
     float* part, unsigned* counters) {
   constexpr int P = KC < 4 ? KC : 4;   // super-blocks resident per wave (P - 1 in flight)
   extern __shared__ half_t xs[];        // [B][KC*256 + 8] activations, then [B][KC][16] x sums
-  __shared__ int xexp[16 * 16];         // XF32: offset of (row b, super-block i) at b * KC + i
+  // per (super-block i, row b) at i * 16 + b: the factors that d and dmin are
+  // multiplied by (XF32 block offset; 32 where the x sums were staged divided by 32)
+  __shared__ float fac_d[16 * 16], fac_m[16 * 16];
   const int ldsx = KC * 256 + 8;
   half_t* xsum = xs + B * ldsx;
   const int lane = threadIdx.x & 63;
@@ -191,6 +195,7 @@ __global__ void __launch_bounds__(256) gemm_q4k_kernel(
   const int n_pieces = B * KC * 32;   // 8-value pieces
   for (int base = 0; base < n_pieces; base += 1024) {
     half8_t hv[4];
+    float xfk[4] = {1.f, 1.f, 1.f, 1.f};
     if constexpr (!XF32) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -226,12 +231,12 @@ __global__ void __launch_bounds__(256) gemm_q4k_kernel(
         for (int o = 16; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 32));
         const int sh = f16_block_shift(am);
         const float inv = exp2i(-sh);
+        xfk[k] = exp2i(sh);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           hv[k][e] = (half_t)(v[k][0][e] * inv);
           hv[k][4 + e] = (half_t)(v[k][1][e] * inv);
         }
-        if (idx < n_pieces && (col & 31) == 0) xexp[b * KC + (col >> 5)] = sh;
       }
     }
 #pragma unroll
@@ -244,18 +249,36 @@ __global__ void __launch_bounds__(256) gemm_q4k_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) ps += (float)hv[k][e];
       }
-      // a 32-value sub-block is 4 consecutive pieces = 4 consecutive threads
+      // a 32-value sub-block is 4 consecutive pieces = 4 consecutive threads,
+      // a super-block 32 consecutive threads
       ps += __shfl_xor(ps, 1);
       ps += __shfl_xor(ps, 2);
+      float ms = fabsf(ps);
+      ms = fmaxf(ms, __shfl_xor(ms, 4, 32));
+      ms = fmaxf(ms, __shfl_xor(ms, 8, 32));
+      ms = fmaxf(ms, __shfl_xor(ms, 16, 32));
+      // a super-block whose sub-block sums leave fp16's range stages them divided
+      // by 32 (32 values of at most 65504 then fit); dmin is multiplied back
+      const bool big = ms > 65504.f;
+      const float pss = big ? ps * 0.03125f : ps;
       if (idx < n_pieces && (col & 3) == 0) {
         const int sbl = col >> 5, sub = (col & 31) >> 2;   // super-block in chunk, sub-block 0..7
-        const half_t hs = (half_t)ps;
-        const half_t ls = (half_t)(ps - (float)hs);
+        const half_t hs = (half_t)pss;
+        const half_t ls = (half_t)(pss - (float)hs);
         half_t* dst = xsum + (b * KC + sbl) * 16 + 4 * (sub >> 1) + (sub & 1);
         dst[0] = hs;
         dst[2] = ls;
+        if ((col & 31) == 0) {
+          fac_d[sbl * 16 + b] = xfk[k];
+          fac_m[sbl * 16 + b] = big ? 32.f * xfk[k] : xfk[k];
+        }
       }
     }
+  }
+  for (int t = threadIdx.x; t < (16 - B) * KC; t += 256) {
+    const int i = t / (16 - B), b = B + t % (16 - B);
+    fac_d[i * 16 + b] = 1.f;
+    fac_m[i * 16 + b] = 1.f;
   }
   __syncthreads();
 
@@ -264,7 +287,7 @@ __global__ void __launch_bounds__(256) gemm_q4k_kernel(
   const half_t* xr = xs + xrow * ldsx + 64 * g;
   floatx4 acc[TW], psq[TW], psm[TW];
   float pd[TW], pdm[TW];
-  floatx4 pxf = {1.f, 1.f, 1.f, 1.f};
+  floatx4 pfd = {1.f, 1.f, 1.f, 1.f}, pfm = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
   for (int t = 0; t < TW; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -279,26 +302,21 @@ __global__ void __launch_bounds__(256) gemm_q4k_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) av[j] = *reinterpret_cast<const half8_t*>(xr + 256 * i + 8 * j);
     const half4_t axs = *reinterpret_cast<const half4_t*>(xsum + (xrow * KC + i) * 16 + 4 * g);
-    floatx4 xf = {1.f, 1.f, 1.f, 1.f};
-    if constexpr (XF32) {
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int b = 4 * g + ii;
-        xf[ii] = exp2i(xexp[(b < B ? b : B - 1) * KC + i]);
-      }
-    }
+    const floatx4 fm = *reinterpret_cast<const floatx4*>(fac_m + i * 16 + 4 * g);
+    floatx4 fd = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (XF32) fd = *reinterpret_cast<const floatx4*>(fac_d + i * 16 + 4 * g);
     floatx4 sq[TW], sm[TW];
     float d[TW], dm[TW];
 #pragma unroll
     for (int t = 0; t < TW; ++t) q4_superblock(fr[i % P][t], av, axs, g, km, sq[t], sm[t], d[t], dm[t]);
     // accumulate the previous super-block now that its MFMAs are long done;
-    // d * xf and dmin * xf are exact (xf is a power of two)
+    // d * fd and dmin * fm are exact (the factors are powers of two)
     if (i > 0) {
 #pragma unroll
       for (int t = 0; t < TW; ++t)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
-          acc[t][ii] = __builtin_fmaf(pd[t] * pxf[ii], psq[t][ii], __builtin_fmaf(-pdm[t] * pxf[ii], psm[t][ii], acc[t][ii]));
+          acc[t][ii] = __builtin_fmaf(pd[t] * pfd[ii], psq[t][ii], __builtin_fmaf(-pdm[t] * pfm[ii], psm[t][ii], acc[t][ii]));
     }
 #pragma unroll
     for (int t = 0; t < TW; ++t) {
@@ -307,13 +325,14 @@ __global__ void __launch_bounds__(256) gemm_q4k_kernel(
       pd[t] = d[t];
       pdm[t] = dm[t];
     }
-    pxf = xf;
+    pfd = fd;
+    pfm = fm;
   }
 #pragma unroll
   for (int t = 0; t < TW; ++t)
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii)
-      acc[t][ii] = __builtin_fmaf(pd[t] * pxf[ii], psq[t][ii], __builtin_fmaf(-pdm[t] * pxf[ii], psm[t][ii], acc[t][ii]));
+      acc[t][ii] = __builtin_fmaf(pd[t] * pfd[ii], psq[t][ii], __builtin_fmaf(-pdm[t] * pfm[ii], psm[t][ii], acc[t][ii]));
 
   __shared__ int s_last;
   if (n_chunks > 1) {
@@ -452,22 +471,27 @@ GemmShape gemm_shape(int64_t n_tiles, int64_t kb, int B, bool swiglu) {
   const int64_t groups = n_groups_of(n_tiles, tw, swiglu);
   for (int kc : cands) {
     if (kb % kc) continue;
-    if (lds_bytes(B, kc) > 48 * 1024) continue;
+    // sized for max(B, 8) so that every batch of up to 8 sequences uses the same
+    // K chunking: a sequence's outputs then do not depend on its batch-mates
+    if (lds_bytes(B > 8 ? B : 8, kc) > 48 * 1024) continue;
     if (groups * (kb / kc) < 192 && kc > 1) continue;
     return {tw, kc};
   }
   return {tw, 1};
 }
 
-static size_t counters_bytes(int64_t n_groups) { return (size_t)(n_groups * 4 + 255) / 256 * 256 + 256; }
+// The split-K arrival counters occupy a fixed area at the start of the
+// workspace, so that calls of different shapes can share one workspace (each
+// last arriver returns its counter to zero; the partial sums of one call then
+// never land on another call's counters).
+static size_t counters_bytes() { return (size_t)kGemmMaxGroups * 4; }
 
 size_t gemm_workspace_bytes(int64_t n_rows, int64_t K, int B, bool swiglu) {
   const int64_t kb = K / 256;
   const int64_t n_tiles = n_rows / 16;
   const GemmShape gs = gemm_shape(n_tiles, kb, B, swiglu);
-  const int64_t n_groups = n_groups_of(n_tiles, gs.tw, swiglu);
   const int64_t chunks = kb / gs.kc;
-  size_t bytes = counters_bytes(n_groups);
+  size_t bytes = counters_bytes();
   if (chunks > 1) bytes += (size_t)chunks * B * n_rows * 4;
   return bytes;
 }
@@ -495,10 +519,10 @@ static hipError_t launch_chunked(int kc, dim3 grid, size_t lds, hipStream_t st, 
   return hipGetLastError();
 }
 
-static void carve(void* ws, int64_t n_groups, unsigned** counters, float** part) {
+static void carve(void* ws, unsigned** counters, float** part) {
   char* p = reinterpret_cast<char*>(ws);
   *counters = reinterpret_cast<unsigned*>(p);
-  *part = reinterpret_cast<float*>(p + counters_bytes(n_groups));
+  *part = reinterpret_cast<float*>(p + counters_bytes());
 }
 
 static hipError_t gemm_run(const void* W, int64_t n_tiles, int64_t K, const void* X, bool x_f32, int64_t ldx, int B,
@@ -510,7 +534,7 @@ static hipError_t gemm_run(const void* W, int64_t n_tiles, int64_t K, const void
   const int64_t n_groups = n_groups_of(n_tiles, gs.tw, swiglu);
   unsigned* counters;
   float* part;
-  carve(ws, n_groups, &counters, &part);
+  carve(ws, &counters, &part);
   const dim3 grid((unsigned)n_groups, (unsigned)(kb / gs.kc));
   const size_t lds = lds_bytes(B, gs.kc);
   const uint8_t* w = reinterpret_cast<const uint8_t*>(W);

@@ -27,6 +27,12 @@ hipError_t launch_dequant_q4k(const void* W, int64_t n_blocks, float* out, hipSt
 
 // ---- attention (attn_decode.hip)
 // tokens per split work item
+// Largest number of row groups (work-groups along N) of one Q4_K GEMM launch:
+// 4 tiles of 16 rows per group, so N <= 16 * 4 * kGemmMaxGroups = 2^20 rows
+// (a SwiGLU launch covers gate and up: 2F <= 2^20).
+constexpr int kGemmMaxGroups = 16384;
+constexpr int64_t kGemmMaxRows = 16 * 4 * (int64_t)kGemmMaxGroups;
+
 constexpr int kAttnChunk = 128;
 inline int attn_n_splits(int capacity) { return (capacity + kAttnChunk - 1) / kAttnChunk; }
 // partial results per (b, q head, split): m, l, then head_dim values of o

@@ -33,7 +33,7 @@ qkdec_status check_gemm(const void* W, int64_t N, int64_t K, const uint16_t* X, 
   if (!W || !X) return QKDEC_E_ARG;
   if (B < 1 || B > 16) return QKDEC_E_SHAPE;
   if (N <= 0 || K <= 0 || N % 16 != 0 || K % 256 != 0) return QKDEC_E_SHAPE;
-  if (N / 16 > (int64_t)1 << 30 || K / 256 > (int64_t)1 << 20) return QKDEC_E_SHAPE;
+  if (N > kGemmMaxRows || K / 256 > (int64_t)1 << 20) return QKDEC_E_SHAPE;
   if (ldx < K) return QKDEC_E_SHAPE;
   if (!aligned(W, 16) || !aligned(X, 16) || ldx % 8 != 0) return QKDEC_E_ALIGN;
   return QKDEC_OK;
@@ -69,6 +69,9 @@ qkdec_status check_model(const qkdec_model* m, const qkdec_kv_layer* kv) {
     return QKDEC_E_SHAPE;
   if (m->head_dim != 64 && m->head_dim != 128) return QKDEC_E_SHAPE;
   if (((int64_t)m->n_q_heads * m->head_dim) % 256 != 0) return QKDEC_E_SHAPE;
+  if ((int64_t)(m->n_q_heads + 2 * m->n_kv_heads) * m->head_dim > kGemmMaxRows || 2 * (int64_t)m->ffn > kGemmMaxRows ||
+      m->hidden > kGemmMaxRows)
+    return QKDEC_E_SHAPE;
   if (!(m->rms_eps >= 0.f) || !(m->rope_base > 0.f)) return QKDEC_E_ARG;
   if (!aligned(m->embed, 16) || !aligned(m->lm_head, 16)) return QKDEC_E_ALIGN;
   for (int l = 0; l < m->n_layers; ++l) {
@@ -206,7 +209,7 @@ qkdec_status qkdec_gemm_q4k_xf32(const void* W, int64_t N, int64_t K, const floa
   if (!W || !X) return QKDEC_E_ARG;
   if (B < 1 || B > 16) return QKDEC_E_SHAPE;
   if (N <= 0 || K <= 0 || N % 16 != 0 || K % 256 != 0) return QKDEC_E_SHAPE;
-  if (N / 16 > (int64_t)1 << 30 || K / 256 > (int64_t)1 << 20) return QKDEC_E_SHAPE;
+  if (N > kGemmMaxRows || K / 256 > (int64_t)1 << 20) return QKDEC_E_SHAPE;
   if (ldx < K) return QKDEC_E_SHAPE;
   if (!aligned(W, 16) || !aligned(X, 16) || ldx % 4 != 0) return QKDEC_E_ALIGN;
   if (!Y) return QKDEC_E_ARG;

@@ -111,6 +111,23 @@ def test_gemm_strided_operands(qd):
     assert_rel(got[:, :n], OO.q4k_gemm(mat, n, k, xfull[:, :k]), what="strided")
 
 
+@pytest.mark.parametrize("b", [3, 16])
+def test_gemm_wide_range_fp16_activations(qd, b):
+    # fp16 activations from 1e-4 up to the format's maximum, per 256-value block: the
+    # sums of 32 of them leave fp16's range in the large blocks and must still be exact
+    n, k = 512, 2048
+    st = synth.Streams(70 + b)
+    mat = synth.q4k_matrix(st.next(), n, k)
+    rng = st.next()
+    mag = 10.0 ** rng.uniform(-4, np.log10(65504.0), (b, k // 256)).repeat(256, axis=1)
+    x = np.clip(rng.uniform(-1, 1, (b, k)) * mag, -65504, 65504).astype(np.float16)
+    x[0, :256] = np.float16(65504.0)
+    x[-1, 256:512] = np.float16(-65504.0)
+    got = _run_gemm(qd, mat, n, k, x)
+    ref = OO.q4k_gemm(mat, n, k, x.astype(np.float64))
+    assert_rel(got, ref, what=f"wide-range fp16 activations, B={b}")
+
+
 def test_gemm_deterministic_and_batch_invariant(qd):
     n, k = 4096, 12288
     st = synth.Streams(33)
@@ -123,6 +140,41 @@ def test_gemm_deterministic_and_batch_invariant(qd):
     for b in (0, 5):
         yb = _run_gemm(qd, mat, n, k, x[b:b + 1])
         assert np.array_equal(yb[0].view(np.uint32), y1[b].view(np.uint32))
+
+
+def test_gemm_workspace_shared_across_shapes(qd):
+    # one workspace, used in turn by launches of different shapes (as inside a decode
+    # step): every launch's split-K bookkeeping must survive the others' partial sums
+    import torch
+    b = 8
+    st = synth.Streams(44)
+    shapes = [(6144, 4096), (4096, 4096), (4096, 12288)]
+    mats = [synth.q4k_matrix(st.next(), n, k) for n, k in shapes]
+    xs = [synth.f16_normal(st.next(), (b, k)) for _, k in shapes]
+    f = 12288
+    gmat = synth.q4k_matrix(st.next(), 2 * f, 4096)
+    gx = synth.f16_normal(st.next(), (b, 4096))
+    need = max([qd.qkdec_gemm_q4k_workspace_size(n, k, b) for n, k in shapes] +
+               [qd.qkdec_gemm_q4k_swiglu_workspace_size(f, 4096, b)])
+    w = ws(need)
+    ga = torch.empty((b, f), dtype=torch.float32, device="cuda")
+    for rep in range(2):
+        for (n, k), mat, x in zip(shapes, mats, xs):
+            y = torch.empty((b, n), dtype=torch.float32, device="cuda")
+            qd.qkdec_gemm_q4k(_dev(mat.reshape(-1)), n, k, _x16(x), b, y, workspace=w)
+            sync()
+            rows = np.unique(np.concatenate([np.arange(64), np.arange(n - 64, n),
+                                             np.random.default_rng(n + k).integers(0, n, 128)]))
+            ref = x.astype(np.float64) @ OF.q4k_dequant_rows(mat, n, k, rows=rows).T
+            assert_rel(y.cpu().numpy()[:, rows], ref, what=f"shared workspace {n}x{k}, pass {rep}")
+        qd.qkdec_gemm_q4k_swiglu(_dev(gmat.reshape(-1)), f, 4096, _x16(gx), b, ga, workspace=w)
+        sync()
+        cols = np.unique(np.concatenate([np.arange(32), np.arange(f - 32, f),
+                                         np.random.default_rng(f).integers(0, f, 96)]))
+        wd = OF.q4k_dequant_rows(gmat, 2 * f, 4096, rows=np.concatenate([cols, f + cols]))
+        gu = gx.astype(np.float64) @ wd.T
+        ref = OO.swiglu(gu[:, :cols.size], gu[:, cols.size:])
+        assert_rel(ga.cpu().numpy()[:, cols], ref, what=f"shared workspace SwiGLU, pass {rep}")
 
 
 @pytest.mark.parametrize("f,k,b", [(1536, 512, 2), (1536, 512, 16), (12288, 4096, 8), (12288, 4096, 1),
