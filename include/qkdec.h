@@ -212,7 +212,8 @@ qkdec_status qkdec_lm_head_argmax(const uint16_t* Wlm, int64_t V, int64_t H, con
  * [(n_q_heads + 2 n_kv_heads) head_dim x hidden] (rows: q heads, k heads, v
  * heads), w_o Q4_K [hidden x n_q_heads head_dim], w_gate_up Q4_K
  * [2 ffn x hidden] (rows: gate, up), w_down Q4_K [hidden x ffn], norm gains
- * fp32 [hidden].  embed, lm_head fp16 [vocab][hidden]. */
+ * fp32 [hidden].  embed, lm_head fp16 [vocab][hidden].  hidden % 256 == 0
+ * and hidden <= 8192; ffn % 256 == 0; vocab % 16 == 0. */
 typedef struct {
   const void* w_qkv;
   const void* w_o;

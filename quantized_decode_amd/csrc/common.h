@@ -74,6 +74,52 @@ __device__ __forceinline__ uint16_t f64_to_f16_bits(double x) {
   return sign | (uint16_t)bits;
 }
 
+
+// ---- sum-of-squares slots for the fused RMSNorm.
+// A residual-stream row of width H is covered by H/64 slots of 64 columns;
+// slot s of row b is ss[s * 16 + b].  The kernel that writes a row also
+// writes its slots; a consumer folds them in a fixed order (deterministic).
+constexpr int kSsCols = 64;
+constexpr int kSsMaxSlots = 128;   // H <= 8192
+
+// Per-thread share of the fold in two halves, so that the loads can be
+// issued early and the adds done later: thread t of a 256-thread block covers
+// row t % 16 and slots t/16, t/16 + 16, ...
+__device__ __forceinline__ void ss_thread_load(const float* __restrict__ ss, int n_slots,
+                                               float (&v)[kSsMaxSlots / 16]) {
+  const int b = threadIdx.x & 15, s0 = threadIdx.x >> 4;
+#pragma unroll
+  for (int j = 0; j < kSsMaxSlots / 16; ++j) {
+    const int s = s0 + 16 * j;
+    v[j] = ss[(s < n_slots ? s : n_slots - 1) * 16 + b];
+  }
+}
+__device__ __forceinline__ float ss_thread_sum(const float (&v)[kSsMaxSlots / 16], int n_slots) {
+  const int s0 = threadIdx.x >> 4;
+  float p = 0.f;
+#pragma unroll
+  for (int j = 0; j < kSsMaxSlots / 16; ++j) p += (s0 + 16 * j < n_slots) ? v[j] : 0.f;
+  return p;
+}
+
+// Second half of the fold: combine the 16 thread parts of each row within a
+// wave, then write one value per (wave, row) to red[4][16].  The caller
+// synchronizes the block before rms_inv().
+__device__ __forceinline__ void ss_wave_fold(float p, float (*red)[16]) {
+  p += __shfl_xor(p, 16);
+  p += __shfl_xor(p, 32);
+  const int lane = threadIdx.x & 63;
+  if (lane < 16) red[threadIdx.x >> 6][lane] = p;
+}
+
+__device__ __forceinline__ float rms_inv(const float (*red)[16], int b, float inv_h, float eps) {
+  const float tot = (red[0][b] + red[1][b]) + (red[2][b] + red[3][b]);
+  return 1.0f / sqrtf(tot * inv_h + eps);
+}
+
+// h = f16(x * rinv * gamma), the one RMSNorm rounding used everywhere
+__device__ __forceinline__ half_t norm_apply(float x, float rinv, float gamma) { return (half_t)((x * rinv) * gamma); }
+
 __device__ __forceinline__ double f16_bits_to_f64(uint16_t b) {
   return (double)__builtin_bit_cast(half_t, b);
 }

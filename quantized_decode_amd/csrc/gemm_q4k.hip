@@ -31,6 +31,8 @@
 // (w & 0x00F000F0) -> 8j+2, 8j+3 (times 16); the same on w >> 8 -> 8j+4..8j+7.
 // OR-ing 0x6400 makes each half the fp16 value 1024 + q (or 1024 + 16q); one
 // packed FMA with (sc, -1024 sc) (or (sc/16, -64 sc)) yields sc*q exactly.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -124,49 +126,80 @@ __device__ __forceinline__ int f16_block_shift(float amax) {
   return sh;
 }
 
-// Tile handled by slot t (0..TW-1) of wave w in row group rg.
-//   MODE 0: consecutive tiles, 4*TW per work-group.
-//   MODE 1 (SwiGLU), TW = 2: slot 0 = gate tile 4rg + w, slot 1 = the up tile F/16 later.
-//   MODE 1, TW = 1: waves 0, 1 = gate tiles 2rg, 2rg + 1; waves 2, 3 = their up tiles.
-template <int MODE, int TW>
-__device__ __forceinline__ int tile_of(int rg, int w, int t, int f_tiles) {
-  if (MODE == 0) return (rg * 4 + w) * TW + t;
-  if (TW == 2) return (t == 0) ? (rg * 4 + w) : (f_tiles + rg * 4 + w);
-  return (w < 2) ? (rg * 2 + w) : (f_tiles + rg * 2 + (w - 2));
+// Tile of wave w in row group rg (WPB waves per work-group).
+//   MODE 0: tiles WPB*rg .. WPB*rg + WPB - 1 (one per wave).
+//   MODE 1 (SwiGLU): waves 0 .. H-1 (H = WPB/2) take gate tiles H*rg + w, waves
+//   H .. WPB-1 the up tiles F/16 later, so one work-group holds both halves of
+//   16*H outputs.
+template <int MODE, int WPB>
+__device__ __forceinline__ int tile_of(int rg, int w, int f_tiles) {
+  constexpr int H = WPB / 2;
+  if (MODE == 0) return rg * WPB + w;
+  return (w < H) ? (rg * H + w) : (f_tiles + rg * H + (w - H));
 }
-template <int MODE, int TW>
-__device__ __forceinline__ bool tile_valid(int rg, int w, int t, int n_tiles, int f_tiles) {
-  if (MODE == 0) return tile_of<MODE, TW>(rg, w, t, f_tiles) < n_tiles;
-  if (TW == 2) return rg * 4 + w < f_tiles;
-  return rg * 2 + (w & 1) < f_tiles;
+template <int MODE, int WPB>
+__device__ __forceinline__ bool tile_valid(int rg, int w, int n_tiles, int f_tiles) {
+  constexpr int H = WPB / 2;
+  if (MODE == 0) return rg * WPB + w < n_tiles;
+  return rg * H + (w % H) < f_tiles;
 }
 
-// Work-group: 4 waves, TW 16-row tiles each, covering super-blocks
-// [c*KC, c*KC + KC) of K (c = blockIdx.y).  The work-group's activations
-// (and their sub-block sums) are staged once in LDS and shared by its tiles.
-// Each wave streams its tiles' super-blocks (2304 contiguous bytes each) with
-// P - 1 of them in flight; a super-block's products are accumulated one
-// super-block later, so the wave keeps issuing while its MFMAs finish.  With
+// How the activations arrive.
+enum XMode : int {
+  kXF16 = 0,         // fp16, used as they are
+  kXF32Blocked = 1,  // fp32, rounded to fp16 with one power-of-two offset per row and 256 values
+  kXNorm = 2,        // fp32 residual stream, RMSNorm applied while staging: f16(x * rinv * gamma)
+};
+
+struct GemmArgs {
+  const uint8_t* W;
+  const void* X;
+  const float* gamma;    // kXNorm: gains of the K inputs
+  const float* ss_in;    // kXNorm: sum-of-squares slots of the rows of X
+  float* Y;              // MODE 0 output (may alias residual)
+  const float* residual;
+  float* ss_out;         // MODE 0: sum-of-squares slots of Y (one slot per work-group), or null
+  float* A;              // MODE 1 output
+  float* part;           // split-K partial sums
+  unsigned* counters;    // split-K arrival counters (one per row group)
+  int64_t ldx, ldy, ldr, lda;
+  int n_tiles, kb, B, f_tiles, ss_slots;
+  float eps, inv_k;
+};
+
+// Work-group: WPB waves, one 16-row tile each, covering super-blocks
+// [c*KC, c*KC + KC) of K (c = blockIdx.y).  More waves per work-group share
+// one staged copy of the activations: each work-group reads B*KC*256
+// activations for 16*WPB*KC*256 weights.
+//
+// The prologue issues every load the work-group can hold before waiting on
+// any: the RMSNorm statistics and gains (kXNorm), the first round of
+// activations, then the weights of the first P super-blocks of each wave's
+// tile (2304 contiguous bytes each; P = min(KC, 8), 4 with 16 waves).
+// Activations are staged once in LDS as fp16 together with the fp32 sum of
+// every 32-value sub-block (split hi/lo for the min-term MFMA) and shared by
+// the work-group's tiles.  The main loop decodes and multiplies one
+// super-block per step and accumulates the previous step's products, so MFMA
+// results are never waited on.  With
 // several K chunks every work-group writes its partial sums with write-through
 // stores and the last one to arrive for a row group adds the chunks in chunk
 // order (so the result does not depend on arrival order).
-//
-// XF32: the activations arrive in fp32 and are rounded to fp16 while staged,
-// per row and 256-value block with the smallest power-of-two offset that
-// keeps the block inside fp16's range (0 whenever plain fp16 fits); the
-// offsets are multiplied back exactly per super-block.
-template <int KC, int MODE, bool XF32, int TW>
-__global__ void __launch_bounds__(256) gemm_q4k_kernel(
-    const uint8_t* __restrict__ W, int n_tiles, int kb, const void* __restrict__ Xv, int64_t ldx, int B,
-    float* Y, int64_t ldy, const float* residual, int64_t ldr, float* __restrict__ A, int64_t lda, int f_tiles,
-    float* part, unsigned* counters) {
-  constexpr int P = KC < 4 ? KC : 4;   // super-blocks resident per wave (P - 1 in flight)
-  extern __shared__ half_t xs[];        // [B][KC*256 + 8] activations, then [B][KC][16] x sums
-  // per (super-block i, row b) at i * 16 + b: the factors that d and dmin are
-  // multiplied by (XF32 block offset; 32 where the x sums were staged divided by 32)
-  __shared__ float fac_d[16 * 16], fac_m[16 * 16];
+template <int KC, int MODE, int XMODE, int WPB>
+__global__ void __launch_bounds__(64 * WPB) gemm_q4k_kernel(const GemmArgs a) {
+  constexpr int NT = 64 * WPB;                           // threads
+  // super-blocks in flight per wave (fewer with 16 waves, which leave 128 registers per lane)
+  constexpr int PMAX = WPB == 16 ? 4 : 8;
+  constexpr int P = KC < PMAX ? KC : PMAX;
+  constexpr int XB = WPB == 16 ? 2 : (XMODE == kXF16 ? 8 : 4);   // activation pieces (8 values) per thread and round
+  constexpr int GL = (KC * 64 + NT - 1) / NT;            // kXNorm: float4 of gains per thread
+  // dynamic LDS: [B][KC*256 + 8] fp16 activations, [B][KC][16] x sums, kXNorm: [KC*256] fp32 gains
+  extern __shared__ half_t xs[];
+  __shared__ float fac_d[16 * 16], fac_m[16 * 16];       // per (super-block i, row b) at i * 16 + b
+  __shared__ float s_red[WPB][16];
+  const int B = a.B;
   const int ldsx = KC * 256 + 8;
   half_t* xsum = xs + B * ldsx;
+  float* gls = reinterpret_cast<float*>(xsum + B * KC * 16);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4;
@@ -175,79 +208,100 @@ __global__ void __launch_bounds__(256) gemm_q4k_kernel(
   const int c = blockIdx.y;
   const int n_chunks = gridDim.y;
   const int sb0 = c * KC;
+  const int n_pieces = B * KC * 32;
 
-  const uint8_t* tbase[TW];
-  bool tok[TW];
+  const bool tok = tile_valid<MODE, WPB>(rg, wave, a.n_tiles, a.f_tiles);
+  const int tl = tok ? tile_of<MODE, WPB>(rg, wave, a.f_tiles) : 0;   // keep addresses in bounds
+  const uint8_t* tbase = a.W + ((size_t)tl * a.kb + sb0) * 2304 + (size_t)r * 144;
+
+  // ---- prologue: loads in the order they are needed
+  float ssv[kSsMaxSlots / 16];
+  floatx4 gv[GL];
+  if constexpr (XMODE == kXNorm) {
+    if (threadIdx.x < 256) ss_thread_load(a.ss_in, a.ss_slots, ssv);
 #pragma unroll
-  for (int t = 0; t < TW; ++t) {
-    tok[t] = tile_valid<MODE, TW>(rg, wave, t, n_tiles, f_tiles);
-    const int tl = tok[t] ? tile_of<MODE, TW>(rg, wave, t, f_tiles) : 0;   // keep addresses in bounds
-    tbase[t] = W + ((size_t)tl * kb + sb0) * 2304 + (size_t)r * 144;
+    for (int k = 0; k < GL; ++k) {
+      const int idx = threadIdx.x + NT * k;
+      const int idc = idx < KC * 64 ? idx : KC * 64 - 1;
+      gv[k] = *reinterpret_cast<const floatx4*>(a.gamma + (size_t)sb0 * 256 + 4 * idc);
+    }
   }
-  Q4Frag fr[P][TW];
+  half8_t hv[XB];
+  floatx4 xv[XB][2];
+  auto load_round = [&](int base) {
 #pragma unroll
-  for (int p = 0; p < P - 1; ++p)
+    for (int k = 0; k < XB; ++k) {
+      int idx = base + threadIdx.x + NT * k;
+      idx = idx < n_pieces ? idx : n_pieces - 1;
+      const int b = idx / (KC * 32), col = idx % (KC * 32);
+      if constexpr (XMODE == kXF16) {
+        hv[k] = *reinterpret_cast<const half8_t*>(reinterpret_cast<const half_t*>(a.X) + (size_t)b * a.ldx +
+                                                  (size_t)sb0 * 256 + 8 * col);
+      } else {
+        const float* src = reinterpret_cast<const float*>(a.X) + (size_t)b * a.ldx + (size_t)sb0 * 256 + 8 * col;
+        xv[k][0] = *reinterpret_cast<const floatx4*>(src);
+        xv[k][1] = *reinterpret_cast<const floatx4*>(src + 4);
+      }
+    }
+  };
+  load_round(0);
+  __builtin_amdgcn_sched_barrier(0);
+  Q4Frag fr[P];
 #pragma unroll
-    for (int t = 0; t < TW; ++t) load_frag(fr[p][t], tbase[t] + (size_t)p * 2304, g);
+  for (int p = 0; p < P; ++p) load_frag(fr[p], tbase + (size_t)p * 2304, g);
+  __builtin_amdgcn_sched_barrier(0);
 
-  // ---- activations of this chunk -> LDS (fp16), with the fp32 sum of every
-  // 32-value sub-block split into an fp16 hi/lo pair for the min-term MFMA.
-  const int n_pieces = B * KC * 32;   // 8-value pieces
-  for (int base = 0; base < n_pieces; base += 1024) {
-    half8_t hv[4];
-    float xfk[4] = {1.f, 1.f, 1.f, 1.f};
-    if constexpr (!XF32) {
+  if constexpr (XMODE == kXNorm) {
+    if (threadIdx.x < 256) ss_wave_fold(ss_thread_sum(ssv, a.ss_slots), s_red);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int idx = base + threadIdx.x + 256 * k;
-        if (idx < n_pieces) {
-          const int b = idx / (KC * 32), col = idx % (KC * 32);
-          hv[k] = *reinterpret_cast<const half8_t*>(reinterpret_cast<const half_t*>(Xv) + (size_t)b * ldx +
-                                                    (size_t)sb0 * 256 + 8 * col);
+    for (int k = 0; k < GL; ++k) {
+      const int idx = threadIdx.x + NT * k;
+      if (idx < KC * 64) *reinterpret_cast<floatx4*>(gls + 4 * idx) = gv[k];
+    }
+    __syncthreads();
+  }
+
+  // ---- activations -> LDS (fp16) with the sub-block sums
+  for (int base = 0; base < n_pieces; base += NT * XB) {
+    if (base > 0) load_round(base);
+#pragma unroll
+    for (int k = 0; k < XB; ++k) {
+      const int idx = base + threadIdx.x + NT * k;
+      const bool valid = idx < n_pieces;
+      const int idc = valid ? idx : n_pieces - 1;
+      const int b = idc / (KC * 32), col = idc % (KC * 32);
+      half8_t h;
+      float xfk = 1.f;
+      if constexpr (XMODE == kXF16) {
+        h = hv[k];
+      } else if constexpr (XMODE == kXNorm) {
+        const float rinv = rms_inv(s_red, b, a.inv_k, a.eps);
+        const float* gr = gls + 8 * col;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          h[e] = norm_apply(xv[k][0][e], rinv, gr[e]);
+          h[4 + e] = norm_apply(xv[k][1][e], rinv, gr[4 + e]);
         }
-      }
-    } else {
-      floatx4 v[4][2];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int idx = base + threadIdx.x + 256 * k;
-        if (idx < n_pieces) {
-          const int b = idx / (KC * 32), col = idx % (KC * 32);
-          const float* src = reinterpret_cast<const float*>(Xv) + (size_t)b * ldx + (size_t)sb0 * 256 + 8 * col;
-          v[k][0] = *reinterpret_cast<const floatx4*>(src);
-          v[k][1] = *reinterpret_cast<const floatx4*>(src + 4);
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      } else {
         // the 32 pieces of one (row, super-block) are 32 consecutive threads
-        const int idx = base + threadIdx.x + 256 * k;
-        const int b = idx / (KC * 32), col = idx % (KC * 32);
         float am = 0.f;
-        if (idx < n_pieces) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) am = fmaxf(am, fmaxf(fabsf(v[k][0][e]), fabsf(v[k][1][e])));
-        }
+        for (int e = 0; e < 4; ++e) am = fmaxf(am, fmaxf(fabsf(xv[k][0][e]), fabsf(xv[k][1][e])));
         for (int o = 16; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 32));
         const int sh = f16_block_shift(am);
         const float inv = exp2i(-sh);
-        xfk[k] = exp2i(sh);
+        xfk = exp2i(sh);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          hv[k][e] = (half_t)(v[k][0][e] * inv);
-          hv[k][4 + e] = (half_t)(v[k][1][e] * inv);
+          h[e] = (half_t)(xv[k][0][e] * inv);
+          h[4 + e] = (half_t)(xv[k][1][e] * inv);
         }
       }
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int idx = base + threadIdx.x + 256 * k;
-      const int b = idx / (KC * 32), col = idx % (KC * 32);
       float ps = 0.f;
-      if (idx < n_pieces) {
-        *reinterpret_cast<half8_t*>(xs + b * ldsx + 8 * col) = hv[k];
+      if (valid) {
+        *reinterpret_cast<half8_t*>(xs + b * ldsx + 8 * col) = h;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ps += (float)hv[k][e];
+        for (int e = 0; e < 8; ++e) ps += (float)h[e];
       }
       // a 32-value sub-block is 4 consecutive pieces = 4 consecutive threads,
       // a super-block 32 consecutive threads
@@ -261,7 +315,7 @@ __global__ void __launch_bounds__(256) gemm_q4k_kernel(
       // by 32 (32 values of at most 65504 then fit); dmin is multiplied back
       const bool big = ms > 65504.f;
       const float pss = big ? ps * 0.03125f : ps;
-      if (idx < n_pieces && (col & 3) == 0) {
+      if (valid && (col & 3) == 0) {
         const int sbl = col >> 5, sub = (col & 31) >> 2;   // super-block in chunk, sub-block 0..7
         const half_t hs = (half_t)pss;
         const half_t ls = (half_t)(pss - (float)hs);
@@ -269,152 +323,184 @@ __global__ void __launch_bounds__(256) gemm_q4k_kernel(
         dst[0] = hs;
         dst[2] = ls;
         if ((col & 31) == 0) {
-          fac_d[sbl * 16 + b] = xfk[k];
-          fac_m[sbl * 16 + b] = big ? 32.f * xfk[k] : xfk[k];
+          fac_d[sbl * 16 + b] = xfk;
+          fac_m[sbl * 16 + b] = big ? 32.f * xfk : xfk;
         }
       }
     }
   }
-  for (int t = threadIdx.x; t < (16 - B) * KC; t += 256) {
+  for (int t = threadIdx.x; t < (16 - B) * KC; t += NT) {
     const int i = t / (16 - B), b = B + t % (16 - B);
     fac_d[i * 16 + b] = 1.f;
     fac_m[i * 16 + b] = 1.f;
   }
   __syncthreads();
 
+  // ---- main loop
   const NibbleMasks km = {in_vgpr(0x000F000Fu), in_vgpr(0x00F000F0u), in_vgpr(0x64006400u)};
   const int xrow = r < B ? r : B - 1;
   const half_t* xr = xs + xrow * ldsx + 64 * g;
-  floatx4 acc[TW], psq[TW], psm[TW];
-  float pd[TW], pdm[TW];
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  floatx4 psq, psm;
+  float pd = 0.f, pdm = 0.f;
   floatx4 pfd = {1.f, 1.f, 1.f, 1.f}, pfm = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
-  for (int t = 0; t < TW; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
   for (int i = 0; i < KC; ++i) {
-    __builtin_amdgcn_sched_barrier(0);
-    // issue the loads of super-block i + P - 1 before decoding super-block i
-    if (i + P - 1 < KC)
-#pragma unroll
-      for (int t = 0; t < TW; ++t) load_frag(fr[(i + P - 1) % P][t], tbase[t] + (size_t)(i + P - 1) * 2304, g);
-    __builtin_amdgcn_sched_barrier(0);
     half8_t av[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) av[j] = *reinterpret_cast<const half8_t*>(xr + 256 * i + 8 * j);
     const half4_t axs = *reinterpret_cast<const half4_t*>(xsum + (xrow * KC + i) * 16 + 4 * g);
     const floatx4 fm = *reinterpret_cast<const floatx4*>(fac_m + i * 16 + 4 * g);
     floatx4 fd = {1.f, 1.f, 1.f, 1.f};
-    if constexpr (XF32) fd = *reinterpret_cast<const floatx4*>(fac_d + i * 16 + 4 * g);
-    floatx4 sq[TW], sm[TW];
-    float d[TW], dm[TW];
-#pragma unroll
-    for (int t = 0; t < TW; ++t) q4_superblock(fr[i % P][t], av, axs, g, km, sq[t], sm[t], d[t], dm[t]);
+    if constexpr (XMODE == kXF32Blocked) fd = *reinterpret_cast<const floatx4*>(fac_d + i * 16 + 4 * g);
+    floatx4 sq, sm;
+    float d, dm;
+    q4_superblock(fr[i % P], av, axs, g, km, sq, sm, d, dm);
+    if (i + P < KC) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_frag(fr[i % P], tbase + (size_t)(i + P) * 2304, g);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // accumulate the previous super-block now that its MFMAs are long done;
     // d * fd and dmin * fm are exact (the factors are powers of two)
     if (i > 0) {
 #pragma unroll
-      for (int t = 0; t < TW; ++t)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          acc[t][ii] = __builtin_fmaf(pd[t] * pfd[ii], psq[t][ii], __builtin_fmaf(-pdm[t] * pfm[ii], psm[t][ii], acc[t][ii]));
+      for (int ii = 0; ii < 4; ++ii)
+        acc[ii] = __builtin_fmaf(pd * pfd[ii], psq[ii], __builtin_fmaf(-pdm * pfm[ii], psm[ii], acc[ii]));
     }
-#pragma unroll
-    for (int t = 0; t < TW; ++t) {
-      psq[t] = sq[t];
-      psm[t] = sm[t];
-      pd[t] = d[t];
-      pdm[t] = dm[t];
-    }
+    psq = sq;
+    psm = sm;
+    pd = d;
+    pdm = dm;
     pfd = fd;
     pfm = fm;
   }
 #pragma unroll
-  for (int t = 0; t < TW; ++t)
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
-      acc[t][ii] = __builtin_fmaf(pd[t] * pfd[ii], psq[t][ii], __builtin_fmaf(-pdm[t] * pfm[ii], psm[t][ii], acc[t][ii]));
+  for (int ii = 0; ii < 4; ++ii)
+    acc[ii] = __builtin_fmaf(pd * pfd[ii], psq[ii], __builtin_fmaf(-pdm * pfm[ii], psm[ii], acc[ii]));
 
+  // ---- split-K: the last work-group of a row group to arrive finishes it
+  const int n = tile_of<MODE, WPB>(rg, wave, a.f_tiles) * 16 + r;   // this lane's output row
+  const int n_total = a.n_tiles * 16;
+  float res[4] = {0.f, 0.f, 0.f, 0.f};
   __shared__ int s_last;
   if (n_chunks > 1) {
-    // write-through partial sums; the arrival counter is a relaxed device-scope
-    // atomic issued after every thread's stores completed
-    const int n_total = n_tiles * 16;
-#pragma unroll
-    for (int t = 0; t < TW; ++t) {
-      if (!tok[t]) continue;
-      const int n = tile_of<MODE, TW>(rg, wave, t, f_tiles) * 16 + r;
+    if (tok) {
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int b = 4 * g + ii;
         if (b < B)
-          __hip_atomic_store(&part[((size_t)c * B + b) * n_total + n], acc[t][ii], __ATOMIC_RELAXED,
+          __hip_atomic_store(&a.part[((size_t)c * B + b) * n_total + n], acc[ii], __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0)
-      s_last = (__hip_atomic_fetch_add(&counters[rg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+      s_last = (__hip_atomic_fetch_add(&a.counters[rg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                 (unsigned)(n_chunks - 1));
     __syncthreads();
     if (!s_last) return;
+    // all chunks' partials (and the residual) in one batch of loads, then the
+    // sum in chunk order
+    const int nc = tok ? n : 0;
+    float pv[8][4];
+    if (n_chunks <= 8) {
 #pragma unroll
-    for (int t = 0; t < TW; ++t) {
-      if (!tok[t]) continue;
-      const int n = tile_of<MODE, TW>(rg, wave, t, f_tiles) * 16 + r;
+      for (int cc = 0; cc < 8; ++cc) {
+        if (cc < n_chunks) {
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int b = 4 * g + ii;
-        float v = 0.f;
-        if (b < B)
-          for (int cc = 0; cc < n_chunks; ++cc)
-            v += __hip_atomic_load(&part[((size_t)cc * B + b) * n_total + n], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        acc[t][ii] = v;
+          for (int ii = 0; ii < 4; ++ii) {
+            const int b = 4 * g + ii < B ? 4 * g + ii : B - 1;
+            pv[cc][ii] = __hip_atomic_load(&a.part[((size_t)cc * B + b) * n_total + nc], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
       }
-    }
-    if (threadIdx.x == 0) counters[rg] = 0u;
-  }
-
-  if (MODE == 0) {
+      if (MODE == 0 && a.residual) {
 #pragma unroll
-    for (int t = 0; t < TW; ++t) {
-      if (!tok[t]) continue;
-      const int n = tile_of<MODE, TW>(rg, wave, t, f_tiles) * 16 + r;
+        for (int ii = 0; ii < 4; ++ii) {
+          const int b = 4 * g + ii < B ? 4 * g + ii : B - 1;
+          res[ii] = a.residual[(size_t)b * a.ldr + nc];
+        }
+      }
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        const int b = 4 * g + ii;
-        if (b < B) {
-          float v = acc[t][ii];
-          if (residual) v += residual[(size_t)b * ldr + n];
-          Y[(size_t)b * ldy + n] = v;
+        float v = pv[0][ii];
+#pragma unroll
+        for (int cc = 1; cc < 8; ++cc)
+          if (cc < n_chunks) v += pv[cc][ii];
+        acc[ii] = v;
+      }
+    } else {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int b = 4 * g + ii < B ? 4 * g + ii : B - 1;
+        float v = 0.f;
+        for (int cc = 0; cc < n_chunks; ++cc)
+          v += __hip_atomic_load(&a.part[((size_t)cc * B + b) * n_total + nc], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        acc[ii] = v;
+      }
+      if (MODE == 0 && a.residual) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int b = 4 * g + ii < B ? 4 * g + ii : B - 1;
+          res[ii] = a.residual[(size_t)b * a.ldr + nc];
         }
       }
     }
-  } else {
-    floatx4 gv, uv;
-    bool write;
-    int n;
-    if constexpr (TW == 2) {
-      gv = acc[0];
-      uv = acc[1];
-      write = tok[0];
-      n = tile_of<MODE, TW>(rg, wave, 0, f_tiles) * 16 + r;
-    } else {
-      __shared__ floatx4 fin[4][64];
-      fin[wave][lane] = acc[0];
-      __syncthreads();
-      gv = fin[wave & 1][lane];
-      uv = fin[(wave & 1) + 2][lane];
-      write = wave < 2 && tok[0];
-      n = tile_of<MODE, TW>(rg, wave & 1, 0, f_tiles) * 16 + r;
+    if (threadIdx.x == 0) a.counters[rg] = 0u;
+  } else if (MODE == 0 && a.residual) {
+    const int nc = tok ? n : 0;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int b = 4 * g + ii < B ? 4 * g + ii : B - 1;
+      res[ii] = a.residual[(size_t)b * a.ldr + nc];
     }
-    if (write) {
+  }
+
+  if constexpr (MODE == 0) {
+    float sq[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int b = 4 * g + ii;
+      const float v = acc[ii] + res[ii];
+      sq[ii] = (tok && b < B) ? v * v : 0.f;
+      if (tok && b < B) a.Y[(size_t)b * a.ldy + n] = v;
+    }
+    if (a.ss_out) {
+      // every 4 waves' 64 columns make one sum-of-squares slot
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        float t = sq[ii];
+        t += __shfl_xor(t, 1);
+        t += __shfl_xor(t, 2);
+        t += __shfl_xor(t, 4);
+        t += __shfl_xor(t, 8);
+        if (r == 0) s_red[wave][4 * g + ii] = t;
+      }
+      __syncthreads();
+      if (threadIdx.x < 16 * (WPB / 4)) {
+        const int b = threadIdx.x & 15, j = threadIdx.x >> 4, w0 = 4 * j;
+        a.ss_out[(rg * (WPB / 4) + j) * 16 + b] =
+            (s_red[w0][b] + s_red[w0 + 1][b]) + (s_red[w0 + 2][b] + s_red[w0 + 3][b]);
+      }
+    }
+  } else {
+    constexpr int H = WPB / 2;
+    __shared__ floatx4 fin[WPB][64];
+    fin[wave][lane] = acc;
+    __syncthreads();
+    const floatx4 gvv = fin[wave % H][lane];
+    const floatx4 uvv = fin[wave % H + H][lane];
+    const int nf = tile_of<MODE, WPB>(rg, wave % H, a.f_tiles) * 16 + r;
+    if (wave < H && tok) {
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int b = 4 * g + ii;
         if (b < B) {
-          const float z = gv[ii];
+          const float z = gvv[ii];
           float sil;
           if (z >= 0.f) {
             sil = z / (1.f + expf(-z));
@@ -422,7 +508,7 @@ __global__ void __launch_bounds__(256) gemm_q4k_kernel(
             const float ez = expf(z);
             sil = z * ez / (1.f + ez);
           }
-          A[(size_t)b * lda + n] = sil * uv[ii];
+          a.A[(size_t)b * a.lda + nf] = sil * uvv[ii];
         }
       }
     }
@@ -450,34 +536,42 @@ __global__ void dequant_q4k_kernel(const uint8_t* __restrict__ W, int64_t n_bloc
 }
 
 // ---------------------------------------------------------------- launchers
-// Tiles per wave (TW) and K chunk (KC) of one launch.  One tile per wave; KC
-// is the largest divisor of kb up to 12 that keeps the staged activations
-// within ~48 KB of LDS and still gives at least 192 work-groups (measured on
-// MI355X for the 6144x4096, 4096x4096, 24576x4096 and 4096x12288 shapes).
-struct GemmShape {
-  int tw, kc;
-};
-
-static size_t lds_bytes(int B, int kc) { return (size_t)B * (kc * 256 + 8) * 2 + (size_t)B * kc * 32; }
-
-static int64_t n_groups_of(int64_t n_tiles, int tw, bool swiglu) {
-  if (swiglu) return tw == 2 ? (n_tiles / 2 + 3) / 4 : (n_tiles / 2 + 1) / 2;
-  return (n_tiles + 4 * tw - 1) / (4 * tw);
+static size_t lds_bytes(int B, int kc, int xmode) {
+  size_t n = (size_t)B * (kc * 256 + 8) * 2 + (size_t)B * kc * 32;
+  if (xmode == kXNorm) n += (size_t)kc * 256 * 4;
+  return n;
 }
 
-GemmShape gemm_shape(int64_t n_tiles, int64_t kb, int B, bool swiglu) {
-  static const int cands[] = {12, 8, 6, 4, 2, 1};
-  const int tw = 1;
-  const int64_t groups = n_groups_of(n_tiles, tw, swiglu);
+static int64_t n_groups_of(int64_t n_tiles, bool swiglu, int wpb) {
+  if (swiglu) return (n_tiles / 2 + wpb / 2 - 1) / (wpb / 2);
+  return (n_tiles + wpb - 1) / wpb;
+}
+
+// Launch shape: K chunk (super-blocks per work-group) and waves per
+// work-group.  Eight waves share one staged copy of the activations where the
+// launch is large (many tiles, or a long K); the chunk is the smallest divisor
+// of kb that keeps at most 8 chunks and at most 1024 work-groups and whose
+// staged activations fit the LDS budget.  The budget is sized for max(B, 8),
+// so every batch of up to 8 sequences uses the same chunking and a sequence's
+// outputs do not depend on its batch-mates.  (Chosen from sweeps on MI355X of
+// the 6144x4096, 4096x4096, 2x12288x4096 and 4096x12288 shapes at B = 8.)
+struct GemmConfig {
+  int kc, wpb;
+};
+
+GemmConfig gemm_config(int64_t n_tiles, int64_t kb, int B, bool swiglu, int xmode) {
+  static const int cands[] = {1, 2, 4, 6, 8, 12, 16};
+  const int wpb = (n_tiles >= 1024 || kb > 32) ? 8 : 4;
+  const int64_t groups = n_groups_of(n_tiles, swiglu, wpb);
+  const int bb = B > 8 ? B : 8;
+  int best = 0;
   for (int kc : cands) {
     if (kb % kc) continue;
-    // sized for max(B, 8) so that every batch of up to 8 sequences uses the same
-    // K chunking: a sequence's outputs then do not depend on its batch-mates
-    if (lds_bytes(B > 8 ? B : 8, kc) > 48 * 1024) continue;
-    if (groups * (kb / kc) < 192 && kc > 1) continue;
-    return {tw, kc};
+    if (lds_bytes(bb, kc, xmode) > 64 * 1024) break;
+    best = kc;
+    if (kb / kc <= 8 && groups * (kb / kc) <= 1024) break;
   }
-  return {tw, 1};
+  return {best ? best : 1, wpb};
 }
 
 // The split-K arrival counters occupy a fixed area at the start of the
@@ -489,95 +583,119 @@ static size_t counters_bytes() { return (size_t)kGemmMaxGroups * 4; }
 size_t gemm_workspace_bytes(int64_t n_rows, int64_t K, int B, bool swiglu) {
   const int64_t kb = K / 256;
   const int64_t n_tiles = n_rows / 16;
-  const GemmShape gs = gemm_shape(n_tiles, kb, B, swiglu);
-  const int64_t chunks = kb / gs.kc;
+  int64_t chunks = 1;
+  for (int xmode : {(int)kXF16, (int)kXF32Blocked, (int)kXNorm})
+    chunks = std::max<int64_t>(chunks, kb / gemm_config(n_tiles, kb, B, swiglu, xmode).kc);
   size_t bytes = counters_bytes();
   if (chunks > 1) bytes += (size_t)chunks * B * n_rows * 4;
   return bytes;
 }
 
-template <int MODE, bool XF32, int TW>
-static hipError_t launch_chunked(int kc, dim3 grid, size_t lds, hipStream_t st, const uint8_t* w, int n_tiles, int kb,
-                                 const void* x, int64_t ldx, int B, float* Y, int64_t ldy, const float* residual,
-                                 int64_t ldr, float* a, int64_t lda, int f_tiles, float* part, unsigned* counters) {
-#define QK_GEMM_CASE(KC)                                                                                           \
-  case KC:                                                                                                         \
-    hipLaunchKernelGGL((gemm_q4k_kernel<KC, MODE, XF32, TW>), grid, dim3(256), lds, st, w, n_tiles, kb, x, ldx, B,  \
-                       Y, ldy, residual, ldr, a, lda, f_tiles, part, counters);                                  \
+// 16-wave work-groups leave 128 registers per lane: K chunks up to 4 only.
+template <int MODE, int XMODE, int WPB>
+static hipError_t launch_kc(int kc, dim3 grid, size_t lds, hipStream_t st, const GemmArgs& a) {
+#define QK_GEMM_CASE(KC)                                                                              \
+  case KC:                                                                                            \
+    hipLaunchKernelGGL((gemm_q4k_kernel<KC, MODE, XMODE, WPB>), grid, dim3(64 * WPB), lds, st, a);    \
     break;
-  switch (kc) {
-    QK_GEMM_CASE(1)
-    QK_GEMM_CASE(2)
-    QK_GEMM_CASE(4)
-    QK_GEMM_CASE(6)
-    QK_GEMM_CASE(8)
-    QK_GEMM_CASE(12)
-    QK_GEMM_CASE(16)
-    default: return hipErrorInvalidValue;
+  if constexpr (WPB == 16) {
+    switch (kc) {
+      QK_GEMM_CASE(1)
+      QK_GEMM_CASE(2)
+      QK_GEMM_CASE(4)
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (kc) {
+      QK_GEMM_CASE(1)
+      QK_GEMM_CASE(2)
+      QK_GEMM_CASE(4)
+      QK_GEMM_CASE(6)
+      QK_GEMM_CASE(8)
+      QK_GEMM_CASE(12)
+      QK_GEMM_CASE(16)
+      default: return hipErrorInvalidValue;
+    }
   }
 #undef QK_GEMM_CASE
   return hipGetLastError();
 }
 
-static void carve(void* ws, unsigned** counters, float** part) {
-  char* p = reinterpret_cast<char*>(ws);
-  *counters = reinterpret_cast<unsigned*>(p);
-  *part = reinterpret_cast<float*>(p + counters_bytes());
+template <int MODE, int XMODE>
+static hipError_t launch_wpb(int wpb, int kc, dim3 grid, size_t lds, hipStream_t st, const GemmArgs& a) {
+  switch (wpb) {
+    case 4: return launch_kc<MODE, XMODE, 4>(kc, grid, lds, st, a);
+    case 8: return launch_kc<MODE, XMODE, 8>(kc, grid, lds, st, a);
+    case 16: return launch_kc<MODE, XMODE, 16>(kc, grid, lds, st, a);
+    default: return hipErrorInvalidValue;
+  }
 }
 
-static hipError_t gemm_run(const void* W, int64_t n_tiles, int64_t K, const void* X, bool x_f32, int64_t ldx, int B,
-                           float* Y, int64_t ldy, const float* residual, int64_t ldr, float* Aout, int64_t lda,
-                           bool swiglu, void* ws, hipStream_t st, GemmShape force) {
-  const int kb = (int)(K / 256);
-  GemmShape gs = gemm_shape(n_tiles, kb, B, swiglu);
-  if (force.kc) gs = force;
-  const int64_t n_groups = n_groups_of(n_tiles, gs.tw, swiglu);
-  unsigned* counters;
-  float* part;
-  carve(ws, &counters, &part);
-  const dim3 grid((unsigned)n_groups, (unsigned)(kb / gs.kc));
-  const size_t lds = lds_bytes(B, gs.kc);
-  const uint8_t* w = reinterpret_cast<const uint8_t*>(W);
-  const int nt = (int)n_tiles, ft = (int)(n_tiles / 2);
-  if (swiglu) {
-    if (gs.tw == 2)
-      return launch_chunked<1, false, 2>(gs.kc, grid, lds, st, w, nt, kb, X, ldx, B, nullptr, 0, nullptr, 0, Aout,
-                                         lda, ft, part, counters);
-    return launch_chunked<1, false, 1>(gs.kc, grid, lds, st, w, nt, kb, X, ldx, B, nullptr, 0, nullptr, 0, Aout, lda,
-                                       ft, part, counters);
+hipError_t launch_gemm(const GemmLaunch& L, hipStream_t st) {
+  const int64_t n_tiles = L.swiglu ? 2 * (L.n_rows / 16) : L.n_rows / 16;
+  const int kb = (int)(L.K / 256);
+  const int xmode = L.x_f32 ? (L.gamma ? kXNorm : kXF32Blocked) : kXF16;
+  GemmConfig cfg = gemm_config(n_tiles, kb, L.B, L.swiglu, xmode);
+  if (L.force_kc) cfg.kc = L.force_kc;
+  if (L.force_wpb) cfg.wpb = L.force_wpb;
+  GemmArgs a{};
+  a.W = reinterpret_cast<const uint8_t*>(L.W);
+  a.X = L.X;
+  a.gamma = L.gamma;
+  a.ss_in = L.ss_in;
+  a.Y = L.Y;
+  a.residual = L.residual;
+  a.ss_out = L.ss_out;
+  a.A = L.A;
+  char* p = reinterpret_cast<char*>(L.ws);
+  a.counters = reinterpret_cast<unsigned*>(p);
+  a.part = reinterpret_cast<float*>(p + counters_bytes());
+  a.ldx = L.ldx;
+  a.ldy = L.ldy;
+  a.ldr = L.ldr;
+  a.lda = L.lda;
+  a.n_tiles = (int)n_tiles;
+  a.kb = kb;
+  a.B = L.B;
+  a.f_tiles = (int)(n_tiles / 2);
+  a.ss_slots = (int)(L.K / kSsCols);
+  a.eps = L.eps;
+  a.inv_k = 1.0f / (float)L.K;
+  const dim3 grid((unsigned)n_groups_of(n_tiles, L.swiglu, cfg.wpb), (unsigned)(kb / cfg.kc));
+  const size_t lds = lds_bytes(L.B, cfg.kc, xmode);
+  if (lds > 150 * 1024) return hipErrorInvalidValue;
+  if (L.swiglu) {
+    if (xmode == kXNorm) return launch_wpb<1, kXNorm>(cfg.wpb, cfg.kc, grid, lds, st, a);
+    return launch_wpb<1, kXF16>(cfg.wpb, cfg.kc, grid, lds, st, a);
   }
-  if (x_f32) {
-    if (gs.tw == 2)
-      return launch_chunked<0, true, 2>(gs.kc, grid, lds, st, w, nt, kb, X, ldx, B, Y, ldy, residual, ldr, nullptr, 0,
-                                        0, part, counters);
-    return launch_chunked<0, true, 1>(gs.kc, grid, lds, st, w, nt, kb, X, ldx, B, Y, ldy, residual, ldr, nullptr, 0, 0,
-                                      part, counters);
-  }
-  if (gs.tw == 2)
-    return launch_chunked<0, false, 2>(gs.kc, grid, lds, st, w, nt, kb, X, ldx, B, Y, ldy, residual, ldr, nullptr, 0,
-                                       0, part, counters);
-  return launch_chunked<0, false, 1>(gs.kc, grid, lds, st, w, nt, kb, X, ldx, B, Y, ldy, residual, ldr, nullptr, 0, 0,
-                                     part, counters);
+  if (xmode == kXNorm) return launch_wpb<0, kXNorm>(cfg.wpb, cfg.kc, grid, lds, st, a);
+  if (xmode == kXF32Blocked) return launch_wpb<0, kXF32Blocked>(cfg.wpb, cfg.kc, grid, lds, st, a);
+  return launch_wpb<0, kXF16>(cfg.wpb, cfg.kc, grid, lds, st, a);
 }
 
 hipError_t launch_gemm_q4k(const void* W, int64_t N, int64_t K, const uint16_t* X, int64_t ldx, int B, float* Y,
-                           int64_t ldy, const float* residual, int64_t ldr, void* ws, hipStream_t st, int force_tw,
-                           int force_kc) {
-  return gemm_run(W, N / 16, K, X, false, ldx, B, Y, ldy, residual, ldr, nullptr, 0, false, ws, st,
-                  {force_tw, force_kc});
+                           int64_t ldy, const float* residual, int64_t ldr, void* ws, hipStream_t st, int force_kc) {
+  GemmLaunch L{};
+  L.W = W; L.n_rows = N; L.K = K; L.X = X; L.ldx = ldx; L.B = B;
+  L.Y = Y; L.ldy = ldy; L.residual = residual; L.ldr = ldr; L.ws = ws; L.force_kc = force_kc;
+  return launch_gemm(L, st);
 }
 
 hipError_t launch_gemm_q4k_xf32(const void* W, int64_t N, int64_t K, const float* X, int64_t ldx, int B, float* Y,
                                 int64_t ldy, const float* residual, int64_t ldr, void* ws, hipStream_t st,
-                                int force_tw, int force_kc) {
-  return gemm_run(W, N / 16, K, X, true, ldx, B, Y, ldy, residual, ldr, nullptr, 0, false, ws, st,
-                  {force_tw, force_kc});
+                                int force_kc) {
+  GemmLaunch L{};
+  L.W = W; L.n_rows = N; L.K = K; L.X = X; L.x_f32 = true; L.ldx = ldx; L.B = B;
+  L.Y = Y; L.ldy = ldy; L.residual = residual; L.ldr = ldr; L.ws = ws; L.force_kc = force_kc;
+  return launch_gemm(L, st);
 }
 
 hipError_t launch_gemm_q4k_swiglu(const void* W, int64_t F, int64_t K, const uint16_t* X, int64_t ldx, int B,
-                                  float* A, int64_t lda, void* ws, hipStream_t st, int force_tw, int force_kc) {
-  return gemm_run(W, 2 * (F / 16), K, X, false, ldx, B, nullptr, 0, nullptr, 0, A, lda, true, ws, st,
-                  {force_tw, force_kc});
+                                  float* A, int64_t lda, void* ws, hipStream_t st, int force_kc) {
+  GemmLaunch L{};
+  L.W = W; L.n_rows = F; L.K = K; L.X = X; L.ldx = ldx; L.B = B; L.swiglu = true;
+  L.A = A; L.lda = lda; L.ws = ws; L.force_kc = force_kc;
+  return launch_gemm(L, st);
 }
 
 hipError_t launch_dequant_q4k(const void* W, int64_t n_blocks, float* out, hipStream_t st) {

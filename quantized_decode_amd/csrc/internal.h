@@ -10,26 +10,54 @@
 
 namespace qk {
 
-// ---- Q4_K GEMM (gemm_q4k.hip); force_tw / force_kc = 0 pick the tiling by shape.
+// ---- Q4_K GEMM (gemm_q4k.hip); force_kc = 0 picks the K chunk by shape.
 // ws: device workspace of gemm_workspace_bytes(); its counters must be zero
 // before the first launch (every launch leaves them zero again).
 size_t gemm_workspace_bytes(int64_t n_rows, int64_t K, int B, bool swiglu);
+
+// One launch of the general kernel.  Activations: fp16 X, or fp32 X (x_f32)
+// rounded per 256-value block, or fp32 residual-stream rows normalized while
+// staged when gamma is set (RMSNorm with the sum-of-squares slots ss_in, see
+// common.h).  Output: Y (+ residual) and optionally ss_out (one slot per 64
+// rows of Y), or, for swiglu, A = silu(gate) * up with n_rows = F.
+struct GemmLaunch {
+  const void* W = nullptr;
+  int64_t n_rows = 0, K = 0;
+  const void* X = nullptr;
+  bool x_f32 = false;
+  int64_t ldx = 0;
+  int B = 0;
+  const float* gamma = nullptr;
+  const float* ss_in = nullptr;
+  float eps = 0.f;
+  float* Y = nullptr;
+  int64_t ldy = 0;
+  const float* residual = nullptr;
+  int64_t ldr = 0;
+  float* ss_out = nullptr;
+  bool swiglu = false;
+  float* A = nullptr;
+  int64_t lda = 0;
+  void* ws = nullptr;
+  int force_kc = 0;    // 0: K chunk chosen by shape
+  int force_wpb = 0;   // 0: waves per work-group chosen by shape (4, 8 or 16)
+};
+hipError_t launch_gemm(const GemmLaunch& L, hipStream_t st);
 hipError_t launch_gemm_q4k(const void* W, int64_t N, int64_t K, const uint16_t* X, int64_t ldx, int B,
                            float* Y, int64_t ldy, const float* residual, int64_t ldr, void* ws, hipStream_t st,
-                           int force_tw = 0, int force_kc = 0);
+                           int force_kc = 0);
 hipError_t launch_gemm_q4k_xf32(const void* W, int64_t N, int64_t K, const float* X, int64_t ldx, int B,
                                 float* Y, int64_t ldy, const float* residual, int64_t ldr, void* ws, hipStream_t st,
-                                int force_tw = 0, int force_kc = 0);
+                                int force_kc = 0);
 hipError_t launch_gemm_q4k_swiglu(const void* W, int64_t F, int64_t K, const uint16_t* X, int64_t ldx, int B,
-                                  float* A, int64_t lda, void* ws, hipStream_t st, int force_tw = 0,
-                                  int force_kc = 0);
+                                  float* A, int64_t lda, void* ws, hipStream_t st, int force_kc = 0);
 hipError_t launch_dequant_q4k(const void* W, int64_t n_blocks, float* out, hipStream_t st);
 
 // ---- attention (attn_decode.hip)
 // tokens per split work item
 // Largest number of row groups (work-groups along N) of one Q4_K GEMM launch:
-// 4 tiles of 16 rows per group, so N <= 16 * 4 * kGemmMaxGroups = 2^20 rows
-// (a SwiGLU launch covers gate and up: 2F <= 2^20).
+// at least 4 tiles of 16 rows per group, so N <= 16 * 4 * kGemmMaxGroups =
+// 2^20 rows (a SwiGLU launch covers gate and up: 2F <= 2^20).
 constexpr int kGemmMaxGroups = 16384;
 constexpr int64_t kGemmMaxRows = 16 * 4 * (int64_t)kGemmMaxGroups;
 
@@ -52,9 +80,12 @@ hipError_t launch_rope_append(const qkdec_kv_layer& kv, const int32_t* slot, con
                               int B, int n_q_heads, float rope_base, uint16_t* q16, int32_t* err, hipStream_t st);
 
 // ---- small kernels (small.hip)
-hipError_t launch_embed(const uint16_t* E, int hidden, int vocab, const int32_t* tok, int B, float* x, hipStream_t st);
-hipError_t launch_rmsnorm_f16(const float* x, const float* gamma, int hidden, int B, float eps, uint16_t* h,
-                              hipStream_t st);
+// x = E[tok] and its sum-of-squares slots ss (common.h); hidden % 256 == 0
+hipError_t launch_embed(const uint16_t* E, int hidden, int vocab, const int32_t* tok, int B, float* x, float* ss,
+                        hipStream_t st);
+// h = f16(RMSNorm(x)) with the sum-of-squares slots of x
+hipError_t launch_rmsnorm_f16(const float* x, const float* gamma, const float* ss, int hidden, int B, float eps,
+                              uint16_t* h, hipStream_t st);
 size_t lm_head_partials_bytes(int64_t V, int B);
 // bytes of LDS the LM head kernel needs for B sequences of width H
 inline size_t lm_head_lds_bytes(int64_t H, int B) { return (size_t)B * (size_t)(H + 8) * 2; }

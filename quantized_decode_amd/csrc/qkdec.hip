@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <new>
 
+#include "common.h"
 #include "internal.h"
 
 namespace {
@@ -70,7 +71,7 @@ qkdec_status check_model(const qkdec_model* m, const qkdec_kv_layer* kv) {
   if (m->head_dim != 64 && m->head_dim != 128) return QKDEC_E_SHAPE;
   if (((int64_t)m->n_q_heads * m->head_dim) % 256 != 0) return QKDEC_E_SHAPE;
   if ((int64_t)(m->n_q_heads + 2 * m->n_kv_heads) * m->head_dim > kGemmMaxRows || 2 * (int64_t)m->ffn > kGemmMaxRows ||
-      m->hidden > kGemmMaxRows)
+      m->hidden > kSsMaxSlots * kSsCols)
     return QKDEC_E_SHAPE;
   if (!(m->rms_eps >= 0.f) || !(m->rope_base > 0.f)) return QKDEC_E_ARG;
   if (!aligned(m->embed, 16) || !aligned(m->lm_head, 16)) return QKDEC_E_ALIGN;
@@ -91,6 +92,7 @@ qkdec_status check_model(const qkdec_model* m, const qkdec_kv_layer* kv) {
 struct StepWs {
   int32_t* err;
   float* x;
+  float* ss;
   uint16_t* h;
   float* qkv;
   uint16_t* q16;
@@ -114,6 +116,7 @@ StepWs step_layout(const qkdec_model* m, int B, const qkdec_kv_layer* kv, char* 
   const int64_t nqkv = (int64_t)(m->n_q_heads + 2 * m->n_kv_heads) * m->head_dim;
   w.err = reinterpret_cast<int32_t*>(take(256));
   w.x = reinterpret_cast<float*>(take((size_t)B * m->hidden * 4));
+  w.ss = reinterpret_cast<float*>(take((size_t)kSsMaxSlots * 16 * 4));
   w.h = reinterpret_cast<uint16_t*>(take((size_t)B * m->hidden * 2));
   w.qkv = reinterpret_cast<float*>(take((size_t)B * nqkv * 4));
   w.q16 = reinterpret_cast<uint16_t*>(take((size_t)B * hq * 2));
@@ -142,19 +145,33 @@ qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int3
     const hipError_t e_ = (expr);                    \
     if (e_ != hipSuccess) return QKDEC_E_HIP;        \
   } while (0)
-  QK_TRY(launch_embed(m->embed, H, m->vocab, tok, B, w.x, st));
+  QK_TRY(launch_embed(m->embed, H, m->vocab, tok, B, w.x, w.ss, st));
   for (int l = 0; l < m->n_layers; ++l) {
     const qkdec_layer& ly = m->layers[l];
-    QK_TRY(launch_rmsnorm_f16(w.x, ly.norm_attn, H, B, m->rms_eps, w.h, st));
-    QK_TRY(launch_gemm_q4k(ly.w_qkv, nqkv, H, w.h, H, B, w.qkv, nqkv, nullptr, 0, w.gemm_ws, st));
+    // RMSNorm is applied while each projection stages x (statistics in w.ss,
+    // written by the kernel that last wrote x)
+    GemmLaunch qkv{};
+    qkv.W = ly.w_qkv; qkv.n_rows = nqkv; qkv.K = H; qkv.X = w.x; qkv.x_f32 = true; qkv.ldx = H; qkv.B = B;
+    qkv.gamma = ly.norm_attn; qkv.ss_in = w.ss; qkv.eps = m->rms_eps;
+    qkv.Y = w.qkv; qkv.ldy = nqkv; qkv.ws = w.gemm_ws;
+    QK_TRY(launch_gemm(qkv, st));
     QK_TRY(launch_rope_append(kv[l], slot, pos, w.qkv, B, Hq, m->rope_base, w.q16, w.err, st));
     QK_TRY(launch_attn_decode(kv[l], slot, pos, B, w.q16, Hq, scale, nullptr, w.o16, w.attn_part, 1, st));
-    QK_TRY(launch_gemm_q4k(ly.w_o, H, hq, w.o16, hq, B, w.x, H, w.x, H, w.gemm_ws, st));
-    QK_TRY(launch_rmsnorm_f16(w.x, ly.norm_ffn, H, B, m->rms_eps, w.h, st));
-    QK_TRY(launch_gemm_q4k_swiglu(ly.w_gate_up, F, H, w.h, H, B, w.a, F, w.gemm_ws, st));
-    QK_TRY(launch_gemm_q4k_xf32(ly.w_down, H, F, w.a, F, B, w.x, H, w.x, H, w.gemm_ws, st));
+    GemmLaunch o{};
+    o.W = ly.w_o; o.n_rows = H; o.K = hq; o.X = w.o16; o.ldx = hq; o.B = B;
+    o.Y = w.x; o.ldy = H; o.residual = w.x; o.ldr = H; o.ss_out = w.ss; o.ws = w.gemm_ws;
+    QK_TRY(launch_gemm(o, st));
+    GemmLaunch gu{};
+    gu.W = ly.w_gate_up; gu.n_rows = F; gu.K = H; gu.X = w.x; gu.x_f32 = true; gu.ldx = H; gu.B = B;
+    gu.gamma = ly.norm_ffn; gu.ss_in = w.ss; gu.eps = m->rms_eps;
+    gu.swiglu = true; gu.A = w.a; gu.lda = F; gu.ws = w.gemm_ws;
+    QK_TRY(launch_gemm(gu, st));
+    GemmLaunch dn{};
+    dn.W = ly.w_down; dn.n_rows = H; dn.K = F; dn.X = w.a; dn.x_f32 = true; dn.ldx = F; dn.B = B;
+    dn.Y = w.x; dn.ldy = H; dn.residual = w.x; dn.ldr = H; dn.ss_out = w.ss; dn.ws = w.gemm_ws;
+    QK_TRY(launch_gemm(dn, st));
   }
-  QK_TRY(launch_rmsnorm_f16(w.x, m->norm_final, H, B, m->rms_eps, w.h, st));
+  QK_TRY(launch_rmsnorm_f16(w.x, m->norm_final, w.ss, H, B, m->rms_eps, w.h, st));
   QK_TRY(launch_lm_head_argmax(m->lm_head, m->vocab, H, w.h, B, logits, tok, w.lm_part, pos, st));
 #undef QK_TRY
   return QKDEC_OK;

@@ -1,4 +1,5 @@
-// Embedding gather, RMSNorm -> fp16, and the fp16 LM head with fused argmax.
+// Embedding gather (with the row statistics for the fused RMSNorm), the final
+// RMSNorm -> fp16, and the fp16 LM head with fused argmax.
 //
 // P1 "The weight read is the only term that does not scale": the norms run
 // over one row per sequence; reading the output embedding is shared by the
@@ -8,31 +9,37 @@
 
 namespace qk {
 
-// x[b] = E[tok[b]] in fp32; a token outside [0, vocab) reads row 0.
-__global__ void embed_kernel(const half_t* __restrict__ E, int hidden, int vocab, const int32_t* tok, float* x) {
+// x[b] = E[tok[b]] in fp32 (a token outside [0, vocab) reads row 0), and the
+// sum-of-squares slots of x: hidden % 256 == 0, one wave per 64-column slot.
+__global__ void __launch_bounds__(256) embed_kernel(const half_t* __restrict__ E, int hidden, int vocab,
+                                                    const int32_t* tok, float* x, float* ss) {
   const int b = blockIdx.y;
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= hidden) return;
+  const int i = blockIdx.x * 256 + threadIdx.x;
   int t = tok[b];
   if (t < 0 || t >= vocab) t = 0;
-  x[(size_t)b * hidden + i] = (float)E[(size_t)t * hidden + i];
+  const float v = (float)E[(size_t)t * hidden + i];
+  x[(size_t)b * hidden + i] = v;
+  float q = v * v;
+  for (int o = 32; o >= 1; o >>= 1) q += __shfl_xor(q, o);
+  if ((threadIdx.x & 63) == 0) ss[(blockIdx.x * 4 + (threadIdx.x >> 6)) * 16 + b] = q;
 }
 
-// h = f16(gamma * x / sqrt(mean(x^2) + eps)), one block per sequence.
+// h = f16(x * rinv * gamma) with rinv from the sum-of-squares slots of x;
+// one 256-column block per work-group.
 __global__ void __launch_bounds__(256) rmsnorm_f16_kernel(const float* __restrict__ x, const float* __restrict__ gamma,
-                                                          int hidden, float eps, half_t* __restrict__ h) {
-  const int b = blockIdx.x;
-  const float* xr = x + (size_t)b * hidden;
-  float ss = 0.f;
-  for (int i = threadIdx.x; i < hidden; i += 256) ss = __builtin_fmaf(xr[i], xr[i], ss);
-  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-  __shared__ float part[4];
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+                                                          const float* __restrict__ ss, int hidden, float eps,
+                                                          half_t* __restrict__ h) {
+  __shared__ float red[4][16];
+  const int b = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  float sv[kSsMaxSlots / 16];
+  const int n_slots = hidden / kSsCols;
+  ss_thread_load(ss, n_slots, sv);
+  const float xv = x[(size_t)b * hidden + i];
+  const float gv = gamma[i];
+  ss_wave_fold(ss_thread_sum(sv, n_slots), red);
   __syncthreads();
-  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
-  const float r = 1.0f / sqrtf(tot / (float)hidden + eps);
-  half_t* hr = h + (size_t)b * hidden;
-  for (int i = threadIdx.x; i < hidden; i += 256) hr[i] = (half_t)(gamma[i] * xr[i] * r);
+  h[(size_t)b * hidden + i] = norm_apply(xv, rms_inv(red, b, 1.0f / (float)hidden, eps), gv);
 }
 
 // ------------------------------------------------------------------ LM head
@@ -149,16 +156,16 @@ __global__ void fill_zero_kernel(uint32_t* p, size_t n_words) {
     p[i] = 0u;
 }
 
-hipError_t launch_embed(const uint16_t* E, int hidden, int vocab, const int32_t* tok, int B, float* x,
+hipError_t launch_embed(const uint16_t* E, int hidden, int vocab, const int32_t* tok, int B, float* x, float* ss,
                         hipStream_t st) {
-  hipLaunchKernelGGL(embed_kernel, dim3((hidden + 255) / 256, B), dim3(256), 0, st, reinterpret_cast<const half_t*>(E),
-                     hidden, vocab, tok, x);
+  hipLaunchKernelGGL(embed_kernel, dim3(hidden / 256, B), dim3(256), 0, st, reinterpret_cast<const half_t*>(E), hidden,
+                     vocab, tok, x, ss);
   return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm_f16(const float* x, const float* gamma, int hidden, int B, float eps, uint16_t* h,
-                              hipStream_t st) {
-  hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3(B), dim3(256), 0, st, x, gamma, hidden, eps,
+hipError_t launch_rmsnorm_f16(const float* x, const float* gamma, const float* ss, int hidden, int B, float eps,
+                              uint16_t* h, hipStream_t st) {
+  hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3(hidden / 256, B), dim3(256), 0, st, x, gamma, ss, hidden, eps,
                      reinterpret_cast<half_t*>(h));
   return hipGetLastError();
 }

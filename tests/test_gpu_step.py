@@ -6,7 +6,8 @@ import pytest
 
 import synth
 from oracle import step as OS
-from tests.gpu_util import LOGIT_ABS_TOL, assert_rel, sync, top2_gap, ws
+from tests.gpu_util import (LOGIT_ABS_TOL, assert_rel, f16_rounding_slack, propagate_slack, sync, top2_gap,
+                            ws)
 
 pytestmark = pytest.mark.gpu
 
@@ -205,8 +206,11 @@ def check_layer_stages(dims, kind, ly, x_in, pos, vw, cache_dev, cache_before, s
     from oracle import formats as OF, ops as OO
     hq, hkv, hd = dims.n_q_heads, dims.n_kv_heads, dims.head_dim
     qrows, krows = hq * hd, hkv * hd
-    h = OF.round_f16(OO.rmsnorm(x_in, ly.norm_attn, dims.rms_eps))
-    assert_rel(vw.qkv, OO.q4k_gemm(ly.w_qkv, qrows + 2 * krows, dims.hidden, h), what="qkv projection")
+    pre = OO.rmsnorm(x_in, ly.norm_attn, dims.rms_eps)
+    h = OF.round_f16(pre)
+    nqkv = qrows + 2 * krows
+    slack = propagate_slack(f16_rounding_slack(pre), nqkv, lambda: OF.q4k_dequant_rows(ly.w_qkv, nqkv, dims.hidden))
+    assert_rel(vw.qkv, OO.q4k_gemm(ly.w_qkv, nqkv, dims.hidden, h), what="qkv projection", slack=slack)
     got = _cache_from_device(cache_dev, kind)
     for b, s in enumerate(slots):
         p = int(pos[b])
@@ -233,9 +237,18 @@ def check_layer_stages(dims, kind, ly, x_in, pos, vw, cache_dev, cache_before, s
         o = OO.attention(vw.q16[b].reshape(hq, hd), kd, vd, 1.0 / np.sqrt(hd)).reshape(-1)
         assert_rel(vw.o16[b], OF.round_f16(o), what=f"attention, sequence {b}")
     x1 = x_in + OO.q4k_gemm(ly.w_o, dims.hidden, qrows, vw.o16)
-    h2 = OF.round_f16(OO.rmsnorm(x1, ly.norm_ffn, dims.rms_eps))
-    gu = OO.q4k_gemm(ly.w_gate_up, 2 * dims.ffn, dims.hidden, h2)
-    assert_rel(vw.a, OO.swiglu(gu[:, :dims.ffn], gu[:, dims.ffn:]), what="SwiGLU activation")
+    pre2 = OO.rmsnorm(x1, ly.norm_ffn, dims.rms_eps)
+    h2 = OF.round_f16(pre2)
+    f = dims.ffn
+    gu = OO.q4k_gemm(ly.w_gate_up, 2 * f, dims.hidden, h2)
+    gs = propagate_slack(f16_rounding_slack(pre2), 2 * f,
+                         lambda: OF.q4k_dequant_rows(ly.w_gate_up, 2 * f, dims.hidden))
+    # first order through silu(g) * u (|silu'| <= 1.1), with the product of the two bounds on top
+    g_, u_ = gu[:, :f], gu[:, f:]
+    sg = 1.0 / (1.0 + np.exp(-np.clip(g_, -700, 700)))
+    dsilu = np.abs(sg * (1.0 + g_ * (1.0 - sg)))
+    a_slack = dsilu * np.abs(u_) * gs[:, :f] + np.abs(OO.silu(g_)) * gs[:, f:] + 1.1 * gs[:, :f] * gs[:, f:]
+    assert_rel(vw.a, OO.swiglu(g_, u_), what="SwiGLU activation", slack=a_slack)
     a16 = OF.round_f16_blocked(vw.a)
     assert_rel(vw.x, x1 + OO.q4k_gemm(ly.w_down, dims.hidden, dims.ffn, a16), what="residual after the layer")
 
