@@ -209,6 +209,7 @@ class StepModel:
         self.model = Model(len(layers), dims.hidden, dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.ffn,
                            dims.vocab, dims.rms_eps, dims.rope_base, _ptr(embed), _ptr(lm_head), _ptr(norm_final),
                            ctypes.cast(self.layer_arr, ctypes.POINTER(Layer)))
+        self.kv_layers = list(kv_layers)
         self.kv_arr = (KVLayer * len(kv_layers))(*kv_layers)
 
 

@@ -3,9 +3,10 @@
 // P2 "The two halves of a decode-step memory bill": each sequence reads its
 // whole private cache every step; P3 FAQ "Is KV cache quantization a kernel
 // change or a storage change?": a quantized cache is dequantized inside the
-// fused attention kernel.  One wave handles one work item (sequence b, KV head
-// g, run of kAttnChunk tokens); the merge of the runs uses their log-sum-exp
-// weights (attn_combine_kernel).
+// fused attention kernel.  One work-group of 4 waves handles one work item
+// (sequence b, KV head g, run of kAttnChunk tokens): wave w takes the run's
+// 32-token tiles w, w + 4, ...; the four waves' states are merged in LDS and
+// the merge of the runs uses their log-sum-exp weights (attn_combine_kernel).
 //
 // Both contractions run on MFMA v_mfma_f32_16x16x32_f16 with the G <= 16
 // query heads of the group as the N columns (zero padded):
@@ -284,18 +285,20 @@ __device__ __forceinline__ void attn_tile(AttnState<D, Q8>& st, const KVFrag<D, 
   }
 }
 
+constexpr int kAttnWaves = 4;
+
 template <int D, bool Q8>
-__global__ void __launch_bounds__(64) attn_split_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(64 * kAttnWaves) attn_split_kernel(AttnArgs a) {
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = a.Hq / a.n_kv;
   const int s = a.slot[b];
   int n = a.n_ctx[b] + a.n_ctx_add;
   if (n > a.cap) n = a.cap;
-  if (s < 0 || s >= a.n_slots) n = 0;
+  if (n < 0 || s < 0 || s >= a.n_slots) n = 0;
   const int t_begin = c * kAttnChunk;
   if (t_begin >= n) return;
   const int t_end = min(t_begin + kAttnChunk, n);
-  const int lane = threadIdx.x, lg = lane >> 4, r = lane & 15;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lg = lane >> 4, r = lane & 15;
 
   half8_t qf[D / 32];
   {
@@ -317,18 +320,22 @@ __global__ void __launch_bounds__(64) attn_split_kernel(AttnArgs a) {
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) st.ex[c] = 127;
 
+  // this wave's tiles: wave, wave + 4, ... (the next one's loads are issued
+  // before the current one is processed)
   const int ntiles = (t_end - t_begin + 31) / 32;
-  KVFrag<D, Q8> buf[2];
-  load_kv<D, Q8>(buf[0], a, head_row0, t_begin, lg, r);
-  for (int it = 0; it < ntiles; it += 2) {
+  if (wave < ntiles) {
+    KVFrag<D, Q8> buf[2];
+    load_kv<D, Q8>(buf[0], a, head_row0, t_begin + 32 * wave, lg, r);
+    for (int it = wave; it < ntiles; it += 2 * kAttnWaves) {
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int i = it + p;
-      if (i < ntiles) {
-        const int nx = (i + 1 < ntiles) ? i + 1 : i;
-        load_kv<D, Q8>(buf[p ^ 1], a, head_row0, t_begin + 32 * nx, lg, r);
-        const int t0 = t_begin + 32 * i;
-        attn_tile<D, Q8>(st, buf[p], qf, a.scale_log2, min(32, t_end - t0), lg);
+      for (int p = 0; p < 2; ++p) {
+        const int i = it + p * kAttnWaves;
+        if (i < ntiles) {
+          const int nx = (i + kAttnWaves < ntiles) ? i + kAttnWaves : i;
+          load_kv<D, Q8>(buf[p ^ 1], a, head_row0, t_begin + 32 * nx, lg, r);
+          const int t0 = t_begin + 32 * i;
+          attn_tile<D, Q8>(st, buf[p], qf, a.scale_log2, min(32, t_end - t0), lg);
+        }
       }
     }
   }
@@ -338,6 +345,36 @@ __global__ void __launch_bounds__(64) attn_split_kernel(AttnArgs a) {
   for (int i = 0; i < D / 16; ++i) {
     const float un = Q8 ? exp2i(-st.ex[i / 2]) : exp2i(-kPScale);
     st.o[i][0] *= un; st.o[i][1] *= un; st.o[i][2] *= un; st.o[i][3] *= un;
+  }
+  // merge the four waves' states (same lane layout in every wave) in LDS;
+  // a wave without tiles has m = -inf, l = 0, o = 0 and weighs nothing
+  __shared__ float s_m[kAttnWaves][64], s_l[kAttnWaves][64];
+  __shared__ floatx4 s_o[kAttnWaves][D / 16][64];
+  s_m[wave][lane] = st.m;
+  s_l[wave][lane] = st.l;
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) s_o[wave][i][lane] = st.o[i];
+  __syncthreads();
+  if (wave != 0) return;
+  float mm = s_m[0][lane];
+#pragma unroll
+  for (int w = 1; w < kAttnWaves; ++w) mm = fmaxf(mm, s_m[w][lane]);
+  float wt[kAttnWaves];
+#pragma unroll
+  for (int w = 0; w < kAttnWaves; ++w) wt[w] = exp2f(s_m[w][lane] - mm);
+  st.m = mm;
+  st.l = 0.f;
+#pragma unroll
+  for (int w = 0; w < kAttnWaves; ++w) st.l += wt[w] * s_l[w][lane];
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) {
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      const floatx4 ow = s_o[w][i][lane];
+      acc[0] += wt[w] * ow[0]; acc[1] += wt[w] * ow[1]; acc[2] += wt[w] * ow[2]; acc[3] += wt[w] * ow[3];
+    }
+    st.o[i] = acc;
   }
   const float ltot = st.l + __shfl_xor(st.l, 16);
   const float lsum = ltot + __shfl_xor(ltot, 32);
@@ -361,7 +398,7 @@ __global__ void attn_combine_kernel(const float* __restrict__ part_o, const floa
   int n = n_ctx[b] + n_ctx_add;
   if (n > cap) n = cap;
   const int s = slot[b];
-  if (s < 0 || s >= n_slots) n = 0;
+  if (n < 0 || s < 0 || s >= n_slots) n = 0;
   const int ns = n > 0 ? (n + kAttnChunk - 1) / kAttnChunk : 0;
   const size_t row0 = ((size_t)b * Hq + h) * n_splits;
   float big = -__builtin_inff();
@@ -403,11 +440,11 @@ hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, con
   const dim3 grid(a.n_splits, kv.n_kv_heads, B);
   const bool q8 = kv.type == QKDEC_KV_Q8_0;
   if (D == 128) {
-    if (q8) hipLaunchKernelGGL((attn_split_kernel<128, true>), grid, dim3(64), 0, st, a);
-    else hipLaunchKernelGGL((attn_split_kernel<128, false>), grid, dim3(64), 0, st, a);
+    if (q8) hipLaunchKernelGGL((attn_split_kernel<128, true>), grid, dim3(64 * kAttnWaves), 0, st, a);
+    else hipLaunchKernelGGL((attn_split_kernel<128, false>), grid, dim3(64 * kAttnWaves), 0, st, a);
   } else {
-    if (q8) hipLaunchKernelGGL((attn_split_kernel<64, true>), grid, dim3(64), 0, st, a);
-    else hipLaunchKernelGGL((attn_split_kernel<64, false>), grid, dim3(64), 0, st, a);
+    if (q8) hipLaunchKernelGGL((attn_split_kernel<64, true>), grid, dim3(64 * kAttnWaves), 0, st, a);
+    else hipLaunchKernelGGL((attn_split_kernel<64, false>), grid, dim3(64 * kAttnWaves), 0, st, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -61,7 +61,7 @@ hipError_t launch_dequant_q4k(const void* W, int64_t n_blocks, float* out, hipSt
 constexpr int kGemmMaxGroups = 16384;
 constexpr int64_t kGemmMaxRows = 16 * 4 * (int64_t)kGemmMaxGroups;
 
-constexpr int kAttnChunk = 128;
+constexpr int kAttnChunk = 256;
 inline int attn_n_splits(int capacity) { return (capacity + kAttnChunk - 1) / kAttnChunk; }
 // partial results per (b, q head, split): m, l, then head_dim values of o
 inline size_t attn_partials_bytes(int B, int n_q_heads, int head_dim, int capacity) {

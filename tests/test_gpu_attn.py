@@ -129,3 +129,30 @@ def test_attention_deterministic(qd):
     o1, _ = _run(qd, cache, "q8_0", q, [0, 1, 2, 3], [1000, 17, 1024, 640], 0.088)
     o2, _ = _run(qd, cache, "q8_0", q, [0, 1, 2, 3], [1000, 17, 1024, 640], 0.088)
     assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+
+
+def test_attention_workspace_reused_across_calls(qd):
+    # the merge's arrival counters live in the workspace: consecutive calls with
+    # different lengths (one sequence empty, one negative) must each be exact
+    import torch
+    from quantized_decode_amd.tensors import dev, upload_cache
+    bsz, hq, hkv, d, cap = 4, 32, 8, 128, 1024
+    cache, st = _make("f16", 79, bsz, hkv, cap, d, [cap] * bsz)
+    dkv = upload_cache(cache)
+    q = synth.f16_normal(st.next(), (bsz, hq, d))
+    qd_t = dev(q.view(np.uint16)).view(torch.float16)
+    w = ws(qd.qkdec_attn_workspace_size(bsz, hq, dkv.desc))
+    slots = dev(np.arange(bsz, dtype=np.int32))
+    for lens in ([1024, 17, 600, 129], [0, 1024, 128, 1], [300, -5, 1000, 513], [1024, 17, 600, 129]):
+        o = torch.empty((bsz, hq, d), dtype=torch.float32, device="cuda")
+        qd.qkdec_attn_decode(dkv.desc, slots, dev(np.asarray(lens, np.int32)), bsz, qd_t, hq, 1 / math.sqrt(d),
+                             o=o, workspace=w)
+        sync()
+        got = o.cpu().numpy()
+        live = [b for b in range(bsz) if lens[b] > 0]
+        for b in range(bsz):
+            if lens[b] <= 0:
+                assert not got[b].any(), f"{lens}: sequence {b} not zero"
+        ref = OS.attention_batch(q[live].astype(np.float64), cache, "f16", live, [lens[b] for b in live],
+                                 1 / math.sqrt(d))
+        assert_rel(got[live], ref, what=f"lengths {lens}")
