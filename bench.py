@@ -43,6 +43,16 @@ W_BYTES = NL * LAYER_Q4K + VOCAB * H * 2 + (2 * NL + 1) * H * 4     # shared byt
 KV_BYTES_PER_TOKEN = {"f16": NL * HKV * D * 2 * 2, "q8_0": NL * HKV * D * 2 * 34 // 32}
 
 
+# HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs (calibrated
+# against a plain 1 GiB copy: fetched = 2.0 x FETCH_SIZE, written = 1.0 x
+# WRITE_SIZE), keyed by the kernels as they were when counted; see
+# profiles/decode_step_b8_l2400_f16_kernel_stats.md.  A kernel changed since
+# has no entry, and its traffic is reported as null.
+COUNTED_TRAFFIC = {
+    ("attention (split + merge)", 8, 2400, "f16"): 81_135_160 + 1_474_567,
+}
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -299,8 +309,9 @@ def main():
     main_pt = results[0]
     dom_name, dom = max(kernels.items(), key=lambda kv: kv[1]["ms_per_step"])
     achieved = dom["bytes_per_launch"] / (dom["avg_ms"] * 1e-3) / 1e9
+    traffic = COUNTED_TRAFFIC.get((dom_name, main_pt["batch"], main_pt["context"], main_pt["kv"]))
     roofline = {"kernel": dom_name, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBPS, "traffic": None, "avg_launch_ms": dom["avg_ms"],
+                "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic, "avg_launch_ms": dom["avg_ms"],
                 "algorithmic_bytes_per_launch": dom["bytes_per_launch"],
                 "launches_per_step": dom["launches_per_step"]}
 

@@ -1,4 +1,5 @@
 """The pages' byte model of a batched decode step (oracle; test infrastructure only).
+(P1, P2, P3: the three pages listed, with their titles, in oracle/__init__.py.)
 
 P2 "The two halves of a decode-step memory bill": with B sequences each
 holding L cached tokens, a step moves the shared weights W once plus the

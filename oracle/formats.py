@@ -1,4 +1,5 @@
 """Storage formats decoded in plain fp64 (oracle; test infrastructure only).
+(P1, P2, P3: the three pages listed, with their titles, in oracle/__init__.py.)
 
 Q4_K super-block (144 bytes, 256 weights), as fixed by the synthetic weight
 workload of the batched-decode pages (P1 names the weights "Q4_K"; the field

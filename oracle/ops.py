@@ -1,5 +1,6 @@
 """The per-layer operations of a decode step in plain fp64 (oracle; test
 infrastructure only).
+(P1, P2, P3: the three pages listed, with their titles, in oracle/__init__.py.)
 
 Each function is the textbook definition; none is blocked, fused or reordered.
 """

@@ -1,4 +1,5 @@
 """One batched decode step in plain fp64 (oracle; test infrastructure only).
+(P1, P2, P3: the three pages listed, with their titles, in oracle/__init__.py.)
 
 P1 "The weight read is the only term that does not scale" and P2 "The two
 halves of a decode-step memory bill" describe the step: the weights are

@@ -1,4 +1,5 @@
 // Split-K flash-decode GQA attention over a slot-arena KV cache, fp16 or Q8_0.
+// (P1, P2, P3: the three pages listed, with their titles, at the top of include/qkdec.h.)
 //
 // P2 "The two halves of a decode-step memory bill": each sequence reads its
 // whole private cache every step; P3 FAQ "Is KV cache quantization a kernel

@@ -1,4 +1,5 @@
 // Q4_K dequant-GEMM for a decode batch of 1..16 sequences on CDNA4 MFMA.
+// (P1, P2, P3: the three pages listed, with their titles, at the top of include/qkdec.h.)
 //
 // P1 "The weight read is the only term that does not scale": the step streams
 // each weight once and multiplies all sequences' hidden states against it.

@@ -1,4 +1,5 @@
 // KV-cache append (fp16 / Q8_0) and the fused RoPE + append of a decode step.
+// (P1, P2, P3: the three pages listed, with their titles, at the top of include/qkdec.h.)
 //
 // P3 "Why Q8 is close to free and where the sharp edges are": the quantized
 // cache stores one byte per element plus a per-block scale.  The Q8_0

@@ -1,5 +1,6 @@
 // Embedding gather (with the row statistics for the fused RMSNorm), the final
 // RMSNorm -> fp16, and the fp16 LM head with fused argmax.
+// (P1, P2, P3: the three pages listed, with their titles, at the top of include/qkdec.h.)
 //
 // P1 "The weight read is the only term that does not scale": the norms run
 // over one row per sequence; reading the output embedding is shared by the
