@@ -26,265 +26,11 @@
 // token's block scale.  Values: the per-(token, block) scale is folded into P
 // before the hi/lo split.  int8 -> fp16 is exact (byte permute into the
 // mantissa of 1024+128+x, then one packed subtract).
+#include "attn_dev.h"
 #include "common.h"
 #include "internal.h"
 
 namespace qk {
-
-template <int D>
-struct DimMap {
-  static constexpr int NQK = D / 32;   // QK MFMAs per 16-row set
-  static constexpr int NPV = D / 16;   // PV MFMAs (16-dim output tiles)
-};
-
-// int8 x 4 (one dword) -> two half2 (exact)
-__device__ __forceinline__ void i8x4_to_h2x2(uint32_t w, half2_t& lo, half2_t& hi) {
-  const uint32_t u = w ^ 0x80808080u;                              // b + 128
-  const uint32_t plo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
-  const uint32_t phi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
-  const half2_t off = {(half_t)-1152.f, (half_t)-1152.f};
-  lo = as_h2(plo) + off;
-  hi = as_h2(phi) + off;
-}
-
-__device__ __forceinline__ half8_t i8x8_to_h8(uint32_t w0, uint32_t w1) {
-  half2_t a, b, c, d;
-  i8x4_to_h2x2(w0, a, b);
-  i8x4_to_h2x2(w1, c, d);
-  half8_t r;
-  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
-  return r;
-}
-
-template <int D, bool Q8>
-struct KVFrag;
-
-template <int D>
-struct KVFrag<D, false> {
-  half8_t k[2][D / 32];
-  half8_t v[D / 16];
-};
-
-template <int D>
-struct KVFrag<D, true> {
-  uint32_t k[2][D / 32][2];
-  uint32_t v[D / 16][2];
-  uint32_t ks[D / 8];   // fp16 scales of tokens 8lg..8lg+7, D/32 blocks each (2 per dword)
-  uint32_t vs[D / 8];
-};
-
-struct AttnArgs {
-  const uint8_t* k;
-  const uint8_t* v;
-  const uint16_t* ks;
-  const uint16_t* vs;
-  int n_kv, cap, n_slots;
-  const int32_t* slot;
-  const int32_t* n_ctx;
-  int n_ctx_add;
-  const half_t* Q;
-  int Hq;
-  float scale_log2;
-  float* part_o;
-  float* part_ml;
-  int n_splits;
-};
-
-template <int D, bool Q8>
-__device__ __forceinline__ void load_kv(KVFrag<D, Q8>& f, const AttnArgs& a, size_t head_row0, int t0, int lg,
-                                        int m) {
-  // head_row0 = (slot * n_kv + g) * cap: index of token 0 of this head
-  if constexpr (!Q8) {
-    const half_t* kb = reinterpret_cast<const half_t*>(a.k) + head_row0 * D;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int tok = t0 + 8 * (m >> 2) + 4 * hf + (m & 3);
-      const half_t* row = kb + (size_t)tok * D + (D / 4) * lg;
-#pragma unroll
-      for (int j = 0; j < D / 32; ++j) f.k[hf][j] = *reinterpret_cast<const half8_t*>(row + 8 * j);
-    }
-    const half_t* vb = reinterpret_cast<const half_t*>(a.v) + head_row0 * D;  // [D][cap] of this head
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i)
-      f.v[i] = *reinterpret_cast<const half8_t*>(vb + (size_t)(16 * i + m) * a.cap + t0 + 8 * lg);
-  } else {
-    const uint8_t* kb = a.k + head_row0 * D;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int tok = t0 + 8 * (m >> 2) + 4 * hf + (m & 3);
-      const uint8_t* row = kb + (size_t)tok * D + 8 * lg;
-#pragma unroll
-      for (int j = 0; j < D / 32; ++j) {
-        const uint2 w = *reinterpret_cast<const uint2*>(row + 32 * j);
-        f.k[hf][j][0] = w.x;
-        f.k[hf][j][1] = w.y;
-      }
-    }
-    const uint8_t* vb = a.v + head_row0 * D;
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) {
-      const uint2 w = *reinterpret_cast<const uint2*>(vb + (size_t)(16 * i + m) * a.cap + t0 + 8 * lg);
-      f.v[i][0] = w.x;
-      f.v[i][1] = w.y;
-    }
-    const uint32_t* ksb = reinterpret_cast<const uint32_t*>(a.ks + (head_row0 + t0 + 8 * lg) * (D / 32));
-    const uint32_t* vsb = reinterpret_cast<const uint32_t*>(a.vs + (head_row0 + t0 + 8 * lg) * (D / 32));
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-      const u32x4 x = reinterpret_cast<const u32x4*>(ksb)[i];
-      const u32x4 y = reinterpret_cast<const u32x4*>(vsb)[i];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        f.ks[4 * i + e] = x[e];
-        f.vs[4 * i + e] = y[e];
-      }
-    }
-  }
-}
-
-// fp16 scale of local token e (0..7) and block j from the packed scale words
-template <int D>
-__device__ __forceinline__ float scale_at(const uint32_t (&w)[D / 8], int e, int j) {
-  const int idx = e * (D / 32) + j;  // fp16 index
-  const uint32_t word = w[idx >> 1];
-  return h2f((idx & 1) ? (word >> 16) : (word & 0xffffu));
-}
-
-template <int D, bool Q8>
-struct AttnState {
-  floatx4 o[D / 16];
-  float m;   // running max (log2 units), same in the 4 lane groups
-  float l;   // this lane group's share of the running denominator
-  int ex[D / 32];   // Q8_0: o of value block c is kept multiplied by 2^ex[c] (never increases)
-};
-
-// 2^k as a float, k clamped to the normal range
-__device__ __forceinline__ float exp2i(int k) {
-  k = k < -126 ? -126 : (k > 127 ? 127 : k);
-  return __builtin_bit_cast(float, (uint32_t)(k + 127) << 23);
-}
-
-// fp16 hi/lo operands of the value MFMA are formed from p * 2^kPScale so that
-// they stay clear of fp16 subnormals; the result is scaled back at the end
-constexpr int kPScale = 14;
-
-template <int D, bool Q8>
-__device__ __forceinline__ void attn_tile(AttnState<D, Q8>& st, const KVFrag<D, Q8>& f, const half8_t (&qf)[D / 32],
-                                          float scale_log2, int valid, int lg) {
-  // valid = number of tokens of this 32-token tile that are in range (1..32)
-  float sc[8];
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (!Q8) {
-#pragma unroll
-      for (int j = 0; j < D / 32; ++j) acc = mfma16x16x32(f.k[hf][j], qf[j], acc);
-    } else {
-#pragma unroll
-      for (int j = 0; j < D / 32; ++j) {
-        const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
-        const floatx4 part = mfma16x16x32(i8x8_to_h8(f.k[hf][j][0], f.k[hf][j][1]), qf[j], zero);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(scale_at<D>(f.ks, 4 * hf + i, j), part[i], acc[i]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sc[4 * hf + i] = acc[i] * scale_log2;
-  }
-  if (valid < 32) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (8 * lg + e >= valid) sc[e] = -__builtin_inff();
-  }
-  float tmax = sc[0];
-#pragma unroll
-  for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, sc[e]);
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-  const float mnew = fmaxf(st.m, tmax);
-  const float corr = exp2f(st.m - mnew);   // 0 on the first tile (m = -inf)
-  st.m = mnew;
-  float p[8];
-  float psum = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    p[e] = exp2f(sc[e] - mnew);
-    psum += p[e];
-  }
-  st.l = st.l * corr + psum;
-#pragma unroll
-  for (int i = 0; i < D / 16; ++i) {
-    st.o[i][0] *= corr; st.o[i][1] *= corr; st.o[i][2] *= corr; st.o[i][3] *= corr;
-  }
-  if constexpr (!Q8) {
-    half8_t phi, plo;
-    const float ps = exp2i(kPScale);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float pe = p[e] * ps;
-      const half_t h = (half_t)pe;
-      phi[e] = h;
-      plo[e] = (half_t)(pe - (float)h);
-    }
-    half8_t vf[D / 16];
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) vf[i] = f.v[i];
-    if (valid < 32) {  // never let values past the end reach the MFMA (0 * NaN)
-      const int lim = valid - 8 * lg;
-#pragma unroll
-      for (int i = 0; i < D / 16; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (e >= lim) vf[i][e] = (half_t)0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) {
-      st.o[i] = mfma16x16x32(vf[i], phi, st.o[i]);
-      st.o[i] = mfma16x16x32(vf[i], plo, st.o[i]);
-    }
-  } else {
-    const int lim = valid - 8 * lg;   // tokens of this lane at or past lim are out of range
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
-      // p * scale is brought near 2^13..2^14 by an exact power of two taken from
-      // the largest scale seen so far in this block, so the fp16 hi/lo pair
-      // keeps ~22 bits instead of sinking into fp16 subnormals
-      float vmax = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (e < lim) vmax = fmaxf(vmax, fabsf(scale_at<D>(f.vs, e, c)));
-      vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
-      vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
-      if (vmax > 0.f) {
-        const int ex = 13 - ((int)((__builtin_bit_cast(uint32_t, vmax) >> 23) & 255u) - 127);
-        if (ex < st.ex[c]) {
-          const float fr = exp2i(ex - st.ex[c]);
-          st.o[2 * c][0] *= fr; st.o[2 * c][1] *= fr; st.o[2 * c][2] *= fr; st.o[2 * c][3] *= fr;
-          st.o[2 * c + 1][0] *= fr; st.o[2 * c + 1][1] *= fr; st.o[2 * c + 1][2] *= fr; st.o[2 * c + 1][3] *= fr;
-          st.ex[c] = ex;
-        }
-      }
-      const float fc = exp2i(st.ex[c]);
-      half8_t phi, plo;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        // an out-of-range token's scale may hold any bits: never multiply it in
-        const float pv = (e < lim) ? p[e] * scale_at<D>(f.vs, e, c) * fc : 0.f;
-        const half_t h = (half_t)pv;
-        phi[e] = h;
-        plo[e] = (half_t)(pv - (float)h);
-      }
-#pragma unroll
-      for (int ii = 0; ii < 2; ++ii) {
-        const int i = 2 * c + ii;
-        half8_t vf = i8x8_to_h8(f.v[i][0], f.v[i][1]);
-        st.o[i] = mfma16x16x32(vf, phi, st.o[i]);
-        st.o[i] = mfma16x16x32(vf, plo, st.o[i]);
-      }
-    }
-  }
-}
 
 constexpr int kAttnWaves = 4;
 

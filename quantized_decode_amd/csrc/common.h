@@ -30,6 +30,12 @@ __device__ __forceinline__ half2_t pack_h2(float lo, float hi) {
   return __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
 }
 
+// 2^k as a float, k clamped to the normal range
+__device__ __forceinline__ float exp2i(int k) {
+  k = k < -126 ? -126 : (k > 127 ? 127 : k);
+  return __builtin_bit_cast(float, (uint32_t)(k + 127) << 23);
+}
+
 __device__ __forceinline__ floatx4 mfma16x16x32(const half8_t& a, const half8_t& b, const floatx4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }

@@ -1,0 +1,94 @@
+// Device code of the Q4_K dequant-GEMM shared by the per-launch kernels and
+// the persistent step kernel: fragment loads, the exact nibble decode and the
+// MFMA pair of one super-block (the layout and the arithmetic are described
+// at the top of gemm_q4k.hip).
+#pragma once
+
+#include "common.h"
+
+namespace qk {
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+
+struct Q4Frag {
+  u32x4 hdr;   // bytes 0-15 of the lane's block: d, dmin, scale groups
+  u32x4 q0;    // quant bytes 16+32g .. +15
+  u32x4 q1;    // quant bytes 32+32g .. +15
+};
+
+__device__ __forceinline__ void load_frag(Q4Frag& f, const uint8_t* __restrict__ blk, int g) {
+  f.hdr = *reinterpret_cast<const u32x4*>(blk);
+  f.q0 = *reinterpret_cast<const u32x4*>(blk + 16 + 32 * g);
+  f.q1 = *reinterpret_cast<const u32x4*>(blk + 32 + 32 * g);
+}
+
+// keep a constant in a VGPR so the mask-and-or pairs fuse into v_and_or_b32
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+struct NibbleMasks {
+  uint32_t lo, hi, magic;
+};
+
+// Decoded B operand for one MFMA: weights 8j..8j+7 of one 32-bit quant word,
+// times the sub-block scale.
+__device__ __forceinline__ half8_t decode_word(uint32_t w, const NibbleMasks& k, half2_t s1, half2_t c1, half2_t s16,
+                                              half2_t c16) {
+  const uint32_t w8 = w >> 8;
+  half2_t v0 = as_h2((w & k.lo) | k.magic);
+  half2_t v1 = as_h2((w & k.hi) | k.magic);
+  half2_t v2 = as_h2((w8 & k.lo) | k.magic);
+  half2_t v3 = as_h2((w8 & k.hi) | k.magic);
+  v0 = __builtin_elementwise_fma(v0, s1, c1);
+  v1 = __builtin_elementwise_fma(v1, s16, c16);
+  v2 = __builtin_elementwise_fma(v2, s1, c1);
+  v3 = __builtin_elementwise_fma(v3, s16, c16);
+  half8_t b;
+  b[0] = v0[0]; b[1] = v0[1]; b[2] = v1[0]; b[3] = v1[1];
+  b[4] = v2[0]; b[5] = v2[1]; b[6] = v3[0]; b[7] = v3[1];
+  return b;
+}
+
+// One super-block of one 16-row tile: sq = X . (sc*q), sm = xsums . m (per
+// sequence row), with d and dmin returned for the deferred accumulation.
+__device__ __forceinline__ void q4_superblock(const Q4Frag& f, const half8_t (&a)[8], const half4_t& axs, int g,
+                                              const NibbleMasks& k, floatx4& sq, floatx4& sm, float& d,
+                                              float& dmin) {
+  const uint32_t h0 = f.hdr[0], h1 = f.hdr[1], h2 = f.hdr[2], h3 = f.hdr[3];
+  d = h2f(h0 & 0xffffu);
+  dmin = h2f(h0 >> 16);
+  // the 24-bit scale group of sub-blocks 2g, 2g+1 sits at bit 24g of bytes 4..15
+  const uint32_t lo = (g < 2) ? h1 : (g == 2 ? h2 : h3);
+  const uint32_t hi = (g < 2) ? h2 : h3;
+  const uint32_t grp = __builtin_amdgcn_alignbit(hi, lo, (24u * (uint32_t)g) & 31u);
+  const float sc0 = (float)(grp & 63u), sc1 = (float)((grp >> 6) & 63u);
+  const float m0 = (float)((grp >> 12) & 63u), m1 = (float)((grp >> 18) & 63u);
+  const half2_t s1a = pack_h2(sc0, sc0), c1a = pack_h2(-1024.f * sc0, -1024.f * sc0);
+  const half2_t s16a = pack_h2(sc0 * 0.0625f, sc0 * 0.0625f), c16a = pack_h2(-64.f * sc0, -64.f * sc0);
+  const half2_t s1b = pack_h2(sc1, sc1), c1b = pack_h2(-1024.f * sc1, -1024.f * sc1);
+  const half2_t s16b = pack_h2(sc1 * 0.0625f, sc1 * 0.0625f), c16b = pack_h2(-64.f * sc1, -64.f * sc1);
+  const half2_t mm = pack_h2(m0, m1);
+  half4_t bm;
+  bm[0] = mm[0]; bm[1] = mm[1]; bm[2] = mm[0]; bm[3] = mm[1];
+  const uint32_t words[8] = {f.q0[0], f.q0[1], f.q0[2], f.q0[3], f.q1[0], f.q1[1], f.q1[2], f.q1[3]};
+  const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+  sm = __builtin_amdgcn_mfma_f32_16x16x16f16(axs, bm, zero, 0, 0, 0);
+  sq = zero;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sq = mfma16x16x32(a[j], decode_word(words[j], k, s1a, c1a, s16a, c16a), sq);
+#pragma unroll
+  for (int j = 4; j < 8; ++j) sq = mfma16x16x32(a[j], decode_word(words[j], k, s1b, c1b, s16b, c16b), sq);
+}
+
+
+// smallest s >= 0 with amax * 2^-s <= 65504 (the largest finite fp16)
+__device__ __forceinline__ int f16_block_shift(float amax) {
+  const int e = (int)((__builtin_bit_cast(uint32_t, amax) >> 23) & 255u) - 127;
+  int sh = e - 15 > 0 ? e - 15 : 0;
+  if (amax * exp2i(-sh) > 65504.f) ++sh;
+  return sh;
+}
+
+}  // namespace qk
