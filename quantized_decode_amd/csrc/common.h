@@ -81,6 +81,35 @@ __device__ __forceinline__ uint16_t f64_to_f16_bits(double x) {
 }
 
 
+
+// ---- device-scope (cross-work-group) access within one launch.  The L2 of
+// each XCD is not coherent with the others: data that another work-group of
+// the same launch wrote is read with sc1 loads (fetched from memory, never a
+// stale L2 line) and such data is written with sc1 stores (written through).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+}
+__device__ __forceinline__ u32x4 dev_load_b128(const void* base, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(dev_rsrc(base), byte_off, 0, 16));
+}
+__device__ __forceinline__ float dev_load(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void dev_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// load that is device-scope when DEV
+template <bool DEV>
+__device__ __forceinline__ float ld(const float* p) {
+  if constexpr (DEV) return dev_load(p);
+  else return *p;
+}
+template <bool DEV>
+__device__ __forceinline__ void st(float* p, float v) {
+  if constexpr (DEV) dev_store(p, v);
+  else *p = v;
+}
+
 // ---- sum-of-squares slots for the fused RMSNorm.
 // A residual-stream row of width H is covered by H/64 slots of 64 columns;
 // slot s of row b is ss[s * 16 + b].  The kernel that writes a row also
@@ -91,13 +120,14 @@ constexpr int kSsMaxSlots = 128;   // H <= 8192
 // Per-thread share of the fold in two halves, so that the loads can be
 // issued early and the adds done later: thread t of a 256-thread block covers
 // row t % 16 and slots t/16, t/16 + 16, ...
+template <bool DEV = false>
 __device__ __forceinline__ void ss_thread_load(const float* __restrict__ ss, int n_slots,
                                                float (&v)[kSsMaxSlots / 16]) {
   const int b = threadIdx.x & 15, s0 = threadIdx.x >> 4;
 #pragma unroll
   for (int j = 0; j < kSsMaxSlots / 16; ++j) {
     const int s = s0 + 16 * j;
-    v[j] = ss[(s < n_slots ? s : n_slots - 1) * 16 + b];
+    v[j] = ld<DEV>(ss + (s < n_slots ? s : n_slots - 1) * 16 + b);
   }
 }
 __device__ __forceinline__ float ss_thread_sum(const float (&v)[kSsMaxSlots / 16], int n_slots) {

@@ -51,6 +51,31 @@ hipError_t launch_gemm_q4k_xf32(const void* W, int64_t N, int64_t K, const float
                                 int force_kc = 0);
 hipError_t launch_gemm_q4k_swiglu(const void* W, int64_t F, int64_t K, const uint16_t* X, int64_t ldx, int B,
                                   float* A, int64_t lda, void* ws, hipStream_t st, int force_kc = 0);
+// One layer's O projection (+ residual), gate/up (+ RMSNorm, SwiGLU) and down
+// projection (+ residual) as one launch of dependent tasks (gemm_q4k.hip).
+// x and its sum-of-squares slots ss are updated in place (through x_mid and
+// ss_mid, the residual stream after the O projection); a is the fp32 SwiGLU
+// activation.  ws: ffn_tasks_workspace_bytes(), zero before the first launch
+// (every launch leaves its counters zero again).  err: the step's error word.
+struct FfnTaskLaunch {
+  int H, HQD, F, B;
+  float eps;
+  const void* w_o;
+  const void* w_gate_up;
+  const void* w_down;
+  const float* norm_ffn;
+  const uint16_t* o16;
+  float* x;
+  float* ss;
+  float* x_mid;
+  float* ss_mid;
+  float* a;
+  void* ws;
+  int32_t* err;
+};
+bool ffn_tasks_supported(int H, int HQD, int F);
+size_t ffn_tasks_workspace_bytes(int H, int HQD, int F, int B);
+hipError_t launch_ffn_tasks(const FfnTaskLaunch& T, hipStream_t st);
 hipError_t launch_dequant_q4k(const void* W, int64_t n_blocks, float* out, hipStream_t st);
 
 // ---- attention (attn_decode.hip)

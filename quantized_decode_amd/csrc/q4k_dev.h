@@ -91,4 +91,54 @@ __device__ __forceinline__ int f16_block_shift(float amax) {
   return sh;
 }
 
+// Tile of wave w in row group rg (WPB waves per work-group).
+//   MODE 0: tiles WPB*rg .. WPB*rg + WPB - 1 (one per wave).
+//   MODE 1 (SwiGLU): waves 0 .. H-1 (H = WPB/2) take gate tiles H*rg + w, waves
+//   H .. WPB-1 the up tiles F/16 later, so one work-group holds both halves of
+//   16*H outputs.
+template <int MODE, int WPB>
+__device__ __forceinline__ int tile_of(int rg, int w, int f_tiles) {
+  constexpr int H = WPB / 2;
+  if (MODE == 0) return rg * WPB + w;
+  return (w < H) ? (rg * H + w) : (f_tiles + rg * H + (w - H));
+}
+template <int MODE, int WPB>
+__device__ __forceinline__ bool tile_valid(int rg, int w, int n_tiles, int f_tiles) {
+  constexpr int H = WPB / 2;
+  if (MODE == 0) return rg * WPB + w < n_tiles;
+  return rg * H + (w % H) < f_tiles;
+}
+
+// How the activations arrive.
+enum XMode : int {
+  kXF16 = 0,         // fp16, used as they are
+  kXF32Blocked = 1,  // fp32, rounded to fp16 with one power-of-two offset per row and 256 values
+  kXNorm = 2,        // fp32 residual stream, RMSNorm applied while staging: f16(x * rinv * gamma)
+};
+
+struct GemmArgs {
+  const uint8_t* W;
+  const void* X;
+  const float* gamma;    // kXNorm: gains of the K inputs
+  const float* ss_in;    // kXNorm: sum-of-squares slots of the rows of X
+  float* Y;              // MODE 0 output (may alias residual)
+  const float* residual;
+  float* ss_out;         // MODE 0: sum-of-squares slots of Y (one slot per work-group), or null
+  float* A;              // MODE 1 output
+  float* part;           // split-K partial sums
+  unsigned* counters;    // split-K arrival counters (one per row group)
+  int64_t ldx, ldy, ldr, lda;
+  int n_tiles, kb, B, f_tiles, ss_slots;
+  float eps, inv_k;
+};
+
+// LDS scratch of one GEMM work item besides its staged activations.
+template <int WPB>
+struct GemmSmem {
+  float fac_d[16 * 16], fac_m[16 * 16];   // per (super-block i, row b) at i * 16 + b: factors of d and dmin
+  float s_red[WPB][16];                   // per-wave partial row statistics
+  floatx4 fin[WPB][64];                   // SwiGLU: gate and up accumulators exchanged between waves
+  int s_last;
+};
+
 }  // namespace qk
