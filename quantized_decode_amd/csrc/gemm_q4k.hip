@@ -501,10 +501,8 @@ __global__ void __launch_bounds__(64 * kTaskWaves) ffn_task_kernel(const FfnArgs
       const unsigned done = __hip_atomic_fetch_add(f.cnt + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (done == (unsigned)f.dn_groups - 1) {
         // every item of every projection has finished: clear the counters for the next launch
-        __hip_atomic_store(f.cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(f.cnt + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (int k = 0; k < f.dn_chunks; ++k)
-          __hip_atomic_store(f.cnt + 2 + k, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int k = 0; k < 2 + f.dn_chunks; ++k)
+          __hip_atomic_store(f.cnt + k, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }

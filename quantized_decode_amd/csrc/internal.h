@@ -78,15 +78,16 @@ size_t ffn_tasks_workspace_bytes(int H, int HQD, int F, int B);
 hipError_t launch_ffn_tasks(const FfnTaskLaunch& T, hipStream_t st);
 hipError_t launch_dequant_q4k(const void* W, int64_t n_blocks, float* out, hipStream_t st);
 
-// ---- attention (attn_decode.hip)
-// tokens per split work item
 // Largest number of row groups (work-groups along N) of one Q4_K GEMM launch:
 // at least 4 tiles of 16 rows per group, so N <= 16 * 4 * kGemmMaxGroups =
 // 2^20 rows (a SwiGLU launch covers gate and up: 2F <= 2^20).
 constexpr int kGemmMaxGroups = 16384;
 constexpr int64_t kGemmMaxRows = 16 * 4 * (int64_t)kGemmMaxGroups;
 
-constexpr int kAttnChunk = 256;
+// ---- attention (attn_decode.hip)
+// tokens per split work item (1024: of 256, 512 and 1024, the fastest for
+// B = 8, L = 2400 on MI355X: fewer, longer-lived waves)
+constexpr int kAttnChunk = 1024;
 inline int attn_n_splits(int capacity) { return (capacity + kAttnChunk - 1) / kAttnChunk; }
 // partial results per (b, q head, split): m, l, then head_dim values of o
 inline size_t attn_partials_bytes(int B, int n_q_heads, int head_dim, int capacity) {
