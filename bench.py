@@ -49,7 +49,8 @@ KV_BYTES_PER_TOKEN = {"f16": NL * HKV * D * 2 * 2, "q8_0": NL * HKV * D * 2 * 34
 # profiles/decode_step_b8_l2400_f16_kernel_stats.md.  A kernel changed since
 # has no entry, and its traffic is reported as null.
 COUNTED_TRAFFIC = {
-    ("attention (split + merge)", 8, 2400, "f16"): 81_135_160 + 1_474_567,
+    # split kernel 79,427,630 fetched + 411,648 written; merge 466,926 + 65,536
+    ("attention (split + merge)", 8, 2400, "f16"): 79_427_630 + 411_648 + 466_926 + 65_536,
 }
 
 

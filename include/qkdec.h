@@ -256,9 +256,7 @@ qkdec_status qkdec_step(const qkdec_model* m, const qkdec_kv_layer* kv, const in
                         int32_t* pos, int32_t* tok, int32_t B, float* logits, void* workspace,
                         size_t ws_bytes, void* stream);
 /* Synchronizes `stream`, returns QKDEC_E_CAPACITY if any step since the last
- * call hit the capacity, QKDEC_E_HIP if a step's in-kernel wait for another
- * work-group timed out (its results are then invalid), else QKDEC_OK; the flag
- * is cleared. */
+ * call hit the capacity, else QKDEC_OK; the flag is cleared. */
 qkdec_status qkdec_step_status(void* workspace, void* stream);
 
 /* Where a step leaves its intermediates inside `workspace` (byte offsets),

@@ -1,7 +1,6 @@
-// Device code of the flash-decode attention shared by the per-launch kernels
-// and the persistent step kernel: KV tile loads (fp16 or Q8_0), the online
-// softmax state and one 32-token tile on MFMA (described at the top of
-// attn_decode.hip).
+// Device code of the flash-decode attention: KV tile loads (fp16 or Q8_0),
+// the online softmax state and one 32-token tile on MFMA (described at the
+// top of attn_decode.hip).
 #pragma once
 
 #include "common.h"

@@ -82,74 +82,55 @@ __device__ __forceinline__ uint16_t f64_to_f16_bits(double x) {
 
 
 
-// ---- device-scope (cross-work-group) access within one launch.  The L2 of
-// each XCD is not coherent with the others: data that another work-group of
-// the same launch wrote is read with sc1 loads (fetched from memory, never a
-// stale L2 line) and such data is written with sc1 stores (written through).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
-}
-__device__ __forceinline__ u32x4 dev_load_b128(const void* base, uint32_t byte_off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(dev_rsrc(base), byte_off, 0, 16));
-}
-__device__ __forceinline__ float dev_load(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void dev_store(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// load that is device-scope when DEV
-template <bool DEV>
-__device__ __forceinline__ float ld(const float* p) {
-  if constexpr (DEV) return dev_load(p);
-  else return *p;
-}
-template <bool DEV>
-__device__ __forceinline__ void st(float* p, float v) {
-  if constexpr (DEV) dev_store(p, v);
-  else *p = v;
-}
-
 // ---- sum-of-squares slots for the fused RMSNorm.
-// A residual-stream row of width H is covered by H/64 slots of 64 columns;
-// slot s of row b is ss[s * 16 + b].  The kernel that writes a row also
-// writes its slots; a consumer folds them in a fixed order (deterministic).
-constexpr int kSsCols = 64;
-constexpr int kSsMaxSlots = 128;   // H <= 8192
+// A residual-stream row of width H is covered by H/16 slots of 16 columns
+// (one matrix-core tile of outputs, so one wave finishes a slot); slot s of
+// row b is ss[s * 16 + b].  The kernel that writes a row also writes its
+// slots; a consumer folds them in a fixed order (deterministic).
+constexpr int kSsCols = 16;
+constexpr int kSsMaxSlots = 512;   // H <= 8192
 
-// Per-thread share of the fold in two halves, so that the loads can be
-// issued early and the adds done later: thread t of a 256-thread block covers
-// row t % 16 and slots t/16, t/16 + 16, ...
-template <bool DEV = false>
-__device__ __forceinline__ void ss_thread_load(const float* __restrict__ ss, int n_slots,
-                                               float (&v)[kSsMaxSlots / 16]) {
-  const int b = threadIdx.x & 15, s0 = threadIdx.x >> 4;
+// Fold of the slots by all NT threads of a work-group, in two halves so that
+// the loads can be issued early and the adds done later.  Thread t loads the
+// float4 of rows 4q..4q+3 (q = t % 4) of slots t/4, t/4 + NT/4, ... (at most
+// SMAX slots: the register array is sized for it); load() then fold() leaves
+// one partial per (wave, row) in red[NT/64][16]; after a barrier rms_inv()
+// adds the waves' partials in order (deterministic).
+template <int NT, int SMAX>
+struct SsFold {
+  static constexpr int G = NT / 4;
+  static constexpr int J = SMAX > 0 ? (SMAX + G - 1) / G : 1;   // SMAX = 0: a caller that never folds
+  floatx4 v[J];
+  __device__ __forceinline__ void load(const float* __restrict__ ss, int n_slots) {
+    const int q = threadIdx.x & 3, s0 = threadIdx.x >> 2;
 #pragma unroll
-  for (int j = 0; j < kSsMaxSlots / 16; ++j) {
-    const int s = s0 + 16 * j;
-    v[j] = ld<DEV>(ss + (s < n_slots ? s : n_slots - 1) * 16 + b);
+    for (int j = 0; j < J; ++j) {
+      const int s = s0 + G * j;
+      v[j] = s < n_slots ? *reinterpret_cast<const floatx4*>(ss + (size_t)s * 16 + 4 * q)
+                         : floatx4{0.f, 0.f, 0.f, 0.f};
+    }
   }
-}
-__device__ __forceinline__ float ss_thread_sum(const float (&v)[kSsMaxSlots / 16], int n_slots) {
-  const int s0 = threadIdx.x >> 4;
-  float p = 0.f;
+  __device__ __forceinline__ void fold(float (*red)[16]) const {
+    floatx4 p = v[0];
 #pragma unroll
-  for (int j = 0; j < kSsMaxSlots / 16; ++j) p += (s0 + 16 * j < n_slots) ? v[j] : 0.f;
-  return p;
-}
+    for (int j = 1; j < J; ++j) p += v[j];
+    // lanes with the same q (lane % 4) hold the same rows
+#pragma unroll
+    for (int o = 4; o < 64; o <<= 1)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] += __shfl_xor(p[i], o);
+    const int lane = threadIdx.x & 63;
+    if (lane < 4)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[threadIdx.x >> 6][4 * lane + i] = p[i];
+  }
+};
 
-// Second half of the fold: combine the 16 thread parts of each row within a
-// wave, then write one value per (wave, row) to red[4][16].  The caller
-// synchronizes the block before rms_inv().
-__device__ __forceinline__ void ss_wave_fold(float p, float (*red)[16]) {
-  p += __shfl_xor(p, 16);
-  p += __shfl_xor(p, 32);
-  const int lane = threadIdx.x & 63;
-  if (lane < 16) red[threadIdx.x >> 6][lane] = p;
-}
-
+template <int NW>
 __device__ __forceinline__ float rms_inv(const float (*red)[16], int b, float inv_h, float eps) {
-  const float tot = (red[0][b] + red[1][b]) + (red[2][b] + red[3][b]);
+  float tot = red[0][b];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) tot += red[w][b];
   return 1.0f / sqrtf(tot * inv_h + eps);
 }
 

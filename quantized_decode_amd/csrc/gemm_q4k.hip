@@ -57,21 +57,10 @@ namespace qk {
 // several K chunks every work-group writes its partial sums with write-through
 // stores and the last one to arrive for a row group adds the chunks in chunk
 // order (so the result does not depend on arrival order).
-// One work item (row group rg, K chunk c).  DEV: the activations, statistics
-// and residual were written by other work-groups of the same launch (read
-// device-scope) and the outputs are read by others (written through).
-// before_x(): called after the weight loads are issued and before anything
-// that depends on other work-groups is read (a task waits there for its
-// inputs while its weights are already in flight).  Returns true if this
-// work-group finished the row group (wrote its outputs).
-struct NoWait {
-  __device__ void operator()() const {}
-};
-
-template <int KC, int MODE, int XMODE, int WPB, bool DEV, typename BeforeX = NoWait>
-__device__ bool gemm_item(const GemmArgs& a, int rg, int c, int n_chunks, half_t* xs, GemmSmem<WPB>& sm,
-                          const BeforeX& before_x = BeforeX()) {
-  constexpr bool kWeightsFirst = !__is_same(BeforeX, NoWait);
+// One work item (row group rg, K chunk c).  SMAX: most sum-of-squares slots
+// the kXNorm statistics fold holds (sizes its registers).
+template <int KC, int MODE, int XMODE, int WPB, int SMAX>
+__device__ void gemm_item(const GemmArgs& a, int rg, int c, int n_chunks, half_t* xs, GemmSmem<WPB>& sm) {
   constexpr int NT = 64 * WPB;                           // threads
   // super-blocks in flight per wave: 8 with 8-wave work-groups, 4 otherwise
   // (16 waves, and 4-wave work-groups packed four to a CU, leave 128 registers per lane)
@@ -98,20 +87,12 @@ __device__ bool gemm_item(const GemmArgs& a, int rg, int c, int n_chunks, half_t
   const int tl = tok ? tile_of<MODE, WPB>(rg, wave, a.f_tiles) : 0;   // keep addresses in bounds
   const uint8_t* tbase = a.W + ((size_t)tl * a.kb + sb0) * 2304 + (size_t)r * 144;
 
-  // ---- prologue: loads in the order they are needed (weights first when this
-  // item waits for its inputs)
+  // ---- prologue: loads in the order they are needed
   Q4Frag fr[P];
-  if constexpr (kWeightsFirst) {
-#pragma unroll
-    for (int p = 0; p < P; ++p) load_frag(fr[p], tbase + (size_t)p * 2304, g);
-    __builtin_amdgcn_sched_barrier(0);
-    before_x();
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  float ssv[kSsMaxSlots / 16];
+  SsFold<NT, SMAX> ssf;
   floatx4 gv[GL];
   if constexpr (XMODE == kXNorm) {
-    if (threadIdx.x < 256) ss_thread_load<DEV>(a.ss_in, a.ss_slots, ssv);
+    ssf.load(a.ss_in, a.ss_slots);
 #pragma unroll
     for (int k = 0; k < GL; ++k) {
       const int idx = threadIdx.x + NT * k;
@@ -129,32 +110,22 @@ __device__ bool gemm_item(const GemmArgs& a, int rg, int c, int n_chunks, half_t
       const int b = idx / (KC * 32), col = idx % (KC * 32);
       const size_t e0 = (size_t)b * a.ldx + (size_t)sb0 * 256 + 8 * col;   // element offset
       if constexpr (XMODE == kXF16) {
-        if constexpr (DEV)
-          hv[k] = __builtin_bit_cast(half8_t, dev_load_b128(a.X, (uint32_t)(2 * e0)));
-        else
-          hv[k] = *reinterpret_cast<const half8_t*>(reinterpret_cast<const half_t*>(a.X) + e0);
+        hv[k] = *reinterpret_cast<const half8_t*>(reinterpret_cast<const half_t*>(a.X) + e0);
       } else {
-        if constexpr (DEV) {
-          xv[k][0] = __builtin_bit_cast(floatx4, dev_load_b128(a.X, (uint32_t)(4 * e0)));
-          xv[k][1] = __builtin_bit_cast(floatx4, dev_load_b128(a.X, (uint32_t)(4 * e0 + 16)));
-        } else {
-          const float* src = reinterpret_cast<const float*>(a.X) + e0;
-          xv[k][0] = *reinterpret_cast<const floatx4*>(src);
-          xv[k][1] = *reinterpret_cast<const floatx4*>(src + 4);
-        }
+        const float* src = reinterpret_cast<const float*>(a.X) + e0;
+        xv[k][0] = *reinterpret_cast<const floatx4*>(src);
+        xv[k][1] = *reinterpret_cast<const floatx4*>(src + 4);
       }
     }
   };
   load_round(0);
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (!kWeightsFirst) {
 #pragma unroll
-    for (int p = 0; p < P; ++p) load_frag(fr[p], tbase + (size_t)p * 2304, g);
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  for (int p = 0; p < P; ++p) load_frag(fr[p], tbase + (size_t)p * 2304, g);
+  __builtin_amdgcn_sched_barrier(0);
 
   if constexpr (XMODE == kXNorm) {
-    if (threadIdx.x < 256) ss_wave_fold(ss_thread_sum(ssv, a.ss_slots), s_red);
+    ssf.fold(s_red);
 #pragma unroll
     for (int k = 0; k < GL; ++k) {
       const int idx = threadIdx.x + NT * k;
@@ -177,7 +148,7 @@ __device__ bool gemm_item(const GemmArgs& a, int rg, int c, int n_chunks, half_t
       if constexpr (XMODE == kXF16) {
         h = hv[k];
       } else if constexpr (XMODE == kXNorm) {
-        const float rinv = rms_inv(s_red, b, a.inv_k, a.eps);
+        const float rinv = rms_inv<WPB>(s_red, b, a.inv_k, a.eps);
         const float* gr = gls + 8 * col;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -285,7 +256,6 @@ __device__ bool gemm_item(const GemmArgs& a, int rg, int c, int n_chunks, half_t
   const int n = tile_of<MODE, WPB>(rg, wave, a.f_tiles) * 16 + r;   // this lane's output row
   const int n_total = a.n_tiles * 16;
   float res[4] = {0.f, 0.f, 0.f, 0.f};
-  bool finish = true;
   if (n_chunks > 1) {
     if (tok) {
 #pragma unroll
@@ -302,8 +272,7 @@ __device__ bool gemm_item(const GemmArgs& a, int rg, int c, int n_chunks, half_t
       sm.s_last = (__hip_atomic_fetch_add(&a.counters[rg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                    (unsigned)(n_chunks - 1));
     __syncthreads();
-    finish = sm.s_last;
-    if (!finish) return false;
+    if (!sm.s_last) return;
     // all chunks' partials (and the residual) in one batch of loads, then the
     // sum in chunk order
     const int nc = tok ? n : 0;
@@ -324,7 +293,7 @@ __device__ bool gemm_item(const GemmArgs& a, int rg, int c, int n_chunks, half_t
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int b = 4 * g + ii < B ? 4 * g + ii : B - 1;
-          res[ii] = ld<DEV>(a.residual + (size_t)b * a.ldr + nc);
+          res[ii] = a.residual[(size_t)b * a.ldr + nc];
         }
       }
 #pragma unroll
@@ -349,7 +318,7 @@ __device__ bool gemm_item(const GemmArgs& a, int rg, int c, int n_chunks, half_t
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int b = 4 * g + ii < B ? 4 * g + ii : B - 1;
-          res[ii] = ld<DEV>(a.residual + (size_t)b * a.ldr + nc);
+          res[ii] = a.residual[(size_t)b * a.ldr + nc];
         }
       }
     }
@@ -359,7 +328,7 @@ __device__ bool gemm_item(const GemmArgs& a, int rg, int c, int n_chunks, half_t
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int b = 4 * g + ii < B ? 4 * g + ii : B - 1;
-      res[ii] = ld<DEV>(a.residual + (size_t)b * a.ldr + nc);
+      res[ii] = a.residual[(size_t)b * a.ldr + nc];
     }
   }
 
@@ -370,10 +339,10 @@ __device__ bool gemm_item(const GemmArgs& a, int rg, int c, int n_chunks, half_t
       const int b = 4 * g + ii;
       const float v = acc[ii] + res[ii];
       sq[ii] = (tok && b < B) ? v * v : 0.f;
-      if (tok && b < B) st<DEV>(a.Y + (size_t)b * a.ldy + n, v);
+      if (tok && b < B) a.Y[(size_t)b * a.ldy + n] = v;
     }
-    if (a.ss_out) {
-      // every 4 waves' 64 columns make one sum-of-squares slot
+    if (a.ss_out && tok) {
+      // each wave's 16 columns make one sum-of-squares slot (zero for rows >= B)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         float t = sq[ii];
@@ -381,13 +350,7 @@ __device__ bool gemm_item(const GemmArgs& a, int rg, int c, int n_chunks, half_t
         t += __shfl_xor(t, 2);
         t += __shfl_xor(t, 4);
         t += __shfl_xor(t, 8);
-        if (r == 0) s_red[wave][4 * g + ii] = t;
-      }
-      __syncthreads();
-      if (threadIdx.x < 16 * (WPB / 4)) {
-        const int b = threadIdx.x & 15, j = threadIdx.x >> 4, w0 = 4 * j;
-        st<DEV>(a.ss_out + (rg * (WPB / 4) + j) * 16 + b,
-                (s_red[w0][b] + s_red[w0 + 1][b]) + (s_red[w0 + 2][b] + s_red[w0 + 3][b]));
+        if (r == 0) a.ss_out[(size_t)(n >> 4) * 16 + 4 * g + ii] = t;
       }
     }
   } else {
@@ -411,101 +374,18 @@ __device__ bool gemm_item(const GemmArgs& a, int rg, int c, int n_chunks, half_t
             const float ez = expf(z);
             sil = z * ez / (1.f + ez);
           }
-          st<DEV>(a.A + (size_t)b * a.lda + nf, sil * uvv[ii]);
+          a.A[(size_t)b * a.lda + nf] = sil * uvv[ii];
         }
       }
     }
   }
-  return true;
 }
 
-template <int KC, int MODE, int XMODE, int WPB>
+template <int KC, int MODE, int XMODE, int WPB, int SMAX>
 __global__ void __launch_bounds__(64 * WPB) gemm_q4k_kernel(const GemmArgs a) {
   extern __shared__ half_t xs[];
   __shared__ GemmSmem<WPB> sm;
-  gemm_item<KC, MODE, XMODE, WPB, false>(a, blockIdx.x, blockIdx.y, gridDim.y, xs, sm);
-}
-
-// ------------------------------------------------------- FFN block as tasks
-// O projection (+ residual) -> gate/up (+ RMSNorm, SwiGLU) -> down (+ residual)
-// of one layer in ONE launch.  Work-group i is one work item of one of the
-// three projections, in that order; an item that needs another item's output
-// waits on a counter that only lower-numbered work-groups increment.  Work-
-// groups start in index order, so every work-group it waits for is running or
-// done: the wait always ends (and is bounded anyway: a timeout sets the error
-// word instead of spinning for ever).  A waiting item has issued its weight
-// loads before it waits.  The gate/up items of one output group are adjacent,
-// so the down items of the first K chunk can start while gate/up still runs.
-constexpr int kTaskWaves = 8;
-constexpr unsigned kSpinLimit = 1u << 22;
-
-struct FfnArgs {
-  GemmArgs o, gu, dn;
-  int o_groups, o_chunks, gu_groups, gu_chunks, dn_groups, dn_chunks;
-  int gu_per_dn_chunk;       // gate/up row groups whose outputs make one down K chunk
-  unsigned* cnt;             // [0] O groups done, [1] down groups done, [2 + c] gate/up groups done for chunk c
-  int32_t* err;              // set to QKDEC_E_HIP if a wait timed out
-};
-
-__device__ __forceinline__ void task_signal(unsigned* c) {
-  __builtin_amdgcn_s_waitcnt(0);   // this thread's write-through stores are done
-  __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-struct TaskWait {
-  const unsigned* c;
-  unsigned target;
-  int32_t* err;
-  __device__ void operator()() const {
-    if (threadIdx.x == 0) {
-      unsigned spins = 0;
-      while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++spins > kSpinLimit) {
-          __hip_atomic_store(err, (int32_t)QKDEC_E_HIP, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-      }
-    }
-    __syncthreads();
-  }
-};
-
-template <int KCO, int KCG, int KCD>
-__global__ void __launch_bounds__(64 * kTaskWaves) ffn_task_kernel(const FfnArgs f) {
-  extern __shared__ half_t xs[];
-  __shared__ GemmSmem<kTaskWaves> sm;
-  int t = blockIdx.x;
-  const int n_o = f.o_groups * f.o_chunks, n_gu = f.gu_groups * f.gu_chunks;
-  if (t < n_o) {
-    const int rg = t / f.o_chunks, c = t % f.o_chunks;
-    if (gemm_item<KCO, 0, kXF16, kTaskWaves, true>(f.o, rg, c, f.o_chunks, xs, sm)) task_signal(f.cnt);
-    return;
-  }
-  t -= n_o;
-  if (t < n_gu) {
-    const int rg = t / f.gu_chunks, c = t % f.gu_chunks;
-    const TaskWait w{f.cnt, (unsigned)f.o_groups, f.err};
-    if (gemm_item<KCG, 1, kXNorm, kTaskWaves, true>(f.gu, rg, c, f.gu_chunks, xs, sm, w))
-      task_signal(f.cnt + 2 + rg / f.gu_per_dn_chunk);
-    return;
-  }
-  t -= n_gu;
-  const int c = t / f.dn_groups, rg = t % f.dn_groups;
-  const TaskWait w{f.cnt + 2 + c, (unsigned)f.gu_per_dn_chunk, f.err};
-  if (gemm_item<KCD, 0, kXF32Blocked, kTaskWaves, true>(f.dn, rg, c, f.dn_chunks, xs, sm, w)) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const unsigned done = __hip_atomic_fetch_add(f.cnt + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (done == (unsigned)f.dn_groups - 1) {
-        // every item of every projection has finished: clear the counters for the next launch
-        for (int k = 0; k < 2 + f.dn_chunks; ++k)
-          __hip_atomic_store(f.cnt + k, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
+  gemm_item<KC, MODE, XMODE, WPB, SMAX>(a, blockIdx.x, blockIdx.y, gridDim.y, xs, sm);
 }
 
 // Bit-exact dequantization of blocks in storage order (test export).
@@ -585,11 +465,11 @@ size_t gemm_workspace_bytes(int64_t n_rows, int64_t K, int B, bool swiglu) {
 }
 
 // 16-wave work-groups leave 128 registers per lane: K chunks up to 4 only.
-template <int MODE, int XMODE, int WPB>
+template <int MODE, int XMODE, int WPB, int SMAX>
 static hipError_t launch_kc(int kc, dim3 grid, size_t lds, hipStream_t st, const GemmArgs& a) {
-#define QK_GEMM_CASE(KC)                                                                              \
-  case KC:                                                                                            \
-    hipLaunchKernelGGL((gemm_q4k_kernel<KC, MODE, XMODE, WPB>), grid, dim3(64 * WPB), lds, st, a);    \
+#define QK_GEMM_CASE(KC)                                                                                \
+  case KC:                                                                                              \
+    hipLaunchKernelGGL((gemm_q4k_kernel<KC, MODE, XMODE, WPB, SMAX>), grid, dim3(64 * WPB), lds, st, a); \
     break;
   if constexpr (WPB == 16) {
     switch (kc) {
@@ -614,14 +494,22 @@ static hipError_t launch_kc(int kc, dim3 grid, size_t lds, hipStream_t st, const
   return hipGetLastError();
 }
 
-template <int MODE, int XMODE>
+template <int MODE, int XMODE, int SMAX>
 static hipError_t launch_wpb(int wpb, int kc, dim3 grid, size_t lds, hipStream_t st, const GemmArgs& a) {
   switch (wpb) {
-    case 4: return launch_kc<MODE, XMODE, 4>(kc, grid, lds, st, a);
-    case 8: return launch_kc<MODE, XMODE, 8>(kc, grid, lds, st, a);
-    case 16: return launch_kc<MODE, XMODE, 16>(kc, grid, lds, st, a);
+    case 4: return launch_kc<MODE, XMODE, 4, SMAX>(kc, grid, lds, st, a);
+    case 8: return launch_kc<MODE, XMODE, 8, SMAX>(kc, grid, lds, st, a);
+    case 16: return launch_kc<MODE, XMODE, 16, SMAX>(kc, grid, lds, st, a);
     default: return hipErrorInvalidValue;
   }
+}
+
+// kXNorm: the statistics fold sized for H <= 4096 (256 slots) or for the
+// largest H (kSsMaxSlots); the other modes do not fold.
+template <int MODE>
+static hipError_t launch_norm(int wpb, int kc, dim3 grid, size_t lds, hipStream_t st, const GemmArgs& a) {
+  if (a.ss_slots <= 256) return launch_wpb<MODE, kXNorm, 256>(wpb, kc, grid, lds, st, a);
+  return launch_wpb<MODE, kXNorm, kSsMaxSlots>(wpb, kc, grid, lds, st, a);
 }
 
 hipError_t launch_gemm(const GemmLaunch& L, hipStream_t st) {
@@ -658,12 +546,12 @@ hipError_t launch_gemm(const GemmLaunch& L, hipStream_t st) {
   const size_t lds = lds_bytes(L.B, cfg.kc, xmode);
   if (lds > 150 * 1024) return hipErrorInvalidValue;
   if (L.swiglu) {
-    if (xmode == kXNorm) return launch_wpb<1, kXNorm>(cfg.wpb, cfg.kc, grid, lds, st, a);
-    return launch_wpb<1, kXF16>(cfg.wpb, cfg.kc, grid, lds, st, a);
+    if (xmode == kXNorm) return launch_norm<1>(cfg.wpb, cfg.kc, grid, lds, st, a);
+    return launch_wpb<1, kXF16, 0>(cfg.wpb, cfg.kc, grid, lds, st, a);
   }
-  if (xmode == kXNorm) return launch_wpb<0, kXNorm>(cfg.wpb, cfg.kc, grid, lds, st, a);
-  if (xmode == kXF32Blocked) return launch_wpb<0, kXF32Blocked>(cfg.wpb, cfg.kc, grid, lds, st, a);
-  return launch_wpb<0, kXF16>(cfg.wpb, cfg.kc, grid, lds, st, a);
+  if (xmode == kXNorm) return launch_norm<0>(cfg.wpb, cfg.kc, grid, lds, st, a);
+  if (xmode == kXF32Blocked) return launch_wpb<0, kXF32Blocked, 0>(cfg.wpb, cfg.kc, grid, lds, st, a);
+  return launch_wpb<0, kXF16, 0>(cfg.wpb, cfg.kc, grid, lds, st, a);
 }
 
 hipError_t launch_gemm_q4k(const void* W, int64_t N, int64_t K, const uint16_t* X, int64_t ldx, int B, float* Y,
@@ -695,117 +583,6 @@ hipError_t launch_dequant_q4k(const void* W, int64_t n_blocks, float* out, hipSt
   if (n_blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL(dequant_q4k_kernel, dim3((unsigned)n_blocks), dim3(256), 0, st,
                      reinterpret_cast<const uint8_t*>(W), n_blocks, out);
-  return hipGetLastError();
-}
-
-// ------------------------------------------------- FFN task launch (host)
-// K chunks of the three projections (kTaskWaves waves per work-group): {O,
-// gate/up, down} = {2, 4, 6} for the full-size shapes, {1, 2, 6} where K is
-// smaller.
-struct FfnKc {
-  int o, g, d;
-};
-static FfnKc ffn_kc(int H, int HQD, int F) {
-  if (H % 1024 == 0 && HQD % 512 == 0 && F % 1536 == 0) return {2, 4, 6};
-  if (H % 512 == 0 && HQD % 256 == 0 && F % 1536 == 0) return {1, 2, 6};
-  return {0, 0, 0};
-}
-
-struct FfnLayout {
-  int o_groups, o_chunks, gu_groups, gu_chunks, dn_groups, dn_chunks;
-  size_t o_part, gu_part, dn_part, cnt, bytes;   // byte offsets of the areas
-};
-
-static FfnLayout ffn_layout(int H, int HQD, int F, int B) {
-  FfnLayout L{};
-  const FfnKc kc = ffn_kc(H, HQD, F);
-  L.o_groups = (H / 16 + kTaskWaves - 1) / kTaskWaves;
-  L.o_chunks = HQD / 256 / kc.o;
-  L.gu_groups = (F / 16 + kTaskWaves / 2 - 1) / (kTaskWaves / 2);
-  L.gu_chunks = H / 256 / kc.g;
-  L.dn_groups = L.o_groups;
-  L.dn_chunks = F / 256 / kc.d;
-  auto up = [](size_t n) { return (n + 255) / 256 * 256; };
-  size_t off = 0;
-  // each projection: its arrival counters (one per row group), then its partial sums
-  L.o_part = off;
-  off += up((size_t)L.o_groups * 4) + up((size_t)L.o_chunks * B * H * 4);
-  L.gu_part = off;
-  off += up((size_t)L.gu_groups * 4) + up((size_t)L.gu_chunks * B * 2 * F * 4);
-  L.dn_part = off;
-  off += up((size_t)L.dn_groups * 4) + up((size_t)L.dn_chunks * B * H * 4);
-  L.cnt = off;
-  off += up((size_t)(2 + L.dn_chunks) * 4);
-  L.bytes = off;
-  return L;
-}
-
-bool ffn_tasks_supported(int H, int HQD, int F) {
-  return ffn_kc(H, HQD, F).o != 0 && H % (16 * kTaskWaves) == 0 && H <= kSsMaxSlots * kSsCols;
-}
-
-size_t ffn_tasks_workspace_bytes(int H, int HQD, int F, int B) { return ffn_layout(H, HQD, F, B).bytes; }
-
-hipError_t launch_ffn_tasks(const FfnTaskLaunch& T, hipStream_t st) {
-  const int H = T.H, F = T.F, HQD = T.HQD, B = T.B;
-  const FfnLayout L = ffn_layout(H, HQD, F, B);
-  char* ws = reinterpret_cast<char*>(T.ws);
-  auto base = [&](int64_t n_rows, int64_t K, bool swiglu, const void* W, const void* X, int64_t ldx, size_t area,
-                  int n_groups) {
-    GemmArgs a{};
-    const int64_t n_tiles = swiglu ? 2 * (n_rows / 16) : n_rows / 16;
-    a.W = reinterpret_cast<const uint8_t*>(W);
-    a.X = X;
-    a.ldx = ldx;
-    a.n_tiles = (int)n_tiles;
-    a.kb = (int)(K / 256);
-    a.B = B;
-    a.f_tiles = (int)(n_tiles / 2);
-    a.ss_slots = (int)(K / kSsCols);
-    a.eps = T.eps;
-    a.inv_k = 1.0f / (float)K;
-    a.counters = reinterpret_cast<unsigned*>(ws + area);
-    a.part = reinterpret_cast<float*>(ws + area + (((size_t)n_groups * 4 + 255) / 256 * 256));
-    return a;
-  };
-  FfnArgs f{};
-  // O writes x_mid (gate/up reads it while down already writes x)
-  f.o = base(H, HQD, false, T.w_o, T.o16, HQD, L.o_part, L.o_groups);
-  f.o.Y = T.x_mid;
-  f.o.ldy = H;
-  f.o.residual = T.x;
-  f.o.ldr = H;
-  f.o.ss_out = T.ss_mid;
-  f.gu = base(F, H, true, T.w_gate_up, T.x_mid, H, L.gu_part, L.gu_groups);
-  f.gu.gamma = T.norm_ffn;
-  f.gu.ss_in = T.ss_mid;
-  f.gu.A = T.a;
-  f.gu.lda = F;
-  f.dn = base(H, F, false, T.w_down, T.a, F, L.dn_part, L.dn_groups);
-  f.dn.Y = T.x;
-  f.dn.ldy = H;
-  f.dn.residual = T.x_mid;
-  f.dn.ldr = H;
-  f.dn.ss_out = T.ss;
-  f.o_groups = L.o_groups;
-  f.o_chunks = L.o_chunks;
-  f.gu_groups = L.gu_groups;
-  f.gu_chunks = L.gu_chunks;
-  f.dn_groups = L.dn_groups;
-  f.dn_chunks = L.dn_chunks;
-  const FfnKc kc = ffn_kc(H, HQD, F);
-  f.gu_per_dn_chunk = kc.d * 256 / (16 * kTaskWaves / 2);
-  f.cnt = reinterpret_cast<unsigned*>(ws + L.cnt);
-  f.err = T.err;
-  const size_t lds = std::max({lds_bytes(B, kc.o, kXF16), lds_bytes(B, kc.g, kXNorm),
-                               lds_bytes(B, kc.d, kXF32Blocked)});
-  const int n_tasks = L.o_groups * L.o_chunks + L.gu_groups * L.gu_chunks + L.dn_groups * L.dn_chunks;
-  if (kc.o == 2)
-    hipLaunchKernelGGL((ffn_task_kernel<2, 4, 6>), dim3(n_tasks), dim3(64 * kTaskWaves), lds, st, f);
-  else if (kc.o == 1)
-    hipLaunchKernelGGL((ffn_task_kernel<1, 2, 6>), dim3(n_tasks), dim3(64 * kTaskWaves), lds, st, f);
-  else
-    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -1,0 +1,340 @@
+// Q4_K dequant-GEMM with K split over the waves of one work-group: the decode
+// step's projections.
+// (P1, P2, P3: the three pages listed, with their titles, at the top of include/qkdec.h.)
+//
+// P1 "The weight read is the only term that does not scale": every weight is
+// read once per step and multiplied against all B sequences' hidden states.
+// P1 "RDNA4 pads the batch dimension to 16 whether you fill it or not": the
+// sequences are the 16 rows of the matrix-core tile (v_mfma_f32_16x16x32_f16,
+// A = activations, B = decoded weights; the exact decode and the min-term MFMA
+// are those of gemm_q4k.hip, in q4k_dev.h).
+//
+// Work decomposition.  One work-group computes one output item: a tile of 16
+// weight rows (MODE 0), or the gate tile and the up tile of 16 SwiGLU outputs
+// (MODE 1).  Its S waves split the item's K super-blocks into S contiguous
+// ranges; their partial sums are added in LDS in wave order.  No item is split
+// across work-groups, so a launch needs no workspace, no arrival counters and
+// no second pass: the latency from the last weight load to the stored output
+// is one LDS exchange.  The price is that every work-group reads the whole
+// activation vector, from L2 (it was written by an earlier launch).
+//
+// Activations are built per wave and per super-block directly in the MFMA A
+// layout: lane (g, r) needs x[r][256 sb + 64 g .. + 63], i.e. 64 consecutive
+// values of one sequence row, which cover its two 32-value sub-blocks 2g and
+// 2g+1 (so the min-term sums need no exchange).  Modes:
+//   kXF16        fp16 activations as they are;
+//   kXNorm       fp32 residual-stream rows, RMSNorm applied on the fly
+//                (statistics folded once per work-group from the 16-column
+//                sum-of-squares slots);
+//   kXF32Blocked fp32 rows rounded to fp16 with one power-of-two offset per row
+//                and super-block (the offset is a factor of d and dmin).
+#include "common.h"
+#include "internal.h"
+#include "q4k_dev.h"
+
+namespace qk {
+
+struct WkArgs {
+  const uint8_t* W;
+  const void* X;         // [B][ldx] fp16 (kXF16) or fp32
+  const float* gamma;    // kXNorm: gains of the K inputs
+  const float* ss_in;    // kXNorm: 16-column sum-of-squares slots of the rows of X
+  float* Y;              // MODE 0 output (may alias residual)
+  const float* residual;
+  float* ss_out;         // MODE 0: slot of each output tile, or null
+  float* A;              // MODE 1 output
+  int64_t ldx, ldy, ldr, lda;
+  int kb, B, f_tiles, ss_slots;
+  float eps, inv_k;
+};
+
+// The A operand of super-block sb for lane (g, r): av (8 MFMA pieces), the
+// hi/lo sub-block sums axs, and this row's factors of d (fdr) and dmin (fmr).
+template <int XMODE>
+__device__ __forceinline__ void build_a(const WkArgs& a, int sb, int g, int r, float rinv, half8_t (&av)[8],
+                                        half4_t& axs, float& fdr, float& fmr) {
+  const bool live = r < a.B;
+  const size_t k0 = (size_t)sb * 256 + 64 * g;
+  fdr = 1.f;
+  if constexpr (XMODE == kXF16) {
+    const half_t* src = reinterpret_cast<const half_t*>(a.X) + (size_t)r * a.ldx + k0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      half8_t v = {};
+      if (live) v = *reinterpret_cast<const half8_t*>(src + 8 * j);
+      av[j] = v;
+    }
+  } else if constexpr (XMODE == kXNorm) {
+    const float* src = reinterpret_cast<const float*>(a.X) + (size_t)r * a.ldx + k0;
+    const float* gm = a.gamma + k0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {   // two halves of 32 values keep fewer registers in flight
+      floatx4 xv[8], gv[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        xv[q] = live ? *reinterpret_cast<const floatx4*>(src + 32 * h + 4 * q) : floatx4{0.f, 0.f, 0.f, 0.f};
+        gv[q] = *reinterpret_cast<const floatx4*>(gm + 32 * h + 4 * q);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        half8_t v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = norm_apply(xv[2 * j + e / 4][e % 4], rinv, gv[2 * j + e / 4][e % 4]);
+        av[4 * h + j] = v;
+      }
+    }
+  } else {
+    const float* src = reinterpret_cast<const float*>(a.X) + (size_t)r * a.ldx + k0;
+    floatx4 xv[16];
+    float am = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      xv[q] = live ? *reinterpret_cast<const floatx4*>(src + 4 * q) : floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) am = fmaxf(am, fabsf(xv[q][e]));
+    }
+    // the row's 256 values of this super-block are held by lanes r, r+16, r+32, r+48
+    am = fmaxf(am, __shfl_xor(am, 16));
+    am = fmaxf(am, __shfl_xor(am, 32));
+    const int sh = f16_block_shift(am);
+    const float inv = exp2i(-sh);
+    fdr = exp2i(sh);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      half8_t v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (half_t)(xv[2 * j + e / 4][e % 4] * inv);
+      av[j] = v;
+    }
+  }
+  // sums of sub-blocks 2g (pieces 0..3) and 2g+1 (pieces 4..7)
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      s0 += (float)av[j][e];
+      s1 += (float)av[4 + j][e];
+    }
+  // a super-block whose sub-block sums leave fp16's range stages them divided
+  // by 32 (32 values of at most 65504 then fit); dmin is multiplied back
+  float ms = fmaxf(fabsf(s0), fabsf(s1));
+  ms = fmaxf(ms, __shfl_xor(ms, 16));
+  ms = fmaxf(ms, __shfl_xor(ms, 32));
+  const bool big = ms > 65504.f;
+  if (big) {
+    s0 *= 0.03125f;
+    s1 *= 0.03125f;
+  }
+  fmr = big ? 32.f * fdr : fdr;
+  const half_t h0 = (half_t)s0, h1 = (half_t)s1;
+  axs[0] = h0;
+  axs[1] = h1;
+  axs[2] = (half_t)(s0 - (float)h0);
+  axs[3] = (half_t)(s1 - (float)h1);
+}
+
+// Waves per SIMD: fp16 activations fit 128 registers (four waves per SIMD);
+// fp32 activations (64 values, and 64 gains for the RMSNorm, per lane and
+// super-block in flight) take up to 256 (two waves per SIMD).
+template <int XMODE>
+constexpr int wk_waves_per_simd() {
+  return XMODE == kXF16 ? 4 : 2;
+}
+
+template <int MODE, int XMODE, int S, int P>
+__global__ void __launch_bounds__(64 * S, wk_waves_per_simd<XMODE>()) gemm_wk_kernel(const WkArgs a) {
+  constexpr int T = MODE == 1 ? 2 : 1;   // weight tiles per item
+  __shared__ floatx4 red[S][T][64];
+  __shared__ float s_part[4 * S][16];
+  __shared__ float s_rinv[16];
+  const int item = blockIdx.x;
+  const int tx = threadIdx.x, lane = tx & 63, wave = tx >> 6, g = lane >> 4, r = lane & 15;
+  const int kb = a.kb;
+  const int sb_begin = wave * kb / S, sb_end = (wave + 1) * kb / S;
+  const int nsb = sb_end - sb_begin;
+  int tile[T];
+  tile[0] = item;
+  if constexpr (T == 2) tile[1] = item + a.f_tiles;
+  auto wptr = [&](int tt, int sb) { return a.W + ((size_t)tile[tt] * kb + sb) * 2304 + (size_t)r * 144; };
+
+  // ---- weights of the first P super-blocks, then the row statistics
+  Q4Frag fr[P][T];
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+    if (p < nsb)
+#pragma unroll
+      for (int tt = 0; tt < T; ++tt) load_frag(fr[p][tt], wptr(tt, sb_begin + p), g);
+  float rinv = 1.f;
+  if constexpr (XMODE == kXNorm) {
+    // thread (j, b) adds slots j, j + 4S, ... of row b; then 16 threads add the
+    // 4S parts in order
+    const int b = tx & 15, j = tx >> 4;
+    float p = 0.f;
+    for (int s = j; s < a.ss_slots; s += 4 * S) p += a.ss_in[(size_t)s * 16 + b];
+    s_part[j][b] = p;
+    __syncthreads();
+    if (tx < 16) {
+      float tot = 0.f;
+      for (int k = 0; k < 4 * S; ++k) tot += s_part[k][tx];
+      s_rinv[tx] = 1.0f / sqrtf(tot * a.inv_k + a.eps);
+    }
+    __syncthreads();
+    rinv = r < a.B ? s_rinv[r] : 0.f;   // rows past B stay zero
+  }
+
+  // ---- main loop: one super-block per step, P weight loads in flight
+  const NibbleMasks km = {in_vgpr(0x000F000Fu), in_vgpr(0x00F000F0u), in_vgpr(0x64006400u)};
+  floatx4 acc[T];
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt) acc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int i0 = 0; i0 < nsb; i0 += P) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int i = i0 + p;
+      // one super-block at a time: its activation loads are not hoisted into
+      // the previous step (they would need another 32-64 registers)
+      __builtin_amdgcn_sched_barrier(0);
+      if (i < nsb) {
+        half8_t av[8];
+        half4_t axs;
+        float fdr, fmr;
+        build_a<XMODE>(a, sb_begin + i, g, r, rinv, av, axs, fdr, fmr);
+        // factors of the D rows 4g + ii come from lanes 4g + ii (g = 0)
+        floatx4 fd, fm;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          fd[ii] = __shfl(fdr, 4 * g + ii);
+          fm[ii] = __shfl(fmr, 4 * g + ii);
+        }
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) {
+          floatx4 sq, sm;
+          float d, dm;
+          q4_superblock(fr[p][tt], av, axs, g, km, sq, sm, d, dm);
+          if (i + P < nsb) load_frag(fr[p][tt], wptr(tt, sb_begin + i + P), g);
+          // d * fd and dmin * fm are exact (the factors are powers of two)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii)
+            acc[tt][ii] = __builtin_fmaf(d * fd[ii], sq[ii], __builtin_fmaf(-dm * fm[ii], sm[ii], acc[tt][ii]));
+        }
+      }
+    }
+  }
+
+  // ---- the S partial sums, added in wave order by wave 0
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt) red[wave][tt][lane] = acc[tt];
+  __syncthreads();
+  if (wave != 0) return;
+  floatx4 v[T];
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt) {
+    v[tt] = red[0][tt][lane];
+#pragma unroll
+    for (int w = 1; w < S; ++w) v[tt] += red[w][tt][lane];
+  }
+  // lane (g, r) holds outputs (sequence 4g + ii, row 16 item + r)
+  const int n = item * 16 + r;
+  if constexpr (MODE == 0) {
+    float sq[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int b = 4 * g + ii;
+      float y = v[0][ii];
+      if (b < a.B) {
+        if (a.residual) y += a.residual[(size_t)b * a.ldr + n];
+        a.Y[(size_t)b * a.ldy + n] = y;
+      }
+      sq[ii] = b < a.B ? y * y : 0.f;
+    }
+    if (a.ss_out) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        float t = sq[ii];
+        t += __shfl_xor(t, 1);
+        t += __shfl_xor(t, 2);
+        t += __shfl_xor(t, 4);
+        t += __shfl_xor(t, 8);
+        if (r == 0) a.ss_out[(size_t)item * 16 + 4 * g + ii] = t;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int b = 4 * g + ii;
+      if (b < a.B) {
+        const float z = v[0][ii];
+        float sil;
+        if (z >= 0.f) {
+          sil = z / (1.f + expf(-z));
+        } else {
+          const float ez = expf(z);
+          sil = z * ez / (1.f + ez);
+        }
+        a.A[(size_t)b * a.lda + n] = sil * v[1][ii];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launcher
+// Waves per work-group and super-blocks in flight per wave, by shape and
+// activation mode (MI355X, B = 8, the 6144x4096, 4096x4096, 2x12288x4096 and
+// 4096x12288 projections): fp16 activations take 8 waves (two work-groups per
+// CU at 128 registers); the fp32 modes, at up to 256 registers, 4 waves (two
+// work-groups per CU), or 8 for a long K (one work-group per CU, 6 super-
+// blocks per wave at K = 12288).
+WkConfig wk_config(int kb, bool swiglu, int xmode) {
+  WkConfig c{4, 2};
+  if (!swiglu && xmode == kXF16 && kb >= 8) c.s = 8;
+  if (!swiglu && xmode == kXF32Blocked && kb >= 32) c.s = 8;
+  return c;
+}
+
+template <int MODE, int XMODE>
+static void launch_mode(int s, int items, const WkArgs& a, hipStream_t st) {
+  if (s == 8)
+    hipLaunchKernelGGL((gemm_wk_kernel<MODE, XMODE, 8, 2>), dim3(items), dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((gemm_wk_kernel<MODE, XMODE, 4, 2>), dim3(items), dim3(256), 0, st, a);
+}
+
+hipError_t launch_gemm_wk(const GemmLaunch& L, hipStream_t st) {
+  const int kb = (int)(L.K / 256);
+  const int64_t items = L.n_rows / 16;   // SwiGLU: n_rows = F, one item per gate/up tile pair
+  const int xmode = L.x_f32 ? (L.gamma ? kXNorm : kXF32Blocked) : kXF16;
+  const WkConfig c = wk_config(kb, L.swiglu, xmode);
+  WkArgs a{};
+  a.W = reinterpret_cast<const uint8_t*>(L.W);
+  a.X = L.X;
+  a.gamma = L.gamma;
+  a.ss_in = L.ss_in;
+  a.Y = L.Y;
+  a.residual = L.residual;
+  a.ss_out = L.ss_out;
+  a.A = L.A;
+  a.ldx = L.ldx;
+  a.ldy = L.ldy;
+  a.ldr = L.ldr;
+  a.lda = L.lda;
+  a.kb = kb;
+  a.B = L.B;
+  a.f_tiles = (int)items;
+  a.ss_slots = (int)(L.K / kSsCols);
+  a.eps = L.eps;
+  a.inv_k = 1.0f / (float)L.K;
+  if (L.swiglu) {
+    if (xmode == kXNorm) launch_mode<1, kXNorm>(c.s, (int)items, a, st);
+    else launch_mode<1, kXF16>(c.s, (int)items, a, st);
+  } else if (xmode == kXNorm) {
+    launch_mode<0, kXNorm>(c.s, (int)items, a, st);
+  } else if (xmode == kXF32Blocked) {
+    launch_mode<0, kXF32Blocked>(c.s, (int)items, a, st);
+  } else {
+    launch_mode<0, kXF16>(c.s, (int)items, a, st);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qk

@@ -43,6 +43,14 @@ struct GemmLaunch {
   int force_wpb = 0;   // 0: waves per work-group chosen by shape (4, 8 or 16)
 };
 hipError_t launch_gemm(const GemmLaunch& L, hipStream_t st);
+// The same product with K split over the waves of one work-group per output
+// tile (gemm_wk.hip): no workspace.  Waves per work-group (s) and super-blocks
+// in flight per wave (p) by shape.
+struct WkConfig {
+  int s, p;
+};
+WkConfig wk_config(int kb, bool swiglu, int xmode);
+hipError_t launch_gemm_wk(const GemmLaunch& L, hipStream_t st);
 hipError_t launch_gemm_q4k(const void* W, int64_t N, int64_t K, const uint16_t* X, int64_t ldx, int B,
                            float* Y, int64_t ldy, const float* residual, int64_t ldr, void* ws, hipStream_t st,
                            int force_kc = 0);
@@ -51,31 +59,6 @@ hipError_t launch_gemm_q4k_xf32(const void* W, int64_t N, int64_t K, const float
                                 int force_kc = 0);
 hipError_t launch_gemm_q4k_swiglu(const void* W, int64_t F, int64_t K, const uint16_t* X, int64_t ldx, int B,
                                   float* A, int64_t lda, void* ws, hipStream_t st, int force_kc = 0);
-// One layer's O projection (+ residual), gate/up (+ RMSNorm, SwiGLU) and down
-// projection (+ residual) as one launch of dependent tasks (gemm_q4k.hip).
-// x and its sum-of-squares slots ss are updated in place (through x_mid and
-// ss_mid, the residual stream after the O projection); a is the fp32 SwiGLU
-// activation.  ws: ffn_tasks_workspace_bytes(), zero before the first launch
-// (every launch leaves its counters zero again).  err: the step's error word.
-struct FfnTaskLaunch {
-  int H, HQD, F, B;
-  float eps;
-  const void* w_o;
-  const void* w_gate_up;
-  const void* w_down;
-  const float* norm_ffn;
-  const uint16_t* o16;
-  float* x;
-  float* ss;
-  float* x_mid;
-  float* ss_mid;
-  float* a;
-  void* ws;
-  int32_t* err;
-};
-bool ffn_tasks_supported(int H, int HQD, int F);
-size_t ffn_tasks_workspace_bytes(int H, int HQD, int F, int B);
-hipError_t launch_ffn_tasks(const FfnTaskLaunch& T, hipStream_t st);
 hipError_t launch_dequant_q4k(const void* W, int64_t n_blocks, float* out, hipStream_t st);
 
 // Largest number of row groups (work-groups along N) of one Q4_K GEMM launch:

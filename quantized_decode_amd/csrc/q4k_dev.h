@@ -1,7 +1,7 @@
-// Device code of the Q4_K dequant-GEMM shared by the per-launch kernels and
-// the persistent step kernel: fragment loads, the exact nibble decode and the
-// MFMA pair of one super-block (the layout and the arithmetic are described
-// at the top of gemm_q4k.hip).
+// Device code of the Q4_K dequant-GEMM shared by both GEMM kernels (split-K
+// in gemm_q4k.hip, K split over waves in gemm_wk.hip): fragment loads, the
+// exact nibble decode and the MFMA pair of one super-block (the layout and
+// the arithmetic are described at the top of gemm_q4k.hip).
 #pragma once
 
 #include "common.h"

@@ -93,9 +93,6 @@ struct StepWs {
   int32_t* err;
   float* x;
   float* ss;
-  float* x_mid;      // FFN tasks: residual stream after the O projection
-  float* ss_mid;
-  void* ffn_ws;      // FFN tasks: split-K areas and task counters (null: separate launches)
   uint16_t* h;
   float* qkv;
   uint16_t* q16;
@@ -120,10 +117,6 @@ StepWs step_layout(const qkdec_model* m, int B, const qkdec_kv_layer* kv, char* 
   w.err = reinterpret_cast<int32_t*>(take(256));
   w.x = reinterpret_cast<float*>(take((size_t)B * m->hidden * 4));
   w.ss = reinterpret_cast<float*>(take((size_t)kSsMaxSlots * 16 * 4));
-  const bool tasks = ffn_tasks_supported(m->hidden, (int)hq, m->ffn);
-  w.x_mid = tasks ? reinterpret_cast<float*>(take((size_t)B * m->hidden * 4)) : nullptr;
-  w.ss_mid = tasks ? reinterpret_cast<float*>(take((size_t)kSsMaxSlots * 16 * 4)) : nullptr;
-  w.ffn_ws = tasks ? take(ffn_tasks_workspace_bytes(m->hidden, (int)hq, m->ffn, B)) : nullptr;
   w.h = reinterpret_cast<uint16_t*>(take((size_t)B * m->hidden * 2));
   w.qkv = reinterpret_cast<float*>(take((size_t)B * nqkv * 4));
   w.q16 = reinterpret_cast<uint16_t*>(take((size_t)B * hq * 2));
@@ -164,20 +157,13 @@ qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int3
     QK_TRY(launch_gemm(qkv, st));
     QK_TRY(launch_rope_append(kv[l], slot, pos, w.qkv, B, Hq, m->rope_base, w.q16, w.err, st));
     QK_TRY(launch_attn_decode(kv[l], slot, pos, B, w.q16, Hq, scale, nullptr, w.o16, w.attn_part, 1, st));
-    if (w.ffn_ws) {
-      // O projection, gate/up and down as one launch of dependent tasks
-      FfnTaskLaunch t{};
-      t.H = H; t.HQD = (int)hq; t.F = F; t.B = B; t.eps = m->rms_eps;
-      t.w_o = ly.w_o; t.w_gate_up = ly.w_gate_up; t.w_down = ly.w_down; t.norm_ffn = ly.norm_ffn;
-      t.o16 = w.o16; t.x = w.x; t.ss = w.ss; t.x_mid = w.x_mid; t.ss_mid = w.ss_mid; t.a = w.a;
-      t.ws = w.ffn_ws; t.err = w.err;
-      QK_TRY(launch_ffn_tasks(t, st));
-      continue;
-    }
+    // O projection: fp16 activations, K split over the waves of one work-group
+    // per output tile (no split-K round trips); the fp32-activation projections
+    // stage their activations once per work-group and split K across work-groups
     GemmLaunch o{};
     o.W = ly.w_o; o.n_rows = H; o.K = hq; o.X = w.o16; o.ldx = hq; o.B = B;
     o.Y = w.x; o.ldy = H; o.residual = w.x; o.ldr = H; o.ss_out = w.ss; o.ws = w.gemm_ws;
-    QK_TRY(launch_gemm(o, st));
+    QK_TRY(launch_gemm_wk(o, st));
     GemmLaunch gu{};
     gu.W = ly.w_gate_up; gu.n_rows = F; gu.K = H; gu.X = w.x; gu.x_f32 = true; gu.ldx = H; gu.B = B;
     gu.gamma = ly.norm_ffn; gu.ss_in = w.ss; gu.eps = m->rms_eps;
@@ -398,7 +384,7 @@ qkdec_status qkdec_step_status(void* workspace, void* stream) {
   const int32_t zero = 0;
   if (hipMemcpyAsync(workspace, &zero, sizeof(zero), hipMemcpyHostToDevice, st) != hipSuccess) return QKDEC_E_HIP;
   if (hipStreamSynchronize(st) != hipSuccess) return QKDEC_E_HIP;
-  return flag == QKDEC_E_HIP ? QKDEC_E_HIP : QKDEC_E_CAPACITY;
+  return QKDEC_E_CAPACITY;
 }
 
 qkdec_status qkdec_plan_create(qkdec_plan** plan, const qkdec_model* m, const qkdec_kv_layer* kv,

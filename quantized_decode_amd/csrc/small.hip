@@ -11,7 +11,7 @@
 namespace qk {
 
 // x[b] = E[tok[b]] in fp32 (a token outside [0, vocab) reads row 0), and the
-// sum-of-squares slots of x: hidden % 256 == 0, one wave per 64-column slot.
+// sum-of-squares slots of x (16 lanes per 16-column slot): hidden % 256 == 0.
 __global__ void __launch_bounds__(256) embed_kernel(const half_t* __restrict__ E, int hidden, int vocab,
                                                     const int32_t* tok, float* x, float* ss) {
   const int b = blockIdx.y;
@@ -21,8 +21,8 @@ __global__ void __launch_bounds__(256) embed_kernel(const half_t* __restrict__ E
   const float v = (float)E[(size_t)t * hidden + i];
   x[(size_t)b * hidden + i] = v;
   float q = v * v;
-  for (int o = 32; o >= 1; o >>= 1) q += __shfl_xor(q, o);
-  if ((threadIdx.x & 63) == 0) ss[(blockIdx.x * 4 + (threadIdx.x >> 6)) * 16 + b] = q;
+  for (int o = 8; o >= 1; o >>= 1) q += __shfl_xor(q, o);
+  if ((threadIdx.x & 15) == 0) ss[(blockIdx.x * 16 + (threadIdx.x >> 4)) * 16 + b] = q;
 }
 
 // h = f16(x * rinv * gamma) with rinv from the sum-of-squares slots of x;
@@ -33,14 +33,13 @@ __global__ void __launch_bounds__(256) rmsnorm_f16_kernel(const float* __restric
   __shared__ float red[4][16];
   const int b = blockIdx.y;
   const int i = blockIdx.x * 256 + threadIdx.x;
-  float sv[kSsMaxSlots / 16];
-  const int n_slots = hidden / kSsCols;
-  ss_thread_load(ss, n_slots, sv);
+  SsFold<256, kSsMaxSlots> f;
+  f.load(ss, hidden / kSsCols);
   const float xv = x[(size_t)b * hidden + i];
   const float gv = gamma[i];
-  ss_wave_fold(ss_thread_sum(sv, n_slots), red);
+  f.fold(red);
   __syncthreads();
-  h[(size_t)b * hidden + i] = norm_apply(xv, rms_inv(red, b, 1.0f / (float)hidden, eps), gv);
+  h[(size_t)b * hidden + i] = norm_apply(xv, rms_inv<4>(red, b, 1.0f / (float)hidden, eps), gv);
 }
 
 // ------------------------------------------------------------------ LM head
