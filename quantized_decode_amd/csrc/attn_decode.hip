@@ -5,8 +5,9 @@
 // whole private cache every step; P3 FAQ "Is KV cache quantization a kernel
 // change or a storage change?": a quantized cache is dequantized inside the
 // fused attention kernel.  One work-group of 4 waves handles one work item
-// (sequence b, KV head g, run of kAttnChunk tokens): wave w takes the run's
-// 32-token tiles w, w + 4, ...; the four waves' states are merged in LDS and
+// (sequence b, KV head g, run c of the sequence's 32-token tiles; the runs
+// split the tiles evenly, as many as fill the chip: attn_runs): wave w takes
+// the run's tiles w, w + 4, ...; the four waves' states are merged in LDS and
 // the merge of the runs uses their log-sum-exp weights (attn_combine_kernel).
 //
 // Both contractions run on MFMA v_mfma_f32_16x16x32_f16 with the G <= 16
@@ -42,9 +43,11 @@ __global__ void __launch_bounds__(64 * kAttnWaves) attn_split_kernel(AttnArgs a)
   int n = a.n_ctx[b] + a.n_ctx_add;
   if (n > a.cap) n = a.cap;
   if (n < 0 || s < 0 || s >= a.n_slots) n = 0;
-  const int t_begin = c * kAttnChunk;
-  if (t_begin >= n) return;
-  const int t_end = min(t_begin + kAttnChunk, n);
+  const int runs = attn_runs(n, a.runs_wanted, a.n_splits);
+  if (c >= runs) return;
+  const int tiles = (n + 31) / 32;
+  const int t_begin = 32 * (c * tiles / runs);
+  const int t_end = min(32 * ((c + 1) * tiles / runs), n);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lg = lane >> 4, r = lane & 15;
 
   half8_t qf[D / 32];
@@ -139,14 +142,14 @@ __global__ void __launch_bounds__(64 * kAttnWaves) attn_split_kernel(AttnArgs a)
 
 // O[b][h] = sum_j 2^(m_j - M) o_j / sum_j 2^(m_j - M) l_j over the splits.
 __global__ void attn_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
-                                    int n_splits, const int32_t* slot, const int32_t* n_ctx, int n_ctx_add,
-                                    int cap, int n_slots, int Hq, int D, float* O, half_t* O16) {
+                                    int n_splits, int runs_wanted, const int32_t* slot, const int32_t* n_ctx,
+                                    int n_ctx_add, int cap, int n_slots, int Hq, int D, float* O, half_t* O16) {
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   int n = n_ctx[b] + n_ctx_add;
   if (n > cap) n = cap;
   const int s = slot[b];
   if (n < 0 || s < 0 || s >= n_slots) n = 0;
-  const int ns = n > 0 ? (n + kAttnChunk - 1) / kAttnChunk : 0;
+  const int ns = attn_runs(n, runs_wanted, n_splits);
   const size_t row0 = ((size_t)b * Hq + h) * n_splits;
   float big = -__builtin_inff();
   for (int j = 0; j < ns; ++j) big = fmaxf(big, part_ml[2 * (row0 + j)]);
@@ -179,12 +182,15 @@ hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, con
   a.Q = reinterpret_cast<const half_t*>(Q);
   a.Hq = n_q_heads;
   a.scale_log2 = scale * 1.4426950408889634f;
-  a.n_splits = attn_n_splits(kv.capacity);
+  a.n_splits = attn_max_runs(kv.capacity, kv.n_kv_heads);
+  a.runs_wanted = attn_runs_wanted(B, kv.n_kv_heads);
   const int D = kv.head_dim;
   const size_t n_rows = (size_t)B * n_q_heads * a.n_splits;
   a.part_o = partials;
   a.part_ml = partials + n_rows * D;
-  const dim3 grid(a.n_splits, kv.n_kv_heads, B);
+  // runs past a sequence's own count return at once
+  const int max_runs = attn_runs(kv.capacity, a.runs_wanted, a.n_splits);
+  const dim3 grid(max_runs, kv.n_kv_heads, B);
   const bool q8 = kv.type == QKDEC_KV_Q8_0;
   if (D == 128) {
     if (q8) hipLaunchKernelGGL((attn_split_kernel<128, true>), grid, dim3(64 * kAttnWaves), 0, st, a);
@@ -196,7 +202,7 @@ hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, con
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(n_q_heads, B), dim3(D), 0, st, a.part_o, a.part_ml, a.n_splits,
-                     slot, n_ctx, n_ctx_add, kv.capacity, kv.n_slots, n_q_heads, D, O,
+                     a.runs_wanted, slot, n_ctx, n_ctx_add, kv.capacity, kv.n_slots, n_q_heads, D, O,
                      reinterpret_cast<half_t*>(O16));
   return hipGetLastError();
 }

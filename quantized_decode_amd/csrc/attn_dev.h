@@ -64,8 +64,24 @@ struct AttnArgs {
   float scale_log2;
   float* part_o;
   float* part_ml;
-  int n_splits;
+  int n_splits;      // partial-result rows per (b, q head): the most runs a sequence can have
+  int runs_wanted;   // runs per sequence this call aims at (see attn_runs)
 };
+
+// Runs of a sequence with n cached tokens (same in the split and merge
+// kernels): the wanted count, at least ceil(n / 1024), at most one per 8
+// tiles and at most max_runs; 0 for n <= 0.
+__host__ __device__ __forceinline__ int attn_runs(int n, int wanted, int max_runs) {
+  if (n <= 0) return 0;
+  const int tiles = (n + 31) / 32;
+  int r = (n + 1023) / 1024;
+  if (wanted > r) r = wanted;
+  const int by_tiles = tiles / 8 > 1 ? tiles / 8 : 1;
+  if (r > by_tiles) r = by_tiles;
+  if (r < (n + 1023) / 1024) r = (n + 1023) / 1024;   // never more than 1024 tokens per run
+  if (r > max_runs) r = max_runs;
+  return r;
+}
 
 template <int D, bool Q8>
 __device__ __forceinline__ void load_kv(KVFrag<D, Q8>& f, const AttnArgs& a, size_t head_row0, int t0, int lg,

@@ -68,13 +68,31 @@ constexpr int kGemmMaxGroups = 16384;
 constexpr int64_t kGemmMaxRows = 16 * 4 * (int64_t)kGemmMaxGroups;
 
 // ---- attention (attn_decode.hip)
-// tokens per split work item (1024: of 256, 512 and 1024, the fastest for
-// B = 8, L = 2400 on MI355X: fewer, longer-lived waves)
+// A sequence's n cached tokens (ceil(n/32) tiles of 32) are cut into runs of
+// whole tiles, spread evenly, one work item each.  Runs per sequence: enough
+// that the B * n_kv * runs work items reach kAttnTargetGroups (one per CU of
+// MI355X), at least ceil(n / kAttnChunk) (long contexts), at most one per 8
+// tiles (4 waves of 2 tiles at least) and at most kAttnMaxRuns (the partial-
+// result stride).  kAttnChunk = 1024: longer-lived waves were faster than 256
+// or 512 tokens per run at B = 8, L = 2400.
 constexpr int kAttnChunk = 1024;
-inline int attn_n_splits(int capacity) { return (capacity + kAttnChunk - 1) / kAttnChunk; }
-// partial results per (b, q head, split): m, l, then head_dim values of o
-inline size_t attn_partials_bytes(int B, int n_q_heads, int head_dim, int capacity) {
-  return (size_t)B * n_q_heads * attn_n_splits(capacity) * (size_t)(head_dim + 2) * sizeof(float);
+constexpr int kAttnTargetGroups = 256;
+// partial-result rows per (b, q head): independent of B, so a workspace sized
+// for one batch serves any smaller one
+inline int attn_max_runs(int capacity, int n_kv) {
+  const int by_len = (capacity + kAttnChunk - 1) / kAttnChunk;
+  const int by_fill = (kAttnTargetGroups + n_kv - 1) / n_kv;
+  return by_len > by_fill ? by_len : by_fill;
+}
+// runs wanted per sequence for a call with B sequences (before the per-
+// sequence limits)
+inline int attn_runs_wanted(int B, int n_kv) {
+  const int w = (kAttnTargetGroups + B * n_kv - 1) / (B * n_kv);
+  return w > 1 ? w : 1;
+}
+// partial results per (b, q head, run): m, l, then head_dim values of o
+inline size_t attn_partials_bytes(int B, int n_q_heads, int head_dim, int capacity, int n_kv) {
+  return (size_t)B * n_q_heads * attn_max_runs(capacity, n_kv) * (size_t)(head_dim + 2) * sizeof(float);
 }
 hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, const int32_t* n_ctx, int B,
                               const uint16_t* Q, int n_q_heads, float scale, float* O, uint16_t* O16,

@@ -122,7 +122,7 @@ StepWs step_layout(const qkdec_model* m, int B, const qkdec_kv_layer* kv, char* 
   w.q16 = reinterpret_cast<uint16_t*>(take((size_t)B * hq * 2));
   w.o16 = reinterpret_cast<uint16_t*>(take((size_t)B * hq * 2));
   w.a = reinterpret_cast<float*>(take((size_t)B * m->ffn * 4));
-  w.attn_part = reinterpret_cast<float*>(take(attn_partials_bytes(B, m->n_q_heads, m->head_dim, kv[0].capacity)));
+  w.attn_part = reinterpret_cast<float*>(take(attn_partials_bytes(B, m->n_q_heads, m->head_dim, kv[0].capacity, kv[0].n_kv_heads)));
   w.lm_part = take(lm_head_partials_bytes(m->vocab, B));
   size_t g = gemm_workspace_bytes(nqkv, m->hidden, B, false);
   g = std::max(g, gemm_workspace_bytes(m->hidden, hq, B, false));
@@ -290,7 +290,7 @@ qkdec_status qkdec_kv_append_q8_0(const qkdec_kv_layer* kv, const int32_t* slot,
 
 size_t qkdec_attn_workspace_size(int32_t B, int32_t n_q_heads, const qkdec_kv_layer* kv) {
   if (!kv || B < 1 || n_q_heads < 1 || kv->capacity < 1 || kv->head_dim < 1) return 0;
-  return attn_partials_bytes(B, n_q_heads, kv->head_dim, kv->capacity);
+  return attn_partials_bytes(B, n_q_heads, kv->head_dim, kv->capacity, kv->n_kv_heads);
 }
 
 qkdec_status qkdec_attn_decode(const qkdec_kv_layer* kv, const int32_t* slot, const int32_t* n_ctx, int32_t B,
@@ -303,7 +303,7 @@ qkdec_status qkdec_attn_decode(const qkdec_kv_layer* kv, const int32_t* slot, co
   if (n_q_heads < 1 || n_q_heads % kv->n_kv_heads != 0 || n_q_heads / kv->n_kv_heads > 16) return QKDEC_E_SHAPE;
   if (!(scale == scale)) return QKDEC_E_ARG;
   if (!aligned(Q, 16) || (O && !aligned(O, 16))) return QKDEC_E_ALIGN;
-  const size_t need = attn_partials_bytes(B, n_q_heads, kv->head_dim, kv->capacity);
+  const size_t need = attn_partials_bytes(B, n_q_heads, kv->head_dim, kv->capacity, kv->n_kv_heads);
   if (!workspace || ws_bytes < need) return QKDEC_E_WORKSPACE;
   if (!aligned(workspace, 16)) return QKDEC_E_ALIGN;
   clear_stale_error();

@@ -132,8 +132,9 @@ def test_attention_deterministic(qd):
 
 
 def test_attention_workspace_reused_across_calls(qd):
-    # the merge's arrival counters live in the workspace: consecutive calls with
-    # different lengths (one sequence empty, one negative) must each be exact
+    # the runs' partial results live in the workspace and the run count follows
+    # each sequence's length: consecutive calls with different lengths (one
+    # sequence empty, one negative) must each be exact
     import torch
     from quantized_decode_amd.tensors import dev, upload_cache
     bsz, hq, hkv, d, cap = 4, 32, 8, 128, 1024
