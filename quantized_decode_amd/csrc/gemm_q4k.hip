@@ -36,6 +36,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "kv_dev.h"
 #include "q4k_dev.h"
 
 namespace qk {
@@ -60,7 +61,7 @@ namespace qk {
 // One work item (row group rg, K chunk c).  SMAX: most sum-of-squares slots
 // the kXNorm statistics fold holds (sizes its registers).
 template <int KC, int MODE, int XMODE, int WPB, int SMAX>
-__device__ void gemm_item(const GemmArgs& a, int rg, int c, int n_chunks, half_t* xs, GemmSmem<WPB>& sm) {
+__device__ void gemm_item(const GemmArgs& a, int rg, int c, int n_chunks, half_t* xs, GemmSmem<WPB, MODE>& sm) {
   constexpr int NT = 64 * WPB;                           // threads
   // super-blocks in flight per wave: 8 with 8-wave work-groups, 4 otherwise
   // (16 waves, and 4-wave work-groups packed four to a CU, leave 128 registers per lane)
@@ -289,7 +290,7 @@ __device__ void gemm_item(const GemmArgs& a, int rg, int c, int n_chunks, half_t
           }
         }
       }
-      if (MODE == 0 && a.residual) {
+      if (MODE != 1 && a.residual) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int b = 4 * g + ii < B ? 4 * g + ii : B - 1;
@@ -314,7 +315,7 @@ __device__ void gemm_item(const GemmArgs& a, int rg, int c, int n_chunks, half_t
                                  __HIP_MEMORY_SCOPE_AGENT);
         acc[ii] = v;
       }
-      if (MODE == 0 && a.residual) {
+      if (MODE != 1 && a.residual) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int b = 4 * g + ii < B ? 4 * g + ii : B - 1;
@@ -323,7 +324,7 @@ __device__ void gemm_item(const GemmArgs& a, int rg, int c, int n_chunks, half_t
       }
     }
     if (threadIdx.x == 0) a.counters[rg] = 0u;
-  } else if (MODE == 0 && a.residual) {
+  } else if (MODE != 1 && a.residual) {
     const int nc = tok ? n : 0;
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
@@ -332,7 +333,94 @@ __device__ void gemm_item(const GemmArgs& a, int rg, int c, int n_chunks, half_t
     }
   }
 
-  if constexpr (MODE == 0) {
+  if constexpr (MODE == 2) {
+    // One head (WPB = head_dim / 16 tiles); wave w holds dims 16w + r of rows
+    // 4g + ii.  The fp32 projection is stored as it is (workspace views), then
+    // q and k are rotated (pair (i, i + D/2) sits in waves w and w ^ WPB/2),
+    // q goes out as fp16 and k, v are appended to the cache at pos.
+    const RopeAppendArgs& ra = a.ra;
+    constexpr int D = 16 * WPB, HALF = D / 2;
+    const int head = rg, d = 16 * wave + r;
+    const int n_kv = ra.n_kv;
+    const bool is_q = head < ra.Hq, is_v = head >= ra.Hq + n_kv;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+      if (4 * g + ii < B) a.Y[(size_t)(4 * g + ii) * a.ldy + n] = acc[ii];
+    if (!is_v) {
+      for (int t = threadIdx.x; t < B * HALF; t += NT) {
+        const int b = t / HALF, i = t % HALF;
+        float cs, sn;
+        rope_cos_sin(ra.pos[b], i, D, ra.rope_base, cs, sn);
+        sm.rope[b][i] = make_float2(cs, sn);
+      }
+    }
+    sm.fin[wave][lane] = acc;
+    __syncthreads();
+    float out[4];
+    if (!is_v) {
+      const floatx4 other = sm.fin[wave ^ (WPB / 2)][lane];
+      const int i = d % HALF;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const float2 c = sm.rope[4 * g + ii < B ? 4 * g + ii : 0][i];
+        // d < D/2: x_i cos - x_{i+D/2} sin; d >= D/2: x_{i+D/2} cos + x_i sin
+        out[ii] = d < HALF ? acc[ii] * c.x - other[ii] * c.y : acc[ii] * c.x + other[ii] * c.y;
+      }
+    } else {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) out[ii] = acc[ii];
+    }
+    if (is_q) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int b = 4 * g + ii;
+        if (b < B) ra.q16[((size_t)b * ra.Hq + head) * D + d] = f2h_bits(out[ii]);
+      }
+    } else {
+      const int kvh = is_v ? head - ra.Hq - n_kv : head - ra.Hq;
+      CacheRef c;
+      c.k = ra.k; c.v = ra.v; c.ks = ra.ks; c.vs = ra.vs;
+      c.n_kv = n_kv; c.cap = ra.cap; c.D = D; c.n_slots = ra.n_slots; c.q8 = ra.q8;
+      int sl[4], ps[4];
+      bool ok[4];
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int b = 4 * g + ii;
+        sl[ii] = b < B ? ra.slot[b] : 0;
+        ps[ii] = b < B ? ra.pos[b] : 0;
+        ok[ii] = b < B && sl[ii] >= 0 && sl[ii] < ra.n_slots && ps[ii] >= 0 && ps[ii] < ra.cap;
+        if (b < B && !ok[ii] && wave == 0 && r == 0) *ra.err = QKDEC_E_CAPACITY;
+      }
+      if (!ra.q8) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          if (ok[ii]) store_f16(c, is_v, sl[ii], kvh, ps[ii], d, out[ii]);
+      } else {
+        // a Q8_0 block is 32 dims: the 16 lanes of this wave's row group and
+        // the same lanes of the partner wave w ^ 1
+        double am[4];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          float m = fabsf(out[ii]);
+          m = fmaxf(m, __shfl_xor(m, 1));
+          m = fmaxf(m, __shfl_xor(m, 2));
+          m = fmaxf(m, __shfl_xor(m, 4));
+          m = fmaxf(m, __shfl_xor(m, 8));
+          if (r == 0) sm.s_red[wave][4 * g + ii] = m;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int b = 4 * g + ii;
+          am[ii] = (double)fmaxf(sm.s_red[wave][b], sm.s_red[wave ^ 1][b]);
+          int8_t q;
+          uint16_t dbits;
+          q8_encode((double)out[ii], am[ii], q, dbits);
+          if (ok[ii]) store_q8(c, is_v, sl[ii], kvh, ps[ii], d, q, dbits);
+        }
+      }
+    }
+  } else if constexpr (MODE == 0) {
     float sq[4];
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
@@ -384,7 +472,7 @@ __device__ void gemm_item(const GemmArgs& a, int rg, int c, int n_chunks, half_t
 template <int KC, int MODE, int XMODE, int WPB, int SMAX>
 __global__ void __launch_bounds__(64 * WPB) gemm_q4k_kernel(const GemmArgs a) {
   extern __shared__ half_t xs[];
-  __shared__ GemmSmem<WPB> sm;
+  __shared__ GemmSmem<WPB, MODE> sm;
   gemm_item<KC, MODE, XMODE, WPB, SMAX>(a, blockIdx.x, blockIdx.y, gridDim.y, xs, sm);
 }
 
@@ -432,9 +520,9 @@ struct GemmConfig {
   int kc, wpb;
 };
 
-GemmConfig gemm_config(int64_t n_tiles, int64_t kb, int B, bool swiglu, int xmode) {
+// The K chunk for a given number of waves per work-group.
+static int gemm_kc(int64_t n_tiles, int64_t kb, int B, bool swiglu, int xmode, int wpb) {
   static const int cands[] = {1, 2, 4, 6, 8, 12, 16};
-  const int wpb = (n_tiles >= 1024 || kb > 32) ? 8 : 4;
   const int64_t groups = n_groups_of(n_tiles, swiglu, wpb);
   const int bb = B > 8 ? B : 8;
   int best = 0;
@@ -444,7 +532,12 @@ GemmConfig gemm_config(int64_t n_tiles, int64_t kb, int B, bool swiglu, int xmod
     best = kc;
     if (kb / kc <= 8 && groups * (kb / kc) <= 1024) break;
   }
-  return {best ? best : 1, wpb};
+  return best ? best : 1;
+}
+
+GemmConfig gemm_config(int64_t n_tiles, int64_t kb, int B, bool swiglu, int xmode) {
+  const int wpb = (n_tiles >= 1024 || kb > 32) ? 8 : 4;
+  return {gemm_kc(n_tiles, kb, B, swiglu, xmode, wpb), wpb};
 }
 
 // The split-K arrival counters occupy a fixed area at the start of the
@@ -512,13 +605,7 @@ static hipError_t launch_norm(int wpb, int kc, dim3 grid, size_t lds, hipStream_
   return launch_wpb<MODE, kXNorm, kSsMaxSlots>(wpb, kc, grid, lds, st, a);
 }
 
-hipError_t launch_gemm(const GemmLaunch& L, hipStream_t st) {
-  const int64_t n_tiles = L.swiglu ? 2 * (L.n_rows / 16) : L.n_rows / 16;
-  const int kb = (int)(L.K / 256);
-  const int xmode = L.x_f32 ? (L.gamma ? kXNorm : kXF32Blocked) : kXF16;
-  GemmConfig cfg = gemm_config(n_tiles, kb, L.B, L.swiglu, xmode);
-  if (L.force_kc) cfg.kc = L.force_kc;
-  if (L.force_wpb) cfg.wpb = L.force_wpb;
+static GemmArgs gemm_args(const GemmLaunch& L, int64_t n_tiles, int kb) {
   GemmArgs a{};
   a.W = reinterpret_cast<const uint8_t*>(L.W);
   a.X = L.X;
@@ -542,6 +629,17 @@ hipError_t launch_gemm(const GemmLaunch& L, hipStream_t st) {
   a.ss_slots = (int)(L.K / kSsCols);
   a.eps = L.eps;
   a.inv_k = 1.0f / (float)L.K;
+  return a;
+}
+
+hipError_t launch_gemm(const GemmLaunch& L, hipStream_t st) {
+  const int64_t n_tiles = L.swiglu ? 2 * (L.n_rows / 16) : L.n_rows / 16;
+  const int kb = (int)(L.K / 256);
+  const int xmode = L.x_f32 ? (L.gamma ? kXNorm : kXF32Blocked) : kXF16;
+  GemmConfig cfg = gemm_config(n_tiles, kb, L.B, L.swiglu, xmode);
+  if (L.force_kc) cfg.kc = L.force_kc;
+  if (L.force_wpb) cfg.wpb = L.force_wpb;
+  const GemmArgs a = gemm_args(L, n_tiles, kb);
   const dim3 grid((unsigned)n_groups_of(n_tiles, L.swiglu, cfg.wpb), (unsigned)(kb / cfg.kc));
   const size_t lds = lds_bytes(L.B, cfg.kc, xmode);
   if (lds > 150 * 1024) return hipErrorInvalidValue;
@@ -552,6 +650,36 @@ hipError_t launch_gemm(const GemmLaunch& L, hipStream_t st) {
   if (xmode == kXNorm) return launch_norm<0>(cfg.wpb, cfg.kc, grid, lds, st, a);
   if (xmode == kXF32Blocked) return launch_wpb<0, kXF32Blocked, 0>(cfg.wpb, cfg.kc, grid, lds, st, a);
   return launch_wpb<0, kXF16, 0>(cfg.wpb, cfg.kc, grid, lds, st, a);
+}
+
+
+// QKV projection with the RoPE / append finish (MODE 2): one head per row
+// group, so head_dim / 16 waves per work-group; K chunks 1, 2 or 4.
+template <int WPB, int SMAX>
+static hipError_t launch_qkv_kc(int kc, dim3 grid, size_t lds, hipStream_t st, const GemmArgs& a) {
+  switch (kc) {
+    case 1: hipLaunchKernelGGL((gemm_q4k_kernel<1, 2, kXNorm, WPB, SMAX>), grid, dim3(64 * WPB), lds, st, a); break;
+    case 2: hipLaunchKernelGGL((gemm_q4k_kernel<2, 2, kXNorm, WPB, SMAX>), grid, dim3(64 * WPB), lds, st, a); break;
+    case 4: hipLaunchKernelGGL((gemm_q4k_kernel<4, 2, kXNorm, WPB, SMAX>), grid, dim3(64 * WPB), lds, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_qkv_rope(const GemmLaunch& L, const RopeAppendArgs& ra, int head_dim, hipStream_t st) {
+  const int64_t n_tiles = L.n_rows / 16;
+  const int kb = (int)(L.K / 256);
+  const int wpb = head_dim / 16;
+  if (!L.x_f32 || !L.gamma || L.residual || L.ss_out || (wpb != 4 && wpb != 8)) return hipErrorInvalidValue;
+  int kc = gemm_kc(n_tiles, kb, L.B, false, kXNorm, wpb);
+  if (kc > 4 || kb % kc) kc = kb % 4 == 0 ? 4 : (kb % 2 == 0 ? 2 : 1);
+  GemmArgs a = gemm_args(L, n_tiles, kb);
+  a.ra = ra;
+  const dim3 grid((unsigned)n_groups_of(n_tiles, false, wpb), (unsigned)(kb / kc));
+  const size_t lds = lds_bytes(L.B, kc, kXNorm);
+  const bool wide = a.ss_slots > 256;
+  if (wpb == 8) return wide ? launch_qkv_kc<8, kSsMaxSlots>(kc, grid, lds, st, a) : launch_qkv_kc<8, 256>(kc, grid, lds, st, a);
+  return wide ? launch_qkv_kc<4, kSsMaxSlots>(kc, grid, lds, st, a) : launch_qkv_kc<4, 256>(kc, grid, lds, st, a);
 }
 
 hipError_t launch_gemm_q4k(const void* W, int64_t N, int64_t K, const uint16_t* X, int64_t ldx, int B, float* Y,

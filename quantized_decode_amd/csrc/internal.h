@@ -43,6 +43,22 @@ struct GemmLaunch {
   int force_wpb = 0;   // 0: waves per work-group chosen by shape (4, 8 or 16)
 };
 hipError_t launch_gemm(const GemmLaunch& L, hipStream_t st);
+// The QKV projection of a decode step (RMSNorm fused, L.x_f32 + L.gamma),
+// finished per head: Y gets the fp32 projection, then q and k are rotated
+// (RoPE at pos), q is written as fp16 to q16 [B][Hq][head_dim] and k, v are
+// appended to the cache at (slot, pos).  One work-group row per head.
+struct RopeAppendArgs {
+  const int32_t* slot;   // [B] cache slot of each sequence
+  const int32_t* pos;    // [B] position of the new token
+  uint8_t *k, *v;        // cache of this layer (fp16 or Q8_0 codes)
+  uint16_t *ks, *vs;     // Q8_0 block scales
+  int n_kv, cap, n_slots, Hq;
+  bool q8;
+  float rope_base;
+  uint16_t* q16;         // rotated queries, fp16 bits
+  int32_t* err;          // set to QKDEC_E_CAPACITY for a position outside the cache
+};
+hipError_t launch_gemm_qkv_rope(const GemmLaunch& L, const RopeAppendArgs& ra, int head_dim, hipStream_t st);
 // The same product with K split over the waves of one work-group per output
 // tile (gemm_wk.hip): no workspace.  Waves per work-group (s) and super-blocks
 // in flight per wave (p) by shape.
@@ -101,10 +117,7 @@ hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, con
 // ---- KV append and RoPE (kv_append.hip)
 hipError_t launch_kv_append(const qkdec_kv_layer& kv, const int32_t* slot, const int32_t* pos, const float* k,
                             const float* v, int B, int32_t* err, hipStream_t st);
-// rotate q, k of a [B][(Hq + 2 Hkv) * D] QKV row at pos[b], write q as fp16 and
-// append k, v to the cache
-hipError_t launch_rope_append(const qkdec_kv_layer& kv, const int32_t* slot, const int32_t* pos, const float* qkv,
-                              int B, int n_q_heads, float rope_base, uint16_t* q16, int32_t* err, hipStream_t st);
+
 
 // ---- small kernels (small.hip)
 // x = E[tok] and its sum-of-squares slots ss (common.h); hidden % 256 == 0

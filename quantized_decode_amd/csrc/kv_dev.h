@@ -1,0 +1,102 @@
+// Device code of the KV-cache store shared by the append kernels and the QKV
+// projection's finishing step: fp16 rounding or the Q8_0 quantizer of one
+// 32-value block (the arithmetic is described at the top of kv_append.hip).
+#pragma once
+
+#include "common.h"
+
+namespace qk {
+
+// max over aligned groups of 32 lanes
+__device__ __forceinline__ double amax32(double v) {
+  for (int o = 16; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o, 32));
+  return v;
+}
+
+__device__ __forceinline__ int8_t q8_code(double x, double d) {
+  if (d == 0.0) return 0;
+  const double y = x / d;
+  const double t = trunc(y);
+  double r = t;
+  if (fabs(y - t) >= 0.5) r += (y > 0.0) ? 1.0 : -1.0;
+  if (r > 127.0) r = 127.0;
+  if (r < -127.0) r = -127.0;
+  return (int8_t)r;
+}
+
+struct CacheRef {
+  uint8_t* k;
+  uint8_t* v;
+  uint16_t* ks;
+  uint16_t* vs;
+  int n_kv, cap, D, n_slots;
+  bool q8;
+};
+
+// Element stores of dim d of (slot s, kv head g, position p), into K
+// (is_v = false) or into the transposed V: fp16 bits, or a Q8_0 code with its
+// block scale (written by the block's dim 0).
+__device__ __forceinline__ void store_f16(const CacheRef& c, bool is_v, int s, int g, int p, int d, float x) {
+  const size_t head = (size_t)s * c.n_kv + g;
+  const uint16_t h = f2h_bits(x);
+  if (!is_v) reinterpret_cast<uint16_t*>(c.k)[(head * c.cap + p) * c.D + d] = h;
+  else reinterpret_cast<uint16_t*>(c.v)[(head * c.D + d) * c.cap + p] = h;
+}
+__device__ __forceinline__ void store_q8(const CacheRef& c, bool is_v, int s, int g, int p, int d, int8_t q,
+                                         uint16_t dbits) {
+  const size_t head = (size_t)s * c.n_kv + g;
+  if (!is_v) {
+    reinterpret_cast<int8_t*>(c.k)[(head * c.cap + p) * c.D + d] = q;
+    if ((d & 31) == 0) c.ks[(head * c.cap + p) * (c.D / 32) + d / 32] = dbits;
+  } else {
+    reinterpret_cast<int8_t*>(c.v)[(head * c.D + d) * c.cap + p] = q;
+    if ((d & 31) == 0) c.vs[(head * c.cap + p) * (c.D / 32) + d / 32] = dbits;
+  }
+}
+
+// One Q8_0 block value: code of x for the block maximum amax (both fp64).
+__device__ __forceinline__ void q8_encode(double x, double amax, int8_t& q, uint16_t& dbits) {
+  dbits = f64_to_f16_bits(amax / 127.0);
+  q = q8_code(x, f16_bits_to_f64(dbits));
+}
+
+// Store value `x` of dim d of (slot, kv head g, pos) into K (is_v = false) or V.
+// For Q8_0 all 32 lanes of the dim's block must call this together.
+__device__ __forceinline__ void store_elem(const CacheRef& c, bool is_v, int s, int g, int p, int d, float x,
+                                           bool ok) {
+  if (!c.q8) {
+    if (ok) store_f16(c, is_v, s, g, p, d, x);
+  } else {
+    const double xd = (double)x;
+    int8_t q;
+    uint16_t dbits;
+    q8_encode(xd, amax32(fabs(xd)), q, dbits);
+    if (ok) store_q8(c, is_v, s, g, p, d, q, dbits);
+  }
+}
+
+// Rotary position embedding, rotate-half pairs (i, i + D/2): the angle of
+// pair i at position p, p * base^(-2i/D), is formed in fp64; cos and sin are
+// rounded once to fp32 and the rotation itself is fp32.
+__device__ __forceinline__ void rope_cos_sin(int p, int i, int D, float base, float& cs, float& sn) {
+  const double theta = pow((double)base, -2.0 * (double)i / (double)D);
+  const double ang = (double)p * theta;
+  cs = (float)cos(ang);
+  sn = (float)sin(ang);
+}
+
+__device__ __forceinline__ CacheRef cache_ref(const qkdec_kv_layer& kv) {
+  CacheRef c;
+  c.k = reinterpret_cast<uint8_t*>(kv.k);
+  c.v = reinterpret_cast<uint8_t*>(kv.v);
+  c.ks = reinterpret_cast<uint16_t*>(kv.k_scale);
+  c.vs = reinterpret_cast<uint16_t*>(kv.v_scale);
+  c.n_kv = kv.n_kv_heads;
+  c.cap = kv.capacity;
+  c.D = kv.head_dim;
+  c.n_slots = kv.n_slots;
+  c.q8 = kv.type == QKDEC_KV_Q8_0;
+  return c;
+}
+
+}  // namespace qk

@@ -5,6 +5,7 @@
 #pragma once
 
 #include "common.h"
+#include "internal.h"
 
 namespace qk {
 
@@ -92,20 +93,20 @@ __device__ __forceinline__ int f16_block_shift(float amax) {
 }
 
 // Tile of wave w in row group rg (WPB waves per work-group).
-//   MODE 0: tiles WPB*rg .. WPB*rg + WPB - 1 (one per wave).
+//   MODE 0 and 2: tiles WPB*rg .. WPB*rg + WPB - 1 (one per wave).
 //   MODE 1 (SwiGLU): waves 0 .. H-1 (H = WPB/2) take gate tiles H*rg + w, waves
 //   H .. WPB-1 the up tiles F/16 later, so one work-group holds both halves of
 //   16*H outputs.
 template <int MODE, int WPB>
 __device__ __forceinline__ int tile_of(int rg, int w, int f_tiles) {
   constexpr int H = WPB / 2;
-  if (MODE == 0) return rg * WPB + w;
+  if (MODE != 1) return rg * WPB + w;
   return (w < H) ? (rg * H + w) : (f_tiles + rg * H + (w - H));
 }
 template <int MODE, int WPB>
 __device__ __forceinline__ bool tile_valid(int rg, int w, int n_tiles, int f_tiles) {
   constexpr int H = WPB / 2;
-  if (MODE == 0) return rg * WPB + w < n_tiles;
+  if (MODE != 1) return rg * WPB + w < n_tiles;
   return rg * H + (w % H) < f_tiles;
 }
 
@@ -130,15 +131,21 @@ struct GemmArgs {
   int64_t ldx, ldy, ldr, lda;
   int n_tiles, kb, B, f_tiles, ss_slots;
   float eps, inv_k;
+  RopeAppendArgs ra;     // MODE 2 only
 };
 
-// LDS scratch of one GEMM work item besides its staged activations.
-template <int WPB>
+// LDS scratch of one GEMM work item besides its staged activations; MODE 2
+// adds the rotary (cos, sin) table.
+template <int WPB, int MODE = 0>
 struct GemmSmem {
   float fac_d[16 * 16], fac_m[16 * 16];   // per (super-block i, row b) at i * 16 + b: factors of d and dmin
   float s_red[WPB][16];                   // per-wave partial row statistics
   floatx4 fin[WPB][64];                   // SwiGLU: gate and up accumulators exchanged between waves
   int s_last;
+};
+template <int WPB>
+struct GemmSmem<WPB, 2> : GemmSmem<WPB, 0> {
+  float2 rope[16][64];                    // (cos, sin) per (sequence, pair), head_dim <= 128
 };
 
 }  // namespace qk

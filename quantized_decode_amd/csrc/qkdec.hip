@@ -154,8 +154,14 @@ qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int3
     qkv.W = ly.w_qkv; qkv.n_rows = nqkv; qkv.K = H; qkv.X = w.x; qkv.x_f32 = true; qkv.ldx = H; qkv.B = B;
     qkv.gamma = ly.norm_attn; qkv.ss_in = w.ss; qkv.eps = m->rms_eps;
     qkv.Y = w.qkv; qkv.ldy = nqkv; qkv.ws = w.gemm_ws;
-    QK_TRY(launch_gemm(qkv, st));
-    QK_TRY(launch_rope_append(kv[l], slot, pos, w.qkv, B, Hq, m->rope_base, w.q16, w.err, st));
+    // ... finished per head: RoPE, q -> fp16, k and v appended to the cache
+    RopeAppendArgs ra{};
+    ra.slot = slot; ra.pos = pos;
+    ra.k = reinterpret_cast<uint8_t*>(kv[l].k); ra.v = reinterpret_cast<uint8_t*>(kv[l].v);
+    ra.ks = reinterpret_cast<uint16_t*>(kv[l].k_scale); ra.vs = reinterpret_cast<uint16_t*>(kv[l].v_scale);
+    ra.n_kv = kv[l].n_kv_heads; ra.cap = kv[l].capacity; ra.n_slots = kv[l].n_slots; ra.Hq = Hq;
+    ra.q8 = kv[l].type == QKDEC_KV_Q8_0; ra.rope_base = m->rope_base; ra.q16 = w.q16; ra.err = w.err;
+    QK_TRY(launch_gemm_qkv_rope(qkv, ra, D, st));
     QK_TRY(launch_attn_decode(kv[l], slot, pos, B, w.q16, Hq, scale, nullptr, w.o16, w.attn_part, 1, st));
     // O projection: fp16 activations, K split over the waves of one work-group
     // per output tile (no split-K round trips); the fp32-activation projections
