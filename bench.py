@@ -49,8 +49,8 @@ KV_BYTES_PER_TOKEN = {"f16": NL * HKV * D * 2 * 2, "q8_0": NL * HKV * D * 2 * 34
 # profiles/decode_step_b8_l2400_f16_kernel_stats.md.  A kernel changed since
 # has no entry, and its traffic is reported as null.
 COUNTED_TRAFFIC = {
-    # split kernel 79,427,630 fetched + 411,648 written; merge 466,926 + 65,536
-    ("attention (split + merge)", 8, 2400, "f16"): 79_427_630 + 411_648 + 466_926 + 65_536,
+    # split kernel 82,747,964 fetched + 557,056 written; merge 590,825 + 65,536
+    ("attention (split + merge)", 8, 2400, "f16"): 82_747_964 + 557_056 + 590_825 + 65_536,
 }
 
 
@@ -151,10 +151,18 @@ def kernel_timing(qd, sd, dev_model, sm, batch, length, seed):
                       q4k_bytes(H, FFN) + batch * FFN * 4 + 2 * batch * H * 4),
     }
     out = {}
+    notes = {
+        "gemm_qkv": "ABI entry, fp16 activations (K over the waves of one work-group per tile); the step runs "
+                    "this shape with RMSNorm fused and the RoPE / KV-append finish (split-K)",
+        "gemm_o": "same kernel as the step's O projection",
+        "gemm_gate_up_swiglu": "ABI entry, fp16 activations (split-K); the step fuses the RMSNorm",
+        "gemm_down": "same kernel as the step's down projection",
+    }
     for name, (fn, nbytes) in kinds.items():
         _timed([lambda ly=layers[0]: fn(ly)], stream)          # first launch of this kernel: not timed
         ms = _timed([lambda ly=ly: fn(ly) for ly in layers], stream)
-        out[name] = {"launches_per_step": len(layers), "avg_ms": sum(ms) / len(ms), "bytes_per_launch": nbytes}
+        out[name] = {"launches_per_step": len(layers), "avg_ms": sum(ms) / len(ms), "bytes_per_launch": nbytes,
+                     "note": notes[name]}
 
     # attention over the 36 per-layer caches of the timed workload, n_ctx = L
     q = sd.f16_normal(g, (batch, HQ, D))
@@ -169,7 +177,9 @@ def kernel_timing(qd, sd, dev_model, sm, batch, length, seed):
     ms = _timed([lambda kv=kv: fa(kv) for kv in kvs], stream)
     kv_bytes = KV_BYTES_PER_TOKEN["f16" if kvs[0].type == 0 else "q8_0"] // NL
     out["attention (split + merge)"] = {"launches_per_step": len(kvs), "avg_ms": sum(ms) / len(ms),
-                                        "bytes_per_launch": batch * length * kv_bytes}
+                                        "bytes_per_launch": batch * length * kv_bytes,
+                                        "note": "same kernels as the step's attention (n_ctx = L here, L + 1 "
+                                                "in the step)"}
 
     tok = torch.empty(batch, dtype=torch.int32, device="cuda")
     lws = torch.zeros(qd.qkdec_lm_head_workspace_size(VOCAB, batch), dtype=torch.uint8, device="cuda")
@@ -181,6 +191,39 @@ def kernel_timing(qd, sd, dev_model, sm, batch, length, seed):
         v["GBps"] = v["bytes_per_launch"] / (v["avg_ms"] * 1e-3) / 1e9
         v["ms_per_step"] = v["avg_ms"] * v["launches_per_step"]
     return out
+
+
+def read_ceiling(gib=4):
+    """The box's practical streaming-read rate: a device-wide sum over `gib`
+    GiB (torch's reduction kernel, not part of the decode path), best of 3."""
+    import torch
+    n = gib << 30
+    buf = torch.ones(n // 8, dtype=torch.int64, device="cuda")
+    buf.sum()
+    best = None
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        buf.sum()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del buf
+    torch.cuda.empty_cache()
+    return {"bytes": n, "ms": best, "GBps": n / (best * 1e-3) / 1e9, "kernel": "torch int64 sum"}
+
+
+def clocks():
+    """Current shader and memory clocks as rocm-smi reports them (None if it
+    is not available)."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        card = next(iter(json.loads(out.stdout).values()))
+        return {k: v for k, v in card.items() if "sclk" in k or "mclk" in k or "fclk" in k}
+    except Exception:
+        return None
 
 
 def cpu_baseline(dims, dev_model, batch, length, seed, min_seconds=10.0):
@@ -316,6 +359,11 @@ def main():
                 "algorithmic_bytes_per_launch": dom["bytes_per_launch"],
                 "launches_per_step": dom["launches_per_step"]}
 
+    log("streaming-read ceiling (4 GiB) and clocks")
+    ceiling = read_ceiling()
+    for pt in results:
+        pt["frac_of_read_ceiling"] = pt["achieved_GBps"] / ceiling["GBps"]
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle on a bounded sample")
@@ -331,6 +379,7 @@ def main():
                                f"B={main_pt['batch']}, L={main_pt['context']}",
                    "batch": main_pt["batch"], "context": main_pt["context"], "kv": main_pt["kv"]},
         "achieved_GBps": main_pt["achieved_GBps"], "frac_of_8TBps": main_pt["frac_of_8TBps"],
+        "frac_of_read_ceiling": main_pt["frac_of_read_ceiling"], "read_ceiling": ceiling, "clocks": clocks(),
         "roofline": roofline, "kernels": kernels, "points": results, "cpu_baseline": cpu,
     }
     print(json.dumps(out))

@@ -93,9 +93,12 @@ int32_t qkdec_abi_version(void);
  * fixed 64 KiB area of split-K arrival counters, then the partial sums; every
  * call leaves the counters zero again, so one workspace serves calls of any
  * shapes it is large enough for).  Calls that share a workspace must not
- * overlap.
- * The K-chunk partial sums are added in a fixed order: results are
- * deterministic and independent of scheduling.
+ * overlap.  The workspace contract is common to the three GEMM entry points:
+ * qkdec_gemm_q4k itself computes each 16-row output tile in one work-group
+ * (K split over its waves, partial sums added in LDS) and does not touch it;
+ * the _xf32 and _swiglu variants split K across work-groups and use it.
+ * Partial sums are added in a fixed order: results are deterministic and
+ * independent of scheduling.
  */
 size_t qkdec_gemm_q4k_workspace_size(int64_t N, int64_t K, int32_t B);
 qkdec_status qkdec_gemm_q4k(const void* W, int64_t N, int64_t K,

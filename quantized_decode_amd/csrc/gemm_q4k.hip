@@ -633,6 +633,8 @@ static GemmArgs gemm_args(const GemmLaunch& L, int64_t n_tiles, int kb) {
 }
 
 hipError_t launch_gemm(const GemmLaunch& L, hipStream_t st) {
+  // fp16 activations without SwiGLU: one work-group per tile, K over its waves
+  if (!L.x_f32 && !L.swiglu) return launch_gemm_wk(L, st);
   const int64_t n_tiles = L.swiglu ? 2 * (L.n_rows / 16) : L.n_rows / 16;
   const int kb = (int)(L.K / 256);
   const int xmode = L.x_f32 ? (L.gamma ? kXNorm : kXF32Blocked) : kXF16;
@@ -648,8 +650,7 @@ hipError_t launch_gemm(const GemmLaunch& L, hipStream_t st) {
     return launch_wpb<1, kXF16, 0>(cfg.wpb, cfg.kc, grid, lds, st, a);
   }
   if (xmode == kXNorm) return launch_norm<0>(cfg.wpb, cfg.kc, grid, lds, st, a);
-  if (xmode == kXF32Blocked) return launch_wpb<0, kXF32Blocked, 0>(cfg.wpb, cfg.kc, grid, lds, st, a);
-  return launch_wpb<0, kXF16, 0>(cfg.wpb, cfg.kc, grid, lds, st, a);
+  return launch_wpb<0, kXF32Blocked, 0>(cfg.wpb, cfg.kc, grid, lds, st, a);
 }
 
 
@@ -680,14 +681,6 @@ hipError_t launch_gemm_qkv_rope(const GemmLaunch& L, const RopeAppendArgs& ra, i
   const bool wide = a.ss_slots > 256;
   if (wpb == 8) return wide ? launch_qkv_kc<8, kSsMaxSlots>(kc, grid, lds, st, a) : launch_qkv_kc<8, 256>(kc, grid, lds, st, a);
   return wide ? launch_qkv_kc<4, kSsMaxSlots>(kc, grid, lds, st, a) : launch_qkv_kc<4, 256>(kc, grid, lds, st, a);
-}
-
-hipError_t launch_gemm_q4k(const void* W, int64_t N, int64_t K, const uint16_t* X, int64_t ldx, int B, float* Y,
-                           int64_t ldy, const float* residual, int64_t ldr, void* ws, hipStream_t st, int force_kc) {
-  GemmLaunch L{};
-  L.W = W; L.n_rows = N; L.K = K; L.X = X; L.ldx = ldx; L.B = B;
-  L.Y = Y; L.ldy = ldy; L.residual = residual; L.ldr = ldr; L.ws = ws; L.force_kc = force_kc;
-  return launch_gemm(L, st);
 }
 
 hipError_t launch_gemm_q4k_xf32(const void* W, int64_t N, int64_t K, const float* X, int64_t ldx, int B, float* Y,

@@ -67,9 +67,6 @@ struct WkConfig {
 };
 WkConfig wk_config(int kb, bool swiglu, int xmode);
 hipError_t launch_gemm_wk(const GemmLaunch& L, hipStream_t st);
-hipError_t launch_gemm_q4k(const void* W, int64_t N, int64_t K, const uint16_t* X, int64_t ldx, int B,
-                           float* Y, int64_t ldy, const float* residual, int64_t ldr, void* ws, hipStream_t st,
-                           int force_kc = 0);
 hipError_t launch_gemm_q4k_xf32(const void* W, int64_t N, int64_t K, const float* X, int64_t ldx, int B,
                                 float* Y, int64_t ldy, const float* residual, int64_t ldr, void* ws, hipStream_t st,
                                 int force_kc = 0);

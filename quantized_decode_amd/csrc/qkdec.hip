@@ -226,7 +226,12 @@ qkdec_status qkdec_gemm_q4k(const void* W, int64_t N, int64_t K, const uint16_t*
   if (!workspace || ws_bytes < gemm_workspace_bytes(N, K, B, false)) return QKDEC_E_WORKSPACE;
   if (!aligned(workspace, 256)) return QKDEC_E_ALIGN;
   clear_stale_error();
-  return hip_status(launch_gemm_q4k(W, N, K, X, ldx, B, Y, ldy, residual, ldr, workspace, as_stream(stream)));
+  // one work-group per 16-row output tile, K split over its waves (the kernel
+  // of the decode step's O projection): the workspace is not touched
+  GemmLaunch L{};
+  L.W = W; L.n_rows = N; L.K = K; L.X = X; L.ldx = ldx; L.B = B;
+  L.Y = Y; L.ldy = ldy; L.residual = residual; L.ldr = ldr;
+  return hip_status(launch_gemm_wk(L, as_stream(stream)));
 }
 
 qkdec_status qkdec_gemm_q4k_xf32(const void* W, int64_t N, int64_t K, const float* X, int64_t ldx, int32_t B,
