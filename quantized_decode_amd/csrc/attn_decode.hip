@@ -35,8 +35,9 @@ namespace qk {
 
 constexpr int kAttnWaves = 4;
 
+// Q8_0: two waves per SIMD (see the run targets next to kAttnChunk)
 template <int D, bool Q8>
-__global__ void __launch_bounds__(64 * kAttnWaves) attn_split_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(64 * kAttnWaves, Q8 ? 2 : 1) attn_split_kernel(AttnArgs a) {
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = a.Hq / a.n_kv;
   const int s = a.slot[b];
@@ -183,7 +184,7 @@ hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, con
   a.Hq = n_q_heads;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.n_splits = attn_max_runs(kv.capacity, kv.n_kv_heads);
-  a.runs_wanted = attn_runs_wanted(B, kv.n_kv_heads);
+  a.runs_wanted = attn_runs_wanted(B, kv.n_kv_heads, kv.type == QKDEC_KV_Q8_0);
   const int D = kv.head_dim;
   const size_t n_rows = (size_t)B * n_q_heads * a.n_splits;
   a.part_o = partials;

@@ -83,24 +83,29 @@ constexpr int64_t kGemmMaxRows = 16 * 4 * (int64_t)kGemmMaxGroups;
 // ---- attention (attn_decode.hip)
 // A sequence's n cached tokens (ceil(n/32) tiles of 32) are cut into runs of
 // whole tiles, spread evenly, one work item each.  Runs per sequence: enough
-// that the B * n_kv * runs work items reach kAttnTargetGroups (one per CU of
-// MI355X), at least ceil(n / kAttnChunk) (long contexts), at most one per 8
-// tiles (4 waves of 2 tiles at least) and at most kAttnMaxRuns (the partial-
-// result stride).  kAttnChunk = 1024: longer-lived waves were faster than 256
-// or 512 tokens per run at B = 8, L = 2400.
+// that the B * n_kv * runs work items reach the target (fp16 cache: 256, one
+// work-group per CU of MI355X, the kernel holding 310 registers per lane;
+// Q8_0: 512, two per CU at 256 registers, its dequantizing tiles gaining more
+// from the second wave per SIMD than they lose to spills), at least
+// ceil(n / kAttnChunk) (long contexts), at most one per 8 tiles (4 waves of 2
+// tiles at least) and at most attn_max_runs (the partial-result stride).
+// kAttnChunk = 1024: longer-lived waves were faster than 256 or 512 tokens
+// per run at B = 8, L = 2400.
 constexpr int kAttnChunk = 1024;
-constexpr int kAttnTargetGroups = 256;
-// partial-result rows per (b, q head): independent of B, so a workspace sized
-// for one batch serves any smaller one
+constexpr int kAttnTargetF16 = 256;
+constexpr int kAttnTargetQ8 = 512;
+// partial-result rows per (b, q head): independent of B and of the cache
+// type, so a workspace sized for one batch serves any smaller one
 inline int attn_max_runs(int capacity, int n_kv) {
   const int by_len = (capacity + kAttnChunk - 1) / kAttnChunk;
-  const int by_fill = (kAttnTargetGroups + n_kv - 1) / n_kv;
+  const int by_fill = (kAttnTargetQ8 + n_kv - 1) / n_kv;
   return by_len > by_fill ? by_len : by_fill;
 }
 // runs wanted per sequence for a call with B sequences (before the per-
 // sequence limits)
-inline int attn_runs_wanted(int B, int n_kv) {
-  const int w = (kAttnTargetGroups + B * n_kv - 1) / (B * n_kv);
+inline int attn_runs_wanted(int B, int n_kv, bool q8) {
+  const int target = q8 ? kAttnTargetQ8 : kAttnTargetF16;
+  const int w = (target + B * n_kv - 1) / (B * n_kv);
   return w > 1 ? w : 1;
 }
 // partial results per (b, q head, run): m, l, then head_dim values of o

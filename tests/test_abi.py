@@ -92,8 +92,8 @@ def test_kv_and_attention_validation(lib):
     att = lib.qkdec_attn_decode
     kv = _kv()
     need = lib.qkdec_attn_workspace_size(8, 32, ctypes.byref(kv))
-    # rows for up to max(ceil(2432 / 1024), 256 / 8) = 32 runs per (sequence, head)
-    assert need == 8 * 32 * 32 * 130 * 4
+    # rows for up to max(ceil(2432 / 1024), 512 / 8) = 64 runs per (sequence, head)
+    assert need == 8 * 32 * 64 * 130 * 4
     assert att(ctypes.byref(kv), FAKE, FAKE, 8, FAKE, 30, 0.1, FAKE, None, FAKE, need, None) == -2   # 30 % 8
     assert att(ctypes.byref(kv), FAKE, FAKE, 8, FAKE, 256, 0.1, FAKE, None, FAKE, need, None) == -2  # group 32
     assert att(ctypes.byref(kv), FAKE, FAKE, 17, FAKE, 32, 0.1, FAKE, None, FAKE, need, None) == -2
