@@ -35,9 +35,10 @@ namespace qk {
 
 constexpr int kAttnWaves = 4;
 
-// Q8_0: two waves per SIMD (see the run targets next to kAttnChunk)
+// Two waves per SIMD: with the split key / value prefetch the fp16 kernel
+// fits 256 registers without spilling (see the run targets next to kAttnChunk)
 template <int D, bool Q8>
-__global__ void __launch_bounds__(64 * kAttnWaves, Q8 ? 2 : 1) attn_split_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs a) {
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = a.Hq / a.n_kv;
   const int s = a.slot[b];
@@ -71,21 +72,24 @@ __global__ void __launch_bounds__(64 * kAttnWaves, Q8 ? 2 : 1) attn_split_kernel
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) st.ex[c] = 127;
 
-  // this wave's tiles: wave, wave + 4, ... (the next one's loads are issued
-  // before the current one is processed)
+  // this wave's tiles: wave, wave + 4, ...  The next tile's keys are issued
+  // before the current tile is processed, its values once the current tile's
+  // softmax is done (two tiles of keys and values are never held at once)
   const int ntiles = (t_end - t_begin + 31) / 32;
   if (wave < ntiles) {
     KVFrag<D, Q8> buf[2];
-    load_kv<D, Q8>(buf[0], a, head_row0, t_begin + 32 * wave, lg, r);
+    load_k<D, Q8>(buf[0], a, head_row0, t_begin + 32 * wave, lg, r);
+    load_v<D, Q8>(buf[0], a, head_row0, t_begin + 32 * wave, lg, r);
     for (int it = wave; it < ntiles; it += 2 * kAttnWaves) {
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         const int i = it + p * kAttnWaves;
         if (i < ntiles) {
           const int nx = (i + kAttnWaves < ntiles) ? i + kAttnWaves : i;
-          load_kv<D, Q8>(buf[p ^ 1], a, head_row0, t_begin + 32 * nx, lg, r);
+          load_k<D, Q8>(buf[p ^ 1], a, head_row0, t_begin + 32 * nx, lg, r);
           const int t0 = t_begin + 32 * i;
-          attn_tile<D, Q8>(st, buf[p], qf, a.scale_log2, min(32, t_end - t0), lg);
+          attn_tile<D, Q8>(st, buf[p], qf, a.scale_log2, min(32, t_end - t0), lg,
+                           [&]() { load_v<D, Q8>(buf[p ^ 1], a, head_row0, t_begin + 32 * nx, lg, r); });
         }
       }
     }

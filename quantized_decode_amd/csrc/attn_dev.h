@@ -83,10 +83,11 @@ __host__ __device__ __forceinline__ int attn_runs(int n, int wanted, int max_run
   return r;
 }
 
+// Keys (and their Q8_0 scales) of the 32-token tile at t0; head_row0 =
+// (slot * n_kv + g) * cap is the index of token 0 of this head.
 template <int D, bool Q8>
-__device__ __forceinline__ void load_kv(KVFrag<D, Q8>& f, const AttnArgs& a, size_t head_row0, int t0, int lg,
-                                        int m) {
-  // head_row0 = (slot * n_kv + g) * cap: index of token 0 of this head
+__device__ __forceinline__ void load_k(KVFrag<D, Q8>& f, const AttnArgs& a, size_t head_row0, int t0, int lg,
+                                       int m) {
   if constexpr (!Q8) {
     const half_t* kb = reinterpret_cast<const half_t*>(a.k) + head_row0 * D;
 #pragma unroll
@@ -96,10 +97,6 @@ __device__ __forceinline__ void load_kv(KVFrag<D, Q8>& f, const AttnArgs& a, siz
 #pragma unroll
       for (int j = 0; j < D / 32; ++j) f.k[hf][j] = *reinterpret_cast<const half8_t*>(row + 8 * j);
     }
-    const half_t* vb = reinterpret_cast<const half_t*>(a.v) + head_row0 * D;  // [D][cap] of this head
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i)
-      f.v[i] = *reinterpret_cast<const half8_t*>(vb + (size_t)(16 * i + m) * a.cap + t0 + 8 * lg);
   } else {
     const uint8_t* kb = a.k + head_row0 * D;
 #pragma unroll
@@ -113,6 +110,26 @@ __device__ __forceinline__ void load_kv(KVFrag<D, Q8>& f, const AttnArgs& a, siz
         f.k[hf][j][1] = w.y;
       }
     }
+    const uint32_t* ksb = reinterpret_cast<const uint32_t*>(a.ks + (head_row0 + t0 + 8 * lg) * (D / 32));
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+      const u32x4 x = reinterpret_cast<const u32x4*>(ksb)[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f.ks[4 * i + e] = x[e];
+    }
+  }
+}
+
+// Values (and their Q8_0 scales) of the same tile, from the transposed cache.
+template <int D, bool Q8>
+__device__ __forceinline__ void load_v(KVFrag<D, Q8>& f, const AttnArgs& a, size_t head_row0, int t0, int lg,
+                                       int m) {
+  if constexpr (!Q8) {
+    const half_t* vb = reinterpret_cast<const half_t*>(a.v) + head_row0 * D;  // [D][cap] of this head
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i)
+      f.v[i] = *reinterpret_cast<const half8_t*>(vb + (size_t)(16 * i + m) * a.cap + t0 + 8 * lg);
+  } else {
     const uint8_t* vb = a.v + head_row0 * D;
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) {
@@ -120,17 +137,12 @@ __device__ __forceinline__ void load_kv(KVFrag<D, Q8>& f, const AttnArgs& a, siz
       f.v[i][0] = w.x;
       f.v[i][1] = w.y;
     }
-    const uint32_t* ksb = reinterpret_cast<const uint32_t*>(a.ks + (head_row0 + t0 + 8 * lg) * (D / 32));
     const uint32_t* vsb = reinterpret_cast<const uint32_t*>(a.vs + (head_row0 + t0 + 8 * lg) * (D / 32));
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) {
-      const u32x4 x = reinterpret_cast<const u32x4*>(ksb)[i];
       const u32x4 y = reinterpret_cast<const u32x4*>(vsb)[i];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        f.ks[4 * i + e] = x[e];
-        f.vs[4 * i + e] = y[e];
-      }
+      for (int e = 0; e < 4; ++e) f.vs[4 * i + e] = y[e];
     }
   }
 }
@@ -156,9 +168,13 @@ struct AttnState {
 // they stay clear of fp16 subnormals; the result is scaled back at the end
 constexpr int kPScale = 14;
 
-template <int D, bool Q8>
-__device__ __forceinline__ void attn_tile(AttnState<D, Q8>& st, const KVFrag<D, Q8>& f, const half8_t (&qf)[D / 32],
-                                          float scale_log2, int valid, int lg) {
+// One 32-token tile.  mid() is called once the scores and the softmax update
+// are done, before the value products (the caller issues the next tile's
+// value loads there, into registers this tile's keys no longer need).  The
+// fp16 values of out-of-range tokens are zeroed in place in f.
+template <int D, bool Q8, typename Mid>
+__device__ __forceinline__ void attn_tile(AttnState<D, Q8>& st, KVFrag<D, Q8>& f, const half8_t (&qf)[D / 32],
+                                          float scale_log2, int valid, int lg, const Mid& mid) {
   // valid = number of tokens of this 32-token tile that are in range (1..32)
   float sc[8];
 #pragma unroll
@@ -204,6 +220,9 @@ __device__ __forceinline__ void attn_tile(AttnState<D, Q8>& st, const KVFrag<D, 
   for (int i = 0; i < D / 16; ++i) {
     st.o[i][0] *= corr; st.o[i][1] *= corr; st.o[i][2] *= corr; st.o[i][3] *= corr;
   }
+  __builtin_amdgcn_sched_barrier(0);
+  mid();
+  __builtin_amdgcn_sched_barrier(0);
   if constexpr (!Q8) {
     half8_t phi, plo;
     const float ps = exp2i(kPScale);
@@ -214,21 +233,18 @@ __device__ __forceinline__ void attn_tile(AttnState<D, Q8>& st, const KVFrag<D, 
       phi[e] = h;
       plo[e] = (half_t)(pe - (float)h);
     }
-    half8_t vf[D / 16];
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) vf[i] = f.v[i];
     if (valid < 32) {  // never let values past the end reach the MFMA (0 * NaN)
       const int lim = valid - 8 * lg;
 #pragma unroll
       for (int i = 0; i < D / 16; ++i)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (e >= lim) vf[i][e] = (half_t)0.f;
+          if (e >= lim) f.v[i][e] = (half_t)0.f;
     }
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) {
-      st.o[i] = mfma16x16x32(vf[i], phi, st.o[i]);
-      st.o[i] = mfma16x16x32(vf[i], plo, st.o[i]);
+      st.o[i] = mfma16x16x32(f.v[i], phi, st.o[i]);
+      st.o[i] = mfma16x16x32(f.v[i], plo, st.o[i]);
     }
   } else {
     const int lim = valid - 8 * lg;   // tokens of this lane at or past lim are out of range

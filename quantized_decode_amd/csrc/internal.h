@@ -84,9 +84,8 @@ constexpr int64_t kGemmMaxRows = 16 * 4 * (int64_t)kGemmMaxGroups;
 // A sequence's n cached tokens (ceil(n/32) tiles of 32) are cut into runs of
 // whole tiles, spread evenly, one work item each.  Runs per sequence: enough
 // that the B * n_kv * runs work items reach the target (fp16 cache: 256, one
-// work-group per CU of MI355X, the kernel holding 310 registers per lane;
-// Q8_0: 512, two per CU at 256 registers, its dequantizing tiles gaining more
-// from the second wave per SIMD than they lose to spills), at least
+// per CU of MI355X; Q8_0: 512, its dequantizing tiles gaining from a second
+// work-group per CU; both kernels run two waves per SIMD), at least
 // ceil(n / kAttnChunk) (long contexts), at most one per 8 tiles (4 waves of 2
 // tiles at least) and at most attn_max_runs (the partial-result stride).
 // kAttnChunk = 1024: longer-lived waves were faster than 256 or 512 tokens
