@@ -183,6 +183,18 @@ __global__ void __launch_bounds__(64 * S, wk_waves_per_simd<XMODE>()) gemm_wk_ke
     rinv = r < a.B ? s_rinv[r] : 0.f;   // rows past B stay zero
   }
 
+  // the residual of wave 0's outputs, loaded now rather than after the sum
+  float resv[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (MODE == 0) {
+    if (wave == 0 && a.residual) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int b = 4 * g + ii;
+        if (b < a.B) resv[ii] = a.residual[(size_t)b * a.ldr + item * 16 + r];
+      }
+    }
+  }
+
   // ---- main loop: one super-block per step, P weight loads in flight
   const NibbleMasks km = {in_vgpr(0x000F000Fu), in_vgpr(0x00F000F0u), in_vgpr(0x64006400u)};
   floatx4 acc[T];
@@ -243,7 +255,7 @@ __global__ void __launch_bounds__(64 * S, wk_waves_per_simd<XMODE>()) gemm_wk_ke
       const int b = 4 * g + ii;
       float y = v[0][ii];
       if (b < a.B) {
-        if (a.residual) y += a.residual[(size_t)b * a.ldr + n];
+        if (a.residual) y += resv[ii];
         a.Y[(size_t)b * a.ldy + n] = y;
       }
       sq[ii] = b < a.B ? y * y : 0.f;
@@ -288,12 +300,19 @@ __global__ void __launch_bounds__(64 * S, wk_waves_per_simd<XMODE>()) gemm_wk_ke
 WkConfig wk_config(int kb, bool swiglu, int xmode) {
   WkConfig c{4, 2};
   if (!swiglu && xmode == kXF16 && kb >= 8) c.s = 8;
+  if (!swiglu && xmode == kXF16 && kb >= 16) c = {16, 1};
   if (!swiglu && xmode == kXF32Blocked && kb >= 32) c.s = 8;
   return c;
 }
 
 template <int MODE, int XMODE>
 static void launch_mode(int s, int items, const WkArgs& a, hipStream_t st) {
+  if constexpr (XMODE == kXF16 && MODE == 0) {
+    if (s == 16) {
+      hipLaunchKernelGGL((gemm_wk_kernel<MODE, XMODE, 16, 1>), dim3(items), dim3(1024), 0, st, a);
+      return;
+    }
+  }
   if (s == 8)
     hipLaunchKernelGGL((gemm_wk_kernel<MODE, XMODE, 8, 2>), dim3(items), dim3(512), 0, st, a);
   else
