@@ -105,9 +105,11 @@ struct SsFold {
     const int q = threadIdx.x & 3, s0 = threadIdx.x >> 2;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
+      // unconditional load of an in-range slot, then a select: no branch
+      // around a load (a branch would make later load waits conservative)
       const int s = s0 + G * j;
-      v[j] = s < n_slots ? *reinterpret_cast<const floatx4*>(ss + (size_t)s * 16 + 4 * q)
-                         : floatx4{0.f, 0.f, 0.f, 0.f};
+      const floatx4 w = *reinterpret_cast<const floatx4*>(ss + (size_t)(s < n_slots ? s : 0) * 16 + 4 * q);
+      v[j] = s < n_slots ? w : floatx4{0.f, 0.f, 0.f, 0.f};
     }
   }
   __device__ __forceinline__ void fold(float (*red)[16]) const {

@@ -48,6 +48,35 @@ struct WkArgs {
   float eps, inv_k;
 };
 
+// The hi/lo sums of sub-blocks 2g (pieces 0..3) and 2g+1 (pieces 4..7) of av
+// and the row's dmin factor; fdr is the row's d factor.
+__device__ __forceinline__ void a_sums(const half8_t (&av)[8], float fdr, half4_t& axs, float& fmr) {
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      s0 += (float)av[j][e];
+      s1 += (float)av[4 + j][e];
+    }
+  // a super-block whose sub-block sums leave fp16's range stages them divided
+  // by 32 (32 values of at most 65504 then fit); dmin is multiplied back
+  float ms = fmaxf(fabsf(s0), fabsf(s1));
+  ms = fmaxf(ms, __shfl_xor(ms, 16));
+  ms = fmaxf(ms, __shfl_xor(ms, 32));
+  const bool big = ms > 65504.f;
+  if (big) {
+    s0 *= 0.03125f;
+    s1 *= 0.03125f;
+  }
+  fmr = big ? 32.f * fdr : fdr;
+  const half_t h0 = (half_t)s0, h1 = (half_t)s1;
+  axs[0] = h0;
+  axs[1] = h1;
+  axs[2] = (half_t)(s0 - (float)h0);
+  axs[3] = (half_t)(s1 - (float)h1);
+}
+
 // The A operand of super-block sb for lane (g, r): av (8 MFMA pieces), the
 // hi/lo sub-block sums axs, and this row's factors of d (fdr) and dmin (fmr).
 template <int XMODE>
@@ -107,31 +136,7 @@ __device__ __forceinline__ void build_a(const WkArgs& a, int sb, int g, int r, f
       av[j] = v;
     }
   }
-  // sums of sub-blocks 2g (pieces 0..3) and 2g+1 (pieces 4..7)
-  float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      s0 += (float)av[j][e];
-      s1 += (float)av[4 + j][e];
-    }
-  // a super-block whose sub-block sums leave fp16's range stages them divided
-  // by 32 (32 values of at most 65504 then fit); dmin is multiplied back
-  float ms = fmaxf(fabsf(s0), fabsf(s1));
-  ms = fmaxf(ms, __shfl_xor(ms, 16));
-  ms = fmaxf(ms, __shfl_xor(ms, 32));
-  const bool big = ms > 65504.f;
-  if (big) {
-    s0 *= 0.03125f;
-    s1 *= 0.03125f;
-  }
-  fmr = big ? 32.f * fdr : fdr;
-  const half_t h0 = (half_t)s0, h1 = (half_t)s1;
-  axs[0] = h0;
-  axs[1] = h1;
-  axs[2] = (half_t)(s0 - (float)h0);
-  axs[3] = (half_t)(s1 - (float)h1);
+  a_sums(av, fdr, axs, fmr);
 }
 
 // Waves per SIMD: fp16 activations fit 128 registers (four waves per SIMD);
@@ -290,6 +295,277 @@ __global__ void __launch_bounds__(64 * S, wk_waves_per_simd<XMODE>()) gemm_wk_ke
   }
 }
 
+// Several output items per work-group.  Wave w owns super-blocks
+// [KW w, KW w + KW) of K (kb = S * KW) for every item, so it builds the A
+// operands of its K slice once and keeps them in registers; the weights of
+// PD items are in flight at a time, issued before anything else.  Each item's
+// S partial sums go to LDS; after one barrier wave i adds item i's partials in
+// wave order and finishes it (no split-K round trips, no workspace).  With
+// IPW items per work-group a launch of ceil(items / IPW) work-groups can be
+// resident on the chip at once.
+template <int MODE, int XMODE, int S, int KW, int IPW, int PD>
+__global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
+  constexpr int T = MODE == 1 ? 2 : 1;   // weight tiles per item
+  static_assert(IPW <= S && PD <= IPW, "one finishing wave per item");
+  // LDS: kXNorm first holds the normalized activations h [16][K + 8] (fp16),
+  // then, after a barrier, the partial sums red[IPW][T][S][64]
+  constexpr size_t kRedBytes = sizeof(floatx4) * IPW * T * S * 64;
+  constexpr size_t kHBytes = XMODE == kXNorm ? (size_t)16 * (S * KW * 256 + 8) * 2 : 0;
+  __shared__ __align__(16) char smem[kRedBytes > kHBytes ? kRedBytes : kHBytes];
+  auto red = reinterpret_cast<floatx4(*)[T][S][64]>(smem);
+  __shared__ float s_part[4 * S][16];
+  __shared__ float s_rinv[16];
+  const int tx = threadIdx.x, lane = tx & 63, wave = tx >> 6, g = lane >> 4, r = lane & 15;
+  const int kb = a.kb;
+  const int item0 = blockIdx.x * IPW;
+  const int n_items = a.f_tiles - item0 < IPW ? a.f_tiles - item0 : IPW;
+  const int sb0 = wave * KW;
+  // items past the launch's last one read the last one's weights again: every
+  // weight load is unconditional, so the compiler's in-order load counting
+  // never has to assume a shorter path and wait for the whole stream
+  auto wptr = [&](int it, int tt, int sb) {
+    const int tile = item0 + (it < n_items ? it : n_items - 1) + (tt ? a.f_tiles : 0);
+    return a.W + ((size_t)tile * kb + sb) * 2304 + (size_t)r * 144;
+  };
+
+  // Vector memory loads return in order, so everything small that the
+  // prologue waits on (RMSNorm statistics, gains, activations) is issued
+  // before the weight stream: waiting on it never waits on the weights.
+  constexpr int K = S * KW * 256, LDH = K + 8;
+  half8_t av[KW][8];
+  half4_t axs[KW];
+  floatx4 fd[KW], fm[KW];
+  // kXNorm: slots of the sum-of-squares fold, gains and x rows 0..7 of the
+  // thread's float4 columns tx + 64 S c (c < KW)
+  SsFold<64 * S, (XMODE == kXNorm ? K / kSsCols : 0)> ssf;   // the K inputs have K / 16 slots
+  floatx4 gv[XMODE == kXNorm ? KW : 1], xv[XMODE == kXNorm ? KW : 1][8];
+  const float* X32 = reinterpret_cast<const float*>(a.X);
+  if constexpr (XMODE == kXNorm) {
+    ssf.load(a.ss_in, a.ss_slots);
+#pragma unroll
+    for (int c = 0; c < KW; ++c) {
+      const int c4 = tx + 64 * S * c;
+      gv[c] = *reinterpret_cast<const floatx4*>(a.gamma + 4 * c4);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int bb = u < a.B ? u : a.B - 1;
+        xv[c][u] = *reinterpret_cast<const floatx4*>(X32 + (size_t)bb * a.ldx + 4 * c4);
+      }
+    }
+  } else if constexpr (XMODE == kXF16) {
+    const half_t* X16 = reinterpret_cast<const half_t*>(a.X);
+    const int rr = r < a.B ? r : a.B - 1;
+#pragma unroll
+    for (int p = 0; p < KW; ++p)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        av[p][j] = *reinterpret_cast<const half8_t*>(X16 + (size_t)rr * a.ldx + (sb0 + p) * 256 + 64 * g + 8 * j);
+  }
+  // the residual of the item this wave finishes
+  float resv[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (MODE == 0) {
+    if (wave < n_items && a.residual) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int b = 4 * g + ii < a.B ? 4 * g + ii : a.B - 1;
+        resv[ii] = a.residual[(size_t)b * a.ldr + (item0 + wave) * 16 + r];
+      }
+    }
+  }
+
+  // ---- weights of the first PD items (kXNorm: of the first item only while
+  // the x rows are held; the rest once the activations are built)
+  Q4Frag fr[PD][KW][T];
+  constexpr int PD0 = XMODE == kXNorm ? 1 : PD;
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < PD0; ++q)
+#pragma unroll
+      for (int p = 0; p < KW; ++p)
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) load_frag(fr[q][p][tt], wptr(q, tt, sb0 + p), g);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- A operands of this wave's K slice, kept for every item
+  if constexpr (XMODE == kXNorm) {
+    ssf.fold(s_part);
+    __syncthreads();
+    if (tx < 16) s_rinv[tx] = rms_inv<S>(s_part, tx, a.inv_k, a.eps);
+    __syncthreads();
+    // h = f16(x * rinv * gamma) of the rows < B into LDS
+    half_t* hs = reinterpret_cast<half_t*>(smem);
+#pragma unroll
+    for (int c = 0; c < KW; ++c) {
+      const int c4 = tx + 64 * S * c;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (u < a.B) {
+          const float ri = s_rinv[u];
+          half4_t h;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h[e] = norm_apply(xv[c][u][e], ri, gv[c][e]);
+          *reinterpret_cast<half4_t*>(hs + u * LDH + 4 * c4) = h;
+        }
+      }
+      // rows 8..15 (B > 8) are loaded only now
+      for (int b0 = 8; b0 < a.B; b0 += 8) {
+        floatx4 xw[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int bb = b0 + u < a.B ? b0 + u : a.B - 1;
+          xw[u] = *reinterpret_cast<const floatx4*>(X32 + (size_t)bb * a.ldx + 4 * c4);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (b0 + u < a.B) {
+            const float ri = s_rinv[b0 + u];
+            half4_t h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = norm_apply(xw[u][e], ri, gv[c][e]);
+            *reinterpret_cast<half4_t*>(hs + (b0 + u) * LDH + 4 * c4) = h;
+          }
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < KW; ++p) {
+      const half_t* src = hs + (r < a.B ? r : 0) * LDH + (sb0 + p) * 256 + 64 * g;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        half8_t v = *reinterpret_cast<const half8_t*>(src + 8 * j);
+        if (r >= a.B) v = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+        av[p][j] = v;
+      }
+      float fmr;
+      a_sums(av[p], 1.f, axs[p], fmr);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        fd[p][ii] = 1.f;
+        fm[p][ii] = __shfl(fmr, 4 * g + ii);
+      }
+    }
+    __syncthreads();   // the h area becomes the partial-sum area
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = PD0; q < PD; ++q)
+#pragma unroll
+        for (int p = 0; p < KW; ++p)
+#pragma unroll
+          for (int tt = 0; tt < T; ++tt) load_frag(fr[q][p][tt], wptr(q, tt, sb0 + p), g);
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    static_assert(XMODE == kXF16, "fp16 or normalized fp32 activations");
+#pragma unroll
+    for (int p = 0; p < KW; ++p) {
+      if (r >= a.B)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) av[p][j] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      float fmr;
+      a_sums(av[p], 1.f, axs[p], fmr);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        fd[p][ii] = 1.f;
+        fm[p][ii] = __shfl(fmr, 4 * g + ii);
+      }
+    }
+  }
+
+  // ---- items: products of the slice, next weights issued into the freed slot
+  const NibbleMasks km = {in_vgpr(0x000F000Fu), in_vgpr(0x00F000F0u), in_vgpr(0x64006400u)};
+#pragma unroll
+  for (int it = 0; it < IPW; ++it) {
+    {
+      floatx4 acc[T];
+#pragma unroll
+      for (int tt = 0; tt < T; ++tt) acc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int p = 0; p < KW; ++p)
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) {
+          floatx4 sq, sm;
+          float d, dm;
+          q4_superblock(fr[it % PD][p][tt], av[p], axs[p], g, km, sq, sm, d, dm);
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii)
+            acc[tt][ii] = __builtin_fmaf(d * fd[p][ii], sq[ii], __builtin_fmaf(-dm * fm[p][ii], sm[ii], acc[tt][ii]));
+        }
+      if (it + PD < IPW) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int p = 0; p < KW; ++p)
+#pragma unroll
+          for (int tt = 0; tt < T; ++tt) load_frag(fr[it % PD][p][tt], wptr(it + PD, tt, sb0 + p), g);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int tt = 0; tt < T; ++tt) red[it][tt][wave][lane] = acc[tt];
+    }
+  }
+  __syncthreads();
+
+  // ---- wave i finishes item i: the S partial sums in wave order
+  if (wave >= n_items) return;
+  floatx4 v[T];
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt) {
+    v[tt] = red[0][tt][0][lane];
+  }
+#pragma unroll
+  for (int it = 0; it < IPW; ++it) {
+    if (it == wave) {
+#pragma unroll
+      for (int tt = 0; tt < T; ++tt) {
+        v[tt] = red[it][tt][0][lane];
+#pragma unroll
+        for (int w = 1; w < S; ++w) v[tt] += red[it][tt][w][lane];
+      }
+    }
+  }
+  const int item = item0 + wave;
+  const int n = item * 16 + r;
+  if constexpr (MODE == 0) {
+    float sq[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int b = 4 * g + ii;
+      float y = v[0][ii];
+      if (b < a.B) {
+        if (a.residual) y += resv[ii];
+        a.Y[(size_t)b * a.ldy + n] = y;
+      }
+      sq[ii] = b < a.B ? y * y : 0.f;
+    }
+    if (a.ss_out) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        float t = sq[ii];
+        t += __shfl_xor(t, 1);
+        t += __shfl_xor(t, 2);
+        t += __shfl_xor(t, 4);
+        t += __shfl_xor(t, 8);
+        if (r == 0) a.ss_out[(size_t)item * 16 + 4 * g + ii] = t;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int b = 4 * g + ii;
+      if (b < a.B) {
+        const float z = v[0][ii];
+        float sil;
+        if (z >= 0.f) {
+          sil = z / (1.f + expf(-z));
+        } else {
+          const float ez = expf(z);
+          sil = z * ez / (1.f + ez);
+        }
+        a.A[(size_t)b * a.lda + n] = sil * v[1][ii];
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- launcher
 // Waves per work-group and super-blocks in flight per wave, by shape and
 // activation mode (MI355X, B = 8, the 6144x4096, 4096x4096, 2x12288x4096 and
@@ -317,6 +593,35 @@ static void launch_mode(int s, int items, const WkArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((gemm_wk_kernel<MODE, XMODE, 8, 2>), dim3(items), dim3(512), 0, st, a);
   else
     hipLaunchKernelGGL((gemm_wk_kernel<MODE, XMODE, 4, 2>), dim3(items), dim3(256), 0, st, a);
+}
+
+// Multi-item launch for the shapes it is built for; hipErrorNotSupported
+// otherwise (the caller then uses another kernel).  SwiGLU over K = 4096: 16
+// waves of one super-block each, three gate/up tile pairs per work-group, two
+// pairs' weights in flight (768 pairs for F = 12288: 256 work-groups).
+hipError_t launch_gemm_wi(const GemmLaunch& L, hipStream_t st) {
+  const int kb = (int)(L.K / 256);
+  const int64_t items = L.n_rows / 16;
+  const int xmode = L.x_f32 ? (L.gamma ? kXNorm : kXF32Blocked) : kXF16;
+  if (!L.swiglu || kb != 16 || xmode == kXF32Blocked) return hipErrorNotSupported;
+  WkArgs a{};
+  a.W = reinterpret_cast<const uint8_t*>(L.W);
+  a.X = L.X;
+  a.gamma = L.gamma;
+  a.ss_in = L.ss_in;
+  a.A = L.A;
+  a.ldx = L.ldx;
+  a.lda = L.lda;
+  a.kb = kb;
+  a.B = L.B;
+  a.f_tiles = (int)items;
+  a.ss_slots = (int)(L.K / kSsCols);
+  a.eps = L.eps;
+  a.inv_k = 1.0f / (float)L.K;
+  const dim3 grid((unsigned)((items + 2) / 3));
+  if (xmode == kXNorm) hipLaunchKernelGGL((gemm_wi_kernel<1, kXNorm, 16, 1, 3, 2>), grid, dim3(1024), 0, st, a);
+  else hipLaunchKernelGGL((gemm_wi_kernel<1, kXF16, 16, 1, 3, 2>), grid, dim3(1024), 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_wk(const GemmLaunch& L, hipStream_t st) {
