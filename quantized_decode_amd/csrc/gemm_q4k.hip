@@ -634,11 +634,11 @@ static GemmArgs gemm_args(const GemmLaunch& L, int64_t n_tiles, int kb) {
 
 hipError_t launch_gemm(const GemmLaunch& L, hipStream_t st) {
   // fp16 activations without SwiGLU: one work-group per tile, K over its waves
-  if (!L.x_f32 && !L.swiglu) return launch_gemm_wk(L, st);
   if (!L.force_kc && !L.force_wpb) {
     const hipError_t e = launch_gemm_wi(L, st);
     if (e != hipErrorNotSupported) return e;
   }
+  if (!L.x_f32 && !L.swiglu) return launch_gemm_wk(L, st);
   const int64_t n_tiles = L.swiglu ? 2 * (L.n_rows / 16) : L.n_rows / 16;
   const int kb = (int)(L.K / 256);
   const int xmode = L.x_f32 ? (L.gamma ? kXNorm : kXF32Blocked) : kXF16;

@@ -596,21 +596,29 @@ static void launch_mode(int s, int items, const WkArgs& a, hipStream_t st) {
 }
 
 // Multi-item launch for the shapes it is built for; hipErrorNotSupported
-// otherwise (the caller then uses another kernel).  SwiGLU over K = 4096: 16
-// waves of one super-block each, three gate/up tile pairs per work-group, two
-// pairs' weights in flight (768 pairs for F = 12288: 256 work-groups).
+// otherwise (the caller then uses another kernel).  K = 4096 only (16 waves of
+// one super-block each):
+//   SwiGLU: three gate/up tile pairs per work-group, two in flight (768 pairs
+//     for F = 12288: 256 work-groups);
+//   plain, RMSNorm fused: two tiles per work-group (6144 rows: 192);
+//   plain, fp16 activations: one tile per work-group up to 4096 rows, else two.
 hipError_t launch_gemm_wi(const GemmLaunch& L, hipStream_t st) {
   const int kb = (int)(L.K / 256);
   const int64_t items = L.n_rows / 16;
   const int xmode = L.x_f32 ? (L.gamma ? kXNorm : kXF32Blocked) : kXF16;
-  if (!L.swiglu || kb != 16 || xmode == kXF32Blocked) return hipErrorNotSupported;
+  if (kb != 16 || xmode == kXF32Blocked) return hipErrorNotSupported;
   WkArgs a{};
   a.W = reinterpret_cast<const uint8_t*>(L.W);
   a.X = L.X;
   a.gamma = L.gamma;
   a.ss_in = L.ss_in;
+  a.Y = L.Y;
+  a.residual = L.residual;
+  a.ss_out = L.ss_out;
   a.A = L.A;
   a.ldx = L.ldx;
+  a.ldy = L.ldy;
+  a.ldr = L.ldr;
   a.lda = L.lda;
   a.kb = kb;
   a.B = L.B;
@@ -618,9 +626,19 @@ hipError_t launch_gemm_wi(const GemmLaunch& L, hipStream_t st) {
   a.ss_slots = (int)(L.K / kSsCols);
   a.eps = L.eps;
   a.inv_k = 1.0f / (float)L.K;
-  const dim3 grid((unsigned)((items + 2) / 3));
-  if (xmode == kXNorm) hipLaunchKernelGGL((gemm_wi_kernel<1, kXNorm, 16, 1, 3, 2>), grid, dim3(1024), 0, st, a);
-  else hipLaunchKernelGGL((gemm_wi_kernel<1, kXF16, 16, 1, 3, 2>), grid, dim3(1024), 0, st, a);
+  if (L.swiglu) {
+    const dim3 grid((unsigned)((items + 2) / 3));
+    if (xmode == kXNorm) hipLaunchKernelGGL((gemm_wi_kernel<1, kXNorm, 16, 1, 3, 2>), grid, dim3(1024), 0, st, a);
+    else hipLaunchKernelGGL((gemm_wi_kernel<1, kXF16, 16, 1, 3, 2>), grid, dim3(1024), 0, st, a);
+  } else if (xmode == kXNorm) {
+    hipLaunchKernelGGL((gemm_wi_kernel<0, kXNorm, 16, 1, 2, 2>), dim3((unsigned)((items + 1) / 2)), dim3(1024), 0,
+                       st, a);
+  } else if (items <= 256) {
+    hipLaunchKernelGGL((gemm_wi_kernel<0, kXF16, 16, 1, 1, 1>), dim3((unsigned)items), dim3(1024), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((gemm_wi_kernel<0, kXF16, 16, 1, 2, 2>), dim3((unsigned)((items + 1) / 2)), dim3(1024), 0,
+                       st, a);
+  }
   return hipGetLastError();
 }
 

@@ -119,6 +119,11 @@ hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, con
                               float* partials, int n_ctx_add, hipStream_t st);
 
 // ---- KV append and RoPE (kv_append.hip)
+// RoPE of q and k, q -> fp16 and the KV append, from the fp32 QKV rows Y
+// (row b: [q heads; k heads; v heads], head_dim each)
+hipError_t launch_rope_append(const qkdec_kv_layer& kv, const float* Y, int64_t ldy, int Hq, int B,
+                              const int32_t* slot, const int32_t* pos, float rope_base, uint16_t* q16, int32_t* err,
+                              hipStream_t st);
 hipError_t launch_kv_append(const qkdec_kv_layer& kv, const int32_t* slot, const int32_t* pos, const float* k,
                             const float* v, int B, int32_t* err, hipStream_t st);
 

@@ -28,6 +28,48 @@ __global__ void kv_append_kernel(qkdec_kv_layer kv, const int32_t* slot, const i
   store_elem(c, true, s, g, p, d, v[src], ok);
 }
 
+// The QKV projection's finish as its own launch (after a projection kernel
+// that only stores the fp32 rows Y = [q heads; k heads; v heads] per
+// sequence): grid (Hq + 2 n_kv, B), block D threads; thread d of head h rotates
+// dims (d, d +- D/2) of q and k at pos[b] (rope_cos_sin), q goes out as fp16,
+// k and v are appended to the cache at (slot[b], pos[b]).
+__global__ void rope_append_kernel(qkdec_kv_layer kv, const float* __restrict__ Y, int64_t ldy, int Hq,
+                                   const int32_t* slot, const int32_t* pos, float rope_base, uint16_t* q16,
+                                   int32_t* err) {
+  const CacheRef c = cache_ref(kv);
+  const int head = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int D = c.D, half = D / 2;
+  const bool is_q = head < Hq, is_v = head >= Hq + c.n_kv;
+  const float* yr = Y + (size_t)b * ldy + (size_t)head * D;
+  const float x = yr[d];
+  const int p = pos[b];
+  float out = x;
+  if (!is_v) {
+    const float other = yr[d < half ? d + half : d - half];
+    float cs, sn;
+    rope_cos_sin(p, d % half, D, rope_base, cs, sn);
+    // d < D/2: x_i cos - x_{i+D/2} sin; d >= D/2: x_{i+D/2} cos + x_i sin
+    out = d < half ? x * cs - other * sn : x * cs + other * sn;
+  }
+  if (is_q) {
+    q16[((size_t)b * Hq + head) * D + d] = f2h_bits(out);
+    return;
+  }
+  const int s = slot[b];
+  const bool ok = s >= 0 && s < c.n_slots && p >= 0 && p < c.cap;
+  if (!ok && d == 0 && err) *err = QKDEC_E_CAPACITY;
+  const int g = is_v ? head - Hq - c.n_kv : head - Hq;
+  store_elem(c, is_v, s, g, p, d, out, ok);
+}
+
+hipError_t launch_rope_append(const qkdec_kv_layer& kv, const float* Y, int64_t ldy, int Hq, int B,
+                              const int32_t* slot, const int32_t* pos, float rope_base, uint16_t* q16, int32_t* err,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(rope_append_kernel, dim3(Hq + 2 * kv.n_kv_heads, B), dim3(kv.head_dim), 0, st, kv, Y, ldy, Hq,
+                     slot, pos, rope_base, q16, err);
+  return hipGetLastError();
+}
+
 hipError_t launch_kv_append(const qkdec_kv_layer& kv, const int32_t* slot, const int32_t* pos, const float* k,
                             const float* v, int B, int32_t* err, hipStream_t st) {
   hipLaunchKernelGGL(kv_append_kernel, dim3(kv.n_kv_heads, B), dim3(kv.head_dim), 0, st, kv, slot, pos, k, v, err);

@@ -161,7 +161,15 @@ qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int3
     ra.ks = reinterpret_cast<uint16_t*>(kv[l].k_scale); ra.vs = reinterpret_cast<uint16_t*>(kv[l].v_scale);
     ra.n_kv = kv[l].n_kv_heads; ra.cap = kv[l].capacity; ra.n_slots = kv[l].n_slots; ra.Hq = Hq;
     ra.q8 = kv[l].type == QKDEC_KV_Q8_0; ra.rope_base = m->rope_base; ra.q16 = w.q16; ra.err = w.err;
-    QK_TRY(launch_gemm_qkv_rope(qkv, ra, D, st));
+    // K = 4096: the resident multi-item projection, then RoPE and the append
+    // as a small launch; otherwise the split-K projection finishes each head
+    const hipError_t eq = launch_gemm_wi(qkv, st);
+    if (eq == hipErrorNotSupported) {
+      QK_TRY(launch_gemm_qkv_rope(qkv, ra, D, st));
+    } else {
+      QK_TRY(eq);
+      QK_TRY(launch_rope_append(kv[l], w.qkv, nqkv, Hq, B, slot, pos, m->rope_base, w.q16, w.err, st));
+    }
     QK_TRY(launch_attn_decode(kv[l], slot, pos, B, w.q16, Hq, scale, nullptr, w.o16, w.attn_part, 1, st));
     // O projection: fp16 activations, K split over the waves of one work-group
     // per output tile (no split-K round trips); the fp32-activation projections
@@ -169,7 +177,7 @@ qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int3
     GemmLaunch o{};
     o.W = ly.w_o; o.n_rows = H; o.K = hq; o.X = w.o16; o.ldx = hq; o.B = B;
     o.Y = w.x; o.ldy = H; o.residual = w.x; o.ldr = H; o.ss_out = w.ss; o.ws = w.gemm_ws;
-    QK_TRY(launch_gemm_wk(o, st));
+    QK_TRY(launch_gemm(o, st));
     GemmLaunch gu{};
     gu.W = ly.w_gate_up; gu.n_rows = F; gu.K = H; gu.X = w.x; gu.x_f32 = true; gu.ldx = H; gu.B = B;
     gu.gamma = ly.norm_ffn; gu.ss_in = w.ss; gu.eps = m->rms_eps;
@@ -226,12 +234,12 @@ qkdec_status qkdec_gemm_q4k(const void* W, int64_t N, int64_t K, const uint16_t*
   if (!workspace || ws_bytes < gemm_workspace_bytes(N, K, B, false)) return QKDEC_E_WORKSPACE;
   if (!aligned(workspace, 256)) return QKDEC_E_ALIGN;
   clear_stale_error();
-  // one work-group per 16-row output tile, K split over its waves (the kernel
-  // of the decode step's O projection): the workspace is not touched
+  // K split over the waves of one work-group per output item (the kernels of
+  // the decode step's O projection): the workspace is not touched
   GemmLaunch L{};
   L.W = W; L.n_rows = N; L.K = K; L.X = X; L.ldx = ldx; L.B = B;
   L.Y = Y; L.ldy = ldy; L.residual = residual; L.ldr = ldr;
-  return hip_status(launch_gemm_wk(L, as_stream(stream)));
+  return hip_status(launch_gemm(L, as_stream(stream)));
 }
 
 qkdec_status qkdec_gemm_q4k_xf32(const void* W, int64_t N, int64_t K, const float* X, int64_t ldx, int32_t B,
