@@ -30,6 +30,7 @@
 //                and super-block (the offset is a factor of d and dmin).
 #include "common.h"
 #include "internal.h"
+#include "kv_dev.h"
 #include "q4k_dev.h"
 
 namespace qk {
@@ -46,6 +47,8 @@ struct WkArgs {
   int64_t ldx, ldy, ldr, lda;
   int kb, B, f_tiles, ss_slots;
   float eps, inv_k;
+  RopeAppendArgs ra;     // MODE 2 (gemm_wi_kernel): QKV finish, fp16 cache
+  int qh;                // MODE 2: tiles per half head (head_dim / 32)
 };
 
 // The hi/lo sums of sub-blocks 2g (pieces 0..3) and 2g+1 (pieces 4..7) of av
@@ -295,6 +298,67 @@ __global__ void __launch_bounds__(64 * S, wk_waves_per_simd<XMODE>()) gemm_wk_ke
   }
 }
 
+// MODE 2 finish of gemm_wi_kernel (all waves call it after the partial sums
+// are in LDS): waves 0 and 1 add the partial sums of tiles hj and hj + D/32 of
+// the head, store the fp32 rows, exchange them for the rotation, then store q
+// as fp16 or append k, v to the fp16 cache.
+template <int S, typename Red>
+__device__ void qkv_finish(const WkArgs& a, Red red, int wave, int lane, int g, int r, int head, int hj,
+                           const int (&sl)[4], const int (&ps)[4], const float2* s_rope) {
+  __shared__ floatx4 s_fin[2][64];
+  const RopeAppendArgs& ra = a.ra;
+  const int D = 32 * a.qh, HALF = D / 2;
+  floatx4 v = {0.f, 0.f, 0.f, 0.f};
+  if (wave < 2) {
+    v = red[wave][0][0][lane];
+#pragma unroll
+    for (int w = 1; w < S; ++w) v += red[wave][0][w][lane];
+    const int n = (head * 2 * a.qh + hj + a.qh * wave) * 16 + r;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+      if (4 * g + ii < a.B) a.Y[(size_t)(4 * g + ii) * a.ldy + n] = v[ii];
+    s_fin[wave][lane] = v;
+  }
+  __syncthreads();
+  if (wave >= 2) return;
+  const bool is_q = head < ra.Hq, is_v = head >= ra.Hq + ra.n_kv;
+  const int d = 16 * (hj + a.qh * wave) + r;   // dim within the head
+  float out[4];
+  if (!is_v) {
+    const floatx4 other = s_fin[wave ^ 1][lane];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int b = 4 * g + ii < a.B ? 4 * g + ii : 0;
+      const float2 c = s_rope[b * 16 + r];
+      // d < D/2: x_i cos - x_{i+D/2} sin; d >= D/2: x_{i+D/2} cos + x_i sin
+      out[ii] = d < HALF ? v[ii] * c.x - other[ii] * c.y : v[ii] * c.x + other[ii] * c.y;
+    }
+  } else {
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) out[ii] = v[ii];
+  }
+  if (is_q) {
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int b = 4 * g + ii;
+      if (b < a.B) ra.q16[((size_t)b * ra.Hq + head) * D + d] = f2h_bits(out[ii]);
+    }
+    return;
+  }
+  CacheRef c;
+  c.k = ra.k; c.v = ra.v; c.ks = ra.ks; c.vs = ra.vs;
+  c.n_kv = ra.n_kv; c.cap = ra.cap; c.D = D; c.n_slots = ra.n_slots; c.q8 = false;
+  const int kvh = is_v ? head - ra.Hq - ra.n_kv : head - ra.Hq;
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) {
+    const int b = 4 * g + ii;
+    if (b >= a.B) continue;
+    const bool ok = sl[ii] >= 0 && sl[ii] < ra.n_slots && ps[ii] >= 0 && ps[ii] < ra.cap;
+    if (ok) store_f16(c, is_v, sl[ii], kvh, ps[ii], d, out[ii]);
+    else if (r == 0) *ra.err = QKDEC_E_CAPACITY;
+  }
+}
+
 // Several output items per work-group.  Wave w owns super-blocks
 // [KW w, KW w + KW) of K (kb = S * KW) for every item, so it builds the A
 // operands of its K slice once and keeps them in registers; the weights of
@@ -303,10 +367,15 @@ __global__ void __launch_bounds__(64 * S, wk_waves_per_simd<XMODE>()) gemm_wk_ke
 // wave order and finishes it (no split-K round trips, no workspace).  With
 // IPW items per work-group a launch of ceil(items / IPW) work-groups can be
 // resident on the chip at once.
+// MODE 2 (the QKV projection of a decode step, fp16 cache): a work-group owns
+// tiles j and j + D/32 of one head (dims 16 j + r and 16 j + r + D/2, the
+// rotate-half pairs), so it finishes the head slice itself: the fp32 rows go
+// to Y, q and k are rotated at pos, q is stored as fp16 and k, v are appended.
 template <int MODE, int XMODE, int S, int KW, int IPW, int PD>
 __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
   constexpr int T = MODE == 1 ? 2 : 1;   // weight tiles per item
   static_assert(IPW <= S && PD <= IPW, "one finishing wave per item");
+  static_assert(MODE != 2 || (IPW == 2 && XMODE == kXNorm), "QKV finish: a tile pair, RMSNorm fused");
   // LDS: kXNorm first holds the normalized activations h [16][K + 8] (fp16),
   // then, after a barrier, the partial sums red[IPW][T][S][64]
   constexpr size_t kRedBytes = sizeof(floatx4) * IPW * T * S * 64;
@@ -318,13 +387,19 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
   const int tx = threadIdx.x, lane = tx & 63, wave = tx >> 6, g = lane >> 4, r = lane & 15;
   const int kb = a.kb;
   const int item0 = blockIdx.x * IPW;
-  const int n_items = a.f_tiles - item0 < IPW ? a.f_tiles - item0 : IPW;
+  const int n_items = MODE == 2 ? 2 : (a.f_tiles - item0 < IPW ? a.f_tiles - item0 : IPW);
+  // MODE 2: head and half-head tile of this work-group
+  const int head = MODE == 2 ? (int)blockIdx.x / a.qh : 0, hj = MODE == 2 ? (int)blockIdx.x % a.qh : 0;
+  auto tile_of_item = [&](int it) {
+    if constexpr (MODE == 2) return head * 2 * a.qh + hj + a.qh * it;
+    return item0 + (it < n_items ? it : n_items - 1);
+  };
   const int sb0 = wave * KW;
   // items past the launch's last one read the last one's weights again: every
   // weight load is unconditional, so the compiler's in-order load counting
   // never has to assume a shorter path and wait for the whole stream
   auto wptr = [&](int it, int tt, int sb) {
-    const int tile = item0 + (it < n_items ? it : n_items - 1) + (tt ? a.f_tiles : 0);
+    const int tile = tile_of_item(it) + (tt ? a.f_tiles : 0);
     return a.W + ((size_t)tile * kb + sb) * 2304 + (size_t)r * 144;
   };
 
@@ -361,6 +436,18 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
       for (int j = 0; j < 8; ++j)
         av[p][j] = *reinterpret_cast<const half8_t*>(X16 + (size_t)rr * a.ldx + (sb0 + p) * 256 + 64 * g + 8 * j);
   }
+  // MODE 2: slot and position of the lane's rows 4g + ii, and of row tx / 16
+  // for the rotary table
+  int sl[4] = {0, 0, 0, 0}, ps[4] = {0, 0, 0, 0}, pos_t = 0;
+  if constexpr (MODE == 2) {
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int b = 4 * g + ii < a.B ? 4 * g + ii : a.B - 1;
+      sl[ii] = a.ra.slot[b];
+      ps[ii] = a.ra.pos[b];
+    }
+    pos_t = a.ra.pos[(tx >> 4) < a.B ? (tx >> 4) : a.B - 1];
+  }
   // the residual of the item this wave finishes
   float resv[4] = {0.f, 0.f, 0.f, 0.f};
   if constexpr (MODE == 0) {
@@ -385,6 +472,16 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
 #pragma unroll
         for (int tt = 0; tt < T; ++tt) load_frag(fr[q][p][tt], wptr(q, tt, sb0 + p), g);
   __builtin_amdgcn_sched_barrier(0);
+
+  // MODE 2: (cos, sin) of pair 16 hj + (tx % 16) at the position of row tx / 16
+  __shared__ float2 s_rope[MODE == 2 ? 16 * 16 : 1];
+  if constexpr (MODE == 2) {
+    if (tx < 16 * 16) {
+      float cs, sn;
+      rope_cos_sin(pos_t, 16 * hj + (tx & 15), 32 * a.qh, a.ra.rope_base, cs, sn);
+      s_rope[tx] = make_float2(cs, sn);
+    }
+  }
 
   // ---- A operands of this wave's K slice, kept for every item
   if constexpr (XMODE == kXNorm) {
@@ -505,6 +602,10 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
   __syncthreads();
 
   // ---- wave i finishes item i: the S partial sums in wave order
+  if constexpr (MODE == 2) {
+    qkv_finish<S>(a, red, wave, lane, g, r, head, hj, sl, ps, s_rope);
+    return;
+  }
   if (wave >= n_items) return;
   floatx4 v[T];
 #pragma unroll
@@ -639,6 +740,34 @@ hipError_t launch_gemm_wi(const GemmLaunch& L, hipStream_t st) {
     hipLaunchKernelGGL((gemm_wi_kernel<0, kXF16, 16, 1, 2, 2>), dim3((unsigned)((items + 1) / 2)), dim3(1024), 0,
                        st, a);
   }
+  return hipGetLastError();
+}
+
+// The QKV projection of a decode step with its RoPE / fp16-append finish:
+// K = 4096, RMSNorm fused, fp16 cache, head_dim 64 or 128; one work-group per
+// (head, half-head tile).  hipErrorNotSupported for any other case.
+hipError_t launch_gemm_wi_qkv(const GemmLaunch& L, const RopeAppendArgs& ra, int head_dim, hipStream_t st) {
+  const int kb = (int)(L.K / 256);
+  if (kb != 16 || !L.x_f32 || !L.gamma || ra.q8 || (head_dim != 64 && head_dim != 128) || L.residual || L.ss_out)
+    return hipErrorNotSupported;
+  WkArgs a{};
+  a.W = reinterpret_cast<const uint8_t*>(L.W);
+  a.X = L.X;
+  a.gamma = L.gamma;
+  a.ss_in = L.ss_in;
+  a.Y = L.Y;
+  a.ldx = L.ldx;
+  a.ldy = L.ldy;
+  a.kb = kb;
+  a.B = L.B;
+  a.f_tiles = (int)(L.n_rows / 16);
+  a.ss_slots = (int)(L.K / kSsCols);
+  a.eps = L.eps;
+  a.inv_k = 1.0f / (float)L.K;
+  a.ra = ra;
+  a.qh = head_dim / 32;
+  const int n_heads = (int)(L.n_rows / head_dim);
+  hipLaunchKernelGGL((gemm_wi_kernel<2, kXNorm, 16, 1, 2, 2>), dim3((unsigned)(n_heads * a.qh)), dim3(1024), 0, st, a);
   return hipGetLastError();
 }
 

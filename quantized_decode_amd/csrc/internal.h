@@ -70,6 +70,9 @@ hipError_t launch_gemm_wk(const GemmLaunch& L, hipStream_t st);
 // Several output items per work-group (gemm_wk.hip), for the shapes it covers;
 // returns hipErrorNotSupported for any other.
 hipError_t launch_gemm_wi(const GemmLaunch& L, hipStream_t st);
+// The decode step's QKV projection with its RoPE and fp16-append finish on the
+// multi-item kernel (K = 4096, fp16 cache); hipErrorNotSupported otherwise.
+hipError_t launch_gemm_wi_qkv(const GemmLaunch& L, const RopeAppendArgs& ra, int head_dim, hipStream_t st);
 hipError_t launch_gemm_q4k_xf32(const void* W, int64_t N, int64_t K, const float* X, int64_t ldx, int B,
                                 float* Y, int64_t ldy, const float* residual, int64_t ldr, void* ws, hipStream_t st,
                                 int force_kc = 0);

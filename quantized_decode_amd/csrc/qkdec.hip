@@ -161,14 +161,21 @@ qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int3
     ra.ks = reinterpret_cast<uint16_t*>(kv[l].k_scale); ra.vs = reinterpret_cast<uint16_t*>(kv[l].v_scale);
     ra.n_kv = kv[l].n_kv_heads; ra.cap = kv[l].capacity; ra.n_slots = kv[l].n_slots; ra.Hq = Hq;
     ra.q8 = kv[l].type == QKDEC_KV_Q8_0; ra.rope_base = m->rope_base; ra.q16 = w.q16; ra.err = w.err;
-    // K = 4096: the resident multi-item projection, then RoPE and the append
-    // as a small launch; otherwise the split-K projection finishes each head
-    const hipError_t eq = launch_gemm_wi(qkv, st);
+    // K = 4096: the resident multi-item projection, finishing each head slice
+    // itself (fp16 cache) or followed by RoPE and the append as a small launch
+    // (Q8_0 blocks span two work-groups); otherwise the split-K projection
+    // finishes each head
+    hipError_t eq = launch_gemm_wi_qkv(qkv, ra, D, st);
     if (eq == hipErrorNotSupported) {
-      QK_TRY(launch_gemm_qkv_rope(qkv, ra, D, st));
+      eq = launch_gemm_wi(qkv, st);
+      if (eq == hipErrorNotSupported) {
+        QK_TRY(launch_gemm_qkv_rope(qkv, ra, D, st));
+      } else {
+        QK_TRY(eq);
+        QK_TRY(launch_rope_append(kv[l], w.qkv, nqkv, Hq, B, slot, pos, m->rope_base, w.q16, w.err, st));
+      }
     } else {
       QK_TRY(eq);
-      QK_TRY(launch_rope_append(kv[l], w.qkv, nqkv, Hq, B, slot, pos, m->rope_base, w.q16, w.err, st));
     }
     QK_TRY(launch_attn_decode(kv[l], slot, pos, B, w.q16, Hq, scale, nullptr, w.o16, w.attn_part, 1, st));
     // O projection: fp16 activations, K split over the waves of one work-group
