@@ -552,6 +552,7 @@ size_t gemm_workspace_bytes(int64_t n_rows, int64_t K, int B, bool swiglu) {
   int64_t chunks = 1;
   for (int xmode : {(int)kXF16, (int)kXF32Blocked, (int)kXNorm})
     chunks = std::max<int64_t>(chunks, kb / gemm_config(n_tiles, kb, B, swiglu, xmode).kc);
+  if (kb == 48 && !swiglu) chunks = std::max<int64_t>(chunks, 4);   // the multi-item kernel's K split
   size_t bytes = counters_bytes();
   if (chunks > 1) bytes += (size_t)chunks * B * n_rows * 4;
   return bytes;

@@ -49,6 +49,8 @@ struct WkArgs {
   float eps, inv_k;
   RopeAppendArgs ra;     // MODE 2 (gemm_wi_kernel): QKV finish, fp16 cache
   int qh;                // MODE 2: tiles per half head (head_dim / 32)
+  float* part;           // K split over work-groups (gemm_wi_kernel): partial sums [chunk][B][N]
+  unsigned* counters;    // ... and one arrival counter per output tile (zero between launches)
 };
 
 // The hi/lo sums of sub-blocks 2g (pieces 0..3) and 2g+1 (pieces 4..7) of av
@@ -371,22 +373,28 @@ __device__ void qkv_finish(const WkArgs& a, Red red, int wave, int lane, int g, 
 // tiles j and j + D/32 of one head (dims 16 j + r and 16 j + r + D/2, the
 // rotate-half pairs), so it finishes the head slice itself: the fp32 rows go
 // to Y, q and k are rotated at pos, q is stored as fp16 and k, v are appended.
-template <int MODE, int XMODE, int S, int KW, int IPW, int PD>
+// KSPLIT > 1 (MODE 0): K is cut into KSPLIT chunks of S KW super-blocks;
+// work-group i takes chunk i / (grid / KSPLIT), and the last of a tile's
+// chunks to arrive adds the chunks' partial sums in chunk order.
+template <int MODE, int XMODE, int S, int KW, int IPW, int PD, int KSPLIT = 1>
 __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
   constexpr int T = MODE == 1 ? 2 : 1;   // weight tiles per item
+  static_assert(KSPLIT == 1 || MODE == 0, "K split: plain outputs only");
   static_assert(IPW <= S && PD <= IPW, "one finishing wave per item");
   static_assert(MODE != 2 || (IPW == 2 && XMODE == kXNorm), "QKV finish: a tile pair, RMSNorm fused");
   // LDS: kXNorm first holds the normalized activations h [16][K + 8] (fp16),
   // then, after a barrier, the partial sums red[IPW][T][S][64]
   constexpr size_t kRedBytes = sizeof(floatx4) * IPW * T * S * 64;
-  constexpr size_t kHBytes = XMODE == kXNorm ? (size_t)16 * (S * KW * 256 + 8) * 2 : 0;
+  constexpr size_t kHBytes = XMODE != kXF16 ? (size_t)16 * (S * KW * 256 + 8) * 2 : 0;
   __shared__ __align__(16) char smem[kRedBytes > kHBytes ? kRedBytes : kHBytes];
   auto red = reinterpret_cast<floatx4(*)[T][S][64]>(smem);
   __shared__ float s_part[4 * S][16];
   __shared__ float s_rinv[16];
   const int tx = threadIdx.x, lane = tx & 63, wave = tx >> 6, g = lane >> 4, r = lane & 15;
   const int kb = a.kb;
-  const int item0 = blockIdx.x * IPW;
+  const int n_groups = (int)gridDim.x / KSPLIT;
+  const int kc = KSPLIT > 1 ? (int)blockIdx.x / n_groups : 0;   // K chunk
+  const int item0 = (KSPLIT > 1 ? (int)blockIdx.x % n_groups : (int)blockIdx.x) * IPW;
   const int n_items = MODE == 2 ? 2 : (a.f_tiles - item0 < IPW ? a.f_tiles - item0 : IPW);
   // MODE 2: head and half-head tile of this work-group
   const int head = MODE == 2 ? (int)blockIdx.x / a.qh : 0, hj = MODE == 2 ? (int)blockIdx.x % a.qh : 0;
@@ -394,7 +402,8 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
     if constexpr (MODE == 2) return head * 2 * a.qh + hj + a.qh * it;
     return item0 + (it < n_items ? it : n_items - 1);
   };
-  const int sb0 = wave * KW;
+  const int sbl = wave * KW;                 // first super-block of this wave in the chunk
+  const int sb0 = kc * S * KW + sbl;         // ... in the row
   // items past the launch's last one read the last one's weights again: every
   // weight load is unconditional, so the compiler's in-order load counting
   // never has to assume a shorter path and wait for the whole stream
@@ -406,14 +415,15 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
   // Vector memory loads return in order, so everything small that the
   // prologue waits on (RMSNorm statistics, gains, activations) is issued
   // before the weight stream: waiting on it never waits on the weights.
-  constexpr int K = S * KW * 256, LDH = K + 8;
+  constexpr int K = S * KW * 256, LDH = K + 8;   // K of one chunk
+  const int cbase = kc * (K / 4);                // the chunk's first float4 column
   half8_t av[KW][8];
   half4_t axs[KW];
   floatx4 fd[KW], fm[KW];
   // kXNorm: slots of the sum-of-squares fold, gains and x rows 0..7 of the
   // thread's float4 columns tx + 64 S c (c < KW)
   SsFold<64 * S, (XMODE == kXNorm ? K / kSsCols : 0)> ssf;   // the K inputs have K / 16 slots
-  floatx4 gv[XMODE == kXNorm ? KW : 1], xv[XMODE == kXNorm ? KW : 1][8];
+  floatx4 gv[XMODE == kXNorm ? KW : 1], xv[XMODE != kXF16 ? KW : 1][8];
   const float* X32 = reinterpret_cast<const float*>(a.X);
   if constexpr (XMODE == kXNorm) {
     ssf.load(a.ss_in, a.ss_slots);
@@ -421,6 +431,16 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
     for (int c = 0; c < KW; ++c) {
       const int c4 = tx + 64 * S * c;
       gv[c] = *reinterpret_cast<const floatx4*>(a.gamma + 4 * c4);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int bb = u < a.B ? u : a.B - 1;
+        xv[c][u] = *reinterpret_cast<const floatx4*>(X32 + (size_t)bb * a.ldx + 4 * c4);
+      }
+    }
+  } else if constexpr (XMODE == kXF32Blocked) {
+#pragma unroll
+    for (int c = 0; c < KW; ++c) {
+      const int c4 = cbase + tx + 64 * S * c;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int bb = u < a.B ? u : a.B - 1;
@@ -451,19 +471,23 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
   // the residual of the item this wave finishes
   float resv[4] = {0.f, 0.f, 0.f, 0.f};
   if constexpr (MODE == 0) {
-    if (wave < n_items && a.residual) {
+    // unconditional (no branch around a load): a missing residual reads Y and
+    // is replaced by zero
+    const float* rp = a.residual ? a.residual : a.Y;
+    const int64_t ld = a.residual ? a.ldr : a.ldy;
+    const int it = wave < n_items ? wave : n_items - 1;
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int b = 4 * g + ii < a.B ? 4 * g + ii : a.B - 1;
-        resv[ii] = a.residual[(size_t)b * a.ldr + (item0 + wave) * 16 + r];
-      }
+    for (int ii = 0; ii < 4; ++ii) {
+      const int b = 4 * g + ii < a.B ? 4 * g + ii : a.B - 1;
+      const float v = rp[(size_t)b * ld + (item0 + it) * 16 + r];
+      resv[ii] = a.residual ? v : 0.f;
     }
   }
 
   // ---- weights of the first PD items (kXNorm: of the first item only while
   // the x rows are held; the rest once the activations are built)
   Q4Frag fr[PD][KW][T];
-  constexpr int PD0 = XMODE == kXNorm ? 1 : PD;
+  constexpr int PD0 = XMODE != kXF16 ? 1 : PD;
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int q = 0; q < PD0; ++q)
@@ -527,7 +551,7 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < KW; ++p) {
-      const half_t* src = hs + (r < a.B ? r : 0) * LDH + (sb0 + p) * 256 + 64 * g;
+      const half_t* src = hs + (r < a.B ? r : 0) * LDH + (sbl + p) * 256 + 64 * g;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         half8_t v = *reinterpret_cast<const half8_t*>(src + 8 * j);
@@ -551,8 +575,73 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
 #pragma unroll
           for (int tt = 0; tt < T; ++tt) load_frag(fr[q][p][tt], wptr(q, tt, sb0 + p), g);
     __builtin_amdgcn_sched_barrier(0);
+  } else if constexpr (XMODE == kXF32Blocked) {
+    // f16b: row u's 256 values of super-block w + S c (the 64 float4 columns of
+    // wave w) are rounded to fp16 after a shift by 2^-sh, sh the smallest
+    // exponent that keeps their maximum finite; 2^sh is the factor of d and dmin
+    __shared__ float s_fac[S * KW][16];
+    half_t* hs = reinterpret_cast<half_t*>(smem);
+    auto stage_row = [&](const floatx4& x4, int u, int c) {
+      float am = fmaxf(fmaxf(fabsf(x4[0]), fabsf(x4[1])), fmaxf(fabsf(x4[2]), fabsf(x4[3])));
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) am = fmaxf(am, __shfl_xor(am, o));
+      const int sh = f16_block_shift(am);
+      const float inv = exp2i(-sh);
+      half4_t h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[e] = (half_t)(x4[e] * inv);
+      const int c4 = tx + 64 * S * c;
+      *reinterpret_cast<half4_t*>(hs + u * LDH + 4 * c4) = h;
+      if (lane == 0) s_fac[wave + S * c][u] = exp2i(sh);
+    };
+#pragma unroll
+    for (int c = 0; c < KW; ++c) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (u < a.B) stage_row(xv[c][u], u, c);
+      for (int b0 = 8; b0 < a.B; b0 += 8) {
+        floatx4 xw[8];
+        const int c4 = cbase + tx + 64 * S * c;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int bb = b0 + u < a.B ? b0 + u : a.B - 1;
+          xw[u] = *reinterpret_cast<const floatx4*>(X32 + (size_t)bb * a.ldx + 4 * c4);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (b0 + u < a.B) stage_row(xw[u], b0 + u, c);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < KW; ++p) {
+      const half_t* src = hs + (r < a.B ? r : 0) * LDH + (sbl + p) * 256 + 64 * g;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        half8_t v = *reinterpret_cast<const half8_t*>(src + 8 * j);
+        if (r >= a.B) v = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+        av[p][j] = v;
+      }
+      const float fdr = r < a.B ? s_fac[sbl + p][r] : 1.f;
+      float fmr;
+      a_sums(av[p], fdr, axs[p], fmr);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        fd[p][ii] = __shfl(fdr, 4 * g + ii);
+        fm[p][ii] = __shfl(fmr, 4 * g + ii);
+      }
+    }
+    __syncthreads();   // the activation area becomes the partial-sum area
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = PD0; q < PD; ++q)
+#pragma unroll
+        for (int p = 0; p < KW; ++p)
+#pragma unroll
+          for (int tt = 0; tt < T; ++tt) load_frag(fr[q][p][tt], wptr(q, tt, sb0 + p), g);
+    __builtin_amdgcn_sched_barrier(0);
   } else {
-    static_assert(XMODE == kXF16, "fp16 or normalized fp32 activations");
+    static_assert(XMODE == kXF16, "fp16 or fp32 activations");
 #pragma unroll
     for (int p = 0; p < KW; ++p) {
       if (r >= a.B)
@@ -625,6 +714,41 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
   }
   const int item = item0 + wave;
   const int n = item * 16 + r;
+  if constexpr (MODE == 0 && KSPLIT > 1) {
+    // this chunk's partial sums, stored through to the device-coherent level;
+    // the last chunk to arrive for the tile adds all chunks in chunk order
+    const int n_total = a.f_tiles * 16;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int b = 4 * g + ii;
+      if (b < a.B)
+        __hip_atomic_store(&a.part[((size_t)kc * a.B + b) * n_total + n], v[0][ii], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    unsigned prev = 0;
+    if (lane == 0)
+      prev = __hip_atomic_fetch_add(&a.counters[item], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    prev = __shfl(prev, 0);
+    if (prev != (unsigned)(KSPLIT - 1)) return;
+    if (lane == 0) a.counters[item] = 0u;
+    float pv[KSPLIT][4];
+#pragma unroll
+    for (int cc = 0; cc < KSPLIT; ++cc)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int b = 4 * g + ii < a.B ? 4 * g + ii : a.B - 1;
+        pv[cc][ii] = __hip_atomic_load(&a.part[((size_t)cc * a.B + b) * n_total + n], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      float t = pv[0][ii];
+#pragma unroll
+      for (int cc = 1; cc < KSPLIT; ++cc) t += pv[cc][ii];
+      v[0][ii] = t;
+    }
+  }
   if constexpr (MODE == 0) {
     float sq[4];
 #pragma unroll
@@ -707,7 +831,7 @@ hipError_t launch_gemm_wi(const GemmLaunch& L, hipStream_t st) {
   const int kb = (int)(L.K / 256);
   const int64_t items = L.n_rows / 16;
   const int xmode = L.x_f32 ? (L.gamma ? kXNorm : kXF32Blocked) : kXF16;
-  if (kb != 16 || xmode == kXF32Blocked) return hipErrorNotSupported;
+  if (kb != 16 && !(kb == 48 && xmode == kXF32Blocked)) return hipErrorNotSupported;
   WkArgs a{};
   a.W = reinterpret_cast<const uint8_t*>(L.W);
   a.X = L.X;
@@ -727,6 +851,18 @@ hipError_t launch_gemm_wi(const GemmLaunch& L, hipStream_t st) {
   a.ss_slots = (int)(L.K / kSsCols);
   a.eps = L.eps;
   a.inv_k = 1.0f / (float)L.K;
+  if (xmode == kXF32Blocked) {
+    // K = 12288 (fp32 activations, blocked fp16 rounding): four K chunks of
+    // 3072 (12 waves of one super-block), four tiles per work-group: 256
+    // work-groups for N = 4096, one round on the chip
+    if (kb != 48 || L.swiglu) return hipErrorNotSupported;
+    char* p = reinterpret_cast<char*>(L.ws);
+    a.counters = reinterpret_cast<unsigned*>(p);
+    a.part = reinterpret_cast<float*>(p + (size_t)kGemmMaxGroups * 4);
+    const unsigned groups = (unsigned)((items + 3) / 4);
+    hipLaunchKernelGGL((gemm_wi_kernel<0, kXF32Blocked, 12, 1, 4, 2, 4>), dim3(groups * 4), dim3(768), 0, st, a);
+    return hipGetLastError();
+  }
   if (L.swiglu) {
     const dim3 grid((unsigned)((items + 2) / 3));
     if (xmode == kXNorm) hipLaunchKernelGGL((gemm_wi_kernel<1, kXNorm, 16, 1, 3, 2>), grid, dim3(1024), 0, st, a);
