@@ -145,7 +145,11 @@ __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs
   }
 }
 
-// O[b][h] = sum_j 2^(m_j - M) o_j / sum_j 2^(m_j - M) l_j over the splits.
+// O[b][h] = sum_j 2^(m_j - M) o_j / sum_j 2^(m_j - M) l_j over the splits, j in
+// run order.  Up to kMergeBatch runs' (m, l, o) are loaded in one batch, so
+// the merge costs one memory round trip (the running maximum is rescaled
+// between batches).
+constexpr int kMergeBatch = 8;
 __global__ void attn_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                                     int n_splits, int runs_wanted, const int32_t* slot, const int32_t* n_ctx,
                                     int n_ctx_add, int cap, int n_slots, int Hq, int D, float* O, half_t* O16) {
@@ -156,13 +160,31 @@ __global__ void attn_combine_kernel(const float* __restrict__ part_o, const floa
   if (n < 0 || s < 0 || s >= n_slots) n = 0;
   const int ns = attn_runs(n, runs_wanted, n_splits);
   const size_t row0 = ((size_t)b * Hq + h) * n_splits;
-  float big = -__builtin_inff();
-  for (int j = 0; j < ns; ++j) big = fmaxf(big, part_ml[2 * (row0 + j)]);
-  float num = 0.f, den = 0.f;
-  for (int j = 0; j < ns; ++j) {
-    const float w = exp2f(part_ml[2 * (row0 + j)] - big);
-    den += w * part_ml[2 * (row0 + j) + 1];
-    num += w * part_o[(row0 + j) * D + d];
+  float num = 0.f, den = 0.f, big = -__builtin_inff();
+  for (int j0 = 0; j0 < ns; j0 += kMergeBatch) {
+    float m[kMergeBatch], l[kMergeBatch], o[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const size_t row = row0 + (j0 + j < ns ? j0 + j : j0);
+      m[j] = part_ml[2 * row];
+      l[j] = part_ml[2 * row + 1];
+      o[j] = part_o[row * D + d];
+    }
+    float nb = big;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j)
+      if (j0 + j < ns) nb = fmaxf(nb, m[j]);
+    const float fr = j0 > 0 ? exp2f(big - nb) : 0.f;
+    num *= fr;
+    den *= fr;
+    big = nb;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j)
+      if (j0 + j < ns) {
+        const float w = exp2f(m[j] - big);
+        den += w * l[j];
+        num += w * o[j];
+      }
   }
   const float out = ns > 0 ? num / den : 0.f;
   const size_t oi = ((size_t)b * Hq + h) * D + d;
