@@ -49,8 +49,8 @@ KV_BYTES_PER_TOKEN = {"f16": NL * HKV * D * 2 * 2, "q8_0": NL * HKV * D * 2 * 34
 # profiles/decode_step_b8_l2400_f16_kernel_stats.md.  A kernel changed since
 # has no entry, and its traffic is reported as null.
 COUNTED_TRAFFIC = {
-    # split kernel 82,747,964 fetched + 557,056 written; merge 590,825 + 65,536
-    ("attention (split + merge)", 8, 2400, "f16"): 82_747_964 + 557_056 + 590_825 + 65_536,
+    # split kernel 81,695,539 fetched + 557,056 written; merge 618,496 + 65,536
+    ("attention (split + merge)", 8, 2400, "f16"): 81_695_539 + 557_056 + 618_496 + 65_536,
 }
 
 
@@ -104,23 +104,38 @@ def time_point(qd, sm, batch, length, steps, warmup, vocab, seed):
     return per, wall
 
 
-def _timed(calls, stream):
-    """Run each call bracketed by HIP events on `stream`; durations in ms."""
+def _timed(calls, stream, replays=5):
+    """Average duration (ms) of one call of `calls`: the calls are captured in
+    order into one HIP graph on `stream` and replayed between HIP events on
+    that stream, so host launch gaps are not counted; median over `replays`."""
     import torch
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
     with torch.cuda.stream(stream):
-        for fn, (a, b) in zip(calls, ev):
-            a.record(stream)
-            fn()
-            b.record(stream)
+        calls[0]()                                   # first launch of the kernel: not timed
     torch.cuda.synchronize()
-    return [a.elapsed_time(b) for a, b in ev]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for fn in calls:
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    per = []
+    with torch.cuda.stream(stream):          # replay() launches on the current stream
+        for _ in range(replays):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            graph.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            per.append(a.elapsed_time(b) / len(calls))
+    del graph
+    return sorted(per)[len(per) // 2]
 
 
 def kernel_timing(qd, sd, dev_model, sm, batch, length, seed):
-    """Per-launch durations of the step's kernels with HIP events on the stream
-    they are launched on, over the 36 layers' own weights and caches (so no
-    launch finds its data in the last-level cache)."""
+    """Per-launch durations of the step's kernels: each kind's 36 launches over
+    the 36 layers' own weights and caches (so no launch finds its data in the
+    last-level cache), captured in a HIP graph and timed with HIP events on the
+    stream they are launched on."""
     import torch
     embed, lm_head, norm, layers = dev_model
     g = sd.generator(seed)
@@ -152,16 +167,16 @@ def kernel_timing(qd, sd, dev_model, sm, batch, length, seed):
     }
     out = {}
     notes = {
-        "gemm_qkv": "ABI entry, fp16 activations (K over the waves of one work-group per tile); the step runs "
-                    "this shape with RMSNorm fused and the RoPE / KV-append finish (split-K)",
+        "gemm_qkv": "ABI entry, fp16 activations, two tiles per work-group; the step runs this shape with the "
+                    "RMSNorm fused and the RoPE / fp16-append finish (one head's tile pair per work-group)",
         "gemm_o": "same kernel as the step's O projection",
-        "gemm_gate_up_swiglu": "ABI entry, fp16 activations (split-K); the step fuses the RMSNorm",
+        "gemm_gate_up_swiglu": "ABI entry, fp16 activations; the step runs the same multi-item kernel with the "
+                               "RMSNorm fused",
         "gemm_down": "same kernel as the step's down projection",
     }
     for name, (fn, nbytes) in kinds.items():
-        _timed([lambda ly=layers[0]: fn(ly)], stream)          # first launch of this kernel: not timed
         ms = _timed([lambda ly=ly: fn(ly) for ly in layers], stream)
-        out[name] = {"launches_per_step": len(layers), "avg_ms": sum(ms) / len(ms), "bytes_per_launch": nbytes,
+        out[name] = {"launches_per_step": len(layers), "avg_ms": ms, "bytes_per_launch": nbytes,
                      "note": notes[name]}
 
     # attention over the 36 per-layer caches of the timed workload, n_ctx = L
@@ -173,10 +188,9 @@ def kernel_timing(qd, sd, dev_model, sm, batch, length, seed):
     aws = torch.zeros(qd.qkdec_attn_workspace_size(batch, HQ, kvs[0]), dtype=torch.uint8, device="cuda")
     fa = lambda kv: qd.qkdec_attn_decode(kv, slot, nctx, batch, q, HQ, D ** -0.5, o16=o, workspace=aws,
                                          stream=stream)
-    _timed([lambda: fa(kvs[0])], stream)
     ms = _timed([lambda kv=kv: fa(kv) for kv in kvs], stream)
     kv_bytes = KV_BYTES_PER_TOKEN["f16" if kvs[0].type == 0 else "q8_0"] // NL
-    out["attention (split + merge)"] = {"launches_per_step": len(kvs), "avg_ms": sum(ms) / len(ms),
+    out["attention (split + merge)"] = {"launches_per_step": len(kvs), "avg_ms": ms,
                                         "bytes_per_launch": batch * length * kv_bytes,
                                         "note": "same kernels as the step's attention (n_ctx = L here, L + 1 "
                                                 "in the step)"}
@@ -184,9 +198,8 @@ def kernel_timing(qd, sd, dev_model, sm, batch, length, seed):
     tok = torch.empty(batch, dtype=torch.int32, device="cuda")
     lws = torch.zeros(qd.qkdec_lm_head_workspace_size(VOCAB, batch), dtype=torch.uint8, device="cuda")
     flm = lambda: qd.qkdec_lm_head_argmax(lm_head, VOCAB, H, x16, batch, tok, workspace=lws, stream=stream)
-    _timed([flm], stream)
     ms = _timed([flm] * 4, stream)
-    out["lm_head_argmax"] = {"launches_per_step": 1, "avg_ms": sum(ms) / len(ms), "bytes_per_launch": VOCAB * H * 2}
+    out["lm_head_argmax"] = {"launches_per_step": 1, "avg_ms": ms, "bytes_per_launch": VOCAB * H * 2}
     for v in out.values():
         v["GBps"] = v["bytes_per_launch"] / (v["avg_ms"] * 1e-3) / 1e9
         v["ms_per_step"] = v["avg_ms"] * v["launches_per_step"]
@@ -291,6 +304,8 @@ def main():
     ap.add_argument("--kv", choices=["f16", "q8_0"], default="f16")
     ap.add_argument("--points", choices=["all", "main"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="do not query rocm-smi (for runs under a profiler, whose preload the child would inherit)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run 3 plain device copies of this many MiB (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -379,7 +394,8 @@ def main():
                                f"B={main_pt['batch']}, L={main_pt['context']}",
                    "batch": main_pt["batch"], "context": main_pt["context"], "kv": main_pt["kv"]},
         "achieved_GBps": main_pt["achieved_GBps"], "frac_of_8TBps": main_pt["frac_of_8TBps"],
-        "frac_of_read_ceiling": main_pt["frac_of_read_ceiling"], "read_ceiling": ceiling, "clocks": clocks(),
+        "frac_of_read_ceiling": main_pt["frac_of_read_ceiling"], "read_ceiling": ceiling,
+        "clocks": None if args.no_clocks else clocks(),
         "roofline": roofline, "kernels": kernels, "points": results, "cpu_baseline": cpu,
     }
     print(json.dumps(out))
