@@ -25,7 +25,9 @@
 // Q8_0: keys are int8 + one fp16 scale per (token, 32 dims).  Each QK MFMA
 // covers exactly one 32-dim block; its fp32 result is multiplied by the
 // token's block scale.  Values: the per-(token, block) scale is folded into P
-// before the hi/lo split.  int8 -> fp16 is exact (byte permute into the
+// before the hi/lo split, with one power-of-two exponent per tile and head
+// (from the tile's largest value scale) keeping the pair clear of fp16
+// subnormals.  int8 -> fp16 is exact (byte permute into the
 // mantissa of 1024+128+x, then one packed subtract).
 #include "attn_dev.h"
 #include "common.h"
@@ -69,8 +71,7 @@ __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs
   for (int i = 0; i < D / 16; ++i) st.o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
   st.m = -__builtin_inff();
   st.l = 0.f;
-#pragma unroll
-  for (int c = 0; c < D / 32; ++c) st.ex[c] = 127;
+  st.ex = 127;
 
   // this wave's tiles: wave, wave + 4, ...  The next tile's keys are issued
   // before the current tile is processed, its values once the current tile's
@@ -98,7 +99,7 @@ __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs
   // undo the operand scaling of the value products (exact powers of two)
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) {
-    const float un = Q8 ? exp2i(-st.ex[i / 2]) : exp2i(-kPScale);
+    const float un = Q8 ? exp2i(-st.ex) : exp2i(-kPScale);
     st.o[i][0] *= un; st.o[i][1] *= un; st.o[i][2] *= un; st.o[i][3] *= un;
   }
   // merge the four waves' states (same lane layout in every wave) in LDS;

@@ -160,7 +160,7 @@ struct AttnState {
   floatx4 o[D / 16];
   float m;   // running max (log2 units), same in the 4 lane groups
   float l;   // this lane group's share of the running denominator
-  int ex[D / 32];   // Q8_0: o of value block c is kept multiplied by 2^ex[c] (never increases)
+  int ex;   // Q8_0: o is kept multiplied by 2^ex (never increases)
 };
 
 
@@ -195,10 +195,9 @@ __device__ __forceinline__ void attn_tile(AttnState<D, Q8>& st, KVFrag<D, Q8>& f
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[4 * hf + i] = acc[i] * scale_log2;
   }
-  if (valid < 32) {
+  if (valid < 32) {   // uniform branch; selects inside
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (8 * lg + e >= valid) sc[e] = -__builtin_inff();
+    for (int e = 0; e < 8; ++e) sc[e] = (8 * lg + e < valid) ? sc[e] : -__builtin_inff();
   }
   float tmax = sc[0];
 #pragma unroll
@@ -248,32 +247,34 @@ __device__ __forceinline__ void attn_tile(AttnState<D, Q8>& st, KVFrag<D, Q8>& f
     }
   } else {
     const int lim = valid - 8 * lg;   // tokens of this lane at or past lim are out of range
+    // p * scale is brought near 2^13..2^14 by an exact power of two taken from
+    // the largest value scale of the tile's in-range tokens (over all blocks),
+    // so the fp16 hi/lo pair keeps ~22 bits instead of sinking into fp16
+    // subnormals; the exponent never increases, a smaller one rescales o.
+    // Branch-free: an out-of-range token's scale may hold any bits and is
+    // selected away, never multiplied in.
+    float vmax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) vmax = fmaxf(vmax, e < lim ? fabsf(scale_at<D>(f.vs, e, c)) : 0.f);
+    vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
+    vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
+    const int exv = 13 - ((int)((__builtin_bit_cast(uint32_t, vmax) >> 23) & 255u) - 127);
+    const int exn = (vmax > 0.f && exv < st.ex) ? exv : st.ex;
+    const float fr = exp2i(exn - st.ex);   // 1 when the exponent stays
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      st.o[i][0] *= fr; st.o[i][1] *= fr; st.o[i][2] *= fr; st.o[i][3] *= fr;
+    }
+    st.ex = exn;
+    const float fc = exp2i(st.ex);
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
-      // p * scale is brought near 2^13..2^14 by an exact power of two taken from
-      // the largest scale seen so far in this block, so the fp16 hi/lo pair
-      // keeps ~22 bits instead of sinking into fp16 subnormals
-      float vmax = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (e < lim) vmax = fmaxf(vmax, fabsf(scale_at<D>(f.vs, e, c)));
-      vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
-      vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
-      if (vmax > 0.f) {
-        const int ex = 13 - ((int)((__builtin_bit_cast(uint32_t, vmax) >> 23) & 255u) - 127);
-        if (ex < st.ex[c]) {
-          const float fr = exp2i(ex - st.ex[c]);
-          st.o[2 * c][0] *= fr; st.o[2 * c][1] *= fr; st.o[2 * c][2] *= fr; st.o[2 * c][3] *= fr;
-          st.o[2 * c + 1][0] *= fr; st.o[2 * c + 1][1] *= fr; st.o[2 * c + 1][2] *= fr; st.o[2 * c + 1][3] *= fr;
-          st.ex[c] = ex;
-        }
-      }
-      const float fc = exp2i(st.ex[c]);
       half8_t phi, plo;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        // an out-of-range token's scale may hold any bits: never multiply it in
-        const float pv = (e < lim) ? p[e] * scale_at<D>(f.vs, e, c) * fc : 0.f;
+        const float pv = e < lim ? p[e] * scale_at<D>(f.vs, e, c) * fc : 0.f;
         const half_t h = (half_t)pv;
         phi[e] = h;
         plo[e] = (half_t)(pv - (float)h);
