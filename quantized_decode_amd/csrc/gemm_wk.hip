@@ -489,6 +489,16 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
   Q4Frag fr[PD][KW][T];
   constexpr int PD0 = XMODE != kXF16 ? 1 : PD;
   __builtin_amdgcn_sched_barrier(0);
+  // fp32 activations: every wave's small loads come home before any wave's
+  // weight stream starts (phase stamps: with weights issued per wave as soon
+  // as its own small loads were home, the last wave's small loads took 3.2 us
+  // against 1.2 us for the first, queued behind the other waves' streams);
+  // the statistics fold is done on the way
+  if constexpr (XMODE != kXF16) {
+    __builtin_amdgcn_s_waitcnt(0);
+    if constexpr (XMODE == kXNorm) ssf.fold(s_part);
+    __syncthreads();
+  }
 #pragma unroll
   for (int q = 0; q < PD0; ++q)
 #pragma unroll
@@ -509,8 +519,6 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
 
   // ---- A operands of this wave's K slice, kept for every item
   if constexpr (XMODE == kXNorm) {
-    ssf.fold(s_part);
-    __syncthreads();
     if (tx < 16) s_rinv[tx] = rms_inv<S>(s_part, tx, a.inv_k, a.eps);
     __syncthreads();
     // h = f16(x * rinv * gamma) of the rows < B into LDS
