@@ -40,7 +40,9 @@ def q4k_bytes(n, k):
 LAYER_Q4K = (q4k_bytes((HQ + 2 * HKV) * D, H) + q4k_bytes(H, HQ * D) + q4k_bytes(2 * FFN, H)
              + q4k_bytes(H, FFN))
 W_BYTES = NL * LAYER_Q4K + VOCAB * H * 2 + (2 * NL + 1) * H * 4     # shared bytes read once per step
-KV_BYTES_PER_TOKEN = {"f16": NL * HKV * D * 2 * 2, "q8_0": NL * HKV * D * 2 * 34 // 32}
+KV_BYTES_PER_TOKEN = {"f16": NL * HKV * D * 2 * 2, "q8_0": NL * HKV * D * 2 * 34 // 32,
+                      # keys and values in different formats: one fp16 tensor, one Q8_0
+                      "q8k_f16v": NL * HKV * D * (2 + 34 / 32), "f16k_q8v": NL * HKV * D * (2 + 34 / 32)}
 
 
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs (calibrated
@@ -60,14 +62,13 @@ def log(msg):
 
 def build_point(qd, sd, dims, dev_model, batch, length, kind, capacity, seed):
     import torch
-    from quantized_decode_amd import KV_F16, KV_Q8_0, kv_layer
+    from quantized_decode_amd import KV_KINDS, kv_layer
     g = sd.generator(seed)
     kvs, keep = [], []
     for _ in range(dims.n_layers):
         k, v, ks, vs = sd.kv_cache(g, kind, batch, dims.n_kv_heads, capacity, dims.head_dim, length)
         keep.append((k, v, ks, vs))
-        kvs.append(kv_layer(KV_F16 if kind == "f16" else KV_Q8_0, dims.n_kv_heads, dims.head_dim, capacity, batch,
-                            k, v, ks, vs))
+        kvs.append(kv_layer(KV_KINDS[kind], dims.n_kv_heads, dims.head_dim, capacity, batch, k, v, ks, vs))
     embed, lm_head, norm, layers = dev_model
     sm = qd.StepModel(dims, embed, lm_head, norm, layers, kvs)
     sm._keep = keep
@@ -189,7 +190,8 @@ def kernel_timing(qd, sd, dev_model, sm, batch, length, seed):
     fa = lambda kv: qd.qkdec_attn_decode(kv, slot, nctx, batch, q, HQ, D ** -0.5, o16=o, workspace=aws,
                                          stream=stream)
     ms = _timed([lambda kv=kv: fa(kv) for kv in kvs], stream)
-    kv_bytes = KV_BYTES_PER_TOKEN["f16" if kvs[0].type == 0 else "q8_0"] // NL
+    kind_of = {v: k for k, v in qd.KV_KINDS.items()}
+    kv_bytes = KV_BYTES_PER_TOKEN[kind_of[kvs[0].type]] / NL
     out["attention (split + merge)"] = {"launches_per_step": len(kvs), "avg_ms": ms,
                                         "bytes_per_launch": batch * length * kv_bytes,
                                         "note": "same kernels as the step's attention (n_ctx = L here, L + 1 "
@@ -301,7 +303,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--batch", type=int, default=8)
     ap.add_argument("--context", type=int, default=2400)
-    ap.add_argument("--kv", choices=["f16", "q8_0"], default="f16")
+    ap.add_argument("--kv", choices=["f16", "q8_0", "q8k_f16v", "f16k_q8v"], default="f16")
     ap.add_argument("--points", choices=["all", "main"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-clocks", action="store_true",
@@ -337,7 +339,8 @@ def main():
 
     points = [(args.batch, args.context, args.kv)]
     if args.points == "all":
-        for p in [(8, 2400, "f16"), (8, 6900, "f16"), (8, 2400, "q8_0"), (8, 6900, "q8_0")]:
+        for p in [(8, 2400, "f16"), (8, 6900, "f16"), (8, 2400, "q8_0"), (8, 6900, "q8_0"), (8, 2400, "q8k_f16v"),
+                  (8, 2400, "f16k_q8v")]:
             if p not in points:
                 points.append(p)
     results = []

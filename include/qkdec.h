@@ -69,7 +69,7 @@ enum {
   QKDEC_E_HIP = -7          /* the HIP runtime reported an error             */
 };
 
-enum { QKDEC_KV_F16 = 0, QKDEC_KV_Q8_0 = 1 };
+enum { QKDEC_KV_F16 = 0, QKDEC_KV_Q8_0 = 1, QKDEC_KV_Q8_0_K_F16_V = 2, QKDEC_KV_F16_K_Q8_0_V = 3 };
 
 /* Human-readable name of a status code (static string). */
 const char* qkdec_status_str(qkdec_status s);
@@ -144,9 +144,16 @@ qkdec_status qkdec_dequant_q4k(const void* W, int64_t n_blocks, float* out, void
  *   QKDEC_KV_Q8_0: k  int8 [n_slots][n_kv][capacity][head_dim]
  *                  v  int8 [n_slots][n_kv][head_dim][capacity]   (transposed)
  *                  k_scale, v_scale fp16 [n_slots][n_kv][capacity][head_dim/32]
- * All four pointers 16-byte aligned.  P3 "Why Q8 is close to free and where
+ *   QKDEC_KV_Q8_0_K_F16_V: keys as in QKDEC_KV_Q8_0 (k, k_scale), values as in
+ *                  QKDEC_KV_F16 (v), v_scale = NULL
+ *   QKDEC_KV_F16_K_Q8_0_V: keys as in QKDEC_KV_F16 (k), k_scale = NULL, values
+ *                  as in QKDEC_KV_Q8_0 (v, v_scale)
+ * All pointers in use 16-byte aligned.  P3 "Why Q8 is close to free and where
  * the sharp edges are": one byte per element plus the per-block scale, read
- * by the attention kernel directly. */
+ * by the attention kernel directly.  The same section and the FAQ "Does KV
+ * cache quantization hurt output quality?": keys are more sensitive to
+ * quantization than values, so the key and value formats are chosen
+ * independently (Q8_0 keys with fp16 values, or the reverse). */
 typedef struct {
   int32_t type;
   int32_t n_kv_heads;
@@ -172,6 +179,10 @@ qkdec_status qkdec_kv_append_f16(const qkdec_kv_layer* kv, const int32_t* slot, 
 qkdec_status qkdec_kv_append_q8_0(const qkdec_kv_layer* kv, const int32_t* slot, const int32_t* pos,
                                   const float* k, const float* v, int32_t B, int32_t* err,
                                   void* stream);
+/* The same store for any cache type: each of k and v is stored in its own
+ * format (fp16 rounding or the Q8_0 quantizer above) as kv->type gives it. */
+qkdec_status qkdec_kv_append(const qkdec_kv_layer* kv, const int32_t* slot, const int32_t* pos,
+                             const float* k, const float* v, int32_t B, int32_t* err, void* stream);
 
 /* ------------------------------------------------------------ attention ---
  * O[b][h] = sum_t softmax_t(scale * Q[b][h] . K[s][g][t]) V[s][g][t]

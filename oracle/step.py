@@ -18,8 +18,9 @@ with one power-of-two exponent offset per 256 values (formats.round_f16_blocked)
 so that the SwiGLU activation cannot overflow; everything else is fp64.
 The model object needs attributes dims, embed, lm_head, norm_final and
 layers[i].{w_qkv, w_o, w_gate_up, w_down, norm_attn, norm_ffn}; caches are per
-layer with k, v (fp16) or kq, ks, vq, vs (Q8_0) arrays of logical shape
-[n_slots, n_kv, capacity, head_dim] (scales [.., head_dim/32]).
+layer with k or (kq, ks) for the keys and v or (vq, vs) for the values (fp16,
+or Q8_0 codes and scales), arrays of logical shape [n_slots, n_kv, capacity,
+head_dim] (scales [.., head_dim/32]).
 """
 from __future__ import annotations
 
@@ -29,21 +30,30 @@ from .formats import q8_0_dequant, q8_0_quantize, round_f16, round_f16_blocked
 from .ops import argmax_lowest, attention, dense_gemm, q4k_gemm, rmsnorm, rope, swiglu
 
 
+# Key and value formats of each cache kind.  P3 "Why Q8 is close to free and
+# where the sharp edges are" and its FAQ "Does KV cache quantization hurt
+# output quality?": keys and values take their formats independently.
+KV_FORMATS = {"f16": ("f16", "f16"), "q8_0": ("q8_0", "q8_0"),
+              "q8k_f16v": ("q8_0", "f16"), "f16k_q8v": ("f16", "q8_0")}
+
+
 def kv_append(cache, kind: str, slot: int, pos: int, k: np.ndarray, v: np.ndarray) -> None:
     """Store one token's keys and values ([n_kv, D], fp64) at index pos of slot.
 
-    fp16 cache: round to nearest-even fp16.  Q8_0 cache (P3 "Why Q8 is close to
-    free and where the sharp edges are"): per 32 values of one token and head,
-    see formats.q8_0_quantize.
+    Each tensor in its own format (KV_FORMATS[kind]).  fp16: round to
+    nearest-even fp16 (fields k / v).  Q8_0 (P3 "Why Q8 is close to free and
+    where the sharp edges are"): per 32 values of one token and head, see
+    formats.q8_0_quantize (fields kq, ks / vq, vs).
     """
-    if kind == "f16":
-        cache.k[slot, :, pos] = np.asarray(k, dtype=np.float64).astype(np.float16)
-        cache.v[slot, :, pos] = np.asarray(v, dtype=np.float64).astype(np.float16)
-    elif kind == "q8_0":
-        cache.kq[slot, :, pos], cache.ks[slot, :, pos] = q8_0_quantize(k)
-        cache.vq[slot, :, pos], cache.vs[slot, :, pos] = q8_0_quantize(v)
-    else:
+    if kind not in KV_FORMATS:
         raise ValueError(kind)
+    for name, fmt, x in (("k", KV_FORMATS[kind][0], k), ("v", KV_FORMATS[kind][1], v)):
+        if fmt == "f16":
+            getattr(cache, name)[slot, :, pos] = np.asarray(x, dtype=np.float64).astype(np.float16)
+        else:
+            q, d = q8_0_quantize(x)
+            getattr(cache, name + "q")[slot, :, pos] = q
+            getattr(cache, name + "s")[slot, :, pos] = d
 
 
 def kv_read(cache, kind: str, slot: int, n: int):
@@ -52,12 +62,15 @@ def kv_read(cache, kind: str, slot: int, n: int):
     P3 (FAQ "Is KV cache quantization a kernel change or a storage change?"):
     the attention reads the quantized values dequantized, d*q.
     """
-    if kind == "f16":
-        return (cache.k[slot, :, :n].astype(np.float64), cache.v[slot, :, :n].astype(np.float64))
-    if kind == "q8_0":
-        return (q8_0_dequant(cache.kq[slot, :, :n], cache.ks[slot, :, :n]),
-                q8_0_dequant(cache.vq[slot, :, :n], cache.vs[slot, :, :n]))
-    raise ValueError(kind)
+    if kind not in KV_FORMATS:
+        raise ValueError(kind)
+    out = []
+    for name, fmt in (("k", KV_FORMATS[kind][0]), ("v", KV_FORMATS[kind][1])):
+        if fmt == "f16":
+            out.append(getattr(cache, name)[slot, :, :n].astype(np.float64))
+        else:
+            out.append(q8_0_dequant(getattr(cache, name + "q")[slot, :, :n], getattr(cache, name + "s")[slot, :, :n]))
+    return out[0], out[1]
 
 
 def attention_batch(q: np.ndarray, cache, kind: str, slots, n_ctx, scale: float) -> np.ndarray:

@@ -17,6 +17,10 @@ LIB_PATH = os.path.join(HERE, "libqkdec.so")
 
 KV_F16 = 0
 KV_Q8_0 = 1
+KV_Q8_0_K_F16_V = 2     # Q8_0 keys, fp16 values
+KV_F16_K_Q8_0_V = 3     # fp16 keys, Q8_0 values
+# cache kinds by name (the oracle's names) and their key / value formats
+KV_KINDS = {"f16": KV_F16, "q8_0": KV_Q8_0, "q8k_f16v": KV_Q8_0_K_F16_V, "f16k_q8v": KV_F16_K_Q8_0_V}
 
 STATUS_NAMES = {0: "QKDEC_OK", -1: "QKDEC_E_ARG", -2: "QKDEC_E_SHAPE", -3: "QKDEC_E_ALIGN",
                 -4: "QKDEC_E_WORKSPACE", -5: "QKDEC_E_CAPACITY", -6: "QKDEC_E_UNSUPPORTED", -7: "QKDEC_E_HIP"}
@@ -68,6 +72,7 @@ _SIGNATURES = {
     "qkdec_dequant_q4k": (_I32, [_P, _I64, _P, _P]),
     "qkdec_kv_append_f16": (_I32, [ctypes.POINTER(KVLayer), _P, _P, _P, _P, _I32, _P, _P]),
     "qkdec_kv_append_q8_0": (_I32, [ctypes.POINTER(KVLayer), _P, _P, _P, _P, _I32, _P, _P]),
+    "qkdec_kv_append": (_I32, [ctypes.POINTER(KVLayer), _P, _P, _P, _P, _I32, _P, _P]),
     "qkdec_attn_workspace_size": (_SZ, [_I32, _I32, ctypes.POINTER(KVLayer)]),
     "qkdec_attn_decode": (_I32, [ctypes.POINTER(KVLayer), _P, _P, _I32, _P, _I32, _F, _P, _P, _P, _SZ, _P]),
     "qkdec_lm_head_workspace_size": (_SZ, [_I64, _I32]),
@@ -174,6 +179,11 @@ def qkdec_kv_append_f16(kv: KVLayer, slot, pos, k, v, b: int, err=None, stream=N
 def qkdec_kv_append_q8_0(kv: KVLayer, slot, pos, k, v, b: int, err=None, stream=None) -> None:
     _check(load_library().qkdec_kv_append_q8_0(ctypes.byref(kv), _ptr(slot), _ptr(pos), _ptr(k), _ptr(v), b,
                                                _ptr(err), _stream(stream)), "qkdec_kv_append_q8_0")
+
+
+def qkdec_kv_append(kv: KVLayer, slot, pos, k, v, b: int, err=None, stream=None) -> None:
+    _check(load_library().qkdec_kv_append(ctypes.byref(kv), _ptr(slot), _ptr(pos), _ptr(k), _ptr(v), b,
+                                          _ptr(err), _stream(stream)), "qkdec_kv_append")
 
 
 def qkdec_attn_workspace_size(b: int, n_q_heads: int, kv: KVLayer) -> int:

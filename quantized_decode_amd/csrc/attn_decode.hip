@@ -39,7 +39,7 @@ constexpr int kAttnWaves = 4;
 
 // Two waves per SIMD: with the split key / value prefetch the fp16 kernel
 // fits 256 registers without spilling (see the run targets next to kAttnChunk)
-template <int D, bool Q8>
+template <int D, bool KQ8, bool VQ8>
 __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs a) {
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = a.Hq / a.n_kv;
@@ -60,13 +60,13 @@ __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs
     const half_t* qrow = a.Q + ((size_t)b * a.Hq + g * G + (hv ? r : 0)) * D;
 #pragma unroll
     for (int j = 0; j < D / 32; ++j) {
-      const int d0 = Q8 ? (32 * j + 8 * lg) : ((D / 4) * lg + 8 * j);
+      const int d0 = KQ8 ? (32 * j + 8 * lg) : ((D / 4) * lg + 8 * j);
       qf[j] = hv ? *reinterpret_cast<const half8_t*>(qrow + d0) : half8_t{0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
   const size_t head_row0 = ((size_t)s * a.n_kv + g) * a.cap;
 
-  AttnState<D, Q8> st;
+  AttnState<D, VQ8> st;
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) st.o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
   st.m = -__builtin_inff();
@@ -78,19 +78,19 @@ __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs
   // softmax is done (two tiles of keys and values are never held at once)
   const int ntiles = (t_end - t_begin + 31) / 32;
   if (wave < ntiles) {
-    KVFrag<D, Q8> buf[2];
-    load_k<D, Q8>(buf[0], a, head_row0, t_begin + 32 * wave, lg, r);
-    load_v<D, Q8>(buf[0], a, head_row0, t_begin + 32 * wave, lg, r);
+    KVFrag<D, KQ8, VQ8> buf[2];
+    load_k(buf[0], a, head_row0, t_begin + 32 * wave, lg, r);
+    load_v(buf[0], a, head_row0, t_begin + 32 * wave, lg, r);
     for (int it = wave; it < ntiles; it += 2 * kAttnWaves) {
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         const int i = it + p * kAttnWaves;
         if (i < ntiles) {
           const int nx = (i + kAttnWaves < ntiles) ? i + kAttnWaves : i;
-          load_k<D, Q8>(buf[p ^ 1], a, head_row0, t_begin + 32 * nx, lg, r);
+          load_k(buf[p ^ 1], a, head_row0, t_begin + 32 * nx, lg, r);
           const int t0 = t_begin + 32 * i;
-          attn_tile<D, Q8>(st, buf[p], qf, a.scale_log2, min(32, t_end - t0), lg,
-                           [&]() { load_v<D, Q8>(buf[p ^ 1], a, head_row0, t_begin + 32 * nx, lg, r); });
+          attn_tile(st, buf[p], qf, a.scale_log2, min(32, t_end - t0), lg,
+                    [&]() { load_v(buf[p ^ 1], a, head_row0, t_begin + 32 * nx, lg, r); });
         }
       }
     }
@@ -99,7 +99,7 @@ __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs
   // undo the operand scaling of the value products (exact powers of two)
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) {
-    const float un = Q8 ? exp2i(-st.ex) : exp2i(-kPScale);
+    const float un = VQ8 ? exp2i(-st.ex) : exp2i(-kPScale);
     st.o[i][0] *= un; st.o[i][1] *= un; st.o[i][2] *= un; st.o[i][3] *= un;
   }
   // merge the four waves' states (same lane layout in every wave) in LDS;
@@ -211,7 +211,7 @@ hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, con
   a.Hq = n_q_heads;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.n_splits = attn_max_runs(kv.capacity, kv.n_kv_heads);
-  a.runs_wanted = attn_runs_wanted(B, kv.n_kv_heads, kv.type == QKDEC_KV_Q8_0);
+  a.runs_wanted = attn_runs_wanted(B, kv.n_kv_heads, kv.type != QKDEC_KV_F16);
   const int D = kv.head_dim;
   const size_t n_rows = (size_t)B * n_q_heads * a.n_splits;
   a.part_o = partials;
@@ -219,14 +219,17 @@ hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, con
   // runs past a sequence's own count return at once
   const int max_runs = attn_runs(kv.capacity, a.runs_wanted, a.n_splits);
   const dim3 grid(max_runs, kv.n_kv_heads, B);
-  const bool q8 = kv.type == QKDEC_KV_Q8_0;
+  const dim3 blk(64 * kAttnWaves);
+#define QK_ATTN(DD, KQ, VQ) hipLaunchKernelGGL((attn_split_kernel<DD, KQ, VQ>), grid, blk, 0, st, a)
+  const bool kq8 = kv_k_q8(kv.type), vq8 = kv_v_q8(kv.type);
   if (D == 128) {
-    if (q8) hipLaunchKernelGGL((attn_split_kernel<128, true>), grid, dim3(64 * kAttnWaves), 0, st, a);
-    else hipLaunchKernelGGL((attn_split_kernel<128, false>), grid, dim3(64 * kAttnWaves), 0, st, a);
+    if (kq8) { if (vq8) QK_ATTN(128, true, true); else QK_ATTN(128, true, false); }
+    else { if (vq8) QK_ATTN(128, false, true); else QK_ATTN(128, false, false); }
   } else {
-    if (q8) hipLaunchKernelGGL((attn_split_kernel<64, true>), grid, dim3(64 * kAttnWaves), 0, st, a);
-    else hipLaunchKernelGGL((attn_split_kernel<64, false>), grid, dim3(64 * kAttnWaves), 0, st, a);
+    if (kq8) { if (vq8) QK_ATTN(64, true, true); else QK_ATTN(64, true, false); }
+    else { if (vq8) QK_ATTN(64, false, true); else QK_ATTN(64, false, false); }
   }
+#undef QK_ATTN
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(n_q_heads, B), dim3(D), 0, st, a.part_o, a.part_ml, a.n_splits,

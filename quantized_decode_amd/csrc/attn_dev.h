@@ -33,22 +33,32 @@ __device__ __forceinline__ half8_t i8x8_to_h8(uint32_t w0, uint32_t w1) {
   return r;
 }
 
+// One 32-token tile of keys and values held by a lane; keys and values each
+// in their own cache format.
 template <int D, bool Q8>
-struct KVFrag;
-
+struct KPart;
 template <int D>
-struct KVFrag<D, false> {
+struct KPart<D, false> {
   half8_t k[2][D / 32];
+};
+template <int D>
+struct KPart<D, true> {
+  uint32_t k[2][D / 32][2];
+  uint32_t ks[D / 8];   // fp16 scales of tokens 8lg..8lg+7, D/32 blocks each (2 per dword)
+};
+template <int D, bool Q8>
+struct VPart;
+template <int D>
+struct VPart<D, false> {
   half8_t v[D / 16];
 };
-
 template <int D>
-struct KVFrag<D, true> {
-  uint32_t k[2][D / 32][2];
+struct VPart<D, true> {
   uint32_t v[D / 16][2];
-  uint32_t ks[D / 8];   // fp16 scales of tokens 8lg..8lg+7, D/32 blocks each (2 per dword)
   uint32_t vs[D / 8];
 };
+template <int D, bool KQ8, bool VQ8>
+struct KVFrag : KPart<D, KQ8>, VPart<D, VQ8> {};
 
 struct AttnArgs {
   const uint8_t* k;
@@ -85,8 +95,8 @@ __host__ __device__ __forceinline__ int attn_runs(int n, int wanted, int max_run
 
 // Keys (and their Q8_0 scales) of the 32-token tile at t0; head_row0 =
 // (slot * n_kv + g) * cap is the index of token 0 of this head.
-template <int D, bool Q8>
-__device__ __forceinline__ void load_k(KVFrag<D, Q8>& f, const AttnArgs& a, size_t head_row0, int t0, int lg,
+template <int D, bool Q8, bool VQ8>
+__device__ __forceinline__ void load_k(KVFrag<D, Q8, VQ8>& f, const AttnArgs& a, size_t head_row0, int t0, int lg,
                                        int m) {
   if constexpr (!Q8) {
     const half_t* kb = reinterpret_cast<const half_t*>(a.k) + head_row0 * D;
@@ -121,8 +131,8 @@ __device__ __forceinline__ void load_k(KVFrag<D, Q8>& f, const AttnArgs& a, size
 }
 
 // Values (and their Q8_0 scales) of the same tile, from the transposed cache.
-template <int D, bool Q8>
-__device__ __forceinline__ void load_v(KVFrag<D, Q8>& f, const AttnArgs& a, size_t head_row0, int t0, int lg,
+template <int D, bool KQ8, bool Q8>
+__device__ __forceinline__ void load_v(KVFrag<D, KQ8, Q8>& f, const AttnArgs& a, size_t head_row0, int t0, int lg,
                                        int m) {
   if constexpr (!Q8) {
     const half_t* vb = reinterpret_cast<const half_t*>(a.v) + head_row0 * D;  // [D][cap] of this head
@@ -172,15 +182,15 @@ constexpr int kPScale = 14;
 // are done, before the value products (the caller issues the next tile's
 // value loads there, into registers this tile's keys no longer need).  The
 // fp16 values of out-of-range tokens are zeroed in place in f.
-template <int D, bool Q8, typename Mid>
-__device__ __forceinline__ void attn_tile(AttnState<D, Q8>& st, KVFrag<D, Q8>& f, const half8_t (&qf)[D / 32],
+template <int D, bool KQ8, bool VQ8, typename Mid>
+__device__ __forceinline__ void attn_tile(AttnState<D, VQ8>& st, KVFrag<D, KQ8, VQ8>& f, const half8_t (&qf)[D / 32],
                                           float scale_log2, int valid, int lg, const Mid& mid) {
   // valid = number of tokens of this 32-token tile that are in range (1..32)
   float sc[8];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (!Q8) {
+    if constexpr (!KQ8) {
 #pragma unroll
       for (int j = 0; j < D / 32; ++j) acc = mfma16x16x32(f.k[hf][j], qf[j], acc);
     } else {
@@ -222,7 +232,7 @@ __device__ __forceinline__ void attn_tile(AttnState<D, Q8>& st, KVFrag<D, Q8>& f
   __builtin_amdgcn_sched_barrier(0);
   mid();
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (!Q8) {
+  if constexpr (!VQ8) {
     half8_t phi, plo;
     const float ps = exp2i(kPScale);
 #pragma unroll

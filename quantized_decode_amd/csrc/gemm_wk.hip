@@ -349,7 +349,7 @@ __device__ void qkv_finish(const WkArgs& a, Red red, int wave, int lane, int g, 
   }
   CacheRef c;
   c.k = ra.k; c.v = ra.v; c.ks = ra.ks; c.vs = ra.vs;
-  c.n_kv = ra.n_kv; c.cap = ra.cap; c.D = D; c.n_slots = ra.n_slots; c.q8 = false;
+  c.n_kv = ra.n_kv; c.cap = ra.cap; c.D = D; c.n_slots = ra.n_slots; c.kq8 = false; c.vq8 = false;
   const int kvh = is_v ? head - ra.Hq - ra.n_kv : head - ra.Hq;
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii) {
@@ -892,7 +892,8 @@ hipError_t launch_gemm_wi(const GemmLaunch& L, hipStream_t st) {
 // (head, half-head tile).  hipErrorNotSupported for any other case.
 hipError_t launch_gemm_wi_qkv(const GemmLaunch& L, const RopeAppendArgs& ra, int head_dim, hipStream_t st) {
   const int kb = (int)(L.K / 256);
-  if (kb != 16 || !L.x_f32 || !L.gamma || ra.q8 || (head_dim != 64 && head_dim != 128) || L.residual || L.ss_out)
+  if (kb != 16 || !L.x_f32 || !L.gamma || ra.kq8 || ra.vq8 || (head_dim != 64 && head_dim != 128) || L.residual ||
+      L.ss_out)
     return hipErrorNotSupported;
   WkArgs a{};
   a.W = reinterpret_cast<const uint8_t*>(L.W);

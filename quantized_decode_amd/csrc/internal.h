@@ -53,7 +53,7 @@ struct RopeAppendArgs {
   uint8_t *k, *v;        // cache of this layer (fp16 or Q8_0 codes)
   uint16_t *ks, *vs;     // Q8_0 block scales
   int n_kv, cap, n_slots, Hq;
-  bool q8;
+  bool kq8, vq8;          // Q8_0 keys / values (else fp16)
   float rope_base;
   uint16_t* q16;         // rotated queries, fp16 bits
   int32_t* err;          // set to QKDEC_E_CAPACITY for a position outside the cache
@@ -85,6 +85,10 @@ hipError_t launch_dequant_q4k(const void* W, int64_t n_blocks, float* out, hipSt
 // 2^20 rows (a SwiGLU launch covers gate and up: 2F <= 2^20).
 constexpr int kGemmMaxGroups = 16384;
 constexpr int64_t kGemmMaxRows = 16 * 4 * (int64_t)kGemmMaxGroups;
+
+// ---- cache formats: Q8_0 keys / values of a cache type (else fp16)
+inline bool kv_k_q8(int type) { return type == QKDEC_KV_Q8_0 || type == QKDEC_KV_Q8_0_K_F16_V; }
+inline bool kv_v_q8(int type) { return type == QKDEC_KV_Q8_0 || type == QKDEC_KV_F16_K_Q8_0_V; }
 
 // ---- attention (attn_decode.hip)
 // A sequence's n cached tokens (ceil(n/32) tiles of 32) are cut into runs of

@@ -30,7 +30,7 @@ struct CacheRef {
   uint16_t* ks;
   uint16_t* vs;
   int n_kv, cap, D, n_slots;
-  bool q8;
+  bool kq8, vq8;   // Q8_0 keys / values (else fp16)
 };
 
 // Element stores of dim d of (slot s, kv head g, position p), into K
@@ -64,7 +64,7 @@ __device__ __forceinline__ void q8_encode(double x, double amax, int8_t& q, uint
 // For Q8_0 all 32 lanes of the dim's block must call this together.
 __device__ __forceinline__ void store_elem(const CacheRef& c, bool is_v, int s, int g, int p, int d, float x,
                                            bool ok) {
-  if (!c.q8) {
+  if (!(is_v ? c.vq8 : c.kq8)) {
     if (ok) store_f16(c, is_v, s, g, p, d, x);
   } else {
     const double xd = (double)x;
@@ -95,7 +95,8 @@ __device__ __forceinline__ CacheRef cache_ref(const qkdec_kv_layer& kv) {
   c.cap = kv.capacity;
   c.D = kv.head_dim;
   c.n_slots = kv.n_slots;
-  c.q8 = kv.type == QKDEC_KV_Q8_0;
+  c.kq8 = kv.type == QKDEC_KV_Q8_0 || kv.type == QKDEC_KV_Q8_0_K_F16_V;
+  c.vq8 = kv.type == QKDEC_KV_Q8_0 || kv.type == QKDEC_KV_F16_K_Q8_0_V;
   return c;
 }
 

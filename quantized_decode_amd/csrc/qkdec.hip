@@ -42,14 +42,18 @@ qkdec_status check_gemm(const void* W, int64_t N, int64_t K, const uint16_t* X, 
 
 qkdec_status check_kv(const qkdec_kv_layer* kv) {
   if (!kv) return QKDEC_E_ARG;
-  if (kv->type != QKDEC_KV_F16 && kv->type != QKDEC_KV_Q8_0) return QKDEC_E_ARG;
+  if (kv->type < QKDEC_KV_F16 || kv->type > QKDEC_KV_F16_K_Q8_0_V) return QKDEC_E_ARG;
   if (!kv->k || !kv->v) return QKDEC_E_ARG;
   if (kv->head_dim != 64 && kv->head_dim != 128) return QKDEC_E_SHAPE;
   if (kv->n_kv_heads < 1 || kv->n_slots < 1 || kv->capacity < 32 || kv->capacity % 32 != 0) return QKDEC_E_SHAPE;
   if (!aligned(kv->k, 16) || !aligned(kv->v, 16)) return QKDEC_E_ALIGN;
-  if (kv->type == QKDEC_KV_Q8_0) {
-    if (!kv->k_scale || !kv->v_scale) return QKDEC_E_ARG;
-    if (!aligned(kv->k_scale, 16) || !aligned(kv->v_scale, 16)) return QKDEC_E_ALIGN;
+  if (kv_k_q8(kv->type)) {
+    if (!kv->k_scale) return QKDEC_E_ARG;
+    if (!aligned(kv->k_scale, 16)) return QKDEC_E_ALIGN;
+  }
+  if (kv_v_q8(kv->type)) {
+    if (!kv->v_scale) return QKDEC_E_ARG;
+    if (!aligned(kv->v_scale, 16)) return QKDEC_E_ALIGN;
   }
   return QKDEC_OK;
 }
@@ -160,7 +164,7 @@ qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int3
     ra.k = reinterpret_cast<uint8_t*>(kv[l].k); ra.v = reinterpret_cast<uint8_t*>(kv[l].v);
     ra.ks = reinterpret_cast<uint16_t*>(kv[l].k_scale); ra.vs = reinterpret_cast<uint16_t*>(kv[l].v_scale);
     ra.n_kv = kv[l].n_kv_heads; ra.cap = kv[l].capacity; ra.n_slots = kv[l].n_slots; ra.Hq = Hq;
-    ra.q8 = kv[l].type == QKDEC_KV_Q8_0; ra.rope_base = m->rope_base; ra.q16 = w.q16; ra.err = w.err;
+    ra.kq8 = kv_k_q8(kv[l].type); ra.vq8 = kv_v_q8(kv[l].type); ra.rope_base = m->rope_base; ra.q16 = w.q16; ra.err = w.err;
     // K = 4096: the resident multi-item projection, finishing each head slice
     // itself (fp16 cache) or followed by RoPE and the append as a small launch
     // (Q8_0 blocks span two work-groups); otherwise the split-K projection
@@ -297,7 +301,7 @@ static qkdec_status kv_append_common(const qkdec_kv_layer* kv, int type, const i
                                      const float* k, const float* v, int32_t B, int32_t* err, void* stream) {
   qkdec_status s = check_kv(kv);
   if (s != QKDEC_OK) return s;
-  if (kv->type != type) return QKDEC_E_ARG;
+  if (type >= 0 && kv->type != type) return QKDEC_E_ARG;
   if (!slot || !pos || !k || !v) return QKDEC_E_ARG;
   if (B < 1 || B > 16) return QKDEC_E_SHAPE;
   clear_stale_error();
@@ -312,6 +316,11 @@ qkdec_status qkdec_kv_append_f16(const qkdec_kv_layer* kv, const int32_t* slot, 
 qkdec_status qkdec_kv_append_q8_0(const qkdec_kv_layer* kv, const int32_t* slot, const int32_t* pos, const float* k,
                                   const float* v, int32_t B, int32_t* err, void* stream) {
   return kv_append_common(kv, QKDEC_KV_Q8_0, slot, pos, k, v, B, err, stream);
+}
+
+qkdec_status qkdec_kv_append(const qkdec_kv_layer* kv, const int32_t* slot, const int32_t* pos, const float* k,
+                             const float* v, int32_t B, int32_t* err, void* stream) {
+  return kv_append_common(kv, -1, slot, pos, k, v, B, err, stream);
 }
 
 size_t qkdec_attn_workspace_size(int32_t B, int32_t n_q_heads, const qkdec_kv_layer* kv) {

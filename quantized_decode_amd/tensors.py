@@ -11,7 +11,7 @@ from typing import Optional
 
 import numpy as np
 
-from . import KV_F16, KV_Q8_0, KVLayer, kv_layer
+from . import KV_F16, KV_F16_K_Q8_0_V, KV_Q8_0, KV_Q8_0_K_F16_V, KVLayer, kv_layer
 
 
 def dev(a: np.ndarray):
@@ -47,6 +47,23 @@ class DeviceKV:
         vq = np.ascontiguousarray(self.v.cpu().numpy().transpose(0, 1, 3, 2))
         return kq, self.k_scale.cpu().numpy(), vq, self.v_scale.cpu().numpy()
 
+    def logical(self):
+        """The cache as a logical object with the fields of its formats: k or
+        (kq, ks), v or (vq, vs), numpy [slots, kv, cap, D] (v transposed back)."""
+        from types import SimpleNamespace
+        k = self.k.cpu().numpy()
+        v = np.ascontiguousarray(self.v.cpu().numpy().transpose(0, 1, 3, 2))
+        out = SimpleNamespace()
+        if self.k_scale is None:
+            out.k = k
+        else:
+            out.kq, out.ks = k, self.k_scale.cpu().numpy()
+        if self.v_scale is None:
+            out.v = v
+        else:
+            out.vq, out.vs = v, self.v_scale.cpu().numpy()
+        return out
+
 
 def _f16_t(a):
     import torch
@@ -71,10 +88,23 @@ def upload_kv_q8(kq: np.ndarray, ks: np.ndarray, vq: np.ndarray, vs: np.ndarray)
 
 
 def upload_cache(c) -> DeviceKV:
-    """A logical cache object with k, v (fp16) or kq, ks, vq, vs (Q8_0)."""
-    if hasattr(c, "kq"):
+    """A logical cache object with k or (kq, ks) for the keys and v or (vq, vs)
+    for the values; fields of the other format absent or None."""
+    kq8 = getattr(c, "kq", None) is not None
+    vq8 = getattr(c, "vq", None) is not None
+    if kq8 and vq8:
         return upload_kv_q8(c.kq, c.ks, c.vq, c.vs)
-    return upload_kv_f16(c.k, c.v)
+    if not kq8 and not vq8:
+        return upload_kv_f16(c.k, c.v)
+    kl = c.kq if kq8 else c.k
+    slots, nkv, cap, d = kl.shape
+    kd = dev(c.kq) if kq8 else _f16_t(c.k)
+    ksd = _f16_t(c.ks) if kq8 else None
+    vd = dev(np.ascontiguousarray(c.vq.transpose(0, 1, 3, 2))) if vq8 else _f16_t(np.ascontiguousarray(
+        c.v.transpose(0, 1, 3, 2)))
+    vsd = _f16_t(c.vs) if vq8 else None
+    kind = KV_Q8_0_K_F16_V if kq8 else KV_F16_K_Q8_0_V
+    return DeviceKV(kind, kd, vd, ksd, vsd, kv_layer(kind, nkv, d, cap, slots, kd, vd, ksd, vsd))
 
 
 def upload_model(model):

@@ -181,6 +181,60 @@ def kv_cache_q8(rng_k: np.random.Generator, rng_v: np.random.Generator, n_slots:
     return out
 
 
+@dataclass
+class KVLayerMixed:
+    """Logical cache of one layer whose keys and values have different formats:
+    the fp16 tensor as in KVLayerF16 (k or v), the Q8_0 one as in KVLayerQ8
+    (kq, ks or vq, vs); the fields of the other format are None."""
+    k: Optional[np.ndarray] = None
+    kq: Optional[np.ndarray] = None
+    ks: Optional[np.ndarray] = None
+    v: Optional[np.ndarray] = None
+    vq: Optional[np.ndarray] = None
+    vs: Optional[np.ndarray] = None
+
+
+# key / value formats of the cache kinds
+KV_FORMATS = {"f16": ("f16", "f16"), "q8_0": ("q8_0", "q8_0"), "q8k_f16v": ("q8_0", "f16"), "f16k_q8v": ("f16", "q8_0")}
+
+
+def kv_cache_mixed(rng_k: np.random.Generator, rng_v: np.random.Generator, n_slots: int, n_kv: int,
+                   capacity: int, head_dim: int, filled, kind: str) -> KVLayerMixed:
+    """Keys and values each drawn as in the cache of their own format (fp16
+    N(0,1), or Q8_0 codes uniform in -127..127 with scales |N(0,1)|*0.02),
+    keys from rng_k and values from rng_v, slot by slot; zero past filled."""
+    shape = (n_slots, n_kv, capacity, head_dim)
+    sshape = (n_slots, n_kv, capacity, head_dim // Q8_BLOCK)
+    out = KVLayerMixed()
+    for name, fmt, rng in (("k", KV_FORMATS[kind][0], rng_k), ("v", KV_FORMATS[kind][1], rng_v)):
+        if fmt == "f16":
+            t = np.zeros(shape, np.float16)
+            for s in range(n_slots):
+                n = int(filled[s])
+                t[s, :, :n] = f16_normal(rng, (n_kv, n, head_dim))
+            setattr(out, name, t)
+        else:
+            q, sc = np.zeros(shape, np.int8), np.zeros(sshape, np.float16)
+            for s in range(n_slots):
+                n = int(filled[s])
+                q[s, :, :n] = rng.integers(-127, 128, size=(n_kv, n, head_dim), dtype=np.int8)
+                sc[s, :, :n] = (np.abs(rng.standard_normal(size=(n_kv, n, head_dim // Q8_BLOCK))) * 0.02).astype(
+                    np.float16)
+            setattr(out, name + "q", q)
+            setattr(out, name + "s", sc)
+    return out
+
+
+def kv_cache(kind: str, rng_k: np.random.Generator, rng_v: np.random.Generator, n_slots: int, n_kv: int,
+             capacity: int, head_dim: int, filled):
+    """The synthetic cache of a kind: "f16", "q8_0", "q8k_f16v" or "f16k_q8v"."""
+    if kind == "f16":
+        return kv_cache_f16(rng_k, rng_v, n_slots, n_kv, capacity, head_dim, filled)
+    if kind == "q8_0":
+        return kv_cache_q8(rng_k, rng_v, n_slots, n_kv, capacity, head_dim, filled)
+    return kv_cache_mixed(rng_k, rng_v, n_slots, n_kv, capacity, head_dim, filled, kind)
+
+
 def tokens(rng: np.random.Generator, batch: int, vocab: int) -> np.ndarray:
     return rng.integers(0, vocab, size=batch, dtype=np.int64).astype(np.int32)
 

@@ -53,10 +53,38 @@ def model(dims, seed: int, n_layers=None):
     return embed, lm_head, norm_final, layers
 
 
+def _tensor(g: torch.Generator, fmt: str, shape, filled: int, transposed: bool):
+    """One cache tensor (keys [.., cap, D] or transposed values [.., D, cap])
+    and its Q8_0 scales ([.., cap, D/32]) or None: fp16 N(0,1), or int8
+    uniform in -127..127 with scales |N|*0.02, for positions < filled."""
+    n_slots, n_kv, capacity, head_dim = shape
+    tshape = (n_slots, n_kv, head_dim, capacity) if transposed else shape
+    fill = (n_slots, n_kv, head_dim, filled) if transposed else (n_slots, n_kv, filled, head_dim)
+    idx = (slice(None), slice(None), slice(None), slice(0, filled)) if transposed else (
+        slice(None), slice(None), slice(0, filled))
+    if fmt == "f16":
+        t = torch.zeros(tshape, dtype=torch.float16, device="cuda")
+        t[idx] = f16_normal(g, fill)
+        return t, None
+    t = torch.zeros(tshape, dtype=torch.int8, device="cuda")
+    t[idx] = torch.randint(-127, 128, fill, dtype=torch.int8, device="cuda", generator=g)
+    sc = torch.zeros((n_slots, n_kv, capacity, head_dim // 32), dtype=torch.float16, device="cuda")
+    sc[:, :, :filled] = (torch.randn((n_slots, n_kv, filled, head_dim // 32), device="cuda", generator=g).abs()
+                         * 0.02).to(torch.float16)
+    return t, sc
+
+
 def kv_cache(g: torch.Generator, kind: str, n_slots: int, n_kv: int, capacity: int, head_dim: int, filled: int):
     """One layer of device cache in the library's layout (values transposed),
     N(0,1) fp16 or Q8_0 (int8 uniform in -127..127, scale |N|*0.02) for
-    positions < filled and zeros beyond.  Returns (k, v, k_scale, v_scale)."""
+    positions < filled and zeros beyond; kind "f16", "q8_0", or keys and values
+    in different formats, "q8k_f16v" / "f16k_q8v".  Returns (k, v, k_scale,
+    v_scale)."""
+    if kind in ("q8k_f16v", "f16k_q8v"):
+        shape = (n_slots, n_kv, capacity, head_dim)
+        k, ks = _tensor(g, "q8_0" if kind == "q8k_f16v" else "f16", shape, filled, False)
+        v, vs = _tensor(g, "f16" if kind == "q8k_f16v" else "q8_0", shape, filled, True)
+        return k, v, ks, vs
     if kind == "f16":
         k = torch.zeros((n_slots, n_kv, capacity, head_dim), dtype=torch.float16, device="cuda")
         v = torch.zeros((n_slots, n_kv, head_dim, capacity), dtype=torch.float16, device="cuda")

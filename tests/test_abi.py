@@ -89,6 +89,17 @@ def test_kv_and_attention_validation(lib):
     q8 = lib.qkdec_kv_append_q8_0
     assert q8(ctypes.byref(_kv(type=1)), FAKE, FAKE, FAKE, FAKE, 1, None, None) == -1   # scales missing
     assert q8(ctypes.byref(_kv()), FAKE, FAKE, FAKE, FAKE, 1, None, None) == -1          # type mismatch
+    # keys and values in different formats: only the Q8_0 tensor needs its scales;
+    # the strict entry points reject the mixed types, the generic one validates them
+    gen = lib.qkdec_kv_append
+    assert gen(ctypes.byref(_kv(type=2, v_scale=FAKE)), FAKE, FAKE, FAKE, FAKE, 1, None, None) == -1   # k_scale
+    assert gen(ctypes.byref(_kv(type=3, k_scale=FAKE)), FAKE, FAKE, FAKE, FAKE, 1, None, None) == -1   # v_scale
+    assert gen(ctypes.byref(_kv(type=2, k_scale=FAKE + 2)), FAKE, FAKE, FAKE, FAKE, 1, None, None) == -3
+    assert gen(ctypes.byref(_kv(type=4)), FAKE, FAKE, FAKE, FAKE, 1, None, None) == -1
+    assert gen(ctypes.byref(_kv(type=2, k_scale=FAKE)), FAKE, FAKE, FAKE, FAKE, 17, None, None) == -2
+    assert app(ctypes.byref(_kv(type=2, k_scale=FAKE)), FAKE, FAKE, FAKE, FAKE, 1, None, None) == -1
+    assert q8(ctypes.byref(_kv(type=3, v_scale=FAKE)), FAKE, FAKE, FAKE, FAKE, 1, None, None) == -1
+    assert lib.qkdec_attn_workspace_size(8, 32, ctypes.byref(_kv(type=3, v_scale=FAKE))) > 0
     att = lib.qkdec_attn_decode
     kv = _kv()
     need = lib.qkdec_attn_workspace_size(8, 32, ctypes.byref(kv))

@@ -20,10 +20,7 @@ def qd():
 
 def _make(kind, seed, n_slots, n_kv, cap, d, filled):
     st = synth.Streams(seed)
-    if kind == "f16":
-        c = synth.kv_cache_f16(st.next(), st.next(), n_slots, n_kv, cap, d, filled)
-    else:
-        c = synth.kv_cache_q8(st.next(), st.next(), n_slots, n_kv, cap, d, filled)
+    c = synth.kv_cache(kind, st.next(), st.next(), n_slots, n_kv, cap, d, filled)
     return c, st
 
 
@@ -32,17 +29,18 @@ def _run(qd, cache, kind, q, slots, n_ctx, scale, poison=False):
     from quantized_decode_amd.tensors import dev, upload_cache
     dkv = upload_cache(cache)
     if poison:   # positions past n_ctx hold NaN / garbage: they must never reach the output
-        if kind == "f16":
-            for s in range(cache.k.shape[0]):
-                used = max(int(n) for b, n in enumerate(n_ctx) if slots[b] == s) if s in list(slots) else 0
+        kfmt, vfmt = synth.KV_FORMATS[kind]
+        for s in range(dkv.desc.n_slots):
+            used = max(int(n) for b, n in enumerate(n_ctx) if slots[b] == s) if s in list(slots) else 0
+            if kfmt == "f16":
                 dkv.k[s, :, used:] = float("nan")
-                dkv.v[s, :, :, used:] = float("nan")
-        else:
-            for s in range(cache.kq.shape[0]):
-                used = max(int(n) for b, n in enumerate(n_ctx) if slots[b] == s) if s in list(slots) else 0
+            else:
                 dkv.k[s, :, used:] = 127
-                dkv.v[s, :, :, used:] = -127
                 dkv.k_scale[s, :, used:] = float("nan")
+            if vfmt == "f16":
+                dkv.v[s, :, :, used:] = float("nan")
+            else:
+                dkv.v[s, :, :, used:] = -127
                 dkv.v_scale[s, :, used:] = float("inf")
     b, hq, d = q.shape
     qd_t = dev(q.view(np.uint16)).view(torch.float16)
@@ -70,6 +68,13 @@ CASES = [
     ("q8_0", 32, 8, 128, 512, [1, 100, 128, 129, 300, 512]),
     ("q8_0", 16, 1, 128, 384, [383, 257, 5]),
     ("q8_0", 32, 4, 128, 288, [200, 288]),
+    # keys and values in different formats
+    ("q8k_f16v", 8, 2, 64, 256, [1, 31]),
+    ("q8k_f16v", 32, 8, 128, 512, [1, 100, 128, 129, 300, 512]),
+    ("q8k_f16v", 16, 1, 128, 384, [383, 257, 5]),
+    ("f16k_q8v", 8, 2, 64, 256, [129, 256]),
+    ("f16k_q8v", 32, 8, 128, 512, [1, 100, 128, 129, 300, 512]),
+    ("f16k_q8v", 32, 4, 128, 288, [200, 288]),
 ]
 
 
@@ -90,7 +95,7 @@ def test_attention_small(qd, kind, hq, hkv, d, cap, n_ctx):
     assert np.array_equal(o16, o.astype(np.float16))
 
 
-@pytest.mark.parametrize("kind", ["f16", "q8_0"])
+@pytest.mark.parametrize("kind", ["f16", "q8_0", "q8k_f16v", "f16k_q8v"])
 def test_attention_full_config(qd, kind):
     # 32 query heads on 8 KV heads of 128, B = 8 sequences of 2400 tokens, one layer
     bsz, hq, hkv, d, L = 8, 32, 8, 128, 2400

@@ -85,6 +85,39 @@ def test_append_q8_0_bit_exact(qd, d, nkv):
     assert int(err.cpu()[0]) == 0
 
 
+@pytest.mark.parametrize("kind", ["q8k_f16v", "f16k_q8v"])
+def test_append_mixed_formats_bit_exact(qd, kind):
+    # keys and values in different formats through the generic entry point,
+    # each stored exactly as the oracle stores that format
+    import copy
+
+    from oracle import step as OS
+    from quantized_decode_amd.tensors import upload_cache
+    st = synth.Streams(300 + len(kind))
+    slots_n, nkv, cap, d, bsz = 3, 8, 64, 128, 3
+    cache = synth.kv_cache(kind, st.next(), st.next(), slots_n, nkv, cap, d, [40, 64, 10])
+    dkv = upload_cache(cache)
+    rng = st.next()
+    slot = np.array([2, 0, 1], np.int32)
+    pos = np.array([63, 0, 17], np.int32)
+    k = (rng.standard_normal((bsz, nkv, d)) * 10.0 ** rng.integers(-6, 3, (bsz, nkv, 1))).astype(np.float32)
+    v = (rng.standard_normal((bsz, nkv, d)) * 20).astype(np.float32)
+    err = _dev(np.zeros(1, np.int32))
+    qd.qkdec_kv_append(dkv.desc, _dev(slot), _dev(pos), _dev(k), _dev(v), bsz, err=err)
+    sync()
+    got = dkv.logical()
+    want = copy.deepcopy(cache)
+    for b in range(bsz):
+        OS.kv_append(want, kind, int(slot[b]), int(pos[b]), k[b].astype(np.float64), v[b].astype(np.float64))
+    for name in ("k", "kq", "ks", "v", "vq", "vs"):
+        w = getattr(want, name, None)
+        if w is None:
+            continue
+        g = getattr(got, name)
+        assert g.dtype == w.dtype and np.array_equal(g.view(np.uint8), w.view(np.uint8)), f"{kind}: {name}"
+    assert int(err.cpu()[0]) == 0
+
+
 def test_append_out_of_range_sets_flag_and_writes_nothing(qd):
     from quantized_decode_amd.tensors import upload_kv_f16
     k0 = np.zeros((2, 2, 32, 64), np.float16)

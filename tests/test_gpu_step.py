@@ -31,8 +31,8 @@ def build(dims, seed, kind, bsz, length, cap, n_layers=None, n_slots=None):
     filled = [length] * n_slots
     caches = []
     for _ in model.layers:
-        mk = synth.kv_cache_f16 if kind == "f16" else synth.kv_cache_q8
-        caches.append(mk(st.next(), st.next(), n_slots, dims.n_kv_heads, cap, dims.head_dim, filled))
+        caches.append(synth.kv_cache(kind, st.next(), st.next(), n_slots, dims.n_kv_heads, cap, dims.head_dim,
+                                     filled))
     tok = synth.tokens(st.next(), bsz, dims.vocab)
     return model, caches, tok
 
@@ -74,7 +74,7 @@ def compare_logits(lg, ref, gtok, what):
     return d
 
 
-@pytest.mark.parametrize("kind", ["f16", "q8_0"])
+@pytest.mark.parametrize("kind", ["f16", "q8_0", "q8k_f16v", "f16k_q8v"])
 def test_toy_step_multi_step(qd, kind):
     # the toy workload: 2-layer decoder, B = 2 sequences with 128 cached tokens
     dims = synth.TOY
@@ -184,12 +184,7 @@ class _View:
 
 
 def _cache_from_device(dkv, kind):
-    from types import SimpleNamespace
-    if kind == "f16":
-        k, v = dkv.logical_f16()
-        return SimpleNamespace(k=k, v=v)
-    kq, ks, vq, vs = dkv.logical_q8()
-    return SimpleNamespace(kq=kq, ks=ks, vq=vq, vs=vs)
+    return dkv.logical()
 
 
 def _within_f16_ulp(got, want, what):
@@ -218,12 +213,13 @@ def check_layer_stages(dims, kind, ly, x_in, pos, vw, cache_dev, cache_before, s
         k = OO.rope(vw.qkv[b, qrows:qrows + krows].reshape(hkv, hd), p, dims.rope_base)
         v = vw.qkv[b, qrows + krows:].reshape(hkv, hd)
         _within_f16_ulp(vw.q16[b], q.reshape(-1), f"rotated q, sequence {b}")
-        if kind == "f16":
-            _within_f16_ulp(got.k[s, :, p], k, f"appended k, sequence {b}")
-            _within_f16_ulp(got.v[s, :, p], v, f"appended v, sequence {b}")
-            assert np.array_equal(got.k[s, :, :p].view(np.uint16), cache_before.k[s, :, :p].view(np.uint16))
-        else:
-            for name, want, gq, gs in (("k", k, got.kq, got.ks), ("v", v, got.vq, got.vs)):
+        for name, want, fmt in (("k", k, synth.KV_FORMATS[kind][0]), ("v", v, synth.KV_FORMATS[kind][1])):
+            if fmt == "f16":
+                _within_f16_ulp(getattr(got, name)[s, :, p], want, f"appended {name}, sequence {b}")
+                assert np.array_equal(getattr(got, name)[s, :, :p].view(np.uint16),
+                                      getattr(cache_before, name)[s, :, :p].view(np.uint16))
+            else:
+                gq, gs = getattr(got, name + "q"), getattr(got, name + "s")
                 wq, wd = OF.q8_0_quantize(want)
                 dg = gs[s, :, p].astype(np.float64)
                 do = wd.astype(np.float64)
@@ -232,7 +228,7 @@ def check_layer_stages(dims, kind, ly, x_in, pos, vw, cache_dev, cache_before, s
                 deq_o = OF.q8_0_dequant(wq, wd)
                 step = np.repeat(np.maximum(dg, do), 32, axis=-1)
                 assert (np.abs(deq_g - deq_o) <= 1.01 * step).all(), f"appended {name}, sequence {b}"
-            assert np.array_equal(got.kq[s, :, :p], cache_before.kq[s, :, :p])
+                assert np.array_equal(gq[s, :, :p], getattr(cache_before, name + "q")[s, :, :p])
         kd, vd = OS.kv_read(got, kind, s, p + 1)
         o = OO.attention(vw.q16[b].reshape(hq, hd), kd, vd, 1.0 / np.sqrt(hd)).reshape(-1)
         assert_rel(vw.o16[b], OF.round_f16(o), what=f"attention, sequence {b}")
@@ -253,7 +249,7 @@ def check_layer_stages(dims, kind, ly, x_in, pos, vw, cache_dev, cache_before, s
     assert_rel(vw.x, x1 + OO.q4k_gemm(ly.w_down, dims.hidden, dims.ffn, a16), what="residual after the layer")
 
 
-@pytest.mark.parametrize("kind", ["f16", "q8_0"])
+@pytest.mark.parametrize("kind", ["f16", "q8_0", "q8k_f16v"])
 def test_full_width_step_stagewise(qd, kind):
     # the Qwen-shaped model (hidden 4096, 32/8 heads of 128, FFN 12288, vocab 151936), first two
     # layers, B = 8 sequences at L = 2400.  With random Q4_K bytes the weights have a

@@ -237,3 +237,32 @@ def test_micro_model_brute_force(kind):
                 assert np.array_equal(got_k, np.array(bf_cache[li]["k"][s])[:, p])
         pos = pos + 1
         tok = nt
+
+
+@pytest.mark.parametrize("kind,kfrom,vfrom", [("q8k_f16v", "q8_0", "f16"), ("f16k_q8v", "f16", "q8_0")])
+def test_mixed_cache_formats_route_each_tensor(kind, kfrom, vfrom):
+    # keys and values in different formats: appending and reading a mixed cache
+    # must give, tensor by tensor, exactly what the pure fp16 and Q8_0 caches give
+    # (a swapped format or tensor would fail)
+    st = synth.Streams(7100)
+    n_slots, n_kv, cap, hd = 2, 2, 64, 64
+    f16c = synth.kv_cache("f16", st.next(), st.next(), n_slots, n_kv, cap, hd, [40, 17])
+    q8c = synth.kv_cache("q8_0", st.next(), st.next(), n_slots, n_kv, cap, hd, [40, 17])
+    pure = {"f16": f16c, "q8_0": q8c}
+    mixed = synth.KVLayerMixed()
+    for name, src in (("k", pure[kfrom]), ("v", pure[vfrom])):
+        for f in (name, name + "q", name + "s"):
+            if hasattr(src, f):
+                setattr(mixed, f, getattr(src, f).copy())
+    rng = st.next()
+    for slot, pos in ((0, 40), (1, 17), (1, 63)):
+        k = rng.standard_normal((n_kv, hd)) * 3.0
+        v = rng.standard_normal((n_kv, hd)) * 0.01
+        S.kv_append(mixed, kind, slot, pos, k, v)
+        S.kv_append(pure[kfrom], kfrom, slot, pos, k, v)
+        S.kv_append(pure[vfrom], vfrom, slot, pos, k, v)
+        km, vm = S.kv_read(mixed, kind, slot, pos + 1)
+        assert np.array_equal(km, S.kv_read(pure[kfrom], kfrom, slot, pos + 1)[0])
+        assert np.array_equal(vm, S.kv_read(pure[vfrom], vfrom, slot, pos + 1)[1])
+    with pytest.raises(ValueError):
+        S.kv_read(mixed, "q4_0", 0, 1)
