@@ -287,3 +287,26 @@ def test_full_width_step_stagewise(qd, kind):
     check_layer_stages(dims, kind, model.layers[1], x_l0, pos, vw2, g.kv[1], caches[1], slots)
     import torch
     assert torch.equal(g.kv[0].k[:, :, L], k0), "layer 0 re-appended different keys"
+
+
+@pytest.mark.parametrize("bsz,kind", [(1, "f16"), (16, "f16"), (16, "q8_0")])
+def test_full_width_step_stagewise_batch_sizes(qd, bsz, kind):
+    # the Qwen-shaped layer at the ends of the batch range: B = 1 and B = 16 (the
+    # projections stage rows 8..15 in a second pass), one layer, L = 300,
+    # every stage against the oracle fed with the GPU's own input to that stage
+    from oracle import ops as OO
+    dims = synth.QWEN_SHAPED
+    L = 300
+    slots = list(range(bsz))
+    model, caches, tok = build(dims, 1103 + bsz, kind, bsz, L, 320, n_layers=1)
+    pos = np.full(bsz, L)
+    g = GpuStep(qd, model, caches, bsz, slots)
+    g.set(pos, tok)
+    g.step()
+    vw = _View(qd, g, dims, bsz)
+    x_emb = model.embed[tok].astype(np.float64)
+    check_layer_stages(dims, kind, model.layers[0], x_emb, pos, vw, g.kv[0], caches[0], slots)
+    _within_f16_ulp(vw.h, OO.rmsnorm(vw.x, model.norm_final, dims.rms_eps), "final RMSNorm")
+    ref = OO.dense_gemm(model.lm_head, vw.h)
+    compare_logits(g.logits.cpu().numpy(), ref, g.tok.cpu().numpy(), f"LM head (B={bsz}, {kind})")
+    assert (g.pos.cpu().numpy() == pos + 1).all()
