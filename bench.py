@@ -9,7 +9,10 @@ split-K attention, O GEMM + residual, RMSNorm, gate/up GEMM + SwiGLU, down
 GEMM + residual), final norm, LM head and argmax, with the token fed back and
 the position advanced on the device; the step is replayed from a HIP graph.
 Inputs (weights, caches) are drawn on the GPU and resident in HBM before the
-timed region.  Extra points on the same line: L = 6900, and the Q8_0 cache.
+timed region.  Extra points on the same line ("points"): L = 6900; the Q8_0
+cache and the two mixed caches (Q8_0 keys with fp16 values and the reverse);
+B = 1 at L = 2400; B = 16 at L = 3400 (fp16 and Q8_0); Q8_0 at L = 8192 and
+19000.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
@@ -340,7 +343,8 @@ def main():
     points = [(args.batch, args.context, args.kv)]
     if args.points == "all":
         for p in [(8, 2400, "f16"), (8, 6900, "f16"), (8, 2400, "q8_0"), (8, 6900, "q8_0"), (8, 2400, "q8k_f16v"),
-                  (8, 2400, "f16k_q8v")]:
+                  (8, 2400, "f16k_q8v"), (1, 2400, "f16"), (16, 3400, "f16"), (16, 3400, "q8_0"), (8, 8192, "q8_0"),
+                  (8, 19000, "q8_0")]:
             if p not in points:
                 points.append(p)
     results = []
