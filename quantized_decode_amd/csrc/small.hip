@@ -48,19 +48,19 @@ __global__ void __launch_bounds__(256) rmsnorm_f16_kernel(const float* __restric
 // (g, r) reads row r of the tile, 8 values at 32j + 8g of each 256-wide chunk.
 // Every wave keeps a running (max, lowest index) per sequence; the work-group
 // result goes to a partials buffer that lm_argmax_reduce_kernel folds.
-constexpr int kLmWaves = 4;
+constexpr int kLmWaves = 8;
 constexpr int kLmGroups = 512;   // work-groups of the LM head launch (grid-stride over tiles)
 
 __device__ __forceinline__ void better(float& v, int& ix, float v2, int ix2) {
   if (v2 > v || (v2 == v && ix2 < ix)) { v = v2; ix = ix2; }
 }
 
-__global__ void __launch_bounds__(256) lm_head_kernel(const half_t* __restrict__ W, int n_tiles, int H,
+__global__ void __launch_bounds__(64 * kLmWaves) lm_head_kernel(const half_t* __restrict__ W, int n_tiles, int H,
                                                       const half_t* __restrict__ X, int B, float* logits, int64_t V,
                                                       float* part_v, int32_t* part_i) {
   extern __shared__ half_t xs[];                 // [B][H + 8]
   const int ldsx = H + 8;
-  for (int idx = threadIdx.x; idx < B * (H / 8); idx += 256) {
+  for (int idx = threadIdx.x; idx < B * (H / 8); idx += 64 * kLmWaves) {
     const int b = idx / (H / 8), c = idx % (H / 8);
     *reinterpret_cast<half8_t*>(xs + b * ldsx + 8 * c) = *reinterpret_cast<const half8_t*>(X + (size_t)b * H + 8 * c);
   }
@@ -184,7 +184,7 @@ hipError_t launch_lm_head_argmax(const uint16_t* Wlm, int64_t V, int64_t H, cons
   float* pv = reinterpret_cast<float*>(partials);
   int32_t* pi = reinterpret_cast<int32_t*>(pv + (size_t)kLmGroups * 16);
   const size_t lds = (size_t)B * (H + 8) * sizeof(half_t);
-  hipLaunchKernelGGL(lm_head_kernel, dim3(groups), dim3(256), lds, st, reinterpret_cast<const half_t*>(Wlm), n_tiles,
+  hipLaunchKernelGGL(lm_head_kernel, dim3(groups), dim3(64 * kLmWaves), lds, st, reinterpret_cast<const half_t*>(Wlm), n_tiles,
                      (int)H, reinterpret_cast<const half_t*>(X), B, logits, V, pv, pi);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
