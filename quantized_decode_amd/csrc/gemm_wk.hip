@@ -484,8 +484,10 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
     }
   }
 
-  // ---- weights of the first PD items (kXNorm: of the first item only while
-  // the x rows are held; the rest once the activations are built)
+  // ---- weights of the first PD items.  fp32 activations: issued only once
+  // the activations are staged in LDS (the first item), then once they are
+  // built (the rest): 16 waves' weight loads issued during the staging held
+  // it up (0.3-0.7 us per launch) and the x rows would share the registers
   Q4Frag fr[PD][KW][T];
   constexpr int PD0 = XMODE != kXF16 ? 1 : PD;
   __builtin_amdgcn_sched_barrier(0);
@@ -499,12 +501,14 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
     if constexpr (XMODE == kXNorm) ssf.fold(s_part);
     __syncthreads();
   }
+  if constexpr (XMODE == kXF16) {
 #pragma unroll
   for (int q = 0; q < PD0; ++q)
 #pragma unroll
       for (int p = 0; p < KW; ++p)
 #pragma unroll
         for (int tt = 0; tt < T; ++tt) load_frag(fr[q][p][tt], wptr(q, tt, sb0 + p), g);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // MODE 2: (cos, sin) of pair 16 hj + (tx % 16) at the position of row tx / 16
@@ -557,6 +561,14 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
       }
     }
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < PD0; ++q)
+#pragma unroll
+      for (int p = 0; p < KW; ++p)
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) load_frag(fr[q][p][tt], wptr(q, tt, sb0 + p), g);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int p = 0; p < KW; ++p) {
       const half_t* src = hs + (r < a.B ? r : 0) * LDH + (sbl + p) * 256 + 64 * g;
@@ -621,6 +633,14 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
       }
     }
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < PD0; ++q)
+#pragma unroll
+      for (int p = 0; p < KW; ++p)
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) load_frag(fr[q][p][tt], wptr(q, tt, sb0 + p), g);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int p = 0; p < KW; ++p) {
       const half_t* src = hs + (r < a.B ? r : 0) * LDH + (sbl + p) * 256 + 64 * g;
