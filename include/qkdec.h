@@ -96,7 +96,8 @@ int32_t qkdec_abi_version(void);
  * overlap.  The workspace contract is common to the three GEMM entry points:
  * qkdec_gemm_q4k itself computes each 16-row output tile in one work-group
  * (K split over its waves, partial sums added in LDS) and does not touch it;
- * the _xf32 and _swiglu variants split K across work-groups and use it.
+ * the _xf32 and _swiglu variants may split K across work-groups (by shape)
+ * and then use it.
  * Partial sums are added in a fixed order: results are deterministic and
  * independent of scheduling.
  */
