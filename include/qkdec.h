@@ -140,10 +140,13 @@ qkdec_status qkdec_dequant_q4k(const void* W, int64_t n_blocks, float* out, void
  * One layer of a slot-arena cache: n_slots independent sequences of up to
  * `capacity` tokens (capacity % 32 == 0), n_kv heads of head_dim (64 or 128).
  *   QKDEC_KV_F16:  k  fp16 [n_slots][n_kv][capacity][head_dim]
- *                  v  fp16 [n_slots][n_kv][head_dim][capacity]   (transposed)
+ *                  v  fp16 [n_slots][n_kv][capacity/32][head_dim][32]
+ *                     (transposed within blocks of 32 tokens: value d of
+ *                     token t at [t/32][d][t%32], so a 32-token tile of one
+ *                     head is one contiguous run)
  *                  k_scale = v_scale = NULL
  *   QKDEC_KV_Q8_0: k  int8 [n_slots][n_kv][capacity][head_dim]
- *                  v  int8 [n_slots][n_kv][head_dim][capacity]   (transposed)
+ *                  v  int8 [n_slots][n_kv][capacity/32][head_dim][32]
  *                  k_scale, v_scale fp16 [n_slots][n_kv][capacity][head_dim/32]
  *   QKDEC_KV_Q8_0_K_F16_V: keys as in QKDEC_KV_Q8_0 (k, k_scale), values as in
  *                  QKDEC_KV_F16 (v), v_scale = NULL

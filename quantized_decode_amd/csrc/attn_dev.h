@@ -130,7 +130,9 @@ __device__ __forceinline__ void load_k(KVFrag<D, Q8, VQ8>& f, const AttnArgs& a,
   }
 }
 
-// Values (and their Q8_0 scales) of the same tile, from the transposed cache.
+// Values (and their Q8_0 scales) of the same tile, from the value cache
+// transposed within 32-token blocks ([cap/32][D][32] per head: the tile at t0
+// is one contiguous run; lane (lg, m) reads tokens 8lg..8lg+7 of dim 16i + m).
 template <int D, bool KQ8, bool Q8>
 __device__ __forceinline__ void load_v(KVFrag<D, KQ8, Q8>& f, const AttnArgs& a, size_t head_row0, int t0, int lg,
                                        int m) {
@@ -138,12 +140,12 @@ __device__ __forceinline__ void load_v(KVFrag<D, KQ8, Q8>& f, const AttnArgs& a,
     const half_t* vb = reinterpret_cast<const half_t*>(a.v) + head_row0 * D;  // [D][cap] of this head
 #pragma unroll
     for (int i = 0; i < D / 16; ++i)
-      f.v[i] = *reinterpret_cast<const half8_t*>(vb + (size_t)(16 * i + m) * a.cap + t0 + 8 * lg);
+      f.v[i] = *reinterpret_cast<const half8_t*>(vb + ((size_t)(t0 >> 5) * D + 16 * i + m) * 32 + 8 * lg);
   } else {
     const uint8_t* vb = a.v + head_row0 * D;
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) {
-      const uint2 w = *reinterpret_cast<const uint2*>(vb + (size_t)(16 * i + m) * a.cap + t0 + 8 * lg);
+      const uint2 w = *reinterpret_cast<const uint2*>(vb + ((size_t)(t0 >> 5) * D + 16 * i + m) * 32 + 8 * lg);
       f.v[i][0] = w.x;
       f.v[i][1] = w.y;
     }

@@ -34,13 +34,17 @@ struct CacheRef {
 };
 
 // Element stores of dim d of (slot s, kv head g, position p), into K
-// (is_v = false) or into the transposed V: fp16 bits, or a Q8_0 code with its
-// block scale (written by the block's dim 0).
+// (is_v = false) or into V, which is transposed within 32-token blocks
+// ([cap/32][D][32] per head): fp16 bits, or a Q8_0 code with its block scale
+// (written by the block's dim 0).
+__device__ __forceinline__ size_t v_index(const CacheRef& c, size_t head, int p, int d) {
+  return ((head * (c.cap >> 5) + (p >> 5)) * c.D + d) * 32 + (p & 31);
+}
 __device__ __forceinline__ void store_f16(const CacheRef& c, bool is_v, int s, int g, int p, int d, float x) {
   const size_t head = (size_t)s * c.n_kv + g;
   const uint16_t h = f2h_bits(x);
   if (!is_v) reinterpret_cast<uint16_t*>(c.k)[(head * c.cap + p) * c.D + d] = h;
-  else reinterpret_cast<uint16_t*>(c.v)[(head * c.D + d) * c.cap + p] = h;
+  else reinterpret_cast<uint16_t*>(c.v)[v_index(c, head, p, d)] = h;
 }
 __device__ __forceinline__ void store_q8(const CacheRef& c, bool is_v, int s, int g, int p, int d, int8_t q,
                                          uint16_t dbits) {
@@ -49,7 +53,7 @@ __device__ __forceinline__ void store_q8(const CacheRef& c, bool is_v, int s, in
     reinterpret_cast<int8_t*>(c.k)[(head * c.cap + p) * c.D + d] = q;
     if ((d & 31) == 0) c.ks[(head * c.cap + p) * (c.D / 32) + d / 32] = dbits;
   } else {
-    reinterpret_cast<int8_t*>(c.v)[(head * c.D + d) * c.cap + p] = q;
+    reinterpret_cast<int8_t*>(c.v)[v_index(c, head, p, d)] = q;
     if ((d & 31) == 0) c.vs[(head * c.cap + p) * (c.D / 32) + d / 32] = dbits;
   }
 }

@@ -1,8 +1,8 @@
 """Device-memory helpers: lay host arrays out in the library's storage formats.
 
 These only move and reorder bytes (torch is used for device memory); the one
-layout change is the value cache, which the library keeps transposed per head
-([slot][kv head][head_dim][capacity]).
+layout change is the value cache, which the library keeps transposed within
+blocks of 32 tokens per head ([slot][kv head][capacity/32][head_dim][32]).
 """
 from __future__ import annotations
 
@@ -26,33 +26,51 @@ def empty(shape, dtype):
     return torch.empty(shape, dtype=dtype, device="cuda")
 
 
+def v_to_blocked(v: np.ndarray) -> np.ndarray:
+    """Logical values [slots, kv, cap, D] -> the cache layout [slots, kv, cap/32, D, 32]."""
+    s, k, cap, d = v.shape
+    return np.ascontiguousarray(v.reshape(s, k, cap // 32, 32, d).transpose(0, 1, 2, 4, 3))
+
+
+def v_from_blocked(vb: np.ndarray) -> np.ndarray:
+    """The cache layout [slots, kv, cap/32, D, 32] -> logical values [slots, kv, cap, D]."""
+    s, k, t, d, _ = vb.shape
+    return np.ascontiguousarray(vb.transpose(0, 1, 2, 4, 3).reshape(s, k, t * 32, d))
+
+
 @dataclass
 class DeviceKV:
     """One layer of device KV cache plus its ctypes descriptor."""
     kind: int
     k: object
-    v: object                 # transposed: [slots][kv][D][cap]
+    v: object                 # transposed in 32-token blocks: [slots][kv][cap/32][D][32]
     k_scale: Optional[object]
     v_scale: Optional[object]
     desc: KVLayer
 
     def logical_f16(self):
         """(k, v) as numpy fp16 [slots, kv, cap, D] (v transposed back)."""
-        k = self.k.cpu().numpy()
-        v = self.v.cpu().numpy().transpose(0, 1, 3, 2)
-        return k, np.ascontiguousarray(v)
+        return self.k.cpu().numpy(), v_from_blocked(self.v.cpu().numpy())
 
     def logical_q8(self):
         kq = self.k.cpu().numpy()
-        vq = np.ascontiguousarray(self.v.cpu().numpy().transpose(0, 1, 3, 2))
+        vq = v_from_blocked(self.v.cpu().numpy())
         return kq, self.k_scale.cpu().numpy(), vq, self.v_scale.cpu().numpy()
+
+    def set_v_from(self, slot: int, first: int, value) -> None:
+        """Set every value of positions >= first of slot (all heads and dims)."""
+        t0, j0 = divmod(first, 32)
+        if j0:
+            self.v[slot, :, t0, :, j0:] = value
+            t0 += 1
+        self.v[slot, :, t0:] = value
 
     def logical(self):
         """The cache as a logical object with the fields of its formats: k or
         (kq, ks), v or (vq, vs), numpy [slots, kv, cap, D] (v transposed back)."""
         from types import SimpleNamespace
         k = self.k.cpu().numpy()
-        v = np.ascontiguousarray(self.v.cpu().numpy().transpose(0, 1, 3, 2))
+        v = v_from_blocked(self.v.cpu().numpy())
         out = SimpleNamespace()
         if self.k_scale is None:
             out.k = k
@@ -74,7 +92,7 @@ def upload_kv_f16(k: np.ndarray, v: np.ndarray) -> DeviceKV:
     """k, v: fp16 [slots, kv, cap, D] (logical)."""
     slots, nkv, cap, d = k.shape
     kd = _f16_t(k)
-    vd = _f16_t(np.ascontiguousarray(v.transpose(0, 1, 3, 2)))
+    vd = _f16_t(v_to_blocked(v))
     return DeviceKV(KV_F16, kd, vd, None, None, kv_layer(KV_F16, nkv, d, cap, slots, kd, vd))
 
 
@@ -82,7 +100,7 @@ def upload_kv_q8(kq: np.ndarray, ks: np.ndarray, vq: np.ndarray, vs: np.ndarray)
     """kq, vq: int8 [slots, kv, cap, D]; ks, vs: fp16 [slots, kv, cap, D/32] (logical)."""
     slots, nkv, cap, d = kq.shape
     kd = dev(kq)
-    vd = dev(np.ascontiguousarray(vq.transpose(0, 1, 3, 2)))
+    vd = dev(v_to_blocked(vq))
     ksd, vsd = _f16_t(ks), _f16_t(vs)
     return DeviceKV(KV_Q8_0, kd, vd, ksd, vsd, kv_layer(KV_Q8_0, nkv, d, cap, slots, kd, vd, ksd, vsd))
 
@@ -100,8 +118,7 @@ def upload_cache(c) -> DeviceKV:
     slots, nkv, cap, d = kl.shape
     kd = dev(c.kq) if kq8 else _f16_t(c.k)
     ksd = _f16_t(c.ks) if kq8 else None
-    vd = dev(np.ascontiguousarray(c.vq.transpose(0, 1, 3, 2))) if vq8 else _f16_t(np.ascontiguousarray(
-        c.v.transpose(0, 1, 3, 2)))
+    vd = dev(v_to_blocked(c.vq)) if vq8 else _f16_t(v_to_blocked(c.v))
     vsd = _f16_t(c.vs) if vq8 else None
     kind = KV_Q8_0_K_F16_V if kq8 else KV_F16_K_Q8_0_V
     return DeviceKV(kind, kd, vd, ksd, vsd, kv_layer(kind, nkv, d, cap, slots, kd, vd, ksd, vsd))

@@ -53,6 +53,12 @@ def model(dims, seed: int, n_layers=None):
     return embed, lm_head, norm_final, layers
 
 
+def _blocked(vt: torch.Tensor) -> torch.Tensor:
+    """Values drawn as [slots, kv, D, cap] -> the cache layout [slots, kv, cap/32, D, 32]."""
+    s, k, d, cap = vt.shape
+    return vt.reshape(s, k, d, cap // 32, 32).permute(0, 1, 3, 2, 4).contiguous()
+
+
 def _tensor(g: torch.Generator, fmt: str, shape, filled: int, transposed: bool):
     """One cache tensor (keys [.., cap, D] or transposed values [.., D, cap])
     and its Q8_0 scales ([.., cap, D/32]) or None: fp16 N(0,1), or int8
@@ -75,7 +81,8 @@ def _tensor(g: torch.Generator, fmt: str, shape, filled: int, transposed: bool):
 
 
 def kv_cache(g: torch.Generator, kind: str, n_slots: int, n_kv: int, capacity: int, head_dim: int, filled: int):
-    """One layer of device cache in the library's layout (values transposed),
+    """One layer of device cache in the library's layout (values transposed
+    within 32-token blocks, drawn as [slots, kv, D, cap] and then blocked),
     N(0,1) fp16 or Q8_0 (int8 uniform in -127..127, scale |N|*0.02) for
     positions < filled and zeros beyond; kind "f16", "q8_0", or keys and values
     in different formats, "q8k_f16v" / "f16k_q8v".  Returns (k, v, k_scale,
@@ -84,13 +91,13 @@ def kv_cache(g: torch.Generator, kind: str, n_slots: int, n_kv: int, capacity: i
         shape = (n_slots, n_kv, capacity, head_dim)
         k, ks = _tensor(g, "q8_0" if kind == "q8k_f16v" else "f16", shape, filled, False)
         v, vs = _tensor(g, "f16" if kind == "q8k_f16v" else "q8_0", shape, filled, True)
-        return k, v, ks, vs
+        return k, _blocked(v), ks, vs
     if kind == "f16":
         k = torch.zeros((n_slots, n_kv, capacity, head_dim), dtype=torch.float16, device="cuda")
         v = torch.zeros((n_slots, n_kv, head_dim, capacity), dtype=torch.float16, device="cuda")
         k[:, :, :filled] = f16_normal(g, (n_slots, n_kv, filled, head_dim))
         v[:, :, :, :filled] = f16_normal(g, (n_slots, n_kv, head_dim, filled))
-        return k, v, None, None
+        return k, _blocked(v), None, None
     k = torch.zeros((n_slots, n_kv, capacity, head_dim), dtype=torch.int8, device="cuda")
     v = torch.zeros((n_slots, n_kv, head_dim, capacity), dtype=torch.int8, device="cuda")
     ks = torch.zeros((n_slots, n_kv, capacity, head_dim // 32), dtype=torch.float16, device="cuda")
@@ -103,4 +110,4 @@ def kv_cache(g: torch.Generator, kind: str, n_slots: int, n_kv: int, capacity: i
                          * 0.02).to(torch.float16)
     vs[:, :, :filled] = (torch.randn((n_slots, n_kv, filled, head_dim // 32), device="cuda", generator=g).abs()
                          * 0.02).to(torch.float16)
-    return k, v, ks, vs
+    return k, _blocked(v), ks, vs

@@ -38,9 +38,9 @@ def _run(qd, cache, kind, q, slots, n_ctx, scale, poison=False):
                 dkv.k[s, :, used:] = 127
                 dkv.k_scale[s, :, used:] = float("nan")
             if vfmt == "f16":
-                dkv.v[s, :, :, used:] = float("nan")
+                dkv.set_v_from(s, used, float("nan"))
             else:
-                dkv.v[s, :, :, used:] = -127
+                dkv.set_v_from(s, used, -127)
                 dkv.v_scale[s, :, used:] = float("inf")
     b, hq, d = q.shape
     qd_t = dev(q.view(np.uint16)).view(torch.float16)
