@@ -44,13 +44,17 @@ def kv_bytes_per_token(dims, kind: str) -> float:
     """Bytes one cached token costs across all layers, K and V.
 
     fp16: 2 bytes per element.  Q8_0: 34 bytes per 32 elements (32 int8 + one
-    fp16 scale); the pages round this to one byte per element.
+    fp16 scale); the pages round this to one byte per element.  fp8: one byte
+    per element, no scale (half of fp16, P2 "What a long-running swarm should
+    actually tune").
     """
     elems = dims.n_layers * dims.n_kv_heads * dims.head_dim * 2
     if kind == "f16":
         return elems * 2
     if kind == "q8_0":
         return elems * 34 // 32
+    if kind == "fp8":
+        return elems
     raise ValueError(kind)
 
 

@@ -23,6 +23,15 @@ the tile, block bytes).
 Q8_0 (P3, "Why Q8 is close to free and where the sharp edges are": one byte per
 KV element plus a per-block scale): 32 int8 values and one fp16 scale per
 block; value = d*q.  Blocks run along head_dim within one token and head.
+
+FP8 E4M3 (P2 "What a long-running swarm should actually tune" and P3 "Why Q8
+is close to free and where the sharp edges are": an 8-bit float KV cache that
+halves the fp16 footprint).  The pages name no variant; this library reads it
+as the OCP E4M3 format with no scale: one byte per element, sign bit, 4-bit
+exponent with bias 7, 3-bit mantissa; exponent field 0 is subnormal
+(m/8 * 2^-6); there is no infinity and S.1111.111 is NaN, so the largest finite
+magnitude is 1.75 * 2^8 = 448.  Stores round to nearest (ties to even) and
+saturate at +-448.
 """
 from __future__ import annotations
 
@@ -163,3 +172,40 @@ def q8_0_quantize(x: np.ndarray):
     r = np.clip(r, -127, 127)
     r = np.where(d == 0.0, 0.0, r)
     return r.astype(np.int8).reshape(x.shape), d16
+
+
+FP8_MAX = 448.0
+
+
+def fp8_e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """uint8 E4M3 codes -> fp64 values (exact; NaN for the two NaN codes)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    out = sign * mag
+    return np.where((c & 0x7F) == 0x7F, np.nan, out)
+
+
+def fp8_e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """fp64 values -> uint8 E4M3 codes: round to nearest, ties to even,
+    magnitudes above 448 saturate to 448 (NaN -> 0x7F, sign kept).
+
+    Below 2^-6 the grid is the subnormal step 2^-9; from 2^e (e >= -6) to
+    2^(e+1) it is 2^(e-3).  A magnitude that rounds up to the next power of
+    two lands on that binade's first code (code arithmetic carries into the
+    exponent field)."""
+    x = np.asarray(x, dtype=np.float64)
+    neg = np.signbit(x)
+    a = np.minimum(np.abs(x), FP8_MAX)
+    nan = np.isnan(x)
+    a = np.where(nan, 0.0, a)
+    _, ex = np.frexp(a)                      # a = f * 2^ex, f in [0.5, 1)
+    e = np.maximum(ex - 1, -6)               # binade floor(log2 a), at least -6
+    step = np.exp2((e - 3).astype(np.float64))
+    q = np.rint(a / step).astype(np.int64)   # rint: ties to even
+    sub = a < 2.0 ** -6
+    code = np.where(sub, q, ((e + 7) << 3) + q - 8)
+    code = np.where(nan, 0x7F, code)
+    return (code | (neg.astype(np.int64) << 7)).astype(np.uint8)

@@ -18,23 +18,26 @@ with one power-of-two exponent offset per 256 values (formats.round_f16_blocked)
 so that the SwiGLU activation cannot overflow; everything else is fp64.
 The model object needs attributes dims, embed, lm_head, norm_final and
 layers[i].{w_qkv, w_o, w_gate_up, w_down, norm_attn, norm_ffn}; caches are per
-layer with k or (kq, ks) for the keys and v or (vq, vs) for the values (fp16,
-or Q8_0 codes and scales), arrays of logical shape [n_slots, n_kv, capacity,
+layer with k, (kq, ks) or kf8 for the keys and v, (vq, vs) or vf8 for the
+values (fp16, Q8_0 codes and scales, or E4M3 codes), arrays of logical shape [n_slots, n_kv, capacity,
 head_dim] (scales [.., head_dim/32]).
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .formats import q8_0_dequant, q8_0_quantize, round_f16, round_f16_blocked
+from .formats import (fp8_e4m3_decode, fp8_e4m3_encode, q8_0_dequant, q8_0_quantize, round_f16,
+                      round_f16_blocked)
 from .ops import argmax_lowest, attention, dense_gemm, q4k_gemm, rmsnorm, rope, swiglu
 
 
 # Key and value formats of each cache kind.  P3 "Why Q8 is close to free and
 # where the sharp edges are" and its FAQ "Does KV cache quantization hurt
-# output quality?": keys and values take their formats independently.
+# output quality?": keys and values take their formats independently.  "fp8":
+# both in the 8-bit float format of formats.fp8_e4m3_encode (P2 "What a
+# long-running swarm should actually tune").
 KV_FORMATS = {"f16": ("f16", "f16"), "q8_0": ("q8_0", "q8_0"),
-              "q8k_f16v": ("q8_0", "f16"), "f16k_q8v": ("f16", "q8_0")}
+              "q8k_f16v": ("q8_0", "f16"), "f16k_q8v": ("f16", "q8_0"), "fp8": ("fp8", "fp8")}
 
 
 def kv_append(cache, kind: str, slot: int, pos: int, k: np.ndarray, v: np.ndarray) -> None:
@@ -43,13 +46,16 @@ def kv_append(cache, kind: str, slot: int, pos: int, k: np.ndarray, v: np.ndarra
     Each tensor in its own format (KV_FORMATS[kind]).  fp16: round to
     nearest-even fp16 (fields k / v).  Q8_0 (P3 "Why Q8 is close to free and
     where the sharp edges are"): per 32 values of one token and head, see
-    formats.q8_0_quantize (fields kq, ks / vq, vs).
+    formats.q8_0_quantize (fields kq, ks / vq, vs).  fp8: one E4M3 code per
+    value, formats.fp8_e4m3_encode (fields kf8 / vf8).
     """
     if kind not in KV_FORMATS:
         raise ValueError(kind)
     for name, fmt, x in (("k", KV_FORMATS[kind][0], k), ("v", KV_FORMATS[kind][1], v)):
         if fmt == "f16":
             getattr(cache, name)[slot, :, pos] = np.asarray(x, dtype=np.float64).astype(np.float16)
+        elif fmt == "fp8":
+            getattr(cache, name + "f8")[slot, :, pos] = fp8_e4m3_encode(x)
         else:
             q, d = q8_0_quantize(x)
             getattr(cache, name + "q")[slot, :, pos] = q
@@ -68,6 +74,8 @@ def kv_read(cache, kind: str, slot: int, n: int):
     for name, fmt in (("k", KV_FORMATS[kind][0]), ("v", KV_FORMATS[kind][1])):
         if fmt == "f16":
             out.append(getattr(cache, name)[slot, :, :n].astype(np.float64))
+        elif fmt == "fp8":
+            out.append(fp8_e4m3_decode(getattr(cache, name + "f8")[slot, :, :n]))
         else:
             out.append(q8_0_dequant(getattr(cache, name + "q")[slot, :, :n], getattr(cache, name + "s")[slot, :, :n]))
     return out[0], out[1]

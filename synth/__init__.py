@@ -194,8 +194,40 @@ class KVLayerMixed:
     vs: Optional[np.ndarray] = None
 
 
+@dataclass
+class KVLayerFp8:
+    """Logical 8-bit float cache of one layer: kf8, vf8 uint8 E4M3 codes
+    [n_slots, n_kv, capacity, head_dim]."""
+    kf8: np.ndarray
+    vf8: np.ndarray
+
+
+# Synthetic 8-bit float codes: sign uniform, the other seven bits uniform over
+# the 72 codes with exponent field 0..8 (magnitudes up to 3.75, subnormals
+# included, never a NaN code).
+FP8_CODE_SPAN = 72
+
+
+def fp8_codes(rng: np.random.Generator, shape) -> np.ndarray:
+    low = rng.integers(0, FP8_CODE_SPAN, size=shape, dtype=np.int64)
+    sign = rng.integers(0, 2, size=shape, dtype=np.int64)
+    return (low | (sign << 7)).astype(np.uint8)
+
+
+def kv_cache_fp8(rng_k: np.random.Generator, rng_v: np.random.Generator, n_slots: int, n_kv: int,
+                 capacity: int, head_dim: int, filled) -> KVLayerFp8:
+    shape = (n_slots, n_kv, capacity, head_dim)
+    out = KVLayerFp8(kf8=np.zeros(shape, np.uint8), vf8=np.zeros(shape, np.uint8))
+    for s in range(n_slots):
+        n = int(filled[s])
+        out.kf8[s, :, :n] = fp8_codes(rng_k, (n_kv, n, head_dim))
+        out.vf8[s, :, :n] = fp8_codes(rng_v, (n_kv, n, head_dim))
+    return out
+
+
 # key / value formats of the cache kinds
-KV_FORMATS = {"f16": ("f16", "f16"), "q8_0": ("q8_0", "q8_0"), "q8k_f16v": ("q8_0", "f16"), "f16k_q8v": ("f16", "q8_0")}
+KV_FORMATS = {"f16": ("f16", "f16"), "q8_0": ("q8_0", "q8_0"), "q8k_f16v": ("q8_0", "f16"), "f16k_q8v": ("f16", "q8_0"),
+              "fp8": ("fp8", "fp8")}
 
 
 def kv_cache_mixed(rng_k: np.random.Generator, rng_v: np.random.Generator, n_slots: int, n_kv: int,
@@ -227,7 +259,9 @@ def kv_cache_mixed(rng_k: np.random.Generator, rng_v: np.random.Generator, n_slo
 
 def kv_cache(kind: str, rng_k: np.random.Generator, rng_v: np.random.Generator, n_slots: int, n_kv: int,
              capacity: int, head_dim: int, filled):
-    """The synthetic cache of a kind: "f16", "q8_0", "q8k_f16v" or "f16k_q8v"."""
+    """The synthetic cache of a kind: "f16", "q8_0", "q8k_f16v", "f16k_q8v" or "fp8"."""
+    if kind == "fp8":
+        return kv_cache_fp8(rng_k, rng_v, n_slots, n_kv, capacity, head_dim, filled)
     if kind == "f16":
         return kv_cache_f16(rng_k, rng_v, n_slots, n_kv, capacity, head_dim, filled)
     if kind == "q8_0":

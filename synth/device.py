@@ -84,9 +84,20 @@ def kv_cache(g: torch.Generator, kind: str, n_slots: int, n_kv: int, capacity: i
     """One layer of device cache in the library's layout (values transposed
     within 32-token blocks, drawn as [slots, kv, D, cap] and then blocked),
     N(0,1) fp16 or Q8_0 (int8 uniform in -127..127, scale |N|*0.02) for
-    positions < filled and zeros beyond; kind "f16", "q8_0", or keys and values
-    in different formats, "q8k_f16v" / "f16k_q8v".  Returns (k, v, k_scale,
-    v_scale)."""
+    positions < filled and zeros beyond; kind "f16", "q8_0", keys and values
+    in different formats, "q8k_f16v" / "f16k_q8v", or "fp8" (uint8 E4M3 codes:
+    sign uniform, the other bits uniform over the 72 codes with exponent field
+    0..8, as synth.fp8_codes).  Returns (k, v, k_scale, v_scale)."""
+    if kind == "fp8":
+        def codes(shape):
+            low = torch.randint(0, 72, shape, dtype=torch.int32, device="cuda", generator=g)
+            sign = torch.randint(0, 2, shape, dtype=torch.int32, device="cuda", generator=g)
+            return (low | (sign << 7)).to(torch.uint8)
+        k = torch.zeros((n_slots, n_kv, capacity, head_dim), dtype=torch.uint8, device="cuda")
+        v = torch.zeros((n_slots, n_kv, head_dim, capacity), dtype=torch.uint8, device="cuda")
+        k[:, :, :filled] = codes((n_slots, n_kv, filled, head_dim))
+        v[:, :, :, :filled] = codes((n_slots, n_kv, head_dim, filled))
+        return k, _blocked(v), None, None
     if kind in ("q8k_f16v", "f16k_q8v"):
         shape = (n_slots, n_kv, capacity, head_dim)
         k, ks = _tensor(g, "q8_0" if kind == "q8k_f16v" else "f16", shape, filled, False)

@@ -19,6 +19,10 @@ def test_kv_bytes_per_token_matches_pages():
     assert kq == 78336                     # 34 bytes per 32 elements
     # the pages count one byte per element for int8 ("74 KB"): 73,728 B
     assert abs(k / 2 / 1000 - GOLD["kv_kb_per_token_int8"]["value"]) < 0.5
+    # an 8-bit float cache has no scales: exactly half of fp16, the pages' 74 KB
+    kf = M.kv_bytes_per_token(synth.QWEN_SHAPED, "fp8")
+    assert kf == 73728 and 2 * kf == k
+    assert abs(kf / 1000 - GOLD["kv_kb_per_token_int8"]["value"]) < 0.5
     # about a gigabyte per agent at 6,900 tokens
     assert abs(6900 * 147e3 / 1e9 - GOLD["kv_gb_at_6900_tokens"]["value"]) < 0.05
 

@@ -301,3 +301,74 @@ def test_blocked_f16_relative_precision():
     # normal-range values keep fp16's half-ulp relative error
     big = np.abs(x).reshape(4, 4, 256) > amax * 2.0 ** -10
     assert (err[big] <= np.abs(x.reshape(4, 4, 256))[big] * 2.0 ** -11).all()
+
+
+# ---- FP8 E4M3 (OCP variant: bias 7, no infinity, S.1111.111 NaN, max 448)
+
+def _finite_codes():
+    c = np.arange(256, dtype=np.uint8)
+    return c[(c & 0x7F) != 0x7F]
+
+
+def test_fp8_decode_hand_values():
+    d = F.fp8_e4m3_decode(np.array([0x00, 0x01, 0x07, 0x08, 0x38, 0x39, 0x3F, 0x40, 0x7E, 0xB8, 0xFE],
+                                   dtype=np.uint8))
+    expect = [0.0, 2.0 ** -9, 7 * 2.0 ** -9, 2.0 ** -6, 1.0, 1.125, 1.875, 2.0, 448.0, -1.0, -448.0]
+    assert d.tolist() == expect
+    assert np.isnan(F.fp8_e4m3_decode(np.array([0x7F, 0xFF], dtype=np.uint8))).all()
+    z = F.fp8_e4m3_decode(np.array([0x80], dtype=np.uint8))
+    assert z[0] == 0.0 and np.signbit(z[0])
+
+
+def test_fp8_decode_matches_torch_float8_e4m3fn():
+    torch = pytest.importorskip("torch")
+    c = _finite_codes()
+    ref = torch.from_numpy(c.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(F.fp8_e4m3_decode(c), ref)
+
+
+def test_fp8_decode_is_monotone_and_distinct():
+    c = np.arange(0x7F, dtype=np.uint8)          # non-negative finite codes in order
+    v = F.fp8_e4m3_decode(c)
+    assert (np.diff(v) > 0).all()
+
+
+def test_fp8_roundtrip_every_finite_code():
+    c = _finite_codes()
+    np.testing.assert_array_equal(F.fp8_e4m3_encode(F.fp8_e4m3_decode(c)), c)
+
+
+def test_fp8_encode_ties_to_even_and_saturation():
+    x = np.array([1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10, 5 * 2.0 ** -10, 15 * 2.0 ** -10, 1.9375,
+                  464.0, 1e9, -1e9, -1.0625, 447.9])
+    expect = [0x38, 0x3A, 0x00, 0x02, 0x02, 0x08, 0x40, 0x7E, 0x7E, 0xFE, 0xB8, 0x7E]
+    assert F.fp8_e4m3_encode(x).tolist() == expect
+    assert F.fp8_e4m3_encode(np.array([np.nan]))[0] == 0x7F
+
+
+def test_fp8_encode_is_nearest_by_brute_force():
+    # every value goes to the nearest finite code (ties: even mantissa), and
+    # magnitudes past 448 to +-448
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.standard_normal(4000) * 3, rng.standard_normal(2000) * 100,
+                        rng.standard_normal(2000) * 2.0 ** -8, rng.uniform(-600, 600, 500)])
+    got = F.fp8_e4m3_encode(x)
+    codes = _finite_codes()
+    vals = F.fp8_e4m3_decode(codes)
+    for xi, gi in zip(x, got):
+        a = min(abs(xi), 448.0)
+        cand = np.abs(vals - np.copysign(a, xi))
+        best = cand.min()
+        ties = codes[cand == best]
+        if len(ties) > 1:   # +0/-0, or a tie between two neighbours: the even mantissa
+            ties = [t for t in ties if (t & 1) == 0 and (np.signbit(xi) == bool(t & 0x80) or a != 0.0)]
+        assert gi in ties, (xi, gi, ties)
+
+
+def test_fp8_encode_matches_torch_in_range():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal(20000) * np.exp2(rng.uniform(-12, 8, 20000))).astype(np.float32)
+    x = np.clip(x, -448, 448)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(F.fp8_e4m3_encode(x.astype(np.float64)), ref)

@@ -31,17 +31,13 @@ def _toy(seed=1000, kind="f16", n_layers=None, batch=2, length=128):
     filled = [length] * batch
     caches = []
     for _ in model.layers:
-        if kind == "f16":
-            caches.append(synth.kv_cache_f16(st.next(), st.next(), batch, dims.n_kv_heads, cap,
-                                             dims.head_dim, filled))
-        else:
-            caches.append(synth.kv_cache_q8(st.next(), st.next(), batch, dims.n_kv_heads, cap,
-                                            dims.head_dim, filled))
+        caches.append(synth.kv_cache(kind, st.next(), st.next(), batch, dims.n_kv_heads, cap, dims.head_dim,
+                                     filled))
     tok = synth.tokens(st.next(), batch, dims.vocab)
     return model, caches, tok
 
 
-@pytest.mark.parametrize("kind", ["f16", "q8_0"])
+@pytest.mark.parametrize("kind", ["f16", "q8_0", "fp8"])
 def test_batch_invariance_bitwise(kind):
     model, caches, tok = _toy(kind=kind)
     slots = np.array([0, 1])
@@ -120,6 +116,37 @@ def _q8_brute(vals):
     return out, d
 
 
+def _fp8_values():
+    """(code, value) of every finite E4M3 code, from the format's definition:
+    bias 7, subnormal at exponent field 0, S.1111.111 NaN."""
+    out = []
+    for code in range(256):
+        sgn, e, m = code >> 7, (code >> 3) & 15, code & 7
+        if e == 15 and m == 7:
+            continue
+        mag = (m / 8) * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+        out.append((code, -mag if sgn else mag))
+    return out
+
+
+_FP8 = _fp8_values()
+
+
+def _fp8_brute(x: float) -> float:
+    """Nearest finite E4M3 value (ties: the even code), magnitudes past 448 to +-448."""
+    a = min(abs(x), 448.0)
+    t = math.copysign(a, x)
+    best = min(abs(v - t) for _, v in _FP8)
+    cands = [(c, v) for c, v in _FP8 if abs(v - t) == best]
+    if len(cands) > 1:
+        cands = [(c, v) for c, v in cands if c % 2 == 0]
+    return cands[0][1]
+
+
+def _fp8_code_value(c: int) -> float:
+    return dict(_FP8)[int(c)]
+
+
 def _brute_step(mdl, cache, kind, slots, pos, tok):
     dm = MICRO
     hq, hkv, hd, f = dm.n_q_heads, dm.n_kv_heads, dm.head_dim, dm.ffn
@@ -150,6 +177,9 @@ def _brute_step(mdl, cache, kind, slots, pos, tok):
                 if kind == "f16":
                     cache[li]["k"][slot][g][p] = [f16(v) for v in ks[g]]
                     cache[li]["v"][slot][g][p] = [f16(v) for v in vs[g]]
+                elif kind == "fp8":
+                    cache[li]["k"][slot][g][p] = [_fp8_brute(v) for v in ks[g]]
+                    cache[li]["v"][slot][g][p] = [_fp8_brute(v) for v in vs[g]]
                 else:
                     for name, src in (("k", ks[g]), ("v", vs[g])):
                         row = []
@@ -185,7 +215,7 @@ def _brute_step(mdl, cache, kind, slots, pos, tok):
     return np.array(logits), np.array(toks)
 
 
-@pytest.mark.parametrize("kind", ["f16", "q8_0"])
+@pytest.mark.parametrize("kind", ["f16", "q8_0", "fp8"])
 def test_micro_model_brute_force(kind):
     rng = np.random.default_rng(77)
     dm = MICRO
@@ -213,6 +243,10 @@ def test_micro_model_brute_force(kind):
         if kind == "f16":
             c = synth.kv_cache_f16(st.next(), st.next(), n_slots, hkv, cap, hd, [length] * n_slots)
             kk, vv = c.k.astype(np.float64), c.v.astype(np.float64)
+        elif kind == "fp8":
+            c = synth.kv_cache_fp8(st.next(), st.next(), n_slots, hkv, cap, hd, [length] * n_slots)
+            kk = np.vectorize(_fp8_code_value, otypes=[np.float64])(c.kf8)
+            vv = np.vectorize(_fp8_code_value, otypes=[np.float64])(c.vf8)
         else:
             c = synth.kv_cache_q8(st.next(), st.next(), n_slots, hkv, cap, hd, [length] * n_slots)
             kk = c.kq.astype(np.float64) * np.repeat(c.ks.astype(np.float64), 32, axis=-1)
@@ -231,6 +265,8 @@ def test_micro_model_brute_force(kind):
                 p = int(pos[b])
                 if kind == "f16":
                     got_k = caches[li].k[s, :, p].astype(np.float64)
+                elif kind == "fp8":
+                    got_k = np.vectorize(_fp8_code_value, otypes=[np.float64])(caches[li].kf8[s, :, p])
                 else:
                     got_k = caches[li].kq[s, :, p].astype(np.float64) * np.repeat(
                         caches[li].ks[s, :, p].astype(np.float64), 32, axis=-1)
