@@ -11,8 +11,8 @@ the position advanced on the device; the step is replayed from a HIP graph.
 Inputs (weights, caches) are drawn on the GPU and resident in HBM before the
 timed region.  Extra points on the same line ("points"): L = 6900; the Q8_0
 cache and the two mixed caches (Q8_0 keys with fp16 values and the reverse);
-B = 1 at L = 2400; B = 16 at L = 3400 (fp16 and Q8_0); Q8_0 at L = 8192 and
-19000.
+the 8-bit float (E4M3) cache at L = 2400 and 6900; B = 1 at L = 2400; B = 16 at
+L = 3400 (fp16 and Q8_0); Q8_0 at L = 8192 and 19000.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
@@ -45,7 +45,8 @@ LAYER_Q4K = (q4k_bytes((HQ + 2 * HKV) * D, H) + q4k_bytes(H, HQ * D) + q4k_bytes
 W_BYTES = NL * LAYER_Q4K + VOCAB * H * 2 + (2 * NL + 1) * H * 4     # shared bytes read once per step
 KV_BYTES_PER_TOKEN = {"f16": NL * HKV * D * 2 * 2, "q8_0": NL * HKV * D * 2 * 34 // 32,
                       # keys and values in different formats: one fp16 tensor, one Q8_0
-                      "q8k_f16v": NL * HKV * D * (2 + 34 / 32), "f16k_q8v": NL * HKV * D * (2 + 34 / 32)}
+                      "q8k_f16v": NL * HKV * D * (2 + 34 / 32), "f16k_q8v": NL * HKV * D * (2 + 34 / 32),
+                      "fp8": NL * HKV * D * 2}
 
 
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs (calibrated
@@ -306,7 +307,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--batch", type=int, default=8)
     ap.add_argument("--context", type=int, default=2400)
-    ap.add_argument("--kv", choices=["f16", "q8_0", "q8k_f16v", "f16k_q8v"], default="f16")
+    ap.add_argument("--kv", choices=["f16", "q8_0", "q8k_f16v", "f16k_q8v", "fp8"], default="f16")
     ap.add_argument("--points", choices=["all", "main"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-clocks", action="store_true",
@@ -343,7 +344,7 @@ def main():
     points = [(args.batch, args.context, args.kv)]
     if args.points == "all":
         for p in [(8, 2400, "f16"), (8, 6900, "f16"), (8, 2400, "q8_0"), (8, 6900, "q8_0"), (8, 2400, "q8k_f16v"),
-                  (8, 2400, "f16k_q8v"), (1, 2400, "f16"), (16, 3400, "f16"), (16, 3400, "q8_0"), (8, 8192, "q8_0"),
+                  (8, 2400, "f16k_q8v"), (8, 2400, "fp8"), (8, 6900, "fp8"), (1, 2400, "f16"), (16, 3400, "f16"), (16, 3400, "q8_0"), (8, 8192, "q8_0"),
                   (8, 19000, "q8_0")]:
             if p not in points:
                 points.append(p)

@@ -1,6 +1,7 @@
 /*
  * qkdec.h - C ABI of libqkdec: one batched LLM decode step with Q4_K weights
- * and an fp16 or Q8_0 KV cache, for AMD Instinct MI355X (gfx950).
+ * and an fp16, Q8_0, mixed or 8-bit float KV cache, for AMD Instinct MI355X
+ * (gfx950).
  *
  * Sources (three pages of one blog series on batched decode on one GPU):
  *   P1 "Batch One Is the Local LLM Assumption Agent Workloads Break on RDNA4"
@@ -69,7 +70,13 @@ enum {
   QKDEC_E_HIP = -7          /* the HIP runtime reported an error             */
 };
 
-enum { QKDEC_KV_F16 = 0, QKDEC_KV_Q8_0 = 1, QKDEC_KV_Q8_0_K_F16_V = 2, QKDEC_KV_F16_K_Q8_0_V = 3 };
+enum {
+  QKDEC_KV_F16 = 0,
+  QKDEC_KV_Q8_0 = 1,
+  QKDEC_KV_Q8_0_K_F16_V = 2,
+  QKDEC_KV_F16_K_Q8_0_V = 3,
+  QKDEC_KV_FP8_E4M3 = 4
+};
 
 /* Human-readable name of a status code (static string). */
 const char* qkdec_status_str(qkdec_status s);
@@ -152,12 +159,21 @@ qkdec_status qkdec_dequant_q4k(const void* W, int64_t n_blocks, float* out, void
  *                  QKDEC_KV_F16 (v), v_scale = NULL
  *   QKDEC_KV_F16_K_Q8_0_V: keys as in QKDEC_KV_F16 (k), k_scale = NULL, values
  *                  as in QKDEC_KV_Q8_0 (v, v_scale)
+ *   QKDEC_KV_FP8_E4M3: k  uint8 [n_slots][n_kv][capacity][head_dim]
+ *                  v  uint8 [n_slots][n_kv][capacity/32][head_dim][32]
+ *                  one OCP FP8 E4M3 code per element, no scale (sign, 4-bit
+ *                  exponent with bias 7, 3-bit mantissa, subnormals at
+ *                  exponent field 0, no infinity, S.1111.111 = NaN, largest
+ *                  finite 448); k_scale = v_scale = NULL
  * All pointers in use 16-byte aligned.  P3 "Why Q8 is close to free and where
  * the sharp edges are": one byte per element plus the per-block scale, read
  * by the attention kernel directly.  The same section and the FAQ "Does KV
  * cache quantization hurt output quality?": keys are more sensitive to
  * quantization than values, so the key and value formats are chosen
- * independently (Q8_0 keys with fp16 values, or the reverse). */
+ * independently (Q8_0 keys with fp16 values, or the reverse).  P2 "What a
+ * long-running swarm should actually tune" and P3 (same section): an 8-bit
+ * float cache halves the fp16 bytes per token; the pages name no variant and
+ * no scale, read here as unscaled E4M3. */
 typedef struct {
   int32_t type;
   int32_t n_kv_heads;
@@ -174,7 +190,9 @@ typedef struct {
  * already rotated) go to index pos[b] of slot slot[b].  fp16: round to
  * nearest even.  Q8_0, per block of 32 values, in fp64: d = RN_fp16(amax/127),
  * q = x/d rounded half away from zero, clamped to [-127, 127] (q = 0 when d is
- * 0).  slot, pos: device int32 [B].  A pos[b] outside [0, capacity) or slot
+ * 0).  FP8 E4M3: the fp32 value rounded to the nearest code (ties to even),
+ * magnitudes above 448 stored as +-448, NaN as 0x7F with its sign.  slot, pos:
+ * device int32 [B].  A pos[b] outside [0, capacity) or slot
  * outside [0, n_slots) stores nothing for b and sets *err (device int32, may
  * be NULL) to QKDEC_E_CAPACITY.  The type in kv must match the entry point. */
 qkdec_status qkdec_kv_append_f16(const qkdec_kv_layer* kv, const int32_t* slot, const int32_t* pos,
@@ -184,7 +202,8 @@ qkdec_status qkdec_kv_append_q8_0(const qkdec_kv_layer* kv, const int32_t* slot,
                                   const float* k, const float* v, int32_t B, int32_t* err,
                                   void* stream);
 /* The same store for any cache type: each of k and v is stored in its own
- * format (fp16 rounding or the Q8_0 quantizer above) as kv->type gives it. */
+ * format (fp16 rounding, the Q8_0 quantizer or the E4M3 rounding above) as
+ * kv->type gives it. */
 qkdec_status qkdec_kv_append(const qkdec_kv_layer* kv, const int32_t* slot, const int32_t* pos,
                              const float* k, const float* v, int32_t B, int32_t* err, void* stream);
 
@@ -196,7 +215,7 @@ qkdec_status qkdec_kv_append(const qkdec_kv_layer* kv, const int32_t* slot, cons
  * whole private cache each step, with query heads grouped onto KV heads.  P3
  * FAQ "Is KV cache quantization a kernel change or a storage change?": a
  * quantized cache is dequantized inside the fused attention kernel, never
- * expanded in memory first.  Split-K flash decoding: each work item covers a
+ * expanded in memory first (E4M3 codes convert to fp16 exactly).  Split-K flash decoding: each work item covers a
  * run of tokens of one (sequence, KV head) and the partial results are merged
  * with their log-sum-exp weights.
  *

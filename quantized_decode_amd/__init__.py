@@ -19,8 +19,10 @@ KV_F16 = 0
 KV_Q8_0 = 1
 KV_Q8_0_K_F16_V = 2     # Q8_0 keys, fp16 values
 KV_F16_K_Q8_0_V = 3     # fp16 keys, Q8_0 values
+KV_FP8_E4M3 = 4         # OCP E4M3 keys and values, one byte each, no scale
 # cache kinds by name (the oracle's names) and their key / value formats
-KV_KINDS = {"f16": KV_F16, "q8_0": KV_Q8_0, "q8k_f16v": KV_Q8_0_K_F16_V, "f16k_q8v": KV_F16_K_Q8_0_V}
+KV_KINDS = {"f16": KV_F16, "q8_0": KV_Q8_0, "q8k_f16v": KV_Q8_0_K_F16_V, "f16k_q8v": KV_F16_K_Q8_0_V,
+            "fp8": KV_FP8_E4M3}
 
 STATUS_NAMES = {0: "QKDEC_OK", -1: "QKDEC_E_ARG", -2: "QKDEC_E_SHAPE", -3: "QKDEC_E_ALIGN",
                 -4: "QKDEC_E_WORKSPACE", -5: "QKDEC_E_CAPACITY", -6: "QKDEC_E_UNSUPPORTED", -7: "QKDEC_E_HIP"}

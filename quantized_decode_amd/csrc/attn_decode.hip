@@ -1,4 +1,5 @@
-// Split-K flash-decode GQA attention over a slot-arena KV cache, fp16 or Q8_0.
+// Split-K flash-decode GQA attention over a slot-arena KV cache: fp16, Q8_0,
+// mixed, or E4M3 keys and values.
 // (P1, P2, P3: the three pages listed, with their titles, at the top of include/qkdec.h.)
 //
 // P2 "The two halves of a decode-step memory bill": each sequence reads its
@@ -29,6 +30,9 @@
 // (from the tile's largest value scale) keeping the pair clear of fp16
 // subnormals.  int8 -> fp16 is exact (byte permute into the
 // mantissa of 1024+128+x, then one packed subtract).
+//
+// E4M3 (no scale): each pair of codes becomes two fp16 values in one hardware
+// conversion (exact), after which keys and values take the fp16 path.
 #include "attn_dev.h"
 #include "common.h"
 #include "internal.h"
@@ -39,7 +43,7 @@ constexpr int kAttnWaves = 4;
 
 // Two waves per SIMD: with the split key / value prefetch the fp16 kernel
 // fits 256 registers without spilling (see the run targets next to kAttnChunk)
-template <int D, bool KQ8, bool VQ8>
+template <int D, int KF, int VF>
 __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs a) {
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = a.Hq / a.n_kv;
@@ -60,13 +64,13 @@ __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs
     const half_t* qrow = a.Q + ((size_t)b * a.Hq + g * G + (hv ? r : 0)) * D;
 #pragma unroll
     for (int j = 0; j < D / 32; ++j) {
-      const int d0 = KQ8 ? (32 * j + 8 * lg) : ((D / 4) * lg + 8 * j);
+      const int d0 = KF == kFmtQ8 ? (32 * j + 8 * lg) : ((D / 4) * lg + 8 * j);
       qf[j] = hv ? *reinterpret_cast<const half8_t*>(qrow + d0) : half8_t{0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
   const size_t head_row0 = ((size_t)s * a.n_kv + g) * a.cap;
 
-  AttnState<D, VQ8> st;
+  AttnState<D, VF == kFmtQ8> st;
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) st.o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
   st.m = -__builtin_inff();
@@ -78,7 +82,7 @@ __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs
   // softmax is done (two tiles of keys and values are never held at once)
   const int ntiles = (t_end - t_begin + 31) / 32;
   if (wave < ntiles) {
-    KVFrag<D, KQ8, VQ8> buf[2];
+    KVFrag<D, KF, VF> buf[2];
     load_k(buf[0], a, head_row0, t_begin + 32 * wave, lg, r);
     load_v(buf[0], a, head_row0, t_begin + 32 * wave, lg, r);
     for (int it = wave; it < ntiles; it += 2 * kAttnWaves) {
@@ -99,7 +103,7 @@ __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs
   // undo the operand scaling of the value products (exact powers of two)
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) {
-    const float un = VQ8 ? exp2i(-st.ex) : exp2i(-kPScale);
+    const float un = VF == kFmtQ8 ? exp2i(-st.ex) : exp2i(-kPScale);
     st.o[i][0] *= un; st.o[i][1] *= un; st.o[i][2] *= un; st.o[i][3] *= un;
   }
   // merge the four waves' states (same lane layout in every wave) in LDS;
@@ -211,7 +215,7 @@ hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, con
   a.Hq = n_q_heads;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.n_splits = attn_max_runs(kv.capacity, kv.n_kv_heads);
-  a.runs_wanted = attn_runs_wanted(B, kv.n_kv_heads, kv.type != QKDEC_KV_F16);
+  a.runs_wanted = attn_runs_wanted(B, kv.n_kv_heads, kv_k_q8(kv.type) || kv_v_q8(kv.type));
   const int D = kv.head_dim;
   const size_t n_rows = (size_t)B * n_q_heads * a.n_splits;
   a.part_o = partials;
@@ -220,15 +224,19 @@ hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, con
   const int max_runs = attn_runs(kv.capacity, a.runs_wanted, a.n_splits);
   const dim3 grid(max_runs, kv.n_kv_heads, B);
   const dim3 blk(64 * kAttnWaves);
-#define QK_ATTN(DD, KQ, VQ) hipLaunchKernelGGL((attn_split_kernel<DD, KQ, VQ>), grid, blk, 0, st, a)
-  const bool kq8 = kv_k_q8(kv.type), vq8 = kv_v_q8(kv.type);
-  if (D == 128) {
-    if (kq8) { if (vq8) QK_ATTN(128, true, true); else QK_ATTN(128, true, false); }
-    else { if (vq8) QK_ATTN(128, false, true); else QK_ATTN(128, false, false); }
-  } else {
-    if (kq8) { if (vq8) QK_ATTN(64, true, true); else QK_ATTN(64, true, false); }
-    else { if (vq8) QK_ATTN(64, false, true); else QK_ATTN(64, false, false); }
-  }
+#define QK_ATTN(DD, KF, VF) hipLaunchKernelGGL((attn_split_kernel<DD, KF, VF>), grid, blk, 0, st, a)
+#define QK_ATTN_D(DD)                                                          \
+  do {                                                                         \
+    if (kf == kFmtF8) QK_ATTN(DD, kFmtF8, kFmtF8);                             \
+    else if (kf == kFmtQ8 && vf == kFmtQ8) QK_ATTN(DD, kFmtQ8, kFmtQ8);        \
+    else if (kf == kFmtQ8) QK_ATTN(DD, kFmtQ8, kFmtF16);                       \
+    else if (vf == kFmtQ8) QK_ATTN(DD, kFmtF16, kFmtQ8);                       \
+    else QK_ATTN(DD, kFmtF16, kFmtF16);                                        \
+  } while (0)
+  const int kf = kv_k_fmt(kv.type), vf = kv_v_fmt(kv.type);
+  if (D == 128) QK_ATTN_D(128);
+  else QK_ATTN_D(64);
+#undef QK_ATTN_D
 #undef QK_ATTN
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

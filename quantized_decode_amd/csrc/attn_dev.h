@@ -1,4 +1,4 @@
-// Device code of the flash-decode attention: KV tile loads (fp16 or Q8_0),
+// Device code of the flash-decode attention: KV tile loads (fp16, Q8_0 or E4M3),
 // the online softmax state and one 32-token tile on MFMA (described at the
 // top of attn_decode.hip).
 #pragma once
@@ -33,32 +33,53 @@ __device__ __forceinline__ half8_t i8x8_to_h8(uint32_t w0, uint32_t w1) {
   return r;
 }
 
+// E4M3 x 8 (two dwords, byte i = element i) -> fp16 x 8: exact (every E4M3
+// value is an fp16 normal or zero), one conversion per two codes
+__device__ __forceinline__ half8_t f8x8_to_h8(uint32_t w0, uint32_t w1) {
+  const half2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+  const half2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+  const half2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+  const half2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+  half8_t r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
 // One 32-token tile of keys and values held by a lane; keys and values each
-// in their own cache format.
-template <int D, bool Q8>
+// in their own cache format (kFmtF16, kFmtQ8, kFmtF8).
+template <int D, int F>
 struct KPart;
 template <int D>
-struct KPart<D, false> {
+struct KPart<D, kFmtF16> {
   half8_t k[2][D / 32];
 };
 template <int D>
-struct KPart<D, true> {
+struct KPart<D, kFmtQ8> {
   uint32_t k[2][D / 32][2];
   uint32_t ks[D / 8];   // fp16 scales of tokens 8lg..8lg+7, D/32 blocks each (2 per dword)
 };
-template <int D, bool Q8>
+template <int D>
+struct KPart<D, kFmtF8> {
+  uint32_t k[2][D / 32][2];
+};
+template <int D, int F>
 struct VPart;
 template <int D>
-struct VPart<D, false> {
+struct VPart<D, kFmtF16> {
   half8_t v[D / 16];
 };
 template <int D>
-struct VPart<D, true> {
+struct VPart<D, kFmtQ8> {
   uint32_t v[D / 16][2];
   uint32_t vs[D / 8];
 };
-template <int D, bool KQ8, bool VQ8>
-struct KVFrag : KPart<D, KQ8>, VPart<D, VQ8> {};
+template <int D>
+struct VPart<D, kFmtF8> {
+  uint32_t v[D / 16][2];
+};
+template <int D, int KF, int VF>
+struct KVFrag : KPart<D, KF>, VPart<D, VF> {};
 
 struct AttnArgs {
   const uint8_t* k;
@@ -94,11 +115,28 @@ __host__ __device__ __forceinline__ int attn_runs(int n, int wanted, int max_run
 }
 
 // Keys (and their Q8_0 scales) of the 32-token tile at t0; head_row0 =
-// (slot * n_kv + g) * cap is the index of token 0 of this head.
-template <int D, bool Q8, bool VQ8>
-__device__ __forceinline__ void load_k(KVFrag<D, Q8, VQ8>& f, const AttnArgs& a, size_t head_row0, int t0, int lg,
+// (slot * n_kv + g) * cap is the index of token 0 of this head.  fp16 and
+// E4M3 lanes hold dims (D/4) lg + 8j .. +7 of their tokens, Q8_0 lanes dims
+// 32j + 8lg .. +7 (one MFMA per 32-dim block and scale).
+template <int D, int KF, int VF>
+__device__ __forceinline__ void load_k(KVFrag<D, KF, VF>& f, const AttnArgs& a, size_t head_row0, int t0, int lg,
                                        int m) {
-  if constexpr (!Q8) {
+  if constexpr (KF == kFmtF8) {
+    const uint8_t* kb = a.k + head_row0 * D;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int tok = t0 + 8 * (m >> 2) + 4 * hf + (m & 3);
+      const uint8_t* row = kb + (size_t)tok * D + (D / 4) * lg;
+#pragma unroll
+      for (int j2 = 0; j2 < D / 64; ++j2) {
+        const uint4 w = *reinterpret_cast<const uint4*>(row + 16 * j2);
+        f.k[hf][2 * j2][0] = w.x;
+        f.k[hf][2 * j2][1] = w.y;
+        f.k[hf][2 * j2 + 1][0] = w.z;
+        f.k[hf][2 * j2 + 1][1] = w.w;
+      }
+    }
+  } else if constexpr (KF == kFmtF16) {
     const half_t* kb = reinterpret_cast<const half_t*>(a.k) + head_row0 * D;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
@@ -133,10 +171,18 @@ __device__ __forceinline__ void load_k(KVFrag<D, Q8, VQ8>& f, const AttnArgs& a,
 // Values (and their Q8_0 scales) of the same tile, from the value cache
 // transposed within 32-token blocks ([cap/32][D][32] per head: the tile at t0
 // is one contiguous run; lane (lg, m) reads tokens 8lg..8lg+7 of dim 16i + m).
-template <int D, bool KQ8, bool Q8>
-__device__ __forceinline__ void load_v(KVFrag<D, KQ8, Q8>& f, const AttnArgs& a, size_t head_row0, int t0, int lg,
+template <int D, int KF, int VF>
+__device__ __forceinline__ void load_v(KVFrag<D, KF, VF>& f, const AttnArgs& a, size_t head_row0, int t0, int lg,
                                        int m) {
-  if constexpr (!Q8) {
+  if constexpr (VF == kFmtF8) {
+    const uint8_t* vb = a.v + head_row0 * D;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      const uint2 w = *reinterpret_cast<const uint2*>(vb + ((size_t)(t0 >> 5) * D + 16 * i + m) * 32 + 8 * lg);
+      f.v[i][0] = w.x;
+      f.v[i][1] = w.y;
+    }
+  } else if constexpr (VF == kFmtF16) {
     const half_t* vb = reinterpret_cast<const half_t*>(a.v) + head_row0 * D;  // [D][cap] of this head
 #pragma unroll
     for (int i = 0; i < D / 16; ++i)
@@ -184,17 +230,21 @@ constexpr int kPScale = 14;
 // are done, before the value products (the caller issues the next tile's
 // value loads there, into registers this tile's keys no longer need).  The
 // fp16 values of out-of-range tokens are zeroed in place in f.
-template <int D, bool KQ8, bool VQ8, typename Mid>
-__device__ __forceinline__ void attn_tile(AttnState<D, VQ8>& st, KVFrag<D, KQ8, VQ8>& f, const half8_t (&qf)[D / 32],
-                                          float scale_log2, int valid, int lg, const Mid& mid) {
+template <int D, int KF, int VF, typename Mid>
+__device__ __forceinline__ void attn_tile(AttnState<D, VF == kFmtQ8>& st, KVFrag<D, KF, VF>& f,
+                                          const half8_t (&qf)[D / 32], float scale_log2, int valid, int lg,
+                                          const Mid& mid) {
   // valid = number of tokens of this 32-token tile that are in range (1..32)
   float sc[8];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (!KQ8) {
+    if constexpr (KF == kFmtF16) {
 #pragma unroll
       for (int j = 0; j < D / 32; ++j) acc = mfma16x16x32(f.k[hf][j], qf[j], acc);
+    } else if constexpr (KF == kFmtF8) {
+#pragma unroll
+      for (int j = 0; j < D / 32; ++j) acc = mfma16x16x32(f8x8_to_h8(f.k[hf][j][0], f.k[hf][j][1]), qf[j], acc);
     } else {
 #pragma unroll
       for (int j = 0; j < D / 32; ++j) {
@@ -234,7 +284,28 @@ __device__ __forceinline__ void attn_tile(AttnState<D, VQ8>& st, KVFrag<D, KQ8, 
   __builtin_amdgcn_sched_barrier(0);
   mid();
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (!VQ8) {
+  if constexpr (VF == kFmtF8) {
+    half8_t phi, plo;
+    const float ps = exp2i(kPScale);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float pe = p[e] * ps;
+      const half_t h = (half_t)pe;
+      phi[e] = h;
+      plo[e] = (half_t)(pe - (float)h);
+    }
+    const int lim = valid - 8 * lg;   // codes past the end may be NaN codes: never reach the MFMA
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      half8_t vf = f8x8_to_h8(f.v[i][0], f.v[i][1]);
+      if (valid < 32) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vf[e] = e < lim ? vf[e] : (half_t)0.f;
+      }
+      st.o[i] = mfma16x16x32(vf, phi, st.o[i]);
+      st.o[i] = mfma16x16x32(vf, plo, st.o[i]);
+    }
+  } else if constexpr (VF == kFmtF16) {
     half8_t phi, plo;
     const float ps = exp2i(kPScale);
 #pragma unroll

@@ -31,6 +31,9 @@ __device__ __forceinline__ half2_t pack_h2(float lo, float hi) {
 }
 
 // 2^k as a float, k clamped to the normal range
+// storage format of one cache tensor (keys or values)
+enum : int { kFmtF16 = 0, kFmtQ8 = 1, kFmtF8 = 2 };
+
 __device__ __forceinline__ float exp2i(int k) {
   k = k < -126 ? -126 : (k > 127 ? 127 : k);
   return __builtin_bit_cast(float, (uint32_t)(k + 127) << 23);

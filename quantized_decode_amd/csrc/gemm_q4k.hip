@@ -380,7 +380,7 @@ __device__ void gemm_item(const GemmArgs& a, int rg, int c, int n_chunks, half_t
       const int kvh = is_v ? head - ra.Hq - n_kv : head - ra.Hq;
       CacheRef c;
       c.k = ra.k; c.v = ra.v; c.ks = ra.ks; c.vs = ra.vs;
-      c.n_kv = n_kv; c.cap = ra.cap; c.D = D; c.n_slots = ra.n_slots; c.kq8 = ra.kq8; c.vq8 = ra.vq8;
+      c.n_kv = n_kv; c.cap = ra.cap; c.D = D; c.n_slots = ra.n_slots; c.kf = ra.kf; c.vf = ra.vf;
       int sl[4], ps[4];
       bool ok[4];
 #pragma unroll
@@ -391,10 +391,10 @@ __device__ void gemm_item(const GemmArgs& a, int rg, int c, int n_chunks, half_t
         ok[ii] = b < B && sl[ii] >= 0 && sl[ii] < ra.n_slots && ps[ii] >= 0 && ps[ii] < ra.cap;
         if (b < B && !ok[ii] && wave == 0 && r == 0) *ra.err = QKDEC_E_CAPACITY;
       }
-      if (!(is_v ? ra.vq8 : ra.kq8)) {   // uniform: one head per work-group
+      if ((is_v ? ra.vf : ra.kf) != kFmtQ8) {   // uniform: one head per work-group
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
-          if (ok[ii]) store_f16(c, is_v, sl[ii], kvh, ps[ii], d, out[ii]);
+          if (ok[ii]) store_point(c, is_v, sl[ii], kvh, ps[ii], d, out[ii]);
       } else {
         // a Q8_0 block is 32 dims: the 16 lanes of this wave's row group and
         // the same lanes of the partner wave w ^ 1

@@ -352,14 +352,14 @@ __device__ void qkv_finish(const WkArgs& a, Red red, int wave, int lane, int g, 
   }
   CacheRef c;
   c.k = ra.k; c.v = ra.v; c.ks = ra.ks; c.vs = ra.vs;
-  c.n_kv = ra.n_kv; c.cap = ra.cap; c.D = D; c.n_slots = ra.n_slots; c.kq8 = false; c.vq8 = false;
+  c.n_kv = ra.n_kv; c.cap = ra.cap; c.D = D; c.n_slots = ra.n_slots; c.kf = ra.kf; c.vf = ra.vf;
   const int kvh = is_v ? head - ra.Hq - ra.n_kv : head - ra.Hq;
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii) {
     const int b = 4 * g + ii;
     if (b >= a.B) continue;
     const bool ok = sl[ii] >= 0 && sl[ii] < ra.n_slots && ps[ii] >= 0 && ps[ii] < ra.cap;
-    if (ok) store_f16(c, is_v, sl[ii], kvh, ps[ii], d, out[ii]);
+    if (ok) store_point(c, is_v, sl[ii], kvh, ps[ii], d, out[ii]);
     else if (r == 0) *ra.err = QKDEC_E_CAPACITY;
   }
 }
@@ -910,12 +910,14 @@ hipError_t launch_gemm_wi(const GemmLaunch& L, hipStream_t st) {
   return hipGetLastError();
 }
 
-// The QKV projection of a decode step with its RoPE / fp16-append finish:
-// K = 4096, RMSNorm fused, fp16 cache, head_dim 64 or 128; one work-group per
+// The QKV projection of a decode step with its RoPE / append finish: K =
+// 4096, RMSNorm fused, fp16 or E4M3 cache (element-wise stores), head_dim 64
+// or 128; one work-group per
 // (head, half-head tile).  hipErrorNotSupported for any other case.
 hipError_t launch_gemm_wi_qkv(const GemmLaunch& L, const RopeAppendArgs& ra, int head_dim, hipStream_t st) {
   const int kb = (int)(L.K / 256);
-  if (kb != 16 || !L.x_f32 || !L.gamma || ra.kq8 || ra.vq8 || (head_dim != 64 && head_dim != 128) || L.residual ||
+  if (kb != 16 || !L.x_f32 || !L.gamma || ra.kf == kFmtQ8 || ra.vf == kFmtQ8 || (head_dim != 64 && head_dim != 128) ||
+      L.residual ||
       L.ss_out)
     return hipErrorNotSupported;
   WkArgs a{};

@@ -53,7 +53,7 @@ struct RopeAppendArgs {
   uint8_t *k, *v;        // cache of this layer (fp16 or Q8_0 codes)
   uint16_t *ks, *vs;     // Q8_0 block scales
   int n_kv, cap, n_slots, Hq;
-  bool kq8, vq8;          // Q8_0 keys / values (else fp16)
+  int kf, vf;             // key / value format (kFmtF16, kFmtQ8, kFmtF8)
   float rope_base;
   uint16_t* q16;         // rotated queries, fp16 bits
   int32_t* err;          // set to QKDEC_E_CAPACITY for a position outside the cache
@@ -70,8 +70,9 @@ hipError_t launch_gemm_wk(const GemmLaunch& L, hipStream_t st);
 // Several output items per work-group (gemm_wk.hip), for the shapes it covers;
 // returns hipErrorNotSupported for any other.
 hipError_t launch_gemm_wi(const GemmLaunch& L, hipStream_t st);
-// The decode step's QKV projection with its RoPE and fp16-append finish on the
-// multi-item kernel (K = 4096, fp16 cache); hipErrorNotSupported otherwise.
+// The decode step's QKV projection with its RoPE and append finish on the
+// multi-item kernel (K = 4096, fp16 or E4M3 cache); hipErrorNotSupported
+// otherwise.
 hipError_t launch_gemm_wi_qkv(const GemmLaunch& L, const RopeAppendArgs& ra, int head_dim, hipStream_t st);
 hipError_t launch_gemm_q4k_xf32(const void* W, int64_t N, int64_t K, const float* X, int64_t ldx, int B,
                                 float* Y, int64_t ldy, const float* residual, int64_t ldr, void* ws, hipStream_t st,
@@ -86,9 +87,17 @@ hipError_t launch_dequant_q4k(const void* W, int64_t n_blocks, float* out, hipSt
 constexpr int kGemmMaxGroups = 16384;
 constexpr int64_t kGemmMaxRows = 16 * 4 * (int64_t)kGemmMaxGroups;
 
-// ---- cache formats: Q8_0 keys / values of a cache type (else fp16)
-inline bool kv_k_q8(int type) { return type == QKDEC_KV_Q8_0 || type == QKDEC_KV_Q8_0_K_F16_V; }
-inline bool kv_v_q8(int type) { return type == QKDEC_KV_Q8_0 || type == QKDEC_KV_F16_K_Q8_0_V; }
+// ---- cache formats: the key / value format of a cache type
+inline int kv_k_fmt(int type) {
+  return type == QKDEC_KV_FP8_E4M3 ? kFmtF8
+         : (type == QKDEC_KV_Q8_0 || type == QKDEC_KV_Q8_0_K_F16_V) ? kFmtQ8 : kFmtF16;
+}
+inline int kv_v_fmt(int type) {
+  return type == QKDEC_KV_FP8_E4M3 ? kFmtF8
+         : (type == QKDEC_KV_Q8_0 || type == QKDEC_KV_F16_K_Q8_0_V) ? kFmtQ8 : kFmtF16;
+}
+inline bool kv_k_q8(int type) { return kv_k_fmt(type) == kFmtQ8; }
+inline bool kv_v_q8(int type) { return kv_v_fmt(type) == kFmtQ8; }
 
 // ---- attention (attn_decode.hip)
 // A sequence's n cached tokens (ceil(n/32) tiles of 32) are cut into runs of

@@ -1,4 +1,4 @@
-// KV-cache append (fp16 / Q8_0).  Within a decode step the append (with the
+// KV-cache append (fp16 / Q8_0 / E4M3).  Within a decode step the append (with the
 // rotary embedding of k) is done by the QKV projection's finishing work-group
 // (gemm_q4k.hip, MODE 2) with the same store helpers (kv_dev.h).
 // (P1, P2, P3: the three pages listed, with their titles, at the top of include/qkdec.h.)
@@ -9,6 +9,10 @@
 // d = RN_fp16(amax / 127), q = x / d rounded half away from zero, clamped to
 // [-127, 127], q = 0 where d = 0.  A thread owns one or two dims; the block
 // amax is a max-reduction over the 32 lanes holding one block.
+//
+// P2 "What a long-running swarm should actually tune": an 8-bit float cache
+// (read here as OCP E4M3, unscaled) stores each value as its nearest code,
+// ties to even, saturating at +-448 (f8_code in kv_dev.h); no reduction.
 #include "common.h"
 #include "internal.h"
 #include "kv_dev.h"

@@ -1,6 +1,7 @@
 // Device code of the KV-cache store shared by the append kernels and the QKV
-// projection's finishing step: fp16 rounding or the Q8_0 quantizer of one
-// 32-value block (the arithmetic is described at the top of kv_append.hip).
+// projection's finishing step: fp16 rounding, the Q8_0 quantizer of one
+// 32-value block or the E4M3 rounding (the arithmetic is described at the top
+// of kv_append.hip).
 #pragma once
 
 #include "common.h"
@@ -30,7 +31,7 @@ struct CacheRef {
   uint16_t* ks;
   uint16_t* vs;
   int n_kv, cap, D, n_slots;
-  bool kq8, vq8;   // Q8_0 keys / values (else fp16)
+  int kf, vf;   // key / value format (kFmtF16, kFmtQ8, kFmtF8)
 };
 
 // Element stores of dim d of (slot s, kv head g, position p), into K
@@ -58,6 +59,32 @@ __device__ __forceinline__ void store_q8(const CacheRef& c, bool is_v, int s, in
   }
 }
 
+// OCP E4M3 code of x: nearest (ties to even), magnitudes above 448 to +-448,
+// NaN to 0x7F (sign kept).  In binade e = floor(log2 |x|) >= -6 the step is
+// 2^(e-3) and below 2^-6 the subnormal step 2^-9; |x| * 2^(3-e) is exact and
+// rintf rounds it to even, and a result of 16 carries into the exponent
+// field (the next binade's first code).
+__device__ __forceinline__ uint8_t f8_code(float x) {
+  const uint32_t sign = (__builtin_bit_cast(uint32_t, x) >> 24) & 0x80u;
+  if (x != x) return (uint8_t)(sign | 0x7Fu);
+  const float a = fminf(fabsf(x), 448.f);
+  int e = (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 255u) - 127;
+  e = e < -6 ? -6 : e;
+  const int q = (int)rintf(a * exp2i(3 - e));
+  return (uint8_t)(sign | (uint32_t)(((e + 7) << 3) + q - 8));
+}
+__device__ __forceinline__ void store_f8(const CacheRef& c, bool is_v, int s, int g, int p, int d, float x) {
+  const size_t head = (size_t)s * c.n_kv + g;
+  const uint8_t q = f8_code(x);
+  if (!is_v) c.k[(head * c.cap + p) * c.D + d] = q;
+  else c.v[v_index(c, head, p, d)] = q;
+}
+// Element-wise formats (fp16, E4M3): one value, no block reduction.
+__device__ __forceinline__ void store_point(const CacheRef& c, bool is_v, int s, int g, int p, int d, float x) {
+  if ((is_v ? c.vf : c.kf) == kFmtF8) store_f8(c, is_v, s, g, p, d, x);
+  else store_f16(c, is_v, s, g, p, d, x);
+}
+
 // One Q8_0 block value: code of x for the block maximum amax (both fp64).
 __device__ __forceinline__ void q8_encode(double x, double amax, int8_t& q, uint16_t& dbits) {
   dbits = f64_to_f16_bits(amax / 127.0);
@@ -68,8 +95,8 @@ __device__ __forceinline__ void q8_encode(double x, double amax, int8_t& q, uint
 // For Q8_0 all 32 lanes of the dim's block must call this together.
 __device__ __forceinline__ void store_elem(const CacheRef& c, bool is_v, int s, int g, int p, int d, float x,
                                            bool ok) {
-  if (!(is_v ? c.vq8 : c.kq8)) {
-    if (ok) store_f16(c, is_v, s, g, p, d, x);
+  if ((is_v ? c.vf : c.kf) != kFmtQ8) {
+    if (ok) store_point(c, is_v, s, g, p, d, x);
   } else {
     const double xd = (double)x;
     int8_t q;
@@ -99,8 +126,10 @@ __device__ __forceinline__ CacheRef cache_ref(const qkdec_kv_layer& kv) {
   c.cap = kv.capacity;
   c.D = kv.head_dim;
   c.n_slots = kv.n_slots;
-  c.kq8 = kv.type == QKDEC_KV_Q8_0 || kv.type == QKDEC_KV_Q8_0_K_F16_V;
-  c.vq8 = kv.type == QKDEC_KV_Q8_0 || kv.type == QKDEC_KV_F16_K_Q8_0_V;
+  c.kf = kv.type == QKDEC_KV_FP8_E4M3 ? kFmtF8
+         : (kv.type == QKDEC_KV_Q8_0 || kv.type == QKDEC_KV_Q8_0_K_F16_V) ? kFmtQ8 : kFmtF16;
+  c.vf = kv.type == QKDEC_KV_FP8_E4M3 ? kFmtF8
+         : (kv.type == QKDEC_KV_Q8_0 || kv.type == QKDEC_KV_F16_K_Q8_0_V) ? kFmtQ8 : kFmtF16;
   return c;
 }
 

@@ -42,7 +42,7 @@ qkdec_status check_gemm(const void* W, int64_t N, int64_t K, const uint16_t* X, 
 
 qkdec_status check_kv(const qkdec_kv_layer* kv) {
   if (!kv) return QKDEC_E_ARG;
-  if (kv->type < QKDEC_KV_F16 || kv->type > QKDEC_KV_F16_K_Q8_0_V) return QKDEC_E_ARG;
+  if (kv->type < QKDEC_KV_F16 || kv->type > QKDEC_KV_FP8_E4M3) return QKDEC_E_ARG;
   if (!kv->k || !kv->v) return QKDEC_E_ARG;
   if (kv->head_dim != 64 && kv->head_dim != 128) return QKDEC_E_SHAPE;
   if (kv->n_kv_heads < 1 || kv->n_slots < 1 || kv->capacity < 32 || kv->capacity % 32 != 0) return QKDEC_E_SHAPE;
@@ -164,9 +164,9 @@ qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int3
     ra.k = reinterpret_cast<uint8_t*>(kv[l].k); ra.v = reinterpret_cast<uint8_t*>(kv[l].v);
     ra.ks = reinterpret_cast<uint16_t*>(kv[l].k_scale); ra.vs = reinterpret_cast<uint16_t*>(kv[l].v_scale);
     ra.n_kv = kv[l].n_kv_heads; ra.cap = kv[l].capacity; ra.n_slots = kv[l].n_slots; ra.Hq = Hq;
-    ra.kq8 = kv_k_q8(kv[l].type); ra.vq8 = kv_v_q8(kv[l].type); ra.rope_base = m->rope_base; ra.q16 = w.q16; ra.err = w.err;
+    ra.kf = kv_k_fmt(kv[l].type); ra.vf = kv_v_fmt(kv[l].type); ra.rope_base = m->rope_base; ra.q16 = w.q16; ra.err = w.err;
     // K = 4096: the resident multi-item projection, finishing each head slice
-    // itself (fp16 cache) or followed by RoPE and the append as a small launch
+    // itself (fp16 or E4M3 cache) or followed by RoPE and the append as a small launch
     // (Q8_0 blocks span two work-groups); otherwise the split-K projection
     // finishes each head
     hipError_t eq = launch_gemm_wi_qkv(qkv, ra, D, st);

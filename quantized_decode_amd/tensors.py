@@ -11,7 +11,7 @@ from typing import Optional
 
 import numpy as np
 
-from . import KV_F16, KV_F16_K_Q8_0_V, KV_Q8_0, KV_Q8_0_K_F16_V, KVLayer, kv_layer
+from . import KV_F16, KV_F16_K_Q8_0_V, KV_FP8_E4M3, KV_Q8_0, KV_Q8_0_K_F16_V, KVLayer, kv_layer
 
 
 def dev(a: np.ndarray):
@@ -66,12 +66,16 @@ class DeviceKV:
         self.v[slot, :, t0:] = value
 
     def logical(self):
-        """The cache as a logical object with the fields of its formats: k or
-        (kq, ks), v or (vq, vs), numpy [slots, kv, cap, D] (v transposed back)."""
+        """The cache as a logical object with the fields of its formats: k,
+        (kq, ks) or kf8, v, (vq, vs) or vf8, numpy [slots, kv, cap, D] (v
+        transposed back)."""
         from types import SimpleNamespace
         k = self.k.cpu().numpy()
         v = v_from_blocked(self.v.cpu().numpy())
         out = SimpleNamespace()
+        if self.kind == KV_FP8_E4M3:
+            out.kf8, out.vf8 = k, v
+            return out
         if self.k_scale is None:
             out.k = k
         else:
@@ -105,9 +109,19 @@ def upload_kv_q8(kq: np.ndarray, ks: np.ndarray, vq: np.ndarray, vs: np.ndarray)
     return DeviceKV(KV_Q8_0, kd, vd, ksd, vsd, kv_layer(KV_Q8_0, nkv, d, cap, slots, kd, vd, ksd, vsd))
 
 
+def upload_kv_fp8(kf8: np.ndarray, vf8: np.ndarray) -> DeviceKV:
+    """kf8, vf8: uint8 E4M3 codes [slots, kv, cap, D] (logical)."""
+    slots, nkv, cap, d = kf8.shape
+    kd = dev(np.asarray(kf8, dtype=np.uint8))
+    vd = dev(v_to_blocked(np.asarray(vf8, dtype=np.uint8)))
+    return DeviceKV(KV_FP8_E4M3, kd, vd, None, None, kv_layer(KV_FP8_E4M3, nkv, d, cap, slots, kd, vd))
+
+
 def upload_cache(c) -> DeviceKV:
-    """A logical cache object with k or (kq, ks) for the keys and v or (vq, vs)
-    for the values; fields of the other format absent or None."""
+    """A logical cache object with k, (kq, ks) or kf8 for the keys and v,
+    (vq, vs) or vf8 for the values; fields of the other formats absent or None."""
+    if getattr(c, "kf8", None) is not None:
+        return upload_kv_fp8(c.kf8, c.vf8)
     kq8 = getattr(c, "kq", None) is not None
     vq8 = getattr(c, "vq", None) is not None
     if kq8 and vq8:

@@ -95,7 +95,12 @@ def test_kv_and_attention_validation(lib):
     assert gen(ctypes.byref(_kv(type=2, v_scale=FAKE)), FAKE, FAKE, FAKE, FAKE, 1, None, None) == -1   # k_scale
     assert gen(ctypes.byref(_kv(type=3, k_scale=FAKE)), FAKE, FAKE, FAKE, FAKE, 1, None, None) == -1   # v_scale
     assert gen(ctypes.byref(_kv(type=2, k_scale=FAKE + 2)), FAKE, FAKE, FAKE, FAKE, 1, None, None) == -3
-    assert gen(ctypes.byref(_kv(type=4)), FAKE, FAKE, FAKE, FAKE, 1, None, None) == -1
+    assert gen(ctypes.byref(_kv(type=5)), FAKE, FAKE, FAKE, FAKE, 1, None, None) == -1
+    # E4M3 keys and values: no scales; only the generic entry point takes the type
+    assert gen(ctypes.byref(_kv(type=4)), FAKE, FAKE, FAKE, FAKE, 17, None, None) == -2
+    assert gen(ctypes.byref(_kv(type=4, v=FAKE + 4)), FAKE, FAKE, FAKE, FAKE, 1, None, None) == -3
+    assert app(ctypes.byref(_kv(type=4)), FAKE, FAKE, FAKE, FAKE, 1, None, None) == -1
+    assert q8(ctypes.byref(_kv(type=4)), FAKE, FAKE, FAKE, FAKE, 1, None, None) == -1
     assert gen(ctypes.byref(_kv(type=2, k_scale=FAKE)), FAKE, FAKE, FAKE, FAKE, 17, None, None) == -2
     assert app(ctypes.byref(_kv(type=2, k_scale=FAKE)), FAKE, FAKE, FAKE, FAKE, 1, None, None) == -1
     assert q8(ctypes.byref(_kv(type=3, v_scale=FAKE)), FAKE, FAKE, FAKE, FAKE, 1, None, None) == -1

@@ -1,4 +1,4 @@
-"""Split-K flash-decode attention (fp16 and Q8_0 caches) on the GPU against the oracle."""
+"""Split-K flash-decode attention (fp16, Q8_0, mixed and E4M3 caches) on the GPU against the oracle."""
 import math
 
 import numpy as np
@@ -32,6 +32,10 @@ def _run(qd, cache, kind, q, slots, n_ctx, scale, poison=False):
         kfmt, vfmt = synth.KV_FORMATS[kind]
         for s in range(dkv.desc.n_slots):
             used = max(int(n) for b, n in enumerate(n_ctx) if slots[b] == s) if s in list(slots) else 0
+            if kfmt == "fp8":   # the E4M3 NaN codes
+                dkv.k[s, :, used:] = 0x7F
+                dkv.set_v_from(s, used, 0xFF)
+                continue
             if kfmt == "f16":
                 dkv.k[s, :, used:] = float("nan")
             else:
@@ -75,6 +79,13 @@ CASES = [
     ("f16k_q8v", 8, 2, 64, 256, [129, 256]),
     ("f16k_q8v", 32, 8, 128, 512, [1, 100, 128, 129, 300, 512]),
     ("f16k_q8v", 32, 4, 128, 288, [200, 288]),
+    ("fp8", 8, 2, 64, 256, [1, 31]),
+    ("fp8", 8, 2, 64, 256, [32, 33]),
+    ("fp8", 8, 2, 64, 256, [129, 256]),
+    ("fp8", 32, 8, 128, 512, [1, 100, 128, 129, 300, 512]),
+    ("fp8", 16, 1, 128, 384, [383, 257, 5]),
+    ("fp8", 16, 16, 64, 160, [160, 65]),
+    ("fp8", 32, 4, 128, 288, [200, 288]),
 ]
 
 
@@ -95,7 +106,7 @@ def test_attention_small(qd, kind, hq, hkv, d, cap, n_ctx):
     assert np.array_equal(o16, o.astype(np.float16))
 
 
-@pytest.mark.parametrize("kind", ["f16", "q8_0", "q8k_f16v", "f16k_q8v"])
+@pytest.mark.parametrize("kind", ["f16", "q8_0", "q8k_f16v", "f16k_q8v", "fp8"])
 def test_attention_full_config(qd, kind):
     # 32 query heads on 8 KV heads of 128, B = 8 sequences of 2400 tokens, one layer
     bsz, hq, hkv, d, L = 8, 32, 8, 128, 2400
@@ -162,3 +173,22 @@ def test_attention_workspace_reused_across_calls(qd):
         ref = OS.attention_batch(q[live].astype(np.float64), cache, "f16", live, [lens[b] for b in live],
                                  1 / math.sqrt(d))
         assert_rel(got[live], ref, what=f"lengths {lens}")
+
+
+def test_attention_fp8_value_decode_exact(qd):
+    # one cached token: the softmax weight is exactly 1, so O is the decoded
+    # value row itself; the rows hold every finite E4M3 code (the two NaN codes
+    # replaced by +-448), so the hardware conversion is checked code by code
+    from oracle import formats as OF
+    hq, hkv, d, cap = 4, 2, 128, 64
+    cache = synth.kv_cache_fp8(np.random.default_rng(5), np.random.default_rng(6), 1, hkv, cap, d, [1])
+    codes = np.arange(256, dtype=np.uint8)
+    codes[0x7F], codes[0xFF] = 0x7E, 0xFE
+    cache.vf8[0, :, 0, :] = codes.reshape(hkv, d)
+    q = synth.f16_normal(np.random.default_rng(7), (1, hq, d))
+    o, o16 = _run(qd, cache, "fp8", q, [0], [1], 1 / math.sqrt(d), poison=True)
+    want = OF.fp8_e4m3_decode(codes).reshape(hkv, d)
+    for h in range(hq):
+        g = h // (hq // hkv)
+        assert np.array_equal(o[0, h].astype(np.float64), want[g]), h
+        assert np.array_equal(o16[0, h].astype(np.float64), want[g]), h

@@ -85,10 +85,10 @@ def test_append_q8_0_bit_exact(qd, d, nkv):
     assert int(err.cpu()[0]) == 0
 
 
-@pytest.mark.parametrize("kind", ["q8k_f16v", "f16k_q8v"])
+@pytest.mark.parametrize("kind", ["q8k_f16v", "f16k_q8v", "fp8"])
 def test_append_mixed_formats_bit_exact(qd, kind):
-    # keys and values in different formats through the generic entry point,
-    # each stored exactly as the oracle stores that format
+    # keys and values in different formats (or E4M3) through the generic entry
+    # point, each stored exactly as the oracle stores that format
     import copy
 
     from oracle import step as OS
@@ -102,6 +102,9 @@ def test_append_mixed_formats_bit_exact(qd, kind):
     pos = np.array([63, 0, 17], np.int32)
     k = (rng.standard_normal((bsz, nkv, d)) * 10.0 ** rng.integers(-6, 3, (bsz, nkv, 1))).astype(np.float32)
     v = (rng.standard_normal((bsz, nkv, d)) * 20).astype(np.float32)
+    if kind == "fp8":   # ties (to even), subnormal ties, saturation, signed zeros
+        k[0, 0, :10] = [1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10, 15 * 2.0 ** -10, 1.9375, 464.0, -1e9, 0.0, -0.0]
+        v[1, 2, :4] = [448.0, -449.0, 2.0 ** -9, -(2.0 ** -12)]
     err = _dev(np.zeros(1, np.int32))
     qd.qkdec_kv_append(dkv.desc, _dev(slot), _dev(pos), _dev(k), _dev(v), bsz, err=err)
     sync()
@@ -109,7 +112,7 @@ def test_append_mixed_formats_bit_exact(qd, kind):
     want = copy.deepcopy(cache)
     for b in range(bsz):
         OS.kv_append(want, kind, int(slot[b]), int(pos[b]), k[b].astype(np.float64), v[b].astype(np.float64))
-    for name in ("k", "kq", "ks", "v", "vq", "vs"):
+    for name in ("k", "kq", "ks", "v", "vq", "vs", "kf8", "vf8"):
         w = getattr(want, name, None)
         if w is None:
             continue

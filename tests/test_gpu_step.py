@@ -74,7 +74,7 @@ def compare_logits(lg, ref, gtok, what):
     return d
 
 
-@pytest.mark.parametrize("kind", ["f16", "q8_0", "q8k_f16v", "f16k_q8v"])
+@pytest.mark.parametrize("kind", ["f16", "q8_0", "q8k_f16v", "f16k_q8v", "fp8"])
 def test_toy_step_multi_step(qd, kind):
     # the toy workload: 2-layer decoder, B = 2 sequences with 128 cached tokens
     dims = synth.TOY
@@ -218,6 +218,16 @@ def check_layer_stages(dims, kind, ly, x_in, pos, vw, cache_dev, cache_before, s
                 _within_f16_ulp(getattr(got, name)[s, :, p], want, f"appended {name}, sequence {b}")
                 assert np.array_equal(getattr(got, name)[s, :, :p].view(np.uint16),
                                       getattr(cache_before, name)[s, :, :p].view(np.uint16))
+            elif fmt == "fp8":
+                # the GPU rounds its fp32 value, the oracle the fp64 one: a code
+                # may differ only by one E4M3 step, at a near-tie
+                gc = getattr(got, name + "f8")
+                dg = OF.fp8_e4m3_decode(gc[s, :, p])
+                do = OF.fp8_e4m3_decode(OF.fp8_e4m3_encode(want))
+                e = np.maximum(np.floor(np.log2(np.maximum(np.abs(do), 2.0 ** -6))), -6)
+                assert (np.abs(dg - do) <= 2.0 ** (e - 3) * 1.0001).all(), f"appended {name}, sequence {b}"
+                assert np.mean(dg != do) < 0.01, f"appended {name}, sequence {b}"
+                assert np.array_equal(gc[s, :, :p], getattr(cache_before, name + "f8")[s, :, :p])
             else:
                 gq, gs = getattr(got, name + "q"), getattr(got, name + "s")
                 wq, wd = OF.q8_0_quantize(want)
@@ -249,7 +259,7 @@ def check_layer_stages(dims, kind, ly, x_in, pos, vw, cache_dev, cache_before, s
     assert_rel(vw.x, x1 + OO.q4k_gemm(ly.w_down, dims.hidden, dims.ffn, a16), what="residual after the layer")
 
 
-@pytest.mark.parametrize("kind", ["f16", "q8_0", "q8k_f16v"])
+@pytest.mark.parametrize("kind", ["f16", "q8_0", "q8k_f16v", "fp8"])
 def test_full_width_step_stagewise(qd, kind):
     # the Qwen-shaped model (hidden 4096, 32/8 heads of 128, FFN 12288, vocab 151936), first two
     # layers, B = 8 sequences at L = 2400.  With random Q4_K bytes the weights have a
