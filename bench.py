@@ -15,6 +15,16 @@ the 8-bit float (E4M3) cache at L = 2400 and 6900; B = 1 at L = 2400; B = 16 at
 L = 3400 (fp16 and Q8_0); Q8_0 at L = 8192 and 19000.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py --sweep [--sweep-kv f16,q8_0,fp8] [--sweep-batches 1,2,4,8,16]
+                    [--sweep-contexts 32,2400,4700,6900,16000,32000]
+
+--sweep measures the step over batch sizes x contexts x cache kinds instead
+(one JSON line per point, then a summary line): the measured speedup of B
+sequences over one at the same context, next to the byte model's prediction
+(P2 "Where the private read overtakes the shared one"), the bandwidth-bound
+ceiling at the box's measured read rate (P3 "What the sagging ceiling costs in
+tokens per second") and the context per sequence the 0.85-of-memory budget
+holds on this GPU (P1 "Where it stops, and the argument I got wrong in May").
 
 Prints one JSON line.  value = aggregate decode tokens/s = B * K / time of the
 K timed replays (mean); per-replay p10/p50/p90 are in "points".  "roofline" is
@@ -300,6 +310,62 @@ def cpu_baseline(dims, dev_model, batch, length, seed, min_seconds=10.0):
             "sample_seconds": elapsed, "host_cpus": os.cpu_count()}
 
 
+def sweep(args, qd, sd, dims, dev_model):
+    """Step time over batch x context x cache kind (graph replays, inputs
+    resident), with the planner's predictions beside each point."""
+    import torch
+    from quantized_decode_amd import planner as P
+    kinds = args.sweep_kv.split(",")
+    batches = [int(x) for x in args.sweep_batches.split(",")]
+    contexts = [int(x) for x in args.sweep_contexts.split(",")]
+    vram = torch.cuda.get_device_properties(0).total_memory
+    log("streaming-read ceiling (4 GiB)")
+    ceiling = read_ceiling()
+    bw = ceiling["GBps"] * 1e9
+    rows = []
+    i = 0
+    for kind in kinds:
+        k = P.kv_bytes_per_token(dims.n_layers, dims.n_kv_heads, dims.head_dim, kind)
+        plan = P.plan_capacity(vram, W_BYTES, k)
+        for L in contexts:
+            one = None
+            for bsz in batches:
+                i += 1
+                cap = P.slot_capacity(L, args.warmup + args.steps + 2)
+                if not plan.fits([cap] * bsz):
+                    log(f"B={bsz} L={L} kv={kind}: over the 0.85 budget, skipped")
+                    continue
+                sm = build_point(qd, sd, dims, dev_model, bsz, L, kind, cap, 6000 + i)
+                torch.cuda.synchronize()
+                per, _ = time_point(qd, sm, bsz, L, args.steps, args.warmup, dims.vocab, 7000 + i)
+                del sm
+                torch.cuda.empty_cache()
+                ms = sum(per) / len(per)
+                tps = bsz / (ms * 1e-3)
+                if bsz == 1:
+                    one = tps
+                l_mean = L + args.warmup + (args.steps - 1) / 2
+                by = P.step_bytes(W_BYTES, [l_mean] * bsz, k)
+                row = {"kv": kind, "batch": bsz, "context": L, "ms_per_step": ms, "tok_per_s": tps,
+                       "bytes_per_step": by, "achieved_GBps": by / (ms * 1e-3) / 1e9,
+                       "frac_of_8TBps": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                       "speedup_vs_b1": tps / one if one else None,
+                       "speedup_model": P.speedup(bsz, l_mean, W_BYTES, k),
+                       "ceiling_tok_s_at_read_rate": P.ceiling_tok_s(bw, W_BYTES, bsz, l_mean, k),
+                       "kv_traffic_bytes": P.kv_traffic_bytes([l_mean] * bsz, k),
+                       "context_per_seq_at_085": plan.context_per_sequence(bsz)}
+                rows.append(row)
+                print(json.dumps(row), flush=True)
+                log(f"B={bsz} L={L} kv={kind}: {ms:.3f} ms, {tps:.1f} tok/s, speedup "
+                    f"{row['speedup_vs_b1'] or 0:.2f} (model {row['speedup_model']:.2f})")
+    summary = {"sweep": "decode step, Qwen-shaped synthetic decoder, Q4_K weights", "steps": args.steps,
+               "warmup": args.warmup, "vram_bytes": vram, "weight_bytes": W_BYTES, "read_ceiling": ceiling,
+               "crossover_b8": {kind: P.crossover_context(W_BYTES, 8, P.kv_bytes_per_token(
+                   dims.n_layers, dims.n_kv_heads, dims.head_dim, kind)) for kind in kinds},
+               "points": len(rows)}
+    print(json.dumps(summary), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -312,6 +378,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-clocks", action="store_true",
                     help="do not query rocm-smi (for runs under a profiler, whose preload the child would inherit)")
+    ap.add_argument("--sweep", action="store_true", help="context x batch x cache sweep (see above)")
+    ap.add_argument("--sweep-kv", default="f16,q8_0,fp8")
+    ap.add_argument("--sweep-batches", default="1,2,4,8,16")
+    ap.add_argument("--sweep-contexts", default="32,2400,4700,6900,16000,32000")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run 3 plain device copies of this many MiB (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -340,6 +410,9 @@ def main():
     log("drawing the synthetic model on the GPU")
     dev_model = sd.model(dims, 1003)
     torch.cuda.synchronize()
+    if args.sweep:
+        sweep(args, qd, sd, dims, dev_model)
+        return
 
     points = [(args.batch, args.context, args.kv)]
     if args.points == "all":
