@@ -62,11 +62,15 @@ KV_BYTES_PER_TOKEN = {"f16": NL * HKV * D * 2 * 2, "q8_0": NL * HKV * D * 2 * 34
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs (calibrated
 # against a plain 1 GiB copy: fetched = 2.0 x FETCH_SIZE, written = 1.0 x
 # WRITE_SIZE), keyed by the kernels as they were when counted; see
-# profiles/decode_step_b8_l2400_f16_kernel_stats.md.  A kernel changed since
+# profiles/decode_step_b8_l2400_f16_kernel_stats.md and
+# profiles/decode_step_b8_l6900_fp8_kernel_stats.md.  A kernel changed since
 # has no entry, and its traffic is reported as null.
 COUNTED_TRAFFIC = {
-    # split kernel 79,172,864 fetched + 555,342 written; merge 606,188 + 65,536
-    ("attention (split + merge)", 8, 2400, "f16"): 79_172_864 + 555_342 + 606_188 + 65_536,
+    # split kernel 79,179,991 fetched + 555,342 written; merge 617,480 + 65,536
+    # (fetched and written each rounded once over split + merge)
+    ("attention (split + merge)", 8, 2400, "f16"): 80_418_348,
+    # E4M3 cache: split 113,884,031 fetched + 974,848 written; merge 1,010,663 + 65,536
+    ("attention (split + merge)", 8, 6900, "fp8"): 115_935_078,
 }
 
 
