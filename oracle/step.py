@@ -90,6 +90,43 @@ def attention_batch(q: np.ndarray, cache, kind: str, slots, n_ctx, scale: float)
     return out
 
 
+# ---- paged cache (P1 "Where it stops, and the argument I got wrong in May":
+# sequences of very different lengths share one pool of fixed-size pages,
+# admitted and released between decode steps).  A pool is a cache object of
+# the layout above whose "slots" are pages of page_tokens positions each;
+# sequence b's token t lives in page pages[b][t // page_tokens] at offset
+# t % page_tokens.
+
+
+def kv_read_paged(pool, kind: str, pages, page_tokens: int, n: int):
+    """Keys and values of the first n tokens of a paged sequence, fp64 [n_kv, n, D]."""
+    if n <= 0:
+        k0, v0 = kv_read(pool, kind, 0, 0)
+        return k0, v0
+    ks, vs = [], []
+    for i in range((n + page_tokens - 1) // page_tokens):
+        take = min(page_tokens, n - i * page_tokens)
+        kd, vd = kv_read(pool, kind, int(pages[i]), take)
+        ks.append(kd)
+        vs.append(vd)
+    return np.concatenate(ks, axis=1), np.concatenate(vs, axis=1)
+
+
+def kv_append_paged(pool, kind: str, pages, page_tokens: int, pos: int, k: np.ndarray, v: np.ndarray) -> None:
+    """kv_append of one token at logical position pos of a paged sequence."""
+    kv_append(pool, kind, int(pages[pos // page_tokens]), pos % page_tokens, k, v)
+
+
+def attention_batch_paged(q: np.ndarray, pool, kind: str, page_table, page_tokens: int, n_ctx,
+                          scale: float) -> np.ndarray:
+    """attention_batch over paged sequences: page_table[b] lists sequence b's pages in order."""
+    out = np.empty(q.shape, dtype=np.float64)
+    for b in range(q.shape[0]):
+        kd, vd = kv_read_paged(pool, kind, page_table[b], page_tokens, int(n_ctx[b]))
+        out[b] = attention(q[b], kd, vd, scale)
+    return out
+
+
 def decode_step(model, caches, kind: str, slots, pos, tok, n_layers=None):
     """Advance every sequence by one token.
 

@@ -302,3 +302,38 @@ def test_mixed_cache_formats_route_each_tensor(kind, kfrom, vfrom):
         assert np.array_equal(vm, S.kv_read(pure[vfrom], vfrom, slot, pos + 1)[1])
     with pytest.raises(ValueError):
         S.kv_read(mixed, "q4_0", 0, 1)
+
+
+@pytest.mark.parametrize("kind", ["f16", "q8_0", "fp8", "q8k_f16v"])
+def test_paged_read_is_the_contiguous_cache_split_into_pages(kind):
+    # a slot of capacity C cut into pages of P tokens, the pages scattered over
+    # a shuffled pool: every paged read, append and attention equals the
+    # contiguous one exactly
+    st = synth.Streams(7300)
+    n_slots, n_kv, cap, hd, P = 2, 2, 128, 64, 32
+    cont = synth.kv_cache(kind, st.next(), st.next(), n_slots, n_kv, cap, hd, [100, 128])
+    npp = cap // P
+    perm = st.next().permutation(n_slots * npp)          # logical page j of slot s -> physical perm[s*npp+j]
+    pool = copy.deepcopy(cont)
+    for name, arr in vars(cont).items():
+        if arr is None:
+            continue
+        pages = arr.reshape((n_slots, n_kv, npp, P) + arr.shape[3:]).transpose(0, 2, 1, 3, 4)
+        pages = pages.reshape((n_slots * npp, n_kv, P) + arr.shape[3:])
+        phys = np.empty_like(pages)
+        phys[perm] = pages
+        setattr(pool, name, phys)
+    table = [perm[s * npp:(s + 1) * npp] for s in range(n_slots)]
+    rng = st.next()
+    for s, n in ((0, 100), (1, 128), (0, 1), (1, 33)):
+        kc, vc = S.kv_read(cont, kind, s, n)
+        kp, vp = S.kv_read_paged(pool, kind, table[s], P, n)
+        assert np.array_equal(kc, kp) and np.array_equal(vc, vp)
+    k = rng.standard_normal((n_kv, hd)) * 2
+    v = rng.standard_normal((n_kv, hd))
+    S.kv_append(cont, kind, 0, 100, k, v)
+    S.kv_append_paged(pool, kind, table[0], P, 100, k, v)
+    q = rng.standard_normal((2, 4, hd))
+    a = S.attention_batch(q, cont, kind, [0, 1], [101, 77], 0.125)
+    b = S.attention_batch_paged(q, pool, kind, table, P, [101, 77], 0.125)
+    assert np.array_equal(a, b)
