@@ -232,6 +232,33 @@ qkdec_status qkdec_attn_decode(const qkdec_kv_layer* kv, const int32_t* slot, co
                                float* O, uint16_t* O16, void* workspace, size_t ws_bytes,
                                void* stream);
 
+/* ------------------------------------------------------------ paged KV ---
+ * P1 "Where it stops, and the argument I got wrong in May": sequences of very
+ * different lengths share one pool of fixed-size pages (admitted and released
+ * between steps).  A pool is a qkdec_kv_layer whose slots are pages:
+ * n_slots = number of pages, capacity = tokens per page (a power of two,
+ * >= 32), any cache type, the layouts above per page.  pages: device int32
+ * [B][max_pages]; token t of sequence b is in page pages[b * max_pages +
+ * t / capacity] at position t % capacity.  max_pages * capacity <= 2^30.
+ * Page entries a call reads must lie in [0, n_slots); an entry outside is
+ * clamped into the pool (no fault; that sequence's result is then
+ * meaningless).  Two sequences must not write the same page in one call.
+ *
+ * Attention: as qkdec_attn_decode, with n_ctx[b] clamped to max_pages *
+ * capacity; workspace of at least qkdec_attn_paged_workspace_size() bytes. */
+size_t qkdec_attn_paged_workspace_size(int32_t B, int32_t n_q_heads, const qkdec_kv_layer* kv, int32_t max_pages);
+qkdec_status qkdec_attn_decode_paged(const qkdec_kv_layer* kv, const int32_t* pages, int32_t max_pages,
+                                     const int32_t* n_ctx, int32_t B, const uint16_t* Q, int32_t n_q_heads,
+                                     float scale, float* O, uint16_t* O16, void* workspace, size_t ws_bytes,
+                                     void* stream);
+/* Append: as qkdec_kv_append (each tensor in its format), token pos[b] of
+ * sequence b into its page; a pos[b] outside [0, max_pages * capacity) or a
+ * page entry outside the pool stores nothing for b and sets *err to
+ * QKDEC_E_CAPACITY. */
+qkdec_status qkdec_kv_append_paged(const qkdec_kv_layer* kv, const int32_t* pages, int32_t max_pages,
+                                   const int32_t* pos, const float* k, const float* v, int32_t B, int32_t* err,
+                                   void* stream);
+
 /* -------------------------------------------------------------- LM head ---
  * logits[b][v] = sum_k Wlm[v][k] * X[b][k];  tok[b] = argmax_v logits[b][v]
  * (lowest v on ties).  P1 "The weight read is the only term that does not

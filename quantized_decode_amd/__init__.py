@@ -77,6 +77,10 @@ _SIGNATURES = {
     "qkdec_kv_append": (_I32, [ctypes.POINTER(KVLayer), _P, _P, _P, _P, _I32, _P, _P]),
     "qkdec_attn_workspace_size": (_SZ, [_I32, _I32, ctypes.POINTER(KVLayer)]),
     "qkdec_attn_decode": (_I32, [ctypes.POINTER(KVLayer), _P, _P, _I32, _P, _I32, _F, _P, _P, _P, _SZ, _P]),
+    "qkdec_attn_paged_workspace_size": (_SZ, [_I32, _I32, ctypes.POINTER(KVLayer), _I32]),
+    "qkdec_attn_decode_paged": (_I32, [ctypes.POINTER(KVLayer), _P, _I32, _P, _I32, _P, _I32, _F, _P, _P, _P, _SZ,
+                                       _P]),
+    "qkdec_kv_append_paged": (_I32, [ctypes.POINTER(KVLayer), _P, _I32, _P, _P, _P, _I32, _P, _P]),
     "qkdec_lm_head_workspace_size": (_SZ, [_I64, _I32]),
     "qkdec_lm_head_argmax": (_I32, [_P, _I64, _I64, _P, _I32, _P, _P, _P, _SZ, _P]),
     "qkdec_step_workspace_size": (_SZ, [ctypes.POINTER(Model), _I32, ctypes.POINTER(KVLayer)]),
@@ -198,6 +202,23 @@ def qkdec_attn_decode(kv: KVLayer, slot, n_ctx, b: int, q, n_q_heads: int, scale
     _check(load_library().qkdec_attn_decode(ctypes.byref(kv), _ptr(slot), _ptr(n_ctx), b, _ptr(q), n_q_heads,
                                             scale, _ptr(o), _ptr(o16), _ptr(workspace), ws_bytes,
                                             _stream(stream)), "qkdec_attn_decode")
+
+
+def qkdec_attn_paged_workspace_size(b: int, n_q_heads: int, kv: KVLayer, max_pages: int) -> int:
+    return load_library().qkdec_attn_paged_workspace_size(b, n_q_heads, ctypes.byref(kv), max_pages)
+
+
+def qkdec_attn_decode_paged(kv: KVLayer, pages, max_pages: int, n_ctx, b: int, q, n_q_heads: int, scale: float,
+                            o=None, o16=None, workspace=None, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load_library().qkdec_attn_decode_paged(ctypes.byref(kv), _ptr(pages), max_pages, _ptr(n_ctx), b, _ptr(q),
+                                                  n_q_heads, scale, _ptr(o), _ptr(o16), _ptr(workspace), ws_bytes,
+                                                  _stream(stream)), "qkdec_attn_decode_paged")
+
+
+def qkdec_kv_append_paged(kv: KVLayer, pages, max_pages: int, pos, k, v, b: int, err=None, stream=None) -> None:
+    _check(load_library().qkdec_kv_append_paged(ctypes.byref(kv), _ptr(pages), max_pages, _ptr(pos), _ptr(k), _ptr(v),
+                                                b, _ptr(err), _stream(stream)), "qkdec_kv_append_paged")
 
 
 def qkdec_lm_head_workspace_size(vocab: int, b: int) -> int:

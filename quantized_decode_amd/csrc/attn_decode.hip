@@ -33,6 +33,11 @@
 //
 // E4M3 (no scale): each pair of codes becomes two fp16 values in one hardware
 // conversion (exact), after which keys and values take the fp16 path.
+//
+// Paged pool (PAGED): the cache layer's slots are fixed-size pages and each
+// 32-token tile's page comes from the sequence's row of the page table (one
+// uniform load per tile, before the tile's key loads); everything else is the
+// arena kernel.
 #include "attn_dev.h"
 #include "common.h"
 #include "internal.h"
@@ -43,14 +48,14 @@ constexpr int kAttnWaves = 4;
 
 // Two waves per SIMD: with the split key / value prefetch the fp16 kernel
 // fits 256 registers without spilling (see the run targets next to kAttnChunk)
-template <int D, int KF, int VF>
+template <int D, int KF, int VF, bool PAGED>
 __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs a) {
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = a.Hq / a.n_kv;
-  const int s = a.slot[b];
+  const int s = PAGED ? 0 : a.slot[b];
   int n = a.n_ctx[b] + a.n_ctx_add;
-  if (n > a.cap) n = a.cap;
-  if (n < 0 || s < 0 || s >= a.n_slots) n = 0;
+  if (n > a.seq_cap) n = a.seq_cap;
+  if (n < 0 || (!PAGED && (s < 0 || s >= a.n_slots))) n = 0;
   const int runs = attn_runs(n, a.runs_wanted, a.n_splits);
   if (c >= runs) return;
   const int tiles = (n + 31) / 32;
@@ -69,6 +74,18 @@ __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs
     }
   }
   const size_t head_row0 = ((size_t)s * a.n_kv + g) * a.cap;
+  // (row of token 0 of this head, position within it) of the tile at t
+  auto tile_at = [&](int t, size_t& row0, int& tt) {
+    if constexpr (PAGED) {
+      int pg = a.pages[(size_t)b * a.max_pages + (t >> a.page_shift)];
+      pg = pg < 0 ? 0 : (pg >= a.n_slots ? a.n_slots - 1 : pg);   // never outside the pool
+      row0 = ((size_t)pg * a.n_kv + g) * a.cap;
+      tt = t & (a.cap - 1);
+    } else {
+      row0 = head_row0;
+      tt = t;
+    }
+  };
 
   AttnState<D, VF == kFmtQ8> st;
 #pragma unroll
@@ -83,18 +100,22 @@ __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs
   const int ntiles = (t_end - t_begin + 31) / 32;
   if (wave < ntiles) {
     KVFrag<D, KF, VF> buf[2];
-    load_k(buf[0], a, head_row0, t_begin + 32 * wave, lg, r);
-    load_v(buf[0], a, head_row0, t_begin + 32 * wave, lg, r);
+    size_t row0;
+    int tt;
+    tile_at(t_begin + 32 * wave, row0, tt);
+    load_k(buf[0], a, row0, tt, lg, r);
+    load_v(buf[0], a, row0, tt, lg, r);
     for (int it = wave; it < ntiles; it += 2 * kAttnWaves) {
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         const int i = it + p * kAttnWaves;
         if (i < ntiles) {
           const int nx = (i + kAttnWaves < ntiles) ? i + kAttnWaves : i;
-          load_k(buf[p ^ 1], a, head_row0, t_begin + 32 * nx, lg, r);
+          tile_at(t_begin + 32 * nx, row0, tt);
+          load_k(buf[p ^ 1], a, row0, tt, lg, r);
           const int t0 = t_begin + 32 * i;
           attn_tile(st, buf[p], qf, a.scale_log2, min(32, t_end - t0), lg,
-                    [&]() { load_v(buf[p ^ 1], a, head_row0, t_begin + 32 * nx, lg, r); });
+                    [&]() { load_v(buf[p ^ 1], a, row0, tt, lg, r); });
         }
       }
     }
@@ -160,9 +181,9 @@ __global__ void attn_combine_kernel(const float* __restrict__ part_o, const floa
                                     int n_ctx_add, int cap, int n_slots, int Hq, int D, float* O, half_t* O16) {
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   int n = n_ctx[b] + n_ctx_add;
-  if (n > cap) n = cap;
-  const int s = slot[b];
-  if (n < 0 || s < 0 || s >= n_slots) n = 0;
+  if (n > cap) n = cap;               // cap: the most tokens a sequence holds
+  const int s = slot ? slot[b] : 0;   // no slot for a paged pool
+  if (n < 0 || (slot && (s < 0 || s >= n_slots))) n = 0;
   const int ns = attn_runs(n, runs_wanted, n_splits);
   const size_t row0 = ((size_t)b * Hq + h) * n_splits;
   float num = 0.f, den = 0.f, big = -__builtin_inff();
@@ -199,7 +220,7 @@ __global__ void attn_combine_kernel(const float* __restrict__ part_o, const floa
 
 hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, const int32_t* n_ctx, int B,
                               const uint16_t* Q, int n_q_heads, float scale, float* O, uint16_t* O16,
-                              float* partials, int n_ctx_add, hipStream_t st) {
+                              float* partials, int n_ctx_add, hipStream_t st, const int32_t* pages, int max_pages) {
   AttnArgs a;
   a.k = reinterpret_cast<const uint8_t*>(kv.k);
   a.v = reinterpret_cast<const uint8_t*>(kv.v);
@@ -214,34 +235,44 @@ hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, con
   a.Q = reinterpret_cast<const half_t*>(Q);
   a.Hq = n_q_heads;
   a.scale_log2 = scale * 1.4426950408889634f;
-  a.n_splits = attn_max_runs(kv.capacity, kv.n_kv_heads);
+  a.pages = pages;
+  a.max_pages = pages ? max_pages : 0;
+  a.page_shift = 0;
+  while (pages && (1 << a.page_shift) < kv.capacity) ++a.page_shift;
+  a.seq_cap = attn_seq_cap(kv, pages ? max_pages : 0);
+  a.n_splits = attn_max_runs(a.seq_cap, kv.n_kv_heads);
   a.runs_wanted = attn_runs_wanted(B, kv.n_kv_heads, kv_k_q8(kv.type) || kv_v_q8(kv.type));
   const int D = kv.head_dim;
   const size_t n_rows = (size_t)B * n_q_heads * a.n_splits;
   a.part_o = partials;
   a.part_ml = partials + n_rows * D;
   // runs past a sequence's own count return at once
-  const int max_runs = attn_runs(kv.capacity, a.runs_wanted, a.n_splits);
+  const int max_runs = attn_runs(a.seq_cap, a.runs_wanted, a.n_splits);
   const dim3 grid(max_runs, kv.n_kv_heads, B);
   const dim3 blk(64 * kAttnWaves);
-#define QK_ATTN(DD, KF, VF) hipLaunchKernelGGL((attn_split_kernel<DD, KF, VF>), grid, blk, 0, st, a)
-#define QK_ATTN_D(DD)                                                          \
+#define QK_ATTN(DD, KF, VF, PG) hipLaunchKernelGGL((attn_split_kernel<DD, KF, VF, PG>), grid, blk, 0, st, a)
+#define QK_ATTN_D(DD, PG)                                                      \
   do {                                                                         \
-    if (kf == kFmtF8) QK_ATTN(DD, kFmtF8, kFmtF8);                             \
-    else if (kf == kFmtQ8 && vf == kFmtQ8) QK_ATTN(DD, kFmtQ8, kFmtQ8);        \
-    else if (kf == kFmtQ8) QK_ATTN(DD, kFmtQ8, kFmtF16);                       \
-    else if (vf == kFmtQ8) QK_ATTN(DD, kFmtF16, kFmtQ8);                       \
-    else QK_ATTN(DD, kFmtF16, kFmtF16);                                        \
+    if (kf == kFmtF8) QK_ATTN(DD, kFmtF8, kFmtF8, PG);                         \
+    else if (kf == kFmtQ8 && vf == kFmtQ8) QK_ATTN(DD, kFmtQ8, kFmtQ8, PG);    \
+    else if (kf == kFmtQ8) QK_ATTN(DD, kFmtQ8, kFmtF16, PG);                   \
+    else if (vf == kFmtQ8) QK_ATTN(DD, kFmtF16, kFmtQ8, PG);                   \
+    else QK_ATTN(DD, kFmtF16, kFmtF16, PG);                                    \
   } while (0)
   const int kf = kv_k_fmt(kv.type), vf = kv_v_fmt(kv.type);
-  if (D == 128) QK_ATTN_D(128);
-  else QK_ATTN_D(64);
+  if (pages) {
+    if (D == 128) QK_ATTN_D(128, true);
+    else QK_ATTN_D(64, true);
+  } else {
+    if (D == 128) QK_ATTN_D(128, false);
+    else QK_ATTN_D(64, false);
+  }
 #undef QK_ATTN_D
 #undef QK_ATTN
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(n_q_heads, B), dim3(D), 0, st, a.part_o, a.part_ml, a.n_splits,
-                     a.runs_wanted, slot, n_ctx, n_ctx_add, kv.capacity, kv.n_slots, n_q_heads, D, O,
+                     a.runs_wanted, pages ? nullptr : slot, n_ctx, n_ctx_add, a.seq_cap, kv.n_slots, n_q_heads, D, O,
                      reinterpret_cast<half_t*>(O16));
   return hipGetLastError();
 }

@@ -97,6 +97,11 @@ struct AttnArgs {
   float* part_ml;
   int n_splits;      // partial-result rows per (b, q head): the most runs a sequence can have
   int runs_wanted;   // runs per sequence this call aims at (see attn_runs)
+  // paged pool (slot = page, cap = page size, a power of two): token t of
+  // sequence b is in page pages[b * max_pages + (t >> page_shift)]
+  const int32_t* pages;
+  int max_pages, page_shift;
+  int seq_cap;       // most tokens a sequence can hold: cap, or max_pages * page size
 };
 
 // Runs of a sequence with n cached tokens (same in the split and merge

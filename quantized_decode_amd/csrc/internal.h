@@ -130,9 +130,17 @@ inline int attn_runs_wanted(int B, int n_kv, bool q8) {
 inline size_t attn_partials_bytes(int B, int n_q_heads, int head_dim, int capacity, int n_kv) {
   return (size_t)B * n_q_heads * attn_max_runs(capacity, n_kv) * (size_t)(head_dim + 2) * sizeof(float);
 }
+// most tokens one sequence can hold: the slot capacity, or for a paged pool
+// (max_pages > 0) max_pages pages of kv.capacity tokens
+inline int attn_seq_cap(const qkdec_kv_layer& kv, int max_pages) {
+  return max_pages > 0 ? max_pages * kv.capacity : kv.capacity;
+}
+// pages != NULL: kv is a pool of n_slots pages of capacity tokens (a power of
+// two) and sequence b's pages are pages[b * max_pages ...]; slot is unused
 hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, const int32_t* n_ctx, int B,
                               const uint16_t* Q, int n_q_heads, float scale, float* O, uint16_t* O16,
-                              float* partials, int n_ctx_add, hipStream_t st);
+                              float* partials, int n_ctx_add, hipStream_t st, const int32_t* pages = nullptr,
+                              int max_pages = 0);
 
 // ---- KV append and RoPE (kv_append.hip)
 // RoPE of q and k, q -> fp16 and the KV append, from the fp32 QKV rows Y
@@ -141,7 +149,8 @@ hipError_t launch_rope_append(const qkdec_kv_layer& kv, const float* Y, int64_t 
                               const int32_t* slot, const int32_t* pos, float rope_base, uint16_t* q16, int32_t* err,
                               hipStream_t st);
 hipError_t launch_kv_append(const qkdec_kv_layer& kv, const int32_t* slot, const int32_t* pos, const float* k,
-                            const float* v, int B, int32_t* err, hipStream_t st);
+                            const float* v, int B, int32_t* err, hipStream_t st, const int32_t* pages = nullptr,
+                            int max_pages = 0);
 
 
 // ---- small kernels (small.hip)

@@ -19,13 +19,25 @@
 
 namespace qk {
 
-// grid (n_kv, B), block D threads: thread d stores dim d of k and v.
+// grid (n_kv, B), block D threads: thread d stores dim d of k and v.  With a
+// page table (pages != NULL) the cache layer is a pool of pages of cap tokens
+// (a power of two, 2^page_shift) and position pos[b] of sequence b goes to
+// page pages[b * max_pages + pos / cap] at pos % cap.
 __global__ void kv_append_kernel(qkdec_kv_layer kv, const int32_t* slot, const int32_t* pos, const float* k,
-                                 const float* v, int32_t* err) {
+                                 const float* v, int32_t* err, const int32_t* pages, int max_pages, int page_shift) {
   const CacheRef c = cache_ref(kv);
   const int g = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  const int s = slot[b], p = pos[b];
-  const bool ok = s >= 0 && s < c.n_slots && p >= 0 && p < c.cap;
+  int s, p = pos[b];
+  bool ok;
+  if (pages) {
+    const bool in = p >= 0 && p < (max_pages << page_shift);
+    s = in ? pages[(size_t)b * max_pages + (p >> page_shift)] : -1;
+    p &= c.cap - 1;
+    ok = in && s >= 0 && s < c.n_slots;
+  } else {
+    s = slot[b];
+    ok = s >= 0 && s < c.n_slots && p >= 0 && p < c.cap;
+  }
   if (!ok && d == 0 && err) *err = QKDEC_E_CAPACITY;
   const size_t src = ((size_t)b * c.n_kv + g) * c.D + d;
   store_elem(c, false, s, g, p, d, k[src], ok);
@@ -75,8 +87,12 @@ hipError_t launch_rope_append(const qkdec_kv_layer& kv, const float* Y, int64_t 
 }
 
 hipError_t launch_kv_append(const qkdec_kv_layer& kv, const int32_t* slot, const int32_t* pos, const float* k,
-                            const float* v, int B, int32_t* err, hipStream_t st) {
-  hipLaunchKernelGGL(kv_append_kernel, dim3(kv.n_kv_heads, B), dim3(kv.head_dim), 0, st, kv, slot, pos, k, v, err);
+                            const float* v, int B, int32_t* err, hipStream_t st, const int32_t* pages,
+                            int max_pages) {
+  int shift = 0;
+  while (pages && (1 << shift) < kv.capacity) ++shift;
+  hipLaunchKernelGGL(kv_append_kernel, dim3(kv.n_kv_heads, B), dim3(kv.head_dim), 0, st, kv, slot, pos, k, v, err,
+                     pages, pages ? max_pages : 0, shift);
   return hipGetLastError();
 }
 

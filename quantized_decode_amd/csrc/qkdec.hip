@@ -346,6 +346,57 @@ qkdec_status qkdec_attn_decode(const qkdec_kv_layer* kv, const int32_t* slot, co
                                        reinterpret_cast<float*>(workspace), 0, as_stream(stream)));
 }
 
+// ---- paged pool: kv's slots are pages of kv->capacity tokens
+static qkdec_status check_pages(const qkdec_kv_layer* kv, const int32_t* pages, int32_t max_pages) {
+  if (!pages) return QKDEC_E_ARG;
+  if (kv->capacity & (kv->capacity - 1)) return QKDEC_E_SHAPE;          // page size: a power of two
+  if (max_pages < 1 || (int64_t)max_pages * kv->capacity > ((int64_t)1 << 30)) return QKDEC_E_SHAPE;
+  if (!aligned(pages, 4)) return QKDEC_E_ALIGN;
+  return QKDEC_OK;
+}
+
+size_t qkdec_attn_paged_workspace_size(int32_t B, int32_t n_q_heads, const qkdec_kv_layer* kv, int32_t max_pages) {
+  if (!kv || B < 1 || n_q_heads < 1 || kv->capacity < 1 || kv->head_dim < 1 || max_pages < 1 ||
+      (int64_t)max_pages * kv->capacity > ((int64_t)1 << 30))
+    return 0;
+  return attn_partials_bytes(B, n_q_heads, kv->head_dim, attn_seq_cap(*kv, max_pages), kv->n_kv_heads);
+}
+
+qkdec_status qkdec_attn_decode_paged(const qkdec_kv_layer* kv, const int32_t* pages, int32_t max_pages,
+                                     const int32_t* n_ctx, int32_t B, const uint16_t* Q, int32_t n_q_heads,
+                                     float scale, float* O, uint16_t* O16, void* workspace, size_t ws_bytes,
+                                     void* stream) {
+  qkdec_status s = check_kv(kv);
+  if (s != QKDEC_OK) return s;
+  s = check_pages(kv, pages, max_pages);
+  if (s != QKDEC_OK) return s;
+  if (!n_ctx || !Q || (!O && !O16)) return QKDEC_E_ARG;
+  if (B < 1 || B > 16) return QKDEC_E_SHAPE;
+  if (n_q_heads < 1 || n_q_heads % kv->n_kv_heads != 0 || n_q_heads / kv->n_kv_heads > 16) return QKDEC_E_SHAPE;
+  if (!(scale == scale)) return QKDEC_E_ARG;
+  if (!aligned(Q, 16) || (O && !aligned(O, 16))) return QKDEC_E_ALIGN;
+  const size_t need =
+      attn_partials_bytes(B, n_q_heads, kv->head_dim, attn_seq_cap(*kv, max_pages), kv->n_kv_heads);
+  if (!workspace || ws_bytes < need) return QKDEC_E_WORKSPACE;
+  if (!aligned(workspace, 16)) return QKDEC_E_ALIGN;
+  clear_stale_error();
+  return hip_status(launch_attn_decode(*kv, nullptr, n_ctx, B, Q, n_q_heads, scale, O, O16,
+                                       reinterpret_cast<float*>(workspace), 0, as_stream(stream), pages, max_pages));
+}
+
+qkdec_status qkdec_kv_append_paged(const qkdec_kv_layer* kv, const int32_t* pages, int32_t max_pages,
+                                   const int32_t* pos, const float* k, const float* v, int32_t B, int32_t* err,
+                                   void* stream) {
+  qkdec_status s = check_kv(kv);
+  if (s != QKDEC_OK) return s;
+  s = check_pages(kv, pages, max_pages);
+  if (s != QKDEC_OK) return s;
+  if (!pos || !k || !v) return QKDEC_E_ARG;
+  if (B < 1 || B > 16) return QKDEC_E_SHAPE;
+  clear_stale_error();
+  return hip_status(launch_kv_append(*kv, nullptr, pos, k, v, B, err, as_stream(stream), pages, max_pages));
+}
+
 size_t qkdec_lm_head_workspace_size(int64_t V, int32_t B) {
   if (V < 1 || B < 1) return 0;
   return lm_head_partials_bytes(V, B);

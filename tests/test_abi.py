@@ -156,3 +156,26 @@ def test_lm_head_and_step_validation(lib):
     assert lib.qkdec_plan_launch(None, None) == -1
     lib.qkdec_plan_destroy(None)
     assert lib.qkdec_workspace_init(None, 16, None) == -1
+
+
+def test_paged_validation(lib):
+    # page size a power of two, a page table, max_pages >= 1, sizes checked before any launch
+    att, app = lib.qkdec_attn_decode_paged, lib.qkdec_kv_append_paged
+    pool = _kv(capacity=256, n_slots=64)
+    need = lib.qkdec_attn_paged_workspace_size(8, 32, ctypes.byref(pool), 16)
+    # rows for up to max(ceil(16 * 256 / 1024), 512 / 8) = 64 runs per (sequence, head)
+    assert need == 8 * 32 * 64 * 130 * 4
+    assert lib.qkdec_attn_paged_workspace_size(8, 32, ctypes.byref(pool), 0) == 0
+    assert att(ctypes.byref(_kv(capacity=96)), FAKE, 4, FAKE, 8, FAKE, 32, 0.1, FAKE, None, FAKE, need, None) == -2
+    assert att(ctypes.byref(pool), None, 4, FAKE, 8, FAKE, 32, 0.1, FAKE, None, FAKE, need, None) == -1
+    assert att(ctypes.byref(pool), FAKE, 0, FAKE, 8, FAKE, 32, 0.1, FAKE, None, FAKE, need, None) == -2
+    assert att(ctypes.byref(pool), FAKE, 1 << 23, FAKE, 8, FAKE, 32, 0.1, FAKE, None, FAKE, need, None) == -2
+    assert att(ctypes.byref(pool), FAKE + 2, 16, FAKE, 8, FAKE, 32, 0.1, FAKE, None, FAKE, need, None) == -3
+    assert att(ctypes.byref(pool), FAKE, 16, FAKE, 17, FAKE, 32, 0.1, FAKE, None, FAKE, need, None) == -2
+    assert att(ctypes.byref(pool), FAKE, 16, FAKE, 8, FAKE, 30, 0.1, FAKE, None, FAKE, need, None) == -2
+    assert att(ctypes.byref(pool), FAKE, 16, FAKE, 8, FAKE, 32, 0.1, FAKE, None, FAKE, need - 4, None) == -4
+    assert att(ctypes.byref(pool), FAKE, 16, FAKE, 8, FAKE, 32, 0.1, None, None, FAKE, need, None) == -1
+    assert app(ctypes.byref(_kv(capacity=96)), FAKE, 4, FAKE, FAKE, FAKE, 1, None, None) == -2
+    assert app(ctypes.byref(pool), None, 4, FAKE, FAKE, FAKE, 1, None, None) == -1
+    assert app(ctypes.byref(pool), FAKE, 4, FAKE, FAKE, FAKE, 0, None, None) == -2
+    assert app(ctypes.byref(_kv(type=1, capacity=256)), FAKE, 4, FAKE, FAKE, FAKE, 1, None, None) == -1  # scales

@@ -1,0 +1,182 @@
+"""Paged KV pool on the GPU: attention and append against the oracle, and
+against the slot-arena path on the same data."""
+import copy
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import step as OS
+from quantized_decode_amd.pager import PagePool
+from tests.gpu_util import assert_rel, sync, ws
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def qd():
+    import quantized_decode_amd as m
+    m.load_library()
+    return m
+
+
+def _dev(a):
+    from quantized_decode_amd.tensors import dev
+    return dev(a)
+
+
+def _pool_from(cont, lengths, P, n_pages, rng):
+    """Copy each sequence's tokens of a contiguous cache (slot b = sequence b)
+    into pages handed out by a PagePool after some shuffling admissions; the
+    pages nobody holds, and every position past a sequence's length, are
+    poisoned (NaN or NaN codes)."""
+    n_pad = n_pages // 3
+    pool = PagePool(n_pages + n_pad, P)
+    # scatter the allocations: one-page dummies first, every other one released
+    # (n_pad // 2 stay held, so at least n_pages pages are free afterwards)
+    for j in range(n_pad):
+        pool.admit(("pad", j), int(rng.integers(1, P + 1)))
+    for j in range(0, n_pad, 2):
+        pool.release(("pad", j))
+    for b, n in enumerate(lengths):
+        pool.admit(b, n)
+    max_pages = max(len(pool.pages(b)) for b in range(len(lengths)))
+    table = pool.table(range(len(lengths)), max_pages)
+    out = copy.deepcopy(cont)
+    for name, arr in vars(cont).items():
+        if arr is None:
+            continue
+        if arr.dtype == np.float16:
+            poison = np.float16(np.nan)
+        elif arr.dtype == np.int8:
+            poison = 127
+        else:
+            poison = 0x7F
+        phys = np.full((pool.n_pages,) + arr.shape[1:2] + (P,) + arr.shape[3:], poison, dtype=arr.dtype)
+        for b, n in enumerate(lengths):
+            for j, pg in enumerate(pool.pages(b)):
+                take = max(0, min(P, n - j * P))
+                phys[pg, :, :take] = arr[b, :, j * P:j * P + take]
+        setattr(out, name, phys)
+    return out, table, pool
+
+
+def _attn_paged(qd, dkv, table, n_ctx, q, scale):
+    import torch
+    from quantized_decode_amd.tensors import dev
+    b, hq, d = q.shape
+    qt = dev(q.view(np.uint16)).view(torch.float16)
+    o = torch.empty((b, hq, d), dtype=torch.float32, device="cuda")
+    mp = table.shape[1]
+    w = ws(qd.qkdec_attn_paged_workspace_size(b, hq, dkv.desc, mp))
+    qd.qkdec_attn_decode_paged(dkv.desc, _dev(table), mp, _dev(np.asarray(n_ctx, np.int32)), b, qt, hq, scale, o=o,
+                               workspace=w)
+    sync()
+    return o.cpu().numpy()
+
+
+CASES = [
+    ("f16", 8, 2, 64, 32, [1, 31, 200]),
+    ("f16", 32, 8, 128, 64, [1000, 65, 128, 3]),
+    ("q8_0", 32, 8, 128, 256, [700, 1, 513]),
+    ("fp8", 32, 8, 128, 128, [300, 129, 1024]),
+    ("fp8", 8, 2, 64, 32, [33, 64, 5]),
+    ("q8k_f16v", 16, 4, 128, 64, [257, 90]),
+]
+
+
+@pytest.mark.parametrize("kind,hq,hkv,d,P,lens", CASES)
+def test_paged_attention_matches_oracle(qd, kind, hq, hkv, d, P, lens):
+    from quantized_decode_amd.tensors import upload_cache
+    st = synth.Streams(8100 + P + d + len(lens))
+    cap = max(lens) + P
+    cap = (cap + P - 1) // P * P
+    cont = synth.kv_cache(kind, st.next(), st.next(), len(lens), hkv, cap, d, lens)
+    rng = st.next()
+    n_pages = sum((n + P - 1) // P for n in lens) + 12
+    pool, table, _ = _pool_from(cont, lens, P, n_pages, rng)
+    dkv = upload_cache(pool)
+    q = synth.f16_normal(st.next(), (len(lens), hq, d))
+    scale = 1 / math.sqrt(d)
+    got = _attn_paged(qd, dkv, table, lens, q, scale)
+    ref = OS.attention_batch_paged(q.astype(np.float64), pool, kind, table, P, lens, scale)
+    assert_rel(got, ref, what=f"paged {kind} P={P} lens={lens}")
+
+
+@pytest.mark.parametrize("kind", ["f16", "q8_0", "fp8"])
+def test_paged_equals_arena_bitwise(qd, kind):
+    # the same tokens in a slot arena and scattered over a pool with
+    # max_pages * P = capacity: the same runs, tiles and arithmetic
+    import torch
+    from quantized_decode_amd.tensors import dev, upload_cache
+    st = synth.Streams(8200 + len(kind))
+    hq, hkv, d, P, lens = 32, 8, 128, 128, [900, 17, 1024, 385]
+    cap = 1024
+    cont = synth.kv_cache(kind, st.next(), st.next(), len(lens), hkv, cap, d, lens)
+    pool, table, _ = _pool_from(cont, lens, P, 40, st.next())
+    table = np.pad(table, ((0, 0), (0, cap // P - table.shape[1])))
+    q = synth.f16_normal(st.next(), (len(lens), hq, d))
+    got_p = _attn_paged(qd, upload_cache(pool), table, lens, q, 0.088)
+    dkv = upload_cache(cont)
+    qt = dev(q.view(np.uint16)).view(torch.float16)
+    o = torch.empty((len(lens), hq, d), dtype=torch.float32, device="cuda")
+    w = ws(qd.qkdec_attn_workspace_size(len(lens), hq, dkv.desc))
+    qd.qkdec_attn_decode(dkv.desc, _dev(np.arange(len(lens), dtype=np.int32)), _dev(np.asarray(lens, np.int32)),
+                         len(lens), qt, hq, 0.088, o=o, workspace=w)
+    sync()
+    assert np.array_equal(got_p.view(np.uint32), o.cpu().numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("kind", ["f16", "q8_0", "fp8"])
+def test_paged_append_bit_exact(qd, kind):
+    from quantized_decode_amd.tensors import upload_cache
+    st = synth.Streams(8300 + len(kind))
+    hkv, d, P, lens = 8, 128, 64, [100, 64, 5]
+    cont = synth.kv_cache(kind, st.next(), st.next(), len(lens), hkv, 256, d, lens)
+    pool, _, pager = _pool_from(cont, lens, P, 20, st.next())
+    for b, n in enumerate(lens):
+        pager.reserve(b, n + 1)                     # room for the new token
+    table = pager.table(range(len(lens)), 3)
+    dkv = upload_cache(pool)
+    rng = st.next()
+    k = (rng.standard_normal((3, hkv, d)) * 3).astype(np.float32)
+    v = rng.standard_normal((3, hkv, d)).astype(np.float32)
+    pos = np.array(lens, np.int32)
+    err = _dev(np.zeros(1, np.int32))
+    qd.qkdec_kv_append_paged(dkv.desc, _dev(table), 3, _dev(pos), _dev(k), _dev(v), 3, err=err)
+    sync()
+    got = dkv.logical()
+    want = copy.deepcopy(pool)
+    for b in range(3):
+        OS.kv_append_paged(want, kind, table[b], P, int(pos[b]), k[b].astype(np.float64), v[b].astype(np.float64))
+    for name in ("k", "kq", "ks", "v", "vq", "vs", "kf8", "vf8"):
+        w = getattr(want, name, None)
+        if w is None:
+            continue
+        assert np.array_equal(getattr(got, name).view(np.uint8), w.view(np.uint8)), name
+    assert int(err.cpu()[0]) == 0
+    # a position past the table stores nothing and raises the flag
+    qd.qkdec_kv_append_paged(dkv.desc, _dev(table), 3, _dev(np.array([192, 0, 0], np.int32)), _dev(k), _dev(v), 1,
+                             err=err)
+    sync()
+    assert int(err.cpu()[0]) == -5
+    after = dkv.logical()
+    for name in ("k", "kq", "v", "vq", "kf8", "vf8"):
+        if getattr(got, name, None) is not None:
+            assert np.array_equal(getattr(after, name).view(np.uint8), getattr(got, name).view(np.uint8))
+
+
+def test_paged_attention_full_shape(qd):
+    # B = 8 sequences of a Qwen-shaped layer, ragged contexts, pages of 256
+    from quantized_decode_amd.tensors import upload_cache
+    st = synth.Streams(8400)
+    lens = [2400, 512, 6900, 1, 3000, 2401, 777, 4096]
+    P, hq, hkv, d = 256, 32, 8, 128
+    cap = 7168
+    cont = synth.kv_cache("f16", st.next(), st.next(), len(lens), hkv, cap, d, lens)
+    pool, table, _ = _pool_from(cont, lens, P, sum((n + P - 1) // P for n in lens) + 4, st.next())
+    q = synth.f16_normal(st.next(), (len(lens), hq, d))
+    got = _attn_paged(qd, upload_cache(pool), table, lens, q, 1 / math.sqrt(d))
+    ref = OS.attention_batch_paged(q.astype(np.float64), pool, "f16", table, P, lens, 1 / math.sqrt(d))
+    assert_rel(got, ref, what="paged full shape")
