@@ -215,6 +215,27 @@ def kernel_timing(qd, sd, dev_model, sm, batch, length, seed):
                                         "note": "same kernels as the step's attention (n_ctx = L here, L + 1 "
                                                 "in the step)"}
 
+    # the same attention over paged pools (pages of 256 tokens, every
+    # sequence's pages scattered by a random permutation of the pool); not part
+    # of the step (launches_per_step 0), timed for the comparison
+    P = 256
+    npp = (length + P - 1) // P
+    kind = kind_of[kvs[0].type]
+    pools, keep = [], []
+    for _ in range(len(kvs)):
+        k, v, ks, vs = sd.kv_cache(g, kind, batch * npp, HKV, P, D, P)
+        keep.append((k, v, ks, vs))
+        pools.append(qd.kv_layer(kvs[0].type, HKV, D, P, batch * npp, k, v, ks, vs))
+    table = torch.randperm(batch * npp, device="cuda", generator=g).to(torch.int32).reshape(batch, npp).contiguous()
+    pws = torch.zeros(qd.qkdec_attn_paged_workspace_size(batch, HQ, pools[0], npp), dtype=torch.uint8, device="cuda")
+    fp = lambda kv: qd.qkdec_attn_decode_paged(kv, table, npp, nctx, batch, q, HQ, D ** -0.5, o16=o, workspace=pws,
+                                               stream=stream)
+    ms = _timed([lambda kv=kv: fp(kv) for kv in pools], stream)
+    out[f"attention, paged pool (pages of {P})"] = {
+        "launches_per_step": 0, "avg_ms": ms, "bytes_per_launch": batch * length * kv_bytes,
+        "note": "qkdec_attn_decode_paged over 36 pools of the same size; not in the step"}
+    del pools, keep
+
     tok = torch.empty(batch, dtype=torch.int32, device="cuda")
     lws = torch.zeros(qd.qkdec_lm_head_workspace_size(VOCAB, batch), dtype=torch.uint8, device="cuda")
     flm = lambda: qd.qkdec_lm_head_argmax(lm_head, VOCAB, H, x16, batch, tok, workspace=lws, stream=stream)

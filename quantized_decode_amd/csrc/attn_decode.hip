@@ -35,9 +35,9 @@
 // conversion (exact), after which keys and values take the fp16 path.
 //
 // Paged pool (PAGED): the cache layer's slots are fixed-size pages and each
-// 32-token tile's page comes from the sequence's row of the page table (one
-// uniform load per tile, before the tile's key loads); everything else is the
-// arena kernel.
+// 32-token tile's page comes from the sequence's row of the page table (the
+// run's entries staged in LDS at the start); everything else is the arena
+// kernel.
 #include "attn_dev.h"
 #include "common.h"
 #include "internal.h"
@@ -74,11 +74,23 @@ __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs
     }
   }
   const size_t head_row0 = ((size_t)s * a.n_kv + g) * a.cap;
+  // Paged: the run's page entries (a run is at most kAttnChunk tokens, so at
+  // most kAttnChunk / 32 + 1 pages) are staged in LDS once, clamped into the
+  // pool, so a tile's lookup is an LDS read rather than a global load.
+  __shared__ int s_pg[PAGED ? kAttnChunk / 32 + 1 : 1];
+  const int pg0 = t_begin >> a.page_shift;
+  if constexpr (PAGED) {
+    const int npg = ((t_end - 1) >> a.page_shift) - pg0 + 1;
+    if ((int)threadIdx.x < npg && (int)threadIdx.x < kAttnChunk / 32 + 1) {
+      int pg = a.pages[(size_t)b * a.max_pages + pg0 + threadIdx.x];
+      s_pg[threadIdx.x] = pg < 0 ? 0 : (pg >= a.n_slots ? a.n_slots - 1 : pg);   // never outside the pool
+    }
+    __syncthreads();
+  }
   // (row of token 0 of this head, position within it) of the tile at t
   auto tile_at = [&](int t, size_t& row0, int& tt) {
     if constexpr (PAGED) {
-      int pg = a.pages[(size_t)b * a.max_pages + (t >> a.page_shift)];
-      pg = pg < 0 ? 0 : (pg >= a.n_slots ? a.n_slots - 1 : pg);   // never outside the pool
+      const int pg = __builtin_amdgcn_readfirstlane(s_pg[(t >> a.page_shift) - pg0]);
       row0 = ((size_t)pg * a.n_kv + g) * a.cap;
       tt = t & (a.cap - 1);
     } else {

@@ -83,6 +83,7 @@ CASES = [
     ("fp8", 32, 8, 128, 128, [300, 129, 1024]),
     ("fp8", 8, 2, 64, 32, [33, 64, 5]),
     ("q8k_f16v", 16, 4, 128, 64, [257, 90]),
+    ("f16", 16, 4, 128, 32, [2000, 1025, 4096, 1024]),   # runs of up to 32 one-tile pages
 ]
 
 
