@@ -319,6 +319,19 @@ size_t qkdec_step_workspace_size(const qkdec_model* m, int32_t B, const qkdec_kv
 qkdec_status qkdec_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int32_t* slot,
                         int32_t* pos, int32_t* tok, int32_t B, float* logits, void* workspace,
                         size_t ws_bytes, void* stream);
+/* The decode step over paged pools: as qkdec_step, with every layer of kv a
+ * pool of the same shape (pages of capacity tokens) and pages / max_pages
+ * the page table shared by all layers (a sequence's token t sits in the same
+ * page index of every layer); there is no slot argument.  The new token goes
+ * to position pos[b] of sequence b, whose page must already be in the table
+ * (the host grows a sequence before the step that crosses into a new page);
+ * a position outside the table sets the step's error word (qkdec_step_status)
+ * to QKDEC_E_CAPACITY.  Workspace: qkdec_step_paged_workspace_size(). */
+size_t qkdec_step_paged_workspace_size(const qkdec_model* m, int32_t B_max, const qkdec_kv_layer* kv,
+                                       int32_t max_pages);
+qkdec_status qkdec_step_paged(const qkdec_model* m, const qkdec_kv_layer* kv, const int32_t* pages,
+                              int32_t max_pages, int32_t* pos, int32_t* tok, int32_t B, float* logits,
+                              void* workspace, size_t ws_bytes, void* stream);
 /* Synchronizes `stream`, returns QKDEC_E_CAPACITY if any step since the last
  * call hit the capacity, else QKDEC_OK; the flag is cleared. */
 qkdec_status qkdec_step_status(void* workspace, void* stream);

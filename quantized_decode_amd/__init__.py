@@ -87,6 +87,9 @@ _SIGNATURES = {
     "qkdec_workspace_init": (_I32, [_P, _SZ, _P]),
     "qkdec_step": (_I32, [ctypes.POINTER(Model), ctypes.POINTER(KVLayer), _P, _P, _P, _I32, _P, _P, _SZ, _P]),
     "qkdec_step_status": (_I32, [_P, _P]),
+    "qkdec_step_paged_workspace_size": (_SZ, [ctypes.POINTER(Model), _I32, ctypes.POINTER(KVLayer), _I32]),
+    "qkdec_step_paged": (_I32, [ctypes.POINTER(Model), ctypes.POINTER(KVLayer), _P, _I32, _P, _P, _I32, _P, _P, _SZ,
+                                _P]),
     "qkdec_step_workspace_views": (_I32, [ctypes.POINTER(Model), _I32, ctypes.POINTER(KVLayer),
                                           ctypes.POINTER(StepViews)]),
     "qkdec_plan_create": (_I32, [ctypes.POINTER(_P), ctypes.POINTER(Model), ctypes.POINTER(KVLayer), _P, _P, _P,
@@ -259,6 +262,18 @@ def qkdec_step(sm: StepModel, slot, pos, tok, b: int, workspace, logits=None, st
     _check(load_library().qkdec_step(ctypes.byref(sm.model), sm.kv_arr, _ptr(slot), _ptr(pos), _ptr(tok), b,
                                      _ptr(logits), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                      _stream(stream)), "qkdec_step")
+
+
+def qkdec_step_paged_workspace_size(sm: StepModel, b: int, max_pages: int) -> int:
+    return load_library().qkdec_step_paged_workspace_size(ctypes.byref(sm.model), b, sm.kv_arr, max_pages)
+
+
+def qkdec_step_paged(sm: StepModel, pages, max_pages: int, pos, tok, b: int, workspace, logits=None,
+                     stream=None) -> None:
+    _check(load_library().qkdec_step_paged(ctypes.byref(sm.model), sm.kv_arr, _ptr(pages), max_pages, _ptr(pos),
+                                           _ptr(tok), b, _ptr(logits), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), _stream(stream)),
+           "qkdec_step_paged")
 
 
 def qkdec_step_status(workspace, stream=None) -> int:

@@ -358,8 +358,9 @@ __device__ void qkv_finish(const WkArgs& a, Red red, int wave, int lane, int g, 
   for (int ii = 0; ii < 4; ++ii) {
     const int b = 4 * g + ii;
     if (b >= a.B) continue;
-    const bool ok = sl[ii] >= 0 && sl[ii] < ra.n_slots && ps[ii] >= 0 && ps[ii] < ra.cap;
-    if (ok) store_point(c, is_v, sl[ii], kvh, ps[ii], d, out[ii]);
+    int s = sl[ii], p = ps[ii];
+    const bool ok = kv_locate(ra.pages, ra.max_pages, ra.page_shift, ra.n_slots, ra.cap, b, s, p);
+    if (ok) store_point(c, is_v, s, kvh, p, d, out[ii]);
     else if (r == 0) *ra.err = QKDEC_E_CAPACITY;
   }
 }

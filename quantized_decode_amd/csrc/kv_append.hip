@@ -27,17 +27,8 @@ __global__ void kv_append_kernel(qkdec_kv_layer kv, const int32_t* slot, const i
                                  const float* v, int32_t* err, const int32_t* pages, int max_pages, int page_shift) {
   const CacheRef c = cache_ref(kv);
   const int g = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  int s, p = pos[b];
-  bool ok;
-  if (pages) {
-    const bool in = p >= 0 && p < (max_pages << page_shift);
-    s = in ? pages[(size_t)b * max_pages + (p >> page_shift)] : -1;
-    p &= c.cap - 1;
-    ok = in && s >= 0 && s < c.n_slots;
-  } else {
-    s = slot[b];
-    ok = s >= 0 && s < c.n_slots && p >= 0 && p < c.cap;
-  }
+  int s = pages ? 0 : slot[b], p = pos[b];
+  const bool ok = kv_locate(pages, max_pages, page_shift, c.n_slots, c.cap, b, s, p);
   if (!ok && d == 0 && err) *err = QKDEC_E_CAPACITY;
   const size_t src = ((size_t)b * c.n_kv + g) * c.D + d;
   store_elem(c, false, s, g, p, d, k[src], ok);
@@ -48,10 +39,11 @@ __global__ void kv_append_kernel(qkdec_kv_layer kv, const int32_t* slot, const i
 // that only stores the fp32 rows Y = [q heads; k heads; v heads] per
 // sequence): grid (Hq + 2 n_kv, B), block D threads; thread d of head h rotates
 // dims (d, d +- D/2) of q and k at pos[b] (rope_cos_sin), q goes out as fp16,
-// k and v are appended to the cache at (slot[b], pos[b]).
+// k and v are appended to the cache at (slot[b], pos[b]) (or, with a page
+// table, into sequence b's page: kv_locate).
 __global__ void rope_append_kernel(qkdec_kv_layer kv, const float* __restrict__ Y, int64_t ldy, int Hq,
                                    const int32_t* slot, const int32_t* pos, float rope_base, uint16_t* q16,
-                                   int32_t* err) {
+                                   int32_t* err, const int32_t* pages, int max_pages, int page_shift) {
   const CacheRef c = cache_ref(kv);
   const int head = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int D = c.D, half = D / 2;
@@ -71,18 +63,20 @@ __global__ void rope_append_kernel(qkdec_kv_layer kv, const float* __restrict__ 
     q16[((size_t)b * Hq + head) * D + d] = f2h_bits(out);
     return;
   }
-  const int s = slot[b];
-  const bool ok = s >= 0 && s < c.n_slots && p >= 0 && p < c.cap;
+  int s = pages ? 0 : slot[b], pp = p;
+  const bool ok = kv_locate(pages, max_pages, page_shift, c.n_slots, c.cap, b, s, pp);
   if (!ok && d == 0 && err) *err = QKDEC_E_CAPACITY;
   const int g = is_v ? head - Hq - c.n_kv : head - Hq;
-  store_elem(c, is_v, s, g, p, d, out, ok);
+  store_elem(c, is_v, s, g, pp, d, out, ok);
 }
 
 hipError_t launch_rope_append(const qkdec_kv_layer& kv, const float* Y, int64_t ldy, int Hq, int B,
                               const int32_t* slot, const int32_t* pos, float rope_base, uint16_t* q16, int32_t* err,
-                              hipStream_t st) {
+                              hipStream_t st, const int32_t* pages, int max_pages) {
+  int shift = 0;
+  while (pages && (1 << shift) < kv.capacity) ++shift;
   hipLaunchKernelGGL(rope_append_kernel, dim3(Hq + 2 * kv.n_kv_heads, B), dim3(kv.head_dim), 0, st, kv, Y, ldy, Hq,
-                     slot, pos, rope_base, q16, err);
+                     slot, pos, rope_base, q16, err, pages, pages ? max_pages : 0, shift);
   return hipGetLastError();
 }
 

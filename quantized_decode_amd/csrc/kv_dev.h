@@ -106,6 +106,21 @@ __device__ __forceinline__ void store_elem(const CacheRef& c, bool is_v, int s, 
   }
 }
 
+// Where logical position p of sequence b is stored.  Slot arena (pages ==
+// nullptr): slot s as given, position p.  Paged pool (slots are pages of cap
+// tokens, cap = 2^page_shift): s = pages[b * max_pages + p / cap], p % cap.
+// On return s and p address the store; false if it lies outside the cache.
+__device__ __forceinline__ bool kv_locate(const int32_t* pages, int max_pages, int page_shift, int n_slots, int cap,
+                                          int b, int& s, int& p) {
+  if (pages) {
+    const bool in = p >= 0 && p < (max_pages << page_shift);
+    s = in ? pages[(size_t)b * max_pages + (p >> page_shift)] : -1;
+    p &= cap - 1;
+    return in && s >= 0 && s < n_slots;
+  }
+  return s >= 0 && s < n_slots && p >= 0 && p < cap;
+}
+
 // Rotary position embedding, rotate-half pairs (i, i + D/2): the angle of
 // pair i at position p, p * base^(-2i/D), is formed in fp64; cos and sin are
 // rounded once to fp32 and the rotation itself is fp32.

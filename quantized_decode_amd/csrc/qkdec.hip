@@ -108,7 +108,7 @@ struct StepWs {
   size_t bytes;
 };
 
-StepWs step_layout(const qkdec_model* m, int B, const qkdec_kv_layer* kv, char* base) {
+StepWs step_layout(const qkdec_model* m, int B, const qkdec_kv_layer* kv, char* base, int max_pages = 0) {
   StepWs w{};
   size_t off = 0;
   auto take = [&](size_t n) {
@@ -126,7 +126,8 @@ StepWs step_layout(const qkdec_model* m, int B, const qkdec_kv_layer* kv, char* 
   w.q16 = reinterpret_cast<uint16_t*>(take((size_t)B * hq * 2));
   w.o16 = reinterpret_cast<uint16_t*>(take((size_t)B * hq * 2));
   w.a = reinterpret_cast<float*>(take((size_t)B * m->ffn * 4));
-  w.attn_part = reinterpret_cast<float*>(take(attn_partials_bytes(B, m->n_q_heads, m->head_dim, kv[0].capacity, kv[0].n_kv_heads)));
+  w.attn_part = reinterpret_cast<float*>(
+      take(attn_partials_bytes(B, m->n_q_heads, m->head_dim, attn_seq_cap(kv[0], max_pages), kv[0].n_kv_heads)));
   w.lm_part = take(lm_head_partials_bytes(m->vocab, B));
   size_t g = gemm_workspace_bytes(nqkv, m->hidden, B, false);
   g = std::max(g, gemm_workspace_bytes(m->hidden, hq, B, false));
@@ -137,9 +138,16 @@ StepWs step_layout(const qkdec_model* m, int B, const qkdec_kv_layer* kv, char* 
   return w;
 }
 
+// pages != nullptr: every layer of kv is a paged pool and sequence b's pages
+// are pages[b * max_pages ...]; slot is unused
 qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int32_t* slot, int32_t* pos,
-                      int32_t* tok, int B, float* logits, void* workspace, hipStream_t st) {
-  const StepWs w = step_layout(m, B, kv, reinterpret_cast<char*>(workspace));
+                      int32_t* tok, int B, float* logits, void* workspace, hipStream_t st,
+                      const int32_t* pages = nullptr, int max_pages = 0) {
+  const StepWs w = step_layout(m, B, kv, reinterpret_cast<char*>(workspace), max_pages);
+  int page_shift = 0;
+  while (pages && (1 << page_shift) < kv[0].capacity) ++page_shift;
+  // the projection finishes load slot[b] unconditionally (no branch around a
+  // load); with a page table any readable int32[B] serves: pos
   const int H = m->hidden, F = m->ffn, D = m->head_dim, Hq = m->n_q_heads;
   const int64_t hq = (int64_t)Hq * D;
   const int64_t nqkv = (int64_t)(Hq + 2 * m->n_kv_heads) * D;
@@ -160,7 +168,8 @@ qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int3
     qkv.Y = w.qkv; qkv.ldy = nqkv; qkv.ws = w.gemm_ws;
     // ... finished per head: RoPE, q -> fp16, k and v appended to the cache
     RopeAppendArgs ra{};
-    ra.slot = slot; ra.pos = pos;
+    ra.slot = pages ? pos : slot; ra.pos = pos;
+    ra.pages = pages; ra.max_pages = pages ? max_pages : 0; ra.page_shift = page_shift;
     ra.k = reinterpret_cast<uint8_t*>(kv[l].k); ra.v = reinterpret_cast<uint8_t*>(kv[l].v);
     ra.ks = reinterpret_cast<uint16_t*>(kv[l].k_scale); ra.vs = reinterpret_cast<uint16_t*>(kv[l].v_scale);
     ra.n_kv = kv[l].n_kv_heads; ra.cap = kv[l].capacity; ra.n_slots = kv[l].n_slots; ra.Hq = Hq;
@@ -176,12 +185,14 @@ qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int3
         QK_TRY(launch_gemm_qkv_rope(qkv, ra, D, st));
       } else {
         QK_TRY(eq);
-        QK_TRY(launch_rope_append(kv[l], w.qkv, nqkv, Hq, B, slot, pos, m->rope_base, w.q16, w.err, st));
+        QK_TRY(launch_rope_append(kv[l], w.qkv, nqkv, Hq, B, slot, pos, m->rope_base, w.q16, w.err, st, pages,
+                                  max_pages));
       }
     } else {
       QK_TRY(eq);
     }
-    QK_TRY(launch_attn_decode(kv[l], slot, pos, B, w.q16, Hq, scale, nullptr, w.o16, w.attn_part, 1, st));
+    QK_TRY(launch_attn_decode(kv[l], slot, pos, B, w.q16, Hq, scale, nullptr, w.o16, w.attn_part, 1, st, pages,
+                              max_pages));
     // O projection: fp16 activations, K split over the waves of one work-group
     // per output tile (no split-K round trips); the fp32-activation projections
     // stage their activations once per work-group and split K across work-groups
@@ -458,6 +469,33 @@ qkdec_status qkdec_step(const qkdec_model* m, const qkdec_kv_layer* kv, const in
   if (s != QKDEC_OK) return s;
   clear_stale_error();
   return run_step(m, kv, slot, pos, tok, B, logits, workspace, as_stream(stream));
+}
+
+size_t qkdec_step_paged_workspace_size(const qkdec_model* m, int32_t B, const qkdec_kv_layer* kv,
+                                       int32_t max_pages) {
+  if (check_model(m, kv) != QKDEC_OK || B < 1 || B > 16 || max_pages < 1 ||
+      (int64_t)max_pages * kv[0].capacity > ((int64_t)1 << 30))
+    return 0;
+  return step_layout(m, B, kv, nullptr, max_pages).bytes;
+}
+
+qkdec_status qkdec_step_paged(const qkdec_model* m, const qkdec_kv_layer* kv, const int32_t* pages,
+                              int32_t max_pages, int32_t* pos, int32_t* tok, int32_t B, float* logits,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  qkdec_status s = check_model(m, kv);
+  if (s != QKDEC_OK) return s;
+  for (int l = 0; l < m->n_layers; ++l) {
+    s = check_pages(&kv[l], pages, max_pages);
+    if (s != QKDEC_OK) return s;
+  }
+  if (!pos || !tok) return QKDEC_E_ARG;
+  if (B < 1 || B > 16) return QKDEC_E_SHAPE;
+  if (!workspace || ws_bytes < step_layout(m, B, kv, nullptr, max_pages).bytes) return QKDEC_E_WORKSPACE;
+  if (!aligned(workspace, 256)) return QKDEC_E_ALIGN;
+  s = check_lds(lm_head_lds_bytes(m->hidden, B));
+  if (s != QKDEC_OK) return s;
+  clear_stale_error();
+  return run_step(m, kv, nullptr, pos, tok, B, logits, workspace, as_stream(stream), pages, max_pages);
 }
 
 qkdec_status qkdec_step_status(void* workspace, void* stream) {

@@ -26,7 +26,7 @@ def _dev(a):
     return dev(a)
 
 
-def _pool_from(cont, lengths, P, n_pages, rng):
+def _pool_from(cont, lengths, P, n_pages, rng, room=0):
     """Copy each sequence's tokens of a contiguous cache (slot b = sequence b)
     into pages handed out by a PagePool after some shuffling admissions; the
     pages nobody holds, and every position past a sequence's length, are
@@ -40,7 +40,7 @@ def _pool_from(cont, lengths, P, n_pages, rng):
     for j in range(0, n_pad, 2):
         pool.release(("pad", j))
     for b, n in enumerate(lengths):
-        pool.admit(b, n)
+        pool.admit(b, n + room)
     max_pages = max(len(pool.pages(b)) for b in range(len(lengths)))
     table = pool.table(range(len(lengths)), max_pages)
     out = copy.deepcopy(cont)
@@ -181,3 +181,65 @@ def test_paged_attention_full_shape(qd):
     got = _attn_paged(qd, upload_cache(pool), table, lens, q, 1 / math.sqrt(d))
     ref = OS.attention_batch_paged(q.astype(np.float64), pool, "f16", table, P, lens, 1 / math.sqrt(d))
     assert_rel(got, ref, what="paged full shape")
+
+
+STEP_CASES = [
+    ("toy", "f16", 2, 128, 32, 160),
+    ("toy", "q8_0", 2, 128, 64, 192),
+    ("toy", "fp8", 2, 128, 32, 160),
+    ("full", "f16", 4, 300, 64, 320),
+    ("full", "q8_0", 4, 300, 64, 320),
+]
+
+
+@pytest.mark.parametrize("shape,kind,bsz,L,P,cap", STEP_CASES)
+def test_paged_step_equals_arena_step(qd, shape, kind, bsz, L, P, cap):
+    # three decode steps over pools whose pages are scattered, against the
+    # slot-arena step on the same data (itself checked against the oracle in
+    # test_gpu_step.py): with max_pages * P = capacity every kernel does the
+    # same arithmetic, so logits, tokens, positions and every cached byte
+    # must be identical
+    import torch
+    from quantized_decode_amd.tensors import upload_cache
+    from tests.test_gpu_step import GpuStep, build
+    dims = synth.TOY if shape == "toy" else synth.QWEN_SHAPED
+    model, caches, tok = build(dims, 1200 + P, kind, bsz, L, cap, n_layers=None if shape == "toy" else 1)
+    steps = 3
+    arena = GpuStep(qd, model, caches, bsz, list(range(bsz)))
+    arena.set([L] * bsz, tok)
+    n_pages = bsz * (cap // P) + 6
+    pools, table = [], None
+    for c in caches:   # the same rng per layer: one page table for all layers
+        pool, t, _ = _pool_from(c, [L] * bsz, P, n_pages, np.random.default_rng(99), room=steps)
+        assert table is None or np.array_equal(t, table)
+        pools.append(pool)
+        table = t
+    max_pages = cap // P
+    table = np.pad(table, ((0, 0), (0, max_pages - table.shape[1])))
+    dpools = [upload_cache(p) for p in pools]
+    sm = qd.StepModel(dims, arena.embed, arena.lm_head, arena.norm, arena.layers, [d.desc for d in dpools])
+    pos = _dev(np.full(bsz, L, np.int32))
+    tk = _dev(np.asarray(tok, np.int32))
+    logits = torch.empty((bsz, dims.vocab), dtype=torch.float32, device="cuda")
+    wsp = ws(qd.qkdec_step_paged_workspace_size(sm, bsz, max_pages))
+    qd.qkdec_workspace_init(wsp)
+    tdev = _dev(table)
+    for i in range(steps):
+        la, ta, pa = arena.step()
+        qd.qkdec_step_paged(sm, tdev, max_pages, pos, tk, bsz, wsp, logits=logits)
+        sync()
+        assert np.array_equal(logits.cpu().numpy().view(np.uint32), la.view(np.uint32)), f"step {i}: logits"
+        assert np.array_equal(tk.cpu().numpy(), ta) and np.array_equal(pos.cpu().numpy(), pa), f"step {i}"
+    assert qd.qkdec_step_status(wsp) == 0
+    n_now = L + steps
+    for li, (dp, da) in enumerate(zip(dpools, arena.kv)):
+        gp, ga = dp.logical(), da.logical()
+        for name, arr in vars(ga).items():
+            if arr is None:
+                continue
+            parr = getattr(gp, name)
+            for b in range(bsz):
+                for j in range((n_now + P - 1) // P):
+                    take = min(P, n_now - j * P)
+                    assert np.array_equal(parr[table[b, j], :, :take].view(np.uint8),
+                                          arr[b, :, j * P:j * P + take].view(np.uint8)), (li, name, b, j)
