@@ -123,6 +123,54 @@ def time_point(qd, sm, batch, length, steps, warmup, vocab, seed):
     return per, wall
 
 
+def time_paged_step(qd, sd, dims, dev_model, batch, length, kind, steps, warmup, seed, page_tokens=256):
+    """The same step over paged pools (qkdec_step_paged): pages of
+    `page_tokens`, each sequence's pages scattered by a random permutation of
+    the pool; one step captured in a HIP graph and replayed like the arena
+    step.  Returns per-replay durations (ms)."""
+    import torch
+    from quantized_decode_amd import KV_KINDS, kv_layer
+    from quantized_decode_amd import planner as PL
+    P = page_tokens
+    max_pages = (PL.slot_capacity(length, warmup + steps + 2) + P - 1) // P
+    n_pages = batch * max_pages
+    g = sd.generator(seed)
+    pools, keep = [], []
+    for _ in range(dims.n_layers):
+        k, v, ks, vs = sd.kv_cache(g, kind, n_pages, dims.n_kv_heads, P, dims.head_dim, P)
+        keep.append((k, v, ks, vs))
+        pools.append(kv_layer(KV_KINDS[kind], dims.n_kv_heads, dims.head_dim, P, n_pages, k, v, ks, vs))
+    table = torch.randperm(n_pages, device="cuda", generator=g).to(torch.int32).reshape(batch, max_pages).contiguous()
+    embed, lm_head, norm, layers = dev_model
+    sm = qd.StepModel(dims, embed, lm_head, norm, layers, pools)
+    pos = torch.full((batch,), length, dtype=torch.int32, device="cuda")
+    tok = torch.randint(0, dims.vocab, (batch,), dtype=torch.int32, device="cuda", generator=g)
+    ws = torch.zeros(qd.qkdec_step_paged_workspace_size(sm, batch, max_pages), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+    run = lambda: qd.qkdec_step_paged(sm, table, max_pages, pos, tok, batch, ws, stream=stream)
+    with torch.cuda.stream(stream):
+        run()                                   # one eager step (pos advances)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        run()
+    per = []
+    with torch.cuda.stream(stream):
+        for i in range(warmup + steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            graph.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            if i >= warmup:
+                per.append(a.elapsed_time(b))
+    status = qd.qkdec_step_status(ws)
+    assert status == 0, f"paged step reported status {status}"
+    assert int(pos[0].item()) == length + 1 + warmup + steps
+    del graph
+    return per
+
+
 def _timed(calls, stream, replays=5):
     """Average duration (ms) of one call of `calls`: the calls are captured in
     order into one HIP graph on `stream` and replayed between HIP events on
@@ -472,6 +520,16 @@ def main():
         torch.cuda.empty_cache()
 
     main_pt = results[0]
+    log("the main point's step over paged pools (pages of 256)")
+    pper = time_paged_step(qd, sd, dims, dev_model, main_pt["batch"], main_pt["context"], main_pt["kv"],
+                           min(args.steps, 16), args.warmup, 8000)
+    pms = sum(pper) / len(pper)
+    paged = {"batch": main_pt["batch"], "context": main_pt["context"], "kv": main_pt["kv"], "page_tokens": 256,
+             "ms_per_step": pms, "tok_per_s": main_pt["batch"] / (pms * 1e-3),
+             "vs_arena_step": pms / main_pt["ms_per_step"],
+             "note": "qkdec_step_paged, each sequence's pages scattered over the pool; graph replays"}
+    log(f"  paged: {pms:.3f} ms/step ({pms / main_pt['ms_per_step']:.3f} x the arena step)")
+    torch.cuda.empty_cache()
     dom_name, dom = max(kernels.items(), key=lambda kv: kv[1]["ms_per_step"])
     achieved = dom["bytes_per_launch"] / (dom["avg_ms"] * 1e-3) / 1e9
     traffic = COUNTED_TRAFFIC.get((dom_name, main_pt["batch"], main_pt["context"], main_pt["kv"]))
@@ -502,7 +560,7 @@ def main():
         "achieved_GBps": main_pt["achieved_GBps"], "frac_of_8TBps": main_pt["frac_of_8TBps"],
         "frac_of_read_ceiling": main_pt["frac_of_read_ceiling"], "read_ceiling": ceiling,
         "clocks": None if args.no_clocks else clocks(),
-        "roofline": roofline, "kernels": kernels, "points": results, "cpu_baseline": cpu,
+        "roofline": roofline, "kernels": kernels, "points": results, "paged_step": paged, "cpu_baseline": cpu,
     }
     print(json.dumps(out))
 
