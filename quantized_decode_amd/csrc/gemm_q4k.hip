@@ -387,8 +387,8 @@ __device__ void gemm_item(const GemmArgs& a, int rg, int c, int n_chunks, half_t
       for (int ii = 0; ii < 4; ++ii) {
         const int b = 4 * g + ii;
         sl[ii] = b < B ? ra.slot[b] : 0;
-        ps[ii] = b < B ? ra.pos[b] : 0;
-        ok[ii] = b < B && kv_locate(ra.pages, ra.max_pages, ra.page_shift, ra.n_slots, ra.cap, b, sl[ii], ps[ii]);
+        ps[ii] = b < B ? ra.spos[b] : 0;
+        ok[ii] = b < B && sl[ii] >= 0 && sl[ii] < ra.n_slots && ps[ii] >= 0 && ps[ii] < ra.cap;
         if (b < B && !ok[ii] && wave == 0 && r == 0) *ra.err = QKDEC_E_CAPACITY;
       }
       if ((is_v ? ra.vf : ra.kf) != kFmtQ8) {   // uniform: one head per work-group

@@ -358,9 +358,8 @@ __device__ void qkv_finish(const WkArgs& a, Red red, int wave, int lane, int g, 
   for (int ii = 0; ii < 4; ++ii) {
     const int b = 4 * g + ii;
     if (b >= a.B) continue;
-    int s = sl[ii], p = ps[ii];
-    const bool ok = kv_locate(ra.pages, ra.max_pages, ra.page_shift, ra.n_slots, ra.cap, b, s, p);
-    if (ok) store_point(c, is_v, s, kvh, p, d, out[ii]);
+    const bool ok = sl[ii] >= 0 && sl[ii] < ra.n_slots && ps[ii] >= 0 && ps[ii] < ra.cap;
+    if (ok) store_point(c, is_v, sl[ii], kvh, ps[ii], d, out[ii]);
     else if (r == 0) *ra.err = QKDEC_E_CAPACITY;
   }
 }
@@ -468,7 +467,7 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
     for (int ii = 0; ii < 4; ++ii) {
       const int b = 4 * g + ii < a.B ? 4 * g + ii : a.B - 1;
       sl[ii] = a.ra.slot[b];
-      ps[ii] = a.ra.pos[b];
+      ps[ii] = a.ra.spos[b];
     }
     pos_t = a.ra.pos[(tx >> 4) < a.B ? (tx >> 4) : a.B - 1];
   }

@@ -53,10 +53,10 @@ struct RopeAppendArgs {
   uint8_t *k, *v;        // cache of this layer (fp16 or Q8_0 codes)
   uint16_t *ks, *vs;     // Q8_0 block scales
   int n_kv, cap, n_slots, Hq;
-  // paged pool (pages != nullptr): the cache's slots are pages of cap =
-  // 2^page_shift tokens and slot is only a readable dummy; see kv_locate
-  const int32_t* pages;
-  int max_pages, page_shift;
+  // where the new token is stored: (slot[b], spos[b]); spos = pos for a slot
+  // arena, the page and the position within it for a paged pool
+  // (launch_page_locate)
+  const int32_t* spos;
   int kf, vf;             // key / value format (kFmtF16, kFmtQ8, kFmtF8)
   float rope_base;
   uint16_t* q16;         // rotated queries, fp16 bits
@@ -151,7 +151,12 @@ hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, con
 // (row b: [q heads; k heads; v heads], head_dim each)
 hipError_t launch_rope_append(const qkdec_kv_layer& kv, const float* Y, int64_t ldy, int Hq, int B,
                               const int32_t* slot, const int32_t* pos, float rope_base, uint16_t* q16, int32_t* err,
-                              hipStream_t st, const int32_t* pages = nullptr, int max_pages = 0);
+                              hipStream_t st, const int32_t* spos = nullptr);
+// Paged step: page[b] and the position within it of logical position pos[b]
+// of sequence b (page -1 when outside the table or the pool), once per step
+// for every layer's stores.
+hipError_t launch_page_locate(const int32_t* pages, int max_pages, int page_tokens, int n_pages, const int32_t* pos,
+                              int B, int32_t* page, int32_t* page_pos, hipStream_t st);
 hipError_t launch_kv_append(const qkdec_kv_layer& kv, const int32_t* slot, const int32_t* pos, const float* k,
                             const float* v, int B, int32_t* err, hipStream_t st, const int32_t* pages = nullptr,
                             int max_pages = 0);

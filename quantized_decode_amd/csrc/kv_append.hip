@@ -39,11 +39,11 @@ __global__ void kv_append_kernel(qkdec_kv_layer kv, const int32_t* slot, const i
 // that only stores the fp32 rows Y = [q heads; k heads; v heads] per
 // sequence): grid (Hq + 2 n_kv, B), block D threads; thread d of head h rotates
 // dims (d, d +- D/2) of q and k at pos[b] (rope_cos_sin), q goes out as fp16,
-// k and v are appended to the cache at (slot[b], pos[b]) (or, with a page
-// table, into sequence b's page: kv_locate).
+// k and v are appended to the cache at (slot[b], spos[b]) (spos: pos, or the
+// position within the page a paged step located).
 __global__ void rope_append_kernel(qkdec_kv_layer kv, const float* __restrict__ Y, int64_t ldy, int Hq,
                                    const int32_t* slot, const int32_t* pos, float rope_base, uint16_t* q16,
-                                   int32_t* err, const int32_t* pages, int max_pages, int page_shift) {
+                                   int32_t* err, const int32_t* spos) {
   const CacheRef c = cache_ref(kv);
   const int head = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int D = c.D, half = D / 2;
@@ -63,8 +63,8 @@ __global__ void rope_append_kernel(qkdec_kv_layer kv, const float* __restrict__ 
     q16[((size_t)b * Hq + head) * D + d] = f2h_bits(out);
     return;
   }
-  int s = pages ? 0 : slot[b], pp = p;
-  const bool ok = kv_locate(pages, max_pages, page_shift, c.n_slots, c.cap, b, s, pp);
+  const int s = slot[b], pp = spos[b];
+  const bool ok = s >= 0 && s < c.n_slots && pp >= 0 && pp < c.cap;
   if (!ok && d == 0 && err) *err = QKDEC_E_CAPACITY;
   const int g = is_v ? head - Hq - c.n_kv : head - Hq;
   store_elem(c, is_v, s, g, pp, d, out, ok);
@@ -72,11 +72,29 @@ __global__ void rope_append_kernel(qkdec_kv_layer kv, const float* __restrict__ 
 
 hipError_t launch_rope_append(const qkdec_kv_layer& kv, const float* Y, int64_t ldy, int Hq, int B,
                               const int32_t* slot, const int32_t* pos, float rope_base, uint16_t* q16, int32_t* err,
-                              hipStream_t st, const int32_t* pages, int max_pages) {
-  int shift = 0;
-  while (pages && (1 << shift) < kv.capacity) ++shift;
+                              hipStream_t st, const int32_t* spos) {
   hipLaunchKernelGGL(rope_append_kernel, dim3(Hq + 2 * kv.n_kv_heads, B), dim3(kv.head_dim), 0, st, kv, Y, ldy, Hq,
-                     slot, pos, rope_base, q16, err, pages, pages ? max_pages : 0, shift);
+                     slot, pos, rope_base, q16, err, spos ? spos : pos);
+  return hipGetLastError();
+}
+
+// one thread per sequence: page and position within it of pos[b]
+__global__ void page_locate_kernel(const int32_t* pages, int max_pages, int page_shift, int n_pages,
+                                   const int32_t* pos, int B, int32_t* page, int32_t* page_pos) {
+  const int b = threadIdx.x;
+  if (b >= B) return;
+  int s = 0, p = pos[b];
+  const bool ok = kv_locate(pages, max_pages, page_shift, n_pages, 1 << page_shift, b, s, p);
+  page[b] = ok ? s : -1;
+  page_pos[b] = p;
+}
+
+hipError_t launch_page_locate(const int32_t* pages, int max_pages, int page_tokens, int n_pages, const int32_t* pos,
+                              int B, int32_t* page, int32_t* page_pos, hipStream_t st) {
+  int shift = 0;
+  while ((1 << shift) < page_tokens) ++shift;
+  hipLaunchKernelGGL(page_locate_kernel, dim3(1), dim3(64), 0, st, pages, max_pages, shift, n_pages, pos, B, page,
+                     page_pos);
   return hipGetLastError();
 }
 

@@ -103,6 +103,8 @@ struct StepWs {
   uint16_t* o16;
   float* a;
   float* attn_part;
+  int32_t* page;       // paged step: page of each sequence's new token (-1: outside)
+  int32_t* page_pos;   // and its position within the page
   void* lm_part;
   void* gemm_ws;
   size_t bytes;
@@ -128,6 +130,8 @@ StepWs step_layout(const qkdec_model* m, int B, const qkdec_kv_layer* kv, char* 
   w.a = reinterpret_cast<float*>(take((size_t)B * m->ffn * 4));
   w.attn_part = reinterpret_cast<float*>(
       take(attn_partials_bytes(B, m->n_q_heads, m->head_dim, attn_seq_cap(kv[0], max_pages), kv[0].n_kv_heads)));
+  w.page = reinterpret_cast<int32_t*>(take((size_t)B * 4));
+  w.page_pos = reinterpret_cast<int32_t*>(take((size_t)B * 4));
   w.lm_part = take(lm_head_partials_bytes(m->vocab, B));
   size_t g = gemm_workspace_bytes(nqkv, m->hidden, B, false);
   g = std::max(g, gemm_workspace_bytes(m->hidden, hq, B, false));
@@ -144,10 +148,6 @@ qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int3
                       int32_t* tok, int B, float* logits, void* workspace, hipStream_t st,
                       const int32_t* pages = nullptr, int max_pages = 0) {
   const StepWs w = step_layout(m, B, kv, reinterpret_cast<char*>(workspace), max_pages);
-  int page_shift = 0;
-  while (pages && (1 << page_shift) < kv[0].capacity) ++page_shift;
-  // the projection finishes load slot[b] unconditionally (no branch around a
-  // load); with a page table any readable int32[B] serves: pos
   const int H = m->hidden, F = m->ffn, D = m->head_dim, Hq = m->n_q_heads;
   const int64_t hq = (int64_t)Hq * D;
   const int64_t nqkv = (int64_t)(Hq + 2 * m->n_kv_heads) * D;
@@ -157,6 +157,10 @@ qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int3
     const hipError_t e_ = (expr);                    \
     if (e_ != hipSuccess) return QKDEC_E_HIP;        \
   } while (0)
+  // paged: every layer stores the new token of sequence b at the same page and
+  // position within it, located once per step
+  if (pages)
+    QK_TRY(launch_page_locate(pages, max_pages, kv[0].capacity, kv[0].n_slots, pos, B, w.page, w.page_pos, st));
   QK_TRY(launch_embed(m->embed, H, m->vocab, tok, B, w.x, w.ss, st));
   for (int l = 0; l < m->n_layers; ++l) {
     const qkdec_layer& ly = m->layers[l];
@@ -168,8 +172,7 @@ qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int3
     qkv.Y = w.qkv; qkv.ldy = nqkv; qkv.ws = w.gemm_ws;
     // ... finished per head: RoPE, q -> fp16, k and v appended to the cache
     RopeAppendArgs ra{};
-    ra.slot = pages ? pos : slot; ra.pos = pos;
-    ra.pages = pages; ra.max_pages = pages ? max_pages : 0; ra.page_shift = page_shift;
+    ra.slot = pages ? w.page : slot; ra.pos = pos; ra.spos = pages ? w.page_pos : pos;
     ra.k = reinterpret_cast<uint8_t*>(kv[l].k); ra.v = reinterpret_cast<uint8_t*>(kv[l].v);
     ra.ks = reinterpret_cast<uint16_t*>(kv[l].k_scale); ra.vs = reinterpret_cast<uint16_t*>(kv[l].v_scale);
     ra.n_kv = kv[l].n_kv_heads; ra.cap = kv[l].capacity; ra.n_slots = kv[l].n_slots; ra.Hq = Hq;
@@ -185,8 +188,8 @@ qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int3
         QK_TRY(launch_gemm_qkv_rope(qkv, ra, D, st));
       } else {
         QK_TRY(eq);
-        QK_TRY(launch_rope_append(kv[l], w.qkv, nqkv, Hq, B, slot, pos, m->rope_base, w.q16, w.err, st, pages,
-                                  max_pages));
+        QK_TRY(launch_rope_append(kv[l], w.qkv, nqkv, Hq, B, ra.slot, pos, m->rope_base, w.q16, w.err, st,
+                                  ra.spos));
       }
     } else {
       QK_TRY(eq);
