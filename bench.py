@@ -66,11 +66,11 @@ KV_BYTES_PER_TOKEN = {"f16": NL * HKV * D * 2 * 2, "q8_0": NL * HKV * D * 2 * 34
 # profiles/decode_step_b8_l6900_fp8_kernel_stats.md.  A kernel changed since
 # has no entry, and its traffic is reported as null.
 COUNTED_TRAFFIC = {
-    # split kernel 79,179,991 fetched + 555,342 written; merge 617,480 + 65,536
+    # split kernel 79,173,829 fetched + 557,056 written; merge 617,800 + 65,536
     # (fetched and written each rounded once over split + merge)
-    ("attention (split + merge)", 8, 2400, "f16"): 80_418_348,
-    # E4M3 cache: split 113,884,031 fetched + 974,848 written; merge 1,010,663 + 65,536
-    ("attention (split + merge)", 8, 6900, "fp8"): 115_935_078,
+    ("attention (split + merge)", 8, 2400, "f16"): 80_414_221,
+    # E4M3 cache: split 113,885,297 fetched + 971,848 written; merge 973,676 + 65,536
+    ("attention (split + merge)", 8, 6900, "fp8"): 115_896_357,
 }
 
 
