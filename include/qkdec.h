@@ -240,9 +240,11 @@ qkdec_status qkdec_attn_decode(const qkdec_kv_layer* kv, const int32_t* slot, co
  * >= 32), any cache type, the layouts above per page.  pages: device int32
  * [B][max_pages]; token t of sequence b is in page pages[b * max_pages +
  * t / capacity] at position t % capacity.  max_pages * capacity <= 2^30.
- * Page entries a call reads must lie in [0, n_slots); an entry outside is
+ * Page entries attention reads must lie in [0, n_slots); an entry outside is
  * clamped into the pool (no fault; that sequence's result is then
- * meaningless).  Two sequences must not write the same page in one call.
+ * meaningless).  A store whose page entry lies outside [0, n_slots) (e.g. -1
+ * for a page not handed out) stores nothing and reports QKDEC_E_CAPACITY.
+ * Two sequences must not write the same page in one call.
  *
  * Attention: as qkdec_attn_decode, with n_ctx[b] clamped to max_pages *
  * capacity; workspace of at least qkdec_attn_paged_workspace_size() bytes. */

@@ -81,10 +81,12 @@ class PagePool:
         self._free.extend(reversed(pages))
 
     def table(self, seqs: Iterable, max_pages: int) -> np.ndarray:
-        """int32 [len(seqs), max_pages] page table; unused entries are 0 (never
-        read: a sequence's reads stop at its own length)."""
+        """int32 [len(seqs), max_pages] page table.  Unused entries are -1, so
+        a store into a page the sequence was not given (a step past its
+        reserved length) stores nothing and raises the library's capacity
+        error instead of writing into another sequence's page."""
         seqs = list(seqs)
-        out = np.zeros((len(seqs), max_pages), dtype=np.int32)
+        out = np.full((len(seqs), max_pages), -1, dtype=np.int32)
         for b, s in enumerate(seqs):
             p = self._pages[s]
             if len(p) > max_pages:

@@ -116,7 +116,7 @@ def test_paged_equals_arena_bitwise(qd, kind):
     cap = 1024
     cont = synth.kv_cache(kind, st.next(), st.next(), len(lens), hkv, cap, d, lens)
     pool, table, _ = _pool_from(cont, lens, P, 40, st.next())
-    table = np.pad(table, ((0, 0), (0, cap // P - table.shape[1])))
+    table = np.pad(table, ((0, 0), (0, cap // P - table.shape[1])), constant_values=-1)
     q = synth.f16_normal(st.next(), (len(lens), hq, d))
     got_p = _attn_paged(qd, upload_cache(pool), table, lens, q, 0.088)
     dkv = upload_cache(cont)
@@ -157,11 +157,15 @@ def test_paged_append_bit_exact(qd, kind):
             continue
         assert np.array_equal(getattr(got, name).view(np.uint8), w.view(np.uint8)), name
     assert int(err.cpu()[0]) == 0
-    # a position past the table stores nothing and raises the flag
-    qd.qkdec_kv_append_paged(dkv.desc, _dev(table), 3, _dev(np.array([192, 0, 0], np.int32)), _dev(k), _dev(v), 1,
-                             err=err)
-    sync()
-    assert int(err.cpu()[0]) == -5
+    # a position past the table, or in a page the sequence was not given (a -1
+    # entry), stores nothing and raises the flag
+    assert table[2, 1] == -1
+    for pos_bad, bb in (([192, 0, 0], 1), ([192, 192, 64], 3)):
+        err = _dev(np.zeros(1, np.int32))
+        qd.qkdec_kv_append_paged(dkv.desc, _dev(table), 3, _dev(np.array(pos_bad, np.int32)), _dev(k), _dev(v), bb,
+                                 err=err)
+        sync()
+        assert int(err.cpu()[0]) == -5, pos_bad
     after = dkv.logical()
     for name in ("k", "kq", "v", "vq", "kf8", "vf8"):
         if getattr(got, name, None) is not None:
@@ -215,7 +219,7 @@ def test_paged_step_equals_arena_step(qd, shape, kind, bsz, L, P, cap):
         pools.append(pool)
         table = t
     max_pages = cap // P
-    table = np.pad(table, ((0, 0), (0, max_pages - table.shape[1])))
+    table = np.pad(table, ((0, 0), (0, max_pages - table.shape[1])), constant_values=-1)
     dpools = [upload_cache(p) for p in pools]
     sm = qd.StepModel(dims, arena.embed, arena.lm_head, arena.norm, arena.layers, [d.desc for d in dpools])
     pos = _dev(np.full(bsz, L, np.int32))

@@ -12,7 +12,7 @@ def test_admit_grow_release_and_table():
     assert pool.reserve("b", 64) == [] and pool.reserve("b", 65) == [3]
     assert pool.length("b") == 65 and pool.free_pages == 4
     t = pool.table(["b", "a"], 4)
-    assert t.dtype == np.int32 and t.tolist() == [[2, 3, 0, 0], [0, 1, 0, 0]]
+    assert t.dtype == np.int32 and t.tolist() == [[2, 3, -1, -1], [0, 1, -1, -1]]
     pool.release("a")
     assert pool.free_pages == 6
     assert pool.admit("c", 128) == [0, 1]            # freed pages are reused
