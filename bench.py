@@ -50,13 +50,14 @@ def q4k_bytes(n, k):
     return n * (k // 256) * 144
 
 
-LAYER_Q4K = (q4k_bytes((HQ + 2 * HKV) * D, H) + q4k_bytes(H, HQ * D) + q4k_bytes(2 * FFN, H)
-             + q4k_bytes(H, FFN))
-W_BYTES = NL * LAYER_Q4K + VOCAB * H * 2 + (2 * NL + 1) * H * 4     # shared bytes read once per step
-KV_BYTES_PER_TOKEN = {"f16": NL * HKV * D * 2 * 2, "q8_0": NL * HKV * D * 2 * 34 // 32,
-                      # keys and values in different formats: one fp16 tensor, one Q8_0
-                      "q8k_f16v": NL * HKV * D * (2 + 34 / 32), "f16k_q8v": NL * HKV * D * (2 + 34 / 32),
-                      "fp8": NL * HKV * D * 2}
+def _byte_model():
+    from quantized_decode_amd import planner as P
+    w = P.model_weight_bytes(NL, H, HQ, HKV, D, FFN, VOCAB)          # shared bytes read once per step
+    k = {kind: P.kv_bytes_per_token(NL, HKV, D, kind) for kind in ("f16", "q8_0", "q8k_f16v", "f16k_q8v", "fp8")}
+    return w, k
+
+
+W_BYTES, KV_BYTES_PER_TOKEN = _byte_model()
 
 
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs (calibrated

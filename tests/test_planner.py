@@ -75,3 +75,15 @@ def test_fp8_doubles_the_crossover():
     # the per-token bytes and so doubles the crossover context
     w = M.weight_bytes(D)
     assert P.crossover_context(w, 8, _k("fp8")) == pytest.approx(2 * P.crossover_context(w, 8, _k("f16")))
+
+
+def test_bench_uses_the_planner_byte_model():
+    # the bench's per-step bytes (W and k per cache kind) are the planner's and
+    # the oracle's: 5,152,849,920 B of weights, 147,456 / 78,336 / 73,728 B per token
+    import bench
+    assert bench.W_BYTES == M.weight_bytes(D) == 5152849920
+    assert bench.KV_BYTES_PER_TOKEN["f16"] == 147456
+    assert bench.KV_BYTES_PER_TOKEN["q8_0"] == 78336
+    assert bench.KV_BYTES_PER_TOKEN["fp8"] == 73728
+    for kind in ("f16", "q8_0", "fp8"):
+        assert bench.KV_BYTES_PER_TOKEN[kind] == M.kv_bytes_per_token(D, kind)
