@@ -1,5 +1,5 @@
-// Split-K flash-decode GQA attention over a slot-arena KV cache: fp16, Q8_0,
-// mixed, or E4M3 keys and values.
+// Split-K flash-decode GQA attention over a slot-arena KV cache or a paged
+// pool: fp16, Q8_0, mixed, or E4M3 keys and values.
 // (P1, P2, P3: the three pages listed, with their titles, at the top of include/qkdec.h.)
 //
 // P2 "The two halves of a decode-step memory bill": each sequence reads its

@@ -106,9 +106,10 @@ inline bool kv_v_q8(int type) { return kv_v_fmt(type) == kFmtQ8; }
 // ---- attention (attn_decode.hip)
 // A sequence's n cached tokens (ceil(n/32) tiles of 32) are cut into runs of
 // whole tiles, spread evenly, one work item each.  Runs per sequence: enough
-// that the B * n_kv * runs work items reach the target (fp16 cache: 256, one
-// per CU of MI355X; Q8_0: 512, its dequantizing tiles gaining from a second
-// work-group per CU; both kernels run two waves per SIMD), at least
+// that the B * n_kv * runs work items reach the target (fp16 and E4M3 caches:
+// 256, one per CU of MI355X; any Q8_0 tensor: 512, its dequantizing tiles
+// gaining from a second work-group per CU; the kernels run two waves per
+// SIMD), at least
 // ceil(n / kAttnChunk) (long contexts), at most one per 8 tiles (4 waves of 2
 // tiles at least) and at most attn_max_runs (the partial-result stride).
 // kAttnChunk = 1024: longer-lived waves were faster than 256 or 512 tokens
