@@ -354,54 +354,6 @@ __device__ void qkv_finish(const WkArgs& a, Red red, int wave, int lane, int g, 
   c.k = ra.k; c.v = ra.v; c.ks = ra.ks; c.vs = ra.vs;
   c.n_kv = ra.n_kv; c.cap = ra.cap; c.D = D; c.n_slots = ra.n_slots; c.kf = ra.kf; c.vf = ra.vf;
   const int kvh = is_v ? head - ra.Hq - ra.n_kv : head - ra.Hq;
-  if ((is_v ? ra.vf : ra.kf) == kFmtQ8) {   // uniform: one head per work-group
-    // A Q8_0 block is 32 dims: tile T of this wave and tile T ^ 1, which the
-    // same wave of work-group hj ^ 1 finishes.  Each wave stores its values
-    // through to the device-coherent level and counts itself in; the second
-    // of the pair to arrive takes the block maximum over both halves and
-    // stores the codes of all 32 dims and the block scale.
-    const int T = hj + a.qh * wave;
-    const int unit = (head - ra.Hq) * 2 * a.qh + T;               // (kv or v head, tile)
-    float* mine = a.part + (size_t)unit * 256;                     // [16 rows][16 dims]
-    const float* other = a.part + (size_t)(unit ^ 1) * 256;
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
-      __hip_atomic_store(&mine[(4 * g + ii) * 16 + r], out[ii], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);
-    unsigned* ctr = a.counters + (unit >> 1);
-    unsigned prev = 0;
-    if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    prev = __shfl(prev, 0);
-    if (prev == 0u) return;   // the partner finishes the block
-    if (lane == 0) *ctr = 0u;
-    float pv[4];
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
-      pv[ii] = __hip_atomic_load(&other[(4 * g + ii) * 16 + r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int dp = 16 * (T ^ 1) + r;   // the partner's dim of this lane
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      float m = fmaxf(fabsf(out[ii]), fabsf(pv[ii]));
-      m = fmaxf(m, __shfl_xor(m, 1));
-      m = fmaxf(m, __shfl_xor(m, 2));
-      m = fmaxf(m, __shfl_xor(m, 4));
-      m = fmaxf(m, __shfl_xor(m, 8));
-      const int b = 4 * g + ii;
-      if (b >= a.B) continue;
-      const bool ok = sl[ii] >= 0 && sl[ii] < ra.n_slots && ps[ii] >= 0 && ps[ii] < ra.cap;
-      if (!ok) {
-        if (r == 0) *ra.err = QKDEC_E_CAPACITY;
-        continue;
-      }
-      int8_t q;
-      uint16_t dbits;
-      q8_encode((double)out[ii], (double)m, q, dbits);
-      store_q8(c, is_v, sl[ii], kvh, ps[ii], d, q, dbits);
-      q8_encode((double)pv[ii], (double)m, q, dbits);
-      store_q8(c, is_v, sl[ii], kvh, ps[ii], dp, q, dbits);
-    }
-    return;
-  }
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii) {
     const int b = 4 * g + ii;
@@ -964,7 +916,8 @@ hipError_t launch_gemm_wi(const GemmLaunch& L, hipStream_t st) {
 // (head, half-head tile).  hipErrorNotSupported for any other case.
 hipError_t launch_gemm_wi_qkv(const GemmLaunch& L, const RopeAppendArgs& ra, int head_dim, hipStream_t st) {
   const int kb = (int)(L.K / 256);
-  if (kb != 16 || !L.x_f32 || !L.gamma || (head_dim != 64 && head_dim != 128) || L.residual ||
+  if (kb != 16 || !L.x_f32 || !L.gamma || ra.kf == kFmtQ8 || ra.vf == kFmtQ8 || (head_dim != 64 && head_dim != 128) ||
+      L.residual ||
       L.ss_out)
     return hipErrorNotSupported;
   WkArgs a{};
@@ -983,12 +936,6 @@ hipError_t launch_gemm_wi_qkv(const GemmLaunch& L, const RopeAppendArgs& ra, int
   a.inv_k = 1.0f / (float)L.K;
   a.ra = ra;
   a.qh = head_dim / 32;
-  // Q8_0 heads: the pair exchange of the finish (arrival counters, then one
-  // [16][16] fp32 block of values per (kv or v head, tile)) in the workspace
-  char* p = reinterpret_cast<char*>(L.ws);
-  a.counters = reinterpret_cast<unsigned*>(p);
-  a.part = reinterpret_cast<float*>(p + (size_t)kGemmMaxGroups * 4);
-  if ((ra.kf == kFmtQ8 || ra.vf == kFmtQ8) && !L.ws) return hipErrorNotSupported;
   const int n_heads = (int)(L.n_rows / head_dim);
   hipLaunchKernelGGL((gemm_wi_kernel<2, kXNorm, 16, 1, 2, 2>), dim3((unsigned)(n_heads * a.qh)), dim3(1024), 0, st, a);
   return hipGetLastError();

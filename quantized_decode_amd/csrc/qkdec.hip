@@ -137,9 +137,6 @@ StepWs step_layout(const qkdec_model* m, int B, const qkdec_kv_layer* kv, char* 
   g = std::max(g, gemm_workspace_bytes(m->hidden, hq, B, false));
   g = std::max(g, gemm_workspace_bytes(2 * (int64_t)m->ffn, m->hidden, B, true));
   g = std::max(g, gemm_workspace_bytes(m->hidden, m->ffn, B, false));
-  // the QKV finish's Q8_0 pair exchange: arrival counters, then a [16][16]
-  // fp32 block per (kv or v head, 16-row tile)
-  g = std::max(g, (size_t)kGemmMaxGroups * 4 + (size_t)2 * m->n_kv_heads * (2 * (m->head_dim / 32)) * 256 * 4);
   w.gemm_ws = take(g);
   w.bytes = off;
   return w;
@@ -181,9 +178,9 @@ qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int3
     ra.n_kv = kv[l].n_kv_heads; ra.cap = kv[l].capacity; ra.n_slots = kv[l].n_slots; ra.Hq = Hq;
     ra.kf = kv_k_fmt(kv[l].type); ra.vf = kv_v_fmt(kv[l].type); ra.rope_base = m->rope_base; ra.q16 = w.q16; ra.err = w.err;
     // K = 4096: the resident multi-item projection, finishing each head slice
-    // itself (Q8_0 blocks through a pair exchange between the two work-groups
-    // that hold a block's halves); otherwise the split-K projection finishes
-    // each head
+    // itself (fp16 or E4M3 cache) or followed by RoPE and the append as a small launch
+    // (Q8_0 blocks span two work-groups); otherwise the split-K projection
+    // finishes each head
     hipError_t eq = launch_gemm_wi_qkv(qkv, ra, D, st);
     if (eq == hipErrorNotSupported) {
       eq = launch_gemm_wi(qkv, st);
