@@ -188,19 +188,45 @@ __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs
 // the merge costs one memory round trip (the running maximum is rescaled
 // between batches).
 constexpr int kMergeBatch = 8;
+// paged: slot holds no slots (any readable int32[B]; its values are ignored).
 __global__ void attn_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
-                                    int n_splits, int runs_wanted, const int32_t* slot, const int32_t* n_ctx,
-                                    int n_ctx_add, int cap, int n_slots, int Hq, int D, float* O, half_t* O16) {
+                                    int n_splits, int runs_wanted, const int32_t* slot, int paged,
+                                    const int32_t* n_ctx, int n_ctx_add, int cap, int n_slots, int Hq, int D,
+                                    float* O, half_t* O16) {
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const size_t row0 = ((size_t)b * Hq + h) * n_splits;
+  // The first batch of run states is loaded before the run count is known
+  // (rows row0 .. row0 + min(kMergeBatch, n_splits) - 1 always lie in the
+  // partial area; rows past the count are never used), so the count's loads
+  // and the states' loads make one memory round trip, not two.
+  float m[kMergeBatch], l[kMergeBatch], o[kMergeBatch];
+#pragma unroll
+  for (int j = 0; j < kMergeBatch; ++j) {
+    const size_t row = row0 + (j < n_splits ? j : 0);
+    m[j] = part_ml[2 * row];
+    l[j] = part_ml[2 * row + 1];
+    o[j] = part_o[row * D + d];
+  }
+  __asm__ volatile("" ::: "memory");   // keep the loads above ahead of the run count's
   int n = n_ctx[b] + n_ctx_add;
   if (n > cap) n = cap;               // cap: the most tokens a sequence holds
-  const int s = slot ? slot[b] : 0;   // no slot for a paged pool
-  if (n < 0 || (slot && (s < 0 || s >= n_slots))) n = 0;
+  const int s = slot[b];   // unconditional: no branch ahead of the loads above
+  if (n < 0 || (!paged && (s < 0 || s >= n_slots))) n = 0;
   const int ns = attn_runs(n, runs_wanted, n_splits);
-  const size_t row0 = ((size_t)b * Hq + h) * n_splits;
-  float num = 0.f, den = 0.f, big = -__builtin_inff();
-  for (int j0 = 0; j0 < ns; j0 += kMergeBatch) {
-    float m[kMergeBatch], l[kMergeBatch], o[kMergeBatch];
+  // first batch: selects rather than branches, so that its loads stay
+  // unconditional and go out together with those of the run count (the
+  // values equal the branchy form: fmax with -inf and additions of +0)
+  float big = -__builtin_inff();
+#pragma unroll
+  for (int j = 0; j < kMergeBatch; ++j) big = fmaxf(big, j < ns ? m[j] : -__builtin_inff());
+  float num = 0.f, den = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMergeBatch; ++j) {
+    const float w = exp2f(m[j] - big);
+    den += j < ns ? w * l[j] : 0.f;
+    num += j < ns ? w * o[j] : 0.f;
+  }
+  for (int j0 = kMergeBatch; j0 < ns; j0 += kMergeBatch) {
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
       const size_t row = row0 + (j0 + j < ns ? j0 + j : j0);
@@ -212,7 +238,7 @@ __global__ void attn_combine_kernel(const float* __restrict__ part_o, const floa
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j)
       if (j0 + j < ns) nb = fmaxf(nb, m[j]);
-    const float fr = j0 > 0 ? exp2f(big - nb) : 0.f;
+    const float fr = exp2f(big - nb);
     num *= fr;
     den *= fr;
     big = nb;
@@ -284,8 +310,8 @@ hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, con
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(n_q_heads, B), dim3(D), 0, st, a.part_o, a.part_ml, a.n_splits,
-                     a.runs_wanted, pages ? nullptr : slot, n_ctx, n_ctx_add, a.seq_cap, kv.n_slots, n_q_heads, D, O,
-                     reinterpret_cast<half_t*>(O16));
+                     a.runs_wanted, pages ? n_ctx : slot, pages ? 1 : 0, n_ctx, n_ctx_add, a.seq_cap, kv.n_slots,
+                     n_q_heads, D, O, reinterpret_cast<half_t*>(O16));
   return hipGetLastError();
 }
 
