@@ -67,11 +67,11 @@ W_BYTES, KV_BYTES_PER_TOKEN = _byte_model()
 # profiles/decode_step_b8_l6900_fp8_kernel_stats.md.  A kernel changed since
 # has no entry, and its traffic is reported as null.
 COUNTED_TRAFFIC = {
-    # split kernel 79,173,829 fetched + 557,056 written; merge 617,800 + 65,536
+    # split kernel 79,424,996 fetched + 557,056 written; merge 1,145,766 + 65,536
     # (fetched and written each rounded once over split + merge)
-    ("attention (split + merge)", 8, 2400, "f16"): 80_414_221,
-    # E4M3 cache: split 113,885,297 fetched + 971,848 written; merge 973,676 + 65,536
-    ("attention (split + merge)", 8, 6900, "fp8"): 115_896_357,
+    ("attention (split + merge)", 8, 2400, "f16"): 81_193_354,
+    # E4M3 cache: split 113,534,512 fetched + 974,848 written; merge 1,146,026 + 65,536
+    ("attention (split + merge)", 8, 6900, "fp8"): 115_720_922,
 }
 
 
@@ -167,7 +167,9 @@ def time_paged_step(qd, sd, dims, dev_model, batch, length, kind, steps, warmup,
                 per.append(a.elapsed_time(b))
     status = qd.qkdec_step_status(ws)
     assert status == 0, f"paged step reported status {status}"
-    assert int(pos[0].item()) == length + 1 + warmup + steps
+    got = pos.cpu().tolist()
+    want = length + 1 + warmup + steps
+    assert all(x == want for x in got), f"paged step: positions {got}, expected {want}"
     del graph
     return per
 
@@ -450,6 +452,7 @@ def main():
     ap.add_argument("--kv", choices=["f16", "q8_0", "q8k_f16v", "f16k_q8v", "fp8"], default="f16")
     ap.add_argument("--points", choices=["all", "main"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-paged", action="store_true", help="skip the paged-pool step beside the main point")
     ap.add_argument("--no-clocks", action="store_true",
                     help="do not query rocm-smi (for runs under a profiler, whose preload the child would inherit)")
     ap.add_argument("--sweep", action="store_true", help="context x batch x cache sweep (see above)")
@@ -515,7 +518,7 @@ def main():
                         "tok_per_s": bsz / (ms * 1e-3), "bytes_per_step": step_bytes, "achieved_GBps": gbps,
                         "frac_of_8TBps": gbps / PEAK_HBM_GBPS, "wall_s": wall})
         log(f"  {ms:.3f} ms/step, {bsz / (ms * 1e-3):.1f} tok/s, {gbps:.0f} GB/s on the byte model")
-        if i == 0:
+        if i == 0 and not args.no_paged:
             log("the same point's step over paged pools (pages of 256)")
             pper = time_paged_step(qd, sd, dims, dev_model, bsz, L, kind, min(args.steps, 16), args.warmup, 8000)
             pms = sum(pper) / len(pper)
@@ -525,6 +528,7 @@ def main():
                              "timed right after the arena step of the same point"}
             log(f"  paged: {pms:.3f} ms/step ({pms / ms:.3f} x the arena step)")
             torch.cuda.empty_cache()
+        if i == 0:
             log("per-kernel timing (HIP events on the launching stream)")
             kernels = kernel_timing(qd, sd, dev_model, sm, bsz, L, 4000)
         del sm
