@@ -193,6 +193,7 @@ STEP_CASES = [
     ("toy", "fp8", 2, 128, 32, 160),
     ("full", "f16", 4, 300, 64, 320),
     ("full", "q8_0", 4, 300, 64, 320),
+    ("full", "fp8", 4, 300, 64, 320),
 ]
 
 

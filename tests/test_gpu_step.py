@@ -299,7 +299,7 @@ def test_full_width_step_stagewise(qd, kind):
     assert torch.equal(g.kv[0].k[:, :, L], k0), "layer 0 re-appended different keys"
 
 
-@pytest.mark.parametrize("bsz,kind", [(1, "f16"), (16, "f16"), (16, "q8_0")])
+@pytest.mark.parametrize("bsz,kind", [(1, "f16"), (16, "f16"), (16, "q8_0"), (16, "fp8")])
 def test_full_width_step_stagewise_batch_sizes(qd, bsz, kind):
     # the Qwen-shaped layer at the ends of the batch range: B = 1 and B = 16 (the
     # projections stage rows 8..15 in a second pass), one layer, L = 300,
