@@ -60,19 +60,60 @@ def _byte_model():
 W_BYTES, KV_BYTES_PER_TOKEN = _byte_model()
 
 
-# HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs (calibrated
-# against a plain 1 GiB copy: fetched = 2.0 x FETCH_SIZE, written = 1.0 x
-# WRITE_SIZE), keyed by the kernels as they were when counted; see
-# profiles/decode_step_b8_l2400_f16_kernel_stats.md and
-# profiles/decode_step_b8_l6900_fp8_kernel_stats.md.  A kernel changed since
-# has no entry, and its traffic is reported as null.
-COUNTED_TRAFFIC = {
-    # split kernel 79,424,996 fetched + 557,056 written; merge 1,145,766 + 65,536
-    # (fetched and written each rounded once over split + merge)
-    ("attention (split + merge)", 8, 2400, "f16"): 81_193_354,
-    # E4M3 cache: split 113,534,512 fetched + 974,848 written; merge 1,146,026 + 65,536
-    ("attention (split + merge)", 8, 6900, "fp8"): 115_720_922,
-}
+# HBM bytes per launch counted by rocprofv3 (FETCH_SIZE and WRITE_SIZE runs,
+# calibrated against a plain 1 GiB copy) live in profiles/counted_traffic.json,
+# written by `bench.py --traffic-from ...` together with the build id of the
+# library the counters ran on.  They are used only while the loaded library
+# has that build id: once a kernel source changes, the figure is stale and
+# the bench reports traffic as null.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "counted_traffic.json")
+
+# the kernels (demangled-name prefixes) behind each kernel kind of the bench,
+# by KV cache kind where the kernel depends on it
+_ATTN_FMT = {"f16": (0, 0), "q8_0": (1, 1), "q8k_f16v": (1, 0), "f16k_q8v": (0, 1), "fp8": (2, 2)}
+
+
+def kind_kernels(name, kv):
+    if name.startswith("attention (split + merge)"):
+        kf, vf = _ATTN_FMT[kv]
+        return [f"void qk::attn_split_kernel<128, {kf}, {vf}, false>", "qk::attn_combine_kernel"]
+    if name == "lm_head_argmax":
+        return ["qk::lm_head_kernel", "qk::lm_argmax_reduce_kernel"]
+    return None
+
+
+def compute_dtype(kv):
+    """Arithmetic type of the path: every contraction (Q4_K GEMMs, attention,
+    LM head) runs as fp16 MFMA with fp32 accumulation; the weights (Q4_K) and
+    the cache (fp16, Q8_0, E4M3) are storage formats decoded exactly to fp16
+    in the kernels, so the arithmetic is f16 whatever `kv` is."""
+    assert kv in _ATTN_FMT
+    return "f16"
+
+
+def counted_traffic(qd, name, batch, context, kv):
+    """Counted HBM bytes per launch of kernel kind `name` at this point, or
+    None when no count was taken on this build of the library."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("build_id") != qd.qkdec_build_id():
+        return None
+    cfg = rec.get("config", {})
+    if (cfg.get("batch"), cfg.get("context"), cfg.get("kv")) != (batch, context, kv):
+        return None
+    names = kind_kernels(name, kv)
+    if not names:
+        return None
+    total = 0.0
+    for prefix in names:
+        hits = [v for k, v in rec["kernels"].items() if k.startswith(prefix)]
+        if len(hits) != 1:
+            return None
+        total += hits[0]["fetched_bytes"] + hits[0]["written_bytes"]
+    return int(round(total))
 
 
 def log(msg):
@@ -120,7 +161,9 @@ def time_point(qd, sm, batch, length, steps, warmup, vocab, seed):
     status = qd.qkdec_step_status(ws)
     plan.destroy()
     assert status == 0, f"step reported status {status}"
-    assert int(pos[0].item()) == length + warmup + steps
+    got = pos.cpu().tolist()
+    want = length + warmup + steps
+    assert all(x == want for x in got), f"step: positions {got}, expected {want} (one per replay)"
     return per, wall
 
 
@@ -149,6 +192,9 @@ def time_paged_step(qd, sd, dims, dev_model, batch, length, kind, steps, warmup,
     ws = torch.zeros(qd.qkdec_step_paged_workspace_size(sm, batch, max_pages), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.Stream()
     run = lambda: qd.qkdec_step_paged(sm, table, max_pages, pos, tok, batch, ws, stream=stream)
+    # the pools, table, positions and workspace were written on the default
+    # stream: they must be complete before the side stream reads them
+    torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         run()                                   # one eager step (pos advances)
     torch.cuda.synchronize()
@@ -179,6 +225,7 @@ def _timed(calls, stream, replays=5):
     order into one HIP graph on `stream` and replayed between HIP events on
     that stream, so host launch gaps are not counted; median over `replays`."""
     import torch
+    torch.cuda.synchronize()                         # inputs and workspaces were made on the default stream
     with torch.cuda.stream(stream):
         calls[0]()                                   # first launch of the kernel: not timed
     torch.cuda.synchronize()
@@ -296,6 +343,126 @@ def kernel_timing(qd, sd, dev_model, sm, batch, length, seed):
         v["GBps"] = v["bytes_per_launch"] / (v["avg_ms"] * 1e-3) / 1e9
         v["ms_per_step"] = v["avg_ms"] * v["launches_per_step"]
     return out
+
+
+def gemm_pass(qd, sd, dev_model, batches, seed, replays=5):
+    """The standalone batched Q4_K GEMM workload: one pass = the four
+    projections of all 36 layers (QKV 6144x4096, O 4096x4096, gate|up
+    24576x4096, down 4096x12288), each a qkdec_gemm_q4k call with fp16 N(0,1)
+    activations of B rows and fp32 outputs, over every layer's own weights
+    (3.9 GB, far beyond the last-level cache).  Captured in one HIP graph and
+    replayed between HIP events on the launching stream."""
+    import torch
+    embed, lm_head, norm, layers = dev_model
+    g = sd.generator(seed)
+    shapes = [("w_qkv", (HQ + 2 * HKV) * D, H), ("w_o", H, HQ * D), ("w_gate_up", 2 * FFN, H), ("w_down", H, FFN)]
+    wbytes = sum(q4k_bytes(n, k) for _, n, k in shapes) * len(layers)
+    stream = torch.cuda.Stream()
+    rows = []
+    for bsz in batches:
+        xs = {k: sd.f16_normal(g, (bsz, k)) for k in {k for _, _, k in shapes}}
+        ys = {n: torch.empty((bsz, n), dtype=torch.float32, device="cuda") for n in {n for _, n, _ in shapes}}
+        wsz = max(qd.qkdec_gemm_q4k_workspace_size(n, k, bsz) for _, n, k in shapes)
+        ws = torch.zeros(wsz, dtype=torch.uint8, device="cuda")
+        calls = [lambda ly=ly, nm=nm, n=n, k=k: qd.qkdec_gemm_q4k(ly[nm], n, k, xs[k], bsz, ys[n], workspace=ws,
+                                                                   stream=stream)
+                 for ly in layers for nm, n, k in shapes]
+        ms = _timed(calls, stream, replays=replays) * len(calls)
+        nbytes = wbytes + len(layers) * sum(bsz * (2 * k + 4 * n) for _, n, k in shapes)
+        rows.append({"batch": bsz, "ms_per_pass": ms, "bytes_per_pass": nbytes,
+                     "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_of_8TBps": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                     "weight_GBps": wbytes / (ms * 1e-3) / 1e9})
+        log(f"  GEMM pass B={bsz}: {ms:.3f} ms, {rows[-1]['GBps']:.0f} GB/s")
+        del xs, ys, ws
+    return {"workload": "36 layers x {QKV 6144x4096, O 4096x4096, gate|up 24576x4096, down 4096x12288} Q4_K, "
+                        "fp16 activations, fp32 out (qkdec_gemm_q4k)", "weight_bytes_per_pass": wbytes,
+            "points": rows}
+
+
+def attention_pass(qd, sd, batch, contexts, ragged_seed, seed, kind="f16", replays=5):
+    """The standalone flash-decode workload: one pass = qkdec_attn_decode over
+    36 per-layer caches (32 query / 8 KV heads of 128, fp16 q, K, V N(0,1),
+    scale 1/sqrt(128)), B sequences of L cached tokens each, or of ragged
+    lengths uniform in 512..8192 (seeded); graph-timed like gemm_pass."""
+    import numpy as np
+    import torch
+    from quantized_decode_amd import KV_KINDS, kv_layer
+    g = sd.generator(seed)
+    stream = torch.cuda.Stream()
+    kvb = KV_BYTES_PER_TOKEN[kind] / NL
+    rows = []
+    cases = [("L=%d" % L, [L] * batch) for L in contexts]
+    if ragged_seed is not None:
+        lens = np.random.default_rng(ragged_seed).integers(512, 8193, size=batch)
+        cases.append(("ragged U{512..8192}", [int(x) for x in lens]))
+    for label, lens in cases:
+        cap = (max(lens) + 31) // 32 * 32
+        kvs, keep = [], []
+        for _ in range(NL):
+            k, v, ks, vs = sd.kv_cache(g, kind, batch, HKV, cap, D, cap)
+            keep.append((k, v, ks, vs))
+            kvs.append(kv_layer(KV_KINDS[kind], HKV, D, cap, batch, k, v, ks, vs))
+        q = sd.f16_normal(g, (batch, HQ, D))
+        o = torch.empty((batch, HQ, D), dtype=torch.float16, device="cuda")
+        slot = torch.arange(batch, dtype=torch.int32, device="cuda")
+        nctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        aws = torch.zeros(qd.qkdec_attn_workspace_size(batch, HQ, kvs[0]), dtype=torch.uint8, device="cuda")
+        calls = [lambda kv=kv: qd.qkdec_attn_decode(kv, slot, nctx, batch, q, HQ, D ** -0.5, o16=o, workspace=aws,
+                                                    stream=stream) for kv in kvs]
+        ms = _timed(calls, stream, replays=replays) * len(calls)
+        nbytes = sum(lens) * kvb * NL
+        rows.append({"case": label, "batch": batch, "lengths": lens, "ms_per_pass": ms, "bytes_per_pass": nbytes,
+                     "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_of_8TBps": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS})
+        log(f"  attention pass {label}: {ms:.3f} ms, {rows[-1]['GBps']:.0f} GB/s")
+        del kvs, keep, aws
+        torch.cuda.empty_cache()
+    return {"workload": f"36 layers x qkdec_attn_decode, 32/8 heads x 128, {kind} KV, B={batch}", "points": rows}
+
+
+def record_traffic(qd, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mb, batch, context, kv, command):
+    """Write profiles/counted_traffic.json from four rocprofv3 counter runs
+    (FETCH_SIZE and WRITE_SIZE of the bench, and of `--copy-probe-mb copy_mb`
+    for the calibration), stamped with the loaded library's build id."""
+    import csv
+    import glob
+    import subprocess
+
+    def load(d):
+        paths = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if len(paths) != 1:
+            raise SystemExit(f"expected one counter CSV under {d}, found {paths}")
+        agg = {}
+        with open(paths[0]) as fh:
+            for r in csv.DictReader(fh):
+                agg.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        names = list(agg)
+        out = subprocess.run(["c++filt"], input="\n".join(names), capture_output=True, text=True).stdout.split("\n")
+        return {dm or nm: sum(v) / len(v) for nm, dm, v in zip(names, out, agg.values())}
+
+    def copy_kib(d):
+        vals = [v for k, v in load(d).items() if "copyBuffer" in k]
+        if not vals:
+            raise SystemExit(f"no copy kernel in {d}")
+        return max(vals)
+
+    nbytes = copy_mb << 20
+    f_cal = nbytes / (copy_kib(copy_fetch_dir) * 1024)
+    w_cal = nbytes / (copy_kib(copy_write_dir) * 1024)
+    fetch, write = load(fetch_dir), load(write_dir)
+    kernels = {}
+    for name, kib in fetch.items():
+        if not name.startswith(("qk::", "void qk::")):
+            continue
+        kernels[name] = {"fetched_bytes": kib * 1024 * f_cal, "written_bytes": write.get(name, 0.0) * 1024 * w_cal,
+                         "fetch_size_kib": kib, "write_size_kib": write.get(name, 0.0)}
+    rec = {"build_id": qd.qkdec_build_id(), "config": {"batch": batch, "context": context, "kv": kv},
+           "calibration": {"copy_bytes": nbytes, "fetched_per_fetch_size_byte": f_cal,
+                           "written_per_write_size_byte": w_cal},
+           "command": command, "kernels": kernels}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(rec, fh, indent=1, sort_keys=True)
+    print(json.dumps({"wrote": TRAFFIC_FILE, "build_id": rec["build_id"], "kernels": len(kernels),
+                      "calibration": rec["calibration"]}))
 
 
 def read_ceiling(gib=4):
@@ -461,7 +628,18 @@ def main():
     ap.add_argument("--sweep-contexts", default="32,2400,4700,6900,16000,32000")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run 3 plain device copies of this many MiB (calibrates the HBM byte counters)")
+    ap.add_argument("--no-passes", action="store_true",
+                    help="skip the standalone GEMM-pass and attention-pass measurements")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write profiles/counted_traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of "
+                         "this bench (--points main at --batch/--context/--kv) and of --copy-probe-mb; no GPU work")
+    ap.add_argument("--traffic-command", default="", help="the profiled command, recorded with --traffic-from")
     args = ap.parse_args()
+    if args.traffic_from:
+        import quantized_decode_amd as qd
+        record_traffic(qd, *args.traffic_from, args.copy_probe_mb or 1024, args.batch, args.context, args.kv,
+                       args.traffic_command)
+        return
     if args.copy_probe_mb:
         import torch
         n = args.copy_probe_mb << 20
@@ -537,11 +715,19 @@ def main():
     main_pt = results[0]
     dom_name, dom = max(kernels.items(), key=lambda kv: kv[1]["ms_per_step"])
     achieved = dom["bytes_per_launch"] / (dom["avg_ms"] * 1e-3) / 1e9
-    traffic = COUNTED_TRAFFIC.get((dom_name, main_pt["batch"], main_pt["context"], main_pt["kv"]))
+    traffic = counted_traffic(qd, dom_name, main_pt["batch"], main_pt["context"], main_pt["kv"])
     roofline = {"kernel": dom_name, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic, "avg_launch_ms": dom["avg_ms"],
                 "algorithmic_bytes_per_launch": dom["bytes_per_launch"],
                 "launches_per_step": dom["launches_per_step"]}
+
+    passes = None
+    if not args.no_passes:
+        log("standalone GEMM pass (fp16 activations, B = 1, 2, 4, 8, 16)")
+        passes = {"gemm": gemm_pass(qd, sd, dev_model, [1, 2, 4, 8, 16], 9000)}
+        log("standalone attention pass (B = 8, L = 2400 / 4700 / 6900 and ragged)")
+        passes["attention"] = attention_pass(qd, sd, 8, [2400, 4700, 6900], 4242, 9100)
+        torch.cuda.empty_cache()
 
     log("streaming-read ceiling (4 GiB) and clocks")
     ceiling = read_ceiling()
@@ -557,7 +743,7 @@ def main():
         "metric": "aggregate decode tok/s at B=8, L=2.4k/6.9k; achieved HBM GB/s vs peak",
         "value": main_pt["tok_per_s"], "unit": "tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": main_pt["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f16", "data": "synthetic",
+        "dtype": compute_dtype(main_pt["kv"]), "data": "synthetic",
         "config": {"workload": f"batched decode step, Qwen-shaped synthetic decoder (36 layers, hidden 4096, "
                                f"32/8 heads x 128, FFN 12288, vocab 151936), Q4_K weights, {main_pt['kv']} KV, "
                                f"B={main_pt['batch']}, L={main_pt['context']}",
@@ -565,7 +751,8 @@ def main():
         "achieved_GBps": main_pt["achieved_GBps"], "frac_of_8TBps": main_pt["frac_of_8TBps"],
         "frac_of_read_ceiling": main_pt["frac_of_read_ceiling"], "read_ceiling": ceiling,
         "clocks": None if args.no_clocks else clocks(),
-        "roofline": roofline, "kernels": kernels, "points": results, "paged_step": paged, "cpu_baseline": cpu,
+        "roofline": roofline, "kernels": kernels, "points": results, "paged_step": paged, "passes": passes,
+        "cpu_baseline": cpu, "library_build_id": qd.qkdec_build_id(),
     }
     print(json.dumps(out))
 

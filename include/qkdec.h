@@ -82,6 +82,10 @@ enum {
 const char* qkdec_status_str(qkdec_status s);
 /* QKDEC_ABI_VERSION of the built library. */
 int32_t qkdec_abi_version(void);
+/* Identifier of the sources the library was built from (a hash of its HIP
+ * sources, headers and compiler flags; static string), so that a measurement
+ * recorded with one build is recognised as stale under another. */
+const char* qkdec_build_id(void);
 
 /* ------------------------------------------------------------------ GEMM ---
  * Y[b][n] = residual[b][n] + sum_k W[n][k] * X[b][k]   for b < B, n < N.
@@ -240,11 +244,11 @@ qkdec_status qkdec_attn_decode(const qkdec_kv_layer* kv, const int32_t* slot, co
  * >= 32), any cache type, the layouts above per page.  pages: device int32
  * [B][max_pages]; token t of sequence b is in page pages[b * max_pages +
  * t / capacity] at position t % capacity.  max_pages * capacity <= 2^30.
- * Page entries attention reads must lie in [0, n_slots); an entry outside is
- * clamped into the pool (no fault; that sequence's result is then
- * meaningless).  A store whose page entry lies outside [0, n_slots) (e.g. -1
- * for a page not handed out) stores nothing and reports QKDEC_E_CAPACITY.
- * Two sequences must not write the same page in one call.
+ * A page entry outside [0, n_slots) (e.g. -1 for a page not handed out) maps
+ * nothing: attention leaves the tokens it would hold out of the softmax (a
+ * sequence with no mapped token among its first n_ctx gets O = 0; nothing
+ * outside the pool is read), and a store to it stores nothing and reports
+ * QKDEC_E_CAPACITY.  Two sequences must not write the same page in one call.
  *
  * Attention: as qkdec_attn_decode, with n_ctx[b] clamped to max_pages *
  * capacity; workspace of at least qkdec_attn_paged_workspace_size() bytes. */

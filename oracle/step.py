@@ -81,12 +81,20 @@ def kv_read(cache, kind: str, slot: int, n: int):
     return out[0], out[1]
 
 
+def _attend(q: np.ndarray, kd: np.ndarray, vd: np.ndarray, scale: float) -> np.ndarray:
+    """attention() of one sequence; a sequence with no cached token gets O = 0."""
+    if kd.shape[1] == 0:
+        return np.zeros(q.shape, dtype=np.float64)
+    return attention(q, kd, vd, scale)
+
+
 def attention_batch(q: np.ndarray, cache, kind: str, slots, n_ctx, scale: float) -> np.ndarray:
-    """Standalone decode attention: q [B, Hq, D] against n_ctx[b] cached tokens of slot[b]."""
+    """Standalone decode attention: q [B, Hq, D] against n_ctx[b] cached tokens
+    of slot[b] (n_ctx[b] <= 0: O = 0)."""
     out = np.empty(q.shape, dtype=np.float64)
     for b in range(q.shape[0]):
-        kd, vd = kv_read(cache, kind, int(slots[b]), int(n_ctx[b]))
-        out[b] = attention(q[b], kd, vd, scale)
+        kd, vd = kv_read(cache, kind, int(slots[b]), max(0, int(n_ctx[b])))
+        out[b] = _attend(q[b], kd, vd, scale)
     return out
 
 
@@ -95,35 +103,54 @@ def attention_batch(q: np.ndarray, cache, kind: str, slots, n_ctx, scale: float)
 # admitted and released between decode steps).  A pool is a cache object of
 # the layout above whose "slots" are pages of page_tokens positions each;
 # sequence b's token t lives in page pages[b][t // page_tokens] at offset
-# t % page_tokens.
+# t % page_tokens.  A table entry outside the pool (-1: no page handed out)
+# maps nothing: the tokens it would hold are not part of the sequence's
+# context (reading skips them, a store to them is dropped).
+
+
+def _pool_pages(pool) -> int:
+    for name in ("k", "kq", "kf8"):
+        arr = getattr(pool, name, None)
+        if arr is not None:
+            return arr.shape[0]
+    raise ValueError("pool without keys")
 
 
 def kv_read_paged(pool, kind: str, pages, page_tokens: int, n: int):
-    """Keys and values of the first n tokens of a paged sequence, fp64 [n_kv, n, D]."""
-    if n <= 0:
-        k0, v0 = kv_read(pool, kind, 0, 0)
-        return k0, v0
-    ks, vs = [], []
-    for i in range((n + page_tokens - 1) // page_tokens):
+    """Keys and values of the mapped tokens among the first n of a paged
+    sequence, in order, fp64 [n_kv, n_mapped, D]."""
+    n_pages = _pool_pages(pool)
+    ks, vs = [kv_read(pool, kind, 0, 0)[0]], [kv_read(pool, kind, 0, 0)[1]]
+    for i in range((max(0, n) + page_tokens - 1) // page_tokens):
+        pg = int(pages[i])
+        if not 0 <= pg < n_pages:
+            continue
         take = min(page_tokens, n - i * page_tokens)
-        kd, vd = kv_read(pool, kind, int(pages[i]), take)
+        kd, vd = kv_read(pool, kind, pg, take)
         ks.append(kd)
         vs.append(vd)
     return np.concatenate(ks, axis=1), np.concatenate(vs, axis=1)
 
 
-def kv_append_paged(pool, kind: str, pages, page_tokens: int, pos: int, k: np.ndarray, v: np.ndarray) -> None:
-    """kv_append of one token at logical position pos of a paged sequence."""
-    kv_append(pool, kind, int(pages[pos // page_tokens]), pos % page_tokens, k, v)
+def kv_append_paged(pool, kind: str, pages, page_tokens: int, pos: int, k: np.ndarray, v: np.ndarray) -> bool:
+    """kv_append of one token at logical position pos of a paged sequence;
+    False (nothing stored) when pos lies outside the table or on an unmapped page."""
+    i = pos // page_tokens
+    if pos < 0 or i >= len(pages) or not 0 <= int(pages[i]) < _pool_pages(pool):
+        return False
+    kv_append(pool, kind, int(pages[i]), pos % page_tokens, k, v)
+    return True
 
 
 def attention_batch_paged(q: np.ndarray, pool, kind: str, page_table, page_tokens: int, n_ctx,
                           scale: float) -> np.ndarray:
-    """attention_batch over paged sequences: page_table[b] lists sequence b's pages in order."""
+    """attention_batch over paged sequences: page_table[b] lists sequence b's
+    pages in order; tokens on unmapped pages are left out of the softmax and a
+    sequence with no mapped token gets O = 0."""
     out = np.empty(q.shape, dtype=np.float64)
     for b in range(q.shape[0]):
         kd, vd = kv_read_paged(pool, kind, page_table[b], page_tokens, int(n_ctx[b]))
-        out[b] = attention(q[b], kd, vd, scale)
+        out[b] = _attend(q[b], kd, vd, scale)
     return out
 
 
@@ -134,6 +161,31 @@ def decode_step(model, caches, kind: str, slots, pos, tok, n_layers=None):
     attends over pos[b]+1 tokens.  Returns (logits fp64 [B, vocab], next token
     int64 [B]); the caller advances pos by one.
     """
+    def append(cache, b, p, k, v):
+        kv_append(cache, kind, int(slots[b]), p, k, v)
+
+    def read(cache, b, n):
+        return kv_read(cache, kind, int(slots[b]), n)
+
+    return _step(model, caches, pos, tok, append, read, n_layers)
+
+
+def decode_step_paged(model, pools, kind: str, page_table, page_tokens: int, pos, tok, n_layers=None):
+    """decode_step over paged pools (one per layer, all sharing page_table:
+    sequence b's token t sits in page page_table[b][t // page_tokens] of every
+    layer).  The new token goes to position pos[b] of sequence b (dropped when
+    its page is unmapped, kv_append_paged); attention reads the mapped tokens
+    among the first pos[b]+1."""
+    def append(pool, b, p, k, v):
+        kv_append_paged(pool, kind, page_table[b], page_tokens, p, k, v)
+
+    def read(pool, b, n):
+        return kv_read_paged(pool, kind, page_table[b], page_tokens, n)
+
+    return _step(model, pools, pos, tok, append, read, n_layers)
+
+
+def _step(model, caches, pos, tok, append, read, n_layers):
     dm = model.dims
     hq, hkv, hd = dm.n_q_heads, dm.n_kv_heads, dm.head_dim
     f = dm.ffn
@@ -153,9 +205,9 @@ def decode_step(model, caches, kind: str, slots, pos, tok, n_layers=None):
             q = rope(qkv[b, :qrows].reshape(hq, hd), p, dm.rope_base)
             k = rope(qkv[b, qrows:qrows + krows].reshape(hkv, hd), p, dm.rope_base)
             v = qkv[b, qrows + krows:].reshape(hkv, hd)
-            kv_append(cache, kind, int(slots[b]), p, k, v)
-            kd, vd = kv_read(cache, kind, int(slots[b]), p + 1)
-            o[b] = attention(round_f16(q), kd, vd, scale).reshape(-1)
+            append(cache, b, p, k, v)
+            kd, vd = read(cache, b, p + 1)
+            o[b] = _attend(round_f16(q), kd, vd, scale).reshape(-1)
         x = x + q4k_gemm(ly.w_o, dm.hidden, qrows, round_f16(o))
         h2 = round_f16(rmsnorm(x, ly.norm_ffn, dm.rms_eps))
         gu = q4k_gemm(ly.w_gate_up, 2 * f, dm.hidden, h2)

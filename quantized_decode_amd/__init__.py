@@ -66,6 +66,7 @@ class StepViews(ctypes.Structure):
 _SIGNATURES = {
     "qkdec_status_str": (ctypes.c_char_p, [_I32]),
     "qkdec_abi_version": (_I32, []),
+    "qkdec_build_id": (ctypes.c_char_p, []),
     "qkdec_gemm_q4k_workspace_size": (_SZ, [_I64, _I64, _I32]),
     "qkdec_gemm_q4k": (_I32, [_P, _I64, _I64, _P, _I64, _I32, _P, _I64, _P, _I64, _P, _SZ, _P]),
     "qkdec_gemm_q4k_xf32": (_I32, [_P, _I64, _I64, _P, _I64, _I32, _P, _I64, _P, _I64, _P, _SZ, _P]),
@@ -137,6 +138,11 @@ def _stream(stream=None) -> int:
 
 
 # ------------------------------------------------------------------ entry points
+def qkdec_build_id() -> str:
+    """The build id of the loaded library (hash of the sources it was built from)."""
+    return load_library().qkdec_build_id().decode()
+
+
 def qkdec_gemm_q4k_workspace_size(n: int, k: int, b: int) -> int:
     return load_library().qkdec_gemm_q4k_workspace_size(n, k, b)
 

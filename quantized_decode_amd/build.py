@@ -7,6 +7,7 @@ quantized_decode_amd/libqkdec.so.  Every call recompiles.
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import subprocess
 import sys
@@ -29,9 +30,24 @@ CFLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
+def source_id() -> str:
+    """Hash of everything the library is built from (its HIP sources and
+    headers, the public header and the compiler flags): the build id that
+    qkdec_build_id() reports, so measurements can be tied to the code they
+    were taken on."""
+    h = hashlib.sha256()
+    h.update(" ".join(CFLAGS).encode())
+    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h")))
+    for path in [os.path.join(CSRC, f) for f in files] + [os.path.join(HERE, "..", "include", "qkdec.h")]:
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _compile(src: str, build_id: str) -> str:
     obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, f'-DQKDEC_BUILD_ID="{build_id}"', "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")
@@ -40,8 +56,9 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
+    bid = source_id()
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(lambda src: _compile(src, bid), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)

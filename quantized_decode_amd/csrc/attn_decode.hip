@@ -75,27 +75,32 @@ __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs
   }
   const size_t head_row0 = ((size_t)s * a.n_kv + g) * a.cap;
   // Paged: the run's page entries (a run is at most kAttnChunk tokens, so at
-  // most kAttnChunk / 32 + 1 pages) are staged in LDS once, clamped into the
-  // pool, so a tile's lookup is an LDS read rather than a global load.
+  // most kAttnChunk / 32 + 1 pages) are staged in LDS once, so a tile's lookup
+  // is an LDS read rather than a global load.  An entry outside the pool (a
+  // page not handed out, -1) is staged as -1: its tiles are loaded from page 0
+  // (never outside the pool) and masked out of the softmax entirely.
   __shared__ int s_pg[PAGED ? kAttnChunk / 32 + 1 : 1];
   const int pg0 = t_begin >> a.page_shift;
   if constexpr (PAGED) {
     const int npg = ((t_end - 1) >> a.page_shift) - pg0 + 1;
     if ((int)threadIdx.x < npg && (int)threadIdx.x < kAttnChunk / 32 + 1) {
-      int pg = a.pages[(size_t)b * a.max_pages + pg0 + threadIdx.x];
-      s_pg[threadIdx.x] = pg < 0 ? 0 : (pg >= a.n_slots ? a.n_slots - 1 : pg);   // never outside the pool
+      const int pg = a.pages[(size_t)b * a.max_pages + pg0 + threadIdx.x];
+      s_pg[threadIdx.x] = (pg < 0 || pg >= a.n_slots) ? -1 : pg;
     }
     __syncthreads();
   }
-  // (row of token 0 of this head, position within it) of the tile at t
-  auto tile_at = [&](int t, size_t& row0, int& tt) {
+  // (row of token 0 of this head, position within it) of the tile at t; false
+  // for a tile on an unmapped page
+  auto tile_at = [&](int t, size_t& row0, int& tt) -> bool {
     if constexpr (PAGED) {
       const int pg = __builtin_amdgcn_readfirstlane(s_pg[(t >> a.page_shift) - pg0]);
-      row0 = ((size_t)pg * a.n_kv + g) * a.cap;
+      row0 = ((size_t)(pg < 0 ? 0 : pg) * a.n_kv + g) * a.cap;
       tt = t & (a.cap - 1);
+      return pg >= 0;
     } else {
       row0 = head_row0;
       tt = t;
+      return true;
     }
   };
 
@@ -114,7 +119,7 @@ __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs
     KVFrag<D, KF, VF> buf[2];
     size_t row0;
     int tt;
-    tile_at(t_begin + 32 * wave, row0, tt);
+    bool mapped = tile_at(t_begin + 32 * wave, row0, tt);
     load_k(buf[0], a, row0, tt, lg, r);
     load_v(buf[0], a, row0, tt, lg, r);
     for (int it = wave; it < ntiles; it += 2 * kAttnWaves) {
@@ -123,10 +128,12 @@ __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs
         const int i = it + p * kAttnWaves;
         if (i < ntiles) {
           const int nx = (i + kAttnWaves < ntiles) ? i + kAttnWaves : i;
-          tile_at(t_begin + 32 * nx, row0, tt);
+          const bool cur_mapped = mapped;
+          mapped = tile_at(t_begin + 32 * nx, row0, tt);
           load_k(buf[p ^ 1], a, row0, tt, lg, r);
           const int t0 = t_begin + 32 * i;
-          attn_tile(st, buf[p], qf, a.scale_log2, min(32, t_end - t0), lg,
+          // a tile on an unmapped page has no valid token (every score -inf)
+          attn_tile(st, buf[p], qf, a.scale_log2, cur_mapped ? min(32, t_end - t0) : 0, lg,
                     [&]() { load_v(buf[p ^ 1], a, row0, tt, lg, r); });
         }
       }
@@ -152,9 +159,11 @@ __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs
   float mm = s_m[0][lane];
 #pragma unroll
   for (int w = 1; w < kAttnWaves; ++w) mm = fmaxf(mm, s_m[w][lane]);
+  // every wave without a valid token (m = -inf): weights 0, not NaN
+  const float mref = mm == -__builtin_inff() ? 0.f : mm;
   float wt[kAttnWaves];
 #pragma unroll
-  for (int w = 0; w < kAttnWaves; ++w) wt[w] = exp2f(s_m[w][lane] - mm);
+  for (int w = 0; w < kAttnWaves; ++w) wt[w] = exp2f(s_m[w][lane] - mref);
   st.m = mm;
   st.l = 0.f;
 #pragma unroll
@@ -219,10 +228,14 @@ __global__ void attn_combine_kernel(const float* __restrict__ part_o, const floa
   float big = -__builtin_inff();
 #pragma unroll
   for (int j = 0; j < kMergeBatch; ++j) big = fmaxf(big, j < ns ? m[j] : -__builtin_inff());
+  // runs without a valid token (all their tiles on unmapped pages) carry
+  // m = -inf, l = 0; a reference of 0 while no run has a finite maximum keeps
+  // their weights at 0 rather than NaN
   float num = 0.f, den = 0.f;
+  float bref = big == -__builtin_inff() ? 0.f : big;
 #pragma unroll
   for (int j = 0; j < kMergeBatch; ++j) {
-    const float w = exp2f(m[j] - big);
+    const float w = exp2f(m[j] - bref);
     den += j < ns ? w * l[j] : 0.f;
     num += j < ns ? w * o[j] : 0.f;
   }
@@ -238,19 +251,22 @@ __global__ void attn_combine_kernel(const float* __restrict__ part_o, const floa
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j)
       if (j0 + j < ns) nb = fmaxf(nb, m[j]);
-    const float fr = exp2f(big - nb);
+    const float nref = nb == -__builtin_inff() ? 0.f : nb;
+    const float fr = exp2f(bref - nref);
     num *= fr;
     den *= fr;
     big = nb;
+    bref = nref;
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j)
       if (j0 + j < ns) {
-        const float w = exp2f(m[j] - big);
+        const float w = exp2f(m[j] - bref);
         den += w * l[j];
         num += w * o[j];
       }
   }
-  const float out = ns > 0 ? num / den : 0.f;
+  // no run with a valid token (or no token at all): O = 0
+  const float out = den > 0.f ? num / den : 0.f;
   const size_t oi = ((size_t)b * Hq + h) * D + d;
   if (O) O[oi] = out;
   if (O16) O16[oi] = (half_t)out;

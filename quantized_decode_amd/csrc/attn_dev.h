@@ -239,7 +239,8 @@ template <int D, int KF, int VF, typename Mid>
 __device__ __forceinline__ void attn_tile(AttnState<D, VF == kFmtQ8>& st, KVFrag<D, KF, VF>& f,
                                           const half8_t (&qf)[D / 32], float scale_log2, int valid, int lg,
                                           const Mid& mid) {
-  // valid = number of tokens of this 32-token tile that are in range (1..32)
+  // valid = number of tokens of this 32-token tile that are in range (0..32;
+  // 0 for a tile on an unmapped page of a paged pool)
   float sc[8];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
@@ -272,13 +273,16 @@ __device__ __forceinline__ void attn_tile(AttnState<D, VF == kFmtQ8>& st, KVFrag
   tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
   const float mnew = fmaxf(st.m, tmax);
-  const float corr = exp2f(st.m - mnew);   // 0 on the first tile (m = -inf)
+  // while no valid token has been seen (a masked tile, valid = 0, first) the
+  // maximum stays -inf; a reference of 0 then keeps corr and p at 0, not NaN
+  const float mref = mnew == -__builtin_inff() ? 0.f : mnew;
+  const float corr = exp2f(st.m - mref);   // 0 on the first tile (m = -inf)
   st.m = mnew;
   float p[8];
   float psum = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    p[e] = exp2f(sc[e] - mnew);
+    p[e] = exp2f(sc[e] - mref);
     psum += p[e];
   }
   st.l = st.l * corr + psum;

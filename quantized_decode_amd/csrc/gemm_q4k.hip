@@ -267,11 +267,16 @@ __device__ void gemm_item(const GemmArgs& a, int rg, int c, int n_chunks, half_t
                              __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);
+    // every wave's partial stores happen before thread 0's release (the
+    // barrier), which publishes them at device scope before the arrival count;
+    // the last arriver's acquire orders its partial loads after the count
     __syncthreads();
-    if (threadIdx.x == 0)
-      sm.s_last = (__hip_atomic_fetch_add(&a.counters[rg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                   (unsigned)(n_chunks - 1));
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      const unsigned prev = __hip_atomic_fetch_add(&a.counters[rg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sm.s_last = prev == (unsigned)(n_chunks - 1);
+      if (sm.s_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
     __syncthreads();
     if (!sm.s_last) return;
     // all chunks' partials (and the residual) in one batch of loads, then the
@@ -323,7 +328,7 @@ __device__ void gemm_item(const GemmArgs& a, int rg, int c, int n_chunks, half_t
         }
       }
     }
-    if (threadIdx.x == 0) a.counters[rg] = 0u;
+    if (threadIdx.x == 0) __hip_atomic_store(&a.counters[rg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else if (MODE != 1 && a.residual) {
     const int nc = tok ? n : 0;
 #pragma unroll

@@ -756,13 +756,17 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
         __hip_atomic_store(&a.part[((size_t)kc * a.B + b) * n_total + n], v[0][ii], __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
-    __builtin_amdgcn_s_waitcnt(0);
+    // one wave stores the tile's chunk: its release (executed by every lane,
+    // ahead of lane 0's count) publishes the stores at device scope; the last
+    // arriver's acquire orders its partial loads after the count
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     unsigned prev = 0;
     if (lane == 0)
       prev = __hip_atomic_fetch_add(&a.counters[item], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     prev = __shfl(prev, 0);
     if (prev != (unsigned)(KSPLIT - 1)) return;
-    if (lane == 0) a.counters[item] = 0u;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (lane == 0) __hip_atomic_store(&a.counters[item], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     float pv[KSPLIT][4];
 #pragma unroll
     for (int cc = 0; cc < KSPLIT; ++cc)

@@ -244,6 +244,11 @@ const char* qkdec_status_str(qkdec_status s) {
 
 int32_t qkdec_abi_version(void) { return QKDEC_ABI_VERSION; }
 
+#ifndef QKDEC_BUILD_ID
+#define QKDEC_BUILD_ID "unknown"
+#endif
+const char* qkdec_build_id(void) { return QKDEC_BUILD_ID; }
+
 size_t qkdec_gemm_q4k_workspace_size(int64_t N, int64_t K, int32_t B) {
   if (N <= 0 || K <= 0 || N % 16 || K % 256 || B < 1 || B > 16) return 0;
   return gemm_workspace_bytes(N, K, B, false);

@@ -78,3 +78,47 @@ def ws(nbytes):
     """Zeroed device workspace (uint8)."""
     import torch
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device="cuda")
+
+
+U32 = 2.0 ** -24    # unit roundoff of fp32
+
+
+def rope_fp32_slack(x, pos, base):
+    """Bound on |fp32 rotation - exact rotation| of x [heads, D] at pos, for a
+    kernel that rounds cos and sin once to fp32 and rotates in fp32: each
+    output x_i c -/+ x_j s carries at most 4 roundings of the size of its two
+    products (cos / sin, two products, one sum).  Near a cancellation this is
+    far more than one fp16 ulp of the (small) result."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    half = d // 2
+    i = np.arange(half, dtype=np.float64)
+    a = float(pos) * base ** (-2.0 * i / d)
+    c, s = np.abs(np.cos(a)), np.abs(np.sin(a))
+    x1, x2 = np.abs(x[..., :half]), np.abs(x[..., half:])
+    mag = np.concatenate([x1 * c + x2 * s, x2 * c + x1 * s], axis=-1)
+    return 4.0 * U32 * mag
+
+
+def attention_fp32_slack(q, k, v, scale):
+    """First-order bound on |O_fp32 - O_exact| for one sequence (q [Hq, D],
+    k, v [Hkv, n, D] as the kernel reads them) caused by computing the scores
+    in fp32: a D-term dot product is within (D + 4) u sum_d |q_d k_d| of
+    exact (any summation order, plus the per-block scale and the softmax
+    scale), and O = sum_t p_t v_t moves by sum_t p_t ds_t (v_t - O) when the
+    scores move by ds.  Where one key holds a large share of the softmax and
+    a very different value, this exceeds 1e-3 of O; elsewhere it is tiny."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    hq, hkv, d = q.shape[0], k.shape[0], q.shape[1]
+    out = np.zeros_like(q)
+    for h in range(hq):
+        g = h // (hq // hkv)
+        s = scale * (k[g] @ q[h])
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        o = p @ v[g]
+        ds = (d + 4) * U32 * scale * (np.abs(k[g]) @ np.abs(q[h]))
+        out[h] = (p * ds) @ np.abs(v[g] - o)
+    return out

@@ -41,6 +41,13 @@ def test_status_strings_and_version(lib):
     assert b"unknown" in lib.qkdec_status_str(42)
 
 
+def test_build_id_names_the_sources_it_was_built_from(lib):
+    # the id is a hash of the sources; a stale build (sources edited since)
+    # reports a different one, which is how recorded counter figures are dropped
+    from quantized_decode_amd.build import source_id
+    assert qd.qkdec_build_id() == source_id()
+
+
 FAKE = 0x10000   # never dereferenced: every call below fails validation first
 
 
@@ -179,3 +186,4 @@ def test_paged_validation(lib):
     assert app(ctypes.byref(pool), None, 4, FAKE, FAKE, FAKE, 1, None, None) == -1
     assert app(ctypes.byref(pool), FAKE, 4, FAKE, FAKE, FAKE, 0, None, None) == -2
     assert app(ctypes.byref(_kv(type=1, capacity=256)), FAKE, 4, FAKE, FAKE, FAKE, 1, None, None) == -1  # scales
+

@@ -192,3 +192,74 @@ def test_attention_fp8_value_decode_exact(qd):
         g = h // (hq // hkv)
         assert np.array_equal(o[0, h].astype(np.float64), want[g]), h
         assert np.array_equal(o16[0, h].astype(np.float64), want[g]), h
+
+
+def _nan_ws(nbytes):
+    """Workspace pre-filled with NaN: a run state the merge should not read
+    (rows past a sequence's run count, stale rows of an earlier call) would
+    turn the output into NaN."""
+    import torch
+    n = (max(int(nbytes), 256) + 3) // 4
+    return torch.full((n,), float("nan"), dtype=torch.float32, device="cuda").view(torch.uint8)
+
+
+@pytest.mark.parametrize("kind", ["f16", "q8_0"])
+@pytest.mark.parametrize("bsz", [1, 2])
+@pytest.mark.parametrize("L", [2400, 6900])
+def test_attention_small_batch_many_runs_nan_workspace(qd, kind, bsz, L):
+    # B = 1 and 2 sequences of a Qwen-shaped layer (32/8 heads of 128): the
+    # runs per sequence (9 at L = 2400, 16-27 at L = 6900) fill the merge's
+    # batches of eight partly, and every row the merge must not use is NaN
+    import torch
+    from quantized_decode_amd.tensors import dev, upload_cache
+    hq, hkv, d = 32, 8, 128
+    cap = (L + 31) // 32 * 32
+    cache, st = _make(kind, 6000 + L + bsz, bsz, hkv, cap, d, [L] * bsz)
+    q = synth.f16_normal(st.next(), (bsz, hq, d))
+    dkv = upload_cache(cache)
+    qt = dev(q.view(np.uint16)).view(torch.float16)
+    o = torch.empty((bsz, hq, d), dtype=torch.float32, device="cuda")
+    w = _nan_ws(qd.qkdec_attn_workspace_size(bsz, hq, dkv.desc))
+    slots = list(range(bsz))
+    qd.qkdec_attn_decode(dkv.desc, dev(np.asarray(slots, np.int32)), dev(np.full(bsz, L, np.int32)), bsz, qt, hq,
+                         1 / math.sqrt(d), o=o, workspace=w)
+    sync()
+    ref = OS.attention_batch(q.astype(np.float64), cache, kind, slots, [L] * bsz, 1 / math.sqrt(d))
+    assert_rel(o.cpu().numpy(), ref, what=f"{kind} B={bsz} L={L}")
+
+
+@pytest.mark.parametrize("kind", ["f16", "q8_0"])
+@pytest.mark.parametrize("L", [8192, 19000])
+def test_attention_long_context(qd, kind, L):
+    # the long-context points of the Q8_0 workload (B = 8 at L = 8192 and
+    # 19000, more than eight runs of up to 1024 tokens per sequence), one
+    # Qwen-shaped layer, against the oracle; NaN workspace
+    import torch
+    from quantized_decode_amd.tensors import dev, upload_cache
+    bsz, hq, hkv, d = 8, 32, 8, 128
+    cap = (L + 31) // 32 * 32
+    cache, st = _make(kind, 7000 + L, bsz, hkv, cap, d, [L] * bsz)
+    q = synth.f16_normal(st.next(), (bsz, hq, d))
+    dkv = upload_cache(cache)
+    qt = dev(q.view(np.uint16)).view(torch.float16)
+    o = torch.empty((bsz, hq, d), dtype=torch.float32, device="cuda")
+    w = _nan_ws(qd.qkdec_attn_workspace_size(bsz, hq, dkv.desc))
+    slots = list(range(bsz))
+    qd.qkdec_attn_decode(dkv.desc, dev(np.asarray(slots, np.int32)), dev(np.full(bsz, L, np.int32)), bsz, qt, hq,
+                         1 / math.sqrt(d), o=o, workspace=w)
+    sync()
+    del dkv
+    ref = OS.attention_batch(q.astype(np.float64), cache, kind, slots, [L] * bsz, 1 / math.sqrt(d))
+    assert_rel(o.cpu().numpy(), ref, what=f"{kind} B=8 L={L}")
+
+
+@pytest.mark.parametrize("kind", ["q8_0", "fp8"])
+def test_attention_ragged_lengths_quantized(qd, kind):
+    # the ragged batch (lengths uniform in 512..8192) over the 8-bit caches
+    bsz, hq, hkv, d = 8, 32, 8, 128
+    lens = synth.ragged_lengths(np.random.default_rng(4244), bsz)
+    cache, st = _make(kind, 4245, bsz, hkv, 8192, d, list(lens))
+    q = synth.f16_normal(st.next(), (bsz, hq, d))
+    o, _ = _run(qd, cache, kind, q, list(range(bsz)), list(lens), 1 / math.sqrt(d), poison=True)
+    ref = OS.attention_batch(q.astype(np.float64), cache, kind, list(range(bsz)), list(lens), 1 / math.sqrt(d))
+    assert_rel(o, ref, what=f"ragged {kind} {list(lens)}")

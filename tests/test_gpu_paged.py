@@ -248,3 +248,125 @@ def test_paged_step_equals_arena_step(qd, shape, kind, bsz, L, P, cap):
                     take = min(P, n_now - j * P)
                     assert np.array_equal(parr[table[b, j], :, :take].view(np.uint8),
                                           arr[b, :, j * P:j * P + take].view(np.uint8)), (li, name, b, j)
+
+
+@pytest.mark.parametrize("kind", ["f16", "q8_0", "fp8"])
+def test_paged_attention_unmapped_pages_are_masked(qd, kind):
+    # table entries of -1 (a page never handed out) and past the pool inside
+    # n_ctx: the tokens they would hold drop out of the softmax, exactly as in
+    # the oracle; a sequence with no mapped page attends to nothing (O = 0).
+    # Every page nobody holds is poisoned (NaN), so a tile that was not masked
+    # would show.
+    from quantized_decode_amd.tensors import upload_cache
+    st = synth.Streams(8500 + len(kind))
+    hq, hkv, d, P = 32, 8, 128, 64
+    lens = [700, 300, 129, 513]
+    cont = synth.kv_cache(kind, st.next(), st.next(), len(lens), hkv, 768, d, lens)
+    pool, table, _ = _pool_from(cont, lens, P, 40, st.next())
+    table = table.copy()
+    table[0, 2] = -1                       # tokens 128..191 of sequence 0
+    table[0, 7] = -1                       # and 448..511
+    n_pool = next(a for a in vars(pool).values() if a is not None).shape[0]
+    table[1, 0] = n_pool                   # past the pool: tokens 0..63 of sequence 1
+    table[2, :] = -1                       # nothing mapped
+    q = synth.f16_normal(st.next(), (len(lens), hq, d))
+    scale = 1 / math.sqrt(d)
+    got = _attn_paged(qd, upload_cache(pool), table, lens, q, scale)
+    ref = OS.attention_batch_paged(q.astype(np.float64), pool, kind, table, P, lens, scale)
+    assert not got[2].any()
+    assert_rel(got, ref, what=f"paged {kind} with unmapped pages")
+
+
+def _host_pool_write(pool, seq_cache, pages, n, P):
+    """Copy the first n tokens of slot 0 of a logical cache into the pages."""
+    for name, arr in vars(seq_cache).items():
+        if arr is None:
+            continue
+        dst = getattr(pool, name)
+        for j, pg in enumerate(pages):
+            take = max(0, min(P, n - j * P))
+            dst[pg, :, :take] = arr[0, :, j * P:j * P + take]
+
+
+@pytest.mark.parametrize("kind", ["f16", "q8_0"])
+def test_paged_steps_with_admission_and_release_match_oracle(qd, kind):
+    # continuous batching on one pool (P1 "What I am building next"): sequences
+    # A (100 cached tokens) and B (60) decode two steps; then A finishes and
+    # returns its pages, C (40 cached tokens) is admitted into the running
+    # batch and gets pages A held (their stale contents beyond C's length must
+    # not matter), and B, C decode two more steps.  Every step is compared with
+    # the oracle's paged step run on the GPU's own pool contents, positions and
+    # tokens from before that step (teacher forcing): logits, argmax, the new
+    # positions, and no byte of any other sequence's pages touched.
+    import torch
+    from quantized_decode_amd.tensors import upload_cache, upload_model
+    from tests.gpu_util import LOGIT_ABS_TOL, top2_gap
+    dims = synth.TOY
+    P, n_pages, max_pages = 32, 14, 6
+    model = synth.make_model(dims, 1300)
+    st = synth.Streams(1301)
+    pager = PagePool(n_pages, P)
+    hist = {s: [synth.kv_cache(kind, st.next(), st.next(), 1, dims.n_kv_heads, 128, dims.head_dim, [n])
+                for _ in model.layers] for s, n in (("A", 100), ("B", 60), ("C", 40))}
+    length = {"A": 100, "B": 60, "C": 40}
+    # host pools, every page poisoned until a sequence's history is written into it
+    pools = []
+    for li in range(dims.n_layers):
+        p = copy.deepcopy(hist["A"][li])
+        for name, arr in vars(p).items():
+            if arr is None:
+                continue
+            poison = np.float16(np.nan) if arr.dtype == np.float16 else (127 if arr.dtype == np.int8 else 0x7F)
+            setattr(p, name, np.full((n_pages,) + arr.shape[1:2] + (P,) + arr.shape[3:], poison, dtype=arr.dtype))
+        pools.append(p)
+    for s in ("A", "B"):
+        pager.admit(s, length[s])
+        for li in range(dims.n_layers):
+            _host_pool_write(pools[li], hist[s][li], pager.pages(s), length[s], P)
+    embed, lm_head, norm, layers = upload_model(model)
+    tok = {s: int(t) for s, t in zip("ABC", synth.tokens(st.next(), 3, dims.vocab))}
+    batch = ["A", "B"]
+    logits = torch.empty((2, dims.vocab), dtype=torch.float32, device="cuda")
+    for step in range(4):
+        if step == 2:                      # A leaves, C joins between steps
+            pager.release("A")
+            batch = ["B", "C"]
+            pager.admit("C", length["C"])
+            for li in range(dims.n_layers):
+                _host_pool_write(pools[li], hist["C"][li], pager.pages("C"), length["C"], P)
+        for s in batch:
+            pager.reserve(s, length[s] + 1)
+        table = pager.table(batch, max_pages)
+        dpools = [upload_cache(p) for p in pools]
+        sm = qd.StepModel(dims, embed, lm_head, norm, layers, [dp.desc for dp in dpools])
+        pos = _dev(np.array([length[s] for s in batch], np.int32))
+        tk = _dev(np.array([tok[s] for s in batch], np.int32))
+        wsp = ws(qd.qkdec_step_paged_workspace_size(sm, 2, max_pages))
+        qd.qkdec_workspace_init(wsp)
+        qd.qkdec_step_paged(sm, _dev(table), max_pages, pos, tk, 2, wsp, logits=logits)
+        sync()
+        assert qd.qkdec_step_status(wsp) == 0, f"step {step}"
+        ref_pools = copy.deepcopy(pools)
+        ref, rtok = OS.decode_step_paged(model, ref_pools, kind, table, P, [length[s] for s in batch],
+                                         [tok[s] for s in batch])
+        lg, gt = logits.cpu().numpy(), tk.cpu().numpy()
+        d = float(np.abs(lg - ref).max())
+        assert d <= LOGIT_ABS_TOL, f"step {step}: max |dlogit| {d:.3e}"
+        for b in range(2):
+            if top2_gap(ref[b]) > 1e-3:
+                assert gt[b] == rtok[b], f"step {step}: argmax of {batch[b]}"
+        assert np.array_equal(pos.cpu().numpy(), [length[s] + 1 for s in batch])
+        # the GPU's pool after the step: only the batch's new positions changed
+        new = [dp.logical() for dp in dpools]
+        for li in range(dims.n_layers):
+            for name, arr in vars(pools[li]).items():
+                if arr is None:
+                    continue
+                got = getattr(new[li], name)
+                changed = np.argwhere((got.view(np.uint8) != arr.view(np.uint8)).reshape(arr.shape[0], -1).any(1))
+                allowed = {int(table[b, length[s] // P]) for b, s in enumerate(batch)}
+                assert set(changed.ravel().tolist()) <= allowed, (step, li, name)
+                setattr(pools[li], name, got)
+        for b, s in enumerate(batch):
+            length[s] += 1
+            tok[s] = int(gt[b])

@@ -337,3 +337,84 @@ def test_paged_read_is_the_contiguous_cache_split_into_pages(kind):
     a = S.attention_batch(q, cont, kind, [0, 1], [101, 77], 0.125)
     b = S.attention_batch_paged(q, pool, kind, table, P, [101, 77], 0.125)
     assert np.array_equal(a, b)
+
+
+def _scatter_into_pool(cont, n_slots, P, perm):
+    """The slots of a contiguous cache cut into pages of P tokens, page j of
+    slot s stored at physical page perm[s * npp + j] of a pool."""
+    pool = copy.deepcopy(cont)
+    for name, arr in vars(cont).items():
+        if arr is None:
+            continue
+        npp = arr.shape[2] // P
+        pages = arr.reshape((n_slots, arr.shape[1], npp, P) + arr.shape[3:]).transpose(0, 2, 1, 3, 4)
+        pages = pages.reshape((n_slots * npp, arr.shape[1], P) + arr.shape[3:])
+        phys = np.empty_like(pages)
+        phys[perm] = pages
+        setattr(pool, name, phys)
+    return pool
+
+
+@pytest.mark.parametrize("kind", ["f16", "q8_0", "fp8"])
+def test_unmapped_pages_drop_out_of_the_context(kind):
+    # a table entry of -1 (or past the pool) maps nothing: the paged read is the
+    # contiguous read with that page's tokens removed (picked out by index here),
+    # attention over it equals attention over exactly those tokens, a store to it
+    # is dropped, and a sequence with no mapped page attends to nothing (O = 0)
+    st = synth.Streams(7310)
+    n_slots, n_kv, cap, hd, P = 2, 2, 128, 64, 32
+    cont = synth.kv_cache(kind, st.next(), st.next(), n_slots, n_kv, cap, hd, [128, 128])
+    npp = cap // P
+    perm = st.next().permutation(n_slots * npp)
+    pool = _scatter_into_pool(cont, n_slots, P, perm)
+    table = np.array([perm[s * npp:(s + 1) * npp] for s in range(n_slots)])
+    holed = table.copy()
+    holed[0, 1] = -1                    # tokens 32..63 of sequence 0
+    holed[1, 3] = n_slots * npp         # past the pool: tokens 96..127 of sequence 1
+    keep0 = np.r_[0:32, 64:100]
+    kc, vc = S.kv_read(cont, kind, 0, 128)
+    kp, vp = S.kv_read_paged(pool, kind, holed[0], P, 100)
+    assert np.array_equal(kp, kc[:, keep0]) and np.array_equal(vp, vc[:, keep0])
+    rng = st.next()
+    q = rng.standard_normal((2, 4, hd))
+    got = S.attention_batch_paged(q, pool, kind, holed, P, [100, 128], 0.125)
+    kc1, vc1 = S.kv_read(cont, kind, 1, 96)
+    assert np.array_equal(got[0], S.attention(q[0], kc[:, keep0], vc[:, keep0], 0.125))
+    assert np.array_equal(got[1], S.attention(q[1], kc1, vc1, 0.125))
+    before = copy.deepcopy(pool)
+    assert not S.kv_append_paged(pool, kind, holed[0], P, 40, rng.standard_normal((n_kv, hd)),
+                                 rng.standard_normal((n_kv, hd)))
+    assert not S.kv_append_paged(pool, kind, holed[0], P, cap, rng.standard_normal((n_kv, hd)),
+                                 rng.standard_normal((n_kv, hd)))
+    for name in vars(pool):
+        if getattr(pool, name) is not None:
+            assert np.array_equal(getattr(pool, name), getattr(before, name))
+    none = np.full((1, npp), -1)
+    assert not S.attention_batch_paged(q[:1], pool, kind, none, P, [77], 0.125).any()
+
+
+@pytest.mark.parametrize("kind", ["f16", "q8_0"])
+def test_paged_decode_step_equals_arena_step(kind):
+    # the toy decoder over pools whose pages hold the arena's slots scattered:
+    # logits, tokens and every stored entry equal the slot-arena step bitwise
+    model, caches, tok = _toy(kind=kind, length=120)     # capacity 128: four pages of 32
+    P = 32
+    cap = caches[0].k.shape[2] if getattr(caches[0], "k", None) is not None else caches[0].kq.shape[2]
+    cap = cap // P * P
+    for c in caches:
+        for name, arr in vars(c).items():
+            if arr is not None:
+                setattr(c, name, np.ascontiguousarray(arr[:, :, :cap]))
+    npp = cap // P
+    perm = np.random.default_rng(7320).permutation(2 * npp)
+    pools = [_scatter_into_pool(c, 2, P, perm) for c in caches]
+    table = np.array([perm[s * npp:(s + 1) * npp] for s in range(2)])
+    pos = np.array([120, 120])
+    lg_a, nt_a = S.decode_step(model, caches, kind, [0, 1], pos, tok)
+    lg_p, nt_p = S.decode_step_paged(model, pools, kind, table, P, pos, tok)
+    assert np.array_equal(lg_a, lg_p) and np.array_equal(nt_a, nt_p)
+    for c, pl in zip(caches, pools):
+        again = _scatter_into_pool(c, 2, P, perm)
+        for name in vars(c):
+            if getattr(c, name) is not None:
+                assert np.array_equal(getattr(pl, name), getattr(again, name))
