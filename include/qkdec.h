@@ -338,6 +338,22 @@ size_t qkdec_step_paged_workspace_size(const qkdec_model* m, int32_t B_max, cons
 qkdec_status qkdec_step_paged(const qkdec_model* m, const qkdec_kv_layer* kv, const int32_t* pages,
                               int32_t max_pages, int32_t* pos, int32_t* tok, int32_t B, float* logits,
                               void* workspace, size_t ws_bytes, void* stream);
+/* The decode step for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): as qkdec_step, with no workspace argument.  Its intermediates
+ * live in a fixed device array of qkdec_step_noalloc_max_bytes() bytes
+ * (32 MiB) inside the library, one per GPU it runs on, held until the
+ * process ends; the call never allocates or frees.  A step whose workspace
+ * (qkdec_step_workspace_size) exceeds that size returns QKDEC_E_WORKSPACE
+ * (the Qwen-shaped 36-layer model fits at B <= 16 with caches of up to 64K
+ * tokens).  Every call on one GPU shares that GPU's array: calls that overlap
+ * on one GPU (different streams or host threads) race and must be ordered by
+ * the caller.  err: device int32, set to QKDEC_E_CAPACITY when a position
+ * reached the capacity (the caller clears it); this entry point keeps no
+ * status for qkdec_step_status. */
+size_t qkdec_step_noalloc_max_bytes(void);
+qkdec_status qkdec_step_noalloc(const qkdec_model* m, const qkdec_kv_layer* kv, const int32_t* slot, int32_t* pos,
+                                int32_t* tok, int32_t B, float* logits, int32_t* err, void* stream);
 /* Synchronizes `stream`, returns QKDEC_E_CAPACITY if any step since the last
  * call hit the capacity, else QKDEC_OK; the flag is cleared. */
 qkdec_status qkdec_step_status(void* workspace, void* stream);

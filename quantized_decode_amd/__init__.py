@@ -88,6 +88,8 @@ _SIGNATURES = {
     "qkdec_workspace_init": (_I32, [_P, _SZ, _P]),
     "qkdec_step": (_I32, [ctypes.POINTER(Model), ctypes.POINTER(KVLayer), _P, _P, _P, _I32, _P, _P, _SZ, _P]),
     "qkdec_step_status": (_I32, [_P, _P]),
+    "qkdec_step_noalloc_max_bytes": (_SZ, []),
+    "qkdec_step_noalloc": (_I32, [ctypes.POINTER(Model), ctypes.POINTER(KVLayer), _P, _P, _P, _I32, _P, _P, _P]),
     "qkdec_step_paged_workspace_size": (_SZ, [ctypes.POINTER(Model), _I32, ctypes.POINTER(KVLayer), _I32]),
     "qkdec_step_paged": (_I32, [ctypes.POINTER(Model), ctypes.POINTER(KVLayer), _P, _I32, _P, _P, _I32, _P, _P, _SZ,
                                 _P]),
@@ -280,6 +282,17 @@ def qkdec_step_paged(sm: StepModel, pages, max_pages: int, pos, tok, b: int, wor
                                            _ptr(tok), b, _ptr(logits), _ptr(workspace),
                                            workspace.numel() * workspace.element_size(), _stream(stream)),
            "qkdec_step_paged")
+
+
+def qkdec_step_noalloc_max_bytes() -> int:
+    return load_library().qkdec_step_noalloc_max_bytes()
+
+
+def qkdec_step_noalloc(sm: StepModel, slot, pos, tok, b: int, err, logits=None, stream=None) -> None:
+    """qkdec_step without a workspace (the library's fixed device scratch);
+    err: device int32 [1], set to QKDEC_E_CAPACITY on a full cache."""
+    _check(load_library().qkdec_step_noalloc(ctypes.byref(sm.model), sm.kv_arr, _ptr(slot), _ptr(pos), _ptr(tok), b,
+                                             _ptr(logits), _ptr(err), _stream(stream)), "qkdec_step_noalloc")
 
 
 def qkdec_step_status(workspace, stream=None) -> int:

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 
 #include "common.h"
@@ -144,10 +145,13 @@ StepWs step_layout(const qkdec_model* m, int B, const qkdec_kv_layer* kv, char* 
 
 // pages != nullptr: every layer of kv is a paged pool and sequence b's pages
 // are pages[b * max_pages ...]; slot is unused
+// err != nullptr: the capacity flag goes there instead of the workspace's
+// error word
 qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int32_t* slot, int32_t* pos,
                       int32_t* tok, int B, float* logits, void* workspace, hipStream_t st,
-                      const int32_t* pages = nullptr, int max_pages = 0) {
+                      const int32_t* pages = nullptr, int max_pages = 0, int32_t* err = nullptr) {
   const StepWs w = step_layout(m, B, kv, reinterpret_cast<char*>(workspace), max_pages);
+  int32_t* const err_word = err ? err : w.err;
   const int H = m->hidden, F = m->ffn, D = m->head_dim, Hq = m->n_q_heads;
   const int64_t hq = (int64_t)Hq * D;
   const int64_t nqkv = (int64_t)(Hq + 2 * m->n_kv_heads) * D;
@@ -176,7 +180,7 @@ qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int3
     ra.k = reinterpret_cast<uint8_t*>(kv[l].k); ra.v = reinterpret_cast<uint8_t*>(kv[l].v);
     ra.ks = reinterpret_cast<uint16_t*>(kv[l].k_scale); ra.vs = reinterpret_cast<uint16_t*>(kv[l].v_scale);
     ra.n_kv = kv[l].n_kv_heads; ra.cap = kv[l].capacity; ra.n_slots = kv[l].n_slots; ra.Hq = Hq;
-    ra.kf = kv_k_fmt(kv[l].type); ra.vf = kv_v_fmt(kv[l].type); ra.rope_base = m->rope_base; ra.q16 = w.q16; ra.err = w.err;
+    ra.kf = kv_k_fmt(kv[l].type); ra.vf = kv_v_fmt(kv[l].type); ra.rope_base = m->rope_base; ra.q16 = w.q16; ra.err = err_word;
     // K = 4096: the resident multi-item projection, finishing each head slice
     // itself (fp16 or E4M3 cache) or followed by RoPE and the append as a small launch
     // (Q8_0 blocks span two work-groups); otherwise the split-K projection
@@ -188,7 +192,7 @@ qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int3
         QK_TRY(launch_gemm_qkv_rope(qkv, ra, D, st));
       } else {
         QK_TRY(eq);
-        QK_TRY(launch_rope_append(kv[l], w.qkv, nqkv, Hq, B, ra.slot, pos, m->rope_base, w.q16, w.err, st,
+        QK_TRY(launch_rope_append(kv[l], w.qkv, nqkv, Hq, B, ra.slot, pos, m->rope_base, w.q16, err_word, st,
                                   ra.spos));
       }
     } else {
@@ -217,6 +221,31 @@ qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int3
   QK_TRY(launch_lm_head_argmax(m->lm_head, m->vocab, H, w.h, B, logits, tok, w.lm_part, pos, st));
 #undef QK_TRY
   return QKDEC_OK;
+}
+
+// ---- the step's fixed device scratch (qkdec_step_noalloc): one array per
+// GPU the library runs on, held until the process ends.  Host code never
+// passes the array's name to a kernel or a copy: it is a host-side stand-in.
+// Each device's address comes from hipGetSymbolAddress, taken once with that
+// device current, and only that address is used.
+constexpr size_t kStepScratchBytes = (size_t)32 << 20;
+__device__ __align__(256) char scratch[kStepScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (nullptr on failure).
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
 }
 
 }  // namespace
@@ -504,6 +533,31 @@ qkdec_status qkdec_step_paged(const qkdec_model* m, const qkdec_kv_layer* kv, co
   if (s != QKDEC_OK) return s;
   clear_stale_error();
   return run_step(m, kv, nullptr, pos, tok, B, logits, workspace, as_stream(stream), pages, max_pages);
+}
+
+size_t qkdec_step_noalloc_max_bytes(void) { return kStepScratchBytes; }
+
+qkdec_status qkdec_step_noalloc(const qkdec_model* m, const qkdec_kv_layer* kv, const int32_t* slot, int32_t* pos,
+                                int32_t* tok, int32_t B, float* logits, int32_t* err, void* stream) {
+  qkdec_status s = check_model(m, kv);
+  if (s != QKDEC_OK) return s;
+  if (!slot || !pos || !tok || !err) return QKDEC_E_ARG;
+  if (B < 1 || B > 16) return QKDEC_E_SHAPE;
+  const size_t need = step_layout(m, B, kv, nullptr).bytes;
+  if (need > kStepScratchBytes) return QKDEC_E_WORKSPACE;
+  s = check_lds(lm_head_lds_bytes(m->hidden, B));
+  if (s != QKDEC_OK) return s;
+  clear_stale_error();
+  void* base = device_scratch();
+  if (!base) return QKDEC_E_HIP;
+  hipStream_t st = as_stream(stream);
+  // The split-K arrival counters must read zero at the first GEMM; where they
+  // sit depends on this call's shapes, so the area is cleared every call (the
+  // previous call on this device may have left other data there).
+  const StepWs w = step_layout(m, B, kv, reinterpret_cast<char*>(base));
+  const size_t ctr = gemm_workspace_bytes(16, 256, 1, false);   // the fixed counter area at the start
+  if (launch_fill_zero(w.gemm_ws, ctr, st) != hipSuccess) return QKDEC_E_HIP;
+  return run_step(m, kv, slot, pos, tok, B, logits, base, st, nullptr, 0, err);
 }
 
 qkdec_status qkdec_step_status(void* workspace, void* stream) {

@@ -187,3 +187,21 @@ def test_paged_validation(lib):
     assert app(ctypes.byref(pool), FAKE, 4, FAKE, FAKE, FAKE, 0, None, None) == -2
     assert app(ctypes.byref(_kv(type=1, capacity=256)), FAKE, 4, FAKE, FAKE, FAKE, 1, None, None) == -1  # scales
 
+
+def test_noalloc_step_validation(lib):
+    # every rejection happens before any device work (this runs without a GPU)
+    layers = (qd.Layer * 2)(qd.Layer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE), qd.Layer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE))
+    m = qd.Model(2, 512, 8, 2, 64, 1536, 4096, 1e-6, 1e6, FAKE, FAKE, FAKE, ctypes.cast(layers, ctypes.POINTER(qd.Layer)))
+    kvs = (qd.KVLayer * 2)(_kv(n_kv_heads=2, head_dim=64, capacity=256, n_slots=2),
+                            _kv(n_kv_heads=2, head_dim=64, capacity=256, n_slots=2))
+    cap = lib.qkdec_step_noalloc_max_bytes()
+    assert cap == 32 << 20
+    step = lib.qkdec_step_noalloc
+    assert step(ctypes.byref(m), kvs, FAKE, FAKE, FAKE, 2, None, None, None) == -1       # no err word
+    assert step(ctypes.byref(m), kvs, None, FAKE, FAKE, 2, None, FAKE, None) == -1
+    assert step(ctypes.byref(m), kvs, FAKE, FAKE, FAKE, 0, None, FAKE, None) == -2
+    # a cache so long that the attention partials alone exceed the scratch
+    big = (qd.KVLayer * 2)(_kv(n_kv_heads=2, head_dim=64, capacity=1 << 25, n_slots=16),
+                            _kv(n_kv_heads=2, head_dim=64, capacity=1 << 25, n_slots=16))
+    assert lib.qkdec_step_workspace_size(ctypes.byref(m), 16, big) > cap
+    assert step(ctypes.byref(m), big, FAKE, FAKE, FAKE, 16, None, FAKE, None) == -4
