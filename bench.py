@@ -364,19 +364,29 @@ def gemm_pass(qd, sd, dev_model, batches, seed, replays=5):
         ys = {n: torch.empty((bsz, n), dtype=torch.float32, device="cuda") for n in {n for _, n, _ in shapes}}
         wsz = max(qd.qkdec_gemm_q4k_workspace_size(n, k, bsz) for _, n, k in shapes)
         ws = torch.zeros(wsz, dtype=torch.uint8, device="cuda")
-        calls = [lambda ly=ly, nm=nm, n=n, k=k: qd.qkdec_gemm_q4k(ly[nm], n, k, xs[k], bsz, ys[n], workspace=ws,
-                                                                   stream=stream)
-                 for ly in layers for nm, n, k in shapes]
-        ms = _timed(calls, stream, replays=replays) * len(calls)
+        engines = [("mfma", qd.GEMM_MFMA)] + ([("matvec", qd.GEMM_MATVEC)] if bsz <= qd.MATVEC_MAX_B else [])
         nbytes = wbytes + len(layers) * sum(bsz * (2 * k + 4 * n) for _, n, k in shapes)
-        rows.append({"batch": bsz, "ms_per_pass": ms, "bytes_per_pass": nbytes,
-                     "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_of_8TBps": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-                     "weight_GBps": wbytes / (ms * 1e-3) / 1e9})
-        log(f"  GEMM pass B={bsz}: {ms:.3f} ms, {rows[-1]['GBps']:.0f} GB/s")
+        for ename, eng in engines:
+            calls = [lambda ly=ly, nm=nm, n=n, k=k, eng=eng: qd.qkdec_gemm_q4k_engine(
+                         ly[nm], n, k, xs[k], bsz, ys[n], eng, workspace=ws, stream=stream)
+                     for ly in layers for nm, n, k in shapes]
+            ms = _timed(calls, stream, replays=replays) * len(calls)
+            rows.append({"batch": bsz, "engine": ename, "ms_per_pass": ms, "bytes_per_pass": nbytes,
+                         "GBps": nbytes / (ms * 1e-3) / 1e9,
+                         "frac_of_8TBps": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                         "weight_GBps": wbytes / (ms * 1e-3) / 1e9})
+            log(f"  GEMM pass B={bsz} {ename}: {ms:.3f} ms, {rows[-1]['GBps']:.0f} GB/s")
         del xs, ys, ws
+    # the largest batch at which the matvec pass is faster than the MFMA pass
+    best = {}
+    for r in rows:
+        best.setdefault(r["batch"], {})[r["engine"]] = r["ms_per_pass"]
+    wins = [bb for bb, e in sorted(best.items()) if "matvec" in e and e["matvec"] < e["mfma"]]
+    crossover = max(wins) if wins else 0
     return {"workload": "36 layers x {QKV 6144x4096, O 4096x4096, gate|up 24576x4096, down 4096x12288} Q4_K, "
-                        "fp16 activations, fp32 out (qkdec_gemm_q4k)", "weight_bytes_per_pass": wbytes,
-            "points": rows}
+                        "fp16 activations, fp32 out (qkdec_gemm_q4k_engine, MFMA tiles and vector-ALU matvec)",
+            "weight_bytes_per_pass": wbytes, "matvec_faster_up_to_batch": crossover,
+            "library_auto_max_batch": qd.MATVEC_AUTO_MAX_B, "points": rows}
 
 
 def attention_pass(qd, sd, batch, contexts, ragged_seed, seed, kind="f16", replays=5):
@@ -417,6 +427,44 @@ def attention_pass(qd, sd, batch, contexts, ragged_seed, seed, kind="f16", repla
         del kvs, keep, aws
         torch.cuda.empty_cache()
     return {"workload": f"36 layers x qkdec_attn_decode, 32/8 heads x 128, {kind} KV, B={batch}", "points": rows}
+
+
+def prefill_point(qd, sd, dims, dev_model, n_prompt, seed, kind="f16"):
+    """Prompt ingestion (qkdec_prefill): n_prompt tokens into an empty slot of
+    the Qwen-shaped model (all 36 layers, keys and values appended, the first
+    generated token taken after the last prompt token); one warm-up call, then
+    the median of three calls timed with HIP events on the launching stream."""
+    import torch
+    from quantized_decode_amd import KV_KINDS, kv_layer
+    g = sd.generator(seed)
+    cap = (n_prompt + 31) // 32 * 32
+    kvs, keep = [], []
+    for _ in range(dims.n_layers):
+        k, v, ks, vs = sd.kv_cache(g, kind, 1, dims.n_kv_heads, cap, dims.head_dim, 0)
+        keep.append((k, v, ks, vs))
+        kvs.append(kv_layer(KV_KINDS[kind], dims.n_kv_heads, dims.head_dim, cap, 1, k, v, ks, vs))
+    embed, lm_head, norm, layers = dev_model
+    sm = qd.StepModel(dims, embed, lm_head, norm, layers, kvs)
+    prompt = torch.randint(0, dims.vocab, (n_prompt,), dtype=torch.int32, device="cuda", generator=g)
+    tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(qd.qkdec_prefill_workspace_size(sm), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    times = []
+    for i in range(4):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        qd.qkdec_prefill(sm, 0, 0, prompt, n_prompt, tok, ws, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        if i:
+            times.append(a.elapsed_time(b))
+    ms = sorted(times)[1]
+    wbytes = W_BYTES * ((n_prompt + 15) // 16)
+    del kvs, keep
+    return {"prompt_tokens": n_prompt, "kv": kind, "ms": ms, "tok_per_s": n_prompt / (ms * 1e-3),
+            "weight_bytes_read": wbytes, "note": "chunks of 16 prompt tokens, each one pass of the layers with the "
+                                                  "tokens as the batched kernels' rows; LM head for the last token"}
 
 
 def record_traffic(qd, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mb, batch, context, kv, command):
@@ -727,6 +775,10 @@ def main():
         passes = {"gemm": gemm_pass(qd, sd, dev_model, [1, 2, 4, 8, 16], 9000)}
         log("standalone attention pass (B = 8, L = 2400 / 4700 / 6900 and ragged)")
         passes["attention"] = attention_pass(qd, sd, 8, [2400, 4700, 6900], 4242, 9100)
+        torch.cuda.empty_cache()
+        log("prefill of a 2048-token prompt")
+        passes["prefill"] = prefill_point(qd, sd, dims, dev_model, 2048, 9200)
+        log(f"  prefill: {passes['prefill']['ms']:.1f} ms, {passes['prefill']['tok_per_s']:.0f} tok/s")
         torch.cuda.empty_cache()
 
     log("streaming-read ceiling (4 GiB) and clocks")

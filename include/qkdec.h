@@ -104,11 +104,11 @@ const char* qkdec_build_id(void);
  * fixed 64 KiB area of split-K arrival counters, then the partial sums; every
  * call leaves the counters zero again, so one workspace serves calls of any
  * shapes it is large enough for).  Calls that share a workspace must not
- * overlap.  The workspace contract is common to the three GEMM entry points:
- * qkdec_gemm_q4k itself computes each 16-row output tile in one work-group
- * (K split over its waves, partial sums added in LDS) and does not touch it;
- * the _xf32 and _swiglu variants may split K across work-groups (by shape)
- * and then use it.
+ * overlap.  The workspace contract is common to the GEMM entry points: each
+ * 16-row output tile is computed in one work-group (K split over its waves,
+ * partial sums added in LDS), except where K is split across work-groups as
+ * well (by shape, e.g. K = 12288), whose partial sums and arrival counters
+ * live in the workspace.
  * Partial sums are added in a fixed order: results are deterministic and
  * independent of scheduling.
  */
@@ -117,6 +117,28 @@ qkdec_status qkdec_gemm_q4k(const void* W, int64_t N, int64_t K,
                             const uint16_t* X, int64_t ldx, int32_t B,
                             float* Y, int64_t ldy, const float* residual, int64_t ldr,
                             void* workspace, size_t ws_bytes, void* stream);
+
+/* Which engine forms the products.  P1 "RDNA4 pads the batch dimension to 16
+ * whether you fill it or not": a one-row GEMM is a matrix-vector product,
+ * bandwidth-bound, which the pages run as a dequant-matvec below about four
+ * sequences and on the matrix cores above.  QKDEC_GEMM_MATVEC runs the same
+ * exact Q4_K decode and forms the products on the vector ALU (packed fp16 dot
+ * products into fp32) for the live sequences only, B <= QKDEC_MATVEC_MAX_B;
+ * QKDEC_GEMM_MFMA pads the batch to the 16-row tile; QKDEC_GEMM_AUTO takes the
+ * matvec for B <= QKDEC_MATVEC_AUTO_MAX_B, the crossover measured on MI355X
+ * (36-layer pass of the four projections: matvec 1.49 ms against MFMA 1.54 ms
+ * at B = 1, 1.79 against 1.53 ms at B = 2; the decode step uses AUTO).  The choice applies where the multi-item
+ * kernel serves the shape (K = 4096; K = 12288 without SwiGLU); elsewhere the
+ * MFMA kernels run. */
+enum { QKDEC_GEMM_AUTO = 0, QKDEC_GEMM_MFMA = 1, QKDEC_GEMM_MATVEC = 2 };
+#define QKDEC_MATVEC_MAX_B 2
+#define QKDEC_MATVEC_AUTO_MAX_B 1
+/* As qkdec_gemm_q4k with the engine chosen (a QKDEC_GEMM_* value);
+ * QKDEC_E_SHAPE for QKDEC_GEMM_MATVEC with B > QKDEC_MATVEC_MAX_B. */
+qkdec_status qkdec_gemm_q4k_engine(const void* W, int64_t N, int64_t K,
+                                   const uint16_t* X, int64_t ldx, int32_t B,
+                                   float* Y, int64_t ldy, const float* residual, int64_t ldr,
+                                   int32_t engine, void* workspace, size_t ws_bytes, void* stream);
 
 /* As qkdec_gemm_q4k, with fp32 activations X (ldx % 4 == 0, 16-byte
  * aligned).  Each row's activations are rounded to fp16 in blocks of 256
@@ -338,6 +360,25 @@ size_t qkdec_step_paged_workspace_size(const qkdec_model* m, int32_t B_max, cons
 qkdec_status qkdec_step_paged(const qkdec_model* m, const qkdec_kv_layer* kv, const int32_t* pages,
                               int32_t max_pages, int32_t* pos, int32_t* tok, int32_t B, float* logits,
                               void* workspace, size_t ws_bytes, void* stream);
+/* Prefill (P2 "This is the mirror image of the prefill story": a prompt is
+ * many tokens of one sequence processed together, which batches the weight
+ * read the way decode batches sequences): the n prompt tokens (device int32
+ * [n]) of slot `slot` go through every layer at positions start .. start+n-1,
+ * their keys and values are appended to the cache, and the final norm, LM
+ * head and argmax run for the last token only: logits fp32 [vocab] (may be
+ * NULL) and tok_out (device int32 [1]) = its argmax, the first generated
+ * token.  Positions before start must already be cached.  The prompt is taken
+ * in chunks of 16 tokens, each chunk one pass of the layers with its tokens as
+ * the rows of the batched kernels: token t attends over positions <= start+t,
+ * the chunk's earlier tokens included (appended before the attention runs).
+ * 0 <= slot < n_slots, n >= 1, start + n <= capacity (else QKDEC_E_CAPACITY,
+ * nothing launched).  workspace: qkdec_prefill_workspace_size() bytes, zeroed
+ * once with qkdec_workspace_init. */
+size_t qkdec_prefill_workspace_size(const qkdec_model* m, const qkdec_kv_layer* kv);
+qkdec_status qkdec_prefill(const qkdec_model* m, const qkdec_kv_layer* kv, int32_t slot, int32_t start,
+                           const int32_t* tokens, int32_t n, float* logits, int32_t* tok_out, void* workspace,
+                           size_t ws_bytes, void* stream);
+
 /* The decode step for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): as qkdec_step, with no workspace argument.  Its intermediates

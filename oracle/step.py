@@ -216,3 +216,16 @@ def _step(model, caches, pos, tok, append, read, n_layers):
     hf = round_f16(rmsnorm(x, model.norm_final, dm.rms_eps))
     logits = dense_gemm(model.lm_head, hf)
     return logits, argmax_lowest(logits)
+
+
+def prefill(model, caches, kind: str, slot: int, start: int, tokens):
+    """Ingest a prompt into one sequence's cache (P2 "This is the mirror image
+    of the prefill story").  By definition this is the decode step applied to
+    the prompt's tokens in order: token i sits at position start + i, its keys
+    and values are appended, and it attends over every earlier position and
+    itself.  Mutates ``caches``; returns (logits fp64 [vocab] after the last
+    token, their argmax)."""
+    logits, nt = None, None
+    for i, t in enumerate(tokens):
+        logits, nt = decode_step(model, caches, kind, [slot], [start + i], [int(t)])
+    return logits[0], int(nt[0])

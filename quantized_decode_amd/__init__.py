@@ -15,6 +15,12 @@ from typing import List, Optional, Sequence
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqkdec.so")
 
+GEMM_AUTO = 0           # matvec for B <= MATVEC_AUTO_MAX_B, else the MFMA tiles
+GEMM_MFMA = 1
+GEMM_MATVEC = 2         # vector-ALU matvec, B <= MATVEC_MAX_B
+MATVEC_MAX_B = 2
+MATVEC_AUTO_MAX_B = 1
+
 KV_F16 = 0
 KV_Q8_0 = 1
 KV_Q8_0_K_F16_V = 2     # Q8_0 keys, fp16 values
@@ -70,6 +76,7 @@ _SIGNATURES = {
     "qkdec_gemm_q4k_workspace_size": (_SZ, [_I64, _I64, _I32]),
     "qkdec_gemm_q4k": (_I32, [_P, _I64, _I64, _P, _I64, _I32, _P, _I64, _P, _I64, _P, _SZ, _P]),
     "qkdec_gemm_q4k_xf32": (_I32, [_P, _I64, _I64, _P, _I64, _I32, _P, _I64, _P, _I64, _P, _SZ, _P]),
+    "qkdec_gemm_q4k_engine": (_I32, [_P, _I64, _I64, _P, _I64, _I32, _P, _I64, _P, _I64, _I32, _P, _SZ, _P]),
     "qkdec_gemm_q4k_swiglu_workspace_size": (_SZ, [_I64, _I64, _I32]),
     "qkdec_gemm_q4k_swiglu": (_I32, [_P, _I64, _I64, _P, _I64, _I32, _P, _I64, _P, _SZ, _P]),
     "qkdec_dequant_q4k": (_I32, [_P, _I64, _P, _P]),
@@ -88,6 +95,9 @@ _SIGNATURES = {
     "qkdec_workspace_init": (_I32, [_P, _SZ, _P]),
     "qkdec_step": (_I32, [ctypes.POINTER(Model), ctypes.POINTER(KVLayer), _P, _P, _P, _I32, _P, _P, _SZ, _P]),
     "qkdec_step_status": (_I32, [_P, _P]),
+    "qkdec_prefill_workspace_size": (_SZ, [ctypes.POINTER(Model), ctypes.POINTER(KVLayer)]),
+    "qkdec_prefill": (_I32, [ctypes.POINTER(Model), ctypes.POINTER(KVLayer), _I32, _I32, _P, _I32, _P, _P, _P, _SZ,
+                             _P]),
     "qkdec_step_noalloc_max_bytes": (_SZ, []),
     "qkdec_step_noalloc": (_I32, [ctypes.POINTER(Model), ctypes.POINTER(KVLayer), _P, _P, _P, _I32, _P, _P, _P]),
     "qkdec_step_paged_workspace_size": (_SZ, [ctypes.POINTER(Model), _I32, ctypes.POINTER(KVLayer), _I32]),
@@ -156,6 +166,16 @@ def qkdec_gemm_q4k(w, n: int, k: int, x, b: int, y, residual=None, workspace=Non
     _check(lib.qkdec_gemm_q4k(_ptr(w), n, k, _ptr(x), x.stride(0), b, _ptr(y), y.stride(0), _ptr(residual),
                               residual.stride(0) if residual is not None else 0, _ptr(workspace), ws_bytes,
                               _stream(stream)), "qkdec_gemm_q4k")
+
+
+def qkdec_gemm_q4k_engine(w, n: int, k: int, x, b: int, y, engine: int, residual=None, workspace=None,
+                          stream=None) -> None:
+    """qkdec_gemm_q4k with the engine chosen (GEMM_AUTO, GEMM_MFMA or GEMM_MATVEC)."""
+    lib = load_library()
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.qkdec_gemm_q4k_engine(_ptr(w), n, k, _ptr(x), x.stride(0), b, _ptr(y), y.stride(0), _ptr(residual),
+                                     residual.stride(0) if residual is not None else 0, engine, _ptr(workspace),
+                                     ws_bytes, _stream(stream)), "qkdec_gemm_q4k_engine")
 
 
 def qkdec_gemm_q4k_xf32(w, n: int, k: int, x, b: int, y, residual=None, workspace=None, stream=None) -> None:
@@ -282,6 +302,20 @@ def qkdec_step_paged(sm: StepModel, pages, max_pages: int, pos, tok, b: int, wor
                                            _ptr(tok), b, _ptr(logits), _ptr(workspace),
                                            workspace.numel() * workspace.element_size(), _stream(stream)),
            "qkdec_step_paged")
+
+
+def qkdec_prefill_workspace_size(sm: StepModel) -> int:
+    return load_library().qkdec_prefill_workspace_size(ctypes.byref(sm.model), sm.kv_arr)
+
+
+def qkdec_prefill(sm: StepModel, slot: int, start: int, tokens, n: int, tok_out, workspace, logits=None,
+                  stream=None) -> None:
+    """Append prompt tokens (device int32 [n]) at positions start.. of slot;
+    tok_out (device int32 [1]) gets the argmax after the last one."""
+    _check(load_library().qkdec_prefill(ctypes.byref(sm.model), sm.kv_arr, slot, start, _ptr(tokens), n,
+                                        _ptr(logits), _ptr(tok_out), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(stream)),
+           "qkdec_prefill")
 
 
 def qkdec_step_noalloc_max_bytes() -> int:

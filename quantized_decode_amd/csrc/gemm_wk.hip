@@ -50,7 +50,7 @@ struct WkArgs {
   RopeAppendArgs ra;     // MODE 2 (gemm_wi_kernel): QKV finish, fp16 cache
   int qh;                // MODE 2: tiles per half head (head_dim / 32)
   float* part;           // K split over work-groups (gemm_wi_kernel): partial sums [chunk][B][N]
-  unsigned* counters;    // ... and one arrival counter per output tile (zero between launches)
+  unsigned* counters;    // ... and one arrival counter per row group (zero between launches)
 };
 
 // The hi/lo sums of sub-blocks 2g (pieces 0..3) and 2g+1 (pieces 4..7) of av
@@ -379,10 +379,18 @@ __device__ void qkv_finish(const WkArgs& a, Red red, int wave, int lane, int g, 
 // KSPLIT > 1 (MODE 0): K is cut into KSPLIT chunks of S KW super-blocks;
 // work-group i takes chunk i / (grid / KSPLIT), and the last of a tile's
 // chunks to arrive adds the chunks' partial sums in chunk order.
-template <int MODE, int XMODE, int S, int KW, int IPW, int PD, int KSPLIT = 1>
+// MV > 0 (the small-batch matvec, B = MV <= 2 sequences): the same items,
+// staging and finishes, with each super-block's products formed on the vector
+// ALU (q4_superblock_mv) for the live sequences only instead of on the
+// matrix cores for a tile padded to 16; lane (g, r) then holds the sums of
+// row r over its K slice for every sequence, which two lane exchanges add
+// over g and which are laid out as the MFMA's results for the finish.
+template <int MODE, int XMODE, int S, int KW, int IPW, int PD, int KSPLIT = 1, int MV = 0>
 __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
   constexpr int T = MODE == 1 ? 2 : 1;   // weight tiles per item
   static_assert(KSPLIT == 1 || MODE == 0, "K split: plain outputs only");
+  static_assert(MV >= 0 && MV <= 2, "matvec: one or two sequences");
+  constexpr int NM = MV > 0 ? MV : 1;
   static_assert(IPW <= S && PD <= IPW, "one finishing wave per item");
   static_assert(MODE != 2 || (IPW == 2 && XMODE == kXNorm), "QKV finish: a tile pair, RMSNorm fused");
   // LDS: kXNorm first holds the normalized activations h [16][K + 8] (fp16),
@@ -423,6 +431,24 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
   half8_t av[KW][8];
   half4_t axs[KW];
   floatx4 fd[KW], fm[KW];
+  // MV: the K slice's activations of every sequence (lane (g, r): values
+  // 64g..64g+63 of each super-block), their sub-block sums and d factors
+  half8_t xm[KW][NM][8];
+  float xs[KW][NM][2], fdm[KW][NM];
+  // sums of the two sub-blocks (pieces 0..3, 4..7) of one row's 64 values
+  auto mv_sums = [&](int p, int b) {
+    const half2_t one = {(half_t)1.f, (half_t)1.f};
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        s0 = __builtin_amdgcn_fdot2(half2_t{xm[p][b][j][e], xm[p][b][j][e + 1]}, one, s0, false);
+        s1 = __builtin_amdgcn_fdot2(half2_t{xm[p][b][4 + j][e], xm[p][b][4 + j][e + 1]}, one, s1, false);
+      }
+    xs[p][b][0] = s0;
+    xs[p][b][1] = s1;
+  };
   // kXNorm: slots of the sum-of-squares fold, gains and x rows 0..7 of the
   // thread's float4 columns tx + 64 S c (c < KW)
   SsFold<64 * S, (XMODE == kXNorm ? K / kSsCols : 0)> ssf;   // the K inputs have K / 16 slots
@@ -452,12 +478,23 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
     }
   } else if constexpr (XMODE == kXF16) {
     const half_t* X16 = reinterpret_cast<const half_t*>(a.X);
-    const int rr = r < a.B ? r : a.B - 1;
+    if constexpr (MV > 0) {
 #pragma unroll
-    for (int p = 0; p < KW; ++p)
+      for (int p = 0; p < KW; ++p)
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        av[p][j] = *reinterpret_cast<const half8_t*>(X16 + (size_t)rr * a.ldx + (sb0 + p) * 256 + 64 * g + 8 * j);
+        for (int b = 0; b < MV; ++b)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            xm[p][b][j] =
+                *reinterpret_cast<const half8_t*>(X16 + (size_t)b * a.ldx + (sb0 + p) * 256 + 64 * g + 8 * j);
+    } else {
+      const int rr = r < a.B ? r : a.B - 1;
+#pragma unroll
+      for (int p = 0; p < KW; ++p)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          av[p][j] = *reinterpret_cast<const half8_t*>(X16 + (size_t)rr * a.ldx + (sb0 + p) * 256 + 64 * g + 8 * j);
+    }
   }
   // MODE 2: slot and position of the lane's rows 4g + ii, and of row tx / 16
   // for the rotary table
@@ -574,6 +611,17 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int p = 0; p < KW; ++p) {
+      if constexpr (MV > 0) {
+#pragma unroll
+        for (int b = 0; b < MV; ++b) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            xm[p][b][j] = *reinterpret_cast<const half8_t*>(hs + b * LDH + (sbl + p) * 256 + 64 * g + 8 * j);
+          mv_sums(p, b);
+          fdm[p][b] = 1.f;
+        }
+        continue;
+      }
       const half_t* src = hs + (r < a.B ? r : 0) * LDH + (sbl + p) * 256 + 64 * g;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -646,6 +694,17 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int p = 0; p < KW; ++p) {
+      if constexpr (MV > 0) {
+#pragma unroll
+        for (int b = 0; b < MV; ++b) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            xm[p][b][j] = *reinterpret_cast<const half8_t*>(hs + b * LDH + (sbl + p) * 256 + 64 * g + 8 * j);
+          mv_sums(p, b);
+          fdm[p][b] = s_fac[sbl + p][b];
+        }
+        continue;
+      }
       const half_t* src = hs + (r < a.B ? r : 0) * LDH + (sbl + p) * 256 + 64 * g;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -675,6 +734,14 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
     static_assert(XMODE == kXF16, "fp16 or fp32 activations");
 #pragma unroll
     for (int p = 0; p < KW; ++p) {
+      if constexpr (MV > 0) {
+#pragma unroll
+        for (int b = 0; b < MV; ++b) {
+          mv_sums(p, b);
+          fdm[p][b] = 1.f;
+        }
+        continue;
+      }
       if (r >= a.B)
 #pragma unroll
         for (int j = 0; j < 8; ++j) av[p][j] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
@@ -696,17 +763,49 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
       floatx4 acc[T];
 #pragma unroll
       for (int tt = 0; tt < T; ++tt) acc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (MV > 0) {
+        float accm[T][MV];
 #pragma unroll
-      for (int p = 0; p < KW; ++p)
+        for (int tt = 0; tt < T; ++tt)
 #pragma unroll
-        for (int tt = 0; tt < T; ++tt) {
-          floatx4 sq, sm;
-          float d, dm;
-          q4_superblock(fr[it % PD][p][tt], av[p], axs[p], g, km, sq, sm, d, dm);
+          for (int b = 0; b < MV; ++b) accm[tt][b] = 0.f;
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii)
-            acc[tt][ii] = __builtin_fmaf(d * fd[p][ii], sq[ii], __builtin_fmaf(-dm * fm[p][ii], sm[ii], acc[tt][ii]));
-        }
+        for (int p = 0; p < KW; ++p)
+#pragma unroll
+          for (int tt = 0; tt < T; ++tt) {
+            float sq[MV], sm[MV];
+            float d, dm;
+            q4_superblock_mv<MV>(fr[it % PD][p][tt], xm[p], xs[p], g, km, sq, sm, d, dm);
+#pragma unroll
+            for (int b = 0; b < MV; ++b)
+              accm[tt][b] = __builtin_fmaf(d * fdm[p][b], sq[b], __builtin_fmaf(-dm * fdm[p][b], sm[b], accm[tt][b]));
+          }
+        // lanes r, r + 16, r + 32, r + 48 hold the four 64-value pieces of
+        // row r; their sum, for sequence b, goes where the MFMA would leave
+        // it: lane (0, r), element b
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt)
+#pragma unroll
+          for (int b = 0; b < MV; ++b) {
+            float v = accm[tt][b];
+            v += __shfl_xor(v, 16);
+            v += __shfl_xor(v, 32);
+            acc[tt][b] = g == 0 ? v : 0.f;
+          }
+      } else {
+#pragma unroll
+        for (int p = 0; p < KW; ++p)
+#pragma unroll
+          for (int tt = 0; tt < T; ++tt) {
+            floatx4 sq, sm;
+            float d, dm;
+            q4_superblock(fr[it % PD][p][tt], av[p], axs[p], g, km, sq, sm, d, dm);
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+              acc[tt][ii] =
+                  __builtin_fmaf(d * fd[p][ii], sq[ii], __builtin_fmaf(-dm * fm[p][ii], sm[ii], acc[tt][ii]));
+          }
+      }
       if (it + PD < IPW) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -726,7 +825,9 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
     qkv_finish<S>(a, red, wave, lane, g, r, head, hj, sl, ps, s_rope);
     return;
   }
-  if (wave >= n_items) return;
+  // (with K split across work-groups every wave takes part in the arrival
+  // below, so the waves without an item leave only after it)
+  if (KSPLIT == 1 && wave >= n_items) return;
   floatx4 v[T];
 #pragma unroll
   for (int tt = 0; tt < T; ++tt) {
@@ -746,27 +847,36 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
   const int item = item0 + wave;
   const int n = item * 16 + r;
   if constexpr (MODE == 0 && KSPLIT > 1) {
-    // this chunk's partial sums, stored through to the device-coherent level;
-    // the last chunk to arrive for the tile adds all chunks in chunk order
+    // this chunk's partial sums of the work-group's items (wave i: item i);
+    // the last of the row group's KSPLIT work-groups to arrive adds the
+    // chunks of every item in chunk order.  One arrival per work-group: the
+    // barrier orders every wave's stores before thread 0's agent-scope
+    // release, which publishes them ahead of the count; the last arriver's
+    // acquire orders the reloads after it.
+    __shared__ int s_last;
     const int n_total = a.f_tiles * 16;
+    const int grp = (int)blockIdx.x % n_groups;
+    if (wave < n_items) {
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int b = 4 * g + ii;
-      if (b < a.B)
-        __hip_atomic_store(&a.part[((size_t)kc * a.B + b) * n_total + n], v[0][ii], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+      for (int ii = 0; ii < 4; ++ii) {
+        const int b = 4 * g + ii;
+        if (b < a.B)
+          __hip_atomic_store(&a.part[((size_t)kc * a.B + b) * n_total + n], v[0][ii], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
-    // one wave stores the tile's chunk: its release (executed by every lane,
-    // ahead of lane 0's count) publishes the stores at device scope; the last
-    // arriver's acquire orders its partial loads after the count
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    unsigned prev = 0;
-    if (lane == 0)
-      prev = __hip_atomic_fetch_add(&a.counters[item], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    prev = __shfl(prev, 0);
-    if (prev != (unsigned)(KSPLIT - 1)) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    if (lane == 0) __hip_atomic_store(&a.counters[item], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (tx == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      const unsigned prev = __hip_atomic_fetch_add(&a.counters[grp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = prev == (unsigned)(KSPLIT - 1);
+      if (s_last) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __hip_atomic_store(&a.counters[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();
+    if (!s_last || wave >= n_items) return;
     float pv[KSPLIT][4];
 #pragma unroll
     for (int cc = 0; cc < KSPLIT; ++cc)
@@ -855,18 +965,42 @@ static void launch_mode(int s, int items, const WkArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((gemm_wk_kernel<MODE, XMODE, 4, 2>), dim3(items), dim3(256), 0, st, a);
 }
 
+// One configuration of the multi-item kernel, as the MFMA tiles (mv = 0) or
+// the matvec for mv = B in {1, 2} sequences.
+// SwiGLU items hold two weight tiles each: with two items in flight the
+// matvec of two sequences spills, so that combination is never built (the
+// caller takes one item in flight for it)
+template <int MODE, int PD>
+constexpr bool wi_mv2_fits() {
+  return !(MODE == 1 && PD > 1);
+}
+template <int MODE, int XMODE, int S, int KW, int IPW, int PD, int KSPLIT = 1>
+static void launch_wi(int mv, dim3 grid, const WkArgs& a, hipStream_t st) {
+  if (mv == 1) {
+    hipLaunchKernelGGL((gemm_wi_kernel<MODE, XMODE, S, KW, IPW, PD, KSPLIT, 1>), grid, dim3(64 * S), 0, st, a);
+  } else if (mv == 2) {
+    if constexpr (wi_mv2_fits<MODE, PD>())
+      hipLaunchKernelGGL((gemm_wi_kernel<MODE, XMODE, S, KW, IPW, PD, KSPLIT, 2>), grid, dim3(64 * S), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((gemm_wi_kernel<MODE, XMODE, S, KW, IPW, PD, KSPLIT, 0>), grid, dim3(64 * S), 0, st, a);
+  }
+}
+
 // Multi-item launch for the shapes it is built for; hipErrorNotSupported
-// otherwise (the caller then uses another kernel).  K = 4096 only (16 waves of
+// otherwise (the caller then uses another kernel).  K = 4096 (16 waves of
 // one super-block each):
 //   SwiGLU: three gate/up tile pairs per work-group, two in flight (768 pairs
 //     for F = 12288: 256 work-groups);
 //   plain, RMSNorm fused: two tiles per work-group (6144 rows: 192);
 //   plain, fp16 activations: one tile per work-group up to 4096 rows, else two.
+// K = 12288, plain (fp32 activations with the blocked fp16 rounding, or fp16):
+// four K chunks of 3072 (12 waves), four tiles per work-group.
 hipError_t launch_gemm_wi(const GemmLaunch& L, hipStream_t st) {
   const int kb = (int)(L.K / 256);
   const int64_t items = L.n_rows / 16;
   const int xmode = L.x_f32 ? (L.gamma ? kXNorm : kXF32Blocked) : kXF16;
-  if (kb != 16 && !(kb == 48 && xmode == kXF32Blocked)) return hipErrorNotSupported;
+  if (kb != 16 && !(kb == 48 && xmode != kXNorm && !L.swiglu)) return hipErrorNotSupported;
+  const int mv = gemm_matvec_rows(L.kernel, L.B);
   WkArgs a{};
   a.W = reinterpret_cast<const uint8_t*>(L.W);
   a.X = L.X;
@@ -886,30 +1020,34 @@ hipError_t launch_gemm_wi(const GemmLaunch& L, hipStream_t st) {
   a.ss_slots = (int)(L.K / kSsCols);
   a.eps = L.eps;
   a.inv_k = 1.0f / (float)L.K;
-  if (xmode == kXF32Blocked) {
-    // K = 12288 (fp32 activations, blocked fp16 rounding): four K chunks of
-    // 3072 (12 waves of one super-block), four tiles per work-group: 256
-    // work-groups for N = 4096, one round on the chip
-    if (kb != 48 || L.swiglu) return hipErrorNotSupported;
+  if (kb == 48) {
+    // K = 12288: four K chunks of 3072 (12 waves of one super-block), four
+    // tiles per work-group: 256 work-groups for N = 4096, one round on the chip
     char* p = reinterpret_cast<char*>(L.ws);
     a.counters = reinterpret_cast<unsigned*>(p);
     a.part = reinterpret_cast<float*>(p + (size_t)kGemmMaxGroups * 4);
-    const unsigned groups = (unsigned)((items + 3) / 4);
-    hipLaunchKernelGGL((gemm_wi_kernel<0, kXF32Blocked, 12, 1, 4, 2, 4>), dim3(groups * 4), dim3(768), 0, st, a);
+    const dim3 grid((unsigned)((items + 3) / 4) * 4);
+    if (xmode == kXF32Blocked) launch_wi<0, kXF32Blocked, 12, 1, 4, 2, 4>(mv, grid, a, st);
+    else launch_wi<0, kXF16, 12, 1, 4, 2, 4>(mv, grid, a, st);
     return hipGetLastError();
   }
   if (L.swiglu) {
+    // two sequences on the vector ALU hold one item's weights in flight (two
+    // would spill)
     const dim3 grid((unsigned)((items + 2) / 3));
-    if (xmode == kXNorm) hipLaunchKernelGGL((gemm_wi_kernel<1, kXNorm, 16, 1, 3, 2>), grid, dim3(1024), 0, st, a);
-    else hipLaunchKernelGGL((gemm_wi_kernel<1, kXF16, 16, 1, 3, 2>), grid, dim3(1024), 0, st, a);
+    if (xmode == kXNorm) {
+      if (mv == 2) launch_wi<1, kXNorm, 16, 1, 3, 1>(mv, grid, a, st);
+      else launch_wi<1, kXNorm, 16, 1, 3, 2>(mv, grid, a, st);
+    } else {
+      if (mv == 2) launch_wi<1, kXF16, 16, 1, 3, 1>(mv, grid, a, st);
+      else launch_wi<1, kXF16, 16, 1, 3, 2>(mv, grid, a, st);
+    }
   } else if (xmode == kXNorm) {
-    hipLaunchKernelGGL((gemm_wi_kernel<0, kXNorm, 16, 1, 2, 2>), dim3((unsigned)((items + 1) / 2)), dim3(1024), 0,
-                       st, a);
+    launch_wi<0, kXNorm, 16, 1, 2, 2>(mv, dim3((unsigned)((items + 1) / 2)), a, st);
   } else if (items <= 256) {
-    hipLaunchKernelGGL((gemm_wi_kernel<0, kXF16, 16, 1, 1, 1>), dim3((unsigned)items), dim3(1024), 0, st, a);
+    launch_wi<0, kXF16, 16, 1, 1, 1>(mv, dim3((unsigned)items), a, st);
   } else {
-    hipLaunchKernelGGL((gemm_wi_kernel<0, kXF16, 16, 1, 2, 2>), dim3((unsigned)((items + 1) / 2)), dim3(1024), 0,
-                       st, a);
+    launch_wi<0, kXF16, 16, 1, 2, 2>(mv, dim3((unsigned)((items + 1) / 2)), a, st);
   }
   return hipGetLastError();
 }
@@ -941,7 +1079,7 @@ hipError_t launch_gemm_wi_qkv(const GemmLaunch& L, const RopeAppendArgs& ra, int
   a.ra = ra;
   a.qh = head_dim / 32;
   const int n_heads = (int)(L.n_rows / head_dim);
-  hipLaunchKernelGGL((gemm_wi_kernel<2, kXNorm, 16, 1, 2, 2>), dim3((unsigned)(n_heads * a.qh)), dim3(1024), 0, st, a);
+  launch_wi<2, kXNorm, 16, 1, 2, 2>(gemm_matvec_rows(L.kernel, L.B), dim3((unsigned)(n_heads * a.qh)), a, st);
   return hipGetLastError();
 }
 

@@ -41,7 +41,15 @@ struct GemmLaunch {
   void* ws = nullptr;
   int force_kc = 0;    // 0: K chunk chosen by shape
   int force_wpb = 0;   // 0: waves per work-group chosen by shape (4, 8 or 16)
+  int kernel = 0;      // QKDEC_GEMM_AUTO / _MFMA / _MATVEC (multi-item shapes)
 };
+// Whether a multi-item launch of B sequences runs the vector-ALU matvec
+// (gemm_wi_kernel MV = B) rather than the MFMA tiles: on request, or for
+// QKDEC_GEMM_AUTO at B <= QKDEC_MATVEC_AUTO_MAX_B.
+inline int gemm_matvec_rows(int kernel, int B) {
+  const bool want = kernel == QKDEC_GEMM_MATVEC || (kernel == QKDEC_GEMM_AUTO && B <= QKDEC_MATVEC_AUTO_MAX_B);
+  return want && B <= QKDEC_MATVEC_MAX_B ? B : 0;
+}
 hipError_t launch_gemm(const GemmLaunch& L, hipStream_t st);
 // The QKV projection of a decode step (RMSNorm fused, L.x_f32 + L.gamma),
 // finished per head: Y gets the fp32 projection, then q and k are rotated
@@ -176,5 +184,9 @@ inline size_t lm_head_lds_bytes(int64_t H, int B) { return (size_t)B * (size_t)(
 hipError_t launch_lm_head_argmax(const uint16_t* Wlm, int64_t V, int64_t H, const uint16_t* X, int B,
                                  float* logits, int32_t* tok, void* partials, int32_t* pos_inc, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+// the rows of one prefill chunk: slot[b] = s, pos[b] = start + b,
+// tok[b] = tokens[b] for b < rows (tokens: device int32)
+hipError_t launch_prefill_rows(int s, int start, const int32_t* tokens, int rows, int32_t* slot, int32_t* pos,
+                               int32_t* tok, hipStream_t st);
 
 }  // namespace qk

@@ -52,35 +52,84 @@ __device__ __forceinline__ half8_t decode_word(uint32_t w, const NibbleMasks& k,
   return b;
 }
 
-// One super-block of one 16-row tile: sq = X . (sc*q), sm = xsums . m (per
-// sequence row), with d and dmin returned for the deferred accumulation.
-__device__ __forceinline__ void q4_superblock(const Q4Frag& f, const half8_t (&a)[8], const half4_t& axs, int g,
-                                              const NibbleMasks& k, floatx4& sq, floatx4& sm, float& d,
-                                              float& dmin) {
+// The block header fields lane (g, r) needs: d, dmin, the mins m0, m1 of its
+// sub-blocks 2g, 2g+1, and the packed constants that turn a nibble expanded
+// to 1024 + q (or 1024 + 16q) into sc * q exactly (decode_word).
+struct Q4Header {
+  float d, dmin, m0, m1;
+  half2_t s1a, c1a, s16a, c16a, s1b, c1b, s16b, c16b;
+};
+
+__device__ __forceinline__ Q4Header q4_header(const Q4Frag& f, int g) {
+  Q4Header h;
   const uint32_t h0 = f.hdr[0], h1 = f.hdr[1], h2 = f.hdr[2], h3 = f.hdr[3];
-  d = h2f(h0 & 0xffffu);
-  dmin = h2f(h0 >> 16);
+  h.d = h2f(h0 & 0xffffu);
+  h.dmin = h2f(h0 >> 16);
   // the 24-bit scale group of sub-blocks 2g, 2g+1 sits at bit 24g of bytes 4..15
   const uint32_t lo = (g < 2) ? h1 : (g == 2 ? h2 : h3);
   const uint32_t hi = (g < 2) ? h2 : h3;
   const uint32_t grp = __builtin_amdgcn_alignbit(hi, lo, (24u * (uint32_t)g) & 31u);
   const float sc0 = (float)(grp & 63u), sc1 = (float)((grp >> 6) & 63u);
-  const float m0 = (float)((grp >> 12) & 63u), m1 = (float)((grp >> 18) & 63u);
-  const half2_t s1a = pack_h2(sc0, sc0), c1a = pack_h2(-1024.f * sc0, -1024.f * sc0);
-  const half2_t s16a = pack_h2(sc0 * 0.0625f, sc0 * 0.0625f), c16a = pack_h2(-64.f * sc0, -64.f * sc0);
-  const half2_t s1b = pack_h2(sc1, sc1), c1b = pack_h2(-1024.f * sc1, -1024.f * sc1);
-  const half2_t s16b = pack_h2(sc1 * 0.0625f, sc1 * 0.0625f), c16b = pack_h2(-64.f * sc1, -64.f * sc1);
-  const half2_t mm = pack_h2(m0, m1);
+  h.m0 = (float)((grp >> 12) & 63u);
+  h.m1 = (float)((grp >> 18) & 63u);
+  h.s1a = pack_h2(sc0, sc0); h.c1a = pack_h2(-1024.f * sc0, -1024.f * sc0);
+  h.s16a = pack_h2(sc0 * 0.0625f, sc0 * 0.0625f); h.c16a = pack_h2(-64.f * sc0, -64.f * sc0);
+  h.s1b = pack_h2(sc1, sc1); h.c1b = pack_h2(-1024.f * sc1, -1024.f * sc1);
+  h.s16b = pack_h2(sc1 * 0.0625f, sc1 * 0.0625f); h.c16b = pack_h2(-64.f * sc1, -64.f * sc1);
+  return h;
+}
+
+// Weights 8j..8j+7 of the lane's 64 (sub-block 2g for j < 4, 2g+1 after), as
+// sc * q in fp16.
+__device__ __forceinline__ half8_t q4_word(const Q4Frag& f, const Q4Header& h, int j, const NibbleMasks& k) {
+  const uint32_t w = j < 4 ? f.q0[j] : f.q1[j - 4];
+  return j < 4 ? decode_word(w, k, h.s1a, h.c1a, h.s16a, h.c16a) : decode_word(w, k, h.s1b, h.c1b, h.s16b, h.c16b);
+}
+
+// One super-block of one 16-row tile: sq = X . (sc*q), sm = xsums . m (per
+// sequence row), with d and dmin returned for the deferred accumulation.
+__device__ __forceinline__ void q4_superblock(const Q4Frag& f, const half8_t (&a)[8], const half4_t& axs, int g,
+                                              const NibbleMasks& k, floatx4& sq, floatx4& sm, float& d,
+                                              float& dmin) {
+  const Q4Header h = q4_header(f, g);
+  d = h.d;
+  dmin = h.dmin;
+  const half2_t mm = pack_h2(h.m0, h.m1);
   half4_t bm;
   bm[0] = mm[0]; bm[1] = mm[1]; bm[2] = mm[0]; bm[3] = mm[1];
-  const uint32_t words[8] = {f.q0[0], f.q0[1], f.q0[2], f.q0[3], f.q1[0], f.q1[1], f.q1[2], f.q1[3]};
   const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
   sm = __builtin_amdgcn_mfma_f32_16x16x16f16(axs, bm, zero, 0, 0, 0);
   sq = zero;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) sq = mfma16x16x32(a[j], decode_word(words[j], k, s1a, c1a, s16a, c16a), sq);
+  for (int j = 0; j < 8; ++j) sq = mfma16x16x32(a[j], q4_word(f, h, j, k), sq);
+}
+
+// The same super-block on the vector ALU for NB <= 2 sequences (the
+// small-batch matvec): the lane decodes exactly the weights it decodes for
+// the MFMA (row r, weights 64g..64g+63) and forms, per sequence b, the packed
+// fp16 dot products sq[b] = sum_k x_b[k] sc q_k (fp32 accumulation; every
+// product exact) and sm[b] = m0 X_b,2g + m1 X_b,2g+1 from the sub-block sums
+// xs[b] (fp32).  No matrix-core instruction and no padding of the batch.
+template <int NB>
+__device__ __forceinline__ void q4_superblock_mv(const Q4Frag& f, const half8_t (&x)[NB][8], const float (&xs)[NB][2],
+                                                 int g, const NibbleMasks& k, float (&sq)[NB], float (&sm)[NB],
+                                                 float& d, float& dmin) {
+  const Q4Header h = q4_header(f, g);
+  d = h.d;
+  dmin = h.dmin;
 #pragma unroll
-  for (int j = 4; j < 8; ++j) sq = mfma16x16x32(a[j], decode_word(words[j], k, s1b, c1b, s16b, c16b), sq);
+  for (int b = 0; b < NB; ++b) sq[b] = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const half8_t w = q4_word(f, h, j, k);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2)
+        sq[b] = __builtin_amdgcn_fdot2(half2_t{x[b][j][e], x[b][j][e + 1]}, half2_t{w[e], w[e + 1]}, sq[b], false);
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) sm[b] = __builtin_fmaf(h.m0, xs[b][0], h.m1 * xs[b][1]);
 }
 
 

@@ -147,10 +147,12 @@ StepWs step_layout(const qkdec_model* m, int B, const qkdec_kv_layer* kv, char* 
 // are pages[b * max_pages ...]; slot is unused
 // err != nullptr: the capacity flag goes there instead of the workspace's
 // error word
-qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int32_t* slot, int32_t* pos,
-                      int32_t* tok, int B, float* logits, void* workspace, hipStream_t st,
-                      const int32_t* pages = nullptr, int max_pages = 0, int32_t* err = nullptr) {
-  const StepWs w = step_layout(m, B, kv, reinterpret_cast<char*>(workspace), max_pages);
+// The embedding and every layer of a step for B rows (row b: token tok[b] at
+// position pos[b] of slot slot[b]), leaving the residual stream in w.x and its
+// sum-of-squares slots in w.ss; w may be laid out for more rows than B.
+qkdec_status run_layers(const qkdec_model* m, const qkdec_kv_layer* kv, const int32_t* slot, const int32_t* pos,
+                        const int32_t* tok, int B, const StepWs& w, hipStream_t st, const int32_t* pages,
+                        int max_pages, int32_t* err) {
   int32_t* const err_word = err ? err : w.err;
   const int H = m->hidden, F = m->ffn, D = m->head_dim, Hq = m->n_q_heads;
   const int64_t hq = (int64_t)Hq * D;
@@ -217,9 +219,58 @@ qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int3
     dn.Y = w.x; dn.ldy = H; dn.residual = w.x; dn.ldr = H; dn.ss_out = w.ss; dn.ws = w.gemm_ws;
     QK_TRY(launch_gemm(dn, st));
   }
-  QK_TRY(launch_rmsnorm_f16(w.x, m->norm_final, w.ss, H, B, m->rms_eps, w.h, st));
-  QK_TRY(launch_lm_head_argmax(m->lm_head, m->vocab, H, w.h, B, logits, tok, w.lm_part, pos, st));
 #undef QK_TRY
+  return QKDEC_OK;
+}
+
+// err != nullptr: the capacity flag goes there instead of the workspace's
+// error word
+qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int32_t* slot, int32_t* pos,
+                      int32_t* tok, int B, float* logits, void* workspace, hipStream_t st,
+                      const int32_t* pages = nullptr, int max_pages = 0, int32_t* err = nullptr) {
+  const StepWs w = step_layout(m, B, kv, reinterpret_cast<char*>(workspace), max_pages);
+  const qkdec_status s = run_layers(m, kv, slot, pos, tok, B, w, st, pages, max_pages, err);
+  if (s != QKDEC_OK) return s;
+  if (launch_rmsnorm_f16(w.x, m->norm_final, w.ss, m->hidden, B, m->rms_eps, w.h, st) != hipSuccess)
+    return QKDEC_E_HIP;
+  if (launch_lm_head_argmax(m->lm_head, m->vocab, m->hidden, w.h, B, logits, tok, w.lm_part, pos, st) != hipSuccess)
+    return QKDEC_E_HIP;
+  return QKDEC_OK;
+}
+
+// ---- prefill: the prompt in chunks of up to kPrefillRows tokens, each chunk
+// one pass of the layers with its tokens as the rows (same slot, consecutive
+// positions); the workspace is laid out once for kPrefillRows rows, followed
+// by the chunk's row arrays
+constexpr int kPrefillRows = 16;
+
+size_t prefill_bytes(const qkdec_model* m, const qkdec_kv_layer* kv) {
+  return step_layout(m, kPrefillRows, kv, nullptr).bytes + 3 * 256;
+}
+
+qkdec_status run_prefill(const qkdec_model* m, const qkdec_kv_layer* kv, int slot, int start, const int32_t* tokens,
+                         int n, float* logits, int32_t* tok_out, void* workspace, hipStream_t st) {
+  char* base = reinterpret_cast<char*>(workspace);
+  const StepWs w = step_layout(m, kPrefillRows, kv, base);
+  int32_t* rs = reinterpret_cast<int32_t*>(base + w.bytes);
+  int32_t* rp = rs + 64;
+  int32_t* rt = rs + 128;
+  int rows = 0;
+  for (int off = 0; off < n; off += kPrefillRows) {
+    rows = n - off < kPrefillRows ? n - off : kPrefillRows;
+    if (launch_prefill_rows(slot, start + off, tokens + off, rows, rs, rp, rt, st) != hipSuccess) return QKDEC_E_HIP;
+    const qkdec_status s = run_layers(m, kv, rs, rp, rt, rows, w, st, nullptr, 0, nullptr);
+    if (s != QKDEC_OK) return s;
+  }
+  // final norm and LM head of the prompt's last token only (row rows - 1 of
+  // the last chunk; its sum-of-squares slots are every 16th value from row)
+  const int last = rows - 1;
+  if (launch_rmsnorm_f16(w.x + (size_t)last * m->hidden, m->norm_final, w.ss + last, m->hidden, 1, m->rms_eps, w.h,
+                         st) != hipSuccess)
+    return QKDEC_E_HIP;
+  if (launch_lm_head_argmax(m->lm_head, m->vocab, m->hidden, w.h, 1, logits, tok_out, w.lm_part, nullptr, st) !=
+      hipSuccess)
+    return QKDEC_E_HIP;
   return QKDEC_OK;
 }
 
@@ -293,11 +344,30 @@ qkdec_status qkdec_gemm_q4k(const void* W, int64_t N, int64_t K, const uint16_t*
   if (!workspace || ws_bytes < gemm_workspace_bytes(N, K, B, false)) return QKDEC_E_WORKSPACE;
   if (!aligned(workspace, 256)) return QKDEC_E_ALIGN;
   clear_stale_error();
-  // K split over the waves of one work-group per output item (the kernels of
-  // the decode step's O projection): the workspace is not touched
+  // the multi-item kernel where it serves the shape (K split over the waves
+  // of a work-group; at K = 12288 also over four work-groups, through the
+  // workspace), else K over the waves of one work-group per tile
   GemmLaunch L{};
   L.W = W; L.n_rows = N; L.K = K; L.X = X; L.ldx = ldx; L.B = B;
-  L.Y = Y; L.ldy = ldy; L.residual = residual; L.ldr = ldr;
+  L.Y = Y; L.ldy = ldy; L.residual = residual; L.ldr = ldr; L.ws = workspace;
+  return hip_status(launch_gemm(L, as_stream(stream)));
+}
+
+qkdec_status qkdec_gemm_q4k_engine(const void* W, int64_t N, int64_t K, const uint16_t* X, int64_t ldx, int32_t B,
+                                   float* Y, int64_t ldy, const float* residual, int64_t ldr, int32_t engine,
+                                   void* workspace, size_t ws_bytes, void* stream) {
+  if (engine < QKDEC_GEMM_AUTO || engine > QKDEC_GEMM_MATVEC) return QKDEC_E_ARG;
+  if (engine == QKDEC_GEMM_MATVEC && B > QKDEC_MATVEC_MAX_B) return QKDEC_E_SHAPE;
+  qkdec_status s = check_gemm(W, N, K, X, ldx, B);
+  if (s != QKDEC_OK) return s;
+  if (!Y) return QKDEC_E_ARG;
+  if (ldy < N || (residual && ldr < N)) return QKDEC_E_SHAPE;
+  if (!workspace || ws_bytes < gemm_workspace_bytes(N, K, B, false)) return QKDEC_E_WORKSPACE;
+  if (!aligned(workspace, 256)) return QKDEC_E_ALIGN;
+  clear_stale_error();
+  GemmLaunch L{};
+  L.W = W; L.n_rows = N; L.K = K; L.X = X; L.ldx = ldx; L.B = B;
+  L.Y = Y; L.ldy = ldy; L.residual = residual; L.ldr = ldr; L.ws = workspace; L.kernel = engine;
   return hip_status(launch_gemm(L, as_stream(stream)));
 }
 
@@ -558,6 +628,27 @@ qkdec_status qkdec_step_noalloc(const qkdec_model* m, const qkdec_kv_layer* kv, 
   const size_t ctr = gemm_workspace_bytes(16, 256, 1, false);   // the fixed counter area at the start
   if (launch_fill_zero(w.gemm_ws, ctr, st) != hipSuccess) return QKDEC_E_HIP;
   return run_step(m, kv, slot, pos, tok, B, logits, base, st, nullptr, 0, err);
+}
+
+size_t qkdec_prefill_workspace_size(const qkdec_model* m, const qkdec_kv_layer* kv) {
+  if (check_model(m, kv) != QKDEC_OK) return 0;
+  return prefill_bytes(m, kv);
+}
+
+qkdec_status qkdec_prefill(const qkdec_model* m, const qkdec_kv_layer* kv, int32_t slot, int32_t start,
+                           const int32_t* tokens, int32_t n, float* logits, int32_t* tok_out, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  qkdec_status s = check_model(m, kv);
+  if (s != QKDEC_OK) return s;
+  if (!tokens || !tok_out) return QKDEC_E_ARG;
+  if (n < 1 || start < 0 || slot < 0 || slot >= kv[0].n_slots) return QKDEC_E_SHAPE;
+  if ((int64_t)start + n > kv[0].capacity) return QKDEC_E_CAPACITY;
+  if (!workspace || ws_bytes < prefill_bytes(m, kv)) return QKDEC_E_WORKSPACE;
+  if (!aligned(workspace, 256)) return QKDEC_E_ALIGN;
+  s = check_lds(lm_head_lds_bytes(m->hidden, kPrefillRows));
+  if (s != QKDEC_OK) return s;
+  clear_stale_error();
+  return run_prefill(m, kv, slot, start, tokens, n, logits, tok_out, workspace, as_stream(stream));
 }
 
 qkdec_status qkdec_step_status(void* workspace, void* stream) {

@@ -192,6 +192,21 @@ hipError_t launch_lm_head_argmax(const uint16_t* Wlm, int64_t V, int64_t H, cons
   return hipGetLastError();
 }
 
+__global__ void prefill_rows_kernel(int s, int start, const int32_t* tokens, int rows, int32_t* slot, int32_t* pos,
+                                    int32_t* tok) {
+  const int b = threadIdx.x;
+  if (b >= rows) return;
+  slot[b] = s;
+  pos[b] = start + b;
+  tok[b] = tokens[b];
+}
+
+hipError_t launch_prefill_rows(int s, int start, const int32_t* tokens, int rows, int32_t* slot, int32_t* pos,
+                               int32_t* tok, hipStream_t st) {
+  hipLaunchKernelGGL(prefill_rows_kernel, dim3(1), dim3(64), 0, st, s, start, tokens, rows, slot, pos, tok);
+  return hipGetLastError();
+}
+
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
   const size_t words = bytes / 4;
   if (words == 0) return hipSuccess;

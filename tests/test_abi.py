@@ -205,3 +205,20 @@ def test_noalloc_step_validation(lib):
                             _kv(n_kv_heads=2, head_dim=64, capacity=1 << 25, n_slots=16))
     assert lib.qkdec_step_workspace_size(ctypes.byref(m), 16, big) > cap
     assert step(ctypes.byref(m), big, FAKE, FAKE, FAKE, 16, None, FAKE, None) == -4
+
+
+def test_prefill_validation(lib):
+    layers = (qd.Layer * 2)(qd.Layer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE), qd.Layer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE))
+    m = qd.Model(2, 512, 8, 2, 64, 1536, 4096, 1e-6, 1e6, FAKE, FAKE, FAKE, ctypes.cast(layers, ctypes.POINTER(qd.Layer)))
+    kvs = (qd.KVLayer * 2)(_kv(n_kv_heads=2, head_dim=64, capacity=256, n_slots=2),
+                            _kv(n_kv_heads=2, head_dim=64, capacity=256, n_slots=2))
+    need = lib.qkdec_prefill_workspace_size(ctypes.byref(m), kvs)
+    assert need > lib.qkdec_step_workspace_size(ctypes.byref(m), 16, kvs)
+    pf = lib.qkdec_prefill
+    assert pf(ctypes.byref(m), kvs, 0, 0, None, 4, None, FAKE, FAKE, need, None) == -1      # no tokens
+    assert pf(ctypes.byref(m), kvs, 0, 0, FAKE, 4, None, None, FAKE, need, None) == -1      # no tok_out
+    assert pf(ctypes.byref(m), kvs, 2, 0, FAKE, 4, None, FAKE, FAKE, need, None) == -2      # slot outside
+    assert pf(ctypes.byref(m), kvs, 0, 0, FAKE, 0, None, FAKE, FAKE, need, None) == -2      # empty prompt
+    assert pf(ctypes.byref(m), kvs, 0, 250, FAKE, 7, None, FAKE, FAKE, need, None) == -5    # past capacity
+    assert pf(ctypes.byref(m), kvs, 0, 0, FAKE, 4, None, FAKE, FAKE, need - 1, None) == -4
+    assert pf(ctypes.byref(m), kvs, 0, 0, FAKE, 4, None, FAKE, FAKE + 16, need, None) == -3

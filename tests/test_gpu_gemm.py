@@ -136,10 +136,16 @@ def test_gemm_deterministic_and_batch_invariant(qd):
     y1 = _run_gemm(qd, mat, n, k, x)
     y2 = _run_gemm(qd, mat, n, k, x)
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
-    # each sequence's row does not depend on the others (same K chunking for B <= 8)
+    # each sequence's row does not depend on the others (same K chunking for
+    # B <= 8, and the same engine: one row alone would otherwise take the
+    # matvec, whose sums are rounded in another order)
+    import torch
+    w = ws(qd.qkdec_gemm_q4k_workspace_size(n, k, 1))
     for b in (0, 5):
-        yb = _run_gemm(qd, mat, n, k, x[b:b + 1])
-        assert np.array_equal(yb[0].view(np.uint32), y1[b].view(np.uint32))
+        yb = torch.empty((1, n), dtype=torch.float32, device="cuda")
+        qd.qkdec_gemm_q4k_engine(_dev(mat.reshape(-1)), n, k, _x16(x[b:b + 1]), 1, yb, qd.GEMM_MFMA, workspace=w)
+        sync()
+        assert np.array_equal(yb.cpu().numpy()[0].view(np.uint32), y1[b].view(np.uint32))
 
 
 def test_gemm_workspace_shared_across_shapes(qd):
@@ -237,3 +243,44 @@ def test_gemm_fp32_activations_blocked_rounding(qd, n, k, b):
     assert_rel(got2[:, rows], ref2, what=f"xf32 in-range {n}x{k} B={b}")
     rms = float(np.sqrt(np.mean(got3.astype(np.float64) ** 2)))
     assert float(np.abs(got2.astype(np.float64) - got3).max()) <= 1e-5 * rms, f"xf32 vs fp16 entry {n}x{k} B={b}"
+
+
+FULL_SHAPES = [(6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288)]
+
+
+@pytest.mark.parametrize("n,k", FULL_SHAPES)
+@pytest.mark.parametrize("b", [1, 2])
+@pytest.mark.parametrize("residual", [False, True])
+def test_gemm_matvec_engine_full_shapes(qd, n, k, b, residual):
+    # the vector-ALU matvec (no batch padding) on the projection shapes of the
+    # Qwen-shaped model, with and without a residual, against the oracle; and
+    # the MFMA engine on the same inputs within the same bound
+    import torch
+    rng = np.random.default_rng(n + k + b)
+    mat = synth.q4k_matrix(rng, n, k)
+    x = synth.f16_normal(rng, (b, k))
+    res = rng.standard_normal((b, n)).astype(np.float32) * 50 if residual else None
+    ref = OO.q4k_gemm(mat, n, k, x.astype(np.float64)) + (0 if res is None else res.astype(np.float64))
+    w = ws(qd.qkdec_gemm_q4k_workspace_size(n, k, b))
+    qd.qkdec_workspace_init(w)
+    for engine in (qd.GEMM_MATVEC, qd.GEMM_MFMA):
+        y = torch.empty((b, n), dtype=torch.float32, device="cuda")
+        qd.qkdec_gemm_q4k_engine(_dev(mat.reshape(-1)), n, k, _x16(x), b, y, engine,
+                                 residual=None if res is None else _dev(res), workspace=w)
+        sync()
+        assert_rel(y.cpu().numpy(), ref, what=f"engine {engine} {n}x{k} B={b}")
+
+
+def test_gemm_matvec_engine_limits(qd):
+    import torch
+    rng = np.random.default_rng(5)
+    mat = synth.q4k_matrix(rng, 64, 4096)
+    x = synth.f16_normal(rng, (3, 4096))
+    y = torch.empty((3, 64), dtype=torch.float32, device="cuda")
+    w = ws(qd.qkdec_gemm_q4k_workspace_size(64, 4096, 3))
+    with pytest.raises(qd.QkdecError) as e:
+        qd.qkdec_gemm_q4k_engine(_dev(mat.reshape(-1)), 64, 4096, _x16(x), 3, y, qd.GEMM_MATVEC, workspace=w)
+    assert e.value.status == -2
+    with pytest.raises(qd.QkdecError) as e:
+        qd.qkdec_gemm_q4k_engine(_dev(mat.reshape(-1)), 64, 4096, _x16(x), 3, y, 7, workspace=w)
+    assert e.value.status == -1

@@ -1,0 +1,104 @@
+"""Prefill (qkdec_prefill) on the GPU: the prompt's keys and values appended
+to the cache and the first generated token, against the oracle's prefill
+(the decode step over the prompt's tokens in order)."""
+import copy
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import step as OS
+from tests.gpu_util import LOGIT_ABS_TOL, sync, top2_gap, ws
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def qd():
+    import quantized_decode_amd as m
+    m.load_library()
+    return m
+
+
+def _prefill(qd, model, caches, slot, start, prompt):
+    import torch
+    from quantized_decode_amd.tensors import dev, upload_cache, upload_model
+    embed, lm_head, norm, layers = upload_model(model)
+    kv = [upload_cache(c) for c in caches]
+    sm = qd.StepModel(model.dims, embed, lm_head, norm, layers, [k.desc for k in kv])
+    w = ws(qd.qkdec_prefill_workspace_size(sm))
+    qd.qkdec_workspace_init(w)
+    logits = torch.empty(model.dims.vocab, dtype=torch.float32, device="cuda")
+    tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+    qd.qkdec_prefill(sm, slot, start, dev(np.asarray(prompt, np.int32)), len(prompt), tok, w, logits=logits)
+    sync()
+    return logits.cpu().numpy(), int(tok.item()), kv, (sm, w, embed, lm_head, norm, layers)
+
+
+@pytest.mark.parametrize("kind", ["f16", "q8_0"])
+@pytest.mark.parametrize("n", [1, 16, 40])
+def test_prefill_toy_matches_oracle(qd, kind, n):
+    # the toy decoder, a prompt of n tokens (one, one full chunk of 16, and
+    # 16 + 16 + 8) appended after 20 cached tokens of slot 1 of 3
+    dims = synth.TOY
+    model = synth.make_model(dims, 1700)
+    st = synth.Streams(1701)
+    caches = [synth.kv_cache(kind, st.next(), st.next(), 3, dims.n_kv_heads, 96, dims.head_dim, [30, 20, 50])
+              for _ in model.layers]
+    prompt = synth.tokens(st.next(), n, dims.vocab)
+    lg, tok, kv, _ = _prefill(qd, model, caches, 1, 20, prompt)
+    ref_caches = copy.deepcopy(caches)
+    ref, rtok = OS.prefill(model, ref_caches, kind, 1, 20, prompt)
+    d = float(np.abs(lg - ref).max())
+    assert d <= LOGIT_ABS_TOL, f"max |dlogit| {d:.3e}"
+    if top2_gap(ref) > 1e-3:
+        assert tok == rtok
+    # the other slots, the history of slot 1 and everything past the prompt untouched
+    for li in range(dims.n_layers):
+        got, was = kv[li].logical(), caches[li]
+        for name, arr in vars(was).items():
+            if arr is None:
+                continue
+            g = getattr(got, name)
+            assert np.array_equal(g[[0, 2]].view(np.uint8), arr[[0, 2]].view(np.uint8)), (li, name)
+            assert np.array_equal(g[1, :, :20].view(np.uint8), arr[1, :, :20].view(np.uint8)), (li, name)
+            assert not g[1, :, 20 + n:].view(np.uint8).any(), (li, name)
+
+
+def test_prefill_full_width_equals_decode_steps(qd):
+    # a two-layer decoder of the full width (every projection on the kernels
+    # the bench times), 24 prompt tokens after 300 cached ones: the prefill's
+    # first generated token and logits against 24 single-token decode steps
+    # on the GPU, and the appended keys and values of the two paths agree
+    import torch
+    from quantized_decode_amd.tensors import dev, upload_cache
+    dims = synth.ModelDims(n_layers=2, hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, ffn=12288,
+                           vocab=16384)
+    model = synth.make_model(dims, 1710)
+    st = synth.Streams(1711)
+    caches = [synth.kv_cache("f16", st.next(), st.next(), 1, dims.n_kv_heads, 352, dims.head_dim, [300])
+              for _ in model.layers]
+    prompt = synth.tokens(st.next(), 24, dims.vocab)
+    lg, tok, kv, (sm, w, embed, lm_head, norm, layers) = _prefill(qd, model, caches, 0, 300, prompt)
+    kv2 = [upload_cache(c) for c in caches]
+    sm2 = qd.StepModel(dims, embed, lm_head, norm, layers, [k.desc for k in kv2])
+    w2 = ws(qd.qkdec_step_workspace_size(sm2, 1))
+    qd.qkdec_workspace_init(w2)
+    slot = dev(np.zeros(1, np.int32))
+    logits = torch.empty((1, dims.vocab), dtype=torch.float32, device="cuda")
+    for i, t in enumerate(prompt):
+        pos = dev(np.array([300 + i], np.int32))
+        tk = dev(np.array([t], np.int32))
+        qd.qkdec_step(sm2, slot, pos, tk, 1, w2, logits=logits)
+    sync()
+    ref = logits.cpu().numpy()[0]
+    d = float(np.abs(lg - ref).max())
+    assert d <= LOGIT_ABS_TOL, f"prefill vs decode steps: max |dlogit| {d:.3e}"
+    if top2_gap(ref) > 1e-3:
+        assert tok == int(np.argmax(ref))
+    for a, b in zip(kv, kv2):
+        ka, va = a.logical_f16()
+        kb, vb = b.logical_f16()
+        for x, y in ((ka, kb), (va, vb)):
+            x64, y64 = x[0, :, 300:324].astype(np.float64), y[0, :, 300:324].astype(np.float64)
+            assert np.abs(x64 - y64).max() <= 1e-3 * np.abs(y64).max()

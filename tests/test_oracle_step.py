@@ -418,3 +418,27 @@ def test_paged_decode_step_equals_arena_step(kind):
         for name in vars(c):
             if getattr(c, name) is not None:
                 assert np.array_equal(getattr(pl, name), getattr(again, name))
+
+
+@pytest.mark.parametrize("kind", ["f16", "q8_0"])
+def test_prefill_is_one_step_over_the_prompt_rows(kind):
+    # the prompt's tokens as the rows of one decode step (same slot,
+    # consecutive positions) give bitwise the sequential prefill: row b's
+    # keys and values are appended before any later row attends, and each
+    # row's arithmetic is its own
+    model, caches, _ = _toy(kind=kind, batch=1, length=20)
+    for c in caches:
+        for name, arr in vars(c).items():
+            if arr is not None:
+                pad = np.zeros(arr.shape[:2] + (64,) + arr.shape[3:], arr.dtype)
+                setattr(c, name, np.concatenate([arr, pad], axis=2))
+    prompt = synth.tokens(np.random.default_rng(3), 12, model.dims.vocab)
+    seq = copy.deepcopy(caches)
+    lg, nt = S.prefill(model, seq, kind, 0, 20, prompt)
+    rows = copy.deepcopy(caches)
+    lg_rows, nt_rows = S.decode_step(model, rows, kind, [0] * 12, 20 + np.arange(12), prompt)
+    assert np.array_equal(lg_rows[-1], lg) and nt_rows[-1] == nt
+    for a, b in zip(seq, rows):
+        for name in vars(a):
+            if getattr(a, name) is not None:
+                assert np.array_equal(getattr(a, name), getattr(b, name))
