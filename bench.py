@@ -473,6 +473,7 @@ def record_traffic(qd, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, cop
     for the calibration), stamped with the loaded library's build id."""
     import csv
     import glob
+    import re
     import subprocess
 
     def load(d):
@@ -485,7 +486,16 @@ def record_traffic(qd, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, cop
                 agg.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         names = list(agg)
         out = subprocess.run(["c++filt"], input="\n".join(names), capture_output=True, text=True).stdout.split("\n")
-        return {dm or nm: sum(v) / len(v) for nm, dm, v in zip(names, out, agg.values())}
+
+        def readable(nm, dm):
+            # symbols whose parameters c++filt cannot read (_Float16, "DF16_")
+            # come back mangled: keep their qualified name
+            m = re.match(r"_ZN2qk(\d+)", dm or nm)
+            if m:
+                n = int(m.group(1))
+                return "qk::" + (dm or nm)[m.end():m.end() + n]
+            return dm or nm
+        return {readable(nm, dm): sum(v) / len(v) for nm, dm, v in zip(names, out, agg.values())}
 
     def copy_kib(d):
         vals = [v for k, v in load(d).items() if "copyBuffer" in k]

@@ -343,13 +343,23 @@ __device__ __forceinline__ void attn_tile(AttnState<D, VF == kFmtQ8>& st, KVFrag
     // the largest value scale of the tile's in-range tokens (over all blocks),
     // so the fp16 hi/lo pair keeps ~22 bits instead of sinking into fp16
     // subnormals; the exponent never increases, a smaller one rescales o.
-    // Branch-free: an out-of-range token's scale may hold any bits and is
-    // selected away, never multiplied in.
+    // A tile whose 32 tokens are all in range (every tile but a run's last)
+    // takes the maximum with packed fp16 instructions over the scale words;
+    // in a partial tile an out-of-range token's scale may hold any bits and
+    // is selected away, never multiplied in.
+    const bool full = valid == 32;   // uniform across the wave
     float vmax = 0.f;
+    if (full) {
+      half2_t m2 = __builtin_elementwise_abs(as_h2(f.vs[0]));
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+      for (int w = 1; w < D / 8; ++w) m2 = __builtin_elementwise_max(m2, __builtin_elementwise_abs(as_h2(f.vs[w])));
+      vmax = fmaxf((float)m2[0], (float)m2[1]);
+    } else {
 #pragma unroll
-      for (int c = 0; c < D / 32; ++c) vmax = fmaxf(vmax, e < lim ? fabsf(scale_at<D>(f.vs, e, c)) : 0.f);
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) vmax = fmaxf(vmax, e < lim ? fabsf(scale_at<D>(f.vs, e, c)) : 0.f);
+    }
     vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
     vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
     const int exv = 13 - ((int)((__builtin_bit_cast(uint32_t, vmax) >> 23) & 255u) - 127);
@@ -361,12 +371,18 @@ __device__ __forceinline__ void attn_tile(AttnState<D, VF == kFmtQ8>& st, KVFrag
     }
     st.ex = exn;
     const float fc = exp2i(st.ex);
+    float pf[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pf[e] = p[e] * fc;   // exact (a power of two)
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
+      // hi = pv rounded to the nearest fp16, lo = the exact remainder rounded
+      // likewise: hi + lo is pv to 2^-22 relative
       half8_t phi, plo;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pv = e < lim ? p[e] * scale_at<D>(f.vs, e, c) * fc : 0.f;
+        float pv = pf[e] * scale_at<D>(f.vs, e, c);
+        if (!full) pv = e < lim ? pv : 0.f;
         const half_t h = (half_t)pv;
         phi[e] = h;
         plo[e] = (half_t)(pv - (float)h);

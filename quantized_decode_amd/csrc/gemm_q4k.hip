@@ -354,9 +354,13 @@ __device__ void gemm_item(const GemmArgs& a, int rg, int c, int n_chunks, half_t
     if (!is_v) {
       for (int t = threadIdx.x; t < B * HALF; t += NT) {
         const int b = t / HALF, i = t % HALF;
-        float cs, sn;
-        rope_cos_sin(ra.pos[b], i, D, ra.rope_base, cs, sn);
-        sm.rope[b][i] = make_float2(cs, sn);
+        float2 c;
+        if (ra.rope) {
+          c = ra.rope[(size_t)b * HALF + i];
+        } else {
+          rope_cos_sin(ra.pos[b], i, D, ra.rope_base, c.x, c.y);
+        }
+        sm.rope[b][i] = c;
       }
     }
     sm.fin[wave][lane] = acc;

@@ -506,7 +506,7 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
       sl[ii] = a.ra.slot[b];
       ps[ii] = a.ra.spos[b];
     }
-    pos_t = a.ra.pos[(tx >> 4) < a.B ? (tx >> 4) : a.B - 1];
+    pos_t = (tx >> 4) < a.B ? (tx >> 4) : a.B - 1;   // the row whose rotary pair this thread stages
   }
   // the residual of the item this wave finishes
   float resv[4] = {0.f, 0.f, 0.f, 0.f};
@@ -552,13 +552,10 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
   __builtin_amdgcn_sched_barrier(0);
 
   // MODE 2: (cos, sin) of pair 16 hj + (tx % 16) at the position of row tx / 16
+  // (pos_t), from the step's rotary table
   __shared__ float2 s_rope[MODE == 2 ? 16 * 16 : 1];
   if constexpr (MODE == 2) {
-    if (tx < 16 * 16) {
-      float cs, sn;
-      rope_cos_sin(pos_t, 16 * hj + (tx & 15), 32 * a.qh, a.ra.rope_base, cs, sn);
-      s_rope[tx] = make_float2(cs, sn);
-    }
+    if (tx < 16 * 16) s_rope[tx] = a.ra.rope[(size_t)pos_t * (16 * a.qh) + 16 * hj + (tx & 15)];
   }
 
   // ---- A operands of this wave's K slice, kept for every item
@@ -1059,8 +1056,7 @@ hipError_t launch_gemm_wi(const GemmLaunch& L, hipStream_t st) {
 hipError_t launch_gemm_wi_qkv(const GemmLaunch& L, const RopeAppendArgs& ra, int head_dim, hipStream_t st) {
   const int kb = (int)(L.K / 256);
   if (kb != 16 || !L.x_f32 || !L.gamma || ra.kf == kFmtQ8 || ra.vf == kFmtQ8 || (head_dim != 64 && head_dim != 128) ||
-      L.residual ||
-      L.ss_out)
+      L.residual || L.ss_out || !ra.rope)
     return hipErrorNotSupported;
   WkArgs a{};
   a.W = reinterpret_cast<const uint8_t*>(L.W);

@@ -67,6 +67,9 @@ struct RopeAppendArgs {
   const int32_t* spos;
   int kf, vf;             // key / value format (kFmtF16, kFmtQ8, kFmtF8)
   float rope_base;
+  // (cos, sin) of every pair at each row's position, [B][head_dim/2]
+  // (launch_rope_table), or null to form them in place
+  const float2* rope;
   uint16_t* q16;         // rotated queries, fp16 bits
   int32_t* err;          // set to QKDEC_E_CAPACITY for a position outside the cache
 };
@@ -160,7 +163,11 @@ hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, con
 // (row b: [q heads; k heads; v heads], head_dim each)
 hipError_t launch_rope_append(const qkdec_kv_layer& kv, const float* Y, int64_t ldy, int Hq, int B,
                               const int32_t* slot, const int32_t* pos, float rope_base, uint16_t* q16, int32_t* err,
-                              hipStream_t st, const int32_t* spos = nullptr);
+                              hipStream_t st, const int32_t* spos = nullptr, const float2* rope = nullptr);
+// The rotary (cos, sin) of pair i of head_dim D at position pos[b], for every
+// row b < B: table[b * D/2 + i] (angle in fp64, rounded once to fp32); the
+// positions are the same in every layer of a step, so one table serves them all.
+hipError_t launch_rope_table(const int32_t* pos, int B, int D, float rope_base, float2* table, hipStream_t st);
 // Paged step: page[b] and the position within it of logical position pos[b]
 // of sequence b (page -1 when outside the table or the pool), once per step
 // for every layer's stores.

@@ -43,7 +43,7 @@ __global__ void kv_append_kernel(qkdec_kv_layer kv, const int32_t* slot, const i
 // position within the page a paged step located).
 __global__ void rope_append_kernel(qkdec_kv_layer kv, const float* __restrict__ Y, int64_t ldy, int Hq,
                                    const int32_t* slot, const int32_t* pos, float rope_base, uint16_t* q16,
-                                   int32_t* err, const int32_t* spos) {
+                                   int32_t* err, const int32_t* spos, const float2* rope) {
   const CacheRef c = cache_ref(kv);
   const int head = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int D = c.D, half = D / 2;
@@ -55,7 +55,13 @@ __global__ void rope_append_kernel(qkdec_kv_layer kv, const float* __restrict__ 
   if (!is_v) {
     const float other = yr[d < half ? d + half : d - half];
     float cs, sn;
-    rope_cos_sin(p, d % half, D, rope_base, cs, sn);
+    if (rope) {
+      const float2 c = rope[(size_t)b * half + d % half];
+      cs = c.x;
+      sn = c.y;
+    } else {
+      rope_cos_sin(p, d % half, D, rope_base, cs, sn);
+    }
     // d < D/2: x_i cos - x_{i+D/2} sin; d >= D/2: x_{i+D/2} cos + x_i sin
     out = d < half ? x * cs - other * sn : x * cs + other * sn;
   }
@@ -72,9 +78,21 @@ __global__ void rope_append_kernel(qkdec_kv_layer kv, const float* __restrict__ 
 
 hipError_t launch_rope_append(const qkdec_kv_layer& kv, const float* Y, int64_t ldy, int Hq, int B,
                               const int32_t* slot, const int32_t* pos, float rope_base, uint16_t* q16, int32_t* err,
-                              hipStream_t st, const int32_t* spos) {
+                              hipStream_t st, const int32_t* spos, const float2* rope) {
   hipLaunchKernelGGL(rope_append_kernel, dim3(Hq + 2 * kv.n_kv_heads, B), dim3(kv.head_dim), 0, st, kv, Y, ldy, Hq,
-                     slot, pos, rope_base, q16, err, spos ? spos : pos);
+                     slot, pos, rope_base, q16, err, spos ? spos : pos, rope);
+  return hipGetLastError();
+}
+
+__global__ void rope_table_kernel(const int32_t* pos, int D, float rope_base, float2* table) {
+  const int b = blockIdx.x, i = threadIdx.x;
+  float cs, sn;
+  rope_cos_sin(pos[b], i, D, rope_base, cs, sn);
+  table[(size_t)b * (D / 2) + i] = make_float2(cs, sn);
+}
+
+hipError_t launch_rope_table(const int32_t* pos, int B, int D, float rope_base, float2* table, hipStream_t st) {
+  hipLaunchKernelGGL(rope_table_kernel, dim3(B), dim3(D / 2), 0, st, pos, D, rope_base, table);
   return hipGetLastError();
 }
 

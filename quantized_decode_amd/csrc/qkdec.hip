@@ -104,6 +104,7 @@ struct StepWs {
   uint16_t* o16;
   float* a;
   float* attn_part;
+  float2* rope;        // rotary (cos, sin) of each row's position, [B][head_dim/2]
   int32_t* page;       // paged step: page of each sequence's new token (-1: outside)
   int32_t* page_pos;   // and its position within the page
   void* lm_part;
@@ -131,6 +132,7 @@ StepWs step_layout(const qkdec_model* m, int B, const qkdec_kv_layer* kv, char* 
   w.a = reinterpret_cast<float*>(take((size_t)B * m->ffn * 4));
   w.attn_part = reinterpret_cast<float*>(
       take(attn_partials_bytes(B, m->n_q_heads, m->head_dim, attn_seq_cap(kv[0], max_pages), kv[0].n_kv_heads)));
+  w.rope = reinterpret_cast<float2*>(take((size_t)B * (m->head_dim / 2) * sizeof(float2)));
   w.page = reinterpret_cast<int32_t*>(take((size_t)B * 4));
   w.page_pos = reinterpret_cast<int32_t*>(take((size_t)B * 4));
   w.lm_part = take(lm_head_partials_bytes(m->vocab, B));
@@ -167,6 +169,7 @@ qkdec_status run_layers(const qkdec_model* m, const qkdec_kv_layer* kv, const in
   // position within it, located once per step
   if (pages)
     QK_TRY(launch_page_locate(pages, max_pages, kv[0].capacity, kv[0].n_slots, pos, B, w.page, w.page_pos, st));
+  QK_TRY(launch_rope_table(pos, B, D, m->rope_base, w.rope, st));
   QK_TRY(launch_embed(m->embed, H, m->vocab, tok, B, w.x, w.ss, st));
   for (int l = 0; l < m->n_layers; ++l) {
     const qkdec_layer& ly = m->layers[l];
@@ -182,7 +185,7 @@ qkdec_status run_layers(const qkdec_model* m, const qkdec_kv_layer* kv, const in
     ra.k = reinterpret_cast<uint8_t*>(kv[l].k); ra.v = reinterpret_cast<uint8_t*>(kv[l].v);
     ra.ks = reinterpret_cast<uint16_t*>(kv[l].k_scale); ra.vs = reinterpret_cast<uint16_t*>(kv[l].v_scale);
     ra.n_kv = kv[l].n_kv_heads; ra.cap = kv[l].capacity; ra.n_slots = kv[l].n_slots; ra.Hq = Hq;
-    ra.kf = kv_k_fmt(kv[l].type); ra.vf = kv_v_fmt(kv[l].type); ra.rope_base = m->rope_base; ra.q16 = w.q16; ra.err = err_word;
+    ra.kf = kv_k_fmt(kv[l].type); ra.vf = kv_v_fmt(kv[l].type); ra.rope_base = m->rope_base; ra.rope = w.rope; ra.q16 = w.q16; ra.err = err_word;
     // K = 4096: the resident multi-item projection, finishing each head slice
     // itself (fp16 or E4M3 cache) or followed by RoPE and the append as a small launch
     // (Q8_0 blocks span two work-groups); otherwise the split-K projection
@@ -195,7 +198,7 @@ qkdec_status run_layers(const qkdec_model* m, const qkdec_kv_layer* kv, const in
       } else {
         QK_TRY(eq);
         QK_TRY(launch_rope_append(kv[l], w.qkv, nqkv, Hq, B, ra.slot, pos, m->rope_base, w.q16, err_word, st,
-                                  ra.spos));
+                                  ra.spos, w.rope));
       }
     } else {
       QK_TRY(eq);
