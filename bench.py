@@ -730,8 +730,8 @@ def main():
     points = [(args.batch, args.context, args.kv)]
     if args.points == "all":
         for p in [(8, 2400, "f16"), (8, 6900, "f16"), (8, 2400, "q8_0"), (8, 6900, "q8_0"), (8, 2400, "q8k_f16v"),
-                  (8, 2400, "f16k_q8v"), (8, 2400, "fp8"), (8, 6900, "fp8"), (1, 2400, "f16"), (16, 3400, "f16"), (16, 3400, "q8_0"), (8, 8192, "q8_0"),
-                  (8, 19000, "q8_0")]:
+                  (8, 2400, "f16k_q8v"), (8, 2400, "fp8"), (8, 6900, "fp8"), (1, 2400, "f16"), (2, 2400, "f16"),
+                  (4, 2400, "f16"), (16, 3400, "f16"), (16, 3400, "q8_0"), (8, 8192, "q8_0"), (8, 19000, "q8_0")]:
             if p not in points:
                 points.append(p)
     results = []

@@ -192,85 +192,7 @@ __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs
   }
 }
 
-// O[b][h] = sum_j 2^(m_j - M) o_j / sum_j 2^(m_j - M) l_j over the splits, j in
-// run order.  Up to kMergeBatch runs' (m, l, o) are loaded in one batch, so
-// the merge costs one memory round trip (the running maximum is rescaled
-// between batches).
-constexpr int kMergeBatch = 8;
-// paged: slot holds no slots (any readable int32[B]; its values are ignored).
-__global__ void attn_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
-                                    int n_splits, int runs_wanted, const int32_t* slot, int paged,
-                                    const int32_t* n_ctx, int n_ctx_add, int cap, int n_slots, int Hq, int D,
-                                    float* O, half_t* O16) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  const size_t row0 = ((size_t)b * Hq + h) * n_splits;
-  // The first batch of run states is loaded before the run count is known
-  // (rows row0 .. row0 + min(kMergeBatch, n_splits) - 1 always lie in the
-  // partial area; rows past the count are never used), so the count's loads
-  // and the states' loads make one memory round trip, not two.
-  float m[kMergeBatch], l[kMergeBatch], o[kMergeBatch];
-#pragma unroll
-  for (int j = 0; j < kMergeBatch; ++j) {
-    const size_t row = row0 + (j < n_splits ? j : 0);
-    m[j] = part_ml[2 * row];
-    l[j] = part_ml[2 * row + 1];
-    o[j] = part_o[row * D + d];
-  }
-  __asm__ volatile("" ::: "memory");   // keep the loads above ahead of the run count's
-  int n = n_ctx[b] + n_ctx_add;
-  if (n > cap) n = cap;               // cap: the most tokens a sequence holds
-  const int s = slot[b];   // unconditional: no branch ahead of the loads above
-  if (n < 0 || (!paged && (s < 0 || s >= n_slots))) n = 0;
-  const int ns = attn_runs(n, runs_wanted, n_splits);
-  // first batch: selects rather than branches, so that its loads stay
-  // unconditional and go out together with those of the run count (the
-  // values equal the branchy form: fmax with -inf and additions of +0)
-  float big = -__builtin_inff();
-#pragma unroll
-  for (int j = 0; j < kMergeBatch; ++j) big = fmaxf(big, j < ns ? m[j] : -__builtin_inff());
-  // runs without a valid token (all their tiles on unmapped pages) carry
-  // m = -inf, l = 0; a reference of 0 while no run has a finite maximum keeps
-  // their weights at 0 rather than NaN
-  float num = 0.f, den = 0.f;
-  float bref = big == -__builtin_inff() ? 0.f : big;
-#pragma unroll
-  for (int j = 0; j < kMergeBatch; ++j) {
-    const float w = exp2f(m[j] - bref);
-    den += j < ns ? w * l[j] : 0.f;
-    num += j < ns ? w * o[j] : 0.f;
-  }
-  for (int j0 = kMergeBatch; j0 < ns; j0 += kMergeBatch) {
-#pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
-      const size_t row = row0 + (j0 + j < ns ? j0 + j : j0);
-      m[j] = part_ml[2 * row];
-      l[j] = part_ml[2 * row + 1];
-      o[j] = part_o[row * D + d];
-    }
-    float nb = big;
-#pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j)
-      if (j0 + j < ns) nb = fmaxf(nb, m[j]);
-    const float nref = nb == -__builtin_inff() ? 0.f : nb;
-    const float fr = exp2f(bref - nref);
-    num *= fr;
-    den *= fr;
-    big = nb;
-    bref = nref;
-#pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j)
-      if (j0 + j < ns) {
-        const float w = exp2f(m[j] - bref);
-        den += w * l[j];
-        num += w * o[j];
-      }
-  }
-  // no run with a valid token (or no token at all): O = 0
-  const float out = den > 0.f ? num / den : 0.f;
-  const size_t oi = ((size_t)b * Hq + h) * D + d;
-  if (O) O[oi] = out;
-  if (O16) O16[oi] = (half_t)out;
-}
+__global__ void attn_combine_kernel(const MergeArgs m) { attn_merge_elem(m, blockIdx.y, blockIdx.x, threadIdx.x); }
 
 hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, const int32_t* n_ctx, int B,
                               const uint16_t* Q, int n_q_heads, float scale, float* O, uint16_t* O16,
@@ -325,9 +247,22 @@ hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, con
 #undef QK_ATTN
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(n_q_heads, B), dim3(D), 0, st, a.part_o, a.part_ml, a.n_splits,
-                     a.runs_wanted, pages ? n_ctx : slot, pages ? 1 : 0, n_ctx, n_ctx_add, a.seq_cap, kv.n_slots,
-                     n_q_heads, D, O, reinterpret_cast<half_t*>(O16));
+  MergeArgs mg;
+  mg.part_o = a.part_o;
+  mg.part_ml = a.part_ml;
+  mg.n_splits = a.n_splits;
+  mg.runs_wanted = a.runs_wanted;
+  mg.slot = pages ? n_ctx : slot;
+  mg.paged = pages ? 1 : 0;
+  mg.n_ctx = n_ctx;
+  mg.n_ctx_add = n_ctx_add;
+  mg.cap = a.seq_cap;
+  mg.n_slots = kv.n_slots;
+  mg.Hq = n_q_heads;
+  mg.D = D;
+  mg.O = O;
+  mg.O16 = reinterpret_cast<half_t*>(O16);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(n_q_heads, B), dim3(D), 0, st, mg);
   return hipGetLastError();
 }
 

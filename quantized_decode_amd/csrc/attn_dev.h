@@ -4,6 +4,7 @@
 #pragma once
 
 #include "common.h"
+#include "internal.h"
 
 namespace qk {
 
@@ -117,6 +118,91 @@ __host__ __device__ __forceinline__ int attn_runs(int n, int wanted, int max_run
   if (r < (n + 1023) / 1024) r = (n + 1023) / 1024;   // never more than 1024 tokens per run
   if (r > max_runs) r = max_runs;
   return r;
+}
+
+// O[b][h] = sum_j 2^(m_j - M) o_j / sum_j 2^(m_j - M) l_j over the splits, j in
+// run order.  Up to kMergeBatch runs' (m, l, o) are loaded in one batch, so
+// the merge costs one memory round trip (the running maximum is rescaled
+// between batches).
+constexpr int kMergeBatch = 8;
+// Output element (b, h, d).  Paged: slot holds no slots (any readable
+// int32[B]; its values are ignored).
+__device__ __forceinline__ void attn_merge_elem(const MergeArgs& mg, int b, int h, int d) {
+  const float* __restrict__ part_o = mg.part_o;
+  const float* __restrict__ part_ml = mg.part_ml;
+  const int n_splits = mg.n_splits, runs_wanted = mg.runs_wanted, paged = mg.paged, n_ctx_add = mg.n_ctx_add;
+  const int cap = mg.cap, n_slots = mg.n_slots, Hq = mg.Hq, D = mg.D;
+  const int32_t* slot = mg.slot;
+  const int32_t* n_ctx = mg.n_ctx;
+  float* O = mg.O;
+  half_t* O16 = mg.O16;
+  const size_t row0 = ((size_t)b * Hq + h) * n_splits;
+  // The first batch of run states is loaded before the run count is known
+  // (rows row0 .. row0 + min(kMergeBatch, n_splits) - 1 always lie in the
+  // partial area; rows past the count are never used), so the count's loads
+  // and the states' loads make one memory round trip, not two.
+  float m[kMergeBatch], l[kMergeBatch], o[kMergeBatch];
+#pragma unroll
+  for (int j = 0; j < kMergeBatch; ++j) {
+    const size_t row = row0 + (j < n_splits ? j : 0);
+    m[j] = part_ml[2 * row];
+    l[j] = part_ml[2 * row + 1];
+    o[j] = part_o[row * D + d];
+  }
+  __asm__ volatile("" ::: "memory");   // keep the loads above ahead of the run count's
+  int n = n_ctx[b] + n_ctx_add;
+  if (n > cap) n = cap;               // cap: the most tokens a sequence holds
+  const int s = slot[b];   // unconditional: no branch ahead of the loads above
+  if (n < 0 || (!paged && (s < 0 || s >= n_slots))) n = 0;
+  const int ns = attn_runs(n, runs_wanted, n_splits);
+  // first batch: selects rather than branches, so that its loads stay
+  // unconditional and go out together with those of the run count (the
+  // values equal the branchy form: fmax with -inf and additions of +0)
+  float big = -__builtin_inff();
+#pragma unroll
+  for (int j = 0; j < kMergeBatch; ++j) big = fmaxf(big, j < ns ? m[j] : -__builtin_inff());
+  // runs without a valid token (all their tiles on unmapped pages) carry
+  // m = -inf, l = 0; a reference of 0 while no run has a finite maximum keeps
+  // their weights at 0 rather than NaN
+  float num = 0.f, den = 0.f;
+  float bref = big == -__builtin_inff() ? 0.f : big;
+#pragma unroll
+  for (int j = 0; j < kMergeBatch; ++j) {
+    const float w = exp2f(m[j] - bref);
+    den += j < ns ? w * l[j] : 0.f;
+    num += j < ns ? w * o[j] : 0.f;
+  }
+  for (int j0 = kMergeBatch; j0 < ns; j0 += kMergeBatch) {
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const size_t row = row0 + (j0 + j < ns ? j0 + j : j0);
+      m[j] = part_ml[2 * row];
+      l[j] = part_ml[2 * row + 1];
+      o[j] = part_o[row * D + d];
+    }
+    float nb = big;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j)
+      if (j0 + j < ns) nb = fmaxf(nb, m[j]);
+    const float nref = nb == -__builtin_inff() ? 0.f : nb;
+    const float fr = exp2f(bref - nref);
+    num *= fr;
+    den *= fr;
+    big = nb;
+    bref = nref;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j)
+      if (j0 + j < ns) {
+        const float w = exp2f(m[j] - bref);
+        den += w * l[j];
+        num += w * o[j];
+      }
+  }
+  // no run with a valid token (or no token at all): O = 0
+  const float out = den > 0.f ? num / den : 0.f;
+  const size_t oi = ((size_t)b * Hq + h) * D + d;
+  if (O) O[oi] = out;
+  if (O16) O16[oi] = (half_t)out;
 }
 
 // Keys (and their Q8_0 scales) of the 32-token tile at t0; head_row0 =

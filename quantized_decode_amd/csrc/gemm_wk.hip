@@ -401,7 +401,9 @@ __global__ void __launch_bounds__(64 * S, 1) gemm_wi_kernel(const WkArgs a) {
   auto red = reinterpret_cast<floatx4(*)[T][S][64]>(smem);
   __shared__ float s_part[4 * S][16];
   __shared__ float s_rinv[16];
-  const int tx = threadIdx.x, lane = tx & 63, wave = tx >> 6, g = lane >> 4, r = lane & 15;
+  // the wave index as a wave-uniform value (scalar registers, uniform branches)
+  const int tx = threadIdx.x, lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
+  const int g = lane >> 4, r = lane & 15;
   const int kb = a.kb;
   const int n_groups = (int)gridDim.x / KSPLIT;
   const int kc = KSPLIT > 1 ? (int)blockIdx.x / n_groups : 0;   // K chunk
@@ -983,6 +985,34 @@ static void launch_wi(int mv, dim3 grid, const WkArgs& a, hipStream_t st) {
   }
 }
 
+// The kernel arguments of one launch (the K-split partials and arrival
+// counters from the workspace, used where the shape splits K).
+static WkArgs wk_args(const GemmLaunch& L) {
+  WkArgs a{};
+  a.W = reinterpret_cast<const uint8_t*>(L.W);
+  a.X = L.X;
+  a.gamma = L.gamma;
+  a.ss_in = L.ss_in;
+  a.Y = L.Y;
+  a.residual = L.residual;
+  a.ss_out = L.ss_out;
+  a.A = L.A;
+  a.ldx = L.ldx;
+  a.ldy = L.ldy;
+  a.ldr = L.ldr;
+  a.lda = L.lda;
+  a.kb = (int)(L.K / 256);
+  a.B = L.B;
+  a.f_tiles = (int)(L.n_rows / 16);
+  a.ss_slots = (int)(L.K / kSsCols);
+  a.eps = L.eps;
+  a.inv_k = 1.0f / (float)L.K;
+  char* p = reinterpret_cast<char*>(L.ws);
+  a.counters = reinterpret_cast<unsigned*>(p);
+  a.part = p ? reinterpret_cast<float*>(p + (size_t)kGemmMaxGroups * 4) : nullptr;
+  return a;
+}
+
 // Multi-item launch for the shapes it is built for; hipErrorNotSupported
 // otherwise (the caller then uses another kernel).  K = 4096 (16 waves of
 // one super-block each):
@@ -998,31 +1028,10 @@ hipError_t launch_gemm_wi(const GemmLaunch& L, hipStream_t st) {
   const int xmode = L.x_f32 ? (L.gamma ? kXNorm : kXF32Blocked) : kXF16;
   if (kb != 16 && !(kb == 48 && xmode != kXNorm && !L.swiglu)) return hipErrorNotSupported;
   const int mv = gemm_matvec_rows(L.kernel, L.B);
-  WkArgs a{};
-  a.W = reinterpret_cast<const uint8_t*>(L.W);
-  a.X = L.X;
-  a.gamma = L.gamma;
-  a.ss_in = L.ss_in;
-  a.Y = L.Y;
-  a.residual = L.residual;
-  a.ss_out = L.ss_out;
-  a.A = L.A;
-  a.ldx = L.ldx;
-  a.ldy = L.ldy;
-  a.ldr = L.ldr;
-  a.lda = L.lda;
-  a.kb = kb;
-  a.B = L.B;
-  a.f_tiles = (int)items;
-  a.ss_slots = (int)(L.K / kSsCols);
-  a.eps = L.eps;
-  a.inv_k = 1.0f / (float)L.K;
+  const WkArgs a = wk_args(L);
   if (kb == 48) {
     // K = 12288: four K chunks of 3072 (12 waves of one super-block), four
     // tiles per work-group: 256 work-groups for N = 4096, one round on the chip
-    char* p = reinterpret_cast<char*>(L.ws);
-    a.counters = reinterpret_cast<unsigned*>(p);
-    a.part = reinterpret_cast<float*>(p + (size_t)kGemmMaxGroups * 4);
     const dim3 grid((unsigned)((items + 3) / 4) * 4);
     if (xmode == kXF32Blocked) launch_wi<0, kXF32Blocked, 12, 1, 4, 2, 4>(mv, grid, a, st);
     else launch_wi<0, kXF16, 12, 1, 4, 2, 4>(mv, grid, a, st);
@@ -1058,20 +1067,7 @@ hipError_t launch_gemm_wi_qkv(const GemmLaunch& L, const RopeAppendArgs& ra, int
   if (kb != 16 || !L.x_f32 || !L.gamma || ra.kf == kFmtQ8 || ra.vf == kFmtQ8 || (head_dim != 64 && head_dim != 128) ||
       L.residual || L.ss_out || !ra.rope)
     return hipErrorNotSupported;
-  WkArgs a{};
-  a.W = reinterpret_cast<const uint8_t*>(L.W);
-  a.X = L.X;
-  a.gamma = L.gamma;
-  a.ss_in = L.ss_in;
-  a.Y = L.Y;
-  a.ldx = L.ldx;
-  a.ldy = L.ldy;
-  a.kb = kb;
-  a.B = L.B;
-  a.f_tiles = (int)(L.n_rows / 16);
-  a.ss_slots = (int)(L.K / kSsCols);
-  a.eps = L.eps;
-  a.inv_k = 1.0f / (float)L.K;
+  WkArgs a = wk_args(L);
   a.ra = ra;
   a.qh = head_dim / 32;
   const int n_heads = (int)(L.n_rows / head_dim);
@@ -1084,25 +1080,7 @@ hipError_t launch_gemm_wk(const GemmLaunch& L, hipStream_t st) {
   const int64_t items = L.n_rows / 16;   // SwiGLU: n_rows = F, one item per gate/up tile pair
   const int xmode = L.x_f32 ? (L.gamma ? kXNorm : kXF32Blocked) : kXF16;
   const WkConfig c = wk_config(kb, L.swiglu, xmode);
-  WkArgs a{};
-  a.W = reinterpret_cast<const uint8_t*>(L.W);
-  a.X = L.X;
-  a.gamma = L.gamma;
-  a.ss_in = L.ss_in;
-  a.Y = L.Y;
-  a.residual = L.residual;
-  a.ss_out = L.ss_out;
-  a.A = L.A;
-  a.ldx = L.ldx;
-  a.ldy = L.ldy;
-  a.ldr = L.ldr;
-  a.lda = L.lda;
-  a.kb = kb;
-  a.B = L.B;
-  a.f_tiles = (int)items;
-  a.ss_slots = (int)(L.K / kSsCols);
-  a.eps = L.eps;
-  a.inv_k = 1.0f / (float)L.K;
+  const WkArgs a = wk_args(L);
   if (L.swiglu) {
     if (xmode == kXNorm) launch_mode<1, kXNorm>(c.s, (int)items, a, st);
     else launch_mode<1, kXF16>(c.s, (int)items, a, st);

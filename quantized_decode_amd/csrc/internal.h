@@ -151,8 +151,22 @@ inline size_t attn_partials_bytes(int B, int n_q_heads, int head_dim, int capaci
 inline int attn_seq_cap(const qkdec_kv_layer& kv, int max_pages) {
   return max_pages > 0 ? max_pages * kv.capacity : kv.capacity;
 }
+// The merge of the runs' partial results into O / O16 (attn_merge_elem, one
+// output element per call)
+struct MergeArgs {
+  const float* part_o;
+  const float* part_ml;
+  int n_splits, runs_wanted;
+  const int32_t* slot;   // paged: any readable int32 [B] (unused)
+  int paged;
+  const int32_t* n_ctx;
+  int n_ctx_add, cap, n_slots, Hq, D;
+  float* O;
+  _Float16* O16;
+};
+
 // pages != NULL: kv is a pool of n_slots pages of capacity tokens (a power of
-// two) and sequence b's pages are pages[b * max_pages ...]; slot is unused
+// two) and sequence b's pages are pages[b * max_pages ...]; slot is unused.
 hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, const int32_t* n_ctx, int B,
                               const uint16_t* Q, int n_q_heads, float scale, float* O, uint16_t* O16,
                               float* partials, int n_ctx_add, hipStream_t st, const int32_t* pages = nullptr,
