@@ -372,9 +372,39 @@ __device__ __forceinline__ void attn_tile(AttnState<D, VF == kFmtQ8>& st, KVFrag
     psum += p[e];
   }
   st.l = st.l * corr + psum;
+  // Q8_0 values: p * scale is brought near 2^13..2^14 by an exact power of
+  // two taken from the largest value scale of the tile's in-range tokens (over
+  // all blocks), so the fp16 hi/lo pair keeps ~22 bits instead of sinking into
+  // fp16 subnormals; the exponent never increases, and a smaller one rescales
+  // o by fr together with the softmax correction.  A tile whose 32 tokens are
+  // all in range (every tile but a run's last) takes the maximum with packed
+  // fp16 instructions over the scale words; in a partial tile an out-of-range
+  // token's scale may hold any bits and is selected away, never multiplied in.
+  float ocorr = corr;
+  if constexpr (VF == kFmtQ8) {
+    const int lim = valid - 8 * lg;
+    float vmax = 0.f;
+    if (valid == 32) {   // uniform across the wave
+      half2_t m2 = __builtin_elementwise_abs(as_h2(f.vs[0]));
+#pragma unroll
+      for (int w = 1; w < D / 8; ++w) m2 = __builtin_elementwise_max(m2, __builtin_elementwise_abs(as_h2(f.vs[w])));
+      vmax = fmaxf((float)m2[0], (float)m2[1]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) vmax = fmaxf(vmax, e < lim ? fabsf(scale_at<D>(f.vs, e, c)) : 0.f);
+    }
+    vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
+    vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
+    const int exv = 13 - ((int)((__builtin_bit_cast(uint32_t, vmax) >> 23) & 255u) - 127);
+    const int exn = (vmax > 0.f && exv < st.ex) ? exv : st.ex;
+    ocorr = corr * exp2i(exn - st.ex);   // the power of two is 1 when the exponent stays
+    st.ex = exn;
+  }
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) {
-    st.o[i][0] *= corr; st.o[i][1] *= corr; st.o[i][2] *= corr; st.o[i][3] *= corr;
+    st.o[i][0] *= ocorr; st.o[i][1] *= ocorr; st.o[i][2] *= ocorr; st.o[i][3] *= ocorr;
   }
   __builtin_amdgcn_sched_barrier(0);
   mid();
@@ -425,53 +455,34 @@ __device__ __forceinline__ void attn_tile(AttnState<D, VF == kFmtQ8>& st, KVFrag
     }
   } else {
     const int lim = valid - 8 * lg;   // tokens of this lane at or past lim are out of range
-    // p * scale is brought near 2^13..2^14 by an exact power of two taken from
-    // the largest value scale of the tile's in-range tokens (over all blocks),
-    // so the fp16 hi/lo pair keeps ~22 bits instead of sinking into fp16
-    // subnormals; the exponent never increases, a smaller one rescales o.
-    // A tile whose 32 tokens are all in range (every tile but a run's last)
-    // takes the maximum with packed fp16 instructions over the scale words;
-    // in a partial tile an out-of-range token's scale may hold any bits and
-    // is selected away, never multiplied in.
-    const bool full = valid == 32;   // uniform across the wave
-    float vmax = 0.f;
-    if (full) {
-      half2_t m2 = __builtin_elementwise_abs(as_h2(f.vs[0]));
-#pragma unroll
-      for (int w = 1; w < D / 8; ++w) m2 = __builtin_elementwise_max(m2, __builtin_elementwise_abs(as_h2(f.vs[w])));
-      vmax = fmaxf((float)m2[0], (float)m2[1]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c) vmax = fmaxf(vmax, e < lim ? fabsf(scale_at<D>(f.vs, e, c)) : 0.f);
-    }
-    vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
-    vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
-    const int exv = 13 - ((int)((__builtin_bit_cast(uint32_t, vmax) >> 23) & 255u) - 127);
-    const int exn = (vmax > 0.f && exv < st.ex) ? exv : st.ex;
-    const float fr = exp2i(exn - st.ex);   // 1 when the exponent stays
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) {
-      st.o[i][0] *= fr; st.o[i][1] *= fr; st.o[i][2] *= fr; st.o[i][3] *= fr;
-    }
-    st.ex = exn;
+    const bool full = valid == 32;    // uniform across the wave
     const float fc = exp2i(st.ex);
     float pf[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) pf[e] = p[e] * fc;   // exact (a power of two)
+    // -1 in a register the compiler cannot see through, so that hi * -1 + pv
+    // stays one mixed-precision fused operation on the fp16 hi
+    float m1 = -1.f;
+    asm volatile("" : "+v"(m1));
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
-      // hi = pv rounded to the nearest fp16, lo = the exact remainder rounded
-      // likewise: hi + lo is pv to 2^-22 relative
+      // hi = pv rounded to the nearest fp16, lo = the exact remainder pv - hi
+      // rounded likewise: hi + lo is pv to 2^-22 relative.  pv and the
+      // remainder are single fused operations on the fp16 scale and hi
       half8_t phi, plo;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float pv = pf[e] * scale_at<D>(f.vs, e, c);
-        if (!full) pv = e < lim ? pv : 0.f;
-        const half_t h = (half_t)pv;
-        phi[e] = h;
-        plo[e] = (half_t)(pv - (float)h);
+      for (int e = 0; e < 8; e += 2) {
+        float pv0 = __builtin_fmaf(pf[e], scale_at<D>(f.vs, e, c), 0.f);
+        float pv1 = __builtin_fmaf(pf[e + 1], scale_at<D>(f.vs, e + 1, c), 0.f);
+        if (!full) {
+          pv0 = e < lim ? pv0 : 0.f;
+          pv1 = e + 1 < lim ? pv1 : 0.f;
+        }
+        const half_t h0 = (half_t)pv0, h1 = (half_t)pv1;
+        phi[e] = h0;
+        phi[e + 1] = h1;
+        plo[e] = (half_t)__builtin_fmaf((float)h0, m1, pv0);
+        plo[e + 1] = (half_t)__builtin_fmaf((float)h1, m1, pv1);
       }
 #pragma unroll
       for (int ii = 0; ii < 2; ++ii) {

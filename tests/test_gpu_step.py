@@ -312,16 +312,31 @@ def test_full_width_step_stagewise(qd, kind):
     assert torch.equal(g.kv[0].k[:, :, L], k0), "layer 0 re-appended different keys"
 
 
-@pytest.mark.parametrize("bsz,kind", [(1, "f16"), (16, "f16"), (16, "q8_0"), (16, "fp8")])
+@pytest.mark.parametrize("bsz,kind", [(1, "f16"), (1, "q8_0"), (2, "f16"), (2, "q8_0"), (16, "f16"), (16, "q8_0"),
+                                      (16, "fp8")])
 def test_full_width_step_stagewise_batch_sizes(qd, bsz, kind):
-    # the Qwen-shaped layer at the ends of the batch range: B = 1 and B = 16 (the
-    # projections stage rows 8..15 in a second pass), one layer, L = 300,
-    # every stage against the oracle fed with the GPU's own input to that stage
+    # the Qwen-shaped layer at the ends of the batch range: B = 1 (the matvec
+    # engine), B = 2 (the first MFMA batch size) and B = 16 (the projections
+    # stage rows 8..15 in a second pass), one layer, L = 300, every stage
+    # against the oracle fed with the GPU's own input to that stage
+    _stagewise_one_layer(qd, synth.QWEN_SHAPED, bsz, kind, 1103 + bsz)
+
+
+@pytest.mark.parametrize("kind", ["f16", "q8_0", "f16k_q8v"])
+def test_full_width_head_dim_64(qd, kind):
+    # hidden 4096 with 64 query and 8 KV heads of 64: the QKV projection's
+    # finish with two tiles per rotation pair (the whole head in one work-group
+    # for a Q8_0 cache), B = 4, L = 300
+    dims = synth.ModelDims(n_layers=1, hidden=4096, n_q_heads=64, n_kv_heads=8, head_dim=64, ffn=12288,
+                           vocab=8192)
+    _stagewise_one_layer(qd, dims, 4, kind, 1163)
+
+
+def _stagewise_one_layer(qd, dims, bsz, kind, seed):
     from oracle import ops as OO
-    dims = synth.QWEN_SHAPED
     L = 300
     slots = list(range(bsz))
-    model, caches, tok = build(dims, 1103 + bsz, kind, bsz, L, 320, n_layers=1)
+    model, caches, tok = build(dims, seed, kind, bsz, L, 320, n_layers=1)
     pos = np.full(bsz, L)
     g = GpuStep(qd, model, caches, bsz, slots)
     g.set(pos, tok)
