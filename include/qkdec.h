@@ -251,7 +251,8 @@ qkdec_status qkdec_kv_append(const qkdec_kv_layer* kv, const int32_t* slot, cons
  * sequence with n_ctx <= 0 gets O = 0).  n_q_heads % n_kv_heads == 0,
  * n_q_heads / n_kv_heads <= 16.  1 <= B <= 16.
  * workspace: device memory of at least qkdec_attn_workspace_size() bytes
- * (the partial results of the runs; calls that share it must not overlap). */
+ * (the partial results of the runs; calls that share it must not overlap);
+ * the size functions return 0 for a shape the entry points reject. */
 size_t qkdec_attn_workspace_size(int32_t B, int32_t n_q_heads, const qkdec_kv_layer* kv);
 qkdec_status qkdec_attn_decode(const qkdec_kv_layer* kv, const int32_t* slot, const int32_t* n_ctx,
                                int32_t B, const uint16_t* Q, int32_t n_q_heads, float scale,

@@ -215,7 +215,7 @@ hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, con
   a.max_pages = pages ? max_pages : 0;
   a.page_shift = 0;
   while (pages && (1 << a.page_shift) < kv.capacity) ++a.page_shift;
-  a.seq_cap = attn_seq_cap(kv, pages ? max_pages : 0);
+  a.seq_cap = (int)attn_seq_cap(kv, pages ? max_pages : 0);   // at most 2^30 (checked by the entry points)
   a.n_splits = attn_max_runs(a.seq_cap, kv.n_kv_heads);
   a.runs_wanted = attn_runs_wanted(B, kv.n_kv_heads, kv_k_q8(kv.type) || kv_v_q8(kv.type));
   const int D = kv.head_dim;

@@ -130,10 +130,11 @@ constexpr int kAttnTargetF16 = 256;
 constexpr int kAttnTargetQ8 = 512;
 // partial-result rows per (b, q head): independent of B and of the cache
 // type, so a workspace sized for one batch serves any smaller one
-inline int attn_max_runs(int capacity, int n_kv) {
-  const int by_len = (capacity + kAttnChunk - 1) / kAttnChunk;
-  const int by_fill = (kAttnTargetQ8 + n_kv - 1) / n_kv;
-  return by_len > by_fill ? by_len : by_fill;
+// (capacity: most tokens of one sequence, at most 2^31 - 1; n_kv >= 1)
+inline int attn_max_runs(int64_t capacity, int n_kv) {
+  const int64_t by_len = (capacity + kAttnChunk - 1) / kAttnChunk;
+  const int64_t by_fill = (kAttnTargetQ8 + (int64_t)n_kv - 1) / n_kv;
+  return (int)(by_len > by_fill ? by_len : by_fill);
 }
 // runs wanted per sequence for a call with B sequences (before the per-
 // sequence limits)
@@ -143,13 +144,13 @@ inline int attn_runs_wanted(int B, int n_kv, bool q8) {
   return w > 1 ? w : 1;
 }
 // partial results per (b, q head, run): m, l, then head_dim values of o
-inline size_t attn_partials_bytes(int B, int n_q_heads, int head_dim, int capacity, int n_kv) {
+inline size_t attn_partials_bytes(int B, int n_q_heads, int head_dim, int64_t capacity, int n_kv) {
   return (size_t)B * n_q_heads * attn_max_runs(capacity, n_kv) * (size_t)(head_dim + 2) * sizeof(float);
 }
 // most tokens one sequence can hold: the slot capacity, or for a paged pool
 // (max_pages > 0) max_pages pages of kv.capacity tokens
-inline int attn_seq_cap(const qkdec_kv_layer& kv, int max_pages) {
-  return max_pages > 0 ? max_pages * kv.capacity : kv.capacity;
+inline int64_t attn_seq_cap(const qkdec_kv_layer& kv, int max_pages) {
+  return max_pages > 0 ? (int64_t)max_pages * kv.capacity : kv.capacity;
 }
 // The merge of the runs' partial results into O / O16 (attn_merge_elem, one
 // output element per call)

@@ -75,7 +75,8 @@ qkdec_status check_model(const qkdec_model* m, const qkdec_kv_layer* kv) {
     return QKDEC_E_SHAPE;
   if (m->head_dim != 64 && m->head_dim != 128) return QKDEC_E_SHAPE;
   if (((int64_t)m->n_q_heads * m->head_dim) % 256 != 0) return QKDEC_E_SHAPE;
-  if ((int64_t)(m->n_q_heads + 2 * m->n_kv_heads) * m->head_dim > kGemmMaxRows || 2 * (int64_t)m->ffn > kGemmMaxRows ||
+  if (((int64_t)m->n_q_heads + 2 * (int64_t)m->n_kv_heads) * m->head_dim > kGemmMaxRows ||
+      2 * (int64_t)m->ffn > kGemmMaxRows ||
       m->hidden > kSsMaxSlots * kSsCols)
     return QKDEC_E_SHAPE;
   if (!(m->rms_eps >= 0.f) || !(m->rope_base > 0.f)) return QKDEC_E_ARG;
@@ -444,8 +445,15 @@ qkdec_status qkdec_kv_append(const qkdec_kv_layer* kv, const int32_t* slot, cons
   return kv_append_common(kv, -1, slot, pos, k, v, B, err, stream);
 }
 
+// The shapes qkdec_attn_decode(_paged) accept (pointers aside): 0 otherwise.
+static bool attn_shape_ok(int32_t B, int32_t n_q_heads, const qkdec_kv_layer* kv) {
+  return kv && (kv->head_dim == 64 || kv->head_dim == 128) && kv->n_kv_heads >= 1 && kv->capacity >= 32 &&
+         kv->capacity % 32 == 0 && B >= 1 && B <= 16 && n_q_heads >= 1 && n_q_heads % kv->n_kv_heads == 0 &&
+         n_q_heads / kv->n_kv_heads <= 16;
+}
+
 size_t qkdec_attn_workspace_size(int32_t B, int32_t n_q_heads, const qkdec_kv_layer* kv) {
-  if (!kv || B < 1 || n_q_heads < 1 || kv->capacity < 1 || kv->head_dim < 1) return 0;
+  if (!attn_shape_ok(B, n_q_heads, kv)) return 0;
   return attn_partials_bytes(B, n_q_heads, kv->head_dim, kv->capacity, kv->n_kv_heads);
 }
 
@@ -477,8 +485,7 @@ static qkdec_status check_pages(const qkdec_kv_layer* kv, const int32_t* pages, 
 }
 
 size_t qkdec_attn_paged_workspace_size(int32_t B, int32_t n_q_heads, const qkdec_kv_layer* kv, int32_t max_pages) {
-  if (!kv || B < 1 || n_q_heads < 1 || kv->capacity < 1 || kv->head_dim < 1 || max_pages < 1 ||
-      (int64_t)max_pages * kv->capacity > ((int64_t)1 << 30))
+  if (!attn_shape_ok(B, n_q_heads, kv) || max_pages < 1 || (int64_t)max_pages * kv->capacity > ((int64_t)1 << 30))
     return 0;
   return attn_partials_bytes(B, n_q_heads, kv->head_dim, attn_seq_cap(*kv, max_pages), kv->n_kv_heads);
 }
