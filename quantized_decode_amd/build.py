@@ -19,7 +19,7 @@ OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqkdec.so")
 ARCH = os.environ.get("QKDEC_ARCH", "gfx950")
 
-SOURCES = ["gemm_q4k.hip", "gemm_wk.hip", "attn_decode.hip", "kv_append.hip", "small.hip", "qkdec.hip"]
+SOURCES = ["gemm_q4k.hip", "gemm_wk.hip", "attn_decode.hip", "kv_append.hip", "small.hip", "prefill.hip", "qkdec.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

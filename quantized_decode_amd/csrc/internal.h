@@ -211,4 +211,30 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_prefill_rows(int s, int start, const int32_t* tokens, int rows, int32_t* slot, int32_t* pos,
                                int32_t* tok, hipStream_t st);
 
+// ---- prompt ingestion (prefill.hip): chunks of up to kPfRows prompt tokens
+// of one sequence.  A projection is gemm_pf (partial sums of ksplit K ranges,
+// part[ks][T][n_rows]) and pf_finish (their sum); a projection's fp16 input
+// comes with its 32-value sub-block sums xs [T][K/256][4] (half4) and the
+// factors fdm [T][K/256] (float2) of each row super-block (pf_norm, or
+// pf_finish for the SwiGLU output).
+constexpr int kPfRows = 64;
+constexpr int kPfTilesPerWave = 2;    // weight tiles of 16 rows per wave: 128 rows per work-group
+constexpr int kPfTargetGroups = 256;  // work-groups per projection launch aimed at (one per CU)
+// K ranges (1 .. K / 256) of a projection with n_rows weight rows
+int pf_ksplit(int64_t n_rows, int64_t K);
+// n_rows % 128 == 0, K % 256 == 0, 1 <= T <= kPfRows
+hipError_t launch_gemm_pf(const void* W, int64_t n_rows, int64_t K, const uint16_t* X, int64_t ldx, const void* xs,
+                          const void* fdm, int T, float* part, int ksplit, hipStream_t st);
+enum PfFinishMode {
+  kPfOut = 0,     // out = res + sum of the partials
+  kPfNorm = 1,    // and ssq [T][N/256]: the sum of squares of each 256 values of out
+  kPfSwiglu = 2,  // h [T][N/2] = f16b(silu(gate) up) with its xs, fdm (gate: columns [0, N/2), up: [N/2, N))
+};
+hipError_t launch_pf_finish(const float* part, int ksplit, int T, int N, const float* res, float* out, int64_t ldo,
+                            int mode, float* ssq, uint16_t* h, void* xs, void* fdm, hipStream_t st);
+// h [T][K] = f16(RMSNorm(x) gamma) from the block sums of squares ssq, with its
+// xs, fdm; x = null: only the sums of the fp16 rows already in h
+hipError_t launch_pf_norm(const float* x, const float* ssq, const float* gamma, float eps, int K, int T, uint16_t* h,
+                          void* xs, void* fdm, hipStream_t st);
+
 }  // namespace qk

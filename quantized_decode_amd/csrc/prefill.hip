@@ -1,0 +1,351 @@
+// Prompt ingestion (qkdec_prefill) on MFMA tiles of up to 64 prompt tokens.
+// (P1, P2, P3: the three pages listed, with their titles, at the top of include/qkdec.h.)
+//
+// P2 "This is the mirror image of the prefill story": unlike decode, a prompt
+// has many rows per weight, so one weight read serves all of them and the
+// products, not the bytes, set the pace.  A chunk of up to kPfRows tokens of
+// one sequence is one pass of the layers.  Each projection is
+//
+//   gemm_pf_kernel   64 prompt rows x 64 * NTW weight rows per work-group over
+//                    a range of K super-blocks (split-K across work-groups).
+//                    The 64 x 256 fp16 activation tile of a super-block, its
+//                    sub-block sums and row factors are staged in LDS once
+//                    per work-group (double-buffered); each wave decodes NTW
+//                    weight tiles of 16 rows exactly (sc*q, as in the decode
+//                    GEMM) and runs them against the four 16-row activation
+//                    tiles read from LDS.  Partial sums go to part[ks][t][n].
+//   pf_finish_kernel one work-group per (256 columns, prompt row): the K
+//                    ranges' partial sums added in order (+ the residual, and
+//                    each block's sum of squares), or the SwiGLU output
+//                    rounded per 256 values with a power-of-two offset (the
+//                    decode step's f16b staging) and its sub-block sums.
+//   pf_norm_kernel   the same blocks: h = f16(x rinv gamma) with rinv from the
+//                    row's block sums of squares, and its sub-block sums.
+//
+// The min term of Q4_K (dmin * m * sum x) uses the fp16 hi/lo split of each
+// 32-value sub-block sum, and a row super-block whose sums leave fp16's range
+// stages them divided by 32 -- the decode GEMM's rule (a_sums in q4k_dev.h),
+// formed here once per row and super-block by the kernel that writes the
+// activations.
+//
+// RoPE, the KV append and the attention are the decode kernels with the
+// chunk's tokens as rows (the append lands before any row attends; row i
+// attends over start + i + 1 tokens).
+#include "common.h"
+#include "internal.h"
+#include "q4k_dev.h"
+
+namespace qk {
+
+constexpr int kPfLd = 264;   // LDS row stride of the activation tile (halfs): 256 + 8 keeps rows off one bank
+
+struct PfGemmArgs {
+  const uint8_t* W;      // Q4_K tiles [N/16][kb][16][144]
+  const half_t* X;       // [T][ldx] fp16 activations
+  int64_t ldx;
+  const half4_t* xs;     // [T][kb][4] sub-block sums of X (pf_block_sums)
+  const float2* fdm;     // [T][kb] (d factor, dmin factor) of each row super-block
+  float* part;           // [ksplit][T][N] partial sums
+  int kb, T, N, ksplit;
+};
+
+template <int NTW>
+__global__ void __launch_bounds__(256, 1) gemm_pf_kernel(const PfGemmArgs a) {
+  __shared__ __attribute__((aligned(16))) half_t s_x[2][kPfRows * kPfLd];
+  __shared__ half4_t s_xs[2][kPfRows][4];   // sub-block sums of lane group g: hi 2g, hi 2g+1, lo 2g, lo 2g+1
+  __shared__ float2 s_f[2][kPfRows];        // (d factor, dmin factor) of each row
+  const int tx = threadIdx.x, lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
+  const int g = lane >> 4, r = lane & 15;
+  const int ks = blockIdx.y;
+  const int b0 = (int)((int64_t)ks * a.kb / a.ksplit), b1 = (int)((int64_t)(ks + 1) * a.kb / a.ksplit);
+  const int tile0 = (blockIdx.x * 4 + wave) * NTW;
+
+  // ---- activation staging: thread tx moves 8 halfs of column (tx & 31) * 8
+  // in rows (tx >> 5) + 8 i, i < 8, the sums of row tx >> 2, group tx & 3 and
+  // (tx < 64) the factors of row tx
+  const int xcol = (tx & 31) * 8, xrow = tx >> 5;
+  u32x4 xr[8];
+  half4_t xsr;
+  float2 fr2;
+  auto load_x = [&](int sb) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = xrow + 8 * i;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row < a.T) v = *reinterpret_cast<const u32x4*>(a.X + (size_t)row * a.ldx + (size_t)sb * 256 + xcol);
+      xr[i] = v;
+    }
+    const int srow = tx >> 2;
+    xsr = half4_t{0, 0, 0, 0};
+    if (srow < a.T) xsr = a.xs[((size_t)srow * a.kb + sb) * 4 + (tx & 3)];
+    fr2 = make_float2(1.f, 1.f);
+    if (tx < a.T) fr2 = a.fdm[(size_t)tx * a.kb + sb];
+  };
+  auto store_x = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(&s_x[buf][(xrow + 8 * i) * kPfLd + xcol]) = xr[i];
+    s_xs[buf][tx >> 2][tx & 3] = xsr;
+    if (tx < kPfRows) s_f[buf][tx] = fr2;
+  };
+
+  auto wsrc = [&](int tt, int sb) { return a.W + ((size_t)(tile0 + tt) * a.kb + sb) * 2304 + (size_t)r * 144; };
+  const NibbleMasks km = {in_vgpr(0x000F000Fu), in_vgpr(0x00F000F0u), in_vgpr(0x64006400u)};
+  floatx4 acc[NTW][4];
+#pragma unroll
+  for (int tt = 0; tt < NTW; ++tt)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[tt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  Q4Frag fr[NTW], fn[NTW];
+  load_x(b0);
+#pragma unroll
+  for (int tt = 0; tt < NTW; ++tt) load_frag(fn[tt], wsrc(tt, b0), g);
+  store_x(0);
+  __syncthreads();
+  for (int sb = b0; sb < b1; ++sb) {
+    const int buf = (sb - b0) & 1;
+    const bool more = sb + 1 < b1;
+#pragma unroll
+    for (int tt = 0; tt < NTW; ++tt) fr[tt] = fn[tt];
+    if (more) {
+      load_x(sb + 1);
+#pragma unroll
+      for (int tt = 0; tt < NTW; ++tt) load_frag(fn[tt], wsrc(tt, sb + 1), g);
+    }
+    float d[NTW], dm[NTW];
+    half4_t bm[NTW];
+    half8_t bq[NTW][8];
+#pragma unroll
+    for (int tt = 0; tt < NTW; ++tt) {
+      const Q4Header h = q4_header(fr[tt], g);
+      d[tt] = h.d;
+      dm[tt] = h.dmin;
+      const half2_t mm = pack_h2(h.m0, h.m1);
+      bm[tt][0] = mm[0]; bm[tt][1] = mm[1]; bm[tt][2] = mm[0]; bm[tt][3] = mm[1];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) bq[tt][j] = q4_word(fr[tt], h, j, km);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const half_t* xs = &s_x[buf][(mt * 16 + r) * kPfLd + 64 * g];
+      half8_t av[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) av[j] = *reinterpret_cast<const half8_t*>(xs + 8 * j);
+      const half4_t axs = s_xs[buf][mt * 16 + r][g];
+      float fd[4], fm[4];
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const float2 f = s_f[buf][mt * 16 + 4 * g + ii];
+        fd[ii] = f.x;
+        fm[ii] = f.y;
+      }
+      const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int tt = 0; tt < NTW; ++tt) {
+        const floatx4 sm = __builtin_amdgcn_mfma_f32_16x16x16f16(axs, bm[tt], zero, 0, 0, 0);
+        floatx4 sq = zero;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sq = mfma16x16x32(av[j], bq[tt][j], sq);
+        // d * fd and dmin * fm are exact (the factors are powers of two)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          acc[tt][mt][ii] =
+              __builtin_fmaf(d[tt] * fd[ii], sq[ii], __builtin_fmaf(-dm[tt] * fm[ii], sm[ii], acc[tt][mt][ii]));
+      }
+    }
+    if (more) store_x(buf ^ 1);
+    __syncthreads();
+  }
+
+  // lane (g, r) holds rows mt * 16 + 4g + ii of output column 16 tile + r
+  float* dst = a.part + (size_t)ks * a.T * a.N;
+#pragma unroll
+  for (int tt = 0; tt < NTW; ++tt) {
+    const int n = (tile0 + tt) * 16 + r;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int t = mt * 16 + 4 * g + ii;
+        if (t < a.T) dst[(size_t)t * a.N + n] = acc[tt][mt][ii];
+      }
+  }
+}
+
+// ---- finish of a projection and staging of the next one's input, one
+// work-group (256 threads) per 256-column block c = blockIdx.x of row t =
+// blockIdx.y: thread tx owns column 256 c + tx.
+
+// The staged fp16 value v of thread tx (super-block c of row t): the 32-value
+// sub-block sums of the block (fp32 over the fp16 values) as the GEMM's min
+// term takes them, hi/lo fp16 pairs per lane group g (divided by 32 when one
+// of them leaves fp16's range, dmin's factor then 32 fd), and (fd, fm).
+__device__ void pf_block_sums(half_t v, float fd, int kb, int t, int c, half4_t* xs, float2* fdm) {
+  __shared__ float s_ms[4];
+  const int tx = threadIdx.x, lane = tx & 63, wave = tx >> 6;
+  float s = (float)v;
+#pragma unroll
+  for (int o = 1; o <= 16; o <<= 1) s += __shfl_xor(s, o);   // lanes 0-31: sub-block 2 wave, 32-63: 2 wave + 1
+  const float s1 = __shfl_xor(s, 32);
+  if (lane == 0) s_ms[wave] = fmaxf(fabsf(s), fabsf(s1));
+  __syncthreads();
+  const float ms = fmaxf(fmaxf(s_ms[0], s_ms[1]), fmaxf(s_ms[2], s_ms[3]));
+  const bool big = ms > 65504.f;
+  if (lane == 0) {
+    const float a0 = big ? s * 0.03125f : s, a1 = big ? s1 * 0.03125f : s1;
+    const half_t h0 = (half_t)a0, h1 = (half_t)a1;
+    half4_t q;
+    q[0] = h0; q[1] = h1; q[2] = (half_t)(a0 - (float)h0); q[3] = (half_t)(a1 - (float)h1);
+    xs[((size_t)t * kb + c) * 4 + wave] = q;
+    if (wave == 0) fdm[(size_t)t * kb + c] = make_float2(fd, big ? 32.f * fd : fd);
+  }
+}
+
+struct PfFinishArgs {
+  const float* part;     // [ksplit][T][N] (ksplit may be 0)
+  int ksplit, T, N;
+  const float* res;      // [T][ldo] added to the sums, or null (may alias out)
+  float* out;            // kPfOut, kPfNorm: [T][ldo]
+  int64_t ldo;
+  int mode;
+  float* ssq;            // kPfNorm: [T][N / 256] sum of squares of each block of out
+  half_t* h;             // kPfSwiglu: [T][N / 2] fp16 input of the down projection
+  half4_t* xs;           // and its sums and factors (pf_block_sums)
+  float2* fdm;
+};
+
+__global__ void __launch_bounds__(256) pf_finish_kernel(const PfFinishArgs a) {
+  __shared__ float s_red[4];
+  const int c = blockIdx.x, t = blockIdx.y, tx = threadIdx.x, lane = tx & 63, wave = tx >> 6;
+  const size_t plane = (size_t)a.T * a.N;
+  const float* pr = a.part + (size_t)t * a.N;
+  auto psum = [&](int k) {
+    float s = 0.f;
+    for (int q = 0; q < a.ksplit; ++q) s += pr[q * plane + k];
+    return s;
+  };
+  const int k = c * 256 + tx;
+  if (a.mode == kPfSwiglu) {
+    // gate in columns [0, F), up in [F, 2F); silu(gate) * up rounded to fp16
+    // with the smallest power-of-two offset that keeps the block finite
+    const int F = a.N / 2;
+    const float z = psum(k), u = psum(F + k);
+    float sil;
+    if (z >= 0.f) {
+      sil = z / (1.f + expf(-z));
+    } else {
+      const float ez = expf(z);
+      sil = z * ez / (1.f + ez);
+    }
+    const float v = sil * u;
+    float am = fabsf(v);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o));
+    if (lane == 0) s_red[wave] = am;
+    __syncthreads();
+    am = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    const int sh = f16_block_shift(am);
+    const half_t hv = (half_t)(v * exp2i(-sh));
+    a.h[(size_t)t * F + k] = hv;
+    pf_block_sums(hv, exp2i(sh), F / 256, t, c, a.xs, a.fdm);
+    return;
+  }
+  if (k >= a.N) return;   // kPfOut only: kPfNorm widths are whole blocks
+  float y = psum(k);
+  if (a.res) y += a.res[(size_t)t * a.ldo + k];
+  a.out[(size_t)t * a.ldo + k] = y;
+  if (a.mode != kPfNorm) return;
+  float q = y * y;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) q += __shfl_xor(q, o);
+  if (lane == 0) s_red[wave] = q;
+  __syncthreads();
+  if (tx == 0) a.ssq[(size_t)t * (a.N / 256) + c] = ((s_red[0] + s_red[1]) + s_red[2]) + s_red[3];
+}
+
+// h = f16(x rinv gamma) for block c of row t, rinv from the row's block sums
+// of squares (added in block order); then its sub-block sums.  x = null:
+// h is already staged (the attention output), only the sums are formed.
+__global__ void __launch_bounds__(256) pf_norm_kernel(const float* __restrict__ x, const float* __restrict__ ssq,
+                                                      const float* __restrict__ gamma, float eps, int K, half_t* h,
+                                                      half4_t* xs, float2* fdm) {
+  __shared__ float s_rinv;
+  const int c = blockIdx.x, t = blockIdx.y, tx = threadIdx.x;
+  const int k = c * 256 + tx, nb = K / 256;
+  half_t hv;
+  if (x) {
+    if (tx == 0) {
+      float tot = 0.f;
+      for (int b = 0; b < nb; ++b) tot += ssq[(size_t)t * nb + b];
+      s_rinv = 1.0f / sqrtf(tot * (1.0f / (float)K) + eps);
+    }
+    __syncthreads();
+    hv = norm_apply(x[(size_t)t * K + k], s_rinv, gamma[k]);
+    h[(size_t)t * K + k] = hv;
+  } else {
+    hv = h[(size_t)t * K + k];
+  }
+  pf_block_sums(hv, 1.f, nb, t, c, xs, fdm);
+}
+
+int pf_ksplit(int64_t n_rows, int64_t K) {
+  const int64_t groups = n_rows / (16 * 4 * kPfTilesPerWave);
+  const int kb = (int)(K / 256);
+  int64_t s = (kPfTargetGroups + groups - 1) / groups;
+  if (s > kb) s = kb;
+  return s < 1 ? 1 : (int)s;
+}
+
+hipError_t launch_gemm_pf(const void* W, int64_t n_rows, int64_t K, const uint16_t* X, int64_t ldx, const void* xs,
+                          const void* fdm, int T, float* part, int ksplit, hipStream_t st) {
+  if (n_rows % (64 * kPfTilesPerWave) != 0 || K % 256 != 0 || T < 1 || T > kPfRows || ksplit < 1 ||
+      ksplit > K / 256)
+    return hipErrorInvalidValue;
+  PfGemmArgs a{};
+  a.W = reinterpret_cast<const uint8_t*>(W);
+  a.X = reinterpret_cast<const half_t*>(X);
+  a.ldx = ldx;
+  a.xs = reinterpret_cast<const half4_t*>(xs);
+  a.fdm = reinterpret_cast<const float2*>(fdm);
+  a.part = part;
+  a.kb = (int)(K / 256);
+  a.T = T;
+  a.N = (int)n_rows;
+  a.ksplit = ksplit;
+  const dim3 grid((unsigned)(n_rows / (64 * kPfTilesPerWave)), (unsigned)ksplit);
+  hipLaunchKernelGGL(gemm_pf_kernel<kPfTilesPerWave>, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pf_finish(const float* part, int ksplit, int T, int N, const float* res, float* out, int64_t ldo,
+                            int mode, float* ssq, uint16_t* h, void* xs, void* fdm, hipStream_t st) {
+  if (T < 1 || T > kPfRows || N < 1 || ksplit < 0 || (mode == kPfNorm && N % 256 != 0) ||
+      (mode == kPfSwiglu && N % 512 != 0))
+    return hipErrorInvalidValue;
+  PfFinishArgs a{};
+  a.part = part;
+  a.ksplit = ksplit;
+  a.T = T;
+  a.N = N;
+  a.res = res;
+  a.out = out;
+  a.ldo = ldo;
+  a.mode = mode;
+  a.ssq = ssq;
+  a.h = reinterpret_cast<half_t*>(h);
+  a.xs = reinterpret_cast<half4_t*>(xs);
+  a.fdm = reinterpret_cast<float2*>(fdm);
+  const int blocks = mode == kPfSwiglu ? N / 512 : (N + 255) / 256;
+  hipLaunchKernelGGL(pf_finish_kernel, dim3(blocks, T), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pf_norm(const float* x, const float* ssq, const float* gamma, float eps, int K, int T, uint16_t* h,
+                          void* xs, void* fdm, hipStream_t st) {
+  if (T < 1 || T > kPfRows || K < 256 || K % 256 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pf_norm_kernel, dim3(K / 256, T), dim3(256), 0, st, x, ssq, gamma, eps, K,
+                     reinterpret_cast<half_t*>(h), reinterpret_cast<half4_t*>(xs), reinterpret_cast<float2*>(fdm));
+  return hipGetLastError();
+}
+
+}  // namespace qk

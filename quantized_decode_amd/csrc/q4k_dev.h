@@ -133,6 +133,38 @@ __device__ __forceinline__ void q4_superblock_mv(const Q4Frag& f, const half8_t 
 }
 
 
+// The hi/lo sums of sub-blocks 2g (pieces 0..3) and 2g+1 (pieces 4..7) of av
+// and the row's dmin factor; fdr is the row's d factor.
+__device__ __forceinline__ void a_sums(const half8_t (&av)[8], float fdr, half4_t& axs, float& fmr) {
+  // pairs of fp16 values added into fp32 accumulators (v_dot2_f32_f16 against
+  // (1, 1)): half the instructions of a convert and an add per value
+  const half2_t one = {(half_t)1.f, (half_t)1.f};
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      s0 = __builtin_amdgcn_fdot2(half2_t{av[j][e], av[j][e + 1]}, one, s0, false);
+      s1 = __builtin_amdgcn_fdot2(half2_t{av[4 + j][e], av[4 + j][e + 1]}, one, s1, false);
+    }
+  // a super-block whose sub-block sums leave fp16's range stages them divided
+  // by 32 (32 values of at most 65504 then fit); dmin is multiplied back
+  float ms = fmaxf(fabsf(s0), fabsf(s1));
+  ms = fmaxf(ms, __shfl_xor(ms, 16));
+  ms = fmaxf(ms, __shfl_xor(ms, 32));
+  const bool big = ms > 65504.f;
+  if (big) {
+    s0 *= 0.03125f;
+    s1 *= 0.03125f;
+  }
+  fmr = big ? 32.f * fdr : fdr;
+  const half_t h0 = (half_t)s0, h1 = (half_t)s1;
+  axs[0] = h0;
+  axs[1] = h1;
+  axs[2] = (half_t)(s0 - (float)h0);
+  axs[3] = (half_t)(s1 - (float)h1);
+}
+
 // smallest s >= 0 with amax * 2^-s <= 65504 (the largest finite fp16)
 __device__ __forceinline__ int f16_block_shift(float amax) {
   const int e = (int)((__builtin_bit_cast(uint32_t, amax) >> 23) & 255u) - 127;

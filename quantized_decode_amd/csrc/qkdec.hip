@@ -242,39 +242,119 @@ qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int3
   return QKDEC_OK;
 }
 
-// ---- prefill: the prompt in chunks of up to kPrefillRows tokens, each chunk
-// one pass of the layers with its tokens as the rows (same slot, consecutive
-// positions); the workspace is laid out once for kPrefillRows rows, followed
-// by the chunk's row arrays
-constexpr int kPrefillRows = 16;
+// ---- prefill: the prompt in chunks of up to kPfRows tokens of the one
+// sequence (consecutive positions), each chunk one pass of the layers with its
+// tokens as the rows: every projection a 64-row MFMA GEMM over split K
+// (gemm_pf) and the finish that adds the K ranges and stages the next input
+// (pf_finish); RoPE, the KV append and the attention are the decode kernels.
+struct PrefillWs {
+  int32_t* err;
+  float* x;        // residual stream [kPfRows][H]
+  float* ss;       // sum-of-squares slots the embedding writes (unused here)
+  uint16_t* h;     // fp16 input of the next projection [kPfRows][max(H, F)]
+  void* xs;        // its sub-block sums [kPfRows][max(H, F, Hq D) / 256][4] (half4)
+  void* fdm;       // and factors [kPfRows][max(H, F, Hq D) / 256] (float2)
+  float* ssq;      // block sums of squares of the residual stream [kPfRows][H / 256]
+  float* qkv;      // [kPfRows][nqkv]
+  uint16_t* q16;   // [kPfRows][Hq D]
+  uint16_t* o16;   // [kPfRows][Hq D]
+  float* part;     // K-range partial sums of the widest projection
+  float* attn_part;
+  float2* rope;
+  void* lm_part;
+  int32_t *rs, *rp, *rt;   // the chunk's slot, position and token of each row
+  size_t bytes;
+};
 
-size_t prefill_bytes(const qkdec_model* m, const qkdec_kv_layer* kv) {
-  return step_layout(m, kPrefillRows, kv, nullptr).bytes + 3 * 256;
+PrefillWs prefill_layout(const qkdec_model* m, const qkdec_kv_layer* kv, char* base) {
+  PrefillWs w{};
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    char* p = base ? base + off : nullptr;
+    off += round_up(n, 256);
+    return p;
+  };
+  const int64_t R = kPfRows, H = m->hidden, F = m->ffn;
+  const int64_t hq = (int64_t)m->n_q_heads * m->head_dim;
+  const int64_t nqkv = (int64_t)(m->n_q_heads + 2 * m->n_kv_heads) * m->head_dim;
+  w.err = reinterpret_cast<int32_t*>(take(256));
+  w.x = reinterpret_cast<float*>(take((size_t)(R * H) * 4));
+  // the embedding kernel writes slot (c / 16) * 16 + row for column c: at most H + 48 floats for 64 rows
+  w.ss = reinterpret_cast<float*>(take((size_t)(H + R) * 4));
+  w.h = reinterpret_cast<uint16_t*>(take((size_t)(R * std::max(H, F)) * 2));
+  const int64_t kbmax = std::max(std::max(H, F), hq) / 256;
+  w.xs = take((size_t)(R * kbmax) * 4 * 8);
+  w.fdm = take((size_t)(R * kbmax) * 8);
+  w.ssq = reinterpret_cast<float*>(take((size_t)(R * (H / 256)) * 4));
+  w.qkv = reinterpret_cast<float*>(take((size_t)(R * nqkv) * 4));
+  w.q16 = reinterpret_cast<uint16_t*>(take((size_t)(R * hq) * 2));
+  w.o16 = reinterpret_cast<uint16_t*>(take((size_t)(R * hq) * 2));
+  size_t pb = 0;
+  const int64_t shapes[4][2] = {{nqkv, H}, {H, hq}, {2 * F, H}, {H, F}};
+  for (const auto& nk : shapes) pb = std::max(pb, (size_t)pf_ksplit(nk[0], nk[1]) * (size_t)(R * nk[0]) * 4);
+  w.part = reinterpret_cast<float*>(take(pb));
+  w.attn_part = reinterpret_cast<float*>(
+      take(attn_partials_bytes(kPfRows, m->n_q_heads, m->head_dim, kv[0].capacity, kv[0].n_kv_heads)));
+  w.rope = reinterpret_cast<float2*>(take((size_t)R * (m->head_dim / 2) * sizeof(float2)));
+  w.lm_part = take(lm_head_partials_bytes(m->vocab, 1));
+  w.rs = reinterpret_cast<int32_t*>(take(R * 4));
+  w.rp = reinterpret_cast<int32_t*>(take(R * 4));
+  w.rt = reinterpret_cast<int32_t*>(take(R * 4));
+  w.bytes = off;
+  return w;
 }
+
+size_t prefill_bytes(const qkdec_model* m, const qkdec_kv_layer* kv) { return prefill_layout(m, kv, nullptr).bytes; }
 
 qkdec_status run_prefill(const qkdec_model* m, const qkdec_kv_layer* kv, int slot, int start, const int32_t* tokens,
                          int n, float* logits, int32_t* tok_out, void* workspace, hipStream_t st) {
-  char* base = reinterpret_cast<char*>(workspace);
-  const StepWs w = step_layout(m, kPrefillRows, kv, base);
-  int32_t* rs = reinterpret_cast<int32_t*>(base + w.bytes);
-  int32_t* rp = rs + 64;
-  int32_t* rt = rs + 128;
+  const PrefillWs w = prefill_layout(m, kv, reinterpret_cast<char*>(workspace));
+  const int H = m->hidden, F = m->ffn, D = m->head_dim, Hq = m->n_q_heads;
+  const int64_t hq = (int64_t)Hq * D;
+  const int nqkv = (Hq + 2 * m->n_kv_heads) * D;
+  const float scale = 1.0f / sqrtf((float)D);
+  const int ks_qkv = pf_ksplit(nqkv, H), ks_o = pf_ksplit(H, hq), ks_gu = pf_ksplit(2 * (int64_t)F, H),
+            ks_dn = pf_ksplit(H, F);
+#define QK_TRY(expr)                                 \
+  do {                                               \
+    const hipError_t e_ = (expr);                    \
+    if (e_ != hipSuccess) return QKDEC_E_HIP;        \
+  } while (0)
   int rows = 0;
-  for (int off = 0; off < n; off += kPrefillRows) {
-    rows = n - off < kPrefillRows ? n - off : kPrefillRows;
-    if (launch_prefill_rows(slot, start + off, tokens + off, rows, rs, rp, rt, st) != hipSuccess) return QKDEC_E_HIP;
-    const qkdec_status s = run_layers(m, kv, rs, rp, rt, rows, w, st, nullptr, 0, nullptr);
-    if (s != QKDEC_OK) return s;
+  for (int off = 0; off < n; off += kPfRows) {
+    rows = n - off < kPfRows ? n - off : kPfRows;
+    QK_TRY(launch_prefill_rows(slot, start + off, tokens + off, rows, w.rs, w.rp, w.rt, st));
+    QK_TRY(launch_rope_table(w.rp, rows, D, m->rope_base, w.rope, st));
+    QK_TRY(launch_embed(m->embed, H, m->vocab, w.rt, rows, w.x, w.ss, st));
+    // the first layer's input: RMSNorm of the embedding rows
+    QK_TRY(launch_pf_finish(w.part, 0, rows, H, w.x, w.x, H, kPfNorm, w.ssq, nullptr, nullptr, nullptr, st));
+    QK_TRY(launch_pf_norm(w.x, w.ssq, m->layers[0].norm_attn, m->rms_eps, H, rows, w.h, w.xs, w.fdm, st));
+    for (int l = 0; l < m->n_layers; ++l) {
+      const qkdec_layer& ly = m->layers[l];
+      QK_TRY(launch_gemm_pf(ly.w_qkv, nqkv, H, w.h, H, w.xs, w.fdm, rows, w.part, ks_qkv, st));
+      QK_TRY(launch_pf_finish(w.part, ks_qkv, rows, nqkv, nullptr, w.qkv, nqkv, kPfOut, nullptr, nullptr, nullptr,
+                              nullptr, st));
+      QK_TRY(launch_rope_append(kv[l], w.qkv, nqkv, Hq, rows, w.rs, w.rp, m->rope_base, w.q16, w.err, st, w.rp,
+                                w.rope));
+      QK_TRY(launch_attn_decode(kv[l], w.rs, w.rp, rows, w.q16, Hq, scale, nullptr, w.o16, w.attn_part, 1, st));
+      QK_TRY(launch_pf_norm(nullptr, nullptr, nullptr, 0.f, (int)hq, rows, w.o16, w.xs, w.fdm, st));
+      QK_TRY(launch_gemm_pf(ly.w_o, H, hq, w.o16, hq, w.xs, w.fdm, rows, w.part, ks_o, st));
+      QK_TRY(launch_pf_finish(w.part, ks_o, rows, H, w.x, w.x, H, kPfNorm, w.ssq, nullptr, nullptr, nullptr, st));
+      QK_TRY(launch_pf_norm(w.x, w.ssq, ly.norm_ffn, m->rms_eps, H, rows, w.h, w.xs, w.fdm, st));
+      QK_TRY(launch_gemm_pf(ly.w_gate_up, 2 * (int64_t)F, H, w.h, H, w.xs, w.fdm, rows, w.part, ks_gu, st));
+      QK_TRY(launch_pf_finish(w.part, ks_gu, rows, 2 * F, nullptr, nullptr, 0, kPfSwiglu, nullptr, w.h, w.xs, w.fdm,
+                              st));
+      QK_TRY(launch_gemm_pf(ly.w_down, H, F, w.h, F, w.xs, w.fdm, rows, w.part, ks_dn, st));
+      QK_TRY(launch_pf_finish(w.part, ks_dn, rows, H, w.x, w.x, H, kPfNorm, w.ssq, nullptr, nullptr, nullptr, st));
+      // the next layer's attention input, or after the last layer the final norm
+      const float* gamma = l + 1 < m->n_layers ? m->layers[l + 1].norm_attn : m->norm_final;
+      QK_TRY(launch_pf_norm(w.x, w.ssq, gamma, m->rms_eps, H, rows, w.h, w.xs, w.fdm, st));
+    }
   }
-  // final norm and LM head of the prompt's last token only (row rows - 1 of
-  // the last chunk; its sum-of-squares slots are every 16th value from row)
-  const int last = rows - 1;
-  if (launch_rmsnorm_f16(w.x + (size_t)last * m->hidden, m->norm_final, w.ss + last, m->hidden, 1, m->rms_eps, w.h,
-                         st) != hipSuccess)
-    return QKDEC_E_HIP;
-  if (launch_lm_head_argmax(m->lm_head, m->vocab, m->hidden, w.h, 1, logits, tok_out, w.lm_part, nullptr, st) !=
-      hipSuccess)
-    return QKDEC_E_HIP;
+  // the LM head of the prompt's last token (row rows - 1 of the last chunk)
+  QK_TRY(launch_lm_head_argmax(m->lm_head, m->vocab, H, w.h + (size_t)(rows - 1) * H, 1, logits, tok_out, w.lm_part,
+                               nullptr, st));
+#undef QK_TRY
   return QKDEC_OK;
 }
 
@@ -655,7 +735,7 @@ qkdec_status qkdec_prefill(const qkdec_model* m, const qkdec_kv_layer* kv, int32
   if ((int64_t)start + n > kv[0].capacity) return QKDEC_E_CAPACITY;
   if (!workspace || ws_bytes < prefill_bytes(m, kv)) return QKDEC_E_WORKSPACE;
   if (!aligned(workspace, 256)) return QKDEC_E_ALIGN;
-  s = check_lds(lm_head_lds_bytes(m->hidden, kPrefillRows));
+  s = check_lds(lm_head_lds_bytes(m->hidden, 1));
   if (s != QKDEC_OK) return s;
   clear_stale_error();
   return run_prefill(m, kv, slot, start, tokens, n, logits, tok_out, workspace, as_stream(stream));

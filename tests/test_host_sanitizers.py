@@ -20,7 +20,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "quantized_decode_amd", "csrc")
 HIPCC = "/opt/rocm/bin/hipcc"
 CLANG = "/opt/rocm/lib/llvm/bin/clang++"
-SOURCES = ["gemm_q4k", "gemm_wk", "attn_decode", "kv_append", "small", "qkdec"]
+SOURCES = ["gemm_q4k", "gemm_wk", "attn_decode", "kv_append", "small", "prefill", "qkdec"]
 SAN = ["address", "undefined"]
 
 
