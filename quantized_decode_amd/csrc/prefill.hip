@@ -31,13 +31,13 @@
 // RoPE, the KV append and the attention are the decode kernels with the
 // chunk's tokens as rows (the append lands before any row attends; row i
 // attends over start + i + 1 tokens).
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 #include "q4k_dev.h"
 
 namespace qk {
-
-constexpr int kPfLd = 264;   // LDS row stride of the activation tile (halfs): 256 + 8 keeps rows off one bank
 
 struct PfGemmArgs {
   const uint8_t* W;      // Q4_K tiles [N/16][kb][16][144]
@@ -50,8 +50,13 @@ struct PfGemmArgs {
 };
 
 template <int NTW>
-__global__ void __launch_bounds__(256, 1) gemm_pf_kernel(const PfGemmArgs a) {
-  __shared__ __attribute__((aligned(16))) half_t s_x[2][kPfRows * kPfLd];
+__global__ void __launch_bounds__(256, 2) gemm_pf_kernel(const PfGemmArgs a) {
+  // activation tile: row t's 16-byte chunk c at slot c ^ (t & 15) of the row
+  // (512 bytes), so the 16 rows a read instruction touches hit 16 distinct slots
+  // (two buffers as separate objects, so the compiler can tell the tile being
+  // read from the one being filled and need not wait for the fill)
+  __shared__ __attribute__((aligned(16))) half_t s_x0[kPfRows * 256];
+  __shared__ __attribute__((aligned(16))) half_t s_x1[kPfRows * 256];
   __shared__ half4_t s_xs[2][kPfRows][4];   // sub-block sums of lane group g: hi 2g, hi 2g+1, lo 2g, lo 2g+1
   __shared__ float2 s_f[2][kPfRows];        // (d factor, dmin factor) of each row
   const int tx = threadIdx.x, lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
@@ -60,20 +65,24 @@ __global__ void __launch_bounds__(256, 1) gemm_pf_kernel(const PfGemmArgs a) {
   const int b0 = (int)((int64_t)ks * a.kb / a.ksplit), b1 = (int)((int64_t)(ks + 1) * a.kb / a.ksplit);
   const int tile0 = (blockIdx.x * 4 + wave) * NTW;
 
-  // ---- activation staging: thread tx moves 8 halfs of column (tx & 31) * 8
-  // in rows (tx >> 5) + 8 i, i < 8, the sums of row tx >> 2, group tx & 3 and
-  // (tx < 64) the factors of row tx
-  const int xcol = (tx & 31) * 8, xrow = tx >> 5;
-  u32x4 xr[8];
+  // ---- activation staging.  The tile goes from global memory straight to LDS:
+  // wave w moves rows 16 w .. 16 w + 15, two rows (1 KB) per instruction, lane
+  // l filling slot l & 31 of row 2 q + (l >> 5) (rows past T repeat row T - 1,
+  // whose products are never stored).  The sums of row tx >> 2, group tx & 3
+  // and (tx < 64) the factors of row tx pass through registers.
   half4_t xsr;
   float2 fr2;
-  auto load_x = [&](int sb) {
+  auto load_x = [&](int sb, half_t* dst) {
+    // the addresses are formed anew at every call (kept out of registers
+    // between super-blocks)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int row = xrow + 8 * i;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row < a.T) v = *reinterpret_cast<const u32x4*>(a.X + (size_t)row * a.ldx + (size_t)sb * 256 + xcol);
-      xr[i] = v;
+      const int q = wave * 8 + i, row = 2 * q + (ln >> 5), slot = ln & 31;
+      const int srow = row < a.T ? row : a.T - 1;
+      const half_t* src = a.X + (size_t)srow * a.ldx + (size_t)sb * 256 + (size_t)((slot ^ (row & 15)) * 8);
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&dst[q * 512], 16, 0, 0);
     }
     const int srow = tx >> 2;
     xsr = half4_t{0, 0, 0, 0};
@@ -82,11 +91,12 @@ __global__ void __launch_bounds__(256, 1) gemm_pf_kernel(const PfGemmArgs a) {
     if (tx < a.T) fr2 = a.fdm[(size_t)tx * a.kb + sb];
   };
   auto store_x = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(&s_x[buf][(xrow + 8 * i) * kPfLd + xcol]) = xr[i];
     s_xs[buf][tx >> 2][tx & 3] = xsr;
     if (tx < kPfRows) s_f[buf][tx] = fr2;
   };
+  // every wave's tile loads have landed in LDS before the barrier that
+  // publishes them (vmcnt(0); expcnt and lgkmcnt left at their maxima)
+  auto wait_loads = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
   auto wsrc = [&](int tt, int sb) { return a.W + ((size_t)(tile0 + tt) * a.kb + sb) * 2304 + (size_t)r * 144; };
   const NibbleMasks km = {in_vgpr(0x000F000Fu), in_vgpr(0x00F000F0u), in_vgpr(0x64006400u)};
@@ -97,18 +107,23 @@ __global__ void __launch_bounds__(256, 1) gemm_pf_kernel(const PfGemmArgs a) {
     for (int mt = 0; mt < 4; ++mt) acc[tt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   Q4Frag fr[NTW], fn[NTW];
-  load_x(b0);
+  load_x(b0, s_x0);
 #pragma unroll
   for (int tt = 0; tt < NTW; ++tt) load_frag(fn[tt], wsrc(tt, b0), g);
   store_x(0);
+  wait_loads();
   __syncthreads();
-  for (int sb = b0; sb < b1; ++sb) {
-    const int buf = (sb - b0) & 1;
+  // one super-block: multiply the tile in buffer BUF while the next one is
+  // loaded into the other
+  auto step = [&](auto bufc, int sb) {
+    constexpr int BUF = decltype(bufc)::value;
+    half_t* const cur = BUF == 0 ? s_x0 : s_x1;
+    half_t* const nxt = BUF == 0 ? s_x1 : s_x0;
     const bool more = sb + 1 < b1;
 #pragma unroll
     for (int tt = 0; tt < NTW; ++tt) fr[tt] = fn[tt];
     if (more) {
-      load_x(sb + 1);
+      load_x(sb + 1, nxt);
 #pragma unroll
       for (int tt = 0; tt < NTW; ++tt) load_frag(fn[tt], wsrc(tt, sb + 1), g);
     }
@@ -127,15 +142,15 @@ __global__ void __launch_bounds__(256, 1) gemm_pf_kernel(const PfGemmArgs a) {
     }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const half_t* xs = &s_x[buf][(mt * 16 + r) * kPfLd + 64 * g];
+      const half_t* xs = &cur[(mt * 16 + r) * 256];
       half8_t av[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) av[j] = *reinterpret_cast<const half8_t*>(xs + 8 * j);
-      const half4_t axs = s_xs[buf][mt * 16 + r][g];
+      for (int j = 0; j < 8; ++j) av[j] = *reinterpret_cast<const half8_t*>(xs + ((8 * g + j) ^ r) * 8);
+      const half4_t axs = s_xs[BUF][mt * 16 + r][g];
       float fd[4], fm[4];
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        const float2 f = s_f[buf][mt * 16 + 4 * g + ii];
+        const float2 f = s_f[BUF][mt * 16 + 4 * g + ii];
         fd[ii] = f.x;
         fm[ii] = f.y;
       }
@@ -153,8 +168,15 @@ __global__ void __launch_bounds__(256, 1) gemm_pf_kernel(const PfGemmArgs a) {
               __builtin_fmaf(d[tt] * fd[ii], sq[ii], __builtin_fmaf(-dm[tt] * fm[ii], sm[ii], acc[tt][mt][ii]));
       }
     }
-    if (more) store_x(buf ^ 1);
+    if (more) store_x(BUF ^ 1);
+    wait_loads();
     __syncthreads();
+  };
+  for (int sb = b0;;) {
+    step(std::integral_constant<int, 0>{}, sb);
+    if (++sb >= b1) break;
+    step(std::integral_constant<int, 1>{}, sb);
+    if (++sb >= b1) break;
   }
 
   // lane (g, r) holds rows mt * 16 + 4g + ii of output column 16 tile + r
