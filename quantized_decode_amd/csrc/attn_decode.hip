@@ -48,12 +48,32 @@ constexpr int kAttnWaves = 4;
 
 // Two waves per SIMD: with the split key / value prefetch the fp16 kernel
 // fits 256 registers without spilling (see the run targets next to kAttnChunk)
-template <int D, int KF, int VF, bool PAGED>
+//
+// MULTI (prompt rows, arena only): work item z covers rows z * tok .. + tok - 1
+// of one sequence (consecutive positions); column r is head r % G of row
+// z * tok + r / G.  The runs are those of the item's last row, and each
+// column masks the keys past its own row's length.
+template <int D, int KF, int VF, bool PAGED, bool MULTI = false>
 __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs a) {
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int c = blockIdx.x, g = blockIdx.y;
   const int G = a.Hq / a.n_kv;
-  const int s = PAGED ? 0 : a.slot[b];
-  int n = a.n_ctx[b] + a.n_ctx_add;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lg = lane >> 4, r = lane & 15;
+  // bl: the row whose length sets the runs; (b, hcol): this lane's column
+  int bl, b, hcol;
+  bool colv;
+  if constexpr (MULTI) {
+    const int z = blockIdx.z, u = r / G;
+    bl = min(z * a.tok + a.tok - 1, a.nrows - 1);
+    hcol = r - u * G;
+    colv = u < a.tok && z * a.tok + u < a.nrows;
+    b = colv ? z * a.tok + u : bl;
+  } else {
+    bl = b = blockIdx.z;
+    hcol = r;
+    colv = r < G;
+  }
+  const int s = PAGED ? 0 : a.slot[bl];
+  int n = a.n_ctx[bl] + a.n_ctx_add;
   if (n > a.seq_cap) n = a.seq_cap;
   if (n < 0 || (!PAGED && (s < 0 || s >= a.n_slots))) n = 0;
   const int runs = attn_runs(n, a.runs_wanted, a.n_splits);
@@ -61,12 +81,14 @@ __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs
   const int tiles = (n + 31) / 32;
   const int t_begin = 32 * (c * tiles / runs);
   const int t_end = min(32 * ((c + 1) * tiles / runs), n);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lg = lane >> 4, r = lane & 15;
+  // MULTI: this column's length (at most the item's)
+  int ncol = n;
+  if constexpr (MULTI) ncol = colv ? min(max(a.n_ctx[b] + a.n_ctx_add, 0), n) : 0;
 
   half8_t qf[D / 32];
   {
-    const bool hv = r < G;
-    const half_t* qrow = a.Q + ((size_t)b * a.Hq + g * G + (hv ? r : 0)) * D;
+    const bool hv = colv;
+    const half_t* qrow = a.Q + ((size_t)b * a.Hq + g * G + (hv ? hcol : 0)) * D;
 #pragma unroll
     for (int j = 0; j < D / 32; ++j) {
       const int d0 = KF == kFmtQ8 ? (32 * j + 8 * lg) : ((D / 4) * lg + 8 * j);
@@ -133,8 +155,13 @@ __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs
           load_k(buf[p ^ 1], a, row0, tt, lg, r);
           const int t0 = t_begin + 32 * i;
           // a tile on an unmapped page has no valid token (every score -inf)
-          attn_tile(st, buf[p], qf, a.scale_log2, cur_mapped ? min(32, t_end - t0) : 0, lg,
-                    [&]() { load_v(buf[p ^ 1], a, row0, tt, lg, r); });
+          const int valid = cur_mapped ? min(32, t_end - t0) : 0;
+          if constexpr (MULTI)
+            attn_tile<D, KF, VF, true>(st, buf[p], qf, a.scale_log2, valid, lg,
+                                       [&]() { load_v(buf[p ^ 1], a, row0, tt, lg, r); },
+                                       min(max(ncol - t0, 0), valid));
+          else
+            attn_tile(st, buf[p], qf, a.scale_log2, valid, lg, [&]() { load_v(buf[p ^ 1], a, row0, tt, lg, r); });
         }
       }
     }
@@ -180,8 +207,8 @@ __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs
   }
   const float ltot = st.l + __shfl_xor(st.l, 16);
   const float lsum = ltot + __shfl_xor(ltot, 32);
-  if (r < G) {
-    const size_t row = ((size_t)b * a.Hq + g * G + r) * a.n_splits + c;
+  if (colv) {
+    const size_t row = ((size_t)b * a.Hq + g * G + hcol) * a.n_splits + c;
     float* po = a.part_o + row * D;
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) *reinterpret_cast<floatx4*>(po + 16 * i + 4 * lg) = st.o[i];
@@ -216,6 +243,8 @@ hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, con
   a.page_shift = 0;
   while (pages && (1 << a.page_shift) < kv.capacity) ++a.page_shift;
   a.seq_cap = (int)attn_seq_cap(kv, pages ? max_pages : 0);   // at most 2^30 (checked by the entry points)
+  a.tok = 1;
+  a.nrows = B;
   a.n_splits = attn_max_runs(a.seq_cap, kv.n_kv_heads);
   a.runs_wanted = attn_runs_wanted(B, kv.n_kv_heads, kv_k_q8(kv.type) || kv_v_q8(kv.type));
   const int D = kv.head_dim;
@@ -260,7 +289,82 @@ hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, con
   mg.n_slots = kv.n_slots;
   mg.Hq = n_q_heads;
   mg.D = D;
+  mg.tok = 1;
+  mg.nrows = B;
   mg.O = O;
+  mg.O16 = reinterpret_cast<half_t*>(O16);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(n_q_heads, B), dim3(D), 0, st, mg);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_prefill(const qkdec_kv_layer& kv, const int32_t* slot, const int32_t* n_ctx, int B,
+                               const uint16_t* Q, int n_q_heads, float scale, uint16_t* O16, float* partials,
+                               int n_ctx_add, hipStream_t st) {
+  const int G = n_q_heads / kv.n_kv_heads;
+  if (16 % G != 0 || G == 16)
+    return launch_attn_decode(kv, slot, n_ctx, B, Q, n_q_heads, scale, nullptr, O16, partials, n_ctx_add, st);
+  const int tok = 16 / G, groups = (B + tok - 1) / tok;
+  AttnArgs a;
+  a.k = reinterpret_cast<const uint8_t*>(kv.k);
+  a.v = reinterpret_cast<const uint8_t*>(kv.v);
+  a.ks = reinterpret_cast<const uint16_t*>(kv.k_scale);
+  a.vs = reinterpret_cast<const uint16_t*>(kv.v_scale);
+  a.n_kv = kv.n_kv_heads;
+  a.cap = kv.capacity;
+  a.n_slots = kv.n_slots;
+  a.slot = slot;
+  a.n_ctx = n_ctx;
+  a.n_ctx_add = n_ctx_add;
+  a.Q = reinterpret_cast<const half_t*>(Q);
+  a.Hq = n_q_heads;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.pages = nullptr;
+  a.max_pages = 0;
+  a.page_shift = 0;
+  a.seq_cap = kv.capacity;
+  a.tok = tok;
+  a.nrows = B;
+  a.n_splits = attn_max_runs(a.seq_cap, kv.n_kv_heads);
+  a.runs_wanted = attn_runs_wanted(groups, kv.n_kv_heads, kv_k_q8(kv.type) || kv_v_q8(kv.type));
+  const int D = kv.head_dim;
+  const size_t n_rows = (size_t)B * n_q_heads * a.n_splits;
+  a.part_o = partials;
+  a.part_ml = partials + n_rows * D;
+  const int max_runs = attn_runs(a.seq_cap, a.runs_wanted, a.n_splits);
+  const dim3 grid(max_runs, kv.n_kv_heads, groups);
+  const dim3 blk(64 * kAttnWaves);
+#define QK_ATTN(DD, KF, VF) hipLaunchKernelGGL((attn_split_kernel<DD, KF, VF, false, true>), grid, blk, 0, st, a)
+#define QK_ATTN_D(DD)                                                      \
+  do {                                                                     \
+    if (kf == kFmtF8) QK_ATTN(DD, kFmtF8, kFmtF8);                         \
+    else if (kf == kFmtQ8 && vf == kFmtQ8) QK_ATTN(DD, kFmtQ8, kFmtQ8);    \
+    else if (kf == kFmtQ8) QK_ATTN(DD, kFmtQ8, kFmtF16);                   \
+    else if (vf == kFmtQ8) QK_ATTN(DD, kFmtF16, kFmtQ8);                   \
+    else QK_ATTN(DD, kFmtF16, kFmtF16);                                    \
+  } while (0)
+  const int kf = kv_k_fmt(kv.type), vf = kv_v_fmt(kv.type);
+  if (D == 128) QK_ATTN_D(128);
+  else QK_ATTN_D(64);
+#undef QK_ATTN_D
+#undef QK_ATTN
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  MergeArgs mg;
+  mg.part_o = a.part_o;
+  mg.part_ml = a.part_ml;
+  mg.n_splits = a.n_splits;
+  mg.runs_wanted = a.runs_wanted;
+  mg.slot = slot;
+  mg.paged = 0;
+  mg.n_ctx = n_ctx;
+  mg.n_ctx_add = n_ctx_add;
+  mg.cap = a.seq_cap;
+  mg.n_slots = kv.n_slots;
+  mg.Hq = n_q_heads;
+  mg.D = D;
+  mg.tok = tok;
+  mg.nrows = B;
+  mg.O = nullptr;
   mg.O16 = reinterpret_cast<half_t*>(O16);
   hipLaunchKernelGGL(attn_combine_kernel, dim3(n_q_heads, B), dim3(D), 0, st, mg);
   return hipGetLastError();

@@ -103,6 +103,8 @@ struct AttnArgs {
   const int32_t* pages;
   int max_pages, page_shift;
   int seq_cap;       // most tokens a sequence can hold: cap, or max_pages * page size
+  // prompt rows (attn_split_kernel MULTI): tok rows per work item, nrows rows
+  int tok, nrows;
 };
 
 // Runs of a sequence with n cached tokens (same in the split and merge
@@ -150,7 +152,8 @@ __device__ __forceinline__ void attn_merge_elem(const MergeArgs& mg, int b, int 
     o[j] = part_o[row * D + d];
   }
   __asm__ volatile("" ::: "memory");   // keep the loads above ahead of the run count's
-  int n = n_ctx[b] + n_ctx_add;
+  const int bn = mg.tok > 1 ? min(b / mg.tok * mg.tok + mg.tok - 1, mg.nrows - 1) : b;
+  int n = n_ctx[bn] + n_ctx_add;
   if (n > cap) n = cap;               // cap: the most tokens a sequence holds
   const int s = slot[b];   // unconditional: no branch ahead of the loads above
   if (n < 0 || (!paged && (s < 0 || s >= n_slots))) n = 0;
@@ -321,12 +324,17 @@ constexpr int kPScale = 14;
 // are done, before the value products (the caller issues the next tile's
 // value loads there, into registers this tile's keys no longer need).  The
 // fp16 values of out-of-range tokens are zeroed in place in f.
-template <int D, int KF, int VF, typename Mid>
+// PERCOL: the columns are different query tokens of one sequence (prompt
+// rows), and vcol (this lane's column, <= valid) is the number of the tile's
+// tokens that column may attend to; scores past it are masked.  Otherwise
+// every column sees the same valid tokens (vcol unused).
+template <int D, int KF, int VF, bool PERCOL = false, typename Mid>
 __device__ __forceinline__ void attn_tile(AttnState<D, VF == kFmtQ8>& st, KVFrag<D, KF, VF>& f,
                                           const half8_t (&qf)[D / 32], float scale_log2, int valid, int lg,
-                                          const Mid& mid) {
+                                          const Mid& mid, int vcol = 0) {
   // valid = number of tokens of this 32-token tile that are in range (0..32;
-  // 0 for a tile on an unmapped page of a paged pool)
+  // 0 for a tile on an unmapped page of a paged pool): data past it is never
+  // used
   float sc[8];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
@@ -349,7 +357,10 @@ __device__ __forceinline__ void attn_tile(AttnState<D, VF == kFmtQ8>& st, KVFrag
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[4 * hf + i] = acc[i] * scale_log2;
   }
-  if (valid < 32) {   // uniform branch; selects inside
+  if constexpr (PERCOL) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sc[e] = (8 * lg + e < vcol) ? sc[e] : -__builtin_inff();
+  } else if (valid < 32) {   // uniform branch; selects inside
 #pragma unroll
     for (int e = 0; e < 8; ++e) sc[e] = (8 * lg + e < valid) ? sc[e] : -__builtin_inff();
   }

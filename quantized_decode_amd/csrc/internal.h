@@ -162,6 +162,9 @@ struct MergeArgs {
   int paged;
   const int32_t* n_ctx;
   int n_ctx_add, cap, n_slots, Hq, D;
+  // prompt rows taken tok at a time (launch_attn_prefill): a row's runs are
+  // those of the last of its tok rows (at most nrows - 1); 1 otherwise
+  int tok, nrows;
   float* O;
   _Float16* O16;
 };
@@ -172,6 +175,14 @@ hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, con
                               const uint16_t* Q, int n_q_heads, float scale, float* O, uint16_t* O16,
                               float* partials, int n_ctx_add, hipStream_t st, const int32_t* pages = nullptr,
                               int max_pages = 0);
+// The same attention for B consecutive prompt rows of one sequence (row b:
+// slot[b], n_ctx[b] + n_ctx_add tokens, ascending by one): 16 / G rows share a
+// work item, their (row, head) pairs the MFMA columns, so each key and value
+// tile is read once for all of them; scores past a row's own length are
+// masked.  For G not dividing 16 it is launch_attn_decode.
+hipError_t launch_attn_prefill(const qkdec_kv_layer& kv, const int32_t* slot, const int32_t* n_ctx, int B,
+                               const uint16_t* Q, int n_q_heads, float scale, uint16_t* O16, float* partials,
+                               int n_ctx_add, hipStream_t st);
 
 // ---- KV append and RoPE (kv_append.hip)
 // RoPE of q and k, q -> fp16 and the KV append, from the fp32 QKV rows Y

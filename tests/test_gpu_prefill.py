@@ -35,14 +35,9 @@ def _prefill(qd, model, caches, slot, start, prompt):
     return logits.cpu().numpy(), int(tok.item()), kv, (sm, w, embed, lm_head, norm, layers)
 
 
-@pytest.mark.parametrize("kind", ["f16", "q8_0"])
-@pytest.mark.parametrize("n", [1, 16, 40, 64, 100])
-def test_prefill_toy_matches_oracle(qd, kind, n):
-    # the toy decoder, a prompt of n tokens (one, part of a 64-row chunk, one
-    # full chunk, and 64 + 36) appended after 20 cached tokens of slot 1 of 3
-    dims = synth.TOY
-    model = synth.make_model(dims, 1700)
-    st = synth.Streams(1701)
+def _toy_case(qd, dims, kind, n, seed):
+    model = synth.make_model(dims, seed)
+    st = synth.Streams(seed + 1)
     caches = [synth.kv_cache(kind, st.next(), st.next(), 3, dims.n_kv_heads, 128, dims.head_dim, [30, 20, 50])
               for _ in model.layers]
     prompt = synth.tokens(st.next(), n, dims.vocab)
@@ -63,6 +58,30 @@ def test_prefill_toy_matches_oracle(qd, kind, n):
             assert np.array_equal(g[[0, 2]].view(np.uint8), arr[[0, 2]].view(np.uint8)), (li, name)
             assert np.array_equal(g[1, :, :20].view(np.uint8), arr[1, :, :20].view(np.uint8)), (li, name)
             assert not g[1, :, 20 + n:].view(np.uint8).any(), (li, name)
+
+
+@pytest.mark.parametrize("kind", ["f16", "q8_0"])
+@pytest.mark.parametrize("n", [1, 16, 40, 64, 100])
+def test_prefill_toy_matches_oracle(qd, kind, n):
+    # the toy decoder, a prompt of n tokens (one, part of a 64-row chunk, one
+    # full chunk, and 64 + 36) appended after 20 cached tokens of slot 1 of 3
+    _toy_case(qd, synth.TOY, kind, n, 1700)
+
+
+@pytest.mark.parametrize("kind", ["fp8", "q8k_f16v", "f16k_q8v"])
+def test_prefill_toy_other_caches(qd, kind):
+    # the remaining cache formats, 64 + 6 prompt tokens
+    _toy_case(qd, synth.TOY, kind, 70, 1720)
+
+
+@pytest.mark.parametrize("heads,kind", [((4, 2), "f16"), ((8, 1), "q8_0"), ((16, 1), "f16"), ((12, 4), "f16")])
+def test_prefill_group_sizes(qd, heads, kind):
+    # query heads per KV head G = 2, 8, 16 and 3: the attention takes 16 / G
+    # prompt rows per work item when G divides 16 (G = 16, and G = 3, one row)
+    hq, hkv = heads
+    dims = synth.ModelDims(n_layers=2, hidden=512, n_q_heads=hq, n_kv_heads=hkv, head_dim=64, ffn=1536,
+                           vocab=4096)
+    _toy_case(qd, dims, kind, 70, 1740)
 
 
 def test_prefill_full_width_equals_decode_steps(qd):
