@@ -460,12 +460,12 @@ def prefill_point(qd, sd, dims, dev_model, n_prompt, seed, kind="f16"):
         if i:
             times.append(a.elapsed_time(b))
     ms = sorted(times)[1]
-    wbytes = W_BYTES * ((n_prompt + 63) // 64)
+    wbytes = W_BYTES * ((n_prompt + 255) // 256)
     del kvs, keep
     return {"prompt_tokens": n_prompt, "kv": kind, "ms": ms, "tok_per_s": n_prompt / (ms * 1e-3),
-            "weight_bytes_read": wbytes, "note": "chunks of 64 prompt tokens, each one pass of the layers: 64-row "
-                                                  "MFMA projections over split K, the decode attention with the "
-                                                  "tokens as rows; LM head for the last token"}
+            "weight_bytes_read": wbytes, "note": "chunks of 256 prompt tokens, each one pass of the layers: MFMA "
+                                                  "projections in 64-row tiles over split K, the split-K attention "
+                                                  "with 4 prompt rows per work item; LM head for the last token"}
 
 
 def record_traffic(qd, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mb, batch, context, kv, command):

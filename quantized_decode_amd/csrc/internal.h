@@ -228,12 +228,13 @@ hipError_t launch_prefill_rows(int s, int start, const int32_t* tokens, int rows
 // comes with its 32-value sub-block sums xs [T][K/256][4] (half4) and the
 // factors fdm [T][K/256] (float2) of each row super-block (pf_norm, or
 // pf_finish for the SwiGLU output).
-constexpr int kPfRows = 64;
+constexpr int kPfChunk = 256;         // prompt rows per pass of the layers
+constexpr int kPfRows = 64;           // prompt rows per GEMM work-group
 constexpr int kPfTilesPerWave = 2;    // weight tiles of 16 rows per wave: 128 rows per work-group
-constexpr int kPfTargetGroups = 256;  // work-groups per projection launch aimed at (one per CU)
-// K ranges (1 .. K / 256) of a projection with n_rows weight rows
-int pf_ksplit(int64_t n_rows, int64_t K);
-// n_rows % 128 == 0, K % 256 == 0, 1 <= T <= kPfRows
+constexpr int kPfTargetGroups = 256;  // work-groups per projection launch aimed at
+// K ranges (1 .. K / 256) of a projection with n_rows weight rows over T prompt rows
+int pf_ksplit(int64_t n_rows, int64_t K, int T);
+// n_rows % 128 == 0, K % 256 == 0, 1 <= T <= kPfChunk
 hipError_t launch_gemm_pf(const void* W, int64_t n_rows, int64_t K, const uint16_t* X, int64_t ldx, const void* xs,
                           const void* fdm, int T, float* part, int ksplit, hipStream_t st);
 enum PfFinishMode {

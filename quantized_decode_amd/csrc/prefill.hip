@@ -64,6 +64,9 @@ __global__ void __launch_bounds__(256, 2) gemm_pf_kernel(const PfGemmArgs a) {
   const int ks = blockIdx.y;
   const int b0 = (int)((int64_t)ks * a.kb / a.ksplit), b1 = (int)((int64_t)(ks + 1) * a.kb / a.ksplit);
   const int tile0 = (blockIdx.x * 4 + wave) * NTW;
+  // rows row0 .. row0 + rows - 1 of the a.T rows
+  const int row0 = kPfRows * blockIdx.z;
+  const int rows = min(kPfRows, a.T - row0);
 
   // ---- activation staging.  The tile goes from global memory straight to LDS:
   // wave w moves rows 16 w .. 16 w + 15, two rows (1 KB) per instruction, lane
@@ -80,15 +83,15 @@ __global__ void __launch_bounds__(256, 2) gemm_pf_kernel(const PfGemmArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int q = wave * 8 + i, row = 2 * q + (ln >> 5), slot = ln & 31;
-      const int srow = row < a.T ? row : a.T - 1;
+      const int srow = row0 + (row < rows ? row : rows - 1);
       const half_t* src = a.X + (size_t)srow * a.ldx + (size_t)sb * 256 + (size_t)((slot ^ (row & 15)) * 8);
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&dst[q * 512], 16, 0, 0);
     }
     const int srow = tx >> 2;
     xsr = half4_t{0, 0, 0, 0};
-    if (srow < a.T) xsr = a.xs[((size_t)srow * a.kb + sb) * 4 + (tx & 3)];
+    if (srow < rows) xsr = a.xs[((size_t)(row0 + srow) * a.kb + sb) * 4 + (tx & 3)];
     fr2 = make_float2(1.f, 1.f);
-    if (tx < a.T) fr2 = a.fdm[(size_t)tx * a.kb + sb];
+    if (tx < rows) fr2 = a.fdm[(size_t)(row0 + tx) * a.kb + sb];
   };
   auto store_x = [&](int buf) {
     s_xs[buf][tx >> 2][tx & 3] = xsr;
@@ -189,7 +192,7 @@ __global__ void __launch_bounds__(256, 2) gemm_pf_kernel(const PfGemmArgs a) {
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int t = mt * 16 + 4 * g + ii;
-        if (t < a.T) dst[(size_t)t * a.N + n] = acc[tt][mt][ii];
+        if (t < rows) dst[(size_t)(row0 + t) * a.N + n] = acc[tt][mt][ii];
       }
   }
 }
@@ -310,8 +313,8 @@ __global__ void __launch_bounds__(256) pf_norm_kernel(const float* __restrict__ 
   pf_block_sums(hv, 1.f, nb, t, c, xs, fdm);
 }
 
-int pf_ksplit(int64_t n_rows, int64_t K) {
-  const int64_t groups = n_rows / (16 * 4 * kPfTilesPerWave);
+int pf_ksplit(int64_t n_rows, int64_t K, int T) {
+  const int64_t groups = n_rows / (16 * 4 * kPfTilesPerWave) * ((T + kPfRows - 1) / kPfRows);
   const int kb = (int)(K / 256);
   int64_t s = (kPfTargetGroups + groups - 1) / groups;
   if (s > kb) s = kb;
@@ -320,7 +323,7 @@ int pf_ksplit(int64_t n_rows, int64_t K) {
 
 hipError_t launch_gemm_pf(const void* W, int64_t n_rows, int64_t K, const uint16_t* X, int64_t ldx, const void* xs,
                           const void* fdm, int T, float* part, int ksplit, hipStream_t st) {
-  if (n_rows % (64 * kPfTilesPerWave) != 0 || K % 256 != 0 || T < 1 || T > kPfRows || ksplit < 1 ||
+  if (n_rows % (64 * kPfTilesPerWave) != 0 || K % 256 != 0 || T < 1 || T > kPfChunk || ksplit < 1 ||
       ksplit > K / 256)
     return hipErrorInvalidValue;
   PfGemmArgs a{};
@@ -334,14 +337,14 @@ hipError_t launch_gemm_pf(const void* W, int64_t n_rows, int64_t K, const uint16
   a.T = T;
   a.N = (int)n_rows;
   a.ksplit = ksplit;
-  const dim3 grid((unsigned)(n_rows / (64 * kPfTilesPerWave)), (unsigned)ksplit);
+  const dim3 grid((unsigned)(n_rows / (64 * kPfTilesPerWave)), (unsigned)ksplit, (unsigned)((T + kPfRows - 1) / kPfRows));
   hipLaunchKernelGGL(gemm_pf_kernel<kPfTilesPerWave>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_pf_finish(const float* part, int ksplit, int T, int N, const float* res, float* out, int64_t ldo,
                             int mode, float* ssq, uint16_t* h, void* xs, void* fdm, hipStream_t st) {
-  if (T < 1 || T > kPfRows || N < 1 || ksplit < 0 || (mode == kPfNorm && N % 256 != 0) ||
+  if (T < 1 || T > kPfChunk || N < 1 || ksplit < 0 || (mode == kPfNorm && N % 256 != 0) ||
       (mode == kPfSwiglu && N % 512 != 0))
     return hipErrorInvalidValue;
   PfFinishArgs a{};
@@ -364,7 +367,7 @@ hipError_t launch_pf_finish(const float* part, int ksplit, int T, int N, const f
 
 hipError_t launch_pf_norm(const float* x, const float* ssq, const float* gamma, float eps, int K, int T, uint16_t* h,
                           void* xs, void* fdm, hipStream_t st) {
-  if (T < 1 || T > kPfRows || K < 256 || K % 256 != 0) return hipErrorInvalidValue;
+  if (T < 1 || T > kPfChunk || K < 256 || K % 256 != 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(pf_norm_kernel, dim3(K / 256, T), dim3(256), 0, st, x, ssq, gamma, eps, K,
                      reinterpret_cast<half_t*>(h), reinterpret_cast<half4_t*>(xs), reinterpret_cast<float2*>(fdm));
   return hipGetLastError();

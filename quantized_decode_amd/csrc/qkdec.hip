@@ -242,22 +242,23 @@ qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int3
   return QKDEC_OK;
 }
 
-// ---- prefill: the prompt in chunks of up to kPfRows tokens of the one
+// ---- prefill: the prompt in chunks of up to kPfChunk tokens of the one
 // sequence (consecutive positions), each chunk one pass of the layers with its
-// tokens as the rows: every projection a 64-row MFMA GEMM over split K
+// tokens as the rows: every projection a 64-row-tile MFMA GEMM over split K
 // (gemm_pf) and the finish that adds the K ranges and stages the next input
-// (pf_finish); RoPE, the KV append and the attention are the decode kernels.
+// (pf_finish, pf_norm); RoPE, the KV append and the attention (64 rows per
+// call) are the decode kernels.
 struct PrefillWs {
   int32_t* err;
-  float* x;        // residual stream [kPfRows][H]
+  float* x;        // residual stream [kPfChunk][H]
   float* ss;       // sum-of-squares slots the embedding writes (unused here)
-  uint16_t* h;     // fp16 input of the next projection [kPfRows][max(H, F)]
-  void* xs;        // its sub-block sums [kPfRows][max(H, F, Hq D) / 256][4] (half4)
-  void* fdm;       // and factors [kPfRows][max(H, F, Hq D) / 256] (float2)
-  float* ssq;      // block sums of squares of the residual stream [kPfRows][H / 256]
-  float* qkv;      // [kPfRows][nqkv]
-  uint16_t* q16;   // [kPfRows][Hq D]
-  uint16_t* o16;   // [kPfRows][Hq D]
+  uint16_t* h;     // fp16 input of the next projection [kPfChunk][max(H, F)]
+  void* xs;        // its sub-block sums [kPfChunk][max(H, F, Hq D) / 256][4] (half4)
+  void* fdm;       // and factors [kPfChunk][max(H, F, Hq D) / 256] (float2)
+  float* ssq;      // block sums of squares of the residual stream [kPfChunk][H / 256]
+  float* qkv;      // [kPfChunk][nqkv]
+  uint16_t* q16;   // [kPfChunk][Hq D]
+  uint16_t* o16;   // [kPfChunk][Hq D]
   float* part;     // K-range partial sums of the widest projection
   float* attn_part;
   float2* rope;
@@ -274,12 +275,12 @@ PrefillWs prefill_layout(const qkdec_model* m, const qkdec_kv_layer* kv, char* b
     off += round_up(n, 256);
     return p;
   };
-  const int64_t R = kPfRows, H = m->hidden, F = m->ffn;
+  const int64_t R = kPfChunk, H = m->hidden, F = m->ffn;
   const int64_t hq = (int64_t)m->n_q_heads * m->head_dim;
   const int64_t nqkv = (int64_t)(m->n_q_heads + 2 * m->n_kv_heads) * m->head_dim;
   w.err = reinterpret_cast<int32_t*>(take(256));
   w.x = reinterpret_cast<float*>(take((size_t)(R * H) * 4));
-  // the embedding kernel writes slot (c / 16) * 16 + row for column c: at most H + 48 floats for 64 rows
+  // the embedding kernel writes slot (c / 16) * 16 + row for column c: at most H + R floats
   w.ss = reinterpret_cast<float*>(take((size_t)(H + R) * 4));
   w.h = reinterpret_cast<uint16_t*>(take((size_t)(R * std::max(H, F)) * 2));
   const int64_t kbmax = std::max(std::max(H, F), hq) / 256;
@@ -289,9 +290,12 @@ PrefillWs prefill_layout(const qkdec_model* m, const qkdec_kv_layer* kv, char* b
   w.qkv = reinterpret_cast<float*>(take((size_t)(R * nqkv) * 4));
   w.q16 = reinterpret_cast<uint16_t*>(take((size_t)(R * hq) * 2));
   w.o16 = reinterpret_cast<uint16_t*>(take((size_t)(R * hq) * 2));
+  // the partial sums of any chunk length (the K split grows as the rows shrink)
   size_t pb = 0;
   const int64_t shapes[4][2] = {{nqkv, H}, {H, hq}, {2 * F, H}, {H, F}};
-  for (const auto& nk : shapes) pb = std::max(pb, (size_t)pf_ksplit(nk[0], nk[1]) * (size_t)(R * nk[0]) * 4);
+  for (const auto& nk : shapes)
+    for (int t = kPfRows; t <= kPfChunk; t += kPfRows)
+      pb = std::max(pb, (size_t)pf_ksplit(nk[0], nk[1], t) * (size_t)(t * nk[0]) * 4);
   w.part = reinterpret_cast<float*>(take(pb));
   w.attn_part = reinterpret_cast<float*>(
       take(attn_partials_bytes(kPfRows, m->n_q_heads, m->head_dim, kv[0].capacity, kv[0].n_kv_heads)));
@@ -313,16 +317,16 @@ qkdec_status run_prefill(const qkdec_model* m, const qkdec_kv_layer* kv, int slo
   const int64_t hq = (int64_t)Hq * D;
   const int nqkv = (Hq + 2 * m->n_kv_heads) * D;
   const float scale = 1.0f / sqrtf((float)D);
-  const int ks_qkv = pf_ksplit(nqkv, H), ks_o = pf_ksplit(H, hq), ks_gu = pf_ksplit(2 * (int64_t)F, H),
-            ks_dn = pf_ksplit(H, F);
 #define QK_TRY(expr)                                 \
   do {                                               \
     const hipError_t e_ = (expr);                    \
     if (e_ != hipSuccess) return QKDEC_E_HIP;        \
   } while (0)
   int rows = 0;
-  for (int off = 0; off < n; off += kPfRows) {
-    rows = n - off < kPfRows ? n - off : kPfRows;
+  for (int off = 0; off < n; off += kPfChunk) {
+    rows = n - off < kPfChunk ? n - off : kPfChunk;
+    const int ks_qkv = pf_ksplit(nqkv, H, rows), ks_o = pf_ksplit(H, hq, rows),
+              ks_gu = pf_ksplit(2 * (int64_t)F, H, rows), ks_dn = pf_ksplit(H, F, rows);
     QK_TRY(launch_prefill_rows(slot, start + off, tokens + off, rows, w.rs, w.rp, w.rt, st));
     QK_TRY(launch_rope_table(w.rp, rows, D, m->rope_base, w.rope, st));
     QK_TRY(launch_embed(m->embed, H, m->vocab, w.rt, rows, w.x, w.ss, st));
@@ -336,7 +340,9 @@ qkdec_status run_prefill(const qkdec_model* m, const qkdec_kv_layer* kv, int slo
                               nullptr, st));
       QK_TRY(launch_rope_append(kv[l], w.qkv, nqkv, Hq, rows, w.rs, w.rp, m->rope_base, w.q16, w.err, st, w.rp,
                                 w.rope));
-      QK_TRY(launch_attn_prefill(kv[l], w.rs, w.rp, rows, w.q16, Hq, scale, w.o16, w.attn_part, 1, st));
+      for (int r0 = 0; r0 < rows; r0 += kPfRows)
+        QK_TRY(launch_attn_prefill(kv[l], w.rs + r0, w.rp + r0, std::min(kPfRows, rows - r0),
+                                   w.q16 + (size_t)r0 * hq, Hq, scale, w.o16 + (size_t)r0 * hq, w.attn_part, 1, st));
       QK_TRY(launch_pf_norm(nullptr, nullptr, nullptr, 0.f, (int)hq, rows, w.o16, w.xs, w.fdm, st));
       QK_TRY(launch_gemm_pf(ly.w_o, H, hq, w.o16, hq, w.xs, w.fdm, rows, w.part, ks_o, st));
       QK_TRY(launch_pf_finish(w.part, ks_o, rows, H, w.x, w.x, H, kPfNorm, w.ssq, nullptr, nullptr, nullptr, st));

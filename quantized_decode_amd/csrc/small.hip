@@ -194,7 +194,7 @@ hipError_t launch_lm_head_argmax(const uint16_t* Wlm, int64_t V, int64_t H, cons
 
 __global__ void prefill_rows_kernel(int s, int start, const int32_t* tokens, int rows, int32_t* slot, int32_t* pos,
                                     int32_t* tok) {
-  const int b = threadIdx.x;
+  const int b = blockIdx.x * 256 + threadIdx.x;
   if (b >= rows) return;
   slot[b] = s;
   pos[b] = start + b;
@@ -203,7 +203,8 @@ __global__ void prefill_rows_kernel(int s, int start, const int32_t* tokens, int
 
 hipError_t launch_prefill_rows(int s, int start, const int32_t* tokens, int rows, int32_t* slot, int32_t* pos,
                                int32_t* tok, hipStream_t st) {
-  hipLaunchKernelGGL(prefill_rows_kernel, dim3(1), dim3(64), 0, st, s, start, tokens, rows, slot, pos, tok);
+  hipLaunchKernelGGL(prefill_rows_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, s, start, tokens, rows, slot, pos,
+                     tok);
   return hipGetLastError();
 }
 

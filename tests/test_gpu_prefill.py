@@ -38,7 +38,7 @@ def _prefill(qd, model, caches, slot, start, prompt):
 def _toy_case(qd, dims, kind, n, seed):
     model = synth.make_model(dims, seed)
     st = synth.Streams(seed + 1)
-    caches = [synth.kv_cache(kind, st.next(), st.next(), 3, dims.n_kv_heads, 128, dims.head_dim, [30, 20, 50])
+    caches = [synth.kv_cache(kind, st.next(), st.next(), 3, dims.n_kv_heads, 352, dims.head_dim, [30, 20, 50])
               for _ in model.layers]
     prompt = synth.tokens(st.next(), n, dims.vocab)
     lg, tok, kv, _ = _prefill(qd, model, caches, 1, 20, prompt)
@@ -61,10 +61,11 @@ def _toy_case(qd, dims, kind, n, seed):
 
 
 @pytest.mark.parametrize("kind", ["f16", "q8_0"])
-@pytest.mark.parametrize("n", [1, 16, 40, 64, 100])
+@pytest.mark.parametrize("n", [1, 16, 40, 64, 100, 300])
 def test_prefill_toy_matches_oracle(qd, kind, n):
-    # the toy decoder, a prompt of n tokens (one, part of a 64-row chunk, one
-    # full chunk, and 64 + 36) appended after 20 cached tokens of slot 1 of 3
+    # the toy decoder, a prompt of n tokens appended after 20 cached tokens of
+    # slot 1 of 3: one token, part of a 64-row tile, one tile, 64 + 36 rows,
+    # and a full pass of 256 rows followed by 44
     _toy_case(qd, synth.TOY, kind, n, 1700)
 
 
@@ -86,9 +87,9 @@ def test_prefill_group_sizes(qd, heads, kind):
 
 def test_prefill_full_width_equals_decode_steps(qd):
     # a two-layer decoder of the full width (every projection on the kernels
-    # the bench times), 70 prompt tokens after 300 cached ones (a full chunk
-    # of 64 rows and a ragged one of 6): the prefill's
-    # first generated token and logits against 70 single-token decode steps
+    # the bench times), 270 prompt tokens after 300 cached ones (a pass of
+    # 256 rows and a ragged one of 14): the prefill's
+    # first generated token and logits against 270 single-token decode steps
     # on the GPU, and the appended keys and values of the two paths agree
     import torch
     from quantized_decode_amd.tensors import dev, upload_cache
@@ -96,9 +97,9 @@ def test_prefill_full_width_equals_decode_steps(qd):
                            vocab=16384)
     model = synth.make_model(dims, 1710)
     st = synth.Streams(1711)
-    caches = [synth.kv_cache("f16", st.next(), st.next(), 1, dims.n_kv_heads, 384, dims.head_dim, [300])
+    caches = [synth.kv_cache("f16", st.next(), st.next(), 1, dims.n_kv_heads, 576, dims.head_dim, [300])
               for _ in model.layers]
-    prompt = synth.tokens(st.next(), 70, dims.vocab)
+    prompt = synth.tokens(st.next(), 270, dims.vocab)
     lg, tok, kv, (sm, w, embed, lm_head, norm, layers) = _prefill(qd, model, caches, 0, 300, prompt)
     kv2 = [upload_cache(c) for c in caches]
     sm2 = qd.StepModel(dims, embed, lm_head, norm, layers, [k.desc for k in kv2])
@@ -120,5 +121,5 @@ def test_prefill_full_width_equals_decode_steps(qd):
         ka, va = a.logical_f16()
         kb, vb = b.logical_f16()
         for x, y in ((ka, kb), (va, vb)):
-            x64, y64 = x[0, :, 300:370].astype(np.float64), y[0, :, 300:370].astype(np.float64)
+            x64, y64 = x[0, :, 300:570].astype(np.float64), y[0, :, 300:570].astype(np.float64)
             assert np.abs(x64 - y64).max() <= 1e-3 * np.abs(y64).max()
