@@ -297,13 +297,37 @@ hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, con
   return hipGetLastError();
 }
 
+// rows per work item of the prompt-row attention (1: the decode kernel)
+static int attn_prefill_tok(int n_q_heads, int n_kv) {
+  const int G = n_q_heads / n_kv;
+  return (16 % G != 0 || G == 16) ? 1 : 16 / G;
+}
+
+int attn_prefill_splits(int B, int n_q_heads, const qkdec_kv_layer& kv) {
+  const int tok = attn_prefill_tok(n_q_heads, kv.n_kv_heads);
+  if (tok == 1) return attn_max_runs(kv.capacity, kv.n_kv_heads);
+  const int groups = (B + tok - 1) / tok;
+  const int by_len = (int)(((int64_t)kv.capacity + kAttnChunk - 1) / kAttnChunk);
+  const int wanted = attn_runs_wanted(groups, kv.n_kv_heads, kv_k_q8(kv.type) || kv_v_q8(kv.type));
+  return by_len > wanted ? by_len : wanted;
+}
+
+size_t attn_prefill_partials_bytes(int max_rows, int n_q_heads, const qkdec_kv_layer& kv) {
+  size_t most = 0;
+  for (int b = 1; b <= max_rows; ++b) {
+    const size_t rows = (size_t)b * n_q_heads * attn_prefill_splits(b, n_q_heads, kv);
+    if (rows > most) most = rows;
+  }
+  return most * (size_t)(kv.head_dim + 2) * sizeof(float);
+}
+
 hipError_t launch_attn_prefill(const qkdec_kv_layer& kv, const int32_t* slot, const int32_t* n_ctx, int B,
                                const uint16_t* Q, int n_q_heads, float scale, uint16_t* O16, float* partials,
                                int n_ctx_add, hipStream_t st) {
-  const int G = n_q_heads / kv.n_kv_heads;
-  if (16 % G != 0 || G == 16)
+  const int tok = attn_prefill_tok(n_q_heads, kv.n_kv_heads);
+  if (tok == 1)
     return launch_attn_decode(kv, slot, n_ctx, B, Q, n_q_heads, scale, nullptr, O16, partials, n_ctx_add, st);
-  const int tok = 16 / G, groups = (B + tok - 1) / tok;
+  const int groups = (B + tok - 1) / tok;
   AttnArgs a;
   a.k = reinterpret_cast<const uint8_t*>(kv.k);
   a.v = reinterpret_cast<const uint8_t*>(kv.v);
@@ -324,7 +348,7 @@ hipError_t launch_attn_prefill(const qkdec_kv_layer& kv, const int32_t* slot, co
   a.seq_cap = kv.capacity;
   a.tok = tok;
   a.nrows = B;
-  a.n_splits = attn_max_runs(a.seq_cap, kv.n_kv_heads);
+  a.n_splits = attn_prefill_splits(B, n_q_heads, kv);
   a.runs_wanted = attn_runs_wanted(groups, kv.n_kv_heads, kv_k_q8(kv.type) || kv_v_q8(kv.type));
   const int D = kv.head_dim;
   const size_t n_rows = (size_t)B * n_q_heads * a.n_splits;

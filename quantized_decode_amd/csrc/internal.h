@@ -180,6 +180,12 @@ hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, con
 // work item, their (row, head) pairs the MFMA columns, so each key and value
 // tile is read once for all of them; scores past a row's own length are
 // masked.  For G not dividing 16 it is launch_attn_decode.
+// Its partial-result rows per (row, head) for a call of B rows: enough runs
+// for the longest sequence (one per kAttnChunk tokens) and for the wanted
+// count, which falls as B grows.
+int attn_prefill_splits(int B, int n_q_heads, const qkdec_kv_layer& kv);
+// Partial-result bytes for any call of 1 .. max_rows rows.
+size_t attn_prefill_partials_bytes(int max_rows, int n_q_heads, const qkdec_kv_layer& kv);
 hipError_t launch_attn_prefill(const qkdec_kv_layer& kv, const int32_t* slot, const int32_t* n_ctx, int B,
                                const uint16_t* Q, int n_q_heads, float scale, uint16_t* O16, float* partials,
                                int n_ctx_add, hipStream_t st);
@@ -228,7 +234,8 @@ hipError_t launch_prefill_rows(int s, int start, const int32_t* tokens, int rows
 // comes with its 32-value sub-block sums xs [T][K/256][4] (half4) and the
 // factors fdm [T][K/256] (float2) of each row super-block (pf_norm, or
 // pf_finish for the SwiGLU output).
-constexpr int kPfChunk = 256;         // prompt rows per pass of the layers
+constexpr int kPfChunk = 1024;        // prompt rows per pass of the layers
+constexpr int kPfAttnRows = 256;      // prompt rows per attention call
 constexpr int kPfRows = 64;           // prompt rows per GEMM work-group
 constexpr int kPfTilesPerWave = 2;    // weight tiles of 16 rows per wave: 128 rows per work-group
 constexpr int kPfTargetGroups = 256;  // work-groups per projection launch aimed at

@@ -246,8 +246,8 @@ qkdec_status run_step(const qkdec_model* m, const qkdec_kv_layer* kv, const int3
 // sequence (consecutive positions), each chunk one pass of the layers with its
 // tokens as the rows: every projection a 64-row-tile MFMA GEMM over split K
 // (gemm_pf) and the finish that adds the K ranges and stages the next input
-// (pf_finish, pf_norm); RoPE, the KV append and the attention (64 rows per
-// call) are the decode kernels.
+// (pf_finish, pf_norm); RoPE, the KV append and the attention (kPfAttnRows
+// rows per call) are the decode kernels.
 struct PrefillWs {
   int32_t* err;
   float* x;        // residual stream [kPfChunk][H]
@@ -297,8 +297,7 @@ PrefillWs prefill_layout(const qkdec_model* m, const qkdec_kv_layer* kv, char* b
     for (int t = kPfRows; t <= kPfChunk; t += kPfRows)
       pb = std::max(pb, (size_t)pf_ksplit(nk[0], nk[1], t) * (size_t)(t * nk[0]) * 4);
   w.part = reinterpret_cast<float*>(take(pb));
-  w.attn_part = reinterpret_cast<float*>(
-      take(attn_partials_bytes(kPfRows, m->n_q_heads, m->head_dim, kv[0].capacity, kv[0].n_kv_heads)));
+  w.attn_part = reinterpret_cast<float*>(take(attn_prefill_partials_bytes(kPfAttnRows, m->n_q_heads, kv[0])));
   w.rope = reinterpret_cast<float2*>(take((size_t)R * (m->head_dim / 2) * sizeof(float2)));
   w.lm_part = take(lm_head_partials_bytes(m->vocab, 1));
   w.rs = reinterpret_cast<int32_t*>(take(R * 4));
@@ -340,8 +339,8 @@ qkdec_status run_prefill(const qkdec_model* m, const qkdec_kv_layer* kv, int slo
                               nullptr, st));
       QK_TRY(launch_rope_append(kv[l], w.qkv, nqkv, Hq, rows, w.rs, w.rp, m->rope_base, w.q16, w.err, st, w.rp,
                                 w.rope));
-      for (int r0 = 0; r0 < rows; r0 += kPfRows)
-        QK_TRY(launch_attn_prefill(kv[l], w.rs + r0, w.rp + r0, std::min(kPfRows, rows - r0),
+      for (int r0 = 0; r0 < rows; r0 += kPfAttnRows)
+        QK_TRY(launch_attn_prefill(kv[l], w.rs + r0, w.rp + r0, std::min(kPfAttnRows, rows - r0),
                                    w.q16 + (size_t)r0 * hq, Hq, scale, w.o16 + (size_t)r0 * hq, w.attn_part, 1, st));
       QK_TRY(launch_pf_norm(nullptr, nullptr, nullptr, 0.f, (int)hq, rows, w.o16, w.xs, w.fdm, st));
       QK_TRY(launch_gemm_pf(ly.w_o, H, hq, w.o16, hq, w.xs, w.fdm, rows, w.part, ks_o, st));

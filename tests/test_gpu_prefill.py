@@ -38,7 +38,8 @@ def _prefill(qd, model, caches, slot, start, prompt):
 def _toy_case(qd, dims, kind, n, seed):
     model = synth.make_model(dims, seed)
     st = synth.Streams(seed + 1)
-    caches = [synth.kv_cache(kind, st.next(), st.next(), 3, dims.n_kv_heads, 352, dims.head_dim, [30, 20, 50])
+    cap = (20 + n + 31) // 32 * 32 + 32
+    caches = [synth.kv_cache(kind, st.next(), st.next(), 3, dims.n_kv_heads, cap, dims.head_dim, [30, 20, 50])
               for _ in model.layers]
     prompt = synth.tokens(st.next(), n, dims.vocab)
     lg, tok, kv, _ = _prefill(qd, model, caches, 1, 20, prompt)
@@ -65,7 +66,7 @@ def _toy_case(qd, dims, kind, n, seed):
 def test_prefill_toy_matches_oracle(qd, kind, n):
     # the toy decoder, a prompt of n tokens appended after 20 cached tokens of
     # slot 1 of 3: one token, part of a 64-row tile, one tile, 64 + 36 rows,
-    # and a full pass of 256 rows followed by 44
+    # and 300 rows (attention calls of 256 + 44 rows)
     _toy_case(qd, synth.TOY, kind, n, 1700)
 
 
@@ -85,22 +86,19 @@ def test_prefill_group_sizes(qd, heads, kind):
     _toy_case(qd, dims, kind, 70, 1740)
 
 
-def test_prefill_full_width_equals_decode_steps(qd):
-    # a two-layer decoder of the full width (every projection on the kernels
-    # the bench times), 270 prompt tokens after 300 cached ones (a pass of
-    # 256 rows and a ragged one of 14): the prefill's
-    # first generated token and logits against 270 single-token decode steps
-    # on the GPU, and the appended keys and values of the two paths agree
+def _vs_decode_steps(qd, dims, kind, n_cached, n_prompt, seed):
+    # the prefill's first generated token and logits against n_prompt
+    # single-token decode steps on the GPU, and the appended keys and values of
+    # the two paths agree
     import torch
     from quantized_decode_amd.tensors import dev, upload_cache
-    dims = synth.ModelDims(n_layers=2, hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, ffn=12288,
-                           vocab=16384)
-    model = synth.make_model(dims, 1710)
-    st = synth.Streams(1711)
-    caches = [synth.kv_cache("f16", st.next(), st.next(), 1, dims.n_kv_heads, 576, dims.head_dim, [300])
+    model = synth.make_model(dims, seed)
+    st = synth.Streams(seed + 1)
+    cap = (n_cached + n_prompt + 31) // 32 * 32 + 32
+    caches = [synth.kv_cache(kind, st.next(), st.next(), 1, dims.n_kv_heads, cap, dims.head_dim, [n_cached])
               for _ in model.layers]
-    prompt = synth.tokens(st.next(), 270, dims.vocab)
-    lg, tok, kv, (sm, w, embed, lm_head, norm, layers) = _prefill(qd, model, caches, 0, 300, prompt)
+    prompt = synth.tokens(st.next(), n_prompt, dims.vocab)
+    lg, tok, kv, (sm, w, embed, lm_head, norm, layers) = _prefill(qd, model, caches, 0, n_cached, prompt)
     kv2 = [upload_cache(c) for c in caches]
     sm2 = qd.StepModel(dims, embed, lm_head, norm, layers, [k.desc for k in kv2])
     w2 = ws(qd.qkdec_step_workspace_size(sm2, 1))
@@ -108,7 +106,7 @@ def test_prefill_full_width_equals_decode_steps(qd):
     slot = dev(np.zeros(1, np.int32))
     logits = torch.empty((1, dims.vocab), dtype=torch.float32, device="cuda")
     for i, t in enumerate(prompt):
-        pos = dev(np.array([300 + i], np.int32))
+        pos = dev(np.array([n_cached + i], np.int32))
         tk = dev(np.array([t], np.int32))
         qd.qkdec_step(sm2, slot, pos, tk, 1, w2, logits=logits)
     sync()
@@ -117,9 +115,30 @@ def test_prefill_full_width_equals_decode_steps(qd):
     assert d <= LOGIT_ABS_TOL, f"prefill vs decode steps: max |dlogit| {d:.3e}"
     if top2_gap(ref) > 1e-3:
         assert tok == int(np.argmax(ref))
+    if kind != "f16":
+        return   # the appended codes are checked through the logits
+    end = n_cached + n_prompt
     for a, b in zip(kv, kv2):
         ka, va = a.logical_f16()
         kb, vb = b.logical_f16()
         for x, y in ((ka, kb), (va, vb)):
-            x64, y64 = x[0, :, 300:570].astype(np.float64), y[0, :, 300:570].astype(np.float64)
+            x64, y64 = x[0, :, n_cached:end].astype(np.float64), y[0, :, n_cached:end].astype(np.float64)
             assert np.abs(x64 - y64).max() <= 1e-3 * np.abs(y64).max()
+
+
+def test_prefill_full_width_equals_decode_steps(qd):
+    # a two-layer decoder of the full width (every projection on the kernels
+    # the bench times), 270 prompt tokens after 300 cached ones (attention
+    # calls of 256 and 14 rows)
+    dims = synth.ModelDims(n_layers=2, hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, ffn=12288,
+                           vocab=16384)
+    _vs_decode_steps(qd, dims, "f16", 300, 270, 1710)
+
+
+@pytest.mark.parametrize("kind", ["f16", "q8_0"])
+def test_prefill_two_passes_equals_decode_steps(qd, kind):
+    # the toy decoder, 1100 prompt tokens after 40 cached ones: a pass of 1024
+    # rows of the layers, then one of 76 (the oracle's prefill of this many
+    # tokens takes minutes; the decode step it is checked against is itself
+    # checked against the oracle)
+    _vs_decode_steps(qd, synth.TOY, kind, 40, 1100, 1770)
