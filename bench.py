@@ -433,7 +433,8 @@ def prefill_point(qd, sd, dims, dev_model, n_prompt, seed, kind="f16"):
     """Prompt ingestion (qkdec_prefill): n_prompt tokens into an empty slot of
     the Qwen-shaped model (all 36 layers, keys and values appended, the first
     generated token taken after the last prompt token); one warm-up call, then
-    the median of three calls timed with HIP events on the launching stream."""
+    the median of three calls timed with HIP events on the launching stream.
+    weight_bytes_read: the Q4_K weights once per pass of the layers."""
     import torch
     from quantized_decode_amd import KV_KINDS, kv_layer
     g = sd.generator(seed)
@@ -460,12 +461,13 @@ def prefill_point(qd, sd, dims, dev_model, n_prompt, seed, kind="f16"):
         if i:
             times.append(a.elapsed_time(b))
     ms = sorted(times)[1]
-    wbytes = W_BYTES * ((n_prompt + 255) // 256)
+    wbytes = W_BYTES * ((n_prompt + 1023) // 1024)
     del kvs, keep
     return {"prompt_tokens": n_prompt, "kv": kind, "ms": ms, "tok_per_s": n_prompt / (ms * 1e-3),
-            "weight_bytes_read": wbytes, "note": "chunks of 256 prompt tokens, each one pass of the layers: MFMA "
-                                                  "projections in 64-row tiles over split K, the split-K attention "
-                                                  "with 4 prompt rows per work item; LM head for the last token"}
+            "weight_bytes_read": wbytes, "note": "passes of up to 1024 prompt tokens through the layers: MFMA "
+                                                  "projections over 64-row tiles, the split-K attention with 4 "
+                                                  "prompt rows per work item (256 rows per call); LM head for the "
+                                                  "last token"}
 
 
 def record_traffic(qd, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mb, batch, context, kv, command):
@@ -689,6 +691,8 @@ def main():
                     help="only run 3 plain device copies of this many MiB (calibrates the HBM byte counters)")
     ap.add_argument("--no-passes", action="store_true",
                     help="skip the standalone GEMM-pass and attention-pass measurements")
+    ap.add_argument("--prefill-only", type=int, default=0, metavar="N",
+                    help="only time the prefill of an N-token prompt and print its JSON line")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write profiles/counted_traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of "
                          "this bench (--points main at --batch/--context/--kv) and of --copy-probe-mb; no GPU work")
@@ -726,6 +730,10 @@ def main():
     torch.cuda.synchronize()
     if args.sweep:
         sweep(args, qd, sd, dims, dev_model)
+        return
+    if args.prefill_only:
+        log(f"prefill of a {args.prefill_only}-token prompt")
+        print(json.dumps({"prefill": prefill_point(qd, sd, dims, dev_model, args.prefill_only, 9200)}))
         return
 
     points = [(args.batch, args.context, args.kv)]
