@@ -231,9 +231,9 @@ hipError_t launch_prefill_rows(int s, int start, const int32_t* tokens, int rows
 // ---- prompt ingestion (prefill.hip): chunks of up to kPfRows prompt tokens
 // of one sequence.  A projection is gemm_pf (partial sums of ksplit K ranges,
 // part[ks][T][n_rows]) and pf_finish (their sum); a projection's fp16 input
-// comes with its 32-value sub-block sums xs [T][K/256][4] (half4) and the
-// factors fdm [T][K/256] (float2) of each row super-block (pf_norm, or
-// pf_finish for the SwiGLU output).
+// comes with its 32-value sub-block sums / 32, xs [T][K/256][4] (half4), and
+// the power-of-two factor fd [T][K/256] of each row super-block (pf_norm: 1,
+// or pf_finish for the SwiGLU output).
 constexpr int kPfChunk = 1024;        // prompt rows per pass of the layers
 constexpr int kPfAttnRows = 256;      // prompt rows per attention call
 constexpr int kPfRows = 64;           // prompt rows per GEMM work-group
@@ -241,19 +241,20 @@ constexpr int kPfTilesPerWave = 2;    // weight tiles of 16 rows per wave: 128 r
 constexpr int kPfTargetGroups = 256;  // work-groups per projection launch aimed at
 // K ranges (1 .. K / 256) of a projection with n_rows weight rows over T prompt rows
 int pf_ksplit(int64_t n_rows, int64_t K, int T);
-// n_rows % 128 == 0, K % 256 == 0, 1 <= T <= kPfChunk
+// n_rows % 128 == 0, K % 256 == 0, 1 <= T <= kPfChunk; fd = null: every
+// factor is 1 (inputs staged by pf_norm)
 hipError_t launch_gemm_pf(const void* W, int64_t n_rows, int64_t K, const uint16_t* X, int64_t ldx, const void* xs,
-                          const void* fdm, int T, float* part, int ksplit, hipStream_t st);
+                          const float* fd, int T, float* part, int ksplit, hipStream_t st);
 enum PfFinishMode {
   kPfOut = 0,     // out = res + sum of the partials
   kPfNorm = 1,    // and ssq [T][N/256]: the sum of squares of each 256 values of out
-  kPfSwiglu = 2,  // h [T][N/2] = f16b(silu(gate) up) with its xs, fdm (gate: columns [0, N/2), up: [N/2, N))
+  kPfSwiglu = 2,  // h [T][N/2] = f16b(silu(gate) up) with its xs, fd (gate: columns [0, N/2), up: [N/2, N))
 };
 hipError_t launch_pf_finish(const float* part, int ksplit, int T, int N, const float* res, float* out, int64_t ldo,
-                            int mode, float* ssq, uint16_t* h, void* xs, void* fdm, hipStream_t st);
+                            int mode, float* ssq, uint16_t* h, void* xs, float* fd, hipStream_t st);
 // h [T][K] = f16(RMSNorm(x) gamma) from the block sums of squares ssq, with its
-// xs, fdm; x = null: only the sums of the fp16 rows already in h
+// xs, fd; x = null: only the sums of the fp16 rows already in h
 hipError_t launch_pf_norm(const float* x, const float* ssq, const float* gamma, float eps, int K, int T, uint16_t* h,
-                          void* xs, void* fdm, hipStream_t st);
+                          void* xs, float* fd, hipStream_t st);
 
 }  // namespace qk

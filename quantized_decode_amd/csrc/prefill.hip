@@ -23,10 +23,14 @@
 //                    row's block sums of squares, and its sub-block sums.
 //
 // The min term of Q4_K (dmin * m * sum x) uses the fp16 hi/lo split of each
-// 32-value sub-block sum, and a row super-block whose sums leave fp16's range
-// stages them divided by 32 -- the decode GEMM's rule (a_sums in q4k_dev.h),
-// formed here once per row and super-block by the kernel that writes the
-// activations.
+// 32-value sub-block sum, formed once per row and super-block by the kernel
+// that writes the activations.  The sums are always staged divided by 32 (a
+// power of two: any sum of 32 fp16 values then fits fp16), so the factor
+// that brings them back is 32 for every row and folds into -32 dmin once
+// per weight row and super-block; the decode GEMM divides only the row
+// super-blocks that need it (a_sums in q4k_dev.h).  A projection whose
+// input has a power-of-two factor per row and super-block (the SwiGLU
+// output, f16b) scales each product by it; the others (UNIT) do not.
 //
 // RoPE, the KV append and the attention are the decode kernels with the
 // chunk's tokens as rows (the append lands before any row attends; row i
@@ -43,13 +47,13 @@ struct PfGemmArgs {
   const uint8_t* W;      // Q4_K tiles [N/16][kb][16][144]
   const half_t* X;       // [T][ldx] fp16 activations
   int64_t ldx;
-  const half4_t* xs;     // [T][kb][4] sub-block sums of X (pf_block_sums)
-  const float2* fdm;     // [T][kb] (d factor, dmin factor) of each row super-block
+  const half4_t* xs;     // [T][kb][4] sub-block sums of X / 32 (pf_block_sums)
+  const float* fd;       // [T][kb] power-of-two factor of each row super-block of X (read unless UNIT)
   float* part;           // [ksplit][T][N] partial sums
   int kb, T, N, ksplit;
 };
 
-template <int NTW>
+template <int NTW, bool UNIT>
 __global__ void __launch_bounds__(256, 2) gemm_pf_kernel(const PfGemmArgs a) {
   // activation tile: row t's 16-byte chunk c at slot c ^ (t & 15) of the row
   // (512 bytes), so the 16 rows a read instruction touches hit 16 distinct slots
@@ -58,7 +62,7 @@ __global__ void __launch_bounds__(256, 2) gemm_pf_kernel(const PfGemmArgs a) {
   __shared__ __attribute__((aligned(16))) half_t s_x0[kPfRows * 256];
   __shared__ __attribute__((aligned(16))) half_t s_x1[kPfRows * 256];
   __shared__ half4_t s_xs[2][kPfRows][4];   // sub-block sums of lane group g: hi 2g, hi 2g+1, lo 2g, lo 2g+1
-  __shared__ float2 s_f[2][kPfRows];        // (d factor, dmin factor) of each row
+  __shared__ float s_f[2][kPfRows];         // factor of each row (not UNIT)
   const int tx = threadIdx.x, lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
   const int g = lane >> 4, r = lane & 15;
   const int ks = blockIdx.y;
@@ -72,9 +76,9 @@ __global__ void __launch_bounds__(256, 2) gemm_pf_kernel(const PfGemmArgs a) {
   // wave w moves rows 16 w .. 16 w + 15, two rows (1 KB) per instruction, lane
   // l filling slot l & 31 of row 2 q + (l >> 5) (rows past T repeat row T - 1,
   // whose products are never stored).  The sums of row tx >> 2, group tx & 3
-  // and (tx < 64) the factors of row tx pass through registers.
+  // and (tx < 64) the factor of row tx pass through registers.
   half4_t xsr;
-  float2 fr2;
+  float fr1 = 1.f;
   auto load_x = [&](int sb, half_t* dst) {
     // the addresses are formed anew at every call (kept out of registers
     // between super-blocks)
@@ -90,12 +94,15 @@ __global__ void __launch_bounds__(256, 2) gemm_pf_kernel(const PfGemmArgs a) {
     const int srow = tx >> 2;
     xsr = half4_t{0, 0, 0, 0};
     if (srow < rows) xsr = a.xs[((size_t)(row0 + srow) * a.kb + sb) * 4 + (tx & 3)];
-    fr2 = make_float2(1.f, 1.f);
-    if (tx < rows) fr2 = a.fdm[(size_t)(row0 + tx) * a.kb + sb];
+    if constexpr (!UNIT) {
+      fr1 = 1.f;
+      if (tx < rows) fr1 = a.fd[(size_t)(row0 + tx) * a.kb + sb];
+    }
   };
   auto store_x = [&](int buf) {
     s_xs[buf][tx >> 2][tx & 3] = xsr;
-    if (tx < kPfRows) s_f[buf][tx] = fr2;
+    if constexpr (!UNIT)
+      if (tx < kPfRows) s_f[buf][tx] = fr1;
   };
   // every wave's tile loads have landed in LDS before the barrier that
   // publishes them (vmcnt(0); expcnt and lgkmcnt left at their maxima)
@@ -137,7 +144,7 @@ __global__ void __launch_bounds__(256, 2) gemm_pf_kernel(const PfGemmArgs a) {
     for (int tt = 0; tt < NTW; ++tt) {
       const Q4Header h = q4_header(fr[tt], g);
       d[tt] = h.d;
-      dm[tt] = h.dmin;
+      dm[tt] = -32.f * h.dmin;   // the sums are staged divided by 32
       const half2_t mm = pack_h2(h.m0, h.m1);
       bm[tt][0] = mm[0]; bm[tt][1] = mm[1]; bm[tt][2] = mm[0]; bm[tt][3] = mm[1];
 #pragma unroll
@@ -150,13 +157,10 @@ __global__ void __launch_bounds__(256, 2) gemm_pf_kernel(const PfGemmArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) av[j] = *reinterpret_cast<const half8_t*>(xs + ((8 * g + j) ^ r) * 8);
       const half4_t axs = s_xs[BUF][mt * 16 + r][g];
-      float fd[4], fm[4];
+      float fd[4];
+      if constexpr (!UNIT)
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const float2 f = s_f[BUF][mt * 16 + 4 * g + ii];
-        fd[ii] = f.x;
-        fm[ii] = f.y;
-      }
+        for (int ii = 0; ii < 4; ++ii) fd[ii] = s_f[BUF][mt * 16 + 4 * g + ii];
       const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int tt = 0; tt < NTW; ++tt) {
@@ -164,11 +168,15 @@ __global__ void __launch_bounds__(256, 2) gemm_pf_kernel(const PfGemmArgs a) {
         floatx4 sq = zero;
 #pragma unroll
         for (int j = 0; j < 8; ++j) sq = mfma16x16x32(av[j], bq[tt][j], sq);
-        // d * fd and dmin * fm are exact (the factors are powers of two)
+        // d * fd and -32 dmin * fd are exact (the factors are powers of two)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          acc[tt][mt][ii] =
-              __builtin_fmaf(d[tt] * fd[ii], sq[ii], __builtin_fmaf(-dm[tt] * fm[ii], sm[ii], acc[tt][mt][ii]));
+        for (int ii = 0; ii < 4; ++ii) {
+          if constexpr (UNIT)
+            acc[tt][mt][ii] = __builtin_fmaf(d[tt], sq[ii], __builtin_fmaf(dm[tt], sm[ii], acc[tt][mt][ii]));
+          else
+            acc[tt][mt][ii] =
+                __builtin_fmaf(d[tt] * fd[ii], sq[ii], __builtin_fmaf(dm[tt] * fd[ii], sm[ii], acc[tt][mt][ii]));
+        }
       }
     }
     if (more) store_x(BUF ^ 1);
@@ -202,27 +210,21 @@ __global__ void __launch_bounds__(256, 2) gemm_pf_kernel(const PfGemmArgs a) {
 // blockIdx.y: thread tx owns column 256 c + tx.
 
 // The staged fp16 value v of thread tx (super-block c of row t): the 32-value
-// sub-block sums of the block (fp32 over the fp16 values) as the GEMM's min
-// term takes them, hi/lo fp16 pairs per lane group g (divided by 32 when one
-// of them leaves fp16's range, dmin's factor then 32 fd), and (fd, fm).
-__device__ void pf_block_sums(half_t v, float fd, int kb, int t, int c, half4_t* xs, float2* fdm) {
-  __shared__ float s_ms[4];
+// sub-block sums of the block (fp32 over the fp16 values) divided by 32, as
+// hi/lo fp16 pairs per lane group g, and the block's factor fd.
+__device__ void pf_block_sums(half_t v, float fd, int kb, int t, int c, half4_t* xs, float* fdv) {
   const int tx = threadIdx.x, lane = tx & 63, wave = tx >> 6;
   float s = (float)v;
 #pragma unroll
   for (int o = 1; o <= 16; o <<= 1) s += __shfl_xor(s, o);   // lanes 0-31: sub-block 2 wave, 32-63: 2 wave + 1
   const float s1 = __shfl_xor(s, 32);
-  if (lane == 0) s_ms[wave] = fmaxf(fabsf(s), fabsf(s1));
-  __syncthreads();
-  const float ms = fmaxf(fmaxf(s_ms[0], s_ms[1]), fmaxf(s_ms[2], s_ms[3]));
-  const bool big = ms > 65504.f;
   if (lane == 0) {
-    const float a0 = big ? s * 0.03125f : s, a1 = big ? s1 * 0.03125f : s1;
+    const float a0 = s * 0.03125f, a1 = s1 * 0.03125f;
     const half_t h0 = (half_t)a0, h1 = (half_t)a1;
     half4_t q;
     q[0] = h0; q[1] = h1; q[2] = (half_t)(a0 - (float)h0); q[3] = (half_t)(a1 - (float)h1);
     xs[((size_t)t * kb + c) * 4 + wave] = q;
-    if (wave == 0) fdm[(size_t)t * kb + c] = make_float2(fd, big ? 32.f * fd : fd);
+    if (wave == 0) fdv[(size_t)t * kb + c] = fd;
   }
 }
 
@@ -236,7 +238,7 @@ struct PfFinishArgs {
   float* ssq;            // kPfNorm: [T][N / 256] sum of squares of each block of out
   half_t* h;             // kPfSwiglu: [T][N / 2] fp16 input of the down projection
   half4_t* xs;           // and its sums and factors (pf_block_sums)
-  float2* fdm;
+  float* fd;
 };
 
 __global__ void __launch_bounds__(256) pf_finish_kernel(const PfFinishArgs a) {
@@ -272,7 +274,7 @@ __global__ void __launch_bounds__(256) pf_finish_kernel(const PfFinishArgs a) {
     const int sh = f16_block_shift(am);
     const half_t hv = (half_t)(v * exp2i(-sh));
     a.h[(size_t)t * F + k] = hv;
-    pf_block_sums(hv, exp2i(sh), F / 256, t, c, a.xs, a.fdm);
+    pf_block_sums(hv, exp2i(sh), F / 256, t, c, a.xs, a.fd);
     return;
   }
   if (k >= a.N) return;   // kPfOut only: kPfNorm widths are whole blocks
@@ -293,7 +295,7 @@ __global__ void __launch_bounds__(256) pf_finish_kernel(const PfFinishArgs a) {
 // h is already staged (the attention output), only the sums are formed.
 __global__ void __launch_bounds__(256) pf_norm_kernel(const float* __restrict__ x, const float* __restrict__ ssq,
                                                       const float* __restrict__ gamma, float eps, int K, half_t* h,
-                                                      half4_t* xs, float2* fdm) {
+                                                      half4_t* xs, float* fdv) {
   __shared__ float s_rinv;
   const int c = blockIdx.x, t = blockIdx.y, tx = threadIdx.x;
   const int k = c * 256 + tx, nb = K / 256;
@@ -310,7 +312,7 @@ __global__ void __launch_bounds__(256) pf_norm_kernel(const float* __restrict__ 
   } else {
     hv = h[(size_t)t * K + k];
   }
-  pf_block_sums(hv, 1.f, nb, t, c, xs, fdm);
+  pf_block_sums(hv, 1.f, nb, t, c, xs, fdv);
 }
 
 int pf_ksplit(int64_t n_rows, int64_t K, int T) {
@@ -322,7 +324,7 @@ int pf_ksplit(int64_t n_rows, int64_t K, int T) {
 }
 
 hipError_t launch_gemm_pf(const void* W, int64_t n_rows, int64_t K, const uint16_t* X, int64_t ldx, const void* xs,
-                          const void* fdm, int T, float* part, int ksplit, hipStream_t st) {
+                          const float* fd, int T, float* part, int ksplit, hipStream_t st) {
   if (n_rows % (64 * kPfTilesPerWave) != 0 || K % 256 != 0 || T < 1 || T > kPfChunk || ksplit < 1 ||
       ksplit > K / 256)
     return hipErrorInvalidValue;
@@ -331,19 +333,22 @@ hipError_t launch_gemm_pf(const void* W, int64_t n_rows, int64_t K, const uint16
   a.X = reinterpret_cast<const half_t*>(X);
   a.ldx = ldx;
   a.xs = reinterpret_cast<const half4_t*>(xs);
-  a.fdm = reinterpret_cast<const float2*>(fdm);
+  a.fd = fd;
   a.part = part;
   a.kb = (int)(K / 256);
   a.T = T;
   a.N = (int)n_rows;
   a.ksplit = ksplit;
   const dim3 grid((unsigned)(n_rows / (64 * kPfTilesPerWave)), (unsigned)ksplit, (unsigned)((T + kPfRows - 1) / kPfRows));
-  hipLaunchKernelGGL(gemm_pf_kernel<kPfTilesPerWave>, grid, dim3(256), 0, st, a);
+  if (fd)
+    hipLaunchKernelGGL((gemm_pf_kernel<kPfTilesPerWave, false>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((gemm_pf_kernel<kPfTilesPerWave, true>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_pf_finish(const float* part, int ksplit, int T, int N, const float* res, float* out, int64_t ldo,
-                            int mode, float* ssq, uint16_t* h, void* xs, void* fdm, hipStream_t st) {
+                            int mode, float* ssq, uint16_t* h, void* xs, float* fd, hipStream_t st) {
   if (T < 1 || T > kPfChunk || N < 1 || ksplit < 0 || (mode == kPfNorm && N % 256 != 0) ||
       (mode == kPfSwiglu && N % 512 != 0))
     return hipErrorInvalidValue;
@@ -359,17 +364,17 @@ hipError_t launch_pf_finish(const float* part, int ksplit, int T, int N, const f
   a.ssq = ssq;
   a.h = reinterpret_cast<half_t*>(h);
   a.xs = reinterpret_cast<half4_t*>(xs);
-  a.fdm = reinterpret_cast<float2*>(fdm);
+  a.fd = fd;
   const int blocks = mode == kPfSwiglu ? N / 512 : (N + 255) / 256;
   hipLaunchKernelGGL(pf_finish_kernel, dim3(blocks, T), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_pf_norm(const float* x, const float* ssq, const float* gamma, float eps, int K, int T, uint16_t* h,
-                          void* xs, void* fdm, hipStream_t st) {
+                          void* xs, float* fd, hipStream_t st) {
   if (T < 1 || T > kPfChunk || K < 256 || K % 256 != 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(pf_norm_kernel, dim3(K / 256, T), dim3(256), 0, st, x, ssq, gamma, eps, K,
-                     reinterpret_cast<half_t*>(h), reinterpret_cast<half4_t*>(xs), reinterpret_cast<float2*>(fdm));
+                     reinterpret_cast<half_t*>(h), reinterpret_cast<half4_t*>(xs), fd);
   return hipGetLastError();
 }
 

@@ -254,7 +254,7 @@ struct PrefillWs {
   float* ss;       // sum-of-squares slots the embedding writes (unused here)
   uint16_t* h;     // fp16 input of the next projection [kPfChunk][max(H, F)]
   void* xs;        // its sub-block sums [kPfChunk][max(H, F, Hq D) / 256][4] (half4)
-  void* fdm;       // and factors [kPfChunk][max(H, F, Hq D) / 256] (float2)
+  float* fd;       // and factors [kPfChunk][max(H, F, Hq D) / 256]
   float* ssq;      // block sums of squares of the residual stream [kPfChunk][H / 256]
   float* qkv;      // [kPfChunk][nqkv]
   uint16_t* q16;   // [kPfChunk][Hq D]
@@ -285,7 +285,7 @@ PrefillWs prefill_layout(const qkdec_model* m, const qkdec_kv_layer* kv, char* b
   w.h = reinterpret_cast<uint16_t*>(take((size_t)(R * std::max(H, F)) * 2));
   const int64_t kbmax = std::max(std::max(H, F), hq) / 256;
   w.xs = take((size_t)(R * kbmax) * 4 * 8);
-  w.fdm = take((size_t)(R * kbmax) * 8);
+  w.fd = reinterpret_cast<float*>(take((size_t)(R * kbmax) * 4));
   w.ssq = reinterpret_cast<float*>(take((size_t)(R * (H / 256)) * 4));
   w.qkv = reinterpret_cast<float*>(take((size_t)(R * nqkv) * 4));
   w.q16 = reinterpret_cast<uint16_t*>(take((size_t)(R * hq) * 2));
@@ -331,10 +331,10 @@ qkdec_status run_prefill(const qkdec_model* m, const qkdec_kv_layer* kv, int slo
     QK_TRY(launch_embed(m->embed, H, m->vocab, w.rt, rows, w.x, w.ss, st));
     // the first layer's input: RMSNorm of the embedding rows
     QK_TRY(launch_pf_finish(w.part, 0, rows, H, w.x, w.x, H, kPfNorm, w.ssq, nullptr, nullptr, nullptr, st));
-    QK_TRY(launch_pf_norm(w.x, w.ssq, m->layers[0].norm_attn, m->rms_eps, H, rows, w.h, w.xs, w.fdm, st));
+    QK_TRY(launch_pf_norm(w.x, w.ssq, m->layers[0].norm_attn, m->rms_eps, H, rows, w.h, w.xs, w.fd, st));
     for (int l = 0; l < m->n_layers; ++l) {
       const qkdec_layer& ly = m->layers[l];
-      QK_TRY(launch_gemm_pf(ly.w_qkv, nqkv, H, w.h, H, w.xs, w.fdm, rows, w.part, ks_qkv, st));
+      QK_TRY(launch_gemm_pf(ly.w_qkv, nqkv, H, w.h, H, w.xs, nullptr, rows, w.part, ks_qkv, st));
       QK_TRY(launch_pf_finish(w.part, ks_qkv, rows, nqkv, nullptr, w.qkv, nqkv, kPfOut, nullptr, nullptr, nullptr,
                               nullptr, st));
       QK_TRY(launch_rope_append(kv[l], w.qkv, nqkv, Hq, rows, w.rs, w.rp, m->rope_base, w.q16, w.err, st, w.rp,
@@ -342,18 +342,18 @@ qkdec_status run_prefill(const qkdec_model* m, const qkdec_kv_layer* kv, int slo
       for (int r0 = 0; r0 < rows; r0 += kPfAttnRows)
         QK_TRY(launch_attn_prefill(kv[l], w.rs + r0, w.rp + r0, std::min(kPfAttnRows, rows - r0),
                                    w.q16 + (size_t)r0 * hq, Hq, scale, w.o16 + (size_t)r0 * hq, w.attn_part, 1, st));
-      QK_TRY(launch_pf_norm(nullptr, nullptr, nullptr, 0.f, (int)hq, rows, w.o16, w.xs, w.fdm, st));
-      QK_TRY(launch_gemm_pf(ly.w_o, H, hq, w.o16, hq, w.xs, w.fdm, rows, w.part, ks_o, st));
+      QK_TRY(launch_pf_norm(nullptr, nullptr, nullptr, 0.f, (int)hq, rows, w.o16, w.xs, w.fd, st));
+      QK_TRY(launch_gemm_pf(ly.w_o, H, hq, w.o16, hq, w.xs, nullptr, rows, w.part, ks_o, st));
       QK_TRY(launch_pf_finish(w.part, ks_o, rows, H, w.x, w.x, H, kPfNorm, w.ssq, nullptr, nullptr, nullptr, st));
-      QK_TRY(launch_pf_norm(w.x, w.ssq, ly.norm_ffn, m->rms_eps, H, rows, w.h, w.xs, w.fdm, st));
-      QK_TRY(launch_gemm_pf(ly.w_gate_up, 2 * (int64_t)F, H, w.h, H, w.xs, w.fdm, rows, w.part, ks_gu, st));
-      QK_TRY(launch_pf_finish(w.part, ks_gu, rows, 2 * F, nullptr, nullptr, 0, kPfSwiglu, nullptr, w.h, w.xs, w.fdm,
+      QK_TRY(launch_pf_norm(w.x, w.ssq, ly.norm_ffn, m->rms_eps, H, rows, w.h, w.xs, w.fd, st));
+      QK_TRY(launch_gemm_pf(ly.w_gate_up, 2 * (int64_t)F, H, w.h, H, w.xs, nullptr, rows, w.part, ks_gu, st));
+      QK_TRY(launch_pf_finish(w.part, ks_gu, rows, 2 * F, nullptr, nullptr, 0, kPfSwiglu, nullptr, w.h, w.xs, w.fd,
                               st));
-      QK_TRY(launch_gemm_pf(ly.w_down, H, F, w.h, F, w.xs, w.fdm, rows, w.part, ks_dn, st));
+      QK_TRY(launch_gemm_pf(ly.w_down, H, F, w.h, F, w.xs, w.fd, rows, w.part, ks_dn, st));
       QK_TRY(launch_pf_finish(w.part, ks_dn, rows, H, w.x, w.x, H, kPfNorm, w.ssq, nullptr, nullptr, nullptr, st));
       // the next layer's attention input, or after the last layer the final norm
       const float* gamma = l + 1 < m->n_layers ? m->layers[l + 1].norm_attn : m->norm_final;
-      QK_TRY(launch_pf_norm(w.x, w.ssq, gamma, m->rms_eps, H, rows, w.h, w.xs, w.fdm, st));
+      QK_TRY(launch_pf_norm(w.x, w.ssq, gamma, m->rms_eps, H, rows, w.h, w.xs, w.fd, st));
     }
   }
   // the LM head of the prompt's last token (row rows - 1 of the last chunk)
