@@ -14,11 +14,11 @@
 //                    weight tiles of 16 rows exactly (sc*q, as in the decode
 //                    GEMM) and runs them against the four 16-row activation
 //                    tiles read from LDS.  Partial sums go to part[ks][t][n].
-//   pf_finish_kernel one work-group per (256 columns, prompt row): the K
-//                    ranges' partial sums added in order (+ the residual, and
-//                    each block's sum of squares), or the SwiGLU output
-//                    rounded per 256 values with a power-of-two offset (the
-//                    decode step's f16b staging) and its sub-block sums.
+//   pf_finish_kernel one wave per (256 columns, prompt row): the K ranges'
+//                    partial sums added in order (+ the residual, and each
+//                    block's sum of squares), or the SwiGLU output rounded
+//                    per 256 values with a power-of-two offset (the decode
+//                    step's f16b staging) and its sub-block sums.
 //   pf_norm_kernel   the same blocks: h = f16(x rinv gamma) with rinv from the
 //                    row's block sums of squares, and its sub-block sums.
 //
@@ -205,27 +205,30 @@ __global__ void __launch_bounds__(256, 2) gemm_pf_kernel(const PfGemmArgs a) {
   }
 }
 
-// ---- finish of a projection and staging of the next one's input, one
-// work-group (256 threads) per 256-column block c = blockIdx.x of row t =
-// blockIdx.y: thread tx owns column 256 c + tx.
+// ---- finish of a projection and staging of the next one's input: one
+// wave per 256-column block c of row t (lane l owns columns 256 c + 4 l ..
+// + 3), four blocks per work-group; no barriers.
+constexpr int kPfBlocksPerGroup = 4;
 
-// The staged fp16 value v of thread tx (super-block c of row t): the 32-value
-// sub-block sums of the block (fp32 over the fp16 values) divided by 32, as
-// hi/lo fp16 pairs per lane group g, and the block's factor fd.
-__device__ void pf_block_sums(half_t v, float fd, int kb, int t, int c, half4_t* xs, float* fdv) {
-  const int tx = threadIdx.x, lane = tx & 63, wave = tx >> 6;
-  float s = (float)v;
-#pragma unroll
-  for (int o = 1; o <= 16; o <<= 1) s += __shfl_xor(s, o);   // lanes 0-31: sub-block 2 wave, 32-63: 2 wave + 1
-  const float s1 = __shfl_xor(s, 32);
-  if (lane == 0) {
+// The staged fp16 values hv of this lane (super-block c of row t): the
+// 32-value sub-block sums of the block (fp32 over the fp16 values, 8 lanes
+// each) divided by 32, as hi/lo fp16 pairs per lane group g of the GEMM, and
+// the block's factor fd.
+__device__ void pf_block_sums(const half_t (&hv)[4], float fd, int kb, int t, int c, half4_t* xs, float* fdv,
+                              int lane) {
+  float s = (((float)hv[0] + (float)hv[1]) + (float)hv[2]) + (float)hv[3];
+  s += __shfl_xor(s, 1);
+  s += __shfl_xor(s, 2);
+  s += __shfl_xor(s, 4);                // lanes 8 j ..: sub-block j = lane >> 3
+  const float s1 = __shfl_xor(s, 8);    // at lane 16 g: sub-block 2 g + 1
+  if ((lane & 15) == 0) {
     const float a0 = s * 0.03125f, a1 = s1 * 0.03125f;
     const half_t h0 = (half_t)a0, h1 = (half_t)a1;
     half4_t q;
     q[0] = h0; q[1] = h1; q[2] = (half_t)(a0 - (float)h0); q[3] = (half_t)(a1 - (float)h1);
-    xs[((size_t)t * kb + c) * 4 + wave] = q;
-    if (wave == 0) fdv[(size_t)t * kb + c] = fd;
+    xs[((size_t)t * kb + c) * 4 + (lane >> 4)] = q;
   }
+  if (lane == 0) fdv[(size_t)t * kb + c] = fd;
 }
 
 struct PfFinishArgs {
@@ -242,77 +245,91 @@ struct PfFinishArgs {
 };
 
 __global__ void __launch_bounds__(256) pf_finish_kernel(const PfFinishArgs a) {
-  __shared__ float s_red[4];
-  const int c = blockIdx.x, t = blockIdx.y, tx = threadIdx.x, lane = tx & 63, wave = tx >> 6;
+  const int tx = threadIdx.x, lane = tx & 63, wave = tx >> 6;
+  const int c = blockIdx.x * kPfBlocksPerGroup + wave, t = blockIdx.y;
   const size_t plane = (size_t)a.T * a.N;
   const float* pr = a.part + (size_t)t * a.N;
   auto psum = [&](int k) {
-    float s = 0.f;
-    for (int q = 0; q < a.ksplit; ++q) s += pr[q * plane + k];
+    floatx4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < a.ksplit; ++q) s += *reinterpret_cast<const floatx4*>(pr + q * plane + k);
     return s;
   };
-  const int k = c * 256 + tx;
   if (a.mode == kPfSwiglu) {
     // gate in columns [0, F), up in [F, 2F); silu(gate) * up rounded to fp16
     // with the smallest power-of-two offset that keeps the block finite
     const int F = a.N / 2;
-    const float z = psum(k), u = psum(F + k);
-    float sil;
-    if (z >= 0.f) {
-      sil = z / (1.f + expf(-z));
-    } else {
-      const float ez = expf(z);
-      sil = z * ez / (1.f + ez);
+    if (c >= F / 256) return;
+    const int k = c * 256 + 4 * lane;
+    const floatx4 z = psum(k), u = psum(F + k);
+    float v[4], am = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float sil;
+      if (z[i] >= 0.f) {
+        sil = z[i] / (1.f + expf(-z[i]));
+      } else {
+        const float ez = expf(z[i]);
+        sil = z[i] * ez / (1.f + ez);
+      }
+      v[i] = sil * u[i];
+      am = fmaxf(am, fabsf(v[i]));
     }
-    const float v = sil * u;
-    float am = fabsf(v);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o));
-    if (lane == 0) s_red[wave] = am;
-    __syncthreads();
-    am = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
     const int sh = f16_block_shift(am);
-    const half_t hv = (half_t)(v * exp2i(-sh));
-    a.h[(size_t)t * F + k] = hv;
-    pf_block_sums(hv, exp2i(sh), F / 256, t, c, a.xs, a.fd);
+    const float inv = exp2i(-sh);
+    half_t hv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hv[i] = (half_t)(v[i] * inv);
+    half4_t h4;
+    h4[0] = hv[0]; h4[1] = hv[1]; h4[2] = hv[2]; h4[3] = hv[3];
+    *reinterpret_cast<half4_t*>(a.h + (size_t)t * F + k) = h4;
+    pf_block_sums(hv, exp2i(sh), F / 256, t, c, a.xs, a.fd, lane);
     return;
   }
-  if (k >= a.N) return;   // kPfOut only: kPfNorm widths are whole blocks
-  float y = psum(k);
-  if (a.res) y += a.res[(size_t)t * a.ldo + k];
-  a.out[(size_t)t * a.ldo + k] = y;
+  if (c >= (a.N + 255) / 256) return;
+  const int k = c * 256 + 4 * lane;
+  float q = 0.f;
+  if (k < a.N) {   // kPfOut only: kPfNorm widths are whole blocks
+    floatx4 y = psum(k);
+    if (a.res) y += *reinterpret_cast<const floatx4*>(a.res + (size_t)t * a.ldo + k);
+    *reinterpret_cast<floatx4*>(a.out + (size_t)t * a.ldo + k) = y;
+    q = ((y[0] * y[0] + y[1] * y[1]) + y[2] * y[2]) + y[3] * y[3];
+  }
   if (a.mode != kPfNorm) return;
-  float q = y * y;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) q += __shfl_xor(q, o);
-  if (lane == 0) s_red[wave] = q;
-  __syncthreads();
-  if (tx == 0) a.ssq[(size_t)t * (a.N / 256) + c] = ((s_red[0] + s_red[1]) + s_red[2]) + s_red[3];
+  if (lane == 0) a.ssq[(size_t)t * (a.N / 256) + c] = q;
 }
 
 // h = f16(x rinv gamma) for block c of row t, rinv from the row's block sums
-// of squares (added in block order); then its sub-block sums.  x = null:
-// h is already staged (the attention output), only the sums are formed.
+// of squares; then its sub-block sums.  x = null: h is already staged (the
+// attention output), only the sums are formed.
 __global__ void __launch_bounds__(256) pf_norm_kernel(const float* __restrict__ x, const float* __restrict__ ssq,
                                                       const float* __restrict__ gamma, float eps, int K, half_t* h,
                                                       half4_t* xs, float* fdv) {
-  __shared__ float s_rinv;
-  const int c = blockIdx.x, t = blockIdx.y, tx = threadIdx.x;
-  const int k = c * 256 + tx, nb = K / 256;
-  half_t hv;
+  const int tx = threadIdx.x, lane = tx & 63, wave = tx >> 6;
+  const int c = blockIdx.x * kPfBlocksPerGroup + wave, t = blockIdx.y, nb = K / 256;
+  if (c >= nb) return;
+  const int k = c * 256 + 4 * lane;
+  half_t hv[4];
   if (x) {
-    if (tx == 0) {
-      float tot = 0.f;
-      for (int b = 0; b < nb; ++b) tot += ssq[(size_t)t * nb + b];
-      s_rinv = 1.0f / sqrtf(tot * (1.0f / (float)K) + eps);
-    }
-    __syncthreads();
-    hv = norm_apply(x[(size_t)t * K + k], s_rinv, gamma[k]);
-    h[(size_t)t * K + k] = hv;
+    float tot = 0.f;
+    for (int b = lane; b < nb; b += 64) tot += ssq[(size_t)t * nb + b];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
+    const float rinv = 1.0f / sqrtf(tot * (1.0f / (float)K) + eps);
+    const floatx4 xv = *reinterpret_cast<const floatx4*>(x + (size_t)t * K + k);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hv[i] = norm_apply(xv[i], rinv, gamma[k + i]);
+    half4_t h4;
+    h4[0] = hv[0]; h4[1] = hv[1]; h4[2] = hv[2]; h4[3] = hv[3];
+    *reinterpret_cast<half4_t*>(h + (size_t)t * K + k) = h4;
   } else {
-    hv = h[(size_t)t * K + k];
+    const half4_t h4 = *reinterpret_cast<const half4_t*>(h + (size_t)t * K + k);
+    hv[0] = h4[0]; hv[1] = h4[1]; hv[2] = h4[2]; hv[3] = h4[3];
   }
-  pf_block_sums(hv, 1.f, nb, t, c, xs, fdv);
+  pf_block_sums(hv, 1.f, nb, t, c, xs, fdv, lane);
 }
 
 int pf_ksplit(int64_t n_rows, int64_t K, int T) {
@@ -366,14 +383,16 @@ hipError_t launch_pf_finish(const float* part, int ksplit, int T, int N, const f
   a.xs = reinterpret_cast<half4_t*>(xs);
   a.fd = fd;
   const int blocks = mode == kPfSwiglu ? N / 512 : (N + 255) / 256;
-  hipLaunchKernelGGL(pf_finish_kernel, dim3(blocks, T), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(pf_finish_kernel, dim3((blocks + kPfBlocksPerGroup - 1) / kPfBlocksPerGroup, T), dim3(256), 0,
+                     st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_pf_norm(const float* x, const float* ssq, const float* gamma, float eps, int K, int T, uint16_t* h,
                           void* xs, float* fd, hipStream_t st) {
   if (T < 1 || T > kPfChunk || K < 256 || K % 256 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(pf_norm_kernel, dim3(K / 256, T), dim3(256), 0, st, x, ssq, gamma, eps, K,
+  hipLaunchKernelGGL(pf_norm_kernel, dim3((K / 256 + kPfBlocksPerGroup - 1) / kPfBlocksPerGroup, T), dim3(256), 0,
+                     st, x, ssq, gamma, eps, K,
                      reinterpret_cast<half_t*>(h), reinterpret_cast<half4_t*>(xs), fd);
   return hipGetLastError();
 }
