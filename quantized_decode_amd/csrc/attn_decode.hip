@@ -38,6 +38,9 @@
 // 32-token tile's page comes from the sequence's row of the page table (the
 // run's entries staged in LDS at the start); everything else is the arena
 // kernel.
+#include <algorithm>
+#include <type_traits>
+
 #include "attn_dev.h"
 #include "common.h"
 #include "internal.h"
@@ -321,9 +324,178 @@ size_t attn_prefill_partials_bytes(int max_rows, int n_q_heads, const qkdec_kv_l
   return most * (size_t)(kv.head_dim + 2) * sizeof(float);
 }
 
+// ---- prompt rows over an fp16 cache: flash attention without a key split.
+// A work-group holds 64 query columns that share one KV head: H4 = min(G, 4)
+// heads of the group times 64 / H4 consecutive prompt rows; wave w takes head
+// w % H4 of 16 rows.  Each 32-token key and value tile is DMA'd to LDS once
+// for all four waves (double-buffered, 16-byte chunks XOR-swizzled so the
+// waves' fragment reads spread over the banks), and every wave runs the
+// decode kernel's tile step (attn_tile, per-column causal masks) over all
+// the keys its rows see, so the softmax state is final at the end: no
+// partial results and no merge.
+struct FlashArgs {
+  const half_t* k;       // cache of the layer: keys [slots][n_kv][cap][D]
+  const half_t* v;       // values [slots][n_kv][cap/32][D][32]
+  int n_kv, cap, n_slots;
+  const int32_t* slot;   // [rows] (one sequence: the first row's slot)
+  const int32_t* pos;    // [rows] ascending; row r attends over pos[r] + n_add tokens
+  int n_add, rows;
+  const half_t* Q;       // [rows][Hq][D]
+  int Hq, h4;
+  float scale_log2;
+  half_t* O16;           // [rows][Hq][D]
+};
+
+// slot of the 16-byte chunk c of key row t in the LDS key tile (D/8 chunks a row)
+template <int D>
+__device__ __forceinline__ int fk_slot(int t, int c) {
+  return (c ^ (((t >> 1) & 12) | (t & 3))) & (D / 8 - 1);
+}
+// slot of chunk c (4 a row of 32 tokens) of value row d in the LDS value tile
+__device__ __forceinline__ int fv_slot(int d, int c) { return c ^ ((d >> 2) & 3); }
+
+template <int D>
+__global__ void __launch_bounds__(256, 2) attn_prefill_kernel(const FlashArgs a) {
+  __shared__ __attribute__((aligned(16))) half_t s_k0[32 * D], s_k1[32 * D];
+  __shared__ __attribute__((aligned(16))) half_t s_v0[32 * D], s_v1[32 * D];
+  const int tx = threadIdx.x, lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
+  const int lg = lane >> 4, r = lane & 15;
+  const int g = blockIdx.y, G = a.Hq / a.n_kv, h4 = a.h4, tb = 64 / h4;
+  const int row_first = blockIdx.x * tb;
+  const int head = g * G + blockIdx.z * h4 + wave % h4;
+  const int row = row_first + (wave / h4) * 16 + r;   // this lane's column
+  const bool colv = row < a.rows;
+  const int last = min(row_first + tb - 1, a.rows - 1);
+  const int s = a.slot[row_first];
+  int n = a.pos[last] + a.n_add;
+  if (n > a.cap) n = a.cap;
+  if (s < 0 || s >= a.n_slots || n < 0) n = 0;
+  const int ncol = colv ? min(max(a.pos[row] + a.n_add, 0), n) : 0;
+  const size_t head_row0 = ((size_t)s * a.n_kv + g) * a.cap;
+  const half_t* kh = a.k + head_row0 * D;
+  const half_t* vh = a.v + head_row0 * D;
+
+  half8_t qf[D / 32];
+  {
+    const half_t* qrow = a.Q + ((size_t)(colv ? row : last) * a.Hq + head) * D;
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j)
+      qf[j] = colv ? *reinterpret_cast<const half8_t*>(qrow + (D / 4) * lg + 8 * j) : half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  // tile t0's keys and values to LDS: D / 16 instructions of 1 KB each for the
+  // keys and for the values, D / 64 of each per wave
+  auto load_tile = [&](int t0, half_t* sk, half_t* sv) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int q = 0; q < D / 64; ++q) {
+      const int i = wave * (D / 64) + q;
+      const int kt = i * (512 / D) + ln / (D / 8), ks = ln % (D / 8);   // key row and slot of this lane
+      const half_t* ksrc = kh + (size_t)(t0 + kt) * D + fk_slot<D>(kt, ks) * 8;
+      __builtin_amdgcn_global_load_lds(ksrc, (__attribute__((address_space(3))) void*)&sk[i * 512], 16, 0, 0);
+      const int vd = 16 * i + (ln >> 2), vs = ln & 3;                  // value row (dim) and slot
+      const half_t* vsrc = vh + ((size_t)(t0 >> 5) * D + vd) * 32 + fv_slot(vd, vs) * 8;
+      __builtin_amdgcn_global_load_lds(vsrc, (__attribute__((address_space(3))) void*)&sv[i * 512], 16, 0, 0);
+    }
+  };
+  auto wait_loads = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
+
+  AttnState<D, false> st;
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) st.o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  st.m = -__builtin_inff();
+  st.l = 0.f;
+  st.ex = 127;
+  const int ntiles = (n + 31) / 32;
+  if (ntiles > 0) {
+    load_tile(0, s_k0, s_v0);
+    wait_loads();
+    __syncthreads();
+  }
+  auto step = [&](auto bufc, int it) {
+    constexpr int BUF = decltype(bufc)::value;
+    const half_t* sk = BUF == 0 ? s_k0 : s_k1;
+    const half_t* sv = BUF == 0 ? s_v0 : s_v1;
+    const int t0 = 32 * it;
+    if (it + 1 < ntiles) load_tile(t0 + 32, BUF == 0 ? s_k1 : s_k0, BUF == 0 ? s_v1 : s_v0);
+    KVFrag<D, kFmtF16, kFmtF16> f;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int kt = 8 * (r >> 2) + 4 * hf + (r & 3);
+#pragma unroll
+      for (int j = 0; j < D / 32; ++j)
+        f.k[hf][j] = *reinterpret_cast<const half8_t*>(sk + kt * D + fk_slot<D>(kt, (D / 32) * lg + j) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      const int vd = 16 * i + r;
+      f.v[i] = *reinterpret_cast<const half8_t*>(sv + vd * 32 + fv_slot(vd, lg) * 8);
+    }
+    const int valid = min(32, n - t0);
+    attn_tile<D, kFmtF16, kFmtF16, true>(st, f, qf, a.scale_log2, valid, lg, [] {}, min(max(ncol - t0, 0), valid));
+    wait_loads();
+    __syncthreads();
+  };
+  for (int it = 0; it < ntiles;) {
+    step(std::integral_constant<int, 0>{}, it);
+    if (++it >= ntiles) break;
+    step(std::integral_constant<int, 1>{}, it);
+    ++it;
+  }
+
+  // O = o / l (the value products carry p * 2^kPScale)
+  const float ltot = st.l + __shfl_xor(st.l, 16);
+  const float lsum = ltot + __shfl_xor(ltot, 32);
+  if (colv) {
+    const float inv = exp2i(-kPScale) / lsum;
+    half_t* orow = a.O16 + ((size_t)row * a.Hq + head) * D;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      // rounded to nearest, as the merge of the split-K kernel stores O16
+      const half2_t lo = {(half_t)(st.o[i][0] * inv), (half_t)(st.o[i][1] * inv)};
+      const half2_t hi = {(half_t)(st.o[i][2] * inv), (half_t)(st.o[i][3] * inv)};
+      *reinterpret_cast<uint2*>(orow + 16 * i + 4 * lg) = make_uint2(h2_bits(lo), h2_bits(hi));
+    }
+  }
+}
+
 hipError_t launch_attn_prefill(const qkdec_kv_layer& kv, const int32_t* slot, const int32_t* n_ctx, int B,
                                const uint16_t* Q, int n_q_heads, float scale, uint16_t* O16, float* partials,
                                int n_ctx_add, hipStream_t st) {
+  const int G = n_q_heads / kv.n_kv_heads;
+  if (kv.type == QKDEC_KV_F16 && G <= 16 && (G & (G - 1)) == 0) {
+    FlashArgs f;
+    f.k = reinterpret_cast<const half_t*>(kv.k);
+    f.v = reinterpret_cast<const half_t*>(kv.v);
+    f.n_kv = kv.n_kv_heads;
+    f.cap = kv.capacity;
+    f.n_slots = kv.n_slots;
+    f.slot = slot;
+    f.pos = n_ctx;
+    f.n_add = n_ctx_add;
+    f.rows = B;
+    f.Q = reinterpret_cast<const half_t*>(Q);
+    f.Hq = n_q_heads;
+    f.h4 = G < 4 ? G : 4;
+    f.scale_log2 = scale * 1.4426950408889634f;
+    f.O16 = reinterpret_cast<half_t*>(O16);
+    const dim3 grid((unsigned)((B + 64 / f.h4 - 1) / (64 / f.h4)), kv.n_kv_heads, G / f.h4);
+    if (kv.head_dim == 128)
+      hipLaunchKernelGGL(attn_prefill_kernel<128>, grid, dim3(256), 0, st, f);
+    else
+      hipLaunchKernelGGL(attn_prefill_kernel<64>, grid, dim3(256), 0, st, f);
+    return hipGetLastError();
+  }
+  // other caches: the split-K kernel, at most kPfAttnRows rows per call
+  if (B > kPfAttnRows) {
+    for (int r0 = 0; r0 < B; r0 += kPfAttnRows) {
+      const hipError_t e = launch_attn_prefill(kv, slot + r0, n_ctx + r0, std::min(kPfAttnRows, B - r0),
+                                               Q + (size_t)r0 * n_q_heads * kv.head_dim, n_q_heads, scale,
+                                               O16 + (size_t)r0 * n_q_heads * kv.head_dim, partials, n_ctx_add, st);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   const int tok = attn_prefill_tok(n_q_heads, kv.n_kv_heads);
   if (tok == 1)
     return launch_attn_decode(kv, slot, n_ctx, B, Q, n_q_heads, scale, nullptr, O16, partials, n_ctx_add, st);

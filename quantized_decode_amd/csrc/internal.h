@@ -176,10 +176,12 @@ hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, con
                               float* partials, int n_ctx_add, hipStream_t st, const int32_t* pages = nullptr,
                               int max_pages = 0);
 // The same attention for B consecutive prompt rows of one sequence (row b:
-// slot[b], n_ctx[b] + n_ctx_add tokens, ascending by one): 16 / G rows share a
-// work item, their (row, head) pairs the MFMA columns, so each key and value
-// tile is read once for all of them; scores past a row's own length are
-// masked.  For G not dividing 16 it is launch_attn_decode.
+// slot[b], n_ctx[b] + n_ctx_add tokens, ascending by one).  An fp16 cache
+// with G a power of two up to 16: flash attention, 64 query columns per
+// work-group sharing each key and value tile, no key split (partials unused).
+// Other caches: the split-K kernel, kPfAttnRows rows per launch, 16 / G rows
+// per work item with their (row, head) pairs as the MFMA columns and scores
+// past a row's own length masked (for G not dividing 16, launch_attn_decode).
 // Its partial-result rows per (row, head) for a call of B rows: enough runs
 // for the longest sequence (one per kAttnChunk tokens) and for the wanted
 // count, which falls as B grows.

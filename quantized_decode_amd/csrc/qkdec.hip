@@ -339,9 +339,7 @@ qkdec_status run_prefill(const qkdec_model* m, const qkdec_kv_layer* kv, int slo
                               nullptr, st));
       QK_TRY(launch_rope_append(kv[l], w.qkv, nqkv, Hq, rows, w.rs, w.rp, m->rope_base, w.q16, w.err, st, w.rp,
                                 w.rope));
-      for (int r0 = 0; r0 < rows; r0 += kPfAttnRows)
-        QK_TRY(launch_attn_prefill(kv[l], w.rs + r0, w.rp + r0, std::min(kPfAttnRows, rows - r0),
-                                   w.q16 + (size_t)r0 * hq, Hq, scale, w.o16 + (size_t)r0 * hq, w.attn_part, 1, st));
+      QK_TRY(launch_attn_prefill(kv[l], w.rs, w.rp, rows, w.q16, Hq, scale, w.o16, w.attn_part, 1, st));
       QK_TRY(launch_pf_norm(nullptr, nullptr, nullptr, 0.f, (int)hq, rows, w.o16, w.xs, w.fd, st));
       QK_TRY(launch_gemm_pf(ly.w_o, H, hq, w.o16, hq, w.xs, nullptr, rows, w.part, ks_o, st));
       QK_TRY(launch_pf_finish(w.part, ks_o, rows, H, w.x, w.x, H, kPfNorm, w.ssq, nullptr, nullptr, nullptr, st));
