@@ -369,13 +369,13 @@ qkdec_status qkdec_step_paged(const qkdec_model* m, const qkdec_kv_layer* kv, co
  * head and argmax run for the last token only: logits fp32 [vocab] (may be
  * NULL) and tok_out (device int32 [1]) = its argmax, the first generated
  * token.  Positions before start must already be cached.  The prompt is taken
- * in chunks of 256 tokens, each chunk one pass of the layers with its tokens
- * as the rows: the projections are matrix-core products over 64-row tiles
- * (each weight read once per chunk and tile, RMSNorm and SwiGLU between them
- * in the decode step's rounding), the attention is the split-K decode
- * attention with several prompt rows per work item: token t attends over
- * positions <= start+t, the chunk's earlier tokens included (appended before
- * the attention runs).
+ * in chunks of 1024 tokens, each chunk one pass of the layers with its
+ * tokens as the rows: the projections are matrix-core products over 64-row
+ * tiles (each weight read once per chunk and tile, RMSNorm and SwiGLU between
+ * them in the decode step's rounding); the attention is a flash kernel for
+ * an fp16 cache and the split-K decode attention with several prompt rows
+ * per work item otherwise: token t attends over positions <= start+t, the
+ * chunk's earlier tokens included (appended before the attention runs).
  * 0 <= slot < n_slots, n >= 1, start + n <= capacity (else QKDEC_E_CAPACITY,
  * nothing launched).  workspace: qkdec_prefill_workspace_size() bytes, zeroed
  * once with qkdec_workspace_init. */
