@@ -693,6 +693,8 @@ def main():
                     help="skip the standalone GEMM-pass and attention-pass measurements")
     ap.add_argument("--prefill-only", type=int, default=0, metavar="N",
                     help="only time the prefill of an N-token prompt and print its JSON line")
+    ap.add_argument("--prefill-kv", choices=["f16", "q8_0", "q8k_f16v", "f16k_q8v", "fp8"], default="f16",
+                    help="cache format of --prefill-only")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write profiles/counted_traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of "
                          "this bench (--points main at --batch/--context/--kv) and of --copy-probe-mb; no GPU work")
@@ -733,7 +735,8 @@ def main():
         return
     if args.prefill_only:
         log(f"prefill of a {args.prefill_only}-token prompt")
-        print(json.dumps({"prefill": prefill_point(qd, sd, dims, dev_model, args.prefill_only, 9200)}))
+        print(json.dumps({"prefill": prefill_point(qd, sd, dims, dev_model, args.prefill_only, 9200,
+                                                   args.prefill_kv)}))
         return
 
     points = [(args.batch, args.context, args.kv)]

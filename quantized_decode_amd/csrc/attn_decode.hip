@@ -324,18 +324,20 @@ size_t attn_prefill_partials_bytes(int max_rows, int n_q_heads, const qkdec_kv_l
   return most * (size_t)(kv.head_dim + 2) * sizeof(float);
 }
 
-// ---- prompt rows over an fp16 cache: flash attention without a key split.
-// A work-group holds 64 query columns that share one KV head: H4 = min(G, 4)
-// heads of the group times 64 / H4 consecutive prompt rows; wave w takes head
-// w % H4 of 16 rows.  Each 32-token key and value tile is DMA'd to LDS once
-// for all four waves (double-buffered, 16-byte chunks XOR-swizzled so the
-// waves' fragment reads spread over the banks), and every wave runs the
-// decode kernel's tile step (attn_tile, per-column causal masks) over all
-// the keys its rows see, so the softmax state is final at the end: no
-// partial results and no merge.
+// ---- prompt rows: flash attention without a key split.  A work-group holds
+// 64 query columns that share one KV head: H4 = min(G, 4) heads of the group
+// times 64 / H4 consecutive prompt rows; wave w takes head w % H4 of 16 rows.
+// Each 32-token key and value tile (codes, and for Q8_0 the block scales) is
+// DMA'd to LDS once for all four waves, double-buffered, with the 16-byte
+// chunks XOR-swizzled so the waves' fragment reads spread over the banks;
+// every wave builds the decode kernel's fragments from LDS and runs its tile
+// step (attn_tile, per-column causal masks) over all the keys its rows see,
+// so the softmax state is final at the end: no partial results, no merge.
 struct FlashArgs {
-  const half_t* k;       // cache of the layer: keys [slots][n_kv][cap][D]
-  const half_t* v;       // values [slots][n_kv][cap/32][D][32]
+  const uint8_t* k;      // keys [slots][n_kv][cap][D] (fp16 or 8-bit codes)
+  const uint8_t* v;      // values [slots][n_kv][cap/32][D][32]
+  const uint16_t* ks;    // Q8_0 key scales [slots][n_kv][cap][D/32]
+  const uint16_t* vs;    // Q8_0 value scales, the same shape
   int n_kv, cap, n_slots;
   const int32_t* slot;   // [rows] (one sequence: the first row's slot)
   const int32_t* pos;    // [rows] ascending; row r attends over pos[r] + n_add tokens
@@ -346,18 +348,28 @@ struct FlashArgs {
   half_t* O16;           // [rows][Hq][D]
 };
 
-// slot of the 16-byte chunk c of key row t in the LDS key tile (D/8 chunks a row)
-template <int D>
+// Swizzle of the LDS tiles: the 16-byte chunk c of key row t (CK chunks a
+// row) sits at slot fk_slot(t, c); chunk c of value row d at fv_slot(d, c).
+template <int CK>
 __device__ __forceinline__ int fk_slot(int t, int c) {
-  return (c ^ (((t >> 1) & 12) | (t & 3))) & (D / 8 - 1);
+  return (c ^ (((t >> 1) & 12) | (t & 3))) & (CK - 1);
 }
-// slot of chunk c (4 a row of 32 tokens) of value row d in the LDS value tile
-__device__ __forceinline__ int fv_slot(int d, int c) { return c ^ ((d >> 2) & 3); }
+template <int CV>
+__device__ __forceinline__ int fv_slot(int d, int c) {
+  return CV == 4 ? c ^ ((d >> 2) & 3) : c ^ ((d >> 3) & 1);
+}
 
-template <int D>
+template <int D, int KF, int VF>
 __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(const FlashArgs a) {
-  __shared__ __attribute__((aligned(16))) half_t s_k0[32 * D], s_k1[32 * D];
-  __shared__ __attribute__((aligned(16))) half_t s_v0[32 * D], s_v1[32 * D];
+  constexpr int KB = KF == kFmtF16 ? 2 : 1, VB = VF == kFmtF16 ? 2 : 1;   // bytes per element
+  constexpr int CK = D * KB / 16, CV = 32 * VB / 16;                       // 16-byte chunks per row
+  constexpr int NK = 32 * D * KB / 1024, NV = 32 * D * VB / 1024;          // 1 KB copies per tile
+  constexpr bool KQ = KF == kFmtQ8, VQ = VF == kFmtQ8;
+  __shared__ __attribute__((aligned(16))) uint8_t s_k0[32 * D * KB], s_k1[32 * D * KB];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v0[32 * D * VB], s_v1[32 * D * VB];
+  // Q8_0 scales of the tile's 32 tokens, [32][D/32] fp16 as in the cache
+  __shared__ __attribute__((aligned(16))) uint8_t s_ks0[KQ ? 2 * D : 16], s_ks1[KQ ? 2 * D : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_vs0[VQ ? 2 * D : 16], s_vs1[VQ ? 2 * D : 16];
   const int tx = threadIdx.x, lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
   const int lg = lane >> 4, r = lane & 15;
   const int g = blockIdx.y, G = a.Hq / a.n_kv, h4 = a.h4, tb = 64 / h4;
@@ -372,35 +384,53 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(const FlashArgs a)
   if (s < 0 || s >= a.n_slots || n < 0) n = 0;
   const int ncol = colv ? min(max(a.pos[row] + a.n_add, 0), n) : 0;
   const size_t head_row0 = ((size_t)s * a.n_kv + g) * a.cap;
-  const half_t* kh = a.k + head_row0 * D;
-  const half_t* vh = a.v + head_row0 * D;
+  const uint8_t* kh = a.k + head_row0 * D * KB;
+  const uint8_t* vh = a.v + head_row0 * D * VB;
 
   half8_t qf[D / 32];
   {
     const half_t* qrow = a.Q + ((size_t)(colv ? row : last) * a.Hq + head) * D;
 #pragma unroll
-    for (int j = 0; j < D / 32; ++j)
-      qf[j] = colv ? *reinterpret_cast<const half8_t*>(qrow + (D / 4) * lg + 8 * j) : half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < D / 32; ++j) {
+      const int d0 = KQ ? (32 * j + 8 * lg) : ((D / 4) * lg + 8 * j);
+      qf[j] = colv ? *reinterpret_cast<const half8_t*>(qrow + d0) : half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    }
   }
-  // tile t0's keys and values to LDS: D / 16 instructions of 1 KB each for the
-  // keys and for the values, D / 64 of each per wave
-  auto load_tile = [&](int t0, half_t* sk, half_t* sv) {
+  // the tile at t0 to LDS: NK + NV copies of 1 KB spread over the waves, then
+  // the Q8_0 scales (2 D bytes each) by waves 0 and 1
+  auto load_tile = [&](int t0, uint8_t* sk, uint8_t* sv, uint8_t* sks, uint8_t* svs) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int q = 0; q < D / 64; ++q) {
-      const int i = wave * (D / 64) + q;
-      const int kt = i * (512 / D) + ln / (D / 8), ks = ln % (D / 8);   // key row and slot of this lane
-      const half_t* ksrc = kh + (size_t)(t0 + kt) * D + fk_slot<D>(kt, ks) * 8;
-      __builtin_amdgcn_global_load_lds(ksrc, (__attribute__((address_space(3))) void*)&sk[i * 512], 16, 0, 0);
-      const int vd = 16 * i + (ln >> 2), vs = ln & 3;                  // value row (dim) and slot
-      const half_t* vsrc = vh + ((size_t)(t0 >> 5) * D + vd) * 32 + fv_slot(vd, vs) * 8;
-      __builtin_amdgcn_global_load_lds(vsrc, (__attribute__((address_space(3))) void*)&sv[i * 512], 16, 0, 0);
+    for (int p = 0; p < (NK + NV + 3) / 4; ++p) {
+      const int q = wave + 4 * p;
+      if (q < NK) {
+        const int kt = q * (1024 / (D * KB)) + ln / CK, sl = ln % CK;   // key row and slot of this lane
+        const uint8_t* src = kh + ((size_t)(t0 + kt) * D * KB) + fk_slot<CK>(kt, sl) * 16;
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&sk[q * 1024], 16, 0, 0);
+      } else if (q < NK + NV) {
+        const int i = q - NK;
+        const int vd = i * (1024 / (32 * VB)) + ln / CV, sl = ln % CV;  // value row (dim) and slot
+        const uint8_t* src = vh + ((size_t)(t0 >> 5) * D + vd) * 32 * VB + fv_slot<CV>(vd, sl) * 16;
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&sv[i * 1024], 16, 0, 0);
+      }
+    }
+    if constexpr (KQ) {
+      if (wave == 0 && ln < D / 8) {
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.ks + (head_row0 + t0) * (D / 32)) + ln * 16;
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)sks, 16, 0, 0);
+      }
+    }
+    if constexpr (VQ) {
+      if (wave == 1 && ln < D / 8) {
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.vs + (head_row0 + t0) * (D / 32)) + ln * 16;
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)svs, 16, 0, 0);
+      }
     }
   };
   auto wait_loads = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
 
-  AttnState<D, false> st;
+  AttnState<D, VQ> st;
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) st.o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
   st.m = -__builtin_inff();
@@ -408,31 +438,78 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(const FlashArgs a)
   st.ex = 127;
   const int ntiles = (n + 31) / 32;
   if (ntiles > 0) {
-    load_tile(0, s_k0, s_v0);
+    load_tile(0, s_k0, s_v0, s_ks0, s_vs0);
     wait_loads();
     __syncthreads();
   }
   auto step = [&](auto bufc, int it) {
     constexpr int BUF = decltype(bufc)::value;
-    const half_t* sk = BUF == 0 ? s_k0 : s_k1;
-    const half_t* sv = BUF == 0 ? s_v0 : s_v1;
+    const uint8_t* sk = BUF == 0 ? s_k0 : s_k1;
+    const uint8_t* sv = BUF == 0 ? s_v0 : s_v1;
+    const uint8_t* sks = BUF == 0 ? s_ks0 : s_ks1;
+    const uint8_t* svs = BUF == 0 ? s_vs0 : s_vs1;
     const int t0 = 32 * it;
-    if (it + 1 < ntiles) load_tile(t0 + 32, BUF == 0 ? s_k1 : s_k0, BUF == 0 ? s_v1 : s_v0);
-    KVFrag<D, kFmtF16, kFmtF16> f;
+    if (it + 1 < ntiles)
+      load_tile(t0 + 32, BUF == 0 ? s_k1 : s_k0, BUF == 0 ? s_v1 : s_v0, BUF == 0 ? s_ks1 : s_ks0,
+                BUF == 0 ? s_vs1 : s_vs0);
+    KVFrag<D, KF, VF> f;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const int kt = 8 * (r >> 2) + 4 * hf + (r & 3);
+      const uint8_t* krow = sk + kt * D * KB;
+      if constexpr (KF == kFmtF16) {
 #pragma unroll
-      for (int j = 0; j < D / 32; ++j)
-        f.k[hf][j] = *reinterpret_cast<const half8_t*>(sk + kt * D + fk_slot<D>(kt, (D / 32) * lg + j) * 8);
+        for (int j = 0; j < D / 32; ++j)
+          f.k[hf][j] = *reinterpret_cast<const half8_t*>(krow + fk_slot<CK>(kt, (D / 32) * lg + j) * 16);
+      } else if constexpr (KF == kFmtQ8) {
+#pragma unroll
+        for (int j = 0; j < D / 32; ++j) {   // bytes 32 j + 8 lg .. + 7
+          const uint2 w = *reinterpret_cast<const uint2*>(krow + fk_slot<CK>(kt, 2 * j + (lg >> 1)) * 16 + 8 * (lg & 1));
+          f.k[hf][j][0] = w.x;
+          f.k[hf][j][1] = w.y;
+        }
+      } else {
+#pragma unroll
+        for (int j2 = 0; j2 < D / 64; ++j2) {   // bytes (D / 4) lg + 16 j2 .. + 15
+          const uint4 w = *reinterpret_cast<const uint4*>(krow + fk_slot<CK>(kt, (D / 64) * lg + j2) * 16);
+          f.k[hf][2 * j2][0] = w.x;
+          f.k[hf][2 * j2][1] = w.y;
+          f.k[hf][2 * j2 + 1][0] = w.z;
+          f.k[hf][2 * j2 + 1][1] = w.w;
+        }
+      }
+    }
+    if constexpr (KQ) {
+      // scales of tokens 8 lg .. 8 lg + 7
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(sks + 16 * lg * (D / 32) + 16 * i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f.ks[4 * i + e] = x[e];
+      }
     }
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) {
       const int vd = 16 * i + r;
-      f.v[i] = *reinterpret_cast<const half8_t*>(sv + vd * 32 + fv_slot(vd, lg) * 8);
+      const uint8_t* vrow = sv + vd * 32 * VB;
+      if constexpr (VF == kFmtF16) {
+        f.v[i] = *reinterpret_cast<const half8_t*>(vrow + fv_slot<CV>(vd, lg) * 16);
+      } else {   // tokens 8 lg .. 8 lg + 7
+        const uint2 w = *reinterpret_cast<const uint2*>(vrow + fv_slot<CV>(vd, lg >> 1) * 16 + 8 * (lg & 1));
+        f.v[i][0] = w.x;
+        f.v[i][1] = w.y;
+      }
+    }
+    if constexpr (VQ) {
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) {
+        const u32x4 y = *reinterpret_cast<const u32x4*>(svs + 16 * lg * (D / 32) + 16 * i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f.vs[4 * i + e] = y[e];
+      }
     }
     const int valid = min(32, n - t0);
-    attn_tile<D, kFmtF16, kFmtF16, true>(st, f, qf, a.scale_log2, valid, lg, [] {}, min(max(ncol - t0, 0), valid));
+    attn_tile<D, KF, VF, true>(st, f, qf, a.scale_log2, valid, lg, [] {}, min(max(ncol - t0, 0), valid));
     wait_loads();
     __syncthreads();
   };
@@ -443,11 +520,11 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(const FlashArgs a)
     ++it;
   }
 
-  // O = o / l (the value products carry p * 2^kPScale)
+  // O = o / l (the value products carry p * 2^kPScale, or p * 2^ex for Q8_0 values)
   const float ltot = st.l + __shfl_xor(st.l, 16);
   const float lsum = ltot + __shfl_xor(ltot, 32);
   if (colv) {
-    const float inv = exp2i(-kPScale) / lsum;
+    const float inv = (VQ ? exp2i(-st.ex) : exp2i(-kPScale)) / lsum;
     half_t* orow = a.O16 + ((size_t)row * a.Hq + head) * D;
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) {
@@ -463,10 +540,12 @@ hipError_t launch_attn_prefill(const qkdec_kv_layer& kv, const int32_t* slot, co
                                const uint16_t* Q, int n_q_heads, float scale, uint16_t* O16, float* partials,
                                int n_ctx_add, hipStream_t st) {
   const int G = n_q_heads / kv.n_kv_heads;
-  if (kv.type == QKDEC_KV_F16 && G <= 16 && (G & (G - 1)) == 0) {
+  if (G <= 16 && (G & (G - 1)) == 0) {
     FlashArgs f;
-    f.k = reinterpret_cast<const half_t*>(kv.k);
-    f.v = reinterpret_cast<const half_t*>(kv.v);
+    f.k = reinterpret_cast<const uint8_t*>(kv.k);
+    f.v = reinterpret_cast<const uint8_t*>(kv.v);
+    f.ks = reinterpret_cast<const uint16_t*>(kv.k_scale);
+    f.vs = reinterpret_cast<const uint16_t*>(kv.v_scale);
     f.n_kv = kv.n_kv_heads;
     f.cap = kv.capacity;
     f.n_slots = kv.n_slots;
@@ -480,10 +559,20 @@ hipError_t launch_attn_prefill(const qkdec_kv_layer& kv, const int32_t* slot, co
     f.scale_log2 = scale * 1.4426950408889634f;
     f.O16 = reinterpret_cast<half_t*>(O16);
     const dim3 grid((unsigned)((B + 64 / f.h4 - 1) / (64 / f.h4)), kv.n_kv_heads, G / f.h4);
-    if (kv.head_dim == 128)
-      hipLaunchKernelGGL(attn_prefill_kernel<128>, grid, dim3(256), 0, st, f);
-    else
-      hipLaunchKernelGGL(attn_prefill_kernel<64>, grid, dim3(256), 0, st, f);
+#define QK_FA(DD, KF, VF) hipLaunchKernelGGL((attn_prefill_kernel<DD, KF, VF>), grid, dim3(256), 0, st, f)
+#define QK_FA_D(DD)                                                      \
+  do {                                                                   \
+    if (kf == kFmtF8) QK_FA(DD, kFmtF8, kFmtF8);                         \
+    else if (kf == kFmtQ8 && vf == kFmtQ8) QK_FA(DD, kFmtQ8, kFmtQ8);    \
+    else if (kf == kFmtQ8) QK_FA(DD, kFmtQ8, kFmtF16);                   \
+    else if (vf == kFmtQ8) QK_FA(DD, kFmtF16, kFmtQ8);                   \
+    else QK_FA(DD, kFmtF16, kFmtF16);                                    \
+  } while (0)
+    const int kf = kv_k_fmt(kv.type), vf = kv_v_fmt(kv.type);
+    if (kv.head_dim == 128) QK_FA_D(128);
+    else QK_FA_D(64);
+#undef QK_FA_D
+#undef QK_FA
     return hipGetLastError();
   }
   // other caches: the split-K kernel, at most kPfAttnRows rows per call

@@ -76,10 +76,12 @@ def test_prefill_toy_other_caches(qd, kind):
     _toy_case(qd, synth.TOY, kind, 70, 1720)
 
 
-@pytest.mark.parametrize("heads,kind", [((4, 2), "f16"), ((8, 1), "q8_0"), ((16, 1), "f16"), ((12, 4), "f16")])
+@pytest.mark.parametrize("heads,kind", [((4, 2), "f16"), ((8, 1), "q8_0"), ((8, 1), "f16"), ((16, 1), "f16"),
+                                        ((12, 4), "f16"), ((12, 4), "q8_0")])
 def test_prefill_group_sizes(qd, heads, kind):
-    # query heads per KV head G = 2, 8, 16 and 3: the attention takes 16 / G
-    # prompt rows per work item when G divides 16 (G = 16, and G = 3, one row)
+    # query heads per KV head G = 2, 8, 16 and 3: the flash kernel takes
+    # min(G, 4) heads of 64 / min(G, 4) rows per work-group for G a power of
+    # two; G = 3 runs the split-K kernel, one row per work item
     hq, hkv = heads
     dims = synth.ModelDims(n_layers=2, hidden=512, n_q_heads=hq, n_kv_heads=hkv, head_dim=64, ffn=1536,
                            vocab=4096)
@@ -126,13 +128,13 @@ def _vs_decode_steps(qd, dims, kind, n_cached, n_prompt, seed):
             assert np.abs(x64 - y64).max() <= 1e-3 * np.abs(y64).max()
 
 
-def test_prefill_full_width_equals_decode_steps(qd):
+@pytest.mark.parametrize("kind", ["f16", "q8_0"])
+def test_prefill_full_width_equals_decode_steps(qd, kind):
     # a two-layer decoder of the full width (every projection on the kernels
-    # the bench times), 270 prompt tokens after 300 cached ones (attention
-    # calls of 256 and 14 rows)
+    # the bench times), 270 prompt tokens after 300 cached ones
     dims = synth.ModelDims(n_layers=2, hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, ffn=12288,
                            vocab=16384)
-    _vs_decode_steps(qd, dims, "f16", 300, 270, 1710)
+    _vs_decode_steps(qd, dims, kind, 300, 270, 1710)
 
 
 @pytest.mark.parametrize("kind", ["f16", "q8_0"])
