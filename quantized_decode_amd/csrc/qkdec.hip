@@ -335,9 +335,14 @@ qkdec_status run_prefill(const qkdec_model* m, const qkdec_kv_layer* kv, int slo
     for (int l = 0; l < m->n_layers; ++l) {
       const qkdec_layer& ly = m->layers[l];
       QK_TRY(launch_gemm_pf(ly.w_qkv, nqkv, H, w.h, H, w.xs, nullptr, rows, w.part, ks_qkv, st));
-      QK_TRY(launch_pf_finish(w.part, ks_qkv, rows, nqkv, nullptr, w.qkv, nqkv, kPfOut, nullptr, nullptr, nullptr,
-                              nullptr, st));
-      QK_TRY(launch_rope_append(kv[l], w.qkv, nqkv, Hq, rows, w.rs, w.rp, m->rope_base, w.q16, w.err, st, w.rp,
+      // one K range: the partial sums are the projection rows themselves
+      const float* qkv = w.part;
+      if (ks_qkv > 1) {
+        QK_TRY(launch_pf_finish(w.part, ks_qkv, rows, nqkv, nullptr, w.qkv, nqkv, kPfOut, nullptr, nullptr, nullptr,
+                                nullptr, st));
+        qkv = w.qkv;
+      }
+      QK_TRY(launch_rope_append(kv[l], qkv, nqkv, Hq, rows, w.rs, w.rp, m->rope_base, w.q16, w.err, st, w.rp,
                                 w.rope));
       QK_TRY(launch_attn_prefill(kv[l], w.rs, w.rp, rows, w.q16, Hq, scale, w.o16, w.attn_part, 1, st));
       QK_TRY(launch_pf_norm(nullptr, nullptr, nullptr, 0.f, (int)hq, rows, w.o16, w.xs, w.fd, st));
