@@ -509,7 +509,8 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(const FlashArgs a)
       }
     }
     const int valid = min(32, n - t0);
-    attn_tile<D, KF, VF, true>(st, f, qf, a.scale_log2, valid, lg, [] {}, min(max(ncol - t0, 0), valid));
+    // O is rounded to fp16 at the end: p is taken to fp16 alone (no low half)
+    attn_tile<D, KF, VF, true, false>(st, f, qf, a.scale_log2, valid, lg, [] {}, min(max(ncol - t0, 0), valid));
     wait_loads();
     __syncthreads();
   };

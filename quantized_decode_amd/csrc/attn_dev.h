@@ -328,7 +328,9 @@ constexpr int kPScale = 14;
 // rows), and vcol (this lane's column, <= valid) is the number of the tile's
 // tokens that column may attend to; scores past it are masked.  Otherwise
 // every column sees the same valid tokens (vcol unused).
-template <int D, int KF, int VF, bool PERCOL = false, typename Mid>
+// PLO = false: the value products take p rounded to fp16 alone (no low half),
+// for a caller that rounds O to fp16 right after.
+template <int D, int KF, int VF, bool PERCOL = false, bool PLO = true, typename Mid>
 __device__ __forceinline__ void attn_tile(AttnState<D, VF == kFmtQ8>& st, KVFrag<D, KF, VF>& f,
                                           const half8_t (&qf)[D / 32], float scale_log2, int valid, int lg,
                                           const Mid& mid, int vcol = 0) {
@@ -421,14 +423,15 @@ __device__ __forceinline__ void attn_tile(AttnState<D, VF == kFmtQ8>& st, KVFrag
   mid();
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (VF == kFmtF8) {
-    half8_t phi, plo;
+    half8_t phi;
+    [[maybe_unused]] half8_t plo;
     const float ps = exp2i(kPScale);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float pe = p[e] * ps;
       const half_t h = (half_t)pe;
       phi[e] = h;
-      plo[e] = (half_t)(pe - (float)h);
+      if constexpr (PLO) plo[e] = (half_t)(pe - (float)h);
     }
     const int lim = valid - 8 * lg;   // codes past the end may be NaN codes: never reach the MFMA
 #pragma unroll
@@ -439,17 +442,18 @@ __device__ __forceinline__ void attn_tile(AttnState<D, VF == kFmtQ8>& st, KVFrag
         for (int e = 0; e < 8; ++e) vf[e] = e < lim ? vf[e] : (half_t)0.f;
       }
       st.o[i] = mfma16x16x32(vf, phi, st.o[i]);
-      st.o[i] = mfma16x16x32(vf, plo, st.o[i]);
+      if constexpr (PLO) st.o[i] = mfma16x16x32(vf, plo, st.o[i]);
     }
   } else if constexpr (VF == kFmtF16) {
-    half8_t phi, plo;
+    half8_t phi;
+    [[maybe_unused]] half8_t plo;
     const float ps = exp2i(kPScale);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float pe = p[e] * ps;
       const half_t h = (half_t)pe;
       phi[e] = h;
-      plo[e] = (half_t)(pe - (float)h);
+      if constexpr (PLO) plo[e] = (half_t)(pe - (float)h);
     }
     if (valid < 32) {  // never let values past the end reach the MFMA (0 * NaN)
       const int lim = valid - 8 * lg;
@@ -462,7 +466,7 @@ __device__ __forceinline__ void attn_tile(AttnState<D, VF == kFmtQ8>& st, KVFrag
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) {
       st.o[i] = mfma16x16x32(f.v[i], phi, st.o[i]);
-      st.o[i] = mfma16x16x32(f.v[i], plo, st.o[i]);
+      if constexpr (PLO) st.o[i] = mfma16x16x32(f.v[i], plo, st.o[i]);
     }
   } else {
     const int lim = valid - 8 * lg;   // tokens of this lane at or past lim are out of range
@@ -480,7 +484,8 @@ __device__ __forceinline__ void attn_tile(AttnState<D, VF == kFmtQ8>& st, KVFrag
       // hi = pv rounded to the nearest fp16, lo = the exact remainder pv - hi
       // rounded likewise: hi + lo is pv to 2^-22 relative.  pv and the
       // remainder are single fused operations on the fp16 scale and hi
-      half8_t phi, plo;
+      half8_t phi;
+      [[maybe_unused]] half8_t plo;
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         float pv0 = __builtin_fmaf(pf[e], scale_at<D>(f.vs, e, c), 0.f);
@@ -492,15 +497,17 @@ __device__ __forceinline__ void attn_tile(AttnState<D, VF == kFmtQ8>& st, KVFrag
         const half_t h0 = (half_t)pv0, h1 = (half_t)pv1;
         phi[e] = h0;
         phi[e + 1] = h1;
-        plo[e] = (half_t)__builtin_fmaf((float)h0, m1, pv0);
-        plo[e + 1] = (half_t)__builtin_fmaf((float)h1, m1, pv1);
+        if constexpr (PLO) {
+          plo[e] = (half_t)__builtin_fmaf((float)h0, m1, pv0);
+          plo[e + 1] = (half_t)__builtin_fmaf((float)h1, m1, pv1);
+        }
       }
 #pragma unroll
       for (int ii = 0; ii < 2; ++ii) {
         const int i = 2 * c + ii;
         half8_t vf = i8x8_to_h8(f.v[i][0], f.v[i][1]);
         st.o[i] = mfma16x16x32(vf, phi, st.o[i]);
-        st.o[i] = mfma16x16x32(vf, plo, st.o[i]);
+        if constexpr (PLO) st.o[i] = mfma16x16x32(vf, plo, st.o[i]);
       }
     }
   }
