@@ -415,9 +415,13 @@ __device__ __forceinline__ void attn_tile(AttnState<D, VF == kFmtQ8>& st, KVFrag
     ocorr = corr * exp2i(exn - st.ex);   // the power of two is 1 when the exponent stays
     st.ex = exn;
   }
+  // once the running maxima settle most tiles change none of them: the
+  // rescale by 1 is skipped (same values) when no lane of the wave needs it
+  if (__ballot(ocorr != 1.f) != 0) {
 #pragma unroll
-  for (int i = 0; i < D / 16; ++i) {
-    st.o[i][0] *= ocorr; st.o[i][1] *= ocorr; st.o[i][2] *= ocorr; st.o[i][3] *= ocorr;
+    for (int i = 0; i < D / 16; ++i) {
+      st.o[i][0] *= ocorr; st.o[i][1] *= ocorr; st.o[i][2] *= ocorr; st.o[i][3] *= ocorr;
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   mid();
