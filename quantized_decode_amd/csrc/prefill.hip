@@ -1,13 +1,16 @@
-// Prompt ingestion (qkdec_prefill) on MFMA tiles of up to 64 prompt tokens.
+// The projections and their finishing kernels of prompt ingestion
+// (qkdec_prefill), on MFMA tiles of 64 prompt tokens.
 // (P1, P2, P3: the three pages listed, with their titles, at the top of include/qkdec.h.)
 //
 // P2 "This is the mirror image of the prefill story": unlike decode, a prompt
 // has many rows per weight, so one weight read serves all of them and the
-// products, not the bytes, set the pace.  A chunk of up to kPfRows tokens of
-// one sequence is one pass of the layers.  Each projection is
+// products, not the bytes, set the pace.  A pass of up to kPfChunk tokens of
+// one sequence goes through the layers at once.  Each projection is
 //
-//   gemm_pf_kernel   64 prompt rows x 64 * NTW weight rows per work-group over
-//                    a range of K super-blocks (split-K across work-groups).
+//   gemm_pf_kernel   64 prompt rows (one row tile, the grid's third
+//                    dimension) x 64 * NTW weight rows per work-group over a
+//                    range of K super-blocks (split-K across work-groups when
+//                    the rows alone do not fill the chip).
 //                    The 64 x 256 fp16 activation tile of a super-block, its
 //                    sub-block sums and row factors are staged in LDS once
 //                    per work-group (double-buffered); each wave decodes NTW
@@ -32,9 +35,10 @@
 // input has a power-of-two factor per row and super-block (the SwiGLU
 // output, f16b) scales each product by it; the others (UNIT) do not.
 //
-// RoPE, the KV append and the attention are the decode kernels with the
-// chunk's tokens as rows (the append lands before any row attends; row i
-// attends over start + i + 1 tokens).
+// RoPE and the KV append are the decode kernels with the pass's tokens as
+// rows, and the attention is launch_attn_prefill (attn_decode.hip); the
+// append lands before any row attends, and row i attends over start + i + 1
+// tokens.
 #include <type_traits>
 
 #include "common.h"
