@@ -76,7 +76,7 @@ _ATTN_FMT = {"f16": (0, 0), "q8_0": (1, 1), "q8k_f16v": (1, 0), "f16k_q8v": (0, 
 def kind_kernels(name, kv):
     if name.startswith("attention (split + merge)"):
         kf, vf = _ATTN_FMT[kv]
-        return [f"void qk::attn_split_kernel<128, {kf}, {vf}, false>", "qk::attn_combine_kernel"]
+        return [f"void qk::attn_split_kernel<128, {kf}, {vf}, false, false>", "qk::attn_combine_kernel"]
     if name == "lm_head_argmax":
         return ["qk::lm_head_kernel", "qk::lm_argmax_reduce_kernel"]
     return None
