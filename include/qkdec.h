@@ -384,6 +384,25 @@ qkdec_status qkdec_prefill(const qkdec_model* m, const qkdec_kv_layer* kv, int32
                            const int32_t* tokens, int32_t n, float* logits, int32_t* tok_out, void* workspace,
                            size_t ws_bytes, void* stream);
 
+/* Prefill into a paged pool (P1 "What I am building next": a sequence
+ * admitted between steps brings its prompt; PagedAttention's pool holds it):
+ * as qkdec_prefill for one sequence whose cache is every layer's paged pool
+ * (kv[l].capacity = tokens per page, a power of two; kv[l].n_slots = pages in
+ * the pool), its page table row pages (device int32 [max_pages]: logical
+ * page j of the sequence is pool page pages[j]).  Positions before start
+ * must already be in its pages.  A position whose table entry is outside the
+ * pool (for instance -1) is not stored and raises QKDEC_E_CAPACITY in the
+ * workspace's error word (qkdec_step_status); attention skips such pages.
+ * Rejected with nothing launched: start + n > max_pages * capacity
+ * (QKDEC_E_CAPACITY), a page size that is not a power of two, or query heads
+ * per KV head that are not a power of two (QKDEC_E_SHAPE).  workspace:
+ * qkdec_prefill_paged_workspace_size() bytes, zeroed once with
+ * qkdec_workspace_init. */
+size_t qkdec_prefill_paged_workspace_size(const qkdec_model* m, const qkdec_kv_layer* kv);
+qkdec_status qkdec_prefill_paged(const qkdec_model* m, const qkdec_kv_layer* kv, const int32_t* pages,
+                                 int32_t max_pages, int32_t start, const int32_t* tokens, int32_t n, float* logits,
+                                 int32_t* tok_out, void* workspace, size_t ws_bytes, void* stream);
+
 /* The decode step for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): as qkdec_step, with no workspace argument.  Its intermediates

@@ -98,6 +98,9 @@ _SIGNATURES = {
     "qkdec_prefill_workspace_size": (_SZ, [ctypes.POINTER(Model), ctypes.POINTER(KVLayer)]),
     "qkdec_prefill": (_I32, [ctypes.POINTER(Model), ctypes.POINTER(KVLayer), _I32, _I32, _P, _I32, _P, _P, _P, _SZ,
                              _P]),
+    "qkdec_prefill_paged_workspace_size": (_SZ, [ctypes.POINTER(Model), ctypes.POINTER(KVLayer)]),
+    "qkdec_prefill_paged": (_I32, [ctypes.POINTER(Model), ctypes.POINTER(KVLayer), _P, _I32, _I32, _P, _I32, _P, _P,
+                                   _P, _SZ, _P]),
     "qkdec_step_noalloc_max_bytes": (_SZ, []),
     "qkdec_step_noalloc": (_I32, [ctypes.POINTER(Model), ctypes.POINTER(KVLayer), _P, _P, _P, _I32, _P, _P, _P]),
     "qkdec_step_paged_workspace_size": (_SZ, [ctypes.POINTER(Model), _I32, ctypes.POINTER(KVLayer), _I32]),
@@ -316,6 +319,21 @@ def qkdec_prefill(sm: StepModel, slot: int, start: int, tokens, n: int, tok_out,
                                         _ptr(logits), _ptr(tok_out), _ptr(workspace),
                                         workspace.numel() * workspace.element_size(), _stream(stream)),
            "qkdec_prefill")
+
+
+def qkdec_prefill_paged_workspace_size(sm: StepModel) -> int:
+    return load_library().qkdec_prefill_paged_workspace_size(ctypes.byref(sm.model), sm.kv_arr)
+
+
+def qkdec_prefill_paged(sm: StepModel, pages, max_pages: int, start: int, tokens, n: int, tok_out, workspace,
+                        logits=None, stream=None) -> None:
+    """Append prompt tokens (device int32 [n]) at positions start.. of the
+    sequence whose page table row is pages (device int32 [max_pages]) in
+    every layer's paged pool; tok_out gets the argmax after the last one."""
+    _check(load_library().qkdec_prefill_paged(ctypes.byref(sm.model), sm.kv_arr, _ptr(pages), max_pages, start,
+                                              _ptr(tokens), n, _ptr(logits), _ptr(tok_out), _ptr(workspace),
+                                              workspace.numel() * workspace.element_size(), _stream(stream)),
+           "qkdec_prefill_paged")
 
 
 def qkdec_step_noalloc_max_bytes() -> int:

@@ -346,6 +346,10 @@ struct FlashArgs {
   int Hq, h4;
   float scale_log2;
   half_t* O16;           // [rows][Hq][D]
+  // paged pool (PAGED): the sequence's page table row, pages of 2^page_shift
+  // (= cap) tokens; a tile on an entry outside the pool is masked out
+  const int32_t* pages;
+  int max_pages, page_shift;
 };
 
 // Swizzle of the LDS tiles: the 16-byte chunk c of key row t (CK chunks a
@@ -359,7 +363,7 @@ __device__ __forceinline__ int fv_slot(int d, int c) {
   return CV == 4 ? c ^ ((d >> 2) & 3) : c ^ ((d >> 3) & 1);
 }
 
-template <int D, int KF, int VF>
+template <int D, int KF, int VF, bool PAGED>
 __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(const FlashArgs a) {
   constexpr int KB = KF == kFmtF16 ? 2 : 1, VB = VF == kFmtF16 ? 2 : 1;   // bytes per element
   constexpr int CK = D * KB / 16, CV = 32 * VB / 16;                       // 16-byte chunks per row
@@ -378,14 +382,27 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(const FlashArgs a)
   const int row = row_first + (wave / h4) * 16 + r;   // this lane's column
   const bool colv = row < a.rows;
   const int last = min(row_first + tb - 1, a.rows - 1);
-  const int s = a.slot[row_first];
+  const int s = PAGED ? 0 : a.slot[row_first];
+  const int seq_cap = PAGED ? (a.max_pages << a.page_shift) : a.cap;
   int n = a.pos[last] + a.n_add;
-  if (n > a.cap) n = a.cap;
+  if (n > seq_cap) n = seq_cap;
   if (s < 0 || s >= a.n_slots || n < 0) n = 0;
   const int ncol = colv ? min(max(a.pos[row] + a.n_add, 0), n) : 0;
-  const size_t head_row0 = ((size_t)s * a.n_kv + g) * a.cap;
-  const uint8_t* kh = a.k + head_row0 * D * KB;
-  const uint8_t* vh = a.v + head_row0 * D * VB;
+  // (row of token 0 of this head, position in it) of the tile at t0, and
+  // whether the tile is on a page of the pool
+  auto tile_at = [&](int t0, size_t& row0, int& tt) -> bool {
+    if constexpr (PAGED) {
+      const int pg = a.pages[t0 >> a.page_shift];
+      const bool ok = pg >= 0 && pg < a.n_slots;
+      row0 = ((size_t)(ok ? pg : 0) * a.n_kv + g) * a.cap;
+      tt = t0 & (a.cap - 1);
+      return ok;
+    } else {
+      row0 = ((size_t)s * a.n_kv + g) * a.cap;
+      tt = t0;
+      return true;
+    }
+  };
 
   half8_t qf[D / 32];
   {
@@ -398,7 +415,12 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(const FlashArgs a)
   }
   // the tile at t0 to LDS: NK + NV copies of 1 KB spread over the waves, then
   // the Q8_0 scales (2 D bytes each) by waves 0 and 1
-  auto load_tile = [&](int t0, uint8_t* sk, uint8_t* sv, uint8_t* sks, uint8_t* svs) {
+  auto load_tile = [&](int t0l, uint8_t* sk, uint8_t* sv, uint8_t* sks, uint8_t* svs) {
+    size_t head_row0;
+    int t0;
+    tile_at(t0l, head_row0, t0);
+    const uint8_t* kh = a.k + head_row0 * D * KB;
+    const uint8_t* vh = a.v + head_row0 * D * VB;
     int ln = lane;
     asm volatile("" : "+v"(ln));
 #pragma unroll
@@ -508,7 +530,10 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(const FlashArgs a)
         for (int e = 0; e < 4; ++e) f.vs[4 * i + e] = y[e];
       }
     }
-    const int valid = min(32, n - t0);
+    size_t row0_unused;
+    int tt_unused;
+    // a tile on a page outside the pool has no valid token (every score -inf)
+    const int valid = tile_at(t0, row0_unused, tt_unused) ? min(32, n - t0) : 0;
     // O is rounded to fp16 at the end: p is taken to fp16 alone (no low half)
     attn_tile<D, KF, VF, true, false>(st, f, qf, a.scale_log2, valid, lg, [] {}, min(max(ncol - t0, 0), valid));
     wait_loads();
@@ -539,8 +564,9 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(const FlashArgs a)
 
 hipError_t launch_attn_prefill(const qkdec_kv_layer& kv, const int32_t* slot, const int32_t* n_ctx, int B,
                                const uint16_t* Q, int n_q_heads, float scale, uint16_t* O16, float* partials,
-                               int n_ctx_add, hipStream_t st) {
+                               int n_ctx_add, hipStream_t st, const int32_t* pages, int max_pages) {
   const int G = n_q_heads / kv.n_kv_heads;
+  if (pages && !(G <= 16 && (G & (G - 1)) == 0)) return hipErrorInvalidValue;
   if (G <= 16 && (G & (G - 1)) == 0) {
     FlashArgs f;
     f.k = reinterpret_cast<const uint8_t*>(kv.k);
@@ -559,8 +585,16 @@ hipError_t launch_attn_prefill(const qkdec_kv_layer& kv, const int32_t* slot, co
     f.h4 = G < 4 ? G : 4;
     f.scale_log2 = scale * 1.4426950408889634f;
     f.O16 = reinterpret_cast<half_t*>(O16);
+    f.pages = pages;
+    f.max_pages = pages ? max_pages : 0;
+    f.page_shift = 0;
+    while (pages && (1 << f.page_shift) < kv.capacity) ++f.page_shift;
     const dim3 grid((unsigned)((B + 64 / f.h4 - 1) / (64 / f.h4)), kv.n_kv_heads, G / f.h4);
-#define QK_FA(DD, KF, VF) hipLaunchKernelGGL((attn_prefill_kernel<DD, KF, VF>), grid, dim3(256), 0, st, f)
+#define QK_FA(DD, KF, VF)                                                                                     \
+  do {                                                                                                        \
+    if (pages) hipLaunchKernelGGL((attn_prefill_kernel<DD, KF, VF, true>), grid, dim3(256), 0, st, f);      \
+    else hipLaunchKernelGGL((attn_prefill_kernel<DD, KF, VF, false>), grid, dim3(256), 0, st, f);           \
+  } while (0)
 #define QK_FA_D(DD)                                                      \
   do {                                                                   \
     if (kf == kFmtF8) QK_FA(DD, kFmtF8, kFmtF8);                         \

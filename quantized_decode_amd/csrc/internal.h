@@ -188,9 +188,12 @@ hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, con
 int attn_prefill_splits(int B, int n_q_heads, const qkdec_kv_layer& kv);
 // Partial-result bytes for any call of 1 .. max_rows rows.
 size_t attn_prefill_partials_bytes(int max_rows, int n_q_heads, const qkdec_kv_layer& kv);
+// pages != NULL: kv is a paged pool (pages of kv.capacity tokens, a power of
+// two) and the sequence's page table row is pages[0 .. max_pages - 1]; slot is
+// unused, and G must be a power of two (hipErrorInvalidValue otherwise).
 hipError_t launch_attn_prefill(const qkdec_kv_layer& kv, const int32_t* slot, const int32_t* n_ctx, int B,
                                const uint16_t* Q, int n_q_heads, float scale, uint16_t* O16, float* partials,
-                               int n_ctx_add, hipStream_t st);
+                               int n_ctx_add, hipStream_t st, const int32_t* pages = nullptr, int max_pages = 0);
 
 // ---- KV append and RoPE (kv_append.hip)
 // RoPE of q and k, q -> fp16 and the KV append, from the fp32 QKV rows Y
@@ -229,6 +232,11 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 // tok[b] = tokens[b] for b < rows (tokens: device int32)
 hipError_t launch_prefill_rows(int s, int start, const int32_t* tokens, int rows, int32_t* slot, int32_t* pos,
                                int32_t* tok, hipStream_t st);
+// the same for one sequence in a paged pool: page[b] (-1 outside the table or
+// the pool of n_pages pages), pos[b] = start + b, page_pos[b] within the page
+hipError_t launch_prefill_page_rows(const int32_t* pages, int max_pages, int page_tokens, int n_pages, int start,
+                                    const int32_t* tokens, int rows, int32_t* page, int32_t* pos, int32_t* page_pos,
+                                    int32_t* tok, hipStream_t st);
 
 // ---- prompt ingestion (prefill.hip): chunks of up to kPfRows prompt tokens
 // of one sequence.  A projection is gemm_pf (partial sums of ksplit K ranges,

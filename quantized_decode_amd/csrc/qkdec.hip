@@ -263,7 +263,8 @@ struct PrefillWs {
   float* attn_part;
   float2* rope;
   void* lm_part;
-  int32_t *rs, *rp, *rt;   // the chunk's slot, position and token of each row
+  int32_t *rs, *rp, *rt;   // the chunk's slot (paged: page), position and token of each row
+  int32_t* rsp;            // paged: each row's position within its page
   size_t bytes;
 };
 
@@ -303,14 +304,18 @@ PrefillWs prefill_layout(const qkdec_model* m, const qkdec_kv_layer* kv, char* b
   w.rs = reinterpret_cast<int32_t*>(take(R * 4));
   w.rp = reinterpret_cast<int32_t*>(take(R * 4));
   w.rt = reinterpret_cast<int32_t*>(take(R * 4));
+  w.rsp = reinterpret_cast<int32_t*>(take(R * 4));
   w.bytes = off;
   return w;
 }
 
 size_t prefill_bytes(const qkdec_model* m, const qkdec_kv_layer* kv) { return prefill_layout(m, kv, nullptr).bytes; }
 
+// pages != nullptr: every layer of kv is a paged pool and the sequence's page
+// table row is pages[0 .. max_pages - 1]; slot is unused
 qkdec_status run_prefill(const qkdec_model* m, const qkdec_kv_layer* kv, int slot, int start, const int32_t* tokens,
-                         int n, float* logits, int32_t* tok_out, void* workspace, hipStream_t st) {
+                         int n, float* logits, int32_t* tok_out, void* workspace, hipStream_t st,
+                         const int32_t* pages = nullptr, int max_pages = 0) {
   const PrefillWs w = prefill_layout(m, kv, reinterpret_cast<char*>(workspace));
   const int H = m->hidden, F = m->ffn, D = m->head_dim, Hq = m->n_q_heads;
   const int64_t hq = (int64_t)Hq * D;
@@ -326,7 +331,11 @@ qkdec_status run_prefill(const qkdec_model* m, const qkdec_kv_layer* kv, int slo
     rows = n - off < kPfChunk ? n - off : kPfChunk;
     const int ks_qkv = pf_ksplit(nqkv, H, rows), ks_o = pf_ksplit(H, hq, rows),
               ks_gu = pf_ksplit(2 * (int64_t)F, H, rows), ks_dn = pf_ksplit(H, F, rows);
-    QK_TRY(launch_prefill_rows(slot, start + off, tokens + off, rows, w.rs, w.rp, w.rt, st));
+    if (pages)
+      QK_TRY(launch_prefill_page_rows(pages, max_pages, kv[0].capacity, kv[0].n_slots, start + off, tokens + off, rows,
+                                      w.rs, w.rp, w.rsp, w.rt, st));
+    else
+      QK_TRY(launch_prefill_rows(slot, start + off, tokens + off, rows, w.rs, w.rp, w.rt, st));
     QK_TRY(launch_rope_table(w.rp, rows, D, m->rope_base, w.rope, st));
     QK_TRY(launch_embed(m->embed, H, m->vocab, w.rt, rows, w.x, w.ss, st));
     // the first layer's input: RMSNorm of the embedding rows
@@ -342,9 +351,10 @@ qkdec_status run_prefill(const qkdec_model* m, const qkdec_kv_layer* kv, int slo
                                 nullptr, st));
         qkv = w.qkv;
       }
-      QK_TRY(launch_rope_append(kv[l], qkv, nqkv, Hq, rows, w.rs, w.rp, m->rope_base, w.q16, w.err, st, w.rp,
-                                w.rope));
-      QK_TRY(launch_attn_prefill(kv[l], w.rs, w.rp, rows, w.q16, Hq, scale, w.o16, w.attn_part, 1, st));
+      QK_TRY(launch_rope_append(kv[l], qkv, nqkv, Hq, rows, w.rs, w.rp, m->rope_base, w.q16, w.err, st,
+                                pages ? w.rsp : w.rp, w.rope));
+      QK_TRY(launch_attn_prefill(kv[l], w.rs, w.rp, rows, w.q16, Hq, scale, w.o16, w.attn_part, 1, st, pages,
+                                 max_pages));
       QK_TRY(launch_pf_norm(nullptr, nullptr, nullptr, 0.f, (int)hq, rows, w.o16, w.xs, w.fd, st));
       QK_TRY(launch_gemm_pf(ly.w_o, H, hq, w.o16, hq, w.xs, nullptr, rows, w.part, ks_o, st));
       QK_TRY(launch_pf_finish(w.part, ks_o, rows, H, w.x, w.x, H, kPfNorm, w.ssq, nullptr, nullptr, nullptr, st));
@@ -747,6 +757,32 @@ qkdec_status qkdec_prefill(const qkdec_model* m, const qkdec_kv_layer* kv, int32
   if (s != QKDEC_OK) return s;
   clear_stale_error();
   return run_prefill(m, kv, slot, start, tokens, n, logits, tok_out, workspace, as_stream(stream));
+}
+
+size_t qkdec_prefill_paged_workspace_size(const qkdec_model* m, const qkdec_kv_layer* kv) {
+  return qkdec_prefill_workspace_size(m, kv);
+}
+
+qkdec_status qkdec_prefill_paged(const qkdec_model* m, const qkdec_kv_layer* kv, const int32_t* pages,
+                                 int32_t max_pages, int32_t start, const int32_t* tokens, int32_t n, float* logits,
+                                 int32_t* tok_out, void* workspace, size_t ws_bytes, void* stream) {
+  qkdec_status s = check_model(m, kv);
+  if (s != QKDEC_OK) return s;
+  for (int l = 0; l < m->n_layers; ++l) {
+    s = check_pages(&kv[l], pages, max_pages);
+    if (s != QKDEC_OK) return s;
+  }
+  const int G = m->n_q_heads / m->n_kv_heads;
+  if (G & (G - 1)) return QKDEC_E_SHAPE;   // the paged prompt attention takes G a power of two
+  if (!tokens || !tok_out) return QKDEC_E_ARG;
+  if (n < 1 || start < 0) return QKDEC_E_SHAPE;
+  if ((int64_t)start + n > (int64_t)max_pages * kv[0].capacity) return QKDEC_E_CAPACITY;
+  if (!workspace || ws_bytes < prefill_bytes(m, kv)) return QKDEC_E_WORKSPACE;
+  if (!aligned(workspace, 256)) return QKDEC_E_ALIGN;
+  s = check_lds(lm_head_lds_bytes(m->hidden, 1));
+  if (s != QKDEC_OK) return s;
+  clear_stale_error();
+  return run_prefill(m, kv, 0, start, tokens, n, logits, tok_out, workspace, as_stream(stream), pages, max_pages);
 }
 
 qkdec_status qkdec_step_status(void* workspace, void* stream) {

@@ -208,6 +208,34 @@ hipError_t launch_prefill_rows(int s, int start, const int32_t* tokens, int rows
   return hipGetLastError();
 }
 
+// the rows of one prefill chunk of a sequence in a paged pool (page table
+// row `pages`, max_pages entries, pages of 2^page_shift tokens): pos[b] =
+// start + b, page[b] = the page holding it (-1 outside the table or the
+// pool), page_pos[b] = its position in the page, tok[b] = tokens[b]
+__global__ void prefill_page_rows_kernel(const int32_t* pages, int max_pages, int page_shift, int n_pages, int start,
+                                         const int32_t* tokens, int rows, int32_t* page, int32_t* pos,
+                                         int32_t* page_pos, int32_t* tok) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= rows) return;
+  const int p = start + b;
+  const int pi = p >> page_shift;
+  const int pg = pi < max_pages ? pages[pi] : -1;
+  page[b] = (pg >= 0 && pg < n_pages) ? pg : -1;
+  pos[b] = p;
+  page_pos[b] = p & ((1 << page_shift) - 1);
+  tok[b] = tokens[b];
+}
+
+hipError_t launch_prefill_page_rows(const int32_t* pages, int max_pages, int page_tokens, int n_pages, int start,
+                                    const int32_t* tokens, int rows, int32_t* page, int32_t* pos, int32_t* page_pos,
+                                    int32_t* tok, hipStream_t st) {
+  int shift = 0;
+  while ((1 << shift) < page_tokens) ++shift;
+  hipLaunchKernelGGL(prefill_page_rows_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, pages, max_pages, shift,
+                     n_pages, start, tokens, rows, page, pos, page_pos, tok);
+  return hipGetLastError();
+}
+
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
   const size_t words = bytes / 4;
   if (words == 0) return hipSuccess;

@@ -125,6 +125,7 @@ static void model_shapes() {
       *f[field] = val;
       (void)qkdec_step_workspace_size(&t.m, 8, t.kv.data());
       (void)qkdec_prefill_workspace_size(&t.m, t.kv.data());
+      (void)qkdec_prefill_paged_workspace_size(&t.m, t.kv.data());
       (void)qkdec_step_paged_workspace_size(&t.m, 8, t.kv.data(), 16);
       qkdec_step_views tv{};
       (void)qkdec_step_workspace_views(&t.m, 8, t.kv.data(), &tv);
@@ -219,6 +220,14 @@ static void rejected_calls() {
                           nullptr, dev_i32, dev_ws, fws, nullptr),
             QKDEC_E_CAPACITY);
   EXPECT_EQ(qkdec_prefill(m, kv, 0, 0, dev_i32, 16, nullptr, dev_i32, dev_ws, fws - 1, nullptr), QKDEC_E_WORKSPACE);
+  // prefill into a paged pool (this cache's 2432-token slots are not a page size)
+  EXPECT_EQ(qkdec_prefill_paged(m, kv, nullptr, 16, 0, dev_i32, 16, nullptr, dev_i32, dev_ws, fws, nullptr),
+            QKDEC_E_ARG);
+  EXPECT_EQ(qkdec_prefill_paged(m, kv, dev_i32, 16, 0, dev_i32, 16, nullptr, dev_i32, dev_ws, fws, nullptr),
+            QKDEC_E_SHAPE);
+  EXPECT_EQ(qkdec_prefill_paged(m, kv, dev_i32, std::numeric_limits<int32_t>::max(), 0, dev_i32, 16, nullptr,
+                                dev_i32, dev_ws, fws, nullptr),
+            QKDEC_E_SHAPE);
   // the step on the library's fixed scratch
   EXPECT_EQ(qkdec_step_noalloc(m, kv, dev_i32, dev_i32, dev_i32, 8, dev_f32, nullptr, nullptr), QKDEC_E_ARG);
   EXPECT_EQ(qkdec_step_noalloc(m, kv, dev_i32, dev_i32, dev_i32, 17, dev_f32, dev_i32, nullptr), QKDEC_E_SHAPE);

@@ -222,3 +222,30 @@ def test_prefill_validation(lib):
     assert pf(ctypes.byref(m), kvs, 0, 250, FAKE, 7, None, FAKE, FAKE, need, None) == -5    # past capacity
     assert pf(ctypes.byref(m), kvs, 0, 0, FAKE, 4, None, FAKE, FAKE, need - 1, None) == -4
     assert pf(ctypes.byref(m), kvs, 0, 0, FAKE, 4, None, FAKE, FAKE + 16, need, None) == -3
+
+
+def test_prefill_paged_validation(lib):
+    # pool page size a power of two, a page table, start + n within max_pages
+    # pages, query heads per KV head a power of two; all before any launch
+    layers = (qd.Layer * 2)(qd.Layer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE), qd.Layer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE))
+    m = qd.Model(2, 512, 8, 2, 64, 1536, 4096, 1e-6, 1e6, FAKE, FAKE, FAKE, ctypes.cast(layers, ctypes.POINTER(qd.Layer)))
+    pools = (qd.KVLayer * 2)(_kv(n_kv_heads=2, head_dim=64, capacity=64, n_slots=32),
+                              _kv(n_kv_heads=2, head_dim=64, capacity=64, n_slots=32))
+    need = lib.qkdec_prefill_paged_workspace_size(ctypes.byref(m), pools)
+    assert need > 0
+    pf = lib.qkdec_prefill_paged
+    assert pf(ctypes.byref(m), pools, None, 4, 0, FAKE, 4, None, FAKE, FAKE, need, None) == -1     # no table
+    assert pf(ctypes.byref(m), pools, FAKE, 0, 0, FAKE, 4, None, FAKE, FAKE, need, None) == -2     # max_pages
+    assert pf(ctypes.byref(m), pools, FAKE, 4, 0, None, 4, None, FAKE, FAKE, need, None) == -1     # no tokens
+    assert pf(ctypes.byref(m), pools, FAKE, 4, 0, FAKE, 0, None, FAKE, FAKE, need, None) == -2     # empty prompt
+    assert pf(ctypes.byref(m), pools, FAKE, 4, 250, FAKE, 7, None, FAKE, FAKE, need, None) == -5   # past 4 pages
+    assert pf(ctypes.byref(m), pools, FAKE, 4, 0, FAKE, 4, None, FAKE, FAKE, need - 1, None) == -4
+    assert pf(ctypes.byref(m), pools, FAKE + 2, 4, 0, FAKE, 4, None, FAKE, FAKE, need, None) == -3
+    odd = (qd.KVLayer * 2)(_kv(n_kv_heads=2, head_dim=64, capacity=96, n_slots=32),
+                            _kv(n_kv_heads=2, head_dim=64, capacity=96, n_slots=32))
+    assert pf(ctypes.byref(m), odd, FAKE, 4, 0, FAKE, 4, None, FAKE, FAKE, need, None) == -2      # page size
+    m3 = qd.Model(2, 512, 12, 4, 64, 1536, 4096, 1e-6, 1e6, FAKE, FAKE, FAKE,
+                  ctypes.cast(layers, ctypes.POINTER(qd.Layer)))
+    p3 = (qd.KVLayer * 2)(_kv(n_kv_heads=4, head_dim=64, capacity=64, n_slots=32),
+                           _kv(n_kv_heads=4, head_dim=64, capacity=64, n_slots=32))
+    assert pf(ctypes.byref(m3), p3, FAKE, 4, 0, FAKE, 4, None, FAKE, FAKE, need, None) == -2      # G = 3

@@ -144,3 +144,94 @@ def test_prefill_two_passes_equals_decode_steps(qd, kind):
     # tokens takes minutes; the decode step it is checked against is itself
     # checked against the oracle)
     _vs_decode_steps(qd, synth.TOY, kind, 40, 1100, 1770)
+
+
+@pytest.mark.parametrize("kind,P", [("f16", 32), ("q8_0", 64), ("fp8", 32)])
+def test_prefill_paged_equals_arena(qd, kind, P):
+    # the toy decoder, 100 prompt tokens after 20 cached ones, into slot 1 of
+    # a slot arena and into the same sequence's pages scattered over a pool
+    # (max_pages * P = the arena's capacity): the same kernels on the same
+    # values, so the logits, the token and every byte of the sequence's
+    # cache must be identical
+    import torch
+    from quantized_decode_amd.tensors import dev, upload_cache
+    from tests.test_gpu_paged import _pool_from
+    dims = synth.TOY
+    model = synth.make_model(dims, 1780)
+    st = synth.Streams(1781)
+    cap, lens, b, n = 192, [30, 20, 50], 1, 100
+    caches = [synth.kv_cache(kind, st.next(), st.next(), 3, dims.n_kv_heads, cap, dims.head_dim, lens)
+              for _ in model.layers]
+    prompt = synth.tokens(st.next(), n, dims.vocab)
+    lg, tok, kv, (sm, w, embed, lm_head, norm, layers) = _prefill(qd, model, caches, b, lens[b], prompt)
+    n_pages = sum((x + n + P - 1) // P for x in lens) + 6
+    pools, table = [], None
+    for c in caches:   # the same rng per layer: one page table for all layers
+        pool, t, _ = _pool_from(c, lens, P, n_pages, np.random.default_rng(7), room=n)
+        assert table is None or np.array_equal(t, table)
+        pools.append(pool)
+        table = t
+    max_pages = cap // P
+    table = np.pad(table, ((0, 0), (0, max_pages - table.shape[1])), constant_values=-1)
+    dpools = [upload_cache(p) for p in pools]
+    smp = qd.StepModel(dims, embed, lm_head, norm, layers, [d.desc for d in dpools])
+    wp = ws(qd.qkdec_prefill_paged_workspace_size(smp))
+    qd.qkdec_workspace_init(wp)
+    logits = torch.empty(dims.vocab, dtype=torch.float32, device="cuda")
+    tk = torch.zeros(1, dtype=torch.int32, device="cuda")
+    qd.qkdec_prefill_paged(smp, dev(np.ascontiguousarray(table[b])), max_pages, lens[b],
+                           dev(np.asarray(prompt, np.int32)), n, tk, wp, logits=logits)
+    sync()
+    assert qd.qkdec_step_status(wp) == 0
+    assert np.array_equal(logits.cpu().numpy().view(np.uint32), lg.view(np.uint32))
+    assert int(tk.item()) == tok
+    end = lens[b] + n
+    for li, (dp, da) in enumerate(zip(dpools, kv)):
+        gp, ga = dp.logical(), da.logical()
+        for name, arr in vars(ga).items():
+            if arr is None:
+                continue
+            parr = getattr(gp, name)
+            for j in range((end + P - 1) // P):
+                take = min(P, end - j * P)
+                assert np.array_equal(parr[table[b, j], :, :take].view(np.uint8),
+                                      arr[b, :, j * P:j * P + take].view(np.uint8)), (li, name, j)
+
+
+def test_prefill_paged_unmapped_page_flags_capacity(qd):
+    # a page table entry of -1 inside the prompt: its tokens are not stored,
+    # the error word says QKDEC_E_CAPACITY, and no other page changes
+    import torch
+    from quantized_decode_amd.tensors import dev, upload_cache, upload_model
+    from tests.test_gpu_paged import _pool_from
+    dims = synth.TOY
+    model = synth.make_model(dims, 1790)
+    st = synth.Streams(1791)
+    P, cap, lens, n = 32, 128, [40], 60
+    caches = [synth.kv_cache("f16", st.next(), st.next(), 1, dims.n_kv_heads, cap, dims.head_dim, lens)
+              for _ in model.layers]
+    pools, table = [], None
+    for c in caches:
+        pool, t, _ = _pool_from(c, lens, P, 8, np.random.default_rng(11), room=n)
+        pools.append(pool)
+        table = t
+    table = np.pad(table, ((0, 0), (0, cap // P - table.shape[1])), constant_values=-1)
+    row = table[0].copy()
+    lost = row[2]
+    row[2] = -1   # positions 64..95 of the prompt's range have no page
+    dpools = [upload_cache(p) for p in pools]
+    embed, lm_head, norm, layers = upload_model(model)
+    smp = qd.StepModel(dims, embed, lm_head, norm, layers, [d.desc for d in dpools])
+    wp = ws(qd.qkdec_prefill_paged_workspace_size(smp))
+    qd.qkdec_workspace_init(wp)
+    tk = torch.zeros(1, dtype=torch.int32, device="cuda")
+    qd.qkdec_prefill_paged(smp, dev(row), cap // P, lens[0], dev(np.asarray(synth.tokens(st.next(), n, dims.vocab),
+                                                                              np.int32)), n, tk, wp)
+    sync()
+    assert qd.qkdec_step_status(wp) == -5   # QKDEC_E_CAPACITY
+    for dp, was in zip(dpools, pools):
+        got = dp.logical()
+        for name, arr in vars(was).items():
+            if arr is None:
+                continue
+            assert np.array_equal(getattr(got, name)[lost].view(np.uint8), arr[lost].view(np.uint8)), name
