@@ -461,10 +461,10 @@ def prefill_point(qd, sd, dims, dev_model, n_prompt, seed, kind="f16"):
         if i:
             times.append(a.elapsed_time(b))
     ms = sorted(times)[1]
-    wbytes = W_BYTES * ((n_prompt + 1023) // 1024)
+    wbytes = W_BYTES * ((n_prompt + 2047) // 2048)
     del kvs, keep
     return {"prompt_tokens": n_prompt, "kv": kind, "ms": ms, "tok_per_s": n_prompt / (ms * 1e-3),
-            "weight_bytes_read": wbytes, "note": "passes of up to 1024 prompt tokens through the layers: MFMA "
+            "weight_bytes_read": wbytes, "note": "passes of up to 2048 prompt tokens through the layers: MFMA "
                                                   "projections over 64-row tiles, the split-K attention with 4 "
                                                   "prompt rows per work item (256 rows per call); LM head for the "
                                                   "last token"}

@@ -369,7 +369,7 @@ qkdec_status qkdec_step_paged(const qkdec_model* m, const qkdec_kv_layer* kv, co
  * head and argmax run for the last token only: logits fp32 [vocab] (may be
  * NULL) and tok_out (device int32 [1]) = its argmax, the first generated
  * token.  Positions before start must already be cached.  The prompt is taken
- * in chunks of 1024 tokens, each chunk one pass of the layers with its
+ * in chunks of 2048 tokens, each chunk one pass of the layers with its
  * tokens as the rows: the projections are matrix-core products over 64-row
  * tiles (each weight read once per chunk and tile, RMSNorm and SwiGLU between
  * them in the decode step's rounding); the attention is a flash kernel for

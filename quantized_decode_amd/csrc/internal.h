@@ -244,7 +244,7 @@ hipError_t launch_prefill_page_rows(const int32_t* pages, int max_pages, int pag
 // comes with its 32-value sub-block sums / 32, xs [T][K/256][4] (half4), and
 // the power-of-two factor fd [T][K/256] of each row super-block (pf_norm: 1,
 // or pf_finish for the SwiGLU output).
-constexpr int kPfChunk = 1024;        // prompt rows per pass of the layers
+constexpr int kPfChunk = 2048;        // prompt rows per pass of the layers
 constexpr int kPfAttnRows = 256;      // prompt rows per attention call
 constexpr int kPfRows = 64;           // prompt rows per GEMM work-group
 constexpr int kPfTilesPerWave = 2;    // weight tiles of 16 rows per wave: 128 rows per work-group

@@ -139,11 +139,11 @@ def test_prefill_full_width_equals_decode_steps(qd, kind):
 
 @pytest.mark.parametrize("kind", ["f16", "q8_0"])
 def test_prefill_two_passes_equals_decode_steps(qd, kind):
-    # the toy decoder, 1100 prompt tokens after 40 cached ones: a pass of 1024
-    # rows of the layers, then one of 76 (the oracle's prefill of this many
+    # the toy decoder, 2100 prompt tokens after 40 cached ones: a pass of 2048
+    # rows of the layers, then one of 52 (the oracle's prefill of this many
     # tokens takes minutes; the decode step it is checked against is itself
     # checked against the oracle)
-    _vs_decode_steps(qd, synth.TOY, kind, 40, 1100, 1770)
+    _vs_decode_steps(qd, synth.TOY, kind, 40, 2100, 1770)
 
 
 @pytest.mark.parametrize("kind,P", [("f16", 32), ("q8_0", 64), ("fp8", 32)])
