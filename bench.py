@@ -465,9 +465,9 @@ def prefill_point(qd, sd, dims, dev_model, n_prompt, seed, kind="f16"):
     del kvs, keep
     return {"prompt_tokens": n_prompt, "kv": kind, "ms": ms, "tok_per_s": n_prompt / (ms * 1e-3),
             "weight_bytes_read": wbytes, "note": "passes of up to 2048 prompt tokens through the layers: MFMA "
-                                                  "projections over 64-row tiles, the split-K attention with 4 "
-                                                  "prompt rows per work item (256 rows per call); LM head for the "
-                                                  "last token"}
+                                                  "projections over 64-row tiles, flash attention over the cache "
+                                                  "(64 query columns per work-group, causal masks); LM head for "
+                                                  "the last token"}
 
 
 def record_traffic(qd, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mb, batch, context, kv, command):
