@@ -146,20 +146,22 @@ def test_prefill_two_passes_equals_decode_steps(qd, kind):
     _vs_decode_steps(qd, synth.TOY, kind, 40, 2100, 1770)
 
 
-@pytest.mark.parametrize("kind,P", [("f16", 32), ("q8_0", 64), ("fp8", 32)])
-def test_prefill_paged_equals_arena(qd, kind, P):
-    # the toy decoder, 100 prompt tokens after 20 cached ones, into slot 1 of
-    # a slot arena and into the same sequence's pages scattered over a pool
+@pytest.mark.parametrize("kind,P,cap,n", [("f16", 32, 192, 100), ("q8_0", 64, 192, 100), ("fp8", 32, 192, 100),
+                                          ("f16", 256, 2304, 2100), ("q8_0", 128, 2304, 2100)])
+def test_prefill_paged_equals_arena(qd, kind, P, cap, n):
+    # the toy decoder, n prompt tokens after 20 cached ones, into slot 1 of a
+    # slot arena and into the same sequence's pages scattered over a pool
     # (max_pages * P = the arena's capacity): the same kernels on the same
     # values, so the logits, the token and every byte of the sequence's
-    # cache must be identical
+    # cache must be identical.  n = 2100 takes two passes of the layers (2048
+    # rows, then 52), the second one's rows on pages the first one filled
     import torch
     from quantized_decode_amd.tensors import dev, upload_cache
     from tests.test_gpu_paged import _pool_from
     dims = synth.TOY
     model = synth.make_model(dims, 1780)
     st = synth.Streams(1781)
-    cap, lens, b, n = 192, [30, 20, 50], 1, 100
+    lens, b = [30, 20, 50], 1
     caches = [synth.kv_cache(kind, st.next(), st.next(), 3, dims.n_kv_heads, cap, dims.head_dim, lens)
               for _ in model.layers]
     prompt = synth.tokens(st.next(), n, dims.vocab)
