@@ -249,7 +249,7 @@ hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, con
   a.tok = 1;
   a.nrows = B;
   a.n_splits = attn_max_runs(a.seq_cap, kv.n_kv_heads);
-  a.runs_wanted = attn_runs_wanted(B, kv.n_kv_heads, kv_k_q8(kv.type) || kv_v_q8(kv.type));
+  a.runs_wanted = attn_runs_wanted(B, kv.n_kv_heads);
   const int D = kv.head_dim;
   const size_t n_rows = (size_t)B * n_q_heads * a.n_splits;
   a.part_o = partials;
@@ -311,8 +311,8 @@ int attn_prefill_splits(int B, int n_q_heads, const qkdec_kv_layer& kv) {
   if (tok == 1) return attn_max_runs(kv.capacity, kv.n_kv_heads);
   const int groups = (B + tok - 1) / tok;
   const int by_len = (int)(((int64_t)kv.capacity + kAttnChunk - 1) / kAttnChunk);
-  const int wanted = attn_runs_wanted(groups, kv.n_kv_heads, kv_k_q8(kv.type) || kv_v_q8(kv.type));
-  return by_len > wanted ? by_len : wanted;
+  const int wanted = attn_runs_wanted(groups, kv.n_kv_heads);
+  return (by_len + wanted - 1) / wanted * wanted;   // the most attn_runs gives (by_len >= 1)
 }
 
 size_t attn_prefill_partials_bytes(int max_rows, int n_q_heads, const qkdec_kv_layer& kv) {
@@ -645,7 +645,7 @@ hipError_t launch_attn_prefill(const qkdec_kv_layer& kv, const int32_t* slot, co
   a.tok = tok;
   a.nrows = B;
   a.n_splits = attn_prefill_splits(B, n_q_heads, kv);
-  a.runs_wanted = attn_runs_wanted(groups, kv.n_kv_heads, kv_k_q8(kv.type) || kv_v_q8(kv.type));
+  a.runs_wanted = attn_runs_wanted(groups, kv.n_kv_heads);
   const int D = kv.head_dim;
   const size_t n_rows = (size_t)B * n_q_heads * a.n_splits;
   a.part_o = partials;

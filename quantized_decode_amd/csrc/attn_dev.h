@@ -108,16 +108,17 @@ struct AttnArgs {
 };
 
 // Runs of a sequence with n cached tokens (same in the split and merge
-// kernels): the wanted count, at least ceil(n / 1024), at most one per 8
-// tiles and at most max_runs; 0 for n <= 0.
+// kernels): ceil(n / 1024) rounded up to a multiple of the wanted count, at
+// most one per 8 tiles but never fewer than ceil(n / 1024), and at most
+// max_runs; 0 for n <= 0.
 __host__ __device__ __forceinline__ int attn_runs(int n, int wanted, int max_runs) {
   if (n <= 0) return 0;
   const int tiles = (n + 31) / 32;
-  int r = (n + 1023) / 1024;
-  if (wanted > r) r = wanted;
+  const int need = (n + 1023) / 1024;   // never more than 1024 tokens per run
+  int r = (need + wanted - 1) / wanted * wanted;
   const int by_tiles = tiles / 8 > 1 ? tiles / 8 : 1;
   if (r > by_tiles) r = by_tiles;
-  if (r < (n + 1023) / 1024) r = (n + 1023) / 1024;   // never more than 1024 tokens per run
+  if (r < need) r = need;
   if (r > max_runs) r = max_runs;
   return r;
 }

@@ -116,32 +116,38 @@ inline bool kv_v_q8(int type) { return kv_v_fmt(type) == kFmtQ8; }
 
 // ---- attention (attn_decode.hip)
 // A sequence's n cached tokens (ceil(n/32) tiles of 32) are cut into runs of
-// whole tiles, spread evenly, one work item each.  Runs per sequence: enough
-// that the B * n_kv * runs work items reach the target (fp16 and E4M3 caches:
-// 256, one per CU of MI355X; any Q8_0 tensor: 512, its dequantizing tiles
-// gaining from a second work-group per CU; the kernels run two waves per
-// SIMD), at least
-// ceil(n / kAttnChunk) (long contexts), at most one per 8 tiles (4 waves of 2
-// tiles at least) and at most attn_max_runs (the partial-result stride).
+// whole tiles, spread evenly, one work item each.  Runs per sequence: the
+// count w that makes the B * n_kv * w work items reach kAttnTarget (one per
+// CU of MI355X), or, when n needs more than w runs of at most kAttnChunk
+// tokens, the next multiple of w, so that a uniform batch's work items fill
+// whole rounds of the chip (B = 8, n_kv = 8: 4, 8, 12, ... runs; 7 runs for
+// L = 6900 would leave a round three quarters full); at most one run per 8
+// tiles (4 waves of 2 tiles at least), never fewer than ceil(n /
+// kAttnChunk), and at most attn_max_runs (the partial-result stride).
 // kAttnChunk = 1024: longer-lived waves were faster than 256 or 512 tokens
 // per run at B = 8, L = 2400.
 constexpr int kAttnChunk = 1024;
-constexpr int kAttnTargetF16 = 256;
-constexpr int kAttnTargetQ8 = 512;
-// partial-result rows per (b, q head): independent of B and of the cache
-// type, so a workspace sized for one batch serves any smaller one
-// (capacity: most tokens of one sequence, at most 2^31 - 1; n_kv >= 1)
-inline int attn_max_runs(int64_t capacity, int n_kv) {
-  const int64_t by_len = (capacity + kAttnChunk - 1) / kAttnChunk;
-  const int64_t by_fill = (kAttnTargetQ8 + (int64_t)n_kv - 1) / n_kv;
-  return (int)(by_len > by_fill ? by_len : by_fill);
-}
+constexpr int kAttnTarget = 256;
+constexpr int kAttnMaxBatch = 16;   // most sequences of a decode attention call
 // runs wanted per sequence for a call with B sequences (before the per-
-// sequence limits)
-inline int attn_runs_wanted(int B, int n_kv, bool q8) {
-  const int target = q8 ? kAttnTargetQ8 : kAttnTargetF16;
-  const int w = (target + B * n_kv - 1) / (B * n_kv);
+// sequence rounding and limits)
+inline int attn_runs_wanted(int B, int n_kv) {
+  const int w = (kAttnTarget + B * n_kv - 1) / (B * n_kv);
   return w > 1 ? w : 1;
+}
+// partial-result rows per (b, q head): the most runs any call of 1 ..
+// kAttnMaxBatch sequences gives a sequence of this capacity, so a workspace
+// sized for one batch serves any smaller one (capacity: most tokens of one
+// sequence, at most 2^31 - 1; n_kv >= 1)
+inline int attn_max_runs(int64_t capacity, int n_kv) {
+  const int by_len = (int)((capacity + kAttnChunk - 1) / kAttnChunk);
+  int most = by_len;
+  for (int B = 1; B <= kAttnMaxBatch; ++B) {
+    const int w = attn_runs_wanted(B, n_kv);
+    const int r = (by_len + w - 1) / w * w;
+    most = r > most ? r : most;
+  }
+  return most;
 }
 // partial results per (b, q head, run): m, l, then head_dim values of o
 inline size_t attn_partials_bytes(int B, int n_q_heads, int head_dim, int64_t capacity, int n_kv) {

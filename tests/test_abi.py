@@ -115,8 +115,9 @@ def test_kv_and_attention_validation(lib):
     att = lib.qkdec_attn_decode
     kv = _kv()
     need = lib.qkdec_attn_workspace_size(8, 32, ctypes.byref(kv))
-    # rows for up to max(ceil(2432 / 1024), 512 / 8) = 64 runs per (sequence, head)
-    assert need == 8 * 32 * 64 * 130 * 4
+    # rows for up to 32 runs per (sequence, head): ceil(2432 / 1024) = 3 rounded
+    # up to a multiple of the runs one sequence takes when alone (256 / 8)
+    assert need == 8 * 32 * 32 * 130 * 4
     assert att(ctypes.byref(kv), FAKE, FAKE, 8, FAKE, 30, 0.1, FAKE, None, FAKE, need, None) == -2   # 30 % 8
     assert att(ctypes.byref(kv), FAKE, FAKE, 8, FAKE, 256, 0.1, FAKE, None, FAKE, need, None) == -2  # group 32
     assert att(ctypes.byref(kv), FAKE, FAKE, 17, FAKE, 32, 0.1, FAKE, None, FAKE, need, None) == -2
@@ -170,8 +171,9 @@ def test_paged_validation(lib):
     att, app = lib.qkdec_attn_decode_paged, lib.qkdec_kv_append_paged
     pool = _kv(capacity=256, n_slots=64)
     need = lib.qkdec_attn_paged_workspace_size(8, 32, ctypes.byref(pool), 16)
-    # rows for up to max(ceil(16 * 256 / 1024), 512 / 8) = 64 runs per (sequence, head)
-    assert need == 8 * 32 * 64 * 130 * 4
+    # rows for up to 32 runs per (sequence, head): ceil(16 * 256 / 1024) = 4
+    # rounded up to a multiple of 256 / 8
+    assert need == 8 * 32 * 32 * 130 * 4
     assert lib.qkdec_attn_paged_workspace_size(8, 32, ctypes.byref(pool), 0) == 0
     assert att(ctypes.byref(_kv(capacity=96)), FAKE, 4, FAKE, 8, FAKE, 32, 0.1, FAKE, None, FAKE, need, None) == -2
     assert att(ctypes.byref(pool), None, 4, FAKE, 8, FAKE, 32, 0.1, FAKE, None, FAKE, need, None) == -1
