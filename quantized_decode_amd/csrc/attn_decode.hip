@@ -44,6 +44,7 @@
 #include "attn_dev.h"
 #include "common.h"
 #include "internal.h"
+#include "kv_dev.h"
 
 namespace qk {
 
@@ -136,6 +137,26 @@ __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs
   st.l = 0.f;
   st.ex = 127;
 
+  // The new token of a decode step with a Q8_0 part (kv_new): its 32-dim
+  // blocks were split over two work-groups of the QKV projection, so the
+  // sequence's last run quantizes it here.  The tile loop leaves the token
+  // out (its cache bytes are not written yet); after its tiles the last wave,
+  // which has the fewest, reads the staged fp32 key and value, forms them
+  // (the appends' Q8_0 arithmetic, or fp16 rounding for an fp16 part),
+  // stores the Q8_0 codes and scales into the cache and adds the token to its
+  // state.  (Its load is issued only then: a load issued before the loop on
+  // one wave's path alone makes the compiler wait for every tile load.)
+  constexpr bool kStage = !MULTI && (KF == kFmtQ8 || VF == kFmtQ8);
+  constexpr int kSubWave = kAttnWaves - 1;
+  __shared__ float s_new[kStage ? 2 * D : 1];   // k, then v
+  bool sub = false;
+  size_t nrow0 = 0;
+  int ntt = 0;
+  if constexpr (kStage) {
+    const int tn = a.n_ctx[bl] + a.n_ctx_add - 1;   // its position (n - 1 unless n was clamped)
+    sub = a.kv_new && c == runs - 1 && tn == n - 1 && tile_at(tn, nrow0, ntt);
+  }
+
   // this wave's tiles: wave, wave + 4, ...  The next tile's keys are issued
   // before the current tile is processed, its values once the current tile's
   // softmax is done (two tiles of keys and values are never held at once)
@@ -157,8 +178,9 @@ __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs
           mapped = tile_at(t_begin + 32 * nx, row0, tt);
           load_k(buf[p ^ 1], a, row0, tt, lg, r);
           const int t0 = t_begin + 32 * i;
-          // a tile on an unmapped page has no valid token (every score -inf)
-          const int valid = cur_mapped ? min(32, t_end - t0) : 0;
+          // a tile on an unmapped page has no valid token (every score -inf);
+          // the staged new token (sub: the run's last token) is added later
+          const int valid = cur_mapped ? min(32, t_end - t0) - (sub && t0 + 32 >= t_end ? 1 : 0) : 0;
           if constexpr (MULTI)
             attn_tile<D, KF, VF, true>(st, buf[p], qf, a.scale_log2, valid, lg,
                                        [&]() { load_v(buf[p ^ 1], a, row0, tt, lg, r); },
@@ -175,6 +197,84 @@ __global__ void __launch_bounds__(64 * kAttnWaves, 2) attn_split_kernel(AttnArgs
   for (int i = 0; i < D / 16; ++i) {
     const float un = VF == kFmtQ8 ? exp2i(-st.ex) : exp2i(-kPScale);
     st.o[i][0] *= un; st.o[i][1] *= un; st.o[i][2] *= un; st.o[i][3] *= un;
+  }
+  if constexpr (kStage) {
+    if (sub && wave == kSubWave) {
+      // lane: dims 2 lane, 2 lane + 1 of each part
+      const bool has = 2 * lane < D;
+      float2 xs[2];
+#pragma unroll
+      for (int part = 0; part < 2; ++part)
+        xs[part] = has ? *reinterpret_cast<const float2*>(a.kv_new + (((size_t)b * 2 + part) * a.n_kv + g) * D +
+                                                         2 * lane)
+                       : make_float2(0.f, 0.f);
+      float y[2][2];
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        const float x0 = xs[part].x, x1 = xs[part].y;
+        if ((part == 0 ? KF : VF) == kFmtQ8) {
+          // block maximum over the 16 lanes of one 32-dim block (exact in fp32)
+          float am = fmaxf(fabsf(x0), fabsf(x1));
+#pragma unroll
+          for (int o = 8; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o));
+          int8_t q0, q1;
+          uint16_t db;
+          q8_encode((double)x0, (double)am, q0, db);
+          q8_encode((double)x1, (double)am, q1, db);
+          const float dd = h2f(db);
+          y[part][0] = (float)q0 * dd;
+          y[part][1] = (float)q1 * dd;
+          if (has) {
+            const int d0 = 2 * lane;
+            if (part == 0) {
+              *reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(a.k) + (nrow0 + ntt) * D + d0) =
+                  (uint16_t)((uint8_t)q0 | ((uint16_t)(uint8_t)q1 << 8));
+              if ((lane & 15) == 0) const_cast<uint16_t*>(a.ks)[(nrow0 + ntt) * (D / 32) + d0 / 32] = db;
+            } else {
+              // values transposed within 32-token blocks ([cap/32][D][32] per head)
+              uint8_t* vc = const_cast<uint8_t*>(a.v) + nrow0 * D;
+              const size_t base = ((size_t)(ntt >> 5) * D + d0) * 32 + (ntt & 31);
+              vc[base] = (uint8_t)q0;
+              vc[base + 32] = (uint8_t)q1;
+              if ((lane & 15) == 0) const_cast<uint16_t*>(a.vs)[(nrow0 + ntt) * (D / 32) + d0 / 32] = db;
+            }
+          }
+        } else {
+          // an fp16 part: the projection stored it; its cached value
+          y[part][0] = h2f(f2h_bits(x0));
+          y[part][1] = h2f(f2h_bits(x1));
+        }
+      }
+      if (has) {
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+          s_new[part * D + 2 * lane] = y[part][0];
+          s_new[part * D + 2 * lane + 1] = y[part][1];
+        }
+      }
+      // its score for this lane's column over this lane's dims of q (the
+      // tile step's layout), summed over the lane groups
+      float sp = 0.f;
+#pragma unroll
+      for (int j = 0; j < D / 32; ++j) {
+        const int d0 = KF == kFmtQ8 ? (32 * j + 8 * lg) : ((D / 4) * lg + 8 * j);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sp = __builtin_fmaf((float)qf[j][k], s_new[d0 + k], sp);
+      }
+      sp += __shfl_xor(sp, 16);
+      sp += __shfl_xor(sp, 32);
+      const float sc = sp * a.scale_log2;
+      const float mnew = fmaxf(st.m, sc);
+      const float co = exp2f(st.m - mnew);   // 0 while the wave saw no token (m = -inf)
+      const float pn = exp2f(sc - mnew);
+      st.l = st.l * co + (lg == 0 ? pn : 0.f);   // one lane group's share carries it
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          st.o[i][rr] = __builtin_fmaf(pn, s_new[D + 16 * i + 4 * lg + rr], st.o[i][rr] * co);
+      st.m = mnew;
+    }
   }
   // merge the four waves' states (same lane layout in every wave) in LDS;
   // a wave without tiles has m = -inf, l = 0, o = 0 and weighs nothing
@@ -226,8 +326,10 @@ __global__ void attn_combine_kernel(const MergeArgs m) { attn_merge_elem(m, bloc
 
 hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, const int32_t* n_ctx, int B,
                               const uint16_t* Q, int n_q_heads, float scale, float* O, uint16_t* O16,
-                              float* partials, int n_ctx_add, hipStream_t st, const int32_t* pages, int max_pages) {
+                              float* partials, int n_ctx_add, hipStream_t st, const int32_t* pages, int max_pages,
+                              const float* kv_new) {
   AttnArgs a;
+  a.kv_new = kv_new;
   a.k = reinterpret_cast<const uint8_t*>(kv.k);
   a.v = reinterpret_cast<const uint8_t*>(kv.v);
   a.ks = reinterpret_cast<const uint16_t*>(kv.k_scale);
@@ -643,6 +745,7 @@ hipError_t launch_attn_prefill(const qkdec_kv_layer& kv, const int32_t* slot, co
   a.page_shift = 0;
   a.seq_cap = kv.capacity;
   a.tok = tok;
+  a.kv_new = nullptr;
   a.nrows = B;
   a.n_splits = attn_prefill_splits(B, n_q_heads, kv);
   a.runs_wanted = attn_runs_wanted(groups, kv.n_kv_heads);

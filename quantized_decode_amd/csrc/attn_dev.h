@@ -105,6 +105,10 @@ struct AttnArgs {
   int seq_cap;       // most tokens a sequence can hold: cap, or max_pages * page size
   // prompt rows (attn_split_kernel MULTI): tok rows per work item, nrows rows
   int tok, nrows;
+  // decode step with a Q8_0 part: the new token's rotated fp32 k and v
+  // ([B][2][n_kv][D], staged by the QKV projection), quantized and stored
+  // into the cache by the sequence's last run; null otherwise
+  const float* kv_new;
 };
 
 // Runs of a sequence with n cached tokens (same in the split and merge

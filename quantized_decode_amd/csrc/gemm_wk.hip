@@ -274,7 +274,7 @@ __global__ void __launch_bounds__(64 * S, wk_waves_per_simd<XMODE>()) gemm_wk_ke
 // MODE 2 finish of gemm_wi_kernel (all waves call it after the partial sums
 // are in LDS): waves 0 and 1 add the partial sums of tiles hj and hj + D/32 of
 // the head, store the fp32 rows, exchange them for the rotation, then store q
-// as fp16 or append k, v to the fp16 cache.
+// as fp16 and append k, v to an fp16 or E4M3 cache, or stage a Q8_0 part.
 template <int S, typename Red>
 __device__ void qkv_finish(const WkArgs& a, Red red, int wave, int lane, int g, int r, int head, int hj,
                            const int (&sl)[4], const int (&ps)[4], const float2* s_rope) {
@@ -322,13 +322,18 @@ __device__ void qkv_finish(const WkArgs& a, Red red, int wave, int lane, int g, 
   c.k = ra.k; c.v = ra.v; c.ks = ra.ks; c.vs = ra.vs;
   c.n_kv = ra.n_kv; c.cap = ra.cap; c.D = D; c.n_slots = ra.n_slots; c.kf = ra.kf; c.vf = ra.vf;
   const int kvh = is_v ? head - ra.Hq - ra.n_kv : head - ra.Hq;
+  // with a Q8_0 part (kv_new set) both parts are staged for the attention
+  // kernel, which quantizes and stores the Q8_0 one (its 32-dim blocks span
+  // two work-groups here); an fp16 part is stored here as well
+  const bool q8 = (is_v ? ra.vf : ra.kf) == kFmtQ8;
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii) {
     const int b = 4 * g + ii;
     if (b >= a.B) continue;
     const bool ok = sl[ii] >= 0 && sl[ii] < ra.n_slots && ps[ii] >= 0 && ps[ii] < ra.cap;
-    if (ok) store_point(c, is_v, sl[ii], kvh, ps[ii], d, out[ii]);
-    else if (r == 0) *ra.err = QKDEC_E_CAPACITY;
+    if (ra.kv_new) ra.kv_new[(((size_t)b * 2 + (is_v ? 1 : 0)) * ra.n_kv + kvh) * D + d] = out[ii];
+    if (ok && !q8) store_point(c, is_v, sl[ii], kvh, ps[ii], d, out[ii]);
+    if (!ok && r == 0) *ra.err = QKDEC_E_CAPACITY;
   }
 }
 
@@ -340,10 +345,11 @@ __device__ void qkv_finish(const WkArgs& a, Red red, int wave, int lane, int g, 
 // wave order and finishes it (no split-K round trips, no workspace).  With
 // IPW items per work-group a launch of ceil(items / IPW) work-groups can be
 // resident on the chip at once.
-// MODE 2 (the QKV projection of a decode step, fp16 cache): a work-group owns
-// tiles j and j + D/32 of one head (dims 16 j + r and 16 j + r + D/2, the
-// rotate-half pairs), so it finishes the head slice itself: the fp32 rows go
-// to Y, q and k are rotated at pos, q is stored as fp16 and k, v are appended.
+// MODE 2 (the QKV projection of a decode step): a work-group owns tiles j and
+// j + D/32 of one head (dims 16 j + r and 16 j + r + D/2, the rotate-half
+// pairs), so it finishes the head slice itself: the fp32 rows go to Y, q and
+// k are rotated at pos, q is stored as fp16 and k, v are appended (fp16 or
+// E4M3) or staged for the attention kernel (Q8_0).
 // KSPLIT > 1 (MODE 0): K is cut into KSPLIT chunks of S KW super-blocks;
 // work-group i takes chunk i / (grid / KSPLIT), and the last of a tile's
 // chunks to arrive adds the chunks' partial sums in chunk order.
@@ -1032,8 +1038,8 @@ hipError_t launch_gemm_wi(const GemmLaunch& L, hipStream_t st) {
 // (head, half-head tile).  hipErrorNotSupported for any other case.
 hipError_t launch_gemm_wi_qkv(const GemmLaunch& L, const RopeAppendArgs& ra, int head_dim, hipStream_t st) {
   const int kb = (int)(L.K / 256);
-  if (kb != 16 || !L.x_f32 || !L.gamma || ra.kf == kFmtQ8 || ra.vf == kFmtQ8 || (head_dim != 64 && head_dim != 128) ||
-      L.residual || L.ss_out || !ra.rope)
+  if (kb != 16 || !L.x_f32 || !L.gamma || ((ra.kf == kFmtQ8 || ra.vf == kFmtQ8) && !ra.kv_new) ||
+      (head_dim != 64 && head_dim != 128) || L.residual || L.ss_out || !ra.rope)
     return hipErrorNotSupported;
   WkArgs a = wk_args(L);
   a.ra = ra;

@@ -72,6 +72,12 @@ struct RopeAppendArgs {
   const float2* rope;
   uint16_t* q16;         // rotated queries, fp16 bits
   int32_t* err;          // set to QKDEC_E_CAPACITY for a position outside the cache
+  // Q8_0 keys or values of a decode step (multi-item QKV projection only):
+  // the rotated fp32 k (part 0) and v (part 1) of the new token go to
+  // kv_new[B][2][n_kv][head_dim] instead of the cache, and the attention
+  // kernel (launch_attn_decode's kv_new) quantizes and stores them; null
+  // otherwise
+  float* kv_new;
 };
 hipError_t launch_gemm_qkv_rope(const GemmLaunch& L, const RopeAppendArgs& ra, int head_dim, hipStream_t st);
 // The same product with K split over the waves of one work-group per output
@@ -177,10 +183,14 @@ struct MergeArgs {
 
 // pages != NULL: kv is a pool of n_slots pages of capacity tokens (a power of
 // two) and sequence b's pages are pages[b * max_pages ...]; slot is unused.
+// kv_new (decode step, a cache with a Q8_0 part, n_ctx_add = 1): the new
+// tokens' rotated k and v staged by the QKV projection (RopeAppendArgs
+// kv_new); each sequence's last run quantizes and stores them and attends to
+// them.  Null: every token is read from the cache.
 hipError_t launch_attn_decode(const qkdec_kv_layer& kv, const int32_t* slot, const int32_t* n_ctx, int B,
                               const uint16_t* Q, int n_q_heads, float scale, float* O, uint16_t* O16,
                               float* partials, int n_ctx_add, hipStream_t st, const int32_t* pages = nullptr,
-                              int max_pages = 0);
+                              int max_pages = 0, const float* kv_new = nullptr);
 // The same attention for B consecutive prompt rows of one sequence (row b:
 // slot[b], n_ctx[b] + n_ctx_add tokens, ascending by one).  An fp16 cache
 // with G a power of two up to 16: flash attention, 64 query columns per

@@ -108,6 +108,7 @@ struct StepWs {
   float2* rope;        // rotary (cos, sin) of each row's position, [B][head_dim/2]
   int32_t* page;       // paged step: page of each sequence's new token (-1: outside)
   int32_t* page_pos;   // and its position within the page
+  float* kv_new;       // a cache with a Q8_0 part: the new token's rotated k, v [B][2][n_kv][head_dim]
   void* lm_part;
   void* gemm_ws;
   size_t bytes;
@@ -136,6 +137,7 @@ StepWs step_layout(const qkdec_model* m, int B, const qkdec_kv_layer* kv, char* 
   w.rope = reinterpret_cast<float2*>(take((size_t)B * (m->head_dim / 2) * sizeof(float2)));
   w.page = reinterpret_cast<int32_t*>(take((size_t)B * 4));
   w.page_pos = reinterpret_cast<int32_t*>(take((size_t)B * 4));
+  w.kv_new = reinterpret_cast<float*>(take((size_t)B * 2 * m->n_kv_heads * m->head_dim * 4));
   w.lm_part = take(lm_head_partials_bytes(m->vocab, B));
   size_t g = gemm_workspace_bytes(nqkv, m->hidden, B, false);
   g = std::max(g, gemm_workspace_bytes(m->hidden, hq, B, false));
@@ -187,11 +189,17 @@ qkdec_status run_layers(const qkdec_model* m, const qkdec_kv_layer* kv, const in
     ra.ks = reinterpret_cast<uint16_t*>(kv[l].k_scale); ra.vs = reinterpret_cast<uint16_t*>(kv[l].v_scale);
     ra.n_kv = kv[l].n_kv_heads; ra.cap = kv[l].capacity; ra.n_slots = kv[l].n_slots; ra.Hq = Hq;
     ra.kf = kv_k_fmt(kv[l].type); ra.vf = kv_v_fmt(kv[l].type); ra.rope_base = m->rope_base; ra.rope = w.rope; ra.q16 = w.q16; ra.err = err_word;
+    const bool q8 = ra.kf == kFmtQ8 || ra.vf == kFmtQ8;
+    ra.kv_new = q8 ? w.kv_new : nullptr;
     // K = 4096: the resident multi-item projection, finishing each head slice
-    // itself (fp16 or E4M3 cache) or followed by RoPE and the append as a small launch
-    // (Q8_0 blocks span two work-groups); otherwise the split-K projection
-    // finishes each head
+    // itself: fp16 and E4M3 parts appended, a Q8_0 part staged for the
+    // attention kernel (its blocks span two work-groups), which quantizes and
+    // appends it.  Otherwise the multi-item projection followed by RoPE and
+    // the append as a small launch, or the split-K projection finishing each
+    // head.
+    const float* kv_new = nullptr;
     hipError_t eq = launch_gemm_wi_qkv(qkv, ra, D, st);
+    if (eq == hipSuccess && q8) kv_new = w.kv_new;
     if (eq == hipErrorNotSupported) {
       eq = launch_gemm_wi(qkv, st);
       if (eq == hipErrorNotSupported) {
@@ -205,7 +213,7 @@ qkdec_status run_layers(const qkdec_model* m, const qkdec_kv_layer* kv, const in
       QK_TRY(eq);
     }
     QK_TRY(launch_attn_decode(kv[l], slot, pos, B, w.q16, Hq, scale, nullptr, w.o16, w.attn_part, 1, st, pages,
-                              max_pages));
+                              max_pages, kv_new));
     // O projection: fp16 activations, K split over the waves of one work-group
     // per output tile (no split-K round trips); the fp32-activation projections
     // stage their activations once per work-group and split K across work-groups
