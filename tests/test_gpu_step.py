@@ -348,3 +348,29 @@ def _stagewise_one_layer(qd, dims, bsz, kind, seed):
     ref = OO.dense_gemm(model.lm_head, vw.h)
     compare_logits(g.logits.cpu().numpy(), ref, g.tok.cpu().numpy(), f"LM head (B={bsz}, {kind})")
     assert (g.pos.cpu().numpy() == pos + 1).all()
+
+
+@pytest.mark.parametrize("kind", ["q8_0", "q8k_f16v", "f16k_q8v"])
+def test_full_width_q8_append_at_capacity_edge(qd, kind):
+    # With a Q8_0 part the QKV projection stages the new token's key and value
+    # and the last run of the attention quantizes and stores them.  One
+    # Qwen-shaped layer, B = 2: sequence 0 appends at the cache's last
+    # position (cap - 1, the last token of the run's last tile), sequence 1
+    # one past it.  Sequence 0 is checked stage by stage against the oracle;
+    # sequence 1 raises the capacity flag and its slot keeps every byte.
+    dims = synth.QWEN_SHAPED
+    bsz, cap = 2, 320
+    model, caches, tok = build(dims, 1611, kind, bsz, cap - 1, cap, n_layers=1)
+    pos = np.array([cap - 1, cap])
+    g = GpuStep(qd, model, caches, bsz, [0, 1])
+    g.set(pos, tok)
+    g.step()
+    assert qd.qkdec_step_status(g.ws) == -5
+    vw = _View(qd, g, dims, bsz)
+    check_layer_stages(dims, kind, model.layers[0], model.embed[tok].astype(np.float64), pos, vw, g.kv[0],
+                       caches[0], [0])
+    got = g.kv[0].logical()
+    for name, arr in vars(caches[0]).items():
+        if arr is None:
+            continue
+        assert np.array_equal(getattr(got, name)[1].view(np.uint8), arr[1].view(np.uint8)), name
