@@ -126,13 +126,15 @@ inline bool kv_v_q8(int type) { return kv_v_fmt(type) == kFmtQ8; }
 // count w that makes the B * n_kv * w work items reach kAttnTarget (one per
 // CU of MI355X), or, when n needs more than w runs of at most kAttnChunk
 // tokens, the next multiple of w, so that a uniform batch's work items fill
-// whole rounds of the chip (B = 8, n_kv = 8: 4, 8, 12, ... runs; 7 runs for
-// L = 6900 would leave a round three quarters full); at most one run per 8
+// whole rounds of the chip (B = 8, n_kv = 8: 4, 8, 12, ... runs; 5 runs
+// would leave the second round three quarters empty); at most one run per 8
 // tiles (4 waves of 2 tiles at least), never fewer than ceil(n /
 // kAttnChunk), and at most attn_max_runs (the partial-result stride).
-// kAttnChunk = 1024: longer-lived waves were faster than 256 or 512 tokens
-// per run at B = 8, L = 2400.
-constexpr int kAttnChunk = 1024;
+// kAttnChunk = 4096: runs of up to 4096 tokens were faster than runs of up to
+// 1024 or 2048 at every long context measured (B = 8 at L = 6900 to 32000,
+// B = 16 at L = 32000) and as fast as 8192 or 16384; below ~4k tokens the
+// limit does not bind at B = 8.
+constexpr int kAttnChunk = 4096;
 constexpr int kAttnTarget = 256;
 constexpr int kAttnMaxBatch = 16;   // most sequences of a decode attention call
 // runs wanted per sequence for a call with B sequences (before the per-

@@ -232,7 +232,7 @@ def test_attention_small_batch_many_runs_nan_workspace(qd, kind, bsz, L):
 @pytest.mark.parametrize("L", [8192, 19000])
 def test_attention_long_context(qd, kind, L):
     # the long-context points of the Q8_0 workload (B = 8 at L = 8192 and
-    # 19000, more than eight runs of up to 1024 tokens per sequence), one
+    # 19000: eight runs per sequence, two rounds of the chip), one
     # Qwen-shaped layer, against the oracle; NaN workspace
     import torch
     from quantized_decode_amd.tensors import dev, upload_cache

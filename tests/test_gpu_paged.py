@@ -172,13 +172,17 @@ def test_paged_append_bit_exact(qd, kind):
             assert np.array_equal(getattr(after, name).view(np.uint8), getattr(got, name).view(np.uint8))
 
 
-def test_paged_attention_full_shape(qd):
-    # B = 8 sequences of a Qwen-shaped layer, ragged contexts, pages of 256
+@pytest.mark.parametrize("P,lens,cap", [
+    (256, [2400, 512, 6900, 1, 3000, 2401, 777, 4096], 7168),
+    # pages of one tile and runs of up to 4096 tokens: up to 129 page entries
+    # staged per run
+    (32, [16384, 9000, 1, 16383, 4097, 12345, 2048, 16000], 16384),
+])
+def test_paged_attention_full_shape(qd, P, lens, cap):
+    # B = 8 sequences of a Qwen-shaped layer, ragged contexts
     from quantized_decode_amd.tensors import upload_cache
-    st = synth.Streams(8400)
-    lens = [2400, 512, 6900, 1, 3000, 2401, 777, 4096]
-    P, hq, hkv, d = 256, 32, 8, 128
-    cap = 7168
+    st = synth.Streams(8400 + P)
+    hq, hkv, d = 32, 8, 128
     cont = synth.kv_cache("f16", st.next(), st.next(), len(lens), hkv, cap, d, lens)
     pool, table, _ = _pool_from(cont, lens, P, sum((n + P - 1) // P for n in lens) + 4, st.next())
     q = synth.f16_normal(st.next(), (len(lens), hq, d))
