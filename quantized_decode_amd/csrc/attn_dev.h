@@ -113,14 +113,14 @@ struct AttnArgs {
 
 // Runs of a sequence with n cached tokens (same in the split and merge
 // kernels): ceil(n / kAttnChunk) rounded up to a multiple of the wanted
-// count, at most one per 8 tiles but never fewer than ceil(n / kAttnChunk),
+// count, at most one per 5 tiles but never fewer than ceil(n / kAttnChunk),
 // and at most max_runs; 0 for n <= 0.
 __host__ __device__ __forceinline__ int attn_runs(int n, int wanted, int max_runs) {
   if (n <= 0) return 0;
   const int tiles = (n + 31) / 32;
   const int need = (n + kAttnChunk - 1) / kAttnChunk;   // never more than kAttnChunk tokens per run
   int r = (need + wanted - 1) / wanted * wanted;
-  const int by_tiles = tiles / 8 > 1 ? tiles / 8 : 1;
+  const int by_tiles = tiles / 5 > 1 ? tiles / 5 : 1;
   if (r > by_tiles) r = by_tiles;
   if (r < need) r = need;
   if (r > max_runs) r = max_runs;

@@ -127,9 +127,10 @@ inline bool kv_v_q8(int type) { return kv_v_fmt(type) == kFmtQ8; }
 // CU of MI355X), or, when n needs more than w runs of at most kAttnChunk
 // tokens, the next multiple of w, so that a uniform batch's work items fill
 // whole rounds of the chip (B = 8, n_kv = 8: 4, 8, 12, ... runs; 5 runs
-// would leave the second round three quarters empty); at most one run per 8
-// tiles (4 waves of 2 tiles at least), never fewer than ceil(n /
-// kAttnChunk), and at most attn_max_runs (the partial-result stride).
+// would leave the second round three quarters empty); at most one run per 5
+// tiles (where this binds, one or two sequences, one per 5 measured faster
+// than one per 4, 6 or 8), never fewer than ceil(n / kAttnChunk), and at
+// most attn_max_runs (the partial-result stride).
 // kAttnChunk = 4096: runs of up to 4096 tokens were faster than runs of up to
 // 1024 or 2048 at every long context measured (B = 8 at L = 6900 to 32000,
 // B = 16 at L = 32000) and as fast as 8192 or 16384; below ~4k tokens the

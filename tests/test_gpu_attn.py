@@ -208,7 +208,7 @@ def _nan_ws(nbytes):
 @pytest.mark.parametrize("L", [2400, 6900])
 def test_attention_small_batch_many_runs_nan_workspace(qd, kind, bsz, L):
     # B = 1 and 2 sequences of a Qwen-shaped layer (32/8 heads of 128): the
-    # runs per sequence (9 at L = 2400, 16-27 at L = 6900) fill the merge's
+    # runs per sequence (15 at L = 2400, 16-32 at L = 6900) fill the merge's
     # batches of eight partly, and every row the merge must not use is NaN
     import torch
     from quantized_decode_amd.tensors import dev, upload_cache
