@@ -30,13 +30,16 @@ def _setup(qd, model, caches, bsz):
     return sm, kv
 
 
-@pytest.mark.parametrize("kind", ["f16", "q8_0"])
-def test_noalloc_step_equals_workspace_step(qd, kind):
+@pytest.mark.parametrize("shape,kind", [("toy", "f16"), ("toy", "q8_0"), ("full", "q8_0")])
+def test_noalloc_step_equals_workspace_step(qd, shape, kind):
+    # full: one Qwen-shaped layer, whose Q8_0 new tokens are staged in the
+    # scratch by the QKV projection and appended by the attention kernel
     import torch
     from quantized_decode_amd.tensors import dev
-    dims = synth.TOY
+    dims = synth.TOY if shape == "toy" else synth.QWEN_SHAPED
+    n_layers = None if shape == "toy" else 1
     for call, (bsz, L) in enumerate([(4, 128), (2, 96)]):
-        model = synth.make_model(dims, 1600 + call)
+        model = synth.make_model(dims, 1600 + call, n_layers=n_layers)
         st = synth.Streams(1610 + call)
         caches = [synth.kv_cache(kind, st.next(), st.next(), bsz, dims.n_kv_heads, 160, dims.head_dim, [L] * bsz)
                   for _ in model.layers]
